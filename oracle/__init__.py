@@ -1,0 +1,282 @@
+"""CPU oracle for the batched verify step (TEST INFRASTRUCTURE ONLY).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library under
+``verify_step_w4_amd/`` never imports, links or calls it, and it imports
+nothing from the product: the two share only the seeded input generators in
+``verify_step_w4_amd/synth.py`` (which hold none of the method's arithmetic).
+
+The arithmetic lives in ``oracle/oracle.c`` (plain C, IEEE binary64,
+sequential sums in the order of each definition) and ``oracle/exact_law.py``
+(rational arithmetic).  This module is argument marshalling over ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc into oracle/_build/liboracle.so."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
+           "-fno-fast-math", "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class WarpStat(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_double), ("tau", ctypes.c_double), ("E", ctypes.c_double),
+                ("Z", ctypes.c_double), ("log_z", ctypes.c_double), ("P", ctypes.c_double),
+                ("S_at", ctypes.c_double), ("S_before", ctypes.c_double),
+                ("argmax", ctypes.c_int64), ("n_kept", ctypes.c_int64), ("k_star", ctypes.c_int64),
+                ("flags", ctypes.c_uint32), ("pad", ctypes.c_uint32)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_ if f != "pad"}
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_U64 = ctypes.c_uint64
+_F32 = ctypes.c_float
+_F64 = ctypes.c_double
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        L.oracle_f32_to_f16.argtypes = [_F32]
+        L.oracle_f32_to_f16.restype = ctypes.c_uint16
+        L.oracle_f16_value.argtypes = [ctypes.c_uint16]
+        L.oracle_f16_value.restype = _F64
+        L.oracle_w4_quantize.argtypes = [_P, _I64, _I64, _P, _P]
+        L.oracle_w4_code.argtypes = [_P, _I64, _I64, _I64]
+        L.oracle_w4_code.restype = ctypes.c_int
+        L.oracle_w4_gemm.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P]
+        L.oracle_w4_gemm_at.argtypes = [_P, _I64, _P, _P, _P]
+        L.oracle_warp.argtypes = [_P, _I64, _F32, _F32, ctypes.POINTER(WarpStat), _P]
+        L.oracle_philox4x64_10.argtypes = [_P, _P, _P]
+        L.oracle_verify_uniforms.argtypes = [_U64, _U64, _I32, _P, _P]
+        L.oracle_accept_with_uniforms.argtypes = [_P, ctypes.POINTER(WarpStat), _P, _P, _I32, _I64,
+                                                  _F32, _P, _P, _P, _P, _P]
+        L.oracle_spec_accept.argtypes = [_P, _P, _P, _I32, _I64, _F32, _F32, _U64, _U64,
+                                         ctypes.POINTER(WarpStat), _P, _P, _P]
+        L.oracle_spec_accept_trials.argtypes = [_P, _P, _P, _I64, _I32, _I64, _F32, _F32, _U64,
+                                                _U64, _P, _P, _P]
+        L.oracle_rmsnorm.argtypes = [_P, _P, _I64, _I64, _F64, _P]
+        L.oracle_swiglu.argtypes = [_P, _P, _I64, _P]
+        L.oracle_rope.argtypes = [_P, _I64, _I64, _F64, _P]
+        L.oracle_decode_attn.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]
+        L.oracle_moe_route.argtypes = [_P, _I64, _I64, _I64, _P, _P]
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# --------------------------------------------------------------------------
+# number formats
+# --------------------------------------------------------------------------
+def f32_to_f16_bits(x: float) -> int:
+    return int(lib().oracle_f32_to_f16(float(np.float32(x))))
+
+
+def f16_value(bits: int) -> float:
+    return float(lib().oracle_f16_value(int(bits)))
+
+
+# --------------------------------------------------------------------------
+# (a1) quantizer and (a2/a3) GEMM
+# --------------------------------------------------------------------------
+def w4_quantize(w: np.ndarray):
+    """w: float32 [N][K] (K % 64 == 0) -> (codes u8 [N][K/2], scales u16 [N][K/64])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    assert K % 64 == 0
+    codes = np.zeros((N, K // 2), dtype=np.uint8)
+    scales = np.zeros((N, K // 64), dtype=np.uint16)
+    lib().oracle_w4_quantize(_ptr(w), N, K, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def w4_codes_int(codes: np.ndarray) -> np.ndarray:
+    """Signed integer codes [N][K] from the canonical packed layout."""
+    N, K2 = codes.shape
+    out = np.empty((N, K2 * 2), dtype=np.int8)
+    L = lib()
+    for n in range(N):
+        for k in range(K2 * 2):
+            out[n, k] = L.oracle_w4_code(_ptr(codes), K2 * 2, n, k)
+    return out
+
+
+def w4_gemm(x_bf16: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """x_bf16: uint16 [M][K]; returns float64 [M][N]."""
+    x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    M, K = x_bf16.shape
+    N = codes.shape[0]
+    assert codes.shape == (N, K // 2) and scales.shape == (N, K // 64)
+    y = np.zeros((M, N), dtype=np.float64)
+    lib().oracle_w4_gemm(_ptr(x_bf16), M, K, _ptr(np.ascontiguousarray(codes)),
+                         _ptr(np.ascontiguousarray(scales)), N, _ptr(y))
+    return y
+
+
+def w4_gemm_at(x_row_bf16: np.ndarray, codes: np.ndarray, scales: np.ndarray, n: int) -> float:
+    x = np.ascontiguousarray(x_row_bf16, dtype=np.uint16)
+    K = x.shape[0]
+    crow = np.ascontiguousarray(codes[n])
+    srow = np.ascontiguousarray(scales[n])
+    out = np.zeros(1, dtype=np.float64)
+    lib().oracle_w4_gemm_at(_ptr(x), K, _ptr(crow), _ptr(srow), _ptr(out))
+    return float(out[0])
+
+
+# --------------------------------------------------------------------------
+# (a4) warp, (a5) Philox, (a6/a7) accept/resample
+# --------------------------------------------------------------------------
+def warp(z: np.ndarray, temperature: float, top_p: float, want_p: bool = False):
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    V = z.shape[0]
+    st = WarpStat()
+    p = np.zeros(V, dtype=np.float64) if want_p else None
+    lib().oracle_warp(_ptr(z), V, float(temperature), float(top_p), ctypes.byref(st),
+                      _ptr(p) if want_p else None)
+    return (st, p) if want_p else st
+
+
+def philox4x64_10(key, ctr):
+    k = np.ascontiguousarray(np.array(key, dtype=np.uint64))
+    c = np.ascontiguousarray(np.array(ctr, dtype=np.uint64))
+    out = np.zeros(4, dtype=np.uint64)
+    lib().oracle_philox4x64_10(_ptr(k), _ptr(c), _ptr(out))
+    return out
+
+
+def verify_uniforms(seed: int, step: int, D: int):
+    ua = np.zeros(D + 1, dtype=np.float64)
+    ur = np.zeros(D + 1, dtype=np.float64)
+    lib().oracle_verify_uniforms(int(seed), int(step), int(D), _ptr(ua), _ptr(ur))
+    return ua, ur
+
+
+def accept_with_uniforms(z: np.ndarray, stats, q: np.ndarray, draft: np.ndarray,
+                         temperature: float, u_acc: np.ndarray, u_res: np.ndarray):
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    M, V = z.shape
+    D = M - 1
+    q = np.ascontiguousarray(q, dtype=np.float32) if D else np.zeros((1, V), np.float32)
+    draft = np.ascontiguousarray(np.asarray(draft, dtype=np.int32).reshape(-1)) if D else np.zeros(1, np.int32)
+    st = (WarpStat * M)(*stats)
+    tok = np.zeros(M, dtype=np.int32)
+    nacc = np.zeros(1, dtype=np.int32)
+    fl = np.zeros(1, dtype=np.uint32)
+    ua = np.ascontiguousarray(u_acc, dtype=np.float64)
+    ur = np.ascontiguousarray(u_res, dtype=np.float64)
+    lib().oracle_accept_with_uniforms(_ptr(z), st, _ptr(q), _ptr(draft), D, V,
+                                      float(temperature), _ptr(ua), _ptr(ur), _ptr(tok),
+                                      _ptr(nacc), _ptr(fl))
+    return tok, int(nacc[0]), int(fl[0])
+
+
+def spec_accept(z: np.ndarray, q: np.ndarray, draft: np.ndarray, temperature: float, top_p: float,
+                seed: int, step: int):
+    """One verify problem. z: float32 [D+1][V], q: float32 [D][V], draft: int32 [D]."""
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    M, V = z.shape
+    D = M - 1
+    qq = np.ascontiguousarray(q, dtype=np.float32) if D else np.zeros((1, V), np.float32)
+    dr = np.ascontiguousarray(np.asarray(draft, dtype=np.int32).reshape(-1)) if D else np.zeros(1, np.int32)
+    st = (WarpStat * M)()
+    tok = np.zeros(M, dtype=np.int32)
+    nacc = np.zeros(1, dtype=np.int32)
+    fl = np.zeros(1, dtype=np.uint32)
+    lib().oracle_spec_accept(_ptr(z), _ptr(qq), _ptr(dr), D, V, float(temperature), float(top_p),
+                             int(seed), int(step), st, _ptr(tok), _ptr(nacc), _ptr(fl))
+    return tok, int(nacc[0]), int(fl[0]), [st[i] for i in range(M)]
+
+
+def spec_accept_trials(z: np.ndarray, q: np.ndarray, drafts: np.ndarray, temperature: float,
+                       top_p: float, seed: int, step0: int):
+    """B problems sharing logits z [D+1][V] and q [D][V]; drafts int32 [B][D]."""
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    M, V = z.shape
+    D = M - 1
+    drafts = np.ascontiguousarray(drafts, dtype=np.int32).reshape(-1, max(D, 1))
+    B = drafts.shape[0]
+    qq = np.ascontiguousarray(q, dtype=np.float32) if D else np.zeros((1, V), np.float32)
+    tok = np.zeros((B, M), dtype=np.int32)
+    nacc = np.zeros(B, dtype=np.int32)
+    fl = np.zeros(B, dtype=np.uint32)
+    lib().oracle_spec_accept_trials(_ptr(z), _ptr(qq), _ptr(drafts), B, D, V, float(temperature),
+                                    float(top_p), int(seed), int(step0), _ptr(tok), _ptr(nacc),
+                                    _ptr(fl))
+    return tok, nacc, fl
+
+
+# --------------------------------------------------------------------------
+# (a8) glue, (a9) attention, (a10) MoE routing
+# --------------------------------------------------------------------------
+def rmsnorm(x_bf16: np.ndarray, gamma_bf16: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    M, D = x.shape
+    y = np.zeros((M, D), dtype=np.float64)
+    lib().oracle_rmsnorm(_ptr(x), _ptr(np.ascontiguousarray(gamma_bf16, dtype=np.uint16)), M, D,
+                         float(eps), _ptr(y))
+    return y
+
+
+def swiglu(g_bf16: np.ndarray, u_bf16: np.ndarray) -> np.ndarray:
+    g = np.ascontiguousarray(g_bf16, dtype=np.uint16)
+    u = np.ascontiguousarray(u_bf16, dtype=np.uint16)
+    y = np.zeros(g.shape, dtype=np.float64)
+    lib().oracle_swiglu(_ptr(g), _ptr(u), g.size, _ptr(y))
+    return y
+
+
+def rope(x: np.ndarray, pos: int, theta: float = 10000.0) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    lib().oracle_rope(_ptr(x), x.shape[0], int(pos), float(theta), _ptr(out))
+    return out
+
+
+def decode_attn(q: np.ndarray, Kc: np.ndarray, Vc: np.ndarray, L: int) -> np.ndarray:
+    """q float64 [M][Hq][Dh] (rotated); Kc, Vc uint16 bf16 [Hkv][Lc][Dh]."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    M, Hq, Dh = q.shape
+    Hkv, Lc, _ = Kc.shape
+    out = np.zeros_like(q)
+    lib().oracle_decode_attn(_ptr(q), _ptr(np.ascontiguousarray(Kc, dtype=np.uint16)),
+                             _ptr(np.ascontiguousarray(Vc, dtype=np.uint16)), M, Hq, Hkv, Dh, L, Lc,
+                             _ptr(out))
+    return out
+
+
+def moe_route(logits: np.ndarray, topk: int):
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    M, E = lg.shape
+    ex = np.zeros((M, topk), dtype=np.int32)
+    wt = np.zeros((M, topk), dtype=np.float64)
+    lib().oracle_moe_route(_ptr(lg), M, E, topk, _ptr(ex), _ptr(wt))
+    return ex, wt

@@ -1,0 +1,110 @@
+"""Pins of the oracle's decoder-layer pieces: RMSNorm, SwiGLU, RoPE (a8),
+GQA decode attention (a9) and the MoE router (a10).
+
+Independent references: closed forms (unit RMS, scale invariance, rotation
+norm, relative-position property), torch's CPU silu and softmax, and special
+cases of attention whose answer is fixed (equal keys give the mean of V, a
+single position gives v0, future positions do not matter).
+"""
+import numpy as np
+import torch
+
+import oracle
+from verify_step_w4_amd import synth
+
+
+def test_rmsnorm_closed_forms():
+    x = synth.activations_bf16(1, 3, 256, 3.0)
+    ones = synth.f32_to_bf16_bits(np.ones(256, np.float32))
+    y = oracle.rmsnorm(x, ones, eps=0.0)
+    assert np.allclose(np.sqrt((y ** 2).mean(axis=1)), 1.0, rtol=1e-13)
+    # scale invariance under an exact power-of-two scaling of the input
+    x2 = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(x) * np.float32(4.0))
+    np.testing.assert_allclose(oracle.rmsnorm(x2, ones, 0.0), y, rtol=1e-13)
+    gam = synth.activations_bf16(2, 1, 256)[0]
+    yg = oracle.rmsnorm(x, gam, 0.0)
+    np.testing.assert_allclose(yg, y * synth.bf16_bits_to_f32(gam).astype(np.float64), rtol=1e-13)
+
+
+def test_swiglu_against_torch():
+    g = synth.activations_bf16(3, 1, 4096, 3.0)[0]
+    u = synth.activations_bf16(4, 1, 4096)[0]
+    y = oracle.swiglu(g, u)
+    gt = torch.from_numpy(synth.bf16_bits_to_f32(g).astype(np.float64))
+    ut = torch.from_numpy(synth.bf16_bits_to_f32(u).astype(np.float64))
+    ref = (torch.nn.functional.silu(gt) * ut).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-300)
+
+
+def test_rope_rotation_properties():
+    g = np.random.default_rng(5)
+    q = g.standard_normal(128)
+    k = g.standard_normal(128)
+    assert np.allclose(oracle.rope(q, 0), q, rtol=0, atol=0)
+    for pos in (1, 77, 4099):
+        assert abs(np.linalg.norm(oracle.rope(q, pos)) - np.linalg.norm(q)) < 1e-10
+    # <R(a) q, R(b) k> depends only on a - b
+    d1 = oracle.rope(q, 1030) @ oracle.rope(k, 1000)
+    d2 = oracle.rope(q, 40) @ oracle.rope(k, 10)
+    assert abs(d1 - d2) < 1e-9
+    # lowest frequency pair rotates by exactly pos radians
+    e = np.zeros(128)
+    e[0] = 1.0
+    r = oracle.rope(e, 3)
+    assert abs(r[0] - np.cos(3)) < 1e-15 and abs(r[64] - np.sin(3)) < 1e-15
+
+
+def _kv(seed, Hkv, Lc, Dh):
+    return (synth.activations_bf16(seed, Hkv * Lc, Dh).reshape(Hkv, Lc, Dh),
+            synth.activations_bf16(seed + 1, Hkv * Lc, Dh).reshape(Hkv, Lc, Dh))
+
+
+def test_attention_special_cases():
+    M, Hq, Hkv, Dh, L = 3, 10, 2, 64, 20
+    Lc = L + M
+    Kc, Vc = _kv(7, Hkv, Lc, Dh)
+    q = np.random.default_rng(1).standard_normal((M, Hq, Dh))
+    # equal keys -> uniform weights -> mean of the visible values
+    Keq = np.repeat(Kc[:, :1, :], Lc, axis=1).copy()
+    out = oracle.decode_attn(q, Keq, Vc, L)
+    Vf = synth.bf16_bits_to_f32(Vc).astype(np.float64)
+    for i in range(M):
+        for h in range(Hq):
+            np.testing.assert_allclose(out[i, h], Vf[h // 5, :L + i + 1].mean(axis=0), rtol=1e-12)
+    # a single visible position returns v0
+    out1 = oracle.decode_attn(q[:1], Kc, Vc, 0)
+    for h in range(Hq):
+        np.testing.assert_allclose(out1[0, h], Vf[h // 5, 0], rtol=1e-15)
+    # causality: changing positions beyond L+i does not change row i
+    Vc2 = Vc.copy()
+    Vc2[:, L + 1:, :] = 0
+    out2 = oracle.decode_attn(q, Kc, Vc2, L)
+    np.testing.assert_array_equal(out2[0], out[0])
+    assert not np.array_equal(out2[1], out[1])
+
+
+def test_attention_matches_torch_softmax():
+    M, Hq, Hkv, Dh, L = 2, 8, 2, 32, 50
+    Kc, Vc = _kv(9, Hkv, L + M, Dh)
+    q = np.random.default_rng(2).standard_normal((M, Hq, Dh))
+    out = oracle.decode_attn(q, Kc, Vc, L)
+    Kf = torch.from_numpy(synth.bf16_bits_to_f32(Kc).astype(np.float64))
+    Vf = torch.from_numpy(synth.bf16_bits_to_f32(Vc).astype(np.float64))
+    for i in range(M):
+        for h in range(Hq):
+            s = Kf[h // 4, :L + i + 1] @ torch.from_numpy(q[i, h]) / np.sqrt(Dh)
+            ref = torch.softmax(s, 0) @ Vf[h // 4, :L + i + 1]
+            np.testing.assert_allclose(out[i, h], ref.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_moe_route_against_sort_and_softmax():
+    lg = synth.synthetic_logits(4, 4, 128, 1.0)
+    lg[2, 5] = lg[2, 9] = lg[2].max() + 1          # tie -> lower index first
+    ex, wt = oracle.moe_route(lg, 8)
+    for m in range(4):
+        order = np.argsort(-lg[m].astype(np.float64), kind="stable")[:8]
+        assert list(ex[m]) == list(order)
+        pr = torch.softmax(torch.from_numpy(lg[m].astype(np.float64)), 0).numpy()
+        np.testing.assert_allclose(wt[m], pr[order] / pr[order].sum(), rtol=1e-13)
+        assert abs(wt[m].sum() - 1) < 1e-14
+    assert ex[2, 0] == 5 and ex[2, 1] == 9
