@@ -78,9 +78,10 @@ def test_attention_special_cases():
     # causality: changing positions beyond L+i does not change row i
     Vc2 = Vc.copy()
     Vc2[:, L + 1:, :] = 0
+    ref = oracle.decode_attn(q, Kc, Vc, L)
     out2 = oracle.decode_attn(q, Kc, Vc2, L)
-    np.testing.assert_array_equal(out2[0], out[0])
-    assert not np.array_equal(out2[1], out[1])
+    np.testing.assert_array_equal(out2[0], ref[0])
+    assert not np.array_equal(out2[1], ref[1])
 
 
 def test_attention_matches_torch_softmax():
