@@ -1,0 +1,179 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched verify step on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line (rank 0): verify steps/s for the workload, plus the
+roofline of the dominant kernel (the W4 skinny GEMM) measured with HIP
+events on the stream it runs on, and the CPU oracle timed on a bounded
+sample of the same workload.
+
+Workloads (synthetic, seeded; the weights are random, drawn on the device):
+  lm_head_verify  LM-head verify step: hidden rows bf16 ~N(0,1) [4][5120],
+                  W4 group-64 LM head [151936][5120] (~N(0,0.02), three copies
+                  rotated so the 256 MB Infinity Cache cannot hold the working
+                  set), temperature 0.6 / top_p 0.95 statistics, Leviathan–Chen
+                  acceptance of 3 drafts drawn from q = softmax(N(0,3)).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "verify steps/s and achieved HBM GB/s (W4 skinny GEMM, M=4) vs peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------
+# LM-head verify workload
+# --------------------------------------------------------------------------
+def lm_head_workload(args):
+    import numpy as np
+    import torch
+
+    from verify_step_w4_amd import binding as B
+    from verify_step_w4_amd.model import BYTES_PER_WEIGHT, LMHeadVerify, W4Linear
+
+    V, d, M, D = 151936, 5120, 4, 3
+    T, top_p = 0.6, 0.95
+    seed = 0x5EED0003
+    ncopies = 3
+    nsteps_inputs = 64
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261203)
+    log(f"generating {ncopies} W4 LM heads [{V}][{d}]")
+    heads = [W4Linear.random(V, d, 0.02, gen) for _ in range(ncopies)]
+    xs = (torch.randn((nsteps_inputs, M, d), generator=gen, device=dev)).to(torch.bfloat16).view(torch.int16)
+    qs = torch.softmax(torch.randn((nsteps_inputs, D, V), generator=gen, device=dev, dtype=torch.float64) * 3.0,
+                       dim=-1).to(torch.float32)
+    drafts = torch.multinomial(qs.reshape(-1, V).double(), 1, generator=gen).reshape(nsteps_inputs, D).to(torch.int32)
+    vs = LMHeadVerify(V, d, M)
+    K, W = args.steps, args.warmup
+    tok_all = torch.empty((K, M), dtype=torch.int32, device=dev)
+    nacc_all = torch.empty(K, dtype=torch.int32, device=dev)
+    flag_all = torch.empty(K, dtype=torch.int32, device=dev)
+
+    def one(i, timed=False, ev=None):
+        j = i % nsteps_inputs
+        head = heads[i % ncopies]
+        if ev is not None:
+            ev[0].record()
+        vs.gemm(xs[j], head)
+        if ev is not None:
+            ev[1].record()
+        out = {}
+        if timed:
+            out = dict(tokens=tok_all[i:i + 1], n_acc=nacc_all[i:i + 1], flags=flag_all[i:i + 1])
+        vs.stats_and_accept(qs[j], drafts[j], T, top_p, seed, i, **out)
+
+    for i in range(W):
+        one(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        one(i, timed=True, ev=evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    gemm_ms = [a.elapsed_time(b) for a, b in evs]
+    gemm_avg = float(np.mean(gemm_ms))
+    alg_bytes = V * d * BYTES_PER_WEIGHT + M * d * 2 + M * V * 4
+    achieved = alg_bytes / (gemm_avg * 1e-3) / 1e9
+    nacc = nacc_all.cpu().numpy()
+    flags = flag_all.cpu().numpy()
+    hist = np.bincount(np.clip(nacc, 0, D), minlength=D + 1).tolist()
+    res = dict(
+        ms_per_step=total_ms / K,
+        value=K / (total_ms * 1e-3),
+        wall_s=wall,
+        config={"workload": "lm_head_verify", "d": d, "V": V, "M": M, "draft_depth": D, "temperature": T,
+                "top_p": top_p, "weights": "int4 group-64 symmetric, fp16 scales", "lm_head_copies": ncopies},
+        roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                  "kernel": "w4_gemm_kernel<4>", "alg_bytes_per_launch": int(alg_bytes),
+                  "avg_launch_us": round(gemm_avg * 1e3, 2)},
+        stages_us={"w4_gemm_lm_head": round(gemm_avg * 1e3, 2),
+                   "stats_and_accept": round(total_ms / K * 1e3 - gemm_avg * 1e3, 2)},
+        accepted_length_hist=hist,
+        flagged_steps=int(((flags & ~B.FLAG_NONFINITE) != 0).sum()),
+    )
+    return res
+
+
+def lm_head_cpu_baseline(nsteps=3):
+    """The CPU oracle on a bounded sample: nsteps full LM-head verify steps
+    (fp64 W4 GEMM over all 151936 rows, sorted-vocab top-p, scalar accept)."""
+    import numpy as np
+
+    import oracle
+    from verify_step_w4_amd import synth
+    V, d, D = 151936, 5120, 3
+    g = synth.rng(synth.SEED_BASE + 3)
+    w = synth.normal_f32(g, (V, d), 0.02)
+    codes, scales = oracle.w4_quantize(w)
+    del w
+    xs = [synth.f32_to_bf16_bits(synth.normal_f32(g, (D + 1, d), 1.0)) for _ in range(nsteps)]
+    q, drafts = synth.q_and_drafts(synth.SEED_BASE + 33, D, V, 3.0, B=nsteps)
+    t0 = time.perf_counter()
+    for s in range(nsteps):
+        z = oracle.w4_gemm(xs[s], codes, scales).astype(np.float32)
+        oracle.spec_accept(z, q, drafts[s], 0.6, 0.95, 0x5EED0003, s)
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(nsteps / dt, 4), "unit": "verify steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nsteps} LM-head verify steps (d=5120, V=151936, M=4), quantisation untimed"}
+
+
+WORKLOADS = {"lm_head_verify": (lm_head_workload, lm_head_cpu_baseline)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="lm_head_verify", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    run, cpu = WORKLOADS[args.workload]
+    res = run(args)
+    out = {"metric": METRIC, "value": round(res["value"], 3), "unit": "verify steps/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic", "config": res["config"], "roofline": res["roofline"]}
+    for k in ("stages_us", "accepted_length_hist", "flagged_steps"):
+        if k in res:
+            out[k] = res[k]
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+/*
+ * vw4.h — C ABI of the batched-verify library for MI355X (gfx950).
+ *
+ * The library implements the verify half of multi-token-prediction
+ * self-speculative decoding: the main model scores all M = D+1 rows (D drafts
+ * plus the bonus position) in one pass, then the drafts are accepted or
+ * corrected so that the emitted tokens follow the target distribution exactly.
+ *   - hazakura.dev, "mtplx——M5 Maxで63tok/s、Apple SiliconのローカルLLMが2倍以上速くなる日",
+ *     section "4層のアーキテクチャ": Layer 0 names the small-M (M = 3..6) matmul
+ *     and the 4-bit LM head; Layer 2 names the cycle draft -> one parallel
+ *     verify -> probability-ratio acceptance -> residual correction -> bonus token.
+ *   - devtrends.cc, "Apple Silicon上でローカルLLMを最大2倍高速化するMTPLX",
+ *     section "2つ目のモデル不要！MTPの裏技": the whole batch of drafts is verified
+ *     in a single forward pass with Leviathan–Chen rejection sampling and
+ *     residual correction; at temperature 0.6 / top_p 0.95 the output law is that
+ *     of plain step-by-step sampling.
+ *   - gist.science, "BaseRT: Best-in-Class LLM Inference on Apple Silicon via
+ *     Native Metal", section "メソドロジー": dequantisation inside the GEMV inner
+ *     loop; all decode buffers preallocated by the caller (zero allocation in the
+ *     decode loop); FlashAttention-style online softmax.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_dev, and every array argument of a compute call, are
+ *     device memory owned by the caller.  The library allocates nothing and
+ *     keeps no pointer after returning.  Scratch memory comes from a caller
+ *     workspace sized by the matching *_workspace_bytes() query; a workspace
+ *     must be zero-filled once when it is allocated (the library leaves its
+ *     counters at zero after every call, so later calls need no clearing).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *     only enqueue work; results are valid once the stream reaches that point.
+ *     Calls that share a workspace must not run concurrently.
+ *   - Return codes: VW4_OK, or a negative error detected on the host before
+ *     anything is enqueued (nothing is written in that case).  vw4_last_error()
+ *     returns a thread-local message for the last failure.  Data-dependent
+ *     conditions (non-finite logits, near-ties) are not errors: they set flag
+ *     bits in the outputs.
+ */
+#ifndef VW4_H
+#define VW4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exported symbols (the library is built with hidden default visibility). */
+#define VW4_API __attribute__((visibility("default")))
+
+#define VW4_OK 0
+#define VW4_EINVAL (-1)       /* bad shape, alignment or parameter */
+#define VW4_EUNSUPPORTED (-2) /* valid request this build does not handle */
+#define VW4_EHIP (-3)         /* HIP runtime or launch failure */
+#define VW4_EWORKSPACE (-4)   /* workspace missing or too small */
+
+/* Output dtypes of the GEMM. */
+#define VW4_F32 0
+#define VW4_BF16 1
+
+/* Row flags (vw4_rowstat.flags) and problem flags (spec_accept out_flags). */
+#define VW4_FLAG_NONFINITE 1u   /* a logit was NaN or infinite */
+#define VW4_FLAG_TOPP_TIE 2u    /* top-p boundary mass within 1e-9 * E of top_p * E */
+#define VW4_FLAG_ACCEPT_TIE 4u  /* an accept test had |u - p/q| < 1e-5 */
+#define VW4_FLAG_CDF_TIE 8u     /* the sampled token's CDF boundary within 1e-9 * R of u * R */
+#define VW4_FLAG_R_ZERO 16u     /* residual mass was zero; sampled from p instead */
+
+/* Per-row statistics of the tempered, top-p-truncated target distribution.
+ * For T > 0 the target is p_j = exp((z_j - max_logit)/T) / exp(log_z) for
+ * z_j >= tau, else 0.  For T == 0 it is one-hot at argmax (tau = max_logit,
+ * log_z = 0, n_kept = 1). */
+typedef struct vw4_rowstat {
+    float max_logit;   /* m = max_j z_j */
+    float tau;         /* cutoff logit: the kept set is { j : z_j >= tau } */
+    double log_z;      /* log of sum over the kept set of exp((z_j - m)/T) */
+    int32_t argmax;    /* lowest index attaining the max */
+    int32_t n_kept;    /* size of the kept set */
+    uint32_t flags;    /* VW4_FLAG_NONFINITE | VW4_FLAG_TOPP_TIE */
+    uint32_t pad;
+} vw4_rowstat;
+
+/* Library version string and the calling thread's last error message. */
+VW4_API const char* vw4_version(void);
+VW4_API const char* vw4_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * W4 weight format (offline), for the 4-bit weights named on
+ * hazakura.dev's mtplx page (section "4層のアーキテクチャ", Layer 0): symmetric
+ * int4 codes c in [-7, 7], one fp16 scale per 64 consecutive elements along K,
+ * scale = fp16_rne(absmax / 7), c = clamp(rint_half_even(w / scale), -7, 7)
+ * with the rounded scale, all-zero groups get scale 0.
+ *
+ * Canonical layout: codes u8 [N][K/2] holding c + 8, even k in the low nibble;
+ * scales f16 [N][K/64].  Kernel ("packed") layout, produced by vw4_w4_pack:
+ * rows padded to a multiple of 64 and stored tile-major so that one wavefront
+ * streams 64 rows with fully coalesced 16-byte loads; sizes from
+ * vw4_w4_packed_bytes.  Requirements: K % 64 == 0, N >= 1, finite weights.
+ * ------------------------------------------------------------------------ */
+
+/* Quantise fp32 host weights w[N][K] into host canonical codes and scales. */
+VW4_API int vw4_w4_quantize_host(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales);
+
+/* Same arithmetic on the GPU: device w_dev[N][K] -> device canonical arrays. */
+VW4_API int vw4_w4_quantize(const float* w_dev, int64_t N, int64_t K, uint8_t* codes_dev,
+                    uint16_t* scales_dev, void* stream);
+
+/* Bytes of the packed code array; *scale_bytes (if not NULL) receives the
+ * bytes of the packed scale array.  Returns 0 for invalid shapes. */
+VW4_API size_t vw4_w4_packed_bytes(int64_t N, int64_t K, size_t* scale_bytes);
+
+/* Canonical (device) -> packed (device). */
+VW4_API int vw4_w4_pack(const uint8_t* codes_dev, const uint16_t* scales_dev, int64_t N, int64_t K,
+                uint8_t* packed_dev, uint16_t* packed_scales_dev, void* stream);
+
+/* Packed (device) -> canonical (device); the inverse of vw4_w4_pack. */
+VW4_API int vw4_w4_unpack(const uint8_t* packed_dev, const uint16_t* packed_scales_dev, int64_t N, int64_t K,
+                  uint8_t* codes_dev, uint16_t* scales_dev, void* stream);
+
+/* Quantise device fp32 weights straight into the packed layout (equals
+ * vw4_w4_quantize followed by vw4_w4_pack, without the canonical copy). */
+VW4_API int vw4_w4_quantize_packed(const float* w_dev, int64_t N, int64_t K, uint8_t* packed_dev,
+                           uint16_t* packed_scales_dev, void* stream);
+
+/* ------------------------------------------------------------------------
+ * W4 skinny GEMM (hazakura.dev mtplx page, "4層のアーキテクチャ" Layer 0: the
+ * small-M matmul of the verify pass; gist.science BaseRT summary, "メソドロジー":
+ * dequantisation in the inner loop, weights never materialised).
+ *   y[m][n] = sum_k x[m][k] * c[n][k] * scale[n][k/64]      0 <= m < M, 0 <= n < N
+ * x: bf16 [M][ldx] (row stride ldx elements, ldx >= K, ldx % 8 == 0, 16-byte
+ * aligned); w: packed codes/scales of an [N][K] matrix; y: fp32 or bf16 (RNE)
+ * [M][ldy] with ldy >= N.  1 <= M <= 8, K % 64 == 0, K <= 65536.
+ * Accumulation is fp32 in a fixed order that does not depend on M, so row m of
+ * an M-row call equals the single-row call on x[m] bit for bit, and repeated
+ * calls are bitwise reproducible.  ws may be NULL when
+ * vw4_gemm_workspace_bytes() returns 0 for the shape.
+ * ------------------------------------------------------------------------ */
+VW4_API size_t vw4_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K);
+
+VW4_API int w4_skinny_gemm(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, const uint16_t* scales_packed,
+                   void* y, int64_t ldy, int32_t y_dtype, int32_t M, int32_t N, int32_t K,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * verify_logits: LM head of the verify rows, then the temperature / top-p
+ * statistics of every row (devtrends.cc MTPLX page, section
+ * "2つ目のモデル不要！MTPの裏技": sampling at temperature 0.6, top_p 0.95).
+ *   hidden (nullable): bf16 [rows][ldh]; lm_packed/lm_scales: packed W4 [V][d].
+ *   If hidden != NULL: logits[rows][V] = w4 GEMM(hidden) (fp32), then stats.
+ *   If hidden == NULL: logits is an INPUT and only the statistics are computed.
+ * Statistics (one vw4_rowstat per row): m = max; for T > 0, e_j = exp((z_j - m)/T)
+ * in fp64, E = sum e_j; the kept set is the smallest prefix of the vocabulary
+ * sorted by (logit desc, index asc) whose mass reaches top_p * E, widened to
+ * all tokens whose logit equals the cutoff tau; top_p >= 1 keeps all; T == 0
+ * is greedy.  Requires 1 <= rows <= 64, 1 <= V <= 2^24, d % 64 == 0,
+ * T >= 0 (finite), 0 < top_p <= 1.  Workspace: vw4_workspace_bytes(rows, V).
+ * ------------------------------------------------------------------------ */
+VW4_API size_t vw4_workspace_bytes(int32_t rows, int32_t V);
+
+VW4_API int verify_logits(const uint16_t* hidden, int64_t ldh, const uint8_t* lm_packed, const uint16_t* lm_scales,
+                  int32_t rows, int32_t V, int32_t d, float temperature, float top_p, float* logits,
+                  vw4_rowstat* stats, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * spec_accept: Leviathan–Chen acceptance, residual resampling and bonus token
+ * for B independent verify problems of M = D+1 rows each (hazakura.dev mtplx
+ * page, "4層のアーキテクチャ" Layer 2 and "mtplxの数字——本当なの？"; devtrends.cc
+ * MTPLX page, "2つ目のモデル不要！MTPの裏技").
+ * Problem b reads logits + b*logits_bstride ([M][V] fp32), stats + b*stats_bstride
+ * ([M] rowstats from verify_logits with the same temperature), q + b*q_bstride
+ * ([D][V] fp32 draft distributions, used as given) and draft + b*D ([D] int32);
+ * a stride of 0 shares one array between all problems.  With key (seed, 0) and
+ * counter (step0 + b, i, 0, 0), Philox4x64-10 (Salmon et al., SC'11) gives the
+ * row-i uniforms u_acc = (r0 >> 11) 2^-53 and u_res = (r1 >> 11) 2^-53.
+ *   for i < D: accept draft x_i iff u_acc[i] * q_i(x_i) < p_i(x_i), else stop (k = i)
+ *   k < D: sample y from max(0, p_k - q_k) / R; k == D: sample the bonus y from p_D
+ *   sampling: y = min{ j : C_j > u_res[k] * R } with C the running sum in index order
+ * Outputs: out_tokens[b][0..k] = x_0..x_{k-1}, y; the rest -1; out_n_acc[b] = k;
+ * out_flags[b] = VW4_FLAG_* bits (a row flagged non-finite gives tokens -1 and
+ * n_acc -1).  D = 0 is plain sampling of p_0 (one autoregressive step).
+ * Requires 1 <= B <= 2^24, 0 <= D <= 7, 1 <= V <= 2^24, draft ids in [0, V).
+ * Workspace: vw4_accept_workspace_bytes(B, V).
+ * ------------------------------------------------------------------------ */
+VW4_API size_t vw4_accept_workspace_bytes(int32_t B, int32_t V);
+
+VW4_API int spec_accept(const float* logits, int64_t logits_bstride, const vw4_rowstat* stats, int64_t stats_bstride,
+                const float* q, int64_t q_bstride, const int32_t* draft, int32_t B, int32_t D, int32_t V,
+                float temperature, uint64_t seed, uint64_t step0, int32_t* out_tokens, int32_t* out_n_acc,
+                uint32_t* out_flags, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VW4_H */

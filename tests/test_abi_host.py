@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol include/vw4.h declares, validates arguments before enqueuing
+anything, and its host quantiser matches the oracle bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from verify_step_w4_amd import binding as B
+from verify_step_w4_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "vw4.h")).read()
+    return set(re.findall(r"^VW4_API\s+[\w\s\*]+?\b(\w+)\(", src, flags=re.M))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert {"w4_skinny_gemm", "verify_logits", "spec_accept"} <= names
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert names == set(B.SIGNATURES), "binding signatures out of sync with vw4.h"
+
+
+def test_version_and_error_strings():
+    assert B.version().startswith("vw4")
+    assert isinstance(B.last_error(), str)
+
+
+def test_rowstat_layout():
+    assert B.ROWSTAT_DTYPE.itemsize == 32
+    assert B.ROWSTAT_DTYPE.fields["log_z"][1] == 8
+    assert B.ROWSTAT_DTYPE.fields["argmax"][1] == 16
+
+
+def test_host_quantizer_matches_oracle():
+    g = np.random.default_rng(4)
+    w = (g.standard_normal((33, 640)) * 0.02).astype(np.float32)
+    w[0, :64] = 0.0
+    w[1, 64:128] *= 1e-7          # fp16-subnormal scale
+    w[2, 128:192] = 1.5e-8         # scale underflows to zero
+    w[3, 192:256] = np.float32(7.5) * np.float32(2.0 ** -10)  # exact halves
+    c1, s1 = B.w4_quantize_host(w)
+    c2, s2 = oracle.w4_quantize(w)
+    assert np.array_equal(s1, s2)
+    assert np.array_equal(c1, c2)
+
+
+def test_host_quantizer_on_a_layer_shape():
+    w = synth.linear_weights(7, 64, 5120)
+    c1, s1 = B.w4_quantize_host(w)
+    c2, s2 = oracle.w4_quantize(w)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+def test_packed_sizes():
+    cb, sb = B.packed_sizes(100, 320)
+    assert cb == 128 * 160 and sb == 128 * 5 * 2
+    assert B.lib().vw4_w4_packed_bytes(10, 100, None) == 0
+
+
+def test_workspace_queries():
+    assert B.gemm_workspace_bytes(4, 151936, 5120) == 0          # enough tiles: no K split across workgroups
+    assert B.gemm_workspace_bytes(4, 5120, 5120) > 0
+    assert B.verify_workspace_bytes(4, 151936) > 0
+    assert B.accept_workspace_bytes(1, 151936) > 0
+    assert B.lib().vw4_workspace_bytes(0, 10) == 0
+    assert B.lib().vw4_accept_workspace_bytes(1, 0) == 0
+
+
+def _call(name, *args):
+    return getattr(B.lib(), name)(*args)
+
+
+@pytest.mark.parametrize("M,N,K,ldx,ldy,ydt", [
+    (0, 64, 64, 64, 64, 0), (9, 64, 64, 64, 64, 0), (1, 0, 64, 64, 64, 0), (1, 64, 100, 128, 64, 0),
+    (1, 64, 64, 60, 64, 0), (1, 64, 64, 64, 10, 0), (1, 64, 64, 64, 64, 7),
+])
+def test_gemm_rejects_bad_arguments(M, N, K, ldx, ldy, ydt):
+    fake = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
+    rc = _call("w4_skinny_gemm", fake, ldx, fake, fake, fake, ldy, ydt, M, N, K, None, 0, None)
+    assert rc == B.VW4_EINVAL
+    assert "w4_skinny_gemm" in B.last_error()
+
+
+def test_gemm_requires_workspace_when_split():
+    fake = ctypes.c_void_p(0x100000)
+    rc = _call("w4_skinny_gemm", fake, 5120, fake, fake, fake, 5120, 0, 4, 5120, 5120, None, 0, None)
+    assert rc == B.VW4_EWORKSPACE
+
+
+def test_verify_logits_rejects_bad_arguments():
+    fake = ctypes.c_void_p(0x100000)
+    assert _call("verify_logits", None, 0, None, None, 0, 100, 64, 0.6, 0.95, fake, fake, fake, 1 << 20,
+                 None) == B.VW4_EINVAL
+    assert _call("verify_logits", None, 0, None, None, 4, 100, 64, -1.0, 0.95, fake, fake, fake, 1 << 20,
+                 None) == B.VW4_EINVAL
+    assert _call("verify_logits", None, 0, None, None, 4, 100, 64, 0.6, 0.0, fake, fake, fake, 1 << 20,
+                 None) == B.VW4_EINVAL
+    assert _call("verify_logits", None, 0, None, None, 4, 100, 64, 0.6, 0.95, fake, fake, fake, 16,
+                 None) == B.VW4_EWORKSPACE
+
+
+def test_spec_accept_rejects_bad_arguments():
+    fake = ctypes.c_void_p(0x100000)
+    args = lambda B_, D, V: (fake, 0, fake, 0, fake, 0, fake, B_, D, V, 0.6, 1, 0, fake, fake, fake, fake,
+                             1 << 20, None)
+    assert _call("spec_accept", *args(1, 8, 100)) == B.VW4_EINVAL
+    assert _call("spec_accept", *args(0, 3, 100)) == B.VW4_EINVAL
+    assert _call("spec_accept", *args(1, 3, 0)) == B.VW4_EINVAL
+    a = list(args(1, 3, 100))
+    a[4] = None  # q missing with D > 0
+    assert _call("spec_accept", *a) == B.VW4_EINVAL

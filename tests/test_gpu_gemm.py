@@ -1,0 +1,148 @@
+"""GPU parity of the W4 format (a1) and the W4 skinny GEMM (a2/a3) against the
+oracle.  Each side quantises the same fp32 weights itself; codes and scales
+must agree bit for bit, GEMM outputs within 1e-3 relative."""
+import numpy as np
+import pytest
+
+import oracle
+from verify_step_w4_amd import binding as B
+from verify_step_w4_amd import synth
+
+from helpers import GEMM_RTOL, dev, gemm_rel_err, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _weights(seed, N, K):
+    w = synth.linear_weights(seed, N, K)
+    return w
+
+
+@pytest.mark.parametrize("N,K", [(1, 64), (64, 64), (100, 320), (257, 1024), (1000, 2048)])
+def test_quantizer_bit_exact(N, K):
+    import torch
+    log(f"quantize N={N} K={K}")
+    w = _weights(N + K, N, K)
+    w[0, :64] = 0.0
+    codes, scales = B.w4_quantize(dev(w))
+    packed, pscales = B.w4_quantize_packed(dev(w))
+    torch.cuda.synchronize()
+    oc, os_ = oracle.w4_quantize(w)
+    assert np.array_equal(host(codes), oc)
+    assert np.array_equal(host(scales), os_)
+    # packing the canonical form gives the fused packed form; unpacking inverts it
+    p2, s2 = B.w4_pack(codes, scales, N, K)
+    c3, s3 = B.w4_unpack(packed, pscales, N, K)
+    torch.cuda.synchronize()
+    assert torch.equal(p2, packed) and torch.equal(s2, pscales)
+    assert np.array_equal(host(c3), oc) and np.array_equal(host(s3), os_)
+
+
+def _gemm(x_bits, packed, pscales, M, N, K, out_dtype="f32"):
+    import torch
+    y = torch.empty((M, N), dtype=torch.float32 if out_dtype == "f32" else torch.int16, device="cuda")
+    ws = B.workspace(B.gemm_workspace_bytes(M, N, K))
+    B.w4_skinny_gemm(dev(x_bits) if isinstance(x_bits, np.ndarray) else x_bits, packed, pscales, y, M, N, K, ws=ws)
+    torch.cuda.synchronize()
+    return y
+
+
+SHAPES = [(1, 64), (64, 128), (100, 320), (257, 1024), (1000, 2048), (333, 5120), (64, 17408)]
+
+
+@pytest.mark.parametrize("N,K", SHAPES)
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 6, 8])
+def test_gemm_matches_oracle(M, N, K):
+    log(f"gemm M={M} N={N} K={K}")
+    w = _weights(7 * N + K, N, K)
+    x = synth.activations_bf16(M * 1000 + N, M, K)
+    packed, pscales = B.w4_quantize_packed(dev(w))
+    y = host(_gemm(x, packed, pscales, M, N, K))
+    oc, os_ = oracle.w4_quantize(w)
+    ref = oracle.w4_gemm(x, oc, os_)
+    err = gemm_rel_err(y, ref)
+    assert err <= GEMM_RTOL, err
+
+
+def test_gemm_bf16_output_is_rounded_fp32():
+    import torch
+    M, N, K = 4, 300, 1024
+    log(f"gemm bf16 out M={M} N={N} K={K}")
+    w = _weights(5, N, K)
+    x = synth.activations_bf16(6, M, K)
+    packed, pscales = B.w4_quantize_packed(dev(w))
+    y32 = host(_gemm(x, packed, pscales, M, N, K))
+    y16 = host(_gemm(x, packed, pscales, M, N, K, "bf16"))
+    assert np.array_equal(y16, synth.f32_to_bf16_bits(y32))
+
+
+@pytest.mark.parametrize("N,K", [(5120, 5120), (1000, 17408), (300, 1024)])
+def test_gemm_rows_independent_of_M_and_deterministic(N, K):
+    log(f"gemm M-independence N={N} K={K}")
+    w = _weights(11, N, K)
+    x = synth.activations_bf16(12, 6, K)
+    packed, pscales = B.w4_quantize_packed(dev(w))
+    y6 = host(_gemm(x, packed, pscales, 6, N, K))
+    y6b = host(_gemm(x, packed, pscales, 6, N, K))
+    assert np.array_equal(y6, y6b)
+    for m in (0, 3, 5):
+        y1 = host(_gemm(x[m:m + 1], packed, pscales, 1, N, K))
+        assert np.array_equal(y1[0], y6[m])
+
+
+def test_gemm_strided_rows():
+    import torch
+    M, N, K = 3, 200, 512
+    log("gemm strided x/y")
+    w = _weights(21, N, K)
+    xfull = synth.activations_bf16(22, M, K + 64)
+    packed, pscales = B.w4_quantize_packed(dev(w))
+    xd = dev(xfull)
+    y = torch.zeros((M, N + 10), dtype=torch.float32, device="cuda")
+    ws = B.workspace(B.gemm_workspace_bytes(M, N, K))
+    B.w4_skinny_gemm(xd, packed, pscales, y, M, N, K, ws=ws, ldx=K + 64, ldy=N + 10)
+    torch.cuda.synchronize()
+    yh = host(y)
+    oc, os_ = oracle.w4_quantize(w)
+    ref = oracle.w4_gemm(np.ascontiguousarray(xfull[:, :K]), oc, os_)
+    assert gemm_rel_err(yh[:, :N], ref) <= GEMM_RTOL
+    assert np.all(yh[:, N:] == 0)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["qkv", "o", "gate_up", "down"])
+def test_gemm_layer_shapes_sampled(name):
+    """Dense 27B-layer linears at full size, M=4, in the benchmark's launch
+    configuration; 128 sampled outputs per row checked against the oracle."""
+    N, K = synth.LAYER27B_LINEARS[name]
+    log(f"gemm full-size {name} N={N} K={K}")
+    w = _weights(100 + N + K, N, K)
+    x = synth.activations_bf16(200 + N, 4, K)
+    packed, pscales = B.w4_quantize_packed(dev(w))
+    y = host(_gemm(x, packed, pscales, 4, N, K))
+    g = np.random.default_rng(N)
+    cols = np.unique(np.concatenate([g.integers(0, N, 124), [0, 63, N - 64, N - 1]]))
+    oc, os_ = oracle.w4_quantize(np.ascontiguousarray(w[cols]))
+    ref = oracle.w4_gemm(x, oc, os_)
+    # row-rms floor from the full GPU row (the sampled reference has too few entries)
+    rms = np.sqrt((y.astype(np.float64) ** 2).mean(axis=1, keepdims=True))
+    err = np.abs(y[:, cols] - ref) / np.maximum(np.abs(ref), rms)
+    assert err.max() <= GEMM_RTOL, err.max()
+
+
+@pytest.mark.slow
+def test_lm_head_large_vocab_sampled():
+    """d=5120, V=151936 LM head at M=4, sampled outputs against the oracle."""
+    V, d = synth.LM_LARGE["V"], synth.LM_LARGE["d"]
+    log(f"gemm LM head V={V} d={d}")
+    w = _weights(31337, V, d)
+    x = synth.activations_bf16(31338, 4, d)
+    packed, pscales = B.w4_quantize_packed(dev(w))
+    y = host(_gemm(x, packed, pscales, 4, V, d))
+    g = np.random.default_rng(1)
+    cols = np.unique(np.concatenate([g.integers(0, V, 250), [0, V - 1, V - 64]]))
+    oc, os_ = oracle.w4_quantize(np.ascontiguousarray(w[cols]))
+    ref = oracle.w4_gemm(x, oc, os_)
+    rms = np.sqrt((y.astype(np.float64) ** 2).mean(axis=1, keepdims=True))
+    err = np.abs(y[:, cols] - ref) / np.maximum(np.abs(ref), rms)
+    assert err.max() <= GEMM_RTOL, err.max()

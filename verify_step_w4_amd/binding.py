@@ -1,0 +1,242 @@
+"""ctypes binding of libvw4.so (the C ABI declared in include/vw4.h).
+
+Argument marshalling only: every step of the verify path runs in the HIP
+kernels of libvw4.so.  torch is used for device memory and streams: tensors
+are passed as raw device pointers and the current torch stream is passed as
+the hipStream_t.  Loading fails loudly when the library has not been built;
+there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libvw4.so")
+
+VW4_OK = 0
+VW4_EINVAL = -1
+VW4_EUNSUPPORTED = -2
+VW4_EHIP = -3
+VW4_EWORKSPACE = -4
+VW4_F32 = 0
+VW4_BF16 = 1
+FLAG_NONFINITE = 1
+FLAG_TOPP_TIE = 2
+FLAG_ACCEPT_TIE = 4
+FLAG_CDF_TIE = 8
+FLAG_R_ZERO = 16
+
+# numpy view of struct vw4_rowstat (32 bytes)
+ROWSTAT_DTYPE = np.dtype([("max_logit", "<f4"), ("tau", "<f4"), ("log_z", "<f8"), ("argmax", "<i4"),
+                          ("n_kept", "<i4"), ("flags", "<u4"), ("pad", "<u4")])
+ROWSTAT_BYTES = 32
+assert ROWSTAT_DTYPE.itemsize == ROWSTAT_BYTES
+
+# name -> (restype, argtypes), mirroring include/vw4.h
+_P, _I32, _I64, _U64, _F32, _SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                                   ctypes.c_float, ctypes.c_size_t)
+SIGNATURES = {
+    "vw4_version": (ctypes.c_char_p, []),
+    "vw4_last_error": (ctypes.c_char_p, []),
+    "vw4_w4_quantize_host": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
+    "vw4_w4_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "vw4_w4_packed_bytes": (_SZ, [_I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
+    "vw4_w4_pack": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "vw4_w4_unpack": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "vw4_w4_quantize_packed": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "vw4_gemm_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "w4_skinny_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+    "vw4_workspace_bytes": (_SZ, [_I32, _I32]),
+    "verify_logits": (ctypes.c_int, [_P, _I64, _P, _P, _I32, _I32, _I32, _F32, _F32, _P, _P, _P, _SZ, _P]),
+    "vw4_accept_workspace_bytes": (_SZ, [_I32, _I32]),
+    "spec_accept": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P, _I32, _I32, _I32, _F32, _U64, _U64, _P, _P,
+                                   _P, _P, _SZ, _P]),
+}
+
+
+class VW4Error(RuntimeError):
+    def __init__(self, name: str, rc: int, msg: str):
+        super().__init__(f"{name} failed with {rc}: {msg}")
+        self.rc = rc
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libvw4.so; raises if it is missing (build it with build.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                               "(python -m verify_step_w4_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().vw4_last_error().decode()
+
+
+def version() -> str:
+    return lib().vw4_version().decode()
+
+
+def _check(name: str, rc: int):
+    if rc != VW4_OK:
+        raise VW4Error(name, rc, last_error())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev_tensor(t, name):
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+# ---------------------------------------------------------------------------
+# W4 weight format
+# ---------------------------------------------------------------------------
+def w4_quantize_host(w: np.ndarray):
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    codes = np.zeros((N, K // 2), dtype=np.uint8)
+    scales = np.zeros((N, K // 64), dtype=np.uint16)
+    _check("vw4_w4_quantize_host", lib().vw4_w4_quantize_host(
+        w.ctypes.data_as(_P), N, K, codes.ctypes.data_as(_P), scales.ctypes.data_as(_P)))
+    return codes, scales
+
+
+def packed_sizes(N: int, K: int):
+    sb = ctypes.c_size_t(0)
+    cb = lib().vw4_w4_packed_bytes(N, K, ctypes.byref(sb))
+    if cb == 0:
+        raise VW4Error("vw4_w4_packed_bytes", VW4_EINVAL, f"invalid shape N={N} K={K}")
+    return int(cb), int(sb.value)
+
+
+def w4_quantize(w, stream=None):
+    """Device fp32 [N][K] -> device canonical (codes u8 [N][K/2], scales i16-bits [N][K/64])."""
+    import torch
+    _dev_tensor(w, "w")
+    N, K = w.shape
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, K // 64), dtype=torch.int16, device=w.device)
+    _check("vw4_w4_quantize", lib().vw4_w4_quantize(_ptr(w), N, K, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def w4_pack(codes, scales, N: int, K: int, stream=None):
+    import torch
+    cb, sb = packed_sizes(N, K)
+    packed = torch.empty(cb, dtype=torch.uint8, device=codes.device)
+    pscales = torch.empty(sb // 2, dtype=torch.int16, device=codes.device)
+    _check("vw4_w4_pack", lib().vw4_w4_pack(_ptr(codes), _ptr(scales), N, K, _ptr(packed), _ptr(pscales),
+                                            _stream(stream)))
+    return packed, pscales
+
+
+def w4_unpack(packed, pscales, N: int, K: int, stream=None):
+    import torch
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=packed.device)
+    scales = torch.empty((N, K // 64), dtype=torch.int16, device=packed.device)
+    _check("vw4_w4_unpack", lib().vw4_w4_unpack(_ptr(packed), _ptr(pscales), N, K, _ptr(codes), _ptr(scales),
+                                                _stream(stream)))
+    return codes, scales
+
+
+def w4_quantize_packed(w, stream=None, out=None):
+    import torch
+    _dev_tensor(w, "w")
+    N, K = w.shape
+    cb, sb = packed_sizes(N, K)
+    if out is None:
+        packed = torch.empty(cb, dtype=torch.uint8, device=w.device)
+        pscales = torch.empty(sb // 2, dtype=torch.int16, device=w.device)
+    else:
+        packed, pscales = out
+    _check("vw4_w4_quantize_packed", lib().vw4_w4_quantize_packed(_ptr(w), N, K, _ptr(packed), _ptr(pscales),
+                                                                  _stream(stream)))
+    return packed, pscales
+
+
+# ---------------------------------------------------------------------------
+# workspaces (zero-filled once; the library leaves its counters at zero)
+# ---------------------------------------------------------------------------
+def workspace(nbytes: int, device="cuda"):
+    import torch
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().vw4_gemm_workspace_bytes(M, N, K))
+
+
+def verify_workspace_bytes(rows: int, V: int, d: int | None = None) -> int:
+    n = int(lib().vw4_workspace_bytes(rows, V))
+    if d is not None:
+        n += gemm_workspace_bytes(rows, V, d)
+    return n
+
+
+def accept_workspace_bytes(B: int, V: int) -> int:
+    return int(lib().vw4_accept_workspace_bytes(B, V))
+
+
+# ---------------------------------------------------------------------------
+# the three calls of the verify step
+# ---------------------------------------------------------------------------
+def w4_skinny_gemm(x, w_packed, scales_packed, y, M: int, N: int, K: int, ws=None, stream=None,
+                   ldx: int | None = None, ldy: int | None = None):
+    """y[M][N] (fp32 or bf16 tensor) = x[M][K] (bf16 bits as int16/bfloat16) @ W4^T."""
+    import torch
+    ydt = VW4_F32 if y.dtype == torch.float32 else VW4_BF16
+    ldx = x.stride(0) if ldx is None else ldx
+    ldy = y.stride(0) if ldy is None else ldy
+    nbytes = ws.numel() if ws is not None else 0
+    _check("w4_skinny_gemm", lib().w4_skinny_gemm(_ptr(x), ldx, _ptr(w_packed), _ptr(scales_packed), _ptr(y), ldy,
+                                                  ydt, M, N, K, _ptr(ws), nbytes, _stream(stream)))
+    return y
+
+
+def verify_logits(hidden, lm_packed, lm_scales, rows: int, V: int, d: int, temperature: float, top_p: float,
+                  logits, stats, ws, stream=None, ldh: int | None = None):
+    """stats: uint8 device tensor of rows * 32 bytes (struct vw4_rowstat)."""
+    if hidden is not None:
+        ldh = hidden.stride(0) if ldh is None else ldh
+    _check("verify_logits", lib().verify_logits(_ptr(hidden), ldh or 0, _ptr(lm_packed), _ptr(lm_scales), rows, V,
+                                                d, float(temperature), float(top_p), _ptr(logits), _ptr(stats),
+                                                _ptr(ws), ws.numel(), _stream(stream)))
+    return logits, stats
+
+
+def spec_accept(logits, logits_bstride: int, stats, stats_bstride: int, q, q_bstride: int, draft, B: int, D: int,
+                V: int, temperature: float, seed: int, step0: int, out_tokens, out_n_acc, out_flags, ws,
+                stream=None):
+    _check("spec_accept", lib().spec_accept(_ptr(logits), logits_bstride, _ptr(stats), stats_bstride, _ptr(q),
+                                            q_bstride, _ptr(draft), B, D, V, float(temperature), int(seed),
+                                            int(step0), _ptr(out_tokens), _ptr(out_n_acc), _ptr(out_flags),
+                                            _ptr(ws), ws.numel(), _stream(stream)))
+    return out_tokens, out_n_acc, out_flags
+
+
+def rowstats_to_numpy(stats_tensor) -> np.ndarray:
+    return stats_tensor.detach().cpu().numpy().view(ROWSTAT_DTYPE)

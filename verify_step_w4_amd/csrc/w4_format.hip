@@ -1,0 +1,305 @@
+// w4_format.hip — the W4 weight format: quantiser (host and device), packing
+// into the kernel layout and back, plus the library's error plumbing.
+//
+// Format (hazakura.dev, "mtplx——M5 Maxで63tok/s…", section "4層のアーキテクチャ",
+// Layer 0 names a 4-bit LM head; the group size, symmetry and fp16 scale are
+// the workload's): per row n and 64-element group g along K,
+//     scale = fp16_rne(absmax / 7)          (binary32 division, then RNE to fp16)
+//     c_k   = clamp(rint(w_k / scale), -7, 7)  with the *rounded* scale, half-even
+//     an all-zero (or fp16-underflowing) group gets scale 0 and codes 0.
+//
+// Packed layout (what w4_skinny_gemm streams).  Rows are padded to a multiple
+// of 64 and grouped in tiles of 64 rows; tile t, group g, half c (k/32 within
+// the group) and row l of the tile own 16 bytes at
+//     ((t * G + g) * 2 + c) * 1024 + l * 16,
+// so one wavefront (lane = row) reads 1 KiB of contiguous memory per load.
+// Within those 16 bytes, dword d covers k = 64g + 32c + 8d + j (j = 0..7) with
+// code nibble u = c + 8 at bit 4*(j/2) for even j and bit 16 + 4*(j/2) for
+// odd j: ((word >> 4i) & 0x000F000F) is the pair (k0 + 2i, k0 + 2i + 1), one
+// per 16-bit half, matching a dword of consecutive bf16 activations.
+// Scales: f16 [t][g][64].
+#include <math.h>
+#include <stdarg.h>
+
+#include "common.h"
+
+namespace vw4 {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+}
+
+int check_launch(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        set_error("%s: launch failed: %s", what, hipGetErrorString(e));
+        return VW4_EHIP;
+    }
+    return VW4_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Quantiser arithmetic, one group of 64.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int quant_code(float w, float sf) {
+    if (sf == 0.0f) return 0;
+    float r = rintf(w / sf);  // correctly rounded binary32 division, half-even rint
+    r = fminf(fmaxf(r, -7.0f), 7.0f);
+    return (int)r;
+}
+
+// One wavefront per (row, group): lane k holds w[n][64g + k].
+// Returns the code of this lane; *scale_bits receives the group's fp16 scale.
+__device__ __forceinline__ int quant_group_wave(float w, uint16_t* scale_bits) {
+    float a = fabsf(w);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    const float s32 = a / 7.0f;
+    const uint16_t s16 = f32_to_f16_bits(s32);
+    const float sf = f16_bits_to_f32(s16);
+    *scale_bits = s16;
+    return quant_code(w, sf);
+}
+
+// Packed-layout position of nibble j (0..7) inside its dword.
+__host__ __device__ __forceinline__ int packed_nibble_shift(int j) {
+    return (j & 1) ? 16 + 4 * (j >> 1) : 4 * (j >> 1);
+}
+
+__global__ __launch_bounds__(256) void quantize_canonical_kernel(const float* __restrict__ w, int64_t N,
+                                                                 int64_t K, uint8_t* __restrict__ codes,
+                                                                 uint16_t* __restrict__ scales) {
+    const int64_t G = K / 64;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (n, g) index
+    const int lane = threadIdx.x & 63;
+    if (wid >= N * G) return;
+    const int64_t n = wid / G, g = wid % G;
+    const float v = w[n * K + g * 64 + lane];
+    uint16_t sb;
+    const int c = quant_group_wave(v, &sb);
+    const uint32_t u = (uint32_t)(c + 8);
+    const uint32_t hi = __shfl_down(u, 1, 64);
+    if ((lane & 1) == 0) codes[n * (K / 2) + g * 32 + (lane >> 1)] = (uint8_t)(u | (hi << 4));
+    if (lane == 0) scales[n * G + g] = sb;
+}
+
+__global__ __launch_bounds__(256) void quantize_packed_kernel(const float* __restrict__ w, int64_t N, int64_t K,
+                                                              int64_t Npad, uint32_t* __restrict__ packed,
+                                                              uint16_t* __restrict__ pscales) {
+    const int64_t G = K / 64;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (wid >= Npad * G) return;
+    const int64_t n = wid / G, g = wid % G;
+    int c = 0;
+    uint16_t sb = 0;
+    if (n < N) {
+        const float v = w[n * K + g * 64 + lane];
+        c = quant_group_wave(v, &sb);
+    }
+    // gather the 8 codes of this lane's dword into lane (lane & ~7)
+    const uint32_t u = (uint32_t)(c + 8) << packed_nibble_shift(lane & 7);
+    uint32_t word = u;
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) word |= __shfl_xor(word, off, 64);
+    const int64_t t = n >> 6, l = n & 63;
+    if ((lane & 7) == 0) {
+        const int half = lane >> 5, d = (lane >> 3) & 3;
+        const int64_t off = (((t * G + g) * 2 + half) * 1024 + l * 16) / 4 + d;
+        packed[off] = word;
+    }
+    if (lane == 0) pscales[(t * G + g) * 64 + l] = sb;
+}
+
+// One thread per (padded row, group): canonical 32 bytes + scale -> packed.
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ codes,
+                                                   const uint16_t* __restrict__ scales, int64_t N, int64_t K,
+                                                   int64_t Npad, uint32_t* __restrict__ packed,
+                                                   uint16_t* __restrict__ pscales) {
+    const int64_t G = K / 64;
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= Npad * G) return;
+    const int64_t n = id / G, g = id % G, t = n >> 6, l = n & 63;
+    const uint8_t* src = codes + n * (K / 2) + g * 32;
+    for (int half = 0; half < 2; ++half) {
+        for (int d = 0; d < 4; ++d) {
+            uint32_t word = 0;
+            for (int j = 0; j < 8; ++j) {
+                const int k = half * 32 + d * 8 + j;  // k within the group
+                uint32_t u = 8;
+                if (n < N) {
+                    const uint8_t b = src[k >> 1];
+                    u = (k & 1) ? (b >> 4) : (b & 15u);
+                }
+                word |= u << packed_nibble_shift(j);
+            }
+            packed[(((t * G + g) * 2 + half) * 1024 + l * 16) / 4 + d] = word;
+        }
+    }
+    pscales[(t * G + g) * 64 + l] = (n < N) ? scales[n * G + g] : (uint16_t)0;
+}
+
+__global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict__ packed,
+                                                     const uint16_t* __restrict__ pscales, int64_t N, int64_t K,
+                                                     uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+    const int64_t G = K / 64;
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= N * G) return;
+    const int64_t n = id / G, g = id % G, t = n >> 6, l = n & 63;
+    uint8_t* dst = codes + n * (K / 2) + g * 32;
+    for (int half = 0; half < 2; ++half) {
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t word = packed[(((t * G + g) * 2 + half) * 1024 + l * 16) / 4 + d];
+            for (int jp = 0; jp < 4; ++jp) {
+                const uint32_t lo = (word >> packed_nibble_shift(2 * jp)) & 15u;
+                const uint32_t hi = (word >> packed_nibble_shift(2 * jp + 1)) & 15u;
+                dst[half * 16 + d * 4 + jp] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
+    scales[n * G + g] = pscales[(t * G + g) * 64 + l];
+}
+
+static int check_shape(int64_t N, int64_t K) {
+    VW4_REQUIRE(N >= 1 && N <= (int64_t)1 << 31, VW4_EINVAL, "N=%lld out of range", (long long)N);
+    VW4_REQUIRE(K >= 64 && K % 64 == 0 && K <= 65536, VW4_EINVAL, "K=%lld must be a multiple of 64 in [64, 65536]",
+                (long long)K);
+    return VW4_OK;
+}
+
+static int64_t pad64(int64_t N) { return (N + 63) / 64 * 64; }
+
+// Host binary32 -> binary16 (round to nearest even) from the bit layout.
+static uint16_t host_f32_to_f16(float f) {
+    uint32_t x;
+    memcpy(&x, &f, 4);
+    const uint32_t sign = (x >> 16) & 0x8000u;
+    const uint32_t ax = x & 0x7fffffffu;
+    if (ax > 0x7f800000u) return (uint16_t)(sign | 0x7e00u);
+    if (ax >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u);  // >= 65520 rounds to inf
+    if (ax < 0x38800000u) {                                     // below 2^-14: subnormal result
+        if (ax < 0x33000000u) return (uint16_t)sign;            // below 2^-25: rounds to 0
+        const uint32_t e = ax >> 23;                            // 102..112
+        const uint32_t m = (ax & 0x7fffffu) | 0x800000u;
+        const uint32_t shift = 126u - e;                        // 14..24
+        uint32_t r = m >> shift;
+        const uint32_t rem = m & ((1u << shift) - 1u), halfway = 1u << (shift - 1u);
+        if (rem > halfway || (rem == halfway && (r & 1u))) ++r;
+        return (uint16_t)(sign | r);
+    }
+    uint32_t r = (ax - 0x38000000u) >> 13;                       // rebias 127 -> 15
+    const uint32_t rem = ax & 0x1fffu;
+    if (rem > 0x1000u || (rem == 0x1000u && (r & 1u))) ++r;
+    return (uint16_t)(sign | r);
+}
+
+static float host_f16_to_f32(uint16_t h) {
+    const uint32_t s = (uint32_t)(h & 0x8000u) << 16, e = (h >> 10) & 31u, m = h & 1023u;
+    float v;
+    if (e == 0) v = ldexpf((float)m, -24);
+    else if (e == 31) v = m ? NAN : INFINITY;
+    else v = ldexpf((float)(1024u + m), (int)e - 25);
+    uint32_t b;
+    memcpy(&b, &v, 4);
+    b |= s;
+    memcpy(&v, &b, 4);
+    return v;
+}
+
+}  // namespace vw4
+
+using namespace vw4;
+
+extern "C" {
+
+const char* vw4_version(void) { return "vw4 0.1.0 (gfx950)"; }
+
+const char* vw4_last_error(void) { return g_err; }
+
+int vw4_w4_quantize_host(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales) {
+    int rc = check_shape(N, K);
+    if (rc) return rc;
+    VW4_REQUIRE(w && codes && scales, VW4_EINVAL, "null pointer");
+    const int64_t G = K / 64;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < G; ++g) {
+            const float* wg = w + n * K + g * 64;
+            float a = 0.0f;
+            for (int k = 0; k < 64; ++k) a = fmaxf(a, fabsf(wg[k]));
+            const uint16_t s16 = host_f32_to_f16(a / 7.0f);
+            const float sf = host_f16_to_f32(s16);
+            scales[n * G + g] = s16;
+            uint8_t* dst = codes + n * (K / 2) + g * 32;
+            for (int k = 0; k < 64; k += 2) {
+                int c0 = 0, c1 = 0;
+                if (sf != 0.0f) {
+                    c0 = (int)fminf(fmaxf(rintf(wg[k] / sf), -7.0f), 7.0f);
+                    c1 = (int)fminf(fmaxf(rintf(wg[k + 1] / sf), -7.0f), 7.0f);
+                }
+                dst[k >> 1] = (uint8_t)((c0 + 8) | ((c1 + 8) << 4));
+            }
+        }
+    }
+    return VW4_OK;
+}
+
+int vw4_w4_quantize(const float* w_dev, int64_t N, int64_t K, uint8_t* codes_dev, uint16_t* scales_dev,
+                    void* stream) {
+    int rc = check_shape(N, K);
+    if (rc) return rc;
+    VW4_REQUIRE(w_dev && codes_dev && scales_dev, VW4_EINVAL, "null pointer");
+    const int64_t waves = N * (K / 64);
+    hipLaunchKernelGGL(quantize_canonical_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                       (hipStream_t)stream, w_dev, N, K, codes_dev, scales_dev);
+    return check_launch("vw4_w4_quantize");
+}
+
+size_t vw4_w4_packed_bytes(int64_t N, int64_t K, size_t* scale_bytes) {
+    if (check_shape(N, K)) return 0;
+    const int64_t Np = pad64(N);
+    if (scale_bytes) *scale_bytes = (size_t)(Np * (K / 64) * 2);
+    return (size_t)(Np * (K / 2));
+}
+
+int vw4_w4_pack(const uint8_t* codes_dev, const uint16_t* scales_dev, int64_t N, int64_t K, uint8_t* packed_dev,
+                uint16_t* packed_scales_dev, void* stream) {
+    int rc = check_shape(N, K);
+    if (rc) return rc;
+    VW4_REQUIRE(codes_dev && scales_dev && packed_dev && packed_scales_dev, VW4_EINVAL, "null pointer");
+    VW4_REQUIRE(aligned(packed_dev, 16), VW4_EINVAL, "packed codes must be 16-byte aligned");
+    const int64_t Np = pad64(N), total = Np * (K / 64);
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                       codes_dev, scales_dev, N, K, Np, (uint32_t*)packed_dev, packed_scales_dev);
+    return check_launch("vw4_w4_pack");
+}
+
+int vw4_w4_unpack(const uint8_t* packed_dev, const uint16_t* packed_scales_dev, int64_t N, int64_t K,
+                  uint8_t* codes_dev, uint16_t* scales_dev, void* stream) {
+    int rc = check_shape(N, K);
+    if (rc) return rc;
+    VW4_REQUIRE(codes_dev && scales_dev && packed_dev && packed_scales_dev, VW4_EINVAL, "null pointer");
+    VW4_REQUIRE(aligned(packed_dev, 16), VW4_EINVAL, "packed codes must be 16-byte aligned");
+    const int64_t total = N * (K / 64);
+    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                       (const uint32_t*)packed_dev, packed_scales_dev, N, K, codes_dev, scales_dev);
+    return check_launch("vw4_w4_unpack");
+}
+
+int vw4_w4_quantize_packed(const float* w_dev, int64_t N, int64_t K, uint8_t* packed_dev,
+                           uint16_t* packed_scales_dev, void* stream) {
+    int rc = check_shape(N, K);
+    if (rc) return rc;
+    VW4_REQUIRE(w_dev && packed_dev && packed_scales_dev, VW4_EINVAL, "null pointer");
+    VW4_REQUIRE(aligned(packed_dev, 16), VW4_EINVAL, "packed codes must be 16-byte aligned");
+    const int64_t Np = pad64(N), waves = Np * (K / 64);
+    hipLaunchKernelGGL(quantize_packed_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                       (hipStream_t)stream, w_dev, N, K, Np, (uint32_t*)packed_dev, packed_scales_dev);
+    return check_launch("vw4_w4_quantize_packed");
+}
+
+}  // extern "C"

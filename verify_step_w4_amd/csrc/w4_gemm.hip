@@ -1,0 +1,327 @@
+// w4_gemm.hip — W4 skinny GEMM for the verify rows (M = 1..8).
+//
+// hazakura.dev, "mtplx——M5 Maxで63tok/s…", section "4層のアーキテクチャ", Layer 0:
+// the verify pass is a matmul with a handful of rows (M = 3..6) that needed its
+// own shader; gist.science, "BaseRT: …", section "メソドロジー": decode GEMVs
+// dequantise inside the inner loop so weights are never materialised.
+//
+// y[m][n] = sum_g scale[n][g] * sum_{k in g} x[m][k] * c[n][k]
+//
+// MI355X design (bandwidth-bound: each weight byte is used M times at most):
+//  * lane = output row.  A wavefront owns a tile of 64 rows and a slice of the
+//    K groups; each lane streams its row's codes with 16-byte loads, and the
+//    packed layout makes every wavefront load 1 KiB of contiguous HBM.
+//  * The activations x are identical for all 64 lanes, so they are read with
+//    scalar loads into SGPRs and feed v_dot2_f32_bf16 directly: no LDS traffic
+//    and no cross-lane reduction in the inner loop.
+//  * Dequantisation in registers: ((word >> 4i) & 0x000F000F) | 0x43004300 is a
+//    pair of bf16 values 128 + u = 136 + c.  The constant 136 is removed once
+//    per group by starting the group's accumulator at -136 * sum_{k in g} x[m][k]
+//    (computed per workgroup in fp64 and rounded once), so the inner loop is
+//    one AND-OR (plus a shift) per pair and M dot2 per pair.
+//  * Split K: S_wg wavefronts of a workgroup take consecutive K slices of the
+//    same tile and are reduced through LDS; S_grid workgroups per tile write
+//    fp32 partials to the workspace and the last one to arrive (integer atomic
+//    counter) sums them in slice order.  The summation order depends only on
+//    (N, K), never on M or on timing, so results are bitwise reproducible and
+//    row m of an M-row call equals the one-row call.
+#include <stdlib.h>
+
+#include "common.h"
+
+namespace vw4 {
+
+constexpr int GEMM_MAX_M = 8;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Constant address space: uniform loads through it become scalar (SGPR) loads.
+typedef const __attribute__((address_space(4))) uint32_t cu32;
+constexpr float GEMM_OFFSET = 136.0f;  // bf16 magic 128 plus the code bias 8
+
+// Marks an address as wavefront-uniform so that loads through it are scalar.
+__device__ __forceinline__ cu32* uniform_ptr(cu32* p) {
+    const uint64_t a = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return (cu32*)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
+                                           false);
+}
+
+// (v & mask) | magic in one VOP3 instruction.  gfx9 VOP3 encodings take no
+// literal constants and at most one SGPR, so the mask comes in an SGPR and
+// the magic in a VGPR; the compiler would otherwise emit a v_and/v_or pair.
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask_s, uint32_t magic_v) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask_s), "v"(magic_v));
+    return r;
+}
+
+template <int M>
+__device__ __forceinline__ void gemm_dword(uint32_t word, cu32* const* xg, int xoff, uint32_t kmask,
+                                           uint32_t kmagic, float (&ag)[M]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t pair = and_or(word >> (4 * i), kmask, kmagic);
+#pragma unroll
+        for (int m = 0; m < M; ++m) ag[m] = dot2_bf16(pair, xg[m][xoff + i], ag[m]);
+    }
+}
+
+template <int M>
+__global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                      const u32x4* __restrict__ wpk,
+                                                      const uint16_t* __restrict__ spk, void* __restrict__ y,
+                                                      int64_t ldy, int ydt, int N, int G, int S_wg, int S_grid,
+                                                      float* __restrict__ part, uint32_t* __restrict__ cnt,
+                                                      int64_t Npad, uint32_t kmask, uint32_t kmagic) {
+    extern __shared__ float lds[];
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int t = blockIdx.x;
+    const int S = S_wg * S_grid;
+    const int sw0 = blockIdx.y * S_wg;
+    const int gw0 = (int)((int64_t)sw0 * G / S);
+    const int gw1 = (int)((int64_t)(sw0 + S_wg) * G / S);
+    const int ng = gw1 - gw0;
+    float* xs = lds;                     // [M][ng]: -136 * sum of the group's x
+    float* red = lds + M * ng;           // [S_wg][M][64]
+
+    // Prologue: group sums of x for every group this workgroup touches.
+    for (int i = tid; i < M * ng; i += blockDim.x) {
+        const int m = i / ng, gg = i - m * ng;
+        const uint4* xr = (const uint4*)(x + m * ldx + (int64_t)(gw0 + gg) * 64);
+        double s = 0.0;
+#pragma unroll 1
+        for (int v = 0; v < 8; ++v) {
+            const uint4 q = xr[v];
+            const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                s += (double)bf16_to_f32((uint16_t)(w4[e] & 0xffffu));
+                s += (double)bf16_to_f32((uint16_t)(w4[e] >> 16));
+            }
+        }
+        xs[m * ng + gg] = (float)(-(double)GEMM_OFFSET * s);
+    }
+    __syncthreads();
+
+    const int s_idx = sw0 + wv;
+    const int g0 = (int)((int64_t)s_idx * G / S);
+    const int g1 = (int)((int64_t)(s_idx + 1) * G / S);
+
+    // Activation rows of the current group, advanced by one group (32 dwords)
+    // per iteration; kept wavefront-uniform so every x load is an s_load.
+    cu32* xp[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) xp[m] = uniform_ptr((cu32*)(x + m * ldx) + g0 * 32);
+    const uint32_t magic_v = kmagic;  // lives in a VGPR for and_or()
+
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+
+    const u32x4* wp = wpk + ((int64_t)t * G + g0) * 128 + lane;
+    const uint16_t* sp = spk + ((int64_t)t * G + g0) * 64 + lane;
+    if (g0 < g1) {
+        u32x4 c0 = __builtin_nontemporal_load(wp);
+        u32x4 c1 = __builtin_nontemporal_load(wp + 64);
+        uint16_t sr = sp[0];
+        for (int g = g0; g < g1; ++g) {
+            u32x4 n0 = c0, n1 = c1;
+            uint16_t nsr = sr;
+            if (g + 1 < g1) {
+                n0 = __builtin_nontemporal_load(wp + 128);
+                n1 = __builtin_nontemporal_load(wp + 192);
+                nsr = sp[64];
+            }
+            float ag[M];
+#pragma unroll
+            for (int m = 0; m < M; ++m) ag[m] = xs[m * ng + (g - gw0)];
+            gemm_dword<M>(c0.x, xp, 0, kmask, magic_v, ag);
+            gemm_dword<M>(c0.y, xp, 4, kmask, magic_v, ag);
+            gemm_dword<M>(c0.z, xp, 8, kmask, magic_v, ag);
+            gemm_dword<M>(c0.w, xp, 12, kmask, magic_v, ag);
+            gemm_dword<M>(c1.x, xp, 16, kmask, magic_v, ag);
+            gemm_dword<M>(c1.y, xp, 20, kmask, magic_v, ag);
+            gemm_dword<M>(c1.z, xp, 24, kmask, magic_v, ag);
+            gemm_dword<M>(c1.w, xp, 28, kmask, magic_v, ag);
+#pragma unroll
+            for (int m = 0; m < M; ++m) xp[m] += 32;
+            const float sc = f16_bits_to_f32(sr);
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[m] = fmaf(sc, ag[m], acc[m]);
+            c0 = n0;
+            c1 = n1;
+            sr = nsr;
+            wp += 128;
+            sp += 64;
+        }
+    }
+
+    // Reduce the S_wg slices of this workgroup in slice order.
+    float v[M];
+    if (S_wg > 1) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) red[(wv * M + m) * 64 + lane] = acc[m];
+        __syncthreads();
+        if (wv == 0) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                float s = red[m * 64 + lane];
+                for (int w = 1; w < S_wg; ++w) s += red[(w * M + m) * 64 + lane];
+                v[m] = s;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < M; ++m) v[m] = acc[m];
+    }
+
+    const int n = t * 64 + lane;
+    if (S_grid == 1) {
+        if (wv == 0 && n < N) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                if (ydt == VW4_F32) ((float*)y)[m * ldy + n] = v[m];
+                else ((uint16_t*)y)[m * ldy + n] = f32_to_bf16(v[m]);
+            }
+        }
+        return;
+    }
+
+    // Cross-workgroup split: partials, then the last workgroup of the tile sums them.
+    __shared__ int s_last;
+    if (wv == 0) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) part[((int64_t)blockIdx.y * M + m) * Npad + n] = v[m];
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t prev = atomicAdd(&cnt[t], 1u);
+        s_last = (prev == (uint32_t)(S_grid - 1));
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    if (wv == 0) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float s = 0.0f;
+            for (int b = 0; b < S_grid; ++b) s += part[((int64_t)b * M + m) * Npad + n];
+            if (n < N) {
+                if (ydt == VW4_F32) ((float*)y)[m * ldy + n] = s;
+                else ((uint16_t*)y)[m * ldy + n] = f32_to_bf16(s);
+            }
+        }
+        if (lane == 0) cnt[t] = 0u;  // leave the counter clear for the next call
+    }
+}
+
+struct GemmPlan {
+    int ntiles, G, S_wg, S_grid;
+    int64_t Npad;
+    size_t ws_bytes;
+    size_t lds_bytes;
+};
+
+// Split of K over wavefronts: enough wavefronts to cover the 256 CUs several
+// times, at least two groups per wavefront.  Depends on (N, K) only.
+static GemmPlan plan_gemm(int M, int N, int K) {
+    GemmPlan p;
+    p.G = K / 64;
+    p.ntiles = (N + 63) / 64;
+    p.Npad = (int64_t)p.ntiles * 64;
+    const int target_waves = 2048;
+    int S = (target_waves + p.ntiles - 1) / p.ntiles;
+    int maxS = p.G / 2 > 0 ? p.G / 2 : 1;
+    if (S > maxS) S = maxS;
+    if (S < 1) S = 1;
+    p.S_wg = S < 4 ? S : 4;
+    p.S_grid = (S + p.S_wg - 1) / p.S_wg;
+    if (const char* e = getenv("VW4_GEMM_SPLIT")) {
+        int a = 0, b = 0;
+        if (sscanf(e, "%d,%d", &a, &b) == 2 && a >= 1 && a <= 4 && b >= 1 && a * b <= p.G) {
+            p.S_wg = a;
+            p.S_grid = b;
+        }
+    }
+    const int S_all = p.S_wg * p.S_grid;
+    const int ng_max = (int)(((int64_t)p.S_wg * p.G + S_all - 1) / S_all) + 1;
+    p.lds_bytes = (size_t)M * ng_max * 4 + (p.S_wg > 1 ? (size_t)p.S_wg * M * 64 * 4 : 0);
+    p.ws_bytes = 0;
+    if (p.S_grid > 1) {
+        size_t part = (size_t)p.S_grid * M * p.Npad * 4;
+        part = (part + 255) / 256 * 256;
+        p.ws_bytes = part + (size_t)p.ntiles * 4;
+    }
+    return p;
+}
+
+template <int M>
+static void launch_gemm(const GemmPlan& p, const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* s,
+                        void* y, int64_t ldy, int ydt, int N, float* part, uint32_t* cnt, hipStream_t st) {
+    hipLaunchKernelGGL(w4_gemm_kernel<M>, dim3(p.ntiles, p.S_grid), dim3(64 * p.S_wg), p.lds_bytes, st, x, ldx,
+                       (const u32x4*)w, s, y, ldy, ydt, N, p.G, p.S_wg, p.S_grid, part, cnt, p.Npad, 0x000F000Fu,
+                       0x43004300u);
+}
+
+int gemm_dispatch(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* s, void* y, int64_t ldy,
+                  int ydt, int M, int N, int K, void* ws, size_t ws_bytes, hipStream_t st) {
+    VW4_REQUIRE(M >= 1 && M <= GEMM_MAX_M, VW4_EINVAL, "w4_skinny_gemm: M=%d must be in [1, 8]", M);
+    VW4_REQUIRE(N >= 1, VW4_EINVAL, "w4_skinny_gemm: N=%d must be >= 1", N);
+    VW4_REQUIRE(K >= 64 && K % 64 == 0 && K <= 65536, VW4_EINVAL,
+                "w4_skinny_gemm: K=%d must be a multiple of 64 in [64, 65536]", K);
+    VW4_REQUIRE(x && w && s && y, VW4_EINVAL, "w4_skinny_gemm: null pointer");
+    VW4_REQUIRE(ldx >= K && ldx % 8 == 0 && aligned(x, 16), VW4_EINVAL,
+                "w4_skinny_gemm: x needs ldx >= K, ldx %% 8 == 0 and 16-byte alignment");
+    VW4_REQUIRE(aligned(w, 16) && aligned(s, 2), VW4_EINVAL, "w4_skinny_gemm: packed weights must be 16-byte aligned");
+    VW4_REQUIRE(ldy >= N, VW4_EINVAL, "w4_skinny_gemm: ldy=%lld < N=%d", (long long)ldy, N);
+    VW4_REQUIRE(ydt == VW4_F32 || ydt == VW4_BF16, VW4_EINVAL, "w4_skinny_gemm: y_dtype must be VW4_F32 or VW4_BF16");
+    VW4_REQUIRE(aligned(y, ydt == VW4_F32 ? 4 : 2), VW4_EINVAL, "w4_skinny_gemm: y misaligned");
+    const GemmPlan p = plan_gemm(M, N, K);
+    float* part = nullptr;
+    uint32_t* cnt = nullptr;
+    if (p.ws_bytes) {
+        VW4_REQUIRE(ws && ws_bytes >= p.ws_bytes && aligned(ws, 256), VW4_EWORKSPACE,
+                    "w4_skinny_gemm: needs a 256-byte aligned workspace of %zu bytes", p.ws_bytes);
+        part = (float*)ws;
+        cnt = (uint32_t*)((char*)ws + (p.ws_bytes - (size_t)p.ntiles * 4));
+    }
+    switch (M) {
+        case 1: launch_gemm<1>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
+        case 2: launch_gemm<2>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
+        case 3: launch_gemm<3>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
+        case 4: launch_gemm<4>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
+        case 5: launch_gemm<5>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
+        case 6: launch_gemm<6>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
+        case 7: launch_gemm<7>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
+        default: launch_gemm<8>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
+    }
+    return check_launch("w4_skinny_gemm");
+}
+
+size_t gemm_ws_bytes(int M, int N, int K) {
+    if (M < 1 || M > GEMM_MAX_M || N < 1 || K < 64 || K % 64) return 0;
+    return plan_gemm(M, N, K).ws_bytes;
+}
+
+}  // namespace vw4
+
+extern "C" {
+
+size_t vw4_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) { return vw4::gemm_ws_bytes(M, N, K); }
+
+int w4_skinny_gemm(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, const uint16_t* scales_packed, void* y,
+                   int64_t ldy, int32_t y_dtype, int32_t M, int32_t N, int32_t K, void* ws, size_t ws_bytes,
+                   void* stream) {
+    return vw4::gemm_dispatch(x, ldx, w_packed, scales_packed, y, ldy, y_dtype, M, N, K, ws, ws_bytes,
+                              (hipStream_t)stream);
+}
+
+}  // extern "C"
