@@ -16,12 +16,14 @@
 // p_i(j) = exp((z_ij - m_i)/T - log_z_i) on the kept set (z_ij >= tau_i), 0
 // elsewhere; T == 0 makes p_i one-hot at the argmax.
 //
-// MI355X design: one launch.  Problem b's residual row is split over P
-// workgroups (grid = (B, P)); every workgroup redoes the D accept tests (D <= 7
-// scalar fp64 evaluations) so no extra launch is needed for them, computes
-// fp64 chunk sums of r in a fixed order, and the last workgroup of the problem
-// (integer counter) locates the chunk holding u * R, rescans that chunk with a
-// block-wide fp64 prefix sum in index order, and writes the tokens.
+// MI355X design: problem b's residual row is split over P workgroups
+// (grid = (B, P)); every workgroup redoes the D accept tests (D <= 7 scalar
+// fp64 evaluations) and stores fixed-order fp64 chunk sums of r.  A second
+// launch (one workgroup per problem) locates the chunk holding u * R, rescans
+// it with a block-wide fp64 prefix sum in index order and writes the tokens.
+// Kernel boundaries, not device-wide atomics, separate the phases (an atomic
+// counter costs tens of ns per arriving workgroup on this part).  Vocabularies
+// of at most 1024 entries use one 64-lane workgroup per problem and one launch.
 #include <math.h>
 
 #include "common.h"
@@ -42,7 +44,7 @@ struct AcceptPart {
 
 struct AcceptLayout {
     int P, chunk, threads;
-    size_t off_part, off_cnt, total;
+    size_t off_part, total;
 };
 
 static AcceptLayout accept_layout(int B, int V) {
@@ -63,9 +65,6 @@ static AcceptLayout accept_layout(int B, int V) {
     size_t o = 0;
     L.off_part = o;
     o += (size_t)B * L.P * sizeof(AcceptPart);
-    o = (o + 255) / 256 * 256;
-    L.off_cnt = o;
-    o += (size_t)B * sizeof(uint32_t);
     L.total = (o + 255) / 256 * 256;
     return L;
 }
@@ -149,102 +148,81 @@ __device__ __forceinline__ double blk_prefix_excl(double v, double* sh) {
     return ex + before;
 }
 
-template <int NT>
-__global__ __launch_bounds__(NT) void spec_accept_kernel(const float* __restrict__ logits, int64_t lstride,
-                                                         const vw4_rowstat* __restrict__ stats, int64_t sstride,
-                                                         const float* __restrict__ q, int64_t qstride,
-                                                         const int32_t* __restrict__ draft, int D, int V,
-                                                         float temperature, uint64_t seed, uint64_t step0, int chunk,
-                                                         int P, int32_t* __restrict__ out_tokens,
-                                                         int32_t* __restrict__ out_nacc, uint32_t* __restrict__ out_flags,
-                                                         AcceptPart* __restrict__ parts, uint32_t* __restrict__ cnts) {
-    __shared__ double sh[8];
-    __shared__ int shi[8];
-    __shared__ int s_last, s_y;
-    __shared__ double s_u[2 * (AMAXD + 1)];
-    const int64_t b = blockIdx.x;
-    const int w = blockIdx.y, tid = threadIdx.x;
-    const float* zb = logits + b * lstride;
-    const vw4_rowstat* sb = stats + b * sstride;
-    const float* qb = q ? q + b * qstride : nullptr;
-    const int32_t* db = draft + b * D;
-    const double T = (double)temperature;
+// State every workgroup of a problem derives identically: uniforms, flags
+// from the row statistics, and the first rejection k.
+struct ProblemState {
+    int k;
+    uint32_t flags;
+    bool bad;
+};
 
-    // uniforms of rows 0..D (thread i computes row i)
-    if (tid <= D) {
-        uint64_t c[4] = {step0 + (uint64_t)b, (uint64_t)tid, 0, 0};
+template <int NT>
+__device__ __forceinline__ ProblemState problem_state(const float* __restrict__ zb, const vw4_rowstat* __restrict__ sb,
+                                                      const float* __restrict__ qb, const int32_t* __restrict__ db,
+                                                      int D, int V, double T, uint64_t seed, uint64_t step,
+                                                      double* s_u) {
+    if (threadIdx.x <= D) {
+        uint64_t c[4] = {step, (uint64_t)threadIdx.x, 0, 0};
         philox4x64_10(seed, 0, c);
-        s_u[2 * tid] = unit53(c[0]);
-        s_u[2 * tid + 1] = unit53(c[1]);
+        s_u[2 * threadIdx.x] = unit53(c[0]);
+        s_u[2 * threadIdx.x + 1] = unit53(c[1]);
     }
     __syncthreads();
-
-    uint32_t flags = 0;
-    bool bad = false;
+    ProblemState ps;
+    ps.flags = 0;
+    ps.bad = false;
     for (int i = 0; i <= D; ++i) {
         const uint32_t f = sb[i].flags;
-        if (f & VW4_FLAG_NONFINITE) bad = true;
-        if (f & VW4_FLAG_TOPP_TIE) flags |= VW4_FLAG_TOPP_TIE;
+        if (f & VW4_FLAG_NONFINITE) ps.bad = true;
+        if (f & VW4_FLAG_TOPP_TIE) ps.flags |= VW4_FLAG_TOPP_TIE;
     }
-    if (bad) {
-        if (w == 0 && tid <= D) out_tokens[b * (D + 1) + tid] = -1;
-        if (w == 0 && tid == 0) {
-            out_nacc[b] = -1;
-            out_flags[b] = VW4_FLAG_NONFINITE;
-        }
-        return;
-    }
-    // accept tests (identical in every workgroup and thread)
-    int k = D;
+    ps.k = D;
+    if (ps.bad) return ps;
     for (int i = 0; i < D; ++i) {
         const int x = db[i];
-        if (x < 0 || x >= V) { k = i; break; }  // malformed draft id: rejected, never dereferenced
+        if (x < 0 || x >= V) { ps.k = i; break; }  // malformed draft id: rejected, never dereferenced
         const double pi = p_of(zb + (int64_t)i * V, sb[i], T, x);
         const double qi = (double)qb[(int64_t)i * V + x];
         const double u = s_u[2 * i];
-        if (qi > 0.0 && fabs(u - pi / qi) < 1e-5) flags |= VW4_FLAG_ACCEPT_TIE;
-        if (!(u * qi < pi)) { k = i; break; }
+        if (qi > 0.0 && fabs(u - pi / qi) < 1e-5) ps.flags |= VW4_FLAG_ACCEPT_TIE;
+        if (!(u * qi < pi)) { ps.k = i; break; }
     }
-    const float* zk = zb + (int64_t)k * V;
-    const vw4_rowstat sk = sb[k];
-    const float* qk = (k < D) ? qb + (int64_t)k * V : nullptr;
+    return ps;
+}
 
-    // chunk sums of r and p_k in a fixed order
-    const int c0 = w * chunk, c1 = min(V, c0 + chunk);
+// Chunk w of the residual row of problem b: fixed-order sums of r and p_k.
+template <int NT>
+__device__ __forceinline__ AcceptPart chunk_sums(const float* __restrict__ zk, const vw4_rowstat& sk,
+                                                 const float* __restrict__ qk, double T, int c0, int c1, double* sh,
+                                                 int* shi) {
     double sr = 0.0, sp = 0.0;
     int lr = -1, lp = -1;
-    for (int j = c0 + tid; j < c1; j += NT) {
+    for (int j = c0 + threadIdx.x; j < c1; j += NT) {
         const double pj = p_of(zk, sk, T, j);
-        double rj = pj;
-        if (qk) rj = fmax(0.0, pj - (double)qk[j]);
+        const double rj = qk ? fmax(0.0, pj - (double)qk[j]) : pj;
         sr += rj;
         sp += pj;
         if (rj > 0.0) lr = j;
         if (pj > 0.0) lp = j;
     }
-    sr = blk_sum<NT>(sr, sh);
-    sp = blk_sum<NT>(sp, sh);
-    lr = blk_max_i<NT>(lr, shi);
-    lp = blk_max_i<NT>(lp, shi);
-    AcceptPart* pb = parts + b * P;
-    if (tid == 0) {
-        AcceptPart a;
-        a.r = sr; a.p = sp; a.last_r = lr; a.last_p = lp;
-        pb[w] = a;
-    }
-    if (P > 1) {
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) s_last = (atomicAdd(&cnts[b], 1u) == (uint32_t)(P - 1));
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
-        if (tid == 0) cnts[b] = 0u;
-    } else {
-        __syncthreads();
-    }
+    AcceptPart a;
+    a.r = blk_sum<NT>(sr, sh);
+    a.p = blk_sum<NT>(sp, sh);
+    a.last_r = blk_max_i<NT>(lr, shi);
+    a.last_p = blk_max_i<NT>(lp, shi);
+    return a;
+}
 
-    // ---- last workgroup of problem b: locate u * R and sample ----
+// Locate u * R among the chunk sums, rescan the chunk that holds it and
+// write the outputs of problem b.  pb: the P chunk parts (in LDS or global).
+template <int NT>
+__device__ void finish_problem(const float* __restrict__ zk, const vw4_rowstat& sk, const float* __restrict__ qk,
+                               const int32_t* __restrict__ db, const AcceptPart* pb, int P, int chunk, int D, int V,
+                               double T, const ProblemState& ps, const double* s_u, int32_t* __restrict__ tb,
+                               int32_t* __restrict__ nacc_b, uint32_t* __restrict__ flags_b, double* sh, int* shi) {
+    __shared__ int s_y;
+    const int k = ps.k;
+    uint32_t flags = ps.flags;
     bool use_p = false;
     double R = 0.0;
     for (int c = 0; c < P; ++c) R += pb[c].r;
@@ -265,39 +243,39 @@ __global__ __launch_bounds__(NT) void spec_accept_kernel(const float* __restrict
         if (wc < 0 && cum + m > target) { wc = c; before = cum; }
         cum += m;
     }
+    const bool resid = !use_p && qk != nullptr;
     int y = -1;
     double cprev = 0.0, cy = 0.0;
     bool found = false;
     if (wc >= 0) {
-        // rescan chunk wc: thread t owns a contiguous run of the chunk
+        // rescan chunk wc: thread t owns a contiguous run, prefix sums in index order
         const int a0 = wc * chunk, a1 = min(V, a0 + chunk);
         const int per = (a1 - a0 + NT - 1) / NT;
-        const int j0 = a0 + tid * per, j1 = min(a1, j0 + per);
+        const int j0 = a0 + threadIdx.x * per, j1 = min(a1, j0 + per);
         double mine = 0.0;
         for (int j = j0; j < j1; ++j) {
             const double pj = p_of(zk, sk, T, j);
-            mine += (use_p || !qk) ? pj : fmax(0.0, pj - (double)qk[j]);
+            mine += resid ? fmax(0.0, pj - (double)qk[j]) : pj;
         }
         double run = before + blk_prefix_excl<NT>(mine, sh);
         int cand = 0x7fffffff;
         double cp = 0.0, cc = 0.0;
         for (int j = j0; j < j1; ++j) {
             const double pj = p_of(zk, sk, T, j);
-            const double rj = (use_p || !qk) ? pj : fmax(0.0, pj - (double)qk[j]);
+            const double rj = resid ? fmax(0.0, pj - (double)qk[j]) : pj;
             const double nxt = run + rj;
             if (nxt > target) { cand = j; cp = run; cc = nxt; break; }
             run = nxt;
         }
-        // lowest candidate index wins
         int best = cand;
         for (int off = 32; off > 0; off >>= 1) best = min(best, __shfl_xor(best, off, 64));
         if (NT > 64) {
-            if ((tid & 63) == 0) shi[tid >> 6] = best;
+            if ((threadIdx.x & 63) == 0) shi[threadIdx.x >> 6] = best;
             __syncthreads();
             best = shi[0];
             for (int q2 = 1; q2 < NT / 64; ++q2) best = min(best, shi[q2]);
         }
-        if (tid == 0) s_y = 0x7fffffff;
+        if (threadIdx.x == 0) s_y = 0x7fffffff;
         __syncthreads();
         if (cand != 0x7fffffff && cand == best) {
             s_y = cand;
@@ -312,7 +290,7 @@ __global__ __launch_bounds__(NT) void spec_accept_kernel(const float* __restrict
             cy = sh[7];
         }
     }
-    if (tid != 0) return;
+    if (threadIdx.x != 0) return;
     if (!found) {
         // u * R at (or past) the end of the located chunk, or of the whole row:
         // only rounding puts it there, so it is a boundary case
@@ -321,12 +299,98 @@ __global__ __launch_bounds__(NT) void spec_accept_kernel(const float* __restrict
     } else if (fabs(target - cprev) < 1e-9 * R || fabs(target - cy) < 1e-9 * R) {
         flags |= VW4_FLAG_CDF_TIE;
     }
-    int32_t* tb = out_tokens + b * (D + 1);
     for (int i = 0; i < k; ++i) tb[i] = db[i];
     tb[k] = y;
     for (int i = k + 1; i <= D; ++i) tb[i] = -1;
-    out_nacc[b] = k;
-    out_flags[b] = flags;
+    *nacc_b = k;
+    *flags_b = flags;
+}
+
+struct AcceptArgs {
+    const float* logits;
+    int64_t lstride;
+    const vw4_rowstat* stats;
+    int64_t sstride;
+    const float* q;
+    int64_t qstride;
+    const int32_t* draft;
+    int D, V;
+    float temperature;
+    uint64_t seed, step0;
+    int chunk, P;
+    int32_t* out_tokens;
+    int32_t* out_nacc;
+    uint32_t* out_flags;
+    AcceptPart* parts;
+};
+
+__device__ __forceinline__ void write_bad(const AcceptArgs& a, int64_t b) {
+    if (threadIdx.x <= a.D) a.out_tokens[b * (a.D + 1) + threadIdx.x] = -1;
+    if (threadIdx.x == 0) {
+        a.out_nacc[b] = -1;
+        a.out_flags[b] = VW4_FLAG_NONFINITE;
+    }
+}
+
+// grid (B, P).  With P == 1 the workgroup finishes its problem itself;
+// otherwise it stores its chunk sums for accept_finish_kernel.
+template <int NT>
+__global__ __launch_bounds__(NT) void accept_chunk_kernel(AcceptArgs a) {
+    __shared__ double sh[8];
+    __shared__ int shi[8];
+    __shared__ double s_u[2 * (AMAXD + 1)];
+    __shared__ AcceptPart s_part;
+    const int64_t b = blockIdx.x;
+    const int w = blockIdx.y;
+    const float* zb = a.logits + b * a.lstride;
+    const vw4_rowstat* sb = a.stats + b * a.sstride;
+    const float* qb = a.q ? a.q + b * a.qstride : nullptr;
+    const int32_t* db = a.draft + b * a.D;
+    const double T = (double)a.temperature;
+    const ProblemState ps = problem_state<NT>(zb, sb, qb, db, a.D, a.V, T, a.seed, a.step0 + (uint64_t)b, s_u);
+    if (ps.bad) {
+        if (w == 0) write_bad(a, b);
+        return;
+    }
+    const int k = ps.k;
+    const float* zk = zb + (int64_t)k * a.V;
+    const vw4_rowstat sk = sb[k];
+    const float* qk = (k < a.D) ? qb + (int64_t)k * a.V : nullptr;
+    const int c0 = w * a.chunk, c1 = min(a.V, c0 + a.chunk);
+    const AcceptPart part = chunk_sums<NT>(zk, sk, qk, T, c0, c1, sh, shi);
+    if (a.P > 1) {
+        if (threadIdx.x == 0) a.parts[b * a.P + w] = part;
+        return;
+    }
+    if (threadIdx.x == 0) s_part = part;
+    __syncthreads();
+    finish_problem<NT>(zk, sk, qk, db, &s_part, 1, a.chunk, a.D, a.V, T, ps, s_u, a.out_tokens + b * (a.D + 1),
+                       a.out_nacc + b, a.out_flags + b, sh, shi);
+}
+
+// grid (B): combine the P chunk sums of problem b and sample its token.
+template <int NT>
+__global__ __launch_bounds__(NT) void accept_finish_kernel(AcceptArgs a) {
+    __shared__ double sh[8];
+    __shared__ int shi[8];
+    __shared__ double s_u[2 * (AMAXD + 1)];
+    __shared__ AcceptPart sp[AMAXP];
+    const int64_t b = blockIdx.x;
+    const float* zb = a.logits + b * a.lstride;
+    const vw4_rowstat* sb = a.stats + b * a.sstride;
+    const float* qb = a.q ? a.q + b * a.qstride : nullptr;
+    const int32_t* db = a.draft + b * a.D;
+    const double T = (double)a.temperature;
+    const ProblemState ps = problem_state<NT>(zb, sb, qb, db, a.D, a.V, T, a.seed, a.step0 + (uint64_t)b, s_u);
+    if (ps.bad) return;  // outputs written by the chunk kernel
+    for (int c = threadIdx.x; c < a.P; c += NT) sp[c] = a.parts[b * a.P + c];
+    __syncthreads();
+    const int k = ps.k;
+    const float* zk = zb + (int64_t)k * a.V;
+    const vw4_rowstat sk = sb[k];
+    const float* qk = (k < a.D) ? qb + (int64_t)k * a.V : nullptr;
+    finish_problem<NT>(zk, sk, qk, db, sp, a.P, a.chunk, a.D, a.V, T, ps, s_u, a.out_tokens + b * (a.D + 1),
+                       a.out_nacc + b, a.out_flags + b, sh, shi);
 }
 
 }  // namespace vw4
@@ -355,18 +419,22 @@ int spec_accept(const float* logits, int64_t logits_bstride, const vw4_rowstat* 
     const AcceptLayout L = accept_layout(B, V);
     VW4_REQUIRE(ws && ws_bytes >= L.total && aligned(ws, 256), VW4_EWORKSPACE,
                 "spec_accept: needs a 256-byte aligned workspace of %zu bytes", L.total);
-    AcceptPart* parts = (AcceptPart*)((char*)ws + L.off_part);
-    uint32_t* cnts = (uint32_t*)((char*)ws + L.off_cnt);
+    AcceptArgs a;
+    a.logits = logits; a.lstride = logits_bstride; a.stats = stats; a.sstride = stats_bstride;
+    a.q = q; a.qstride = q_bstride;
+    a.draft = draft ? draft : (const int32_t*)out_tokens;  // D == 0: never read
+    a.D = D; a.V = V; a.temperature = temperature; a.seed = seed; a.step0 = step0;
+    a.chunk = L.chunk; a.P = L.P;
+    a.out_tokens = out_tokens; a.out_nacc = out_n_acc; a.out_flags = out_flags;
+    a.parts = (AcceptPart*)((char*)ws + L.off_part);
     hipStream_t st = (hipStream_t)stream;
     const dim3 grid((unsigned)B, (unsigned)L.P);
-    if (L.threads == 64)
-        hipLaunchKernelGGL(spec_accept_kernel<64>, grid, dim3(64), 0, st, logits, logits_bstride, stats, stats_bstride,
-                           q, q_bstride, draft ? draft : (const int32_t*)out_tokens, D, V, temperature, seed, step0,
-                           L.chunk, L.P, out_tokens, out_n_acc, out_flags, parts, cnts);
-    else
-        hipLaunchKernelGGL(spec_accept_kernel<AT>, grid, dim3(AT), 0, st, logits, logits_bstride, stats, stats_bstride,
-                           q, q_bstride, draft ? draft : (const int32_t*)out_tokens, D, V, temperature, seed, step0,
-                           L.chunk, L.P, out_tokens, out_n_acc, out_flags, parts, cnts);
+    if (L.threads == 64) {
+        hipLaunchKernelGGL(accept_chunk_kernel<64>, grid, dim3(64), 0, st, a);
+    } else {
+        hipLaunchKernelGGL(accept_chunk_kernel<AT>, grid, dim3(AT), 0, st, a);
+        if (L.P > 1) hipLaunchKernelGGL(accept_finish_kernel<AT>, dim3((unsigned)B), dim3(AT), 0, st, a);
+    }
     return check_launch("spec_accept");
 }
 

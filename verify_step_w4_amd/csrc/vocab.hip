@@ -13,55 +13,59 @@
 //   kept set = { j : z_j >= tau },  Z = sum over the kept set,  log_z = log Z.
 //   T == 0: greedy (argmax, lowest index on ties); top_p >= 1: everything kept.
 //
-// MI355X design: no sort.  Each row is split over P workgroups; tau is found
-// by a radix descent on the order-preserving 32-bit key of the logits with
-// fp64 mass histograms (11 + 11 + 10 key bits, one kernel per level, LDS
-// histograms per workgroup).  Each level's workgroup histograms are combined
-// by the last workgroup of the row to arrive (integer counter), in workgroup
-// order.  A final pass recomputes E, Z, the mass strictly above tau and n_kept
-// with fixed-order reductions, so every statistic is reproducible bit for bit;
-// the histogram atomics only steer the descent and can matter only when the
-// boundary mass is within rounding of top_p * E, which the final pass flags.
+// MI355X design.  No sort: tau is found by a radix descent on the
+// order-preserving 32-bit key of the logits.  Each row is split over P
+// workgroups.  Phases communicate only through kernel boundaries (a device-wide
+// atomic counter costs tens of ns per arriving workgroup on this part, a
+// dependent launch about 1.7 us), and every cross-workgroup combination is a
+// fixed-order sum, so all statistics are reproducible bit for bit:
+//   1. per chunk: local max m_w, e_j relative to m_w (stored, fp64), E_w, and a
+//      mass histogram of the top 11 key bits (LDS)
+//   2. combine: rescale by exp((m_w - m)/T), sum the histograms in chunk order
+//   3. per chunk: descend the level-1 histogram to the bin holding the cutoff;
+//      histogram of the next 11 key bits inside it
+//   4. combine level 2
+//   5. per chunk: descend both levels; fixed-order mass and count above the
+//      22-bit key prefix of the cutoff; counts of the last 10 key bits inside it
+//   6. per row: with the 10-bit counts every bin is one float value, so its mass
+//      is count * exp((z - m)/T) exactly; finish the descent, tau, Z, n_kept.
+// The LDS histogram atomics only steer steps 3 and 5; the final decision in
+// step 6 uses fixed-order sums and flags (VW4_FLAG_TOPP_TIE) any row whose
+// boundary mass lies within 1e-9 * E of top_p * E.
 #include <math.h>
 
 #include "common.h"
 
 namespace vw4 {
 
-constexpr int VT = 256;            // threads per workgroup
-constexpr int VCHUNK = 4096;       // logits per workgroup (grown for huge V)
-constexpr int VMAXP = 64;          // workgroups per row at most
+constexpr int VT = 256;        // threads per workgroup
+constexpr int VCHUNK = 4096;   // logits per workgroup (grown for huge V)
+constexpr int VMAXP = 64;      // workgroups per row at most
 constexpr int L1BITS = 11, L2BITS = 11, L3BITS = 10;
-constexpr int HBINS = 2048;
+constexpr int HB = 2048;       // histogram bins of levels 1 and 2
+constexpr int HB3 = 1024;      // bins of level 3
+constexpr int CB = 256;        // bins combined per workgroup in the combine kernel
 
-struct RowState {
-    float m;            // row max
-    int32_t argmax;
-    double E;           // sum of e over the row (descent target base)
-    double target;      // top_p * E
-    double above;       // mass of keys above the current prefix range
-    uint32_t prefix;    // key prefix fixed so far
-    uint32_t done;      // 1: statistics already final (T == 0 or non-finite)
-    uint32_t flags;
-    uint32_t pad;
-};
-
-struct WgPart {            // per-workgroup partial results
+struct ChunkPart {   // per-workgroup results of phase 1
     float m;
     int32_t argmax;
     uint32_t bad;
-    uint32_t n;
-    double E;
-    double Z;
-    double gt;
     float mn;
+    double E;        // sum of exp((z - m_w)/T) over the chunk
+};
+
+struct ChunkSums {   // per-workgroup results of phase 5
+    double above;    // mass of keys above the 22-bit cutoff prefix
+    uint32_t n_above;
     uint32_t pad;
 };
 
 struct VocabLayout {
-    int P, chunk;
-    size_t off_state, off_part, off_hist, off_cnt, total;
+    int P, chunk, V, rows;
+    size_t off_part, off_e, off_h1p, off_h1, off_h2p, off_h2, off_sums, off_c3, total;
 };
+
+static size_t al256(size_t o) { return (o + 255) / 256 * 256; }
 
 static VocabLayout vocab_layout(int rows, int V) {
     VocabLayout L;
@@ -73,48 +77,70 @@ static VocabLayout vocab_layout(int rows, int V) {
     }
     L.P = P;
     L.chunk = chunk;
+    L.V = V;
+    L.rows = rows;
     size_t o = 0;
-    L.off_state = o;
-    o += (size_t)rows * sizeof(RowState);
-    o = (o + 255) / 256 * 256;
-    L.off_part = o;
-    o += (size_t)rows * P * sizeof(WgPart);
-    o = (o + 255) / 256 * 256;
-    L.off_hist = o;
-    o += (size_t)rows * P * HBINS * sizeof(double);
-    L.off_cnt = o;
-    o += (size_t)rows * 4 * sizeof(uint32_t);
-    L.total = (o + 255) / 256 * 256;
+    L.off_part = o; o = al256(o + (size_t)rows * P * sizeof(ChunkPart));
+    L.off_e = o;    o = al256(o + (size_t)rows * V * sizeof(double));
+    L.off_h1p = o;  o = al256(o + (size_t)rows * P * HB * sizeof(double));
+    L.off_h1 = o;   o = al256(o + (size_t)rows * HB * sizeof(double));
+    L.off_h2p = o;  o = al256(o + (size_t)rows * P * HB * sizeof(double));
+    L.off_h2 = o;   o = al256(o + (size_t)rows * HB * sizeof(double));
+    L.off_sums = o; o = al256(o + (size_t)rows * P * sizeof(ChunkSums));
+    L.off_c3 = o;   o = al256(o + (size_t)rows * P * HB3 * sizeof(uint32_t));
+    L.total = o;
     return L;
 }
 
+struct RowView {     // pointers of one row inside the workspace
+    ChunkPart* part;
+    double* e;
+    double* h1p;
+    double* h1;
+    double* h2p;
+    double* h2;
+    ChunkSums* sums;
+    uint32_t* c3;
+};
+
+__device__ __forceinline__ RowView row_view(char* ws, const VocabLayout& L, int r) {
+    RowView v;
+    v.part = (ChunkPart*)(ws + L.off_part) + (int64_t)r * L.P;
+    v.e = (double*)(ws + L.off_e) + (int64_t)r * L.V;
+    v.h1p = (double*)(ws + L.off_h1p) + (int64_t)r * L.P * HB;
+    v.h1 = (double*)(ws + L.off_h1) + (int64_t)r * HB;
+    v.h2p = (double*)(ws + L.off_h2p) + (int64_t)r * L.P * HB;
+    v.h2 = (double*)(ws + L.off_h2) + (int64_t)r * HB;
+    v.sums = (ChunkSums*)(ws + L.off_sums) + (int64_t)r * L.P;
+    v.c3 = (uint32_t*)(ws + L.off_c3) + (int64_t)r * L.P * HB3;
+    return v;
+}
+
 // ---------------------------------------------------------------------------
-// Block-level helpers (256 threads, fixed combination order).
+// Block helpers (VT = 256 threads, fixed combination order).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double block_sum_f64(double v, double* sh) {
     v = wave_sum(v);
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
     __syncthreads();
-    double s = sh[0] + sh[1] + sh[2] + sh[3];
+    const double s = (sh[0] + sh[1]) + (sh[2] + sh[3]);
     __syncthreads();
     return s;
 }
 
 __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* sh) {
     v = wave_sum(v);
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
     __syncthreads();
-    uint32_t s = sh[0] + sh[1] + sh[2] + sh[3];
+    const uint32_t s = sh[0] + sh[1] + sh[2] + sh[3];
     __syncthreads();
     return s;
 }
 
-// Exclusive suffix sum over threads: returns sum_{t' > t} v_{t'}.
+// Exclusive suffix sum over threads: sum_{t' > t} v_{t'}.
 __device__ __forceinline__ double block_suffix_excl_f64(double v, double* sh) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    double s = v;  // inclusive suffix within the wave
+    double s = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const double t = __shfl_down(s, off, 64);
@@ -130,295 +156,391 @@ __device__ __forceinline__ double block_suffix_excl_f64(double v, double* sh) {
     return ex + later;
 }
 
-// Last workgroup of a row to finish (release/acquire around an integer counter).
-__device__ __forceinline__ bool arrive_last(uint32_t* cnt, uint32_t total, int* sh_flag) {
-    __threadfence();
+// Row max / argmax (lowest index) / non-finite / min over the P chunk parts.
+struct RowMax {
+    float m, mn;
+    int32_t argmax;
+    uint32_t bad;
+};
+
+// Stage the P chunk parts in LDS with one load per thread (independent loads:
+// a dependent chain of global loads costs a full memory latency per part).
+__device__ __forceinline__ void stage_parts(const ChunkPart* __restrict__ part, int P, ChunkPart* sp) {
+    for (int k = threadIdx.x; k < P; k += blockDim.x) sp[k] = part[k];
     __syncthreads();
-    if (threadIdx.x == 0) *sh_flag = (atomicAdd(cnt, 1u) == total - 1u);
-    __syncthreads();
-    const bool last = *sh_flag != 0;
-    if (last) __threadfence();
-    return last;
 }
 
-// Find, among HBINS combined bins (8 per thread, ascending key), the largest
-// bin b with  above + sum_{b' >= b} H[b'] >= target.  Returns b (or -1) and
-// the mass above it in *new_above.  nb = number of valid bins.
-__device__ int descend_bins(const double* H, int nb, double above, double target, double* new_above, double* sh,
-                            int* shi) {
-    const int per = HBINS / VT;  // 8
+__device__ __forceinline__ RowMax combine_max(const ChunkPart* sp, int P) {
+    RowMax r;
+    r.m = -INFINITY;
+    r.mn = INFINITY;
+    r.argmax = 0;
+    r.bad = 0;
+    for (int k = 0; k < P; ++k) {
+        r.bad |= sp[k].bad;
+        r.mn = fminf(r.mn, sp[k].mn);
+        if (sp[k].m > r.m) { r.m = sp[k].m; r.argmax = sp[k].argmax; }  // chunks ascend: first max = lowest index
+    }
+    return r;
+}
+
+// Rescale factors f_w = exp((m_w - m)/T) into LDS, then
+// E = sum_w f_w E_w in chunk order.
+__device__ __forceinline__ double combine_E(const ChunkPart* sp, int P, float m, double T, double* f) {
+    for (int k = threadIdx.x; k < P; k += blockDim.x) f[k] = exp(((double)sp[k].m - (double)m) / T);
+    __syncthreads();
+    double E = 0.0;
+    for (int k = 0; k < P; ++k) E += f[k] * sp[k].E;
+    return E;
+}
+
+// Descend nb combined bins (ascending key, HB/VT = 8 per thread): the largest
+// bin b with above + sum_{b' >= b} H[b'] >= target.  Returns -1 if none.
+__device__ int descend(const double* __restrict__ H, int nb, double above, double target, double* new_above,
+                       double* sh, int* shi) {
+    const int per = HB / VT;
     const int b0 = threadIdx.x * per;
+    double h[HB / VT];
     double mine = 0.0;
-    for (int i = 0; i < per; ++i)
-        if (b0 + i < nb) mine += H[b0 + i];
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+        h[i] = (b0 + i < nb) ? H[b0 + i] : 0.0;
+        mine += h[i];
+    }
     const double later = block_suffix_excl_f64(mine, sh);
     if (threadIdx.x == 0) *shi = -1;
     __syncthreads();
-    double cum = above + later;  // mass of all bins above this thread's range
+    double cum = above + later;
+#pragma unroll
     for (int i = per - 1; i >= 0; --i) {
-        const int b = b0 + i;
-        if (b >= nb) continue;
-        const double h = H[b];
-        if (cum < target && cum + h >= target) {
-            *shi = b;  // exactly one bin can satisfy this (cum is monotone)
+        if (cum < target && cum + h[i] >= target && b0 + i < nb) {
+            *shi = b0 + i;
             sh[8] = cum;
         }
-        cum += h;
+        cum += h[i];
     }
     __syncthreads();
-    const int b = *shi;
-    *new_above = (b >= 0) ? sh[8] : above;
+    int b = *shi;
+    double na = (b >= 0) ? sh[8] : above;
     __syncthreads();
+    if (b < 0) {
+        // target beyond the histogram's total (rounding, or top_p within an ulp
+        // of 1): keep the lowest non-empty bin; the finishing pass flags it
+        if (threadIdx.x == 0) *shi = 0x7fffffff;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < per; ++i)
+            if (h[i] > 0.0) atomicMin(shi, b0 + i);
+        __syncthreads();
+        b = *shi;
+        if (b == 0x7fffffff) b = -1;
+        double mass_above = 0.0;
+#pragma unroll
+        for (int i = 0; i < per; ++i)
+            if (b0 + i > b) mass_above += h[i];
+        na = above + block_sum_f64(mass_above, sh);
+    }
+    *new_above = na;
     return b;
 }
 
 // ---------------------------------------------------------------------------
-// Level 1: max / argmax / non-finite check, local e relative to the
-// workgroup max, level-1 histogram; the last workgroup combines.
+// Phase 1: chunk max / argmax / min / non-finite; e relative to the chunk max;
+// level-1 histogram.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(VT) void stats_level1_kernel(const float* __restrict__ logits, int V, int chunk, int P,
-                                                          float temperature, float top_p, char* __restrict__ ws,
-                                                          VocabLayout L, vw4_rowstat* __restrict__ stats) {
-    __shared__ double hist[HBINS];
+__global__ __launch_bounds__(VT) void vs_chunk_kernel(const float* __restrict__ logits, float temperature,
+                                                      float top_p, char* __restrict__ ws, VocabLayout L) {
+    __shared__ double hist[HB];
     __shared__ double shd[16];
-    __shared__ float shf[4];
-    __shared__ int shi[4];
-    __shared__ int sflag;
+    __shared__ float shf[8];
+    __shared__ int shi[8];
     const int w = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
-    const float* z = logits + (int64_t)r * V;
-    const int c0 = w * chunk, c1 = min(V, c0 + chunk);
-    RowState* state = (RowState*)(ws + L.off_state) + r;
-    WgPart* parts = (WgPart*)(ws + L.off_part) + (int64_t)r * P;
-    double* hists = (double*)(ws + L.off_hist) + (int64_t)r * P * HBINS;
-    uint32_t* cnt = (uint32_t*)(ws + L.off_cnt) + r * 4;
+    const RowView rv = row_view(ws, L, r);
+    const float* z = logits + (int64_t)r * L.V;
+    const int c0 = w * L.chunk, c1 = min(L.V, c0 + L.chunk);
     const double T = (double)temperature;
 
-    float lm = -INFINITY;
+    float lm = -INFINITY, lmn = INFINITY;
     int li = 0x7fffffff;
     uint32_t bad = 0;
     for (int j = c0 + tid; j < c1; j += VT) {
         const float v = z[j];
         if (!isfinite(v)) bad = 1;
+        lmn = fminf(lmn, v);
         if (v > lm || (v == lm && j < li)) { lm = v; li = j; }
     }
-    // block max with lowest index on ties
     for (int off = 32; off > 0; off >>= 1) {
         const float om = __shfl_xor(lm, off, 64);
         const int oi = __shfl_xor(li, off, 64);
         if (om > lm || (om == lm && oi < li)) { lm = om; li = oi; }
+        lmn = fminf(lmn, __shfl_xor(lmn, off, 64));
     }
-    if ((tid & 63) == 0) { shf[tid >> 6] = lm; shi[tid >> 6] = li; }
+    if ((tid & 63) == 0) { shf[tid >> 6] = lm; shi[tid >> 6] = li; shf[4 + (tid >> 6)] = lmn; }
     __syncthreads();
     float m_w = shf[0];
     int a_w = shi[0];
     for (int k = 1; k < 4; ++k)
         if (shf[k] > m_w || (shf[k] == m_w && shi[k] < a_w)) { m_w = shf[k]; a_w = shi[k]; }
+    const float mn_w = fminf(fminf(shf[4], shf[5]), fminf(shf[6], shf[7]));
     __syncthreads();
     const uint32_t bad_w = block_sum_u32(bad, (uint32_t*)shi) != 0;
 
     double E_w = 0.0;
-    const bool need_mass = T > 0.0 && !bad_w && top_p < 1.0f;
     if (T > 0.0 && !bad_w) {
-        for (int b = tid; b < HBINS; b += VT) hist[b] = 0.0;
-        __syncthreads();
+        const bool hist_on = top_p < 1.0f;
+        if (hist_on) {
+            for (int b = tid; b < HB; b += VT) hist[b] = 0.0;
+            __syncthreads();
+        }
         double es = 0.0;
         for (int j = c0 + tid; j < c1; j += VT) {
             const float v = z[j];
             const double e = exp(((double)v - (double)m_w) / T);
             es += e;
-            if (need_mass) atomicAdd(&hist[f32_key(v) >> (32 - L1BITS)], e);
+            if (hist_on) {
+                rv.e[j] = e;
+                atomicAdd(&hist[f32_key(v) >> (32 - L1BITS)], e);
+            }
         }
         E_w = block_sum_f64(es, shd);
-        if (need_mass)
-            for (int b = tid; b < HBINS; b += VT) hists[(int64_t)w * HBINS + b] = hist[b];
+        if (hist_on)
+            for (int b = tid; b < HB; b += VT) rv.h1p[(int64_t)w * HB + b] = hist[b];
     }
     if (tid == 0) {
-        WgPart p;
-        p.m = m_w; p.argmax = a_w; p.bad = bad_w; p.n = 0; p.E = E_w; p.Z = 0; p.gt = 0; p.mn = 0; p.pad = 0;
-        parts[w] = p;
+        ChunkPart p;
+        p.m = m_w; p.argmax = a_w; p.bad = bad_w; p.mn = mn_w; p.E = E_w;
+        rv.part[w] = p;
     }
-    if (!arrive_last(&cnt[0], (uint32_t)P, &sflag)) return;
+}
 
-    // ---- last workgroup of the row: combine in workgroup order ----
-    float m = parts[0].m;
-    int a = parts[0].argmax;
-    uint32_t anybad = parts[0].bad;
-    for (int k = 1; k < P; ++k) {
-        anybad |= parts[k].bad;
-        if (parts[k].m > m) { m = parts[k].m; a = parts[k].argmax; }  // chunks ascend: first max is lowest index
+// Phases 2 and 4: combine the chunk histograms of one level, in chunk order.
+// Level 1 rescales chunk w by exp((m_w - m)/T); level 2 histograms are
+// already relative to the row max.  grid = (HB / CB, rows), CB threads.
+template <int LEVEL>
+__global__ __launch_bounds__(CB) void vs_combine_kernel(float temperature, char* __restrict__ ws, VocabLayout L) {
+    __shared__ double f[VMAXP];
+    __shared__ ChunkPart sp[VMAXP];
+    const int r = blockIdx.y, b = blockIdx.x * CB + threadIdx.x;
+    const RowView rv = row_view(ws, L, r);
+    stage_parts(rv.part, L.P, sp);
+    const RowMax mx = combine_max(sp, L.P);
+    if (mx.bad || !(temperature > 0.0f)) return;
+    const double T = (double)temperature;
+    if (LEVEL == 1) {
+        for (int k = threadIdx.x; k < L.P; k += CB) f[k] = exp(((double)sp[k].m - (double)mx.m) / T);
+        __syncthreads();
     }
-    if (tid == 0) cnt[0] = 0u;
-    if (anybad || T == 0.0) {
+    const double* src = (LEVEL == 1) ? rv.h1p : rv.h2p;
+    double* dst = (LEVEL == 1) ? rv.h1 : rv.h2;
+    double acc = 0.0;
+    for (int k0 = 0; k0 < L.P; k0 += 16) {
+        double v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = (k0 + i < L.P) ? src[(int64_t)(k0 + i) * HB + b] : 0.0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (k0 + i < L.P) acc += (LEVEL == 1) ? f[k0 + i] * v[i] : v[i];
+    }
+    dst[b] = acc;
+}
+
+// Phase 3: level-2 histogram of the chunk's logits inside the level-1 cutoff bin.
+__global__ __launch_bounds__(VT) void vs_level2_kernel(const float* __restrict__ logits, float temperature,
+                                                       float top_p, char* __restrict__ ws, VocabLayout L) {
+    __shared__ double hist[HB];
+    __shared__ double shd[16];
+    __shared__ int shi[4];
+    __shared__ ChunkPart sp[VMAXP];
+    __shared__ double f[VMAXP];
+    const int w = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+    const RowView rv = row_view(ws, L, r);
+    stage_parts(rv.part, L.P, sp);
+    const RowMax mx = combine_max(sp, L.P);
+    if (mx.bad || !(temperature > 0.0f)) return;
+    const double T = (double)temperature;
+    const double E = combine_E(sp, L.P, mx.m, T, f);
+    const double target = (double)top_p * E;
+    double above1;
+    int b1 = descend(rv.h1, HB, 0.0, target, &above1, shd, shi);
+    const float* z = logits + (int64_t)r * L.V;
+    const int c0 = w * L.chunk, c1 = min(L.V, c0 + L.chunk);
+    const double fw = f[w];
+    for (int b = tid; b < HB; b += VT) hist[b] = 0.0;
+    __syncthreads();
+    if (b1 >= 0) {
+        for (int j = c0 + tid; j < c1; j += VT) {
+            const uint32_t k = f32_key(z[j]);
+            if ((k >> (32 - L1BITS)) == (uint32_t)b1)
+                atomicAdd(&hist[(k >> L3BITS) & (HB - 1)], rv.e[j] * fw);
+        }
+    }
+    __syncthreads();
+    for (int b = tid; b < HB; b += VT) rv.h2p[(int64_t)w * HB + b] = hist[b];
+}
+
+// Phase 5: fixed-order mass/count above the 22-bit cutoff prefix and the
+// level-3 counts inside it.
+__global__ __launch_bounds__(VT) void vs_level3_kernel(const float* __restrict__ logits, float temperature,
+                                                       float top_p, char* __restrict__ ws, VocabLayout L) {
+    __shared__ uint32_t cnt[HB3];
+    __shared__ double shd[16];
+    __shared__ uint32_t shu[4];
+    __shared__ int shi[4];
+    __shared__ ChunkPart sp[VMAXP];
+    __shared__ double f[VMAXP];
+    const int w = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+    const RowView rv = row_view(ws, L, r);
+    stage_parts(rv.part, L.P, sp);
+    const RowMax mx = combine_max(sp, L.P);
+    if (mx.bad || !(temperature > 0.0f)) return;
+    const double T = (double)temperature;
+    const double E = combine_E(sp, L.P, mx.m, T, f);
+    const double target = (double)top_p * E;
+    double above1, above2 = 0.0;
+    int b1 = descend(rv.h1, HB, 0.0, target, &above1, shd, shi);
+    int b2 = (b1 >= 0) ? descend(rv.h2, HB, above1, target, &above2, shd, shi) : -1;
+    const float* z = logits + (int64_t)r * L.V;
+    const int c0 = w * L.chunk, c1 = min(L.V, c0 + L.chunk);
+    const double fw = f[w];
+    for (int b = tid; b < HB3; b += VT) cnt[b] = 0u;
+    __syncthreads();
+    // without a usable steering bin (only rounding can cause this) the prefix
+    // is placed above every key: nothing is "above", all counts land in bins
+    // the finishing pass treats as a flagged boundary case
+    const uint32_t prefix = (b1 >= 0 && b2 >= 0) ? (((uint32_t)b1 << L2BITS) | (uint32_t)b2) : 0x3fffffu;
+    double sa = 0.0;
+    uint32_t na = 0;
+    for (int j = c0 + tid; j < c1; j += VT) {
+        const uint32_t k = f32_key(z[j]);
+        const uint32_t hi = k >> L3BITS;
+        if (hi > prefix) { sa += rv.e[j] * fw; ++na; }
+        else if (hi == prefix) atomicAdd(&cnt[k & (HB3 - 1)], 1u);
+    }
+    sa = block_sum_f64(sa, shd);
+    na = block_sum_u32(na, shu);
+    for (int b = tid; b < HB3; b += VT) rv.c3[(int64_t)w * HB3 + b] = cnt[b];
+    if (tid == 0) {
+        ChunkSums s;
+        s.above = sa; s.n_above = na; s.pad = prefix;
+        rv.sums[w] = s;
+    }
+}
+
+// Phase 6: per row (HB3 = 1024 threads): finish and write the statistics.
+__global__ __launch_bounds__(HB3) void vs_finish_kernel(float temperature, float top_p, char* __restrict__ ws,
+                                                        VocabLayout L, vw4_rowstat* __restrict__ stats) {
+    __shared__ double sh[HB3 / 64 + 4];
+    __shared__ int s_b;
+    __shared__ double s_cum;
+    __shared__ ChunkPart sp[VMAXP];
+    __shared__ double f[VMAXP];
+    __shared__ ChunkSums ss[VMAXP];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const RowView rv = row_view(ws, L, r);
+    stage_parts(rv.part, L.P, sp);
+    for (int k = tid; k < L.P; k += blockDim.x) ss[k] = rv.sums[k];
+    __syncthreads();
+    const RowMax mx = combine_max(sp, L.P);
+    const double T = (double)temperature;
+    vw4_rowstat s;
+    s.max_logit = mx.m;
+    s.argmax = mx.argmax;
+    s.pad = 0;
+    if (mx.bad || !(T > 0.0)) {
         if (tid == 0) {
-            vw4_rowstat s;
-            s.max_logit = anybad ? NAN : m;
+            s.max_logit = mx.bad ? NAN : mx.m;
             s.tau = s.max_logit;
             s.log_z = 0.0;
-            s.argmax = anybad ? -1 : a;
-            s.n_kept = anybad ? 0 : 1;
-            s.flags = anybad ? VW4_FLAG_NONFINITE : 0u;
-            s.pad = 0;
+            s.argmax = mx.bad ? -1 : mx.argmax;
+            s.n_kept = mx.bad ? 0 : 1;
+            s.flags = mx.bad ? VW4_FLAG_NONFINITE : 0u;
             stats[r] = s;
-            RowState st = {};
-            st.m = m; st.argmax = a; st.done = 1; st.flags = s.flags;
-            *state = st;
         }
         return;
     }
-    __shared__ double fk[VMAXP];  // rescale factors exp((m_k - m)/T) of the workgroup partials
-    for (int k = tid; k < P; k += VT) fk[k] = exp(((double)parts[k].m - (double)m) / T);
-    __syncthreads();
-    double E = 0.0;
-    for (int k = 0; k < P; ++k) E += fk[k] * parts[k].E;
-    const double target = (double)top_p * E;
-    RowState st = {};
-    st.m = m; st.argmax = a; st.E = E; st.target = target; st.done = 0; st.flags = 0;
-    if (!need_mass) {
-        st.prefix = 0; st.above = 0.0;
-        if (tid == 0) *state = st;
+    const double E = combine_E(sp, L.P, mx.m, T, f);
+    if (!(top_p < 1.0f)) {
+        if (tid == 0) {
+            s.tau = mx.mn;
+            s.log_z = log(E);
+            s.n_kept = L.V;
+            s.flags = 0;
+            stats[r] = s;
+        }
         return;
     }
-    // combined level-1 histogram, then the descent
-    for (int b = tid; b < HBINS; b += VT) {
-        double h = 0.0;
-        for (int k = 0; k < P; ++k) h += fk[k] * hists[(int64_t)k * HBINS + b];
-        hist[b] = h;
+    const double target = (double)top_p * E;
+    double above = 0.0;
+    uint32_t n_above = 0;
+    for (int k = 0; k < L.P; ++k) { above += ss[k].above; n_above += ss[k].n_above; }
+    const uint32_t prefix = ss[0].pad;
+    // level-3 bin b (thread b): one float value, mass = count * e(value)
+    uint32_t c = 0;
+    for (int k0 = 0; k0 < L.P; k0 += 16) {
+        uint32_t v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = (k0 + i < L.P) ? rv.c3[(int64_t)(k0 + i) * HB3 + tid] : 0u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c += v[i];
     }
+    const float zb = key_f32((prefix << L3BITS) | (uint32_t)tid);
+    const double eb = (c && prefix != 0x3fffffu) ? exp(((double)zb - (double)mx.m) / T) : 0.0;
+    const double mass = (double)c * eb;
+    // suffix sums over the bins above each thread's bin (fixed tree order)
+    const int lane = tid & 63, wv = tid >> 6;
+    double sfx = mass;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double t = __shfl_down(sfx, off, 64);
+        if (lane + off < 64) sfx += t;
+    }
+    if (lane == 0) sh[wv] = sfx;
+    if (tid == 0) s_b = -1;
     __syncthreads();
-    double above;
-    int b1 = descend_bins(hist, 1 << L1BITS, 0.0, target, &above, shd, &shi[0]);
-    if (b1 < 0) {  // rounding left the target unreached: take the lowest non-empty bin
-        for (int b = 0; b < HBINS; ++b) if (hist[b] > 0.0) { b1 = b; break; }
-        above = 0.0;
-        for (int b = b1 + 1; b < HBINS; ++b) above += hist[b];
-        st.flags |= VW4_FLAG_TOPP_TIE;
-    }
-    st.prefix = (uint32_t)b1;
-    st.above = above;
-    if (tid == 0) *state = st;
-}
-
-// Levels 2 and 3: histogram of the next key bits among the logits whose key
-// matches the prefix fixed so far; the last workgroup extends the prefix.
-template <int SHIFT, int BITS>
-__global__ __launch_bounds__(VT) void stats_level_kernel(const float* __restrict__ logits, int V, int chunk, int P,
-                                                         float temperature, char* __restrict__ ws, VocabLayout L,
-                                                         int cnt_slot) {
-    __shared__ double hist[HBINS];
-    __shared__ double shd[16];
-    __shared__ int shi[4];
-    __shared__ int sflag;
-    const int w = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
-    RowState* state = (RowState*)(ws + L.off_state) + r;
-    const RowState st = *state;
-    if (st.done || st.target <= 0.0) return;
-    const float* z = logits + (int64_t)r * V;
-    const int c0 = w * chunk, c1 = min(V, c0 + chunk);
-    double* hists = (double*)(ws + L.off_hist) + (int64_t)r * P * HBINS;
-    uint32_t* cnt = (uint32_t*)(ws + L.off_cnt) + r * 4 + cnt_slot;
-    const double T = (double)temperature;
-    const int nb = 1 << BITS;
-    for (int b = tid; b < nb; b += VT) hist[b] = 0.0;
+    double later = 0.0;
+    for (int w2 = HB3 / 64 - 1; w2 > wv; --w2) later += sh[w2];
+    double ex = __shfl_down(sfx, 1, 64);
+    if (lane == 63) ex = 0.0;
+    const double cum_above = above + later + ex;  // mass of every key above this bin
+    if (c && cum_above < target && cum_above + mass >= target) { s_b = tid; s_cum = cum_above; }
     __syncthreads();
-    for (int j = c0 + tid; j < c1; j += VT) {
-        const float v = z[j];
-        const uint32_t k = f32_key(v);
-        if ((k >> (SHIFT + BITS)) == st.prefix)
-            atomicAdd(&hist[(k >> SHIFT) & (uint32_t)(nb - 1)], exp(((double)v - (double)st.m) / T));
+    uint32_t flags = 0;
+    int b3 = s_b;
+    double G = s_cum;
+    if (b3 < 0) {
+        // steering missed the boundary by rounding: keep the nearest bin and flag it
+        flags |= VW4_FLAG_TOPP_TIE;
+        __shared__ int s_lo, s_hi;
+        if (tid == 0) { s_lo = 0x7fffffff; s_hi = -1; }
+        __syncthreads();
+        if (c) { atomicMin(&s_lo, tid); atomicMax(&s_hi, tid); }
+        __syncthreads();
+        b3 = (above >= target) ? s_hi : s_lo;
+        if (b3 < 0 || b3 >= HB3) b3 = 0;
+        G = 0.0;
     }
+    // Z = mass above + bins >= b3, in bin order from the top
     __syncthreads();
-    for (int b = tid; b < nb; b += VT) hists[(int64_t)w * HBINS + b] = hist[b];
-    if (!arrive_last(cnt, (uint32_t)P, &sflag)) return;
-    if (tid == 0) *cnt = 0u;
-    for (int b = tid; b < HBINS; b += VT) {
-        double h = 0.0;
-        if (b < nb)
-            for (int k = 0; k < P; ++k) h += hists[(int64_t)k * HBINS + b];
-        hist[b] = h;
-    }
+    const double mine = (tid >= b3) ? mass : 0.0;
+    double zsum = wave_sum(mine);
+    uint32_t nmine = (tid >= b3) ? c : 0u;
+    uint32_t nsum = wave_sum(nmine);
+    __shared__ double shz[HB3 / 64];
+    __shared__ uint32_t shn[HB3 / 64];
+    if (lane == 0) { shz[wv] = zsum; shn[wv] = nsum; }
     __syncthreads();
-    double above;
-    int bb = descend_bins(hist, nb, st.above, st.target, &above, shd, &shi[0]);
-    RowState ns = st;
-    if (bb < 0) {
-        for (int b = 0; b < nb; ++b) if (hist[b] > 0.0) { bb = b; break; }
-        if (bb < 0) bb = 0;
-        above = st.above;
-        for (int b = bb + 1; b < nb; ++b) above += hist[b];
-        ns.flags |= VW4_FLAG_TOPP_TIE;
-    }
-    ns.prefix = (st.prefix << BITS) | (uint32_t)bb;
-    ns.above = above;
-    if (tid == 0) *state = ns;
-}
-
-// Final pass: fixed-order sums over the row with the global max and the
-// selected cutoff; writes the row statistics.
-__global__ __launch_bounds__(VT) void stats_final_kernel(const float* __restrict__ logits, int V, int chunk, int P,
-                                                         float temperature, float top_p, char* __restrict__ ws,
-                                                         VocabLayout L, vw4_rowstat* __restrict__ stats) {
-    __shared__ double shd[16];
-    __shared__ uint32_t shu[4];
-    __shared__ float shf[4];
-    __shared__ int sflag;
-    const int w = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
-    RowState* state = (RowState*)(ws + L.off_state) + r;
-    const RowState st = *state;
-    if (st.done) return;
-    const float* z = logits + (int64_t)r * V;
-    const int c0 = w * chunk, c1 = min(V, c0 + chunk);
-    WgPart* parts = (WgPart*)(ws + L.off_part) + (int64_t)r * P;
-    uint32_t* cnt = (uint32_t*)(ws + L.off_cnt) + r * 4 + 3;
-    const double T = (double)temperature;
-    const bool keep_all = !(top_p < 1.0f);
-    const float tau = keep_all ? -INFINITY : key_f32(st.prefix);
-    double se = 0.0, sz = 0.0, sg = 0.0;
-    uint32_t n = 0;
-    float mn = INFINITY;
-    for (int j = c0 + tid; j < c1; j += VT) {
-        const float v = z[j];
-        const double e = exp(((double)v - (double)st.m) / T);
-        se += e;
-        mn = fminf(mn, v);
-        if (v >= tau) { sz += e; ++n; }
-        if (v > tau) sg += e;
-    }
-    se = block_sum_f64(se, shd);
-    sz = block_sum_f64(sz, shd);
-    sg = block_sum_f64(sg, shd);
-    n = block_sum_u32(n, shu);
-    for (int off = 32; off > 0; off >>= 1) mn = fminf(mn, __shfl_xor(mn, off, 64));
-    if ((tid & 63) == 0) shf[tid >> 6] = mn;
-    __syncthreads();
-    mn = fminf(fminf(shf[0], shf[1]), fminf(shf[2], shf[3]));
-    if (tid == 0) {
-        WgPart p = parts[w];
-        p.E = se; p.Z = sz; p.gt = sg; p.n = n; p.mn = mn;
-        parts[w] = p;
-    }
-    if (!arrive_last(cnt, (uint32_t)P, &sflag)) return;
     if (tid != 0) return;
-    *cnt = 0u;
-    double E = 0.0, Z = 0.0, G = 0.0;
-    uint32_t nk = 0;
-    float rmin = INFINITY;
-    for (int k = 0; k < P; ++k) {
-        E += parts[k].E; Z += parts[k].Z; G += parts[k].gt; nk += parts[k].n;
-        rmin = fminf(rmin, parts[k].mn);
+    double Zin = 0.0;
+    uint32_t nin = 0;
+    for (int k = HB3 / 64 - 1; k >= 0; --k) { Zin += shz[k]; nin += shn[k]; }
+    const double Z = above + Zin;
+    if (!(flags & VW4_FLAG_TOPP_TIE)) {
+        if (fabs(Z - target) < 1e-9 * E || fabs(G - target) < 1e-9 * E) flags |= VW4_FLAG_TOPP_TIE;
     }
-    uint32_t flags = st.flags;
-    if (!keep_all) {
-        const double Pt = (double)top_p * E;
-        if (fabs(Z - Pt) < 1e-9 * E || fabs(G - Pt) < 1e-9 * E || !(G < Pt && Z >= Pt)) flags |= VW4_FLAG_TOPP_TIE;
-    }
-    vw4_rowstat s;
-    s.max_logit = st.m;
-    s.tau = keep_all ? rmin : tau;
+    s.tau = key_f32((prefix << L3BITS) | (uint32_t)b3);
     s.log_z = log(Z);
-    s.argmax = st.argmax;
-    s.n_kept = (int32_t)nk;
+    s.n_kept = (int32_t)(n_above + nin);
     s.flags = flags;
-    s.pad = 0;
     stats[r] = s;
 }
 
@@ -460,19 +582,16 @@ int verify_logits(const uint16_t* hidden, int64_t ldh, const uint8_t* lm_packed,
                                gws ? (char*)ws + L.total : nullptr, gws, st);
         if (rc) return rc;
     }
-    const dim3 grid(L.P, rows);
-    hipLaunchKernelGGL(stats_level1_kernel, grid, dim3(VT), 0, st, logits, V, L.chunk, L.P, temperature, top_p,
-                       (char*)ws, L, stats);
-    if (temperature > 0.0f) {
-        if (top_p < 1.0f) {
-            hipLaunchKernelGGL((stats_level_kernel<L3BITS, L2BITS>), grid, dim3(VT), 0, st, logits, V, L.chunk, L.P,
-                               temperature, (char*)ws, L, 1);
-            hipLaunchKernelGGL((stats_level_kernel<0, L3BITS>), grid, dim3(VT), 0, st, logits, V, L.chunk, L.P,
-                               temperature, (char*)ws, L, 2);
-        }
-        hipLaunchKernelGGL(stats_final_kernel, grid, dim3(VT), 0, st, logits, V, L.chunk, L.P, temperature, top_p,
-                           (char*)ws, L, stats);
+    char* w = (char*)ws;
+    const dim3 grid(L.P, rows), cgrid(HB / CB, rows);
+    hipLaunchKernelGGL(vs_chunk_kernel, grid, dim3(VT), 0, st, logits, temperature, top_p, w, L);
+    if (temperature > 0.0f && top_p < 1.0f) {
+        hipLaunchKernelGGL(vs_combine_kernel<1>, cgrid, dim3(CB), 0, st, temperature, w, L);
+        hipLaunchKernelGGL(vs_level2_kernel, grid, dim3(VT), 0, st, logits, temperature, top_p, w, L);
+        hipLaunchKernelGGL(vs_combine_kernel<2>, cgrid, dim3(CB), 0, st, temperature, w, L);
+        hipLaunchKernelGGL(vs_level3_kernel, grid, dim3(VT), 0, st, logits, temperature, top_p, w, L);
     }
+    hipLaunchKernelGGL(vs_finish_kernel, dim3(rows), dim3(HB3), 0, st, temperature, top_p, w, L, stats);
     return check_launch("verify_logits");
 }
 

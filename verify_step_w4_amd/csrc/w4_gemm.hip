@@ -20,11 +20,11 @@
 //    (computed per workgroup in fp64 and rounded once), so the inner loop is
 //    one AND-OR (plus a shift) per pair and M dot2 per pair.
 //  * Split K: S_wg wavefronts of a workgroup take consecutive K slices of the
-//    same tile and are reduced through LDS; S_grid workgroups per tile write
-//    fp32 partials to the workspace and the last one to arrive (integer atomic
-//    counter) sums them in slice order.  The summation order depends only on
-//    (N, K), never on M or on timing, so results are bitwise reproducible and
-//    row m of an M-row call equals the one-row call.
+//    same tile and are reduced through LDS; when the tiles are too few to fill
+//    the chip, S_grid workgroups per tile write fp32 partials to the workspace
+//    and a second launch sums them in slice order.  The summation order
+//    depends only on (N, K), never on M or on timing, so results are bitwise
+//    reproducible and row m of an M-row call equals the one-row call.
 #include <stdlib.h>
 
 #include "common.h"
@@ -76,8 +76,8 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
                                                       const u32x4* __restrict__ wpk,
                                                       const uint16_t* __restrict__ spk, void* __restrict__ y,
                                                       int64_t ldy, int ydt, int N, int G, int S_wg, int S_grid,
-                                                      float* __restrict__ part, uint32_t* __restrict__ cnt,
-                                                      int64_t Npad, uint32_t kmask, uint32_t kmagic) {
+                                                      float* __restrict__ part, int64_t Npad, uint32_t kmask,
+                                                      uint32_t kmagic) {
     extern __shared__ float lds[];
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -183,8 +183,9 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
     }
 
     const int n = t * 64 + lane;
+    if (wv != 0) return;
     if (S_grid == 1) {
-        if (wv == 0 && n < N) {
+        if (n < N) {
 #pragma unroll
             for (int m = 0; m < M; ++m) {
                 if (ydt == VW4_F32) ((float*)y)[m * ldy + n] = v[m];
@@ -193,34 +194,30 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
         }
         return;
     }
+    // Split across workgroups: fp32 partials; w4_gemm_reduce_kernel sums them.
+#pragma unroll
+    for (int m = 0; m < M; ++m) part[((int64_t)blockIdx.y * M + m) * Npad + n] = v[m];
+}
 
-    // Cross-workgroup split: partials, then the last workgroup of the tile sums them.
-    __shared__ int s_last;
-    if (wv == 0) {
+// Sum of the S_grid partials of each output in slice order (a separate launch:
+// on this part a dependent launch is cheaper than a device-wide atomic
+// counter per workgroup).  grid = (ntiles, M), 64 threads.
+__global__ __launch_bounds__(64) void w4_gemm_reduce_kernel(const float* __restrict__ part, int S_grid, int M,
+                                                            int64_t Npad, int N, void* __restrict__ y, int64_t ldy,
+                                                            int ydt) {
+    const int n = blockIdx.x * 64 + threadIdx.x, m = blockIdx.y;
+    if (n >= N) return;
+    float s = 0.0f;
+    for (int b0 = 0; b0 < S_grid; b0 += 8) {
+        float v[8];
 #pragma unroll
-        for (int m = 0; m < M; ++m) part[((int64_t)blockIdx.y * M + m) * Npad + n] = v[m];
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = atomicAdd(&cnt[t], 1u);
-        s_last = (prev == (uint32_t)(S_grid - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (wv == 0) {
+        for (int i = 0; i < 8; ++i) v[i] = (b0 + i < S_grid) ? part[((int64_t)(b0 + i) * M + m) * Npad + n] : 0.0f;
 #pragma unroll
-        for (int m = 0; m < M; ++m) {
-            float s = 0.0f;
-            for (int b = 0; b < S_grid; ++b) s += part[((int64_t)b * M + m) * Npad + n];
-            if (n < N) {
-                if (ydt == VW4_F32) ((float*)y)[m * ldy + n] = s;
-                else ((uint16_t*)y)[m * ldy + n] = f32_to_bf16(s);
-            }
-        }
-        if (lane == 0) cnt[t] = 0u;  // leave the counter clear for the next call
+        for (int i = 0; i < 8; ++i)
+            if (b0 + i < S_grid) s += v[i];
     }
+    if (ydt == VW4_F32) ((float*)y)[m * ldy + n] = s;
+    else ((uint16_t*)y)[m * ldy + n] = f32_to_bf16(s);
 }
 
 struct GemmPlan {
@@ -237,7 +234,7 @@ static GemmPlan plan_gemm(int M, int N, int K) {
     p.G = K / 64;
     p.ntiles = (N + 63) / 64;
     p.Npad = (int64_t)p.ntiles * 64;
-    const int target_waves = 2048;
+    const int target_waves = 8192;
     int S = (target_waves + p.ntiles - 1) / p.ntiles;
     int maxS = p.G / 2 > 0 ? p.G / 2 : 1;
     if (S > maxS) S = maxS;
@@ -255,20 +252,19 @@ static GemmPlan plan_gemm(int M, int N, int K) {
     const int ng_max = (int)(((int64_t)p.S_wg * p.G + S_all - 1) / S_all) + 1;
     p.lds_bytes = (size_t)M * ng_max * 4 + (p.S_wg > 1 ? (size_t)p.S_wg * M * 64 * 4 : 0);
     p.ws_bytes = 0;
-    if (p.S_grid > 1) {
-        size_t part = (size_t)p.S_grid * M * p.Npad * 4;
-        part = (part + 255) / 256 * 256;
-        p.ws_bytes = part + (size_t)p.ntiles * 4;
-    }
+    if (p.S_grid > 1) p.ws_bytes = ((size_t)p.S_grid * M * p.Npad * 4 + 255) / 256 * 256;
     return p;
 }
 
 template <int M>
 static void launch_gemm(const GemmPlan& p, const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* s,
-                        void* y, int64_t ldy, int ydt, int N, float* part, uint32_t* cnt, hipStream_t st) {
+                        void* y, int64_t ldy, int ydt, int N, float* part, hipStream_t st) {
     hipLaunchKernelGGL(w4_gemm_kernel<M>, dim3(p.ntiles, p.S_grid), dim3(64 * p.S_wg), p.lds_bytes, st, x, ldx,
-                       (const u32x4*)w, s, y, ldy, ydt, N, p.G, p.S_wg, p.S_grid, part, cnt, p.Npad, 0x000F000Fu,
+                       (const u32x4*)w, s, y, ldy, ydt, N, p.G, p.S_wg, p.S_grid, part, p.Npad, 0x000F000Fu,
                        0x43004300u);
+    if (p.S_grid > 1)
+        hipLaunchKernelGGL(w4_gemm_reduce_kernel, dim3(p.ntiles, M), dim3(64), 0, st, part, p.S_grid, M, p.Npad, N,
+                           y, ldy, ydt);
 }
 
 int gemm_dispatch(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* s, void* y, int64_t ldy,
@@ -286,22 +282,20 @@ int gemm_dispatch(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16
     VW4_REQUIRE(aligned(y, ydt == VW4_F32 ? 4 : 2), VW4_EINVAL, "w4_skinny_gemm: y misaligned");
     const GemmPlan p = plan_gemm(M, N, K);
     float* part = nullptr;
-    uint32_t* cnt = nullptr;
     if (p.ws_bytes) {
         VW4_REQUIRE(ws && ws_bytes >= p.ws_bytes && aligned(ws, 256), VW4_EWORKSPACE,
                     "w4_skinny_gemm: needs a 256-byte aligned workspace of %zu bytes", p.ws_bytes);
         part = (float*)ws;
-        cnt = (uint32_t*)((char*)ws + (p.ws_bytes - (size_t)p.ntiles * 4));
     }
     switch (M) {
-        case 1: launch_gemm<1>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
-        case 2: launch_gemm<2>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
-        case 3: launch_gemm<3>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
-        case 4: launch_gemm<4>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
-        case 5: launch_gemm<5>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
-        case 6: launch_gemm<6>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
-        case 7: launch_gemm<7>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
-        default: launch_gemm<8>(p, x, ldx, w, s, y, ldy, ydt, N, part, cnt, st); break;
+        case 1: launch_gemm<1>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
+        case 2: launch_gemm<2>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
+        case 3: launch_gemm<3>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
+        case 4: launch_gemm<4>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
+        case 5: launch_gemm<5>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
+        case 6: launch_gemm<6>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
+        case 7: launch_gemm<7>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
+        default: launch_gemm<8>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
     }
     return check_launch("w4_skinny_gemm");
 }
