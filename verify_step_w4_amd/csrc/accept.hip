@@ -44,7 +44,7 @@ struct AcceptPart {
 
 struct AcceptLayout {
     int P, chunk, threads;
-    size_t off_part, total;
+    size_t off_part, off_state, total;
 };
 
 static AcceptLayout accept_layout(int B, int V) {
@@ -65,6 +65,9 @@ static AcceptLayout accept_layout(int B, int V) {
     size_t o = 0;
     L.off_part = o;
     o += (size_t)B * L.P * sizeof(AcceptPart);
+    o = (o + 255) / 256 * 256;
+    L.off_state = o;
+    o += (size_t)B * 16;
     L.total = (o + 255) / 256 * 256;
     return L;
 }
@@ -94,12 +97,14 @@ __device__ __forceinline__ void philox4x64_10(uint64_t k0, uint64_t k1, uint64_t
 
 __device__ __forceinline__ double unit53(uint64_t r) { return (double)(r >> 11) * 0x1.0p-53; }
 
-__device__ __forceinline__ double p_of(const float* __restrict__ z, const vw4_rowstat& s, double T, int j) {
+// Target probability of token j whose logit is v.
+__device__ __forceinline__ double p_val(float v, const vw4_rowstat& s, double T, int j) {
     if (T == 0.0) return (j == s.argmax) ? 1.0 : 0.0;
-    const float v = z[j];
     if (!(v >= s.tau)) return 0.0;
     return exp(((double)v - (double)s.max_logit) / T - s.log_z);
 }
+
+constexpr int AU = 16;  // elements per thread loaded together (one latency per tile)
 
 template <int NT>
 __device__ __forceinline__ double blk_sum(double v, double* sh) {
@@ -155,35 +160,47 @@ struct ProblemState {
     uint32_t flags;
     bool bad;
 };
+static_assert(sizeof(ProblemState) <= 16, "ProblemState slot is 16 bytes");
 
 template <int NT>
 __device__ __forceinline__ ProblemState problem_state(const float* __restrict__ zb, const vw4_rowstat* __restrict__ sb,
                                                       const float* __restrict__ qb, const int32_t* __restrict__ db,
                                                       int D, int V, double T, uint64_t seed, uint64_t step,
-                                                      double* s_u) {
+                                                      double* s_u, vw4_rowstat* s_st) {
+    __shared__ double s_p[AMAXD + 1], s_q[AMAXD + 1];
+    __shared__ int s_ok[AMAXD + 1];
+    // thread i (<= D): row i's uniforms, statistics, and p_i(x_i), q_i(x_i) --
+    // all rows' loads in flight together
     if (threadIdx.x <= D) {
-        uint64_t c[4] = {step, (uint64_t)threadIdx.x, 0, 0};
+        const int i = threadIdx.x;
+        uint64_t c[4] = {step, (uint64_t)i, 0, 0};
         philox4x64_10(seed, 0, c);
-        s_u[2 * threadIdx.x] = unit53(c[0]);
-        s_u[2 * threadIdx.x + 1] = unit53(c[1]);
+        s_u[2 * i] = unit53(c[0]);
+        s_u[2 * i + 1] = unit53(c[1]);
+        const vw4_rowstat st = sb[i];
+        s_st[i] = st;
+        if (i < D) {
+            const int x = db[i];
+            const bool ok = x >= 0 && x < V;  // a malformed draft id is rejected, never dereferenced
+            s_ok[i] = ok;
+            s_p[i] = ok ? p_val(zb[(int64_t)i * V + x], st, T, x) : 0.0;
+            s_q[i] = ok ? (double)qb[(int64_t)i * V + x] : 0.0;
+        }
     }
     __syncthreads();
     ProblemState ps;
     ps.flags = 0;
     ps.bad = false;
     for (int i = 0; i <= D; ++i) {
-        const uint32_t f = sb[i].flags;
+        const uint32_t f = s_st[i].flags;
         if (f & VW4_FLAG_NONFINITE) ps.bad = true;
         if (f & VW4_FLAG_TOPP_TIE) ps.flags |= VW4_FLAG_TOPP_TIE;
     }
     ps.k = D;
     if (ps.bad) return ps;
     for (int i = 0; i < D; ++i) {
-        const int x = db[i];
-        if (x < 0 || x >= V) { ps.k = i; break; }  // malformed draft id: rejected, never dereferenced
-        const double pi = p_of(zb + (int64_t)i * V, sb[i], T, x);
-        const double qi = (double)qb[(int64_t)i * V + x];
-        const double u = s_u[2 * i];
+        if (!s_ok[i]) { ps.k = i; break; }
+        const double pi = s_p[i], qi = s_q[i], u = s_u[2 * i];
         if (qi > 0.0 && fabs(u - pi / qi) < 1e-5) ps.flags |= VW4_FLAG_ACCEPT_TIE;
         if (!(u * qi < pi)) { ps.k = i; break; }
     }
@@ -197,13 +214,25 @@ __device__ __forceinline__ AcceptPart chunk_sums(const float* __restrict__ zk, c
                                                  int* shi) {
     double sr = 0.0, sp = 0.0;
     int lr = -1, lp = -1;
-    for (int j = c0 + threadIdx.x; j < c1; j += NT) {
-        const double pj = p_of(zk, sk, T, j);
-        const double rj = qk ? fmax(0.0, pj - (double)qk[j]) : pj;
-        sr += rj;
-        sp += pj;
-        if (rj > 0.0) lr = j;
-        if (pj > 0.0) lp = j;
+    for (int base = c0; base < c1; base += NT * AU) {
+        float zv[AU], qv[AU];
+#pragma unroll
+        for (int u = 0; u < AU; ++u) {
+            const int j = base + u * NT + threadIdx.x;
+            zv[u] = (j < c1) ? zk[j] : 0.0f;
+            qv[u] = (qk && j < c1) ? qk[j] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < AU; ++u) {
+            const int j = base + u * NT + threadIdx.x;
+            if (j >= c1) break;
+            const double pj = p_val(zv[u], sk, T, j);
+            const double rj = qk ? fmax(0.0, pj - (double)qv[u]) : pj;
+            sr += rj;
+            sp += pj;
+            if (rj > 0.0) lr = j;
+            if (pj > 0.0) lp = j;
+        }
     }
     AcceptPart a;
     a.r = blk_sum<NT>(sr, sh);
@@ -252,20 +281,40 @@ __device__ void finish_problem(const float* __restrict__ zk, const vw4_rowstat& 
         const int a0 = wc * chunk, a1 = min(V, a0 + chunk);
         const int per = (a1 - a0 + NT - 1) / NT;
         const int j0 = a0 + threadIdx.x * per, j1 = min(a1, j0 + per);
+        // this thread's residual masses, computed once (runs of up to AU per pass)
         double mine = 0.0;
-        for (int j = j0; j < j1; ++j) {
-            const double pj = p_of(zk, sk, T, j);
-            mine += resid ? fmax(0.0, pj - (double)qk[j]) : pj;
+        for (int t0 = j0; t0 < j1; t0 += AU) {
+            float zv[AU], qv[AU];
+#pragma unroll
+            for (int u = 0; u < AU; ++u) {
+                zv[u] = (t0 + u < j1) ? zk[t0 + u] : 0.0f;
+                qv[u] = (resid && t0 + u < j1) ? qk[t0 + u] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < AU; ++u) {
+                if (t0 + u >= j1) break;
+                const double pj = p_val(zv[u], sk, T, t0 + u);
+                mine += resid ? fmax(0.0, pj - (double)qv[u]) : pj;
+            }
         }
         double run = before + blk_prefix_excl<NT>(mine, sh);
         int cand = 0x7fffffff;
         double cp = 0.0, cc = 0.0;
-        for (int j = j0; j < j1; ++j) {
-            const double pj = p_of(zk, sk, T, j);
-            const double rj = resid ? fmax(0.0, pj - (double)qk[j]) : pj;
-            const double nxt = run + rj;
-            if (nxt > target) { cand = j; cp = run; cc = nxt; break; }
-            run = nxt;
+        for (int t0 = j0; t0 < j1 && cand == 0x7fffffff; t0 += AU) {
+            float zv[AU], qv[AU];
+#pragma unroll
+            for (int u = 0; u < AU; ++u) {
+                zv[u] = (t0 + u < j1) ? zk[t0 + u] : 0.0f;
+                qv[u] = (resid && t0 + u < j1) ? qk[t0 + u] : 0.0f;
+            }
+            for (int u = 0; u < AU; ++u) {
+                if (t0 + u >= j1) break;
+                const double pj = p_val(zv[u], sk, T, t0 + u);
+                const double rj = resid ? fmax(0.0, pj - (double)qv[u]) : pj;
+                const double nxt = run + rj;
+                if (nxt > target) { cand = t0 + u; cp = run; cc = nxt; break; }
+                run = nxt;
+            }
         }
         int best = cand;
         for (int off = 32; off > 0; off >>= 1) best = min(best, __shfl_xor(best, off, 64));
@@ -322,6 +371,7 @@ struct AcceptArgs {
     int32_t* out_nacc;
     uint32_t* out_flags;
     AcceptPart* parts;
+    ProblemState* states;  // per problem, written by workgroup 0 of the chunk kernel
 };
 
 __device__ __forceinline__ void write_bad(const AcceptArgs& a, int64_t b) {
@@ -340,6 +390,7 @@ __global__ __launch_bounds__(NT) void accept_chunk_kernel(AcceptArgs a) {
     __shared__ int shi[8];
     __shared__ double s_u[2 * (AMAXD + 1)];
     __shared__ AcceptPart s_part;
+    __shared__ vw4_rowstat s_st[AMAXD + 1];
     const int64_t b = blockIdx.x;
     const int w = blockIdx.y;
     const float* zb = a.logits + b * a.lstride;
@@ -347,19 +398,23 @@ __global__ __launch_bounds__(NT) void accept_chunk_kernel(AcceptArgs a) {
     const float* qb = a.q ? a.q + b * a.qstride : nullptr;
     const int32_t* db = a.draft + b * a.D;
     const double T = (double)a.temperature;
-    const ProblemState ps = problem_state<NT>(zb, sb, qb, db, a.D, a.V, T, a.seed, a.step0 + (uint64_t)b, s_u);
+    const ProblemState ps =
+        problem_state<NT>(zb, sb, qb, db, a.D, a.V, T, a.seed, a.step0 + (uint64_t)b, s_u, s_st);
     if (ps.bad) {
         if (w == 0) write_bad(a, b);
         return;
     }
     const int k = ps.k;
     const float* zk = zb + (int64_t)k * a.V;
-    const vw4_rowstat sk = sb[k];
+    const vw4_rowstat sk = s_st[k];
     const float* qk = (k < a.D) ? qb + (int64_t)k * a.V : nullptr;
     const int c0 = w * a.chunk, c1 = min(a.V, c0 + a.chunk);
     const AcceptPart part = chunk_sums<NT>(zk, sk, qk, T, c0, c1, sh, shi);
     if (a.P > 1) {
-        if (threadIdx.x == 0) a.parts[b * a.P + w] = part;
+        if (threadIdx.x == 0) {
+            a.parts[b * a.P + w] = part;
+            if (w == 0) a.states[b] = ps;
+        }
         return;
     }
     if (threadIdx.x == 0) s_part = part;
@@ -381,13 +436,26 @@ __global__ __launch_bounds__(NT) void accept_finish_kernel(AcceptArgs a) {
     const float* qb = a.q ? a.q + b * a.qstride : nullptr;
     const int32_t* db = a.draft + b * a.D;
     const double T = (double)a.temperature;
-    const ProblemState ps = problem_state<NT>(zb, sb, qb, db, a.D, a.V, T, a.seed, a.step0 + (uint64_t)b, s_u);
-    if (ps.bad) return;  // outputs written by the chunk kernel
+    __shared__ ProblemState s_ps;
+    __shared__ vw4_rowstat s_sk;
+    // the accept decisions were taken by the chunk kernel; only the residual
+    // row's uniform is needed here
+    if (threadIdx.x == 0) s_ps = a.states[b];
     for (int c = threadIdx.x; c < a.P; c += NT) sp[c] = a.parts[b * a.P + c];
     __syncthreads();
+    const ProblemState ps = s_ps;
+    if (ps.bad) return;  // outputs written by the chunk kernel
     const int k = ps.k;
+    if (threadIdx.x == 0) {
+        uint64_t c[4] = {a.step0 + (uint64_t)b, (uint64_t)k, 0, 0};
+        philox4x64_10(a.seed, 0, c);
+        s_u[2 * k] = unit53(c[0]);
+        s_u[2 * k + 1] = unit53(c[1]);
+        s_sk = sb[k];
+    }
+    __syncthreads();
     const float* zk = zb + (int64_t)k * a.V;
-    const vw4_rowstat sk = sb[k];
+    const vw4_rowstat sk = s_sk;
     const float* qk = (k < a.D) ? qb + (int64_t)k * a.V : nullptr;
     finish_problem<NT>(zk, sk, qk, db, sp, a.P, a.chunk, a.D, a.V, T, ps, s_u, a.out_tokens + b * (a.D + 1),
                        a.out_nacc + b, a.out_flags + b, sh, shi);
@@ -427,6 +495,7 @@ int spec_accept(const float* logits, int64_t logits_bstride, const vw4_rowstat* 
     a.chunk = L.chunk; a.P = L.P;
     a.out_tokens = out_tokens; a.out_nacc = out_n_acc; a.out_flags = out_flags;
     a.parts = (AcceptPart*)((char*)ws + L.off_part);
+    a.states = (ProblemState*)((char*)ws + L.off_state);
     hipStream_t st = (hipStream_t)stream;
     const dim3 grid((unsigned)B, (unsigned)L.P);
     if (L.threads == 64) {

@@ -156,6 +156,19 @@ __device__ __forceinline__ double block_suffix_excl_f64(double v, double* sh) {
     return ex + later;
 }
 
+// Elements base + u*VT + threadIdx.x (u < VU) of a chunk ending at c1, loaded
+// together before any is used: one memory latency per tile instead of one per
+// element.  Out-of-range slots are left unread.
+constexpr int VU = 16;
+template <typename T>
+__device__ __forceinline__ void load_tile(const T* __restrict__ src, int base, int c1, T (&v)[VU]) {
+#pragma unroll
+    for (int u = 0; u < VU; ++u) {
+        const int j = base + u * VT + threadIdx.x;
+        v[u] = (j < c1) ? src[j] : T(0);
+    }
+}
+
 // Row max / argmax (lowest index) / non-finite / min over the P chunk parts.
 struct RowMax {
     float m, mn;
@@ -263,11 +276,17 @@ __global__ __launch_bounds__(VT) void vs_chunk_kernel(const float* __restrict__ 
     float lm = -INFINITY, lmn = INFINITY;
     int li = 0x7fffffff;
     uint32_t bad = 0;
-    for (int j = c0 + tid; j < c1; j += VT) {
-        const float v = z[j];
-        if (!isfinite(v)) bad = 1;
-        lmn = fminf(lmn, v);
-        if (v > lm || (v == lm && j < li)) { lm = v; li = j; }
+    for (int base = c0; base < c1; base += VT * VU) {
+        float v[VU];
+        load_tile(z, base, c1, v);
+#pragma unroll
+        for (int u = 0; u < VU; ++u) {
+            const int j = base + u * VT + tid;
+            if (j >= c1) break;
+            if (!isfinite(v[u])) bad = 1;
+            lmn = fminf(lmn, v[u]);
+            if (v[u] > lm || (v[u] == lm && j < li)) { lm = v[u]; li = j; }
+        }
     }
     for (int off = 32; off > 0; off >>= 1) {
         const float om = __shfl_xor(lm, off, 64);
@@ -293,13 +312,19 @@ __global__ __launch_bounds__(VT) void vs_chunk_kernel(const float* __restrict__ 
             __syncthreads();
         }
         double es = 0.0;
-        for (int j = c0 + tid; j < c1; j += VT) {
-            const float v = z[j];
-            const double e = exp(((double)v - (double)m_w) / T);
-            es += e;
-            if (hist_on) {
-                rv.e[j] = e;
-                atomicAdd(&hist[f32_key(v) >> (32 - L1BITS)], e);
+        for (int base = c0; base < c1; base += VT * VU) {
+            float v[VU];
+            load_tile(z, base, c1, v);
+#pragma unroll
+            for (int u = 0; u < VU; ++u) {
+                const int j = base + u * VT + tid;
+                if (j >= c1) break;
+                const double e = exp(((double)v[u] - (double)m_w) / T);
+                es += e;
+                if (hist_on) {
+                    rv.e[j] = e;
+                    atomicAdd(&hist[f32_key(v[u]) >> (32 - L1BITS)], e);
+                }
             }
         }
         E_w = block_sum_f64(es, shd);
@@ -332,15 +357,14 @@ __global__ __launch_bounds__(CB) void vs_combine_kernel(float temperature, char*
     }
     const double* src = (LEVEL == 1) ? rv.h1p : rv.h2p;
     double* dst = (LEVEL == 1) ? rv.h1 : rv.h2;
+    // all P partials of this bin in flight at once (P <= VMAXP), then summed in order
+    double v[VMAXP];
+#pragma unroll
+    for (int i = 0; i < VMAXP; ++i) v[i] = (i < L.P) ? src[(int64_t)i * HB + b] : 0.0;
     double acc = 0.0;
-    for (int k0 = 0; k0 < L.P; k0 += 16) {
-        double v[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = (k0 + i < L.P) ? src[(int64_t)(k0 + i) * HB + b] : 0.0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if (k0 + i < L.P) acc += (LEVEL == 1) ? f[k0 + i] * v[i] : v[i];
-    }
+    for (int i = 0; i < VMAXP; ++i)
+        if (i < L.P) acc += (LEVEL == 1) ? f[i] * v[i] : v[i];
     dst[b] = acc;
 }
 
@@ -368,10 +392,17 @@ __global__ __launch_bounds__(VT) void vs_level2_kernel(const float* __restrict__
     for (int b = tid; b < HB; b += VT) hist[b] = 0.0;
     __syncthreads();
     if (b1 >= 0) {
-        for (int j = c0 + tid; j < c1; j += VT) {
-            const uint32_t k = f32_key(z[j]);
-            if ((k >> (32 - L1BITS)) == (uint32_t)b1)
-                atomicAdd(&hist[(k >> L3BITS) & (HB - 1)], rv.e[j] * fw);
+        for (int base = c0; base < c1; base += VT * VU) {
+            float v[VU];
+            double ev[VU];
+            load_tile(z, base, c1, v);
+            load_tile((const double*)rv.e, base, c1, ev);
+#pragma unroll
+            for (int u = 0; u < VU; ++u) {
+                if (base + u * VT + tid >= c1) break;
+                const uint32_t k = f32_key(v[u]);
+                if ((k >> (32 - L1BITS)) == (uint32_t)b1) atomicAdd(&hist[(k >> L3BITS) & (HB - 1)], ev[u] * fw);
+            }
         }
     }
     __syncthreads();
@@ -410,11 +441,19 @@ __global__ __launch_bounds__(VT) void vs_level3_kernel(const float* __restrict__
     const uint32_t prefix = (b1 >= 0 && b2 >= 0) ? (((uint32_t)b1 << L2BITS) | (uint32_t)b2) : 0x3fffffu;
     double sa = 0.0;
     uint32_t na = 0;
-    for (int j = c0 + tid; j < c1; j += VT) {
-        const uint32_t k = f32_key(z[j]);
-        const uint32_t hi = k >> L3BITS;
-        if (hi > prefix) { sa += rv.e[j] * fw; ++na; }
-        else if (hi == prefix) atomicAdd(&cnt[k & (HB3 - 1)], 1u);
+    for (int base = c0; base < c1; base += VT * VU) {
+        float v[VU];
+        double ev[VU];
+        load_tile(z, base, c1, v);
+        load_tile((const double*)rv.e, base, c1, ev);
+#pragma unroll
+        for (int u = 0; u < VU; ++u) {
+            if (base + u * VT + tid >= c1) break;
+            const uint32_t k = f32_key(v[u]);
+            const uint32_t hi = k >> L3BITS;
+            if (hi > prefix) { sa += ev[u] * fw; ++na; }
+            else if (hi == prefix) atomicAdd(&cnt[k & (HB3 - 1)], 1u);
+        }
     }
     sa = block_sum_f64(sa, shd);
     na = block_sum_u32(na, shu);
@@ -476,12 +515,12 @@ __global__ __launch_bounds__(HB3) void vs_finish_kernel(float temperature, float
     const uint32_t prefix = ss[0].pad;
     // level-3 bin b (thread b): one float value, mass = count * e(value)
     uint32_t c = 0;
-    for (int k0 = 0; k0 < L.P; k0 += 16) {
-        uint32_t v[16];
+    {
+        uint32_t v[VMAXP];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = (k0 + i < L.P) ? rv.c3[(int64_t)(k0 + i) * HB3 + tid] : 0u;
+        for (int i = 0; i < VMAXP; ++i) v[i] = (i < L.P) ? rv.c3[(int64_t)i * HB3 + tid] : 0u;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) c += v[i];
+        for (int i = 0; i < VMAXP; ++i) c += v[i];
     }
     const float zb = key_f32((prefix << L3BITS) | (uint32_t)tid);
     const double eb = (c && prefix != 0x3fffffu) ? exp(((double)zb - (double)mx.m) / T) : 0.0;

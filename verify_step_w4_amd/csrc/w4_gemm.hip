@@ -36,6 +36,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Constant address space: uniform loads through it become scalar (SGPR) loads.
 typedef const __attribute__((address_space(4))) uint32_t cu32;
 constexpr float GEMM_OFFSET = 136.0f;  // bf16 magic 128 plus the code bias 8
+constexpr int PF = 4;                  // weight groups in flight per lane
 
 // Marks an address as wavefront-uniform so that loads through it are scalar.
 __device__ __forceinline__ cu32* uniform_ptr(cu32* p) {
@@ -51,13 +52,12 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            false);
 }
 
-// (v & mask) | magic in one VOP3 instruction.  gfx9 VOP3 encodings take no
-// literal constants and at most one SGPR, so the mask comes in an SGPR and
-// the magic in a VGPR; the compiler would otherwise emit a v_and/v_or pair.
+// (v & mask) | magic in one instruction: gfx950's three-input bitwise op with
+// truth table 0xEA = (A & B) | C.  gfx9 VOP3 encodings take no literal
+// constants and at most one SGPR, so the mask comes in an SGPR and the magic
+// in a VGPR (the compiler would otherwise emit a v_and / v_or pair).
 __device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask_s, uint32_t magic_v) {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "s"(mask_s), "v"(magic_v));
-    return r;
+    return __builtin_amdgcn_bitop3_b32(v, mask_s, magic_v, 0xEA);
 }
 
 template <int M>
@@ -68,6 +68,31 @@ __device__ __forceinline__ void gemm_dword(uint32_t word, cu32* const* xg, int x
         const uint32_t pair = and_or(word >> (4 * i), kmask, kmagic);
 #pragma unroll
         for (int m = 0; m < M; ++m) ag[m] = dot2_bf16(pair, xg[m][xoff + i], ag[m]);
+    }
+}
+
+// One 64-element group of one row per lane: M partial sums started at
+// -136 * sum(x) (xsg[m * ng]), 8 code dwords, then acc += scale * partial.
+// Advances the activation pointers by one group.
+template <int M>
+__device__ __forceinline__ void gemm_group(u32x4 c0, u32x4 c1, uint32_t sbits, cu32** xp, const float* xsg, int ng,
+                                           uint32_t kmask, uint32_t magic_v, float (&acc)[M]) {
+    float ag[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) ag[m] = xsg[m * ng];
+    gemm_dword<M>(c0.x, xp, 0, kmask, magic_v, ag);
+    gemm_dword<M>(c0.y, xp, 4, kmask, magic_v, ag);
+    gemm_dword<M>(c0.z, xp, 8, kmask, magic_v, ag);
+    gemm_dword<M>(c0.w, xp, 12, kmask, magic_v, ag);
+    gemm_dword<M>(c1.x, xp, 16, kmask, magic_v, ag);
+    gemm_dword<M>(c1.y, xp, 20, kmask, magic_v, ag);
+    gemm_dword<M>(c1.z, xp, 24, kmask, magic_v, ag);
+    gemm_dword<M>(c1.w, xp, 28, kmask, magic_v, ag);
+    const float sc = f16_bits_to_f32((uint16_t)sbits);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        acc[m] = fmaf(sc, ag[m], acc[m]);
+        xp[m] += 32;
     }
 }
 
@@ -125,42 +150,41 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[m] = 0.0f;
 
-    const u32x4* wp = wpk + ((int64_t)t * G + g0) * 128 + lane;
-    const uint16_t* sp = spk + ((int64_t)t * G + g0) * 64 + lane;
+    // PF groups in flight per lane, each in its own registers: the main loop
+    // consumes buffer i and refills it with the group PF further on (clamped to
+    // the slice's last group, so every load address is valid and the loop body
+    // has no branches); the last < PF groups are consumed after the loop.
+    const u32x4* wbase = wpk + (int64_t)t * G * 128 + lane;
+    const uint16_t* sbase = spk + (int64_t)t * G * 64 + lane;
+    const int glast = g1 - 1;
     if (g0 < g1) {
-        u32x4 c0 = __builtin_nontemporal_load(wp);
-        u32x4 c1 = __builtin_nontemporal_load(wp + 64);
-        uint16_t sr = sp[0];
-        for (int g = g0; g < g1; ++g) {
-            u32x4 n0 = c0, n1 = c1;
-            uint16_t nsr = sr;
-            if (g + 1 < g1) {
-                n0 = __builtin_nontemporal_load(wp + 128);
-                n1 = __builtin_nontemporal_load(wp + 192);
-                nsr = sp[64];
-            }
-            float ag[M];
+        u32x4 b0[PF], b1[PF];
+        uint32_t bs[PF];  // fp16 scale bits, one register each (packing two would force early waits)
 #pragma unroll
-            for (int m = 0; m < M; ++m) ag[m] = xs[m * ng + (g - gw0)];
-            gemm_dword<M>(c0.x, xp, 0, kmask, magic_v, ag);
-            gemm_dword<M>(c0.y, xp, 4, kmask, magic_v, ag);
-            gemm_dword<M>(c0.z, xp, 8, kmask, magic_v, ag);
-            gemm_dword<M>(c0.w, xp, 12, kmask, magic_v, ag);
-            gemm_dword<M>(c1.x, xp, 16, kmask, magic_v, ag);
-            gemm_dword<M>(c1.y, xp, 20, kmask, magic_v, ag);
-            gemm_dword<M>(c1.z, xp, 24, kmask, magic_v, ag);
-            gemm_dword<M>(c1.w, xp, 28, kmask, magic_v, ag);
-#pragma unroll
-            for (int m = 0; m < M; ++m) xp[m] += 32;
-            const float sc = f16_bits_to_f32(sr);
-#pragma unroll
-            for (int m = 0; m < M; ++m) acc[m] = fmaf(sc, ag[m], acc[m]);
-            c0 = n0;
-            c1 = n1;
-            sr = nsr;
-            wp += 128;
-            sp += 64;
+        for (int i = 0; i < PF; ++i) {
+            const int gi = min(g0 + i, glast);
+            b0[i] = __builtin_nontemporal_load(wbase + (int64_t)gi * 128);
+            b1[i] = __builtin_nontemporal_load(wbase + (int64_t)gi * 128 + 64);
+            bs[i] = sbase[(int64_t)gi * 64];
         }
+        int g = g0;
+        for (; g + PF <= g1; g += PF) {
+#pragma unroll
+            for (int i = 0; i < PF; ++i) {
+                gemm_group<M>(b0[i], b1[i], bs[i], xp, xs + (g + i - gw0), ng, kmask, magic_v, acc);
+                const int gn = min(g + i + PF, glast);
+                // keep the refill right after its buffer's last use: the
+                // scheduler would otherwise sink all refills to the loop end
+                __builtin_amdgcn_sched_barrier(0);
+                b0[i] = __builtin_nontemporal_load(wbase + (int64_t)gn * 128);
+                b1[i] = __builtin_nontemporal_load(wbase + (int64_t)gn * 128 + 64);
+                bs[i] = sbase[(int64_t)gn * 64];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < PF - 1; ++i)
+            if (g + i < g1) gemm_group<M>(b0[i], b1[i], bs[i], xp, xs + (g + i - gw0), ng, kmask, magic_v, acc);
     }
 
     // Reduce the S_wg slices of this workgroup in slice order.
