@@ -187,6 +187,54 @@ VW4_API int spec_accept(const float* logits, int64_t logits_bstride, const vw4_r
                 float temperature, uint64_t seed, uint64_t step0, int32_t* out_tokens, int32_t* out_n_acc,
                 uint32_t* out_flags, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Decoder-layer calls of the verify forward (hazakura.dev mtplx page,
+ * "4層のアーキテクチャ" Layer 1: target and drafter share one checkpoint and a
+ * KV cache; gist.science BaseRT summary, "メソドロジー": decode-step operator
+ * sequences fused so that short kernels do not pay extra round trips, and
+ * attention computed tile by tile with an online softmax).  All tensors bf16
+ * unless stated; M <= 8 verify rows at positions L .. L+M-1.
+ *
+ * Split GEMM outputs.  w4_skinny_gemm_partials writes the GEMM as S fp32
+ * partial sums part[S][M][ldp] (S and ldp from vw4_gemm_partials_layout; the
+ * output is the sum over S in slice order, and S == 1 means part[0] is the
+ * product itself).  The layer calls below take such partials and fold the
+ * reduction into their own pass, so no separate reduction launch is needed.
+ * ------------------------------------------------------------------------ */
+VW4_API int vw4_gemm_partials_layout(int32_t M, int32_t N, int32_t K, int32_t* S, int64_t* ldp);
+
+VW4_API int w4_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w_packed,
+                                    const uint16_t* scales_packed, float* part, int32_t M, int32_t N, int32_t K,
+                                    void* stream);
+
+/* resid[M][D] (bf16, in/out) += sum_s part[s][m][d] (fp32; part may be NULL to
+ * skip the add), rounded to bf16; then h = bf16(rmsnorm(resid) * gamma):
+ * h = r / sqrt(mean_d(r^2) + eps) * gamma.  D <= 65536. */
+VW4_API int vw4_add_rmsnorm(uint16_t* resid, const float* part, int32_t S, int64_t ldp, const uint16_t* gamma,
+                            float eps, int32_t M, int32_t D, uint16_t* h, void* stream);
+
+/* From the fused q|k|v projection (partials of [M][(nq + 2 nkv) * hd]): rotary
+ * embedding (rotate-half, base theta, position L + m) of q and k; q -> q_out
+ * [M][nq][hd]; k and v appended to the caches Kc, Vc [nkv][Lmax][hd] at
+ * positions L + m.  hd even, L + M <= Lmax. */
+VW4_API int vw4_rope_kv_append(const float* part, int32_t S, int64_t ldp, int32_t M, int32_t nq, int32_t nkv,
+                               int32_t hd, int32_t L, float theta, uint16_t* q_out, uint16_t* Kc, uint16_t* Vc,
+                               int64_t Lmax, void* stream);
+
+/* a[M][F] = bf16(silu(g) * u) with g = part[.][m][0:F], u = part[.][m][F:2F]
+ * (fused gate|up projection), silu(g) = g / (1 + exp(-g)). */
+VW4_API int vw4_swiglu(const float* part, int32_t S, int64_t ldp, int32_t M, int32_t F, uint16_t* a, void* stream);
+
+/* Grouped-query decode attention for M verify rows: query head h reads KV head
+ * h / (nq / nkv); row m attends to positions 0 .. L + m of the cache (causal
+ * inside the verify rows); softmax(q k^T / sqrt(hd)) v with fp32 accumulation.
+ * q [M][nq][hd]; Kc, Vc [nkv][Lmax][hd]; out [M][nq * hd] bf16.  hd == 128,
+ * nq % nkv == 0, (nq / nkv) * M <= 64.  Workspace: vw4_attn_workspace_bytes. */
+VW4_API size_t vw4_attn_workspace_bytes(int32_t M, int32_t nq, int32_t nkv, int32_t hd, int64_t ctx);
+VW4_API int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_t* Vc, int64_t Lmax, int64_t L,
+                            int32_t M, int32_t nq, int32_t nkv, int32_t hd, uint16_t* out, void* ws, size_t ws_bytes,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -66,6 +66,10 @@ def lib():
         L.oracle_f32_to_f16.restype = ctypes.c_uint16
         L.oracle_f16_value.argtypes = [ctypes.c_uint16]
         L.oracle_f16_value.restype = _F64
+        L.oracle_bf16_round.argtypes = [_F64]
+        L.oracle_bf16_round.restype = ctypes.c_uint16
+        L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_value.restype = _F64
         L.oracle_w4_quantize.argtypes = [_P, _I64, _I64, _P, _P]
         L.oracle_w4_code.argtypes = [_P, _I64, _I64, _I64]
         L.oracle_w4_code.restype = ctypes.c_int
@@ -103,6 +107,19 @@ def f32_to_f16_bits(x: float) -> int:
 
 def f16_value(bits: int) -> float:
     return float(lib().oracle_f16_value(int(bits)))
+
+
+def bf16_round(v) -> np.ndarray:
+    """Round float64 values to bfloat16 bits (one RNE rounding)."""
+    a = np.asarray(v, dtype=np.float64)
+    f = lib().oracle_bf16_round
+    return np.array([f(float(x)) for x in a.reshape(-1)], dtype=np.uint16).reshape(a.shape)
+
+
+def bf16_value(bits) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16)
+    f = lib().oracle_bf16_value
+    return np.array([f(int(x)) for x in b.reshape(-1)], dtype=np.float64).reshape(b.shape)
 
 
 # --------------------------------------------------------------------------

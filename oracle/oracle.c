@@ -87,6 +87,28 @@ EXPORT uint16_t oracle_f32_to_f16(float f) {
 
 EXPORT double oracle_f16_value(uint16_t h) { return f16_value(h); }
 
+/* binary64 -> bfloat16 (1 sign, 8 exponent bits with bias 127, 7 fraction
+ * bits), one rounding to nearest, ties to even; overflow -> inf. */
+EXPORT uint16_t oracle_bf16_round(double v) {
+    uint16_t sign = (uint16_t)(signbit(v) ? 0x8000u : 0u);
+    double x = fabs(v);
+    if (isnan(v)) return (uint16_t)(sign | 0x7fc0u);
+    if (x == 0.0) return sign;
+    if (x < ldexp(1.0, -126)) {                    /* subnormal, ulp 2^-133 */
+        double q = rint(x * ldexp(1.0, 133));      /* 0 .. 128 (128 = min normal) */
+        return (uint16_t)(sign | (uint16_t)q);
+    }
+    int e;
+    (void)frexp(x, &e);
+    e -= 1;                                        /* x in [2^e, 2^(e+1)) */
+    double m = rint(ldexp(x, 7 - e));              /* 128 .. 256 */
+    if (m == 256.0) { m = 128.0; e += 1; }
+    if (e + 127 >= 255) return (uint16_t)(sign | 0x7f80u);
+    return (uint16_t)(sign | (uint16_t)((e + 127) << 7) | (uint16_t)(m - 128.0));
+}
+
+EXPORT double oracle_bf16_value(uint16_t h) { return bf16_value(h); }
+
 /* ------------------------------------------------------------------------ */
 /* (a1) W4 weight format: symmetric int4, group 64 along K, fp16 scales.    */
 /* Reading (the pages say only "4-bit", [mtplx/4層] Layer 0): codes in       */

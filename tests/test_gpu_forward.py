@@ -1,0 +1,169 @@
+"""The whole verify forward (a2-a9, a11) on the GPU.
+
+* End to end against the oracle on a small decoder (2 layers, d=256, GQA 4/2
+  heads of 128, FFN 512, V=1000) with identical synthetic weights, KV context
+  and inputs; the oracle composes its own fp64 ops with bf16 rounding at the
+  same points.  bf16 rounding flips (one ulp, 2^-8) propagate through the
+  layers, so the logits are compared with a looser bound than the GEMM's.
+* Verify row i of an M-row pass equals the autoregressive M=1 step at position
+  L + i (teacher forced: rows 0..i-1 already in the KV cache), bit for bit,
+  at the full layer width.  This is the property behind "the verify pass
+  changes nothing but speed".
+* Bitwise determinism of the verify step.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from verify_step_w4_amd import binding as B
+from verify_step_w4_amd import synth
+from verify_step_w4_amd.model import DENSE_27B, Decoder, VerifyStep, W4Linear
+
+from helpers import dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+TINY = dict(d=256, nq=4, nkv=2, hd=128, F=512, layers=2, V=1000, eps=1e-6, theta=10000.0)
+
+
+def _host_model(cfg, seed):
+    g = synth.rng(seed)
+    d, nq, nkv, hd, F, V = (cfg[k] for k in ("d", "nq", "nkv", "hd", "F", "V"))
+    layers = []
+    for _ in range(cfg["layers"]):
+        layers.append(dict(qkv=synth.normal_f32(g, ((nq + 2 * nkv) * hd, d), 0.02),
+                           o=synth.normal_f32(g, (d, nq * hd), 0.02),
+                           gate_up=synth.normal_f32(g, (2 * F, d), 0.02),
+                           down=synth.normal_f32(g, (d, F), 0.02),
+                           g1=synth.f32_to_bf16_bits(1 + synth.normal_f32(g, (d,), 0.02)),
+                           g2=synth.f32_to_bf16_bits(1 + synth.normal_f32(g, (d,), 0.02))))
+    return dict(layers=layers, final_gamma=synth.f32_to_bf16_bits(1 + synth.normal_f32(g, (d,), 0.02)),
+                lm_head=synth.normal_f32(g, (V, d), 0.02))
+
+
+def _device_weights(hm):
+    layers = []
+    for l in hm["layers"]:
+        layers.append({k: (W4Linear.from_fp32(dev(l[k])) if k not in ("g1", "g2") else dev(l[k]))
+                       for k in l})
+    return dict(layers=layers, final_gamma=dev(hm["final_gamma"]), lm_head=W4Linear.from_fp32(dev(hm["lm_head"])))
+
+
+def _oracle_forward(cfg, hm, Kc, Vc, x, L):
+    """Oracle composition of the layer ops; Kc/Vc: per-layer uint16 arrays (modified)."""
+    d, nq, nkv, hd, F, eps = (cfg[k] for k in ("d", "nq", "nkv", "hd", "F", "eps"))
+    M = x.shape[0]
+    q4 = {}
+    for li, l in enumerate(hm["layers"]):
+        q4[li] = {k: oracle.w4_quantize(l[k]) for k in ("qkv", "o", "gate_up", "down")}
+    lm = oracle.w4_quantize(hm["lm_head"])
+    resid = x.copy()
+    for li, l in enumerate(hm["layers"]):
+        Q = q4[li]
+        h = oracle.bf16_round(oracle.rmsnorm(resid, l["g1"], eps))
+        qkv = oracle.w4_gemm(h, *Q["qkv"])
+        q = np.zeros((M, nq, hd))
+        for m in range(M):
+            for hh in range(nq):
+                q[m, hh] = oracle.bf16_value(oracle.bf16_round(oracle.rope(qkv[m, hh * hd:(hh + 1) * hd], L + m)))
+            for hh in range(nkv):
+                kk = oracle.rope(qkv[m, (nq + hh) * hd:(nq + hh + 1) * hd], L + m)
+                Kc[li][hh, L + m] = oracle.bf16_round(kk)
+                Vc[li][hh, L + m] = oracle.bf16_round(qkv[m, (nq + nkv + hh) * hd:(nq + nkv + hh + 1) * hd])
+        att = oracle.bf16_round(oracle.decode_attn(q, Kc[li], Vc[li], L).reshape(M, nq * hd))
+        o = oracle.w4_gemm(att, *Q["o"])
+        resid = oracle.bf16_round(oracle.bf16_value(resid) + o)
+        h = oracle.bf16_round(oracle.rmsnorm(resid, l["g2"], eps))
+        gu = oracle.w4_gemm(h, *Q["gate_up"])
+        a = oracle.bf16_round(oracle.swiglu(oracle.bf16_round(gu[:, :F]), oracle.bf16_round(gu[:, F:])))
+        dn = oracle.w4_gemm(a, *Q["down"])
+        resid = oracle.bf16_round(oracle.bf16_value(resid) + dn)
+    h = oracle.bf16_round(oracle.rmsnorm(resid, hm["final_gamma"], eps))
+    return oracle.w4_gemm(h, *lm)
+
+
+def test_forward_matches_oracle_small_decoder():
+    cfg = TINY
+    M, L = 4, 37
+    Lmax = L + M + 8
+    log("forward vs oracle, small decoder")
+    hm = _host_model(cfg, 4242)
+    dec = Decoder(cfg, M, Lmax, weights=_device_weights(hm), kv_fill=False)
+    g = synth.rng(77)
+    Kh = [synth.f32_to_bf16_bits(synth.normal_f32(g, (cfg["nkv"], Lmax, cfg["hd"]), 1.0)) for _ in range(cfg["layers"])]
+    Vh = [synth.f32_to_bf16_bits(synth.normal_f32(g, (cfg["nkv"], Lmax, cfg["hd"]), 1.0)) for _ in range(cfg["layers"])]
+    for li in range(cfg["layers"]):
+        dec.Kc[li].copy_(dev(Kh[li]))
+        dec.Vc[li].copy_(dev(Vh[li]))
+    x = synth.activations_bf16(78, M, cfg["d"])
+    import torch
+    logits = host(dec.forward(dev(x), L, M))
+    torch.cuda.synchronize()
+    ref = _oracle_forward(cfg, hm, Kh, Vh, x, L)
+    rms = np.sqrt((ref ** 2).mean(axis=1, keepdims=True))
+    rel = np.abs(logits - ref) / np.maximum(np.abs(ref), rms)
+    print(f"[forward] max rel err {rel.max():.3e}, median {np.median(rel):.3e}", flush=True)
+    assert rel.max() < 2e-2
+    assert np.median(rel) < 2e-3
+    # the KV rows the verify pass appended agree with the oracle's within bf16
+    for li in range(cfg["layers"]):
+        kg = host(dec.Kc[li])[:, L:L + M].astype(np.int32)
+        ko = Kh[li][:, L:L + M].astype(np.int32)
+        assert np.mean(kg == ko) > 0.9
+
+
+def _dense_cfg(layers, V):
+    c = dict(DENSE_27B)
+    c["layers"] = layers
+    c["V"] = V
+    return c
+
+
+def test_verify_rows_equal_autoregressive_steps():
+    import torch
+    cfg = _dense_cfg(2, 4096)
+    M, L = 4, 1000
+    Lmax = L + M + 4
+    log("verify rows == AR steps (full width, 2 layers)")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    dec = Decoder(cfg, M, Lmax, gen=gen)
+    K0 = [k.clone() for k in dec.Kc]
+    V0 = [v.clone() for v in dec.Vc]
+    x = dev(synth.activations_bf16(9, M, cfg["d"]))
+    verify = host(dec.forward(x, L, M)).copy()
+    # sequential single-row steps on a fresh copy of the cache
+    for li in range(cfg["layers"]):
+        dec.Kc[li].copy_(K0[li])
+        dec.Vc[li].copy_(V0[li])
+    for i in range(M):
+        ar = host(dec.forward(x[i:i + 1], L + i, 1))
+        assert np.array_equal(ar[0], verify[i]), f"row {i} differs"
+
+
+def test_verify_step_deterministic_and_accepts():
+    import torch
+    cfg = _dense_cfg(2, 151936)
+    M, L = 4, 512
+    Lmax = L + M + 4
+    log("verify step determinism (full width, 2 layers, V=151936)")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(6)
+    dec = Decoder(cfg, M, Lmax, gen=gen)
+    vs = VerifyStep(dec, M)
+    x = dev(synth.activations_bf16(10, M, cfg["d"]))
+    q, drafts = synth.q_and_drafts(11, M - 1, cfg["V"], 3.0, B=1)
+    qd, dd = dev(q), dev(drafts[0])
+    K0 = [k.clone() for k in dec.Kc]
+    outs = []
+    for rep in range(2):
+        for li in range(cfg["layers"]):
+            dec.Kc[li].copy_(K0[li])
+        tok, nacc, fl = vs.run(x, L, qd, dd, 0.6, 0.95, 0x5EED0004, 0)
+        torch.cuda.synchronize()
+        outs.append((host(tok).copy(), host(nacc).copy(), host(dec.logits[:M]).copy(), B.rowstats_to_numpy(vs.stats)))
+    assert np.array_equal(outs[0][2], outs[1][2])
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    assert outs[0][3].tobytes() == outs[1][3].tobytes()
+    n = int(outs[0][1][0])
+    assert 0 <= n <= M - 1 and 0 <= int(outs[0][0][0, n]) < cfg["V"]

@@ -1,0 +1,153 @@
+"""GPU parity of the decoder-layer calls (a8, a9) against the oracle on the
+same synthetic bf16/fp32 inputs.
+
+Outputs are stored as bf16, so the bar is the bf16 rounding of the exact
+value: |gpu - ref| <= 2^-8 |ref| + 1e-3 * rms(ref) (half an ulp of rounding on
+each side plus fp32 accumulation), with almost all elements bit-identical."""
+import numpy as np
+import pytest
+
+import oracle
+from verify_step_w4_amd import binding as B
+from verify_step_w4_amd import synth
+
+from helpers import dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+BF16_REL = 2.0 ** -8
+
+
+def bf16_close(gpu_bits, ref, rms_axis=-1, min_exact=0.97):
+    g = synth.bf16_bits_to_f32(gpu_bits).astype(np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = np.sqrt((ref ** 2).mean(axis=rms_axis, keepdims=True))
+    err = np.abs(g - ref)
+    assert np.all(err <= BF16_REL * np.abs(ref) + 1e-3 * rms), float((err / (np.abs(ref) + rms)).max())
+    exact = (gpu_bits == oracle.bf16_round(ref)).mean()
+    assert exact >= min_exact, exact
+
+
+def partials(seed, S, M, N, ldp, std=1.0):
+    p = synth.normal_f32(synth.rng(seed), (S, M, ldp), std)
+    return p
+
+
+@pytest.mark.parametrize("M,D,S", [(1, 5120, 1), (4, 5120, 3), (6, 1000, 2), (4, 2048, 1)])
+def test_add_rmsnorm(M, D, S):
+    import torch
+    log(f"add_rmsnorm M={M} D={D} S={S}")
+    ldp = (D + 63) // 64 * 64
+    resid = synth.activations_bf16(M + D, M, D)
+    part = partials(S + D, S, M, D, ldp, 0.5)
+    gamma = synth.f32_to_bf16_bits(1.0 + synth.normal_f32(synth.rng(3), (D,), 0.02))
+    rd, hd = dev(resid), torch.empty((M, D), dtype=torch.int16, device="cuda")
+    B.add_rmsnorm(rd, dev(part), S, ldp, dev(gamma), 1e-6, M, D, hd)
+    torch.cuda.synchronize()
+    # oracle: exact sum, one bf16 rounding, then RMSNorm of the rounded residual
+    exact = synth.bf16_bits_to_f32(resid).astype(np.float64) + part[:, :, :D].astype(np.float64).sum(axis=0)
+    r_ref_bits = oracle.bf16_round(exact)
+    bf16_close(host(rd), exact)
+    h_ref = oracle.rmsnorm(r_ref_bits, gamma, 1e-6)
+    bf16_close(host(hd), h_ref)
+
+
+def test_rmsnorm_without_add():
+    import torch
+    M, D = 3, 5120
+    resid = synth.activations_bf16(5, M, D, 2.0)
+    gamma = synth.f32_to_bf16_bits(1.0 + synth.normal_f32(synth.rng(6), (D,), 0.02))
+    rd, hd = dev(resid), torch.empty((M, D), dtype=torch.int16, device="cuda")
+    B.add_rmsnorm(rd, None, 1, D, dev(gamma), 1e-6, M, D, hd)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(rd), resid)
+    bf16_close(host(hd), oracle.rmsnorm(resid, gamma, 1e-6))
+
+
+@pytest.mark.parametrize("M,L,S", [(4, 0, 1), (4, 8191, 2), (1, 32767, 3)])
+def test_rope_kv_append(M, L, S):
+    import torch
+    nq, nkv, hd = 40, 8, 128
+    N = (nq + 2 * nkv) * hd
+    ldp = N
+    Lmax = L + M + 3
+    log(f"rope_kv M={M} L={L} S={S}")
+    part = partials(L + S, S, M, N, ldp)
+    qd = torch.empty((M, nq, hd), dtype=torch.int16, device="cuda")
+    Kc = torch.zeros((nkv, Lmax, hd), dtype=torch.int16, device="cuda")
+    Vc = torch.zeros((nkv, Lmax, hd), dtype=torch.int16, device="cuda")
+    B.rope_kv_append(dev(part), S, ldp, M, nq, nkv, hd, L, 10000.0, qd, Kc, Vc, Lmax)
+    torch.cuda.synchronize()
+    x = part.astype(np.float64).sum(axis=0)          # exact sum of the partials
+    q_ref = np.zeros((M, nq, hd))
+    k_ref = np.zeros((M, nkv, hd))
+    for m in range(M):
+        for h in range(nq):
+            q_ref[m, h] = oracle.rope(x[m, h * hd:(h + 1) * hd], L + m)
+        for h in range(nkv):
+            k_ref[m, h] = oracle.rope(x[m, (nq + h) * hd:(nq + h + 1) * hd], L + m)
+    v_ref = x[:, (nq + nkv) * hd:].reshape(M, nkv, hd)
+    bf16_close(host(qd), q_ref)
+    Kh, Vh = host(Kc), host(Vc)
+    bf16_close(np.stack([Kh[:, L + m] for m in range(M)]), k_ref)
+    bf16_close(np.stack([Vh[:, L + m] for m in range(M)]), v_ref)
+    # nothing else of the cache is touched
+    mask = np.ones(Lmax, bool)
+    mask[L:L + M] = False
+    assert not Kh[:, mask].any() and not Vh[:, mask].any()
+
+
+@pytest.mark.parametrize("M,F,S", [(4, 17408, 2), (1, 768, 1), (6, 300, 3)])
+def test_swiglu(M, F, S):
+    import torch
+    log(f"swiglu M={M} F={F} S={S}")
+    ldp = (2 * F + 63) // 64 * 64
+    part = partials(F + S, S, M, 2 * F, ldp, 1.5)
+    ad = torch.empty((M, F), dtype=torch.int16, device="cuda")
+    B.swiglu(dev(part), S, ldp, M, F, ad)
+    torch.cuda.synchronize()
+    x = part.astype(np.float64).sum(axis=0)
+    g, u = x[:, :F], x[:, F:2 * F]
+    ref = g / (1.0 + np.exp(-g)) * u
+    bf16_close(host(ad), ref)
+
+
+def _attn_case(M, nq, nkv, L, seed):
+    import torch
+    hd = 128
+    Lmax = L + M + 5
+    q = synth.activations_bf16(seed, M * nq, hd).reshape(M, nq, hd)
+    Kc = synth.activations_bf16(seed + 1, nkv * Lmax, hd).reshape(nkv, Lmax, hd)
+    Vc = synth.activations_bf16(seed + 2, nkv * Lmax, hd).reshape(nkv, Lmax, hd)
+    out = torch.empty((M, nq * hd), dtype=torch.int16, device="cuda")
+    ws = B.workspace(B.attn_workspace_bytes(M, nq, nkv, hd, L + M))
+    B.decode_attn(dev(q), dev(Kc), dev(Vc), Lmax, L, M, nq, nkv, hd, out, ws)
+    torch.cuda.synchronize()
+    return q, Kc, Vc, host(out).reshape(M, nq, hd)
+
+
+@pytest.mark.parametrize("M,nq,nkv,L", [(4, 40, 8, 0), (4, 40, 8, 100), (1, 40, 8, 1023), (4, 40, 8, 1024),
+                                        (2, 8, 2, 777), (6, 10, 2, 300), (4, 40, 8, 8192)])
+def test_decode_attn(M, nq, nkv, L):
+    log(f"attn M={M} nq={nq} nkv={nkv} L={L}")
+    q, Kc, Vc, out = _attn_case(M, nq, nkv, L, 1000 + L + M)
+    ref = oracle.decode_attn(synth.bf16_bits_to_f32(q).astype(np.float64), Kc, Vc, L)
+    bf16_close(out, ref)
+
+
+def test_decode_attn_causal_rows():
+    """Row m must not see positions beyond L + m: perturbing them leaves it unchanged."""
+    import torch
+    M, nq, nkv, L, hd = 4, 40, 8, 500, 128
+    q, Kc, Vc, out = _attn_case(M, nq, nkv, L, 7)
+    Lmax = Kc.shape[1]
+    Kc2, Vc2 = Kc.copy(), Vc.copy()
+    Kc2[:, L + 1:] = synth.activations_bf16(99, nkv * (Lmax - L - 1), hd).reshape(nkv, Lmax - L - 1, hd)
+    Vc2[:, L + 1:] = 0
+    out2 = torch.empty((M, nq * hd), dtype=torch.int16, device="cuda")
+    ws = B.workspace(B.attn_workspace_bytes(M, nq, nkv, hd, L + M))
+    B.decode_attn(dev(q), dev(Kc2), dev(Vc2), Lmax, L, M, nq, nkv, hd, out2, ws)
+    torch.cuda.synchronize()
+    o2 = host(out2).reshape(M, nq, hd)
+    assert np.array_equal(o2[0], out[0])
+    assert not np.array_equal(o2[1], out[1])

@@ -162,3 +162,29 @@ def test_gemm_one_hot_codes():
         k = 31 * n + 3
         s = oracle.f16_value(int(scales[n, k // 64]))
         assert np.all(y[:, n] == xf[:, k] * 7 * s)
+
+
+def test_bf16_rounding_matches_torch_on_fp32_values():
+    # for binary32 inputs, one rounding binary64 -> bf16 equals torch's RNE cast
+    import torch
+    g = np.random.default_rng(2)
+    vals = (g.standard_normal(4000) * 10.0 ** g.integers(-30, 30, 4000)).astype(np.float32)
+    # exact ties between consecutive bf16 values, and the subnormal range
+    b = np.arange(0, 0x7f7f, 37, dtype=np.uint32)
+    lo = (b << 16).view(np.float32).astype(np.float64)
+    hi = ((b + 1) << 16).view(np.float32).astype(np.float64)
+    ties = ((lo + hi) / 2).astype(np.float32)
+    sub = (np.arange(1, 300, dtype=np.uint32) << 13).view(np.float32)
+    allv = np.concatenate([vals, ties, sub, -vals[:100], np.array([0.0, 1.0, 3.389e38], np.float32)])
+    want = torch.from_numpy(allv).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_round(allv.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+def test_bf16_double_rounding_case():
+    # a binary64 value just above a bf16 tie: one rounding goes up, rounding
+    # through binary32 first would land on the tie and go to even (down)
+    tie = 1.0 + 2.0 ** -8
+    v = tie + 2.0 ** -40
+    assert oracle.bf16_round(np.array([v]))[0] == 0x3F81
+    assert oracle.bf16_round(np.array([tie]))[0] == 0x3F80

@@ -54,6 +54,14 @@ SIGNATURES = {
     "vw4_accept_workspace_bytes": (_SZ, [_I32, _I32]),
     "spec_accept": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P, _I32, _I32, _I32, _F32, _U64, _U64, _P, _P,
                                    _P, _P, _SZ, _P]),
+    "vw4_gemm_partials_layout": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
+                                                ctypes.POINTER(ctypes.c_int64)]),
+    "w4_skinny_gemm_partials": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I32, _I32, _I32, _P]),
+    "vw4_add_rmsnorm": (ctypes.c_int, [_P, _P, _I32, _I64, _P, _F32, _I32, _I32, _P, _P]),
+    "vw4_rope_kv_append": (ctypes.c_int, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _I64, _P]),
+    "vw4_swiglu": (ctypes.c_int, [_P, _I32, _I64, _I32, _I32, _P, _P]),
+    "vw4_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I64]),
+    "vw4_decode_attn": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
 }
 
 
@@ -240,3 +248,49 @@ def spec_accept(logits, logits_bstride: int, stats, stats_bstride: int, q, q_bst
 
 def rowstats_to_numpy(stats_tensor) -> np.ndarray:
     return stats_tensor.detach().cpu().numpy().view(ROWSTAT_DTYPE)
+
+
+# ---------------------------------------------------------------------------
+# decoder-layer calls
+# ---------------------------------------------------------------------------
+def gemm_partials_layout(M: int, N: int, K: int):
+    S = ctypes.c_int32(0)
+    ldp = ctypes.c_int64(0)
+    _check("vw4_gemm_partials_layout", lib().vw4_gemm_partials_layout(M, N, K, ctypes.byref(S), ctypes.byref(ldp)))
+    return int(S.value), int(ldp.value)
+
+
+def w4_skinny_gemm_partials(x, w_packed, scales_packed, part, M: int, N: int, K: int, stream=None,
+                            ldx: int | None = None):
+    ldx = x.stride(0) if ldx is None else ldx
+    _check("w4_skinny_gemm_partials", lib().w4_skinny_gemm_partials(_ptr(x), ldx, _ptr(w_packed), _ptr(scales_packed),
+                                                                    _ptr(part), M, N, K, _stream(stream)))
+    return part
+
+
+def add_rmsnorm(resid, part, S: int, ldp: int, gamma, eps: float, M: int, D: int, h, stream=None):
+    _check("vw4_add_rmsnorm", lib().vw4_add_rmsnorm(_ptr(resid), _ptr(part), S, ldp, _ptr(gamma), float(eps), M, D,
+                                                    _ptr(h), _stream(stream)))
+    return resid, h
+
+
+def rope_kv_append(part, S: int, ldp: int, M: int, nq: int, nkv: int, hd: int, L: int, theta: float, q_out, Kc, Vc,
+                   Lmax: int, stream=None):
+    _check("vw4_rope_kv_append", lib().vw4_rope_kv_append(_ptr(part), S, ldp, M, nq, nkv, hd, L, float(theta),
+                                                          _ptr(q_out), _ptr(Kc), _ptr(Vc), Lmax, _stream(stream)))
+    return q_out
+
+
+def swiglu(part, S: int, ldp: int, M: int, F: int, a, stream=None):
+    _check("vw4_swiglu", lib().vw4_swiglu(_ptr(part), S, ldp, M, F, _ptr(a), _stream(stream)))
+    return a
+
+
+def attn_workspace_bytes(M: int, nq: int, nkv: int, hd: int, ctx: int) -> int:
+    return int(lib().vw4_attn_workspace_bytes(M, nq, nkv, hd, ctx))
+
+
+def decode_attn(q, Kc, Vc, Lmax: int, L: int, M: int, nq: int, nkv: int, hd: int, out, ws, stream=None):
+    _check("vw4_decode_attn", lib().vw4_decode_attn(_ptr(q), _ptr(Kc), _ptr(Vc), Lmax, L, M, nq, nkv, hd, _ptr(out),
+                                                    _ptr(ws), ws.numel(), _stream(stream)))
+    return out

@@ -324,6 +324,49 @@ int gemm_dispatch(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16
     return check_launch("w4_skinny_gemm");
 }
 
+// Partials form: the main kernel only (no reduction launch); part is the
+// caller's [S_grid][M][Npad] fp32 buffer.
+int gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* s, float* part, int M, int N,
+                  int K, hipStream_t st) {
+    VW4_REQUIRE(M >= 1 && M <= GEMM_MAX_M, VW4_EINVAL, "w4_skinny_gemm_partials: M=%d must be in [1, 8]", M);
+    VW4_REQUIRE(N >= 1, VW4_EINVAL, "w4_skinny_gemm_partials: N=%d must be >= 1", N);
+    VW4_REQUIRE(K >= 64 && K % 64 == 0 && K <= 65536, VW4_EINVAL,
+                "w4_skinny_gemm_partials: K=%d must be a multiple of 64 in [64, 65536]", K);
+    VW4_REQUIRE(x && w && s && part, VW4_EINVAL, "w4_skinny_gemm_partials: null pointer");
+    VW4_REQUIRE(ldx >= K && ldx % 8 == 0 && aligned(x, 16), VW4_EINVAL,
+                "w4_skinny_gemm_partials: x needs ldx >= K, ldx %% 8 == 0 and 16-byte alignment");
+    VW4_REQUIRE(aligned(w, 16) && aligned(s, 2) && aligned(part, 4), VW4_EINVAL,
+                "w4_skinny_gemm_partials: misaligned pointer");
+    const GemmPlan p = plan_gemm(M, N, K);
+    GemmPlan q = p;
+    q.ws_bytes = 0;
+    // S_grid == 1 writes the product straight into part[0] with row stride Npad
+    void* y = part;
+    const int64_t ldy = p.Npad;
+    float* pp = part;
+    switch (M) {
+#define VW4_CASE(MM)                                                                                               \
+    case MM:                                                                                                       \
+        hipLaunchKernelGGL(w4_gemm_kernel<MM>, dim3(p.ntiles, p.S_grid), dim3(64 * p.S_wg), p.lds_bytes, st, x, ldx, \
+                           (const u32x4*)w, s, y, ldy, VW4_F32, N, p.G, p.S_wg, p.S_grid, pp, p.Npad, 0x000F000Fu,   \
+                           0x43004300u);                                                                           \
+        break;
+        VW4_CASE(1) VW4_CASE(2) VW4_CASE(3) VW4_CASE(4) VW4_CASE(5) VW4_CASE(6) VW4_CASE(7) VW4_CASE(8)
+#undef VW4_CASE
+    }
+    (void)q;
+    return check_launch("w4_skinny_gemm_partials");
+}
+
+int gemm_layout(int M, int N, int K, int* S, int64_t* ldp) {
+    VW4_REQUIRE(M >= 1 && M <= GEMM_MAX_M && N >= 1 && K >= 64 && K % 64 == 0 && K <= 65536, VW4_EINVAL,
+                "vw4_gemm_partials_layout: bad shape M=%d N=%d K=%d", M, N, K);
+    const GemmPlan p = plan_gemm(M, N, K);
+    if (S) *S = p.S_grid;
+    if (ldp) *ldp = p.Npad;
+    return VW4_OK;
+}
+
 size_t gemm_ws_bytes(int M, int N, int K) {
     if (M < 1 || M > GEMM_MAX_M || N < 1 || K < 64 || K % 64) return 0;
     return plan_gemm(M, N, K).ws_bytes;
@@ -334,6 +377,18 @@ size_t gemm_ws_bytes(int M, int N, int K) {
 extern "C" {
 
 size_t vw4_gemm_workspace_bytes(int32_t M, int32_t N, int32_t K) { return vw4::gemm_ws_bytes(M, N, K); }
+
+int vw4_gemm_partials_layout(int32_t M, int32_t N, int32_t K, int32_t* S, int64_t* ldp) {
+    int s = 0;
+    int rc = vw4::gemm_layout(M, N, K, &s, ldp);
+    if (S) *S = s;
+    return rc;
+}
+
+int w4_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, const uint16_t* scales_packed,
+                            float* part, int32_t M, int32_t N, int32_t K, void* stream) {
+    return vw4::gemm_partials(x, ldx, w_packed, scales_packed, part, M, N, K, (hipStream_t)stream);
+}
 
 int w4_skinny_gemm(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, const uint16_t* scales_packed, void* y,
                    int64_t ldy, int32_t y_dtype, int32_t M, int32_t N, int32_t K, void* ws, size_t ws_bytes,

@@ -80,3 +80,150 @@ class LMHeadVerify:
     def step(self, x, head: W4Linear, q, drafts, T, top_p, seed, step, stream=None, **out):
         self.gemm(x, head, stream)
         self.stats_and_accept(q, drafts, T, top_p, seed, step, stream, **out)
+
+
+# ---------------------------------------------------------------------------
+# Full verify forward of a dense decoder (synthetic weights)
+# ---------------------------------------------------------------------------
+DENSE_27B = dict(d=5120, nq=40, nkv=8, hd=128, F=17408, layers=64, V=151936, eps=1e-6, theta=10000.0)
+
+
+class Decoder:
+    """Pre-norm dense decoder with GQA attention and a SwiGLU FFN, every linear
+    a W4 skinny GEMM.  One call of ``forward`` scores M rows at positions
+    L .. L+M-1 (the verify pass); M = 1 is an autoregressive step.  Weights,
+    KV caches and activation buffers are allocated once (device-resident)."""
+
+    def __init__(self, cfg: dict, M_max: int, Lmax: int, gen=None, device="cuda", weights=None,
+                 kv_fill: bool = True):
+        import torch
+        self.cfg = dict(cfg)
+        c = self.cfg
+        self.M_max, self.Lmax, self.device = M_max, Lmax, device
+        d, nq, nkv, hd, F, nl, V = c["d"], c["nq"], c["nkv"], c["hd"], c["F"], c["layers"], c["V"]
+        self.nqkv = (nq + 2 * nkv) * hd
+        self.shapes = {"qkv": (self.nqkv, d), "o": (d, nq * hd), "gate_up": (2 * F, d), "down": (d, F)}
+        if weights is None:
+            weights = self.random_weights(cfg, gen, device)
+        self.layers = weights["layers"]
+        self.final_gamma = weights["final_gamma"]
+        self.lm_head = weights["lm_head"]
+        # KV caches [layer][nkv][Lmax][hd] bf16; synthetic N(0,1) context
+        self.Kc, self.Vc = [], []
+        for _ in range(nl):
+            if kv_fill:
+                k = torch.randn((nkv, Lmax, hd), generator=gen, device=device).to(torch.bfloat16).view(torch.int16)
+                v = torch.randn((nkv, Lmax, hd), generator=gen, device=device).to(torch.bfloat16).view(torch.int16)
+            else:
+                k = torch.zeros((nkv, Lmax, hd), dtype=torch.int16, device=device)
+                v = torch.zeros((nkv, Lmax, hd), dtype=torch.int16, device=device)
+            self.Kc.append(k)
+            self.Vc.append(v)
+        # activation buffers
+        i16 = torch.int16
+        self.resid = torch.empty((M_max, d), dtype=i16, device=device)
+        self.h = torch.empty((M_max, d), dtype=i16, device=device)
+        self.q = torch.empty((M_max, nq, hd), dtype=i16, device=device)
+        self.attn = torch.empty((M_max, nq * hd), dtype=i16, device=device)
+        self.a = torch.empty((M_max, F), dtype=i16, device=device)
+        self.parts = {}
+        for name, (N, K) in self.shapes.items():
+            S, ldp = B.gemm_partials_layout(M_max, N, K)
+            self.parts[name] = torch.empty(S * M_max * ldp, dtype=torch.float32, device=device)
+        self.attn_ws = B.workspace(B.attn_workspace_bytes(M_max, nq, nkv, hd, Lmax), device)
+        self.logits = torch.empty((M_max, V), dtype=torch.float32, device=device)
+        self.lm_ws = B.workspace(B.gemm_workspace_bytes(M_max, V, d), device)
+
+    @staticmethod
+    def random_weights(cfg: dict, gen, device="cuda"):
+        """~N(0, 0.02) fp32 weights drawn on the device and quantised to W4;
+        RMSNorm gains ~N(1, 0.02) in bf16."""
+        import torch
+        d, nq, nkv, hd, F, nl, V = (cfg[k] for k in ("d", "nq", "nkv", "hd", "F", "layers", "V"))
+        nqkv = (nq + 2 * nkv) * hd
+
+        def gamma():
+            return (1.0 + 0.02 * torch.randn(d, generator=gen, device=device)).to(torch.bfloat16).view(torch.int16)
+
+        layers = []
+        for _ in range(nl):
+            layers.append(dict(qkv=W4Linear.random(nqkv, d, 0.02, gen, device),
+                               o=W4Linear.random(d, nq * hd, 0.02, gen, device),
+                               gate_up=W4Linear.random(2 * F, d, 0.02, gen, device),
+                               down=W4Linear.random(d, F, 0.02, gen, device),
+                               g1=gamma(), g2=gamma()))
+        return dict(layers=layers, final_gamma=gamma(), lm_head=W4Linear.random(V, d, 0.02, gen, device))
+
+    def weight_bytes(self) -> int:
+        n = sum(l[k].nbytes() for l in self.layers for k in ("qkv", "o", "gate_up", "down"))
+        return n + self.lm_head.nbytes()
+
+    def kv_bytes(self, L: int, M: int) -> int:
+        c = self.cfg
+        return c["layers"] * 2 * c["nkv"] * (L + M) * c["hd"] * 2
+
+    def forward(self, x, L: int, M: int, stream=None):
+        """x: int16 (bf16 bits) [M][d] hidden rows; fills self.logits[:M]."""
+        c = self.cfg
+        d, nq, nkv, hd, F, eps = c["d"], c["nq"], c["nkv"], c["hd"], c["F"], c["eps"]
+        assert 1 <= M <= self.M_max and L + M <= self.Lmax
+        resid, h = self.resid[:M], self.h[:M]
+        resid.copy_(x[:M])
+        lay = self.layers
+        B.add_rmsnorm(resid, None, 1, d, lay[0]["g1"], eps, M, d, h, stream)
+        for li, W in enumerate(lay):
+            # attention block
+            N, K = self.shapes["qkv"]
+            S, ldp = B.gemm_partials_layout(M, N, K)
+            B.w4_skinny_gemm_partials(h, W["qkv"].packed, W["qkv"].pscales, self.parts["qkv"], M, N, K, stream)
+            B.rope_kv_append(self.parts["qkv"], S, ldp, M, nq, nkv, hd, L, c["theta"], self.q, self.Kc[li],
+                             self.Vc[li], self.Lmax, stream)
+            B.decode_attn(self.q, self.Kc[li], self.Vc[li], self.Lmax, L, M, nq, nkv, hd, self.attn, self.attn_ws,
+                          stream)
+            N, K = self.shapes["o"]
+            S, ldp = B.gemm_partials_layout(M, N, K)
+            B.w4_skinny_gemm_partials(self.attn, W["o"].packed, W["o"].pscales, self.parts["o"], M, N, K, stream)
+            B.add_rmsnorm(resid, self.parts["o"], S, ldp, W["g2"], eps, M, d, h, stream)
+            # FFN block
+            N, K = self.shapes["gate_up"]
+            S, ldp = B.gemm_partials_layout(M, N, K)
+            B.w4_skinny_gemm_partials(h, W["gate_up"].packed, W["gate_up"].pscales, self.parts["gate_up"], M, N, K,
+                                      stream)
+            B.swiglu(self.parts["gate_up"], S, ldp, M, F, self.a, stream)
+            N, K = self.shapes["down"]
+            S, ldp = B.gemm_partials_layout(M, N, K)
+            B.w4_skinny_gemm_partials(self.a, W["down"].packed, W["down"].pscales, self.parts["down"], M, N, K,
+                                      stream)
+            g_next = lay[li + 1]["g1"] if li + 1 < len(lay) else self.final_gamma
+            B.add_rmsnorm(resid, self.parts["down"], S, ldp, g_next, eps, M, d, h, stream)
+        B.w4_skinny_gemm(h, self.lm_head.packed, self.lm_head.pscales, self.logits[:M], M, c["V"], d,
+                         ws=self.lm_ws, stream=stream)
+        return self.logits[:M]
+
+
+class VerifyStep:
+    """Decoder forward over the M = D + 1 verify rows, then the temperature /
+    top-p statistics and Leviathan–Chen acceptance (D = 0: one plain
+    autoregressive sampling step)."""
+
+    def __init__(self, dec: Decoder, M: int):
+        import torch
+        self.dec, self.M, self.D = dec, M, M - 1
+        V = dec.cfg["V"]
+        dev = dec.device
+        self.stats = torch.zeros(M * B.ROWSTAT_BYTES, dtype=torch.uint8, device=dev)
+        self.stat_ws = B.workspace(B.verify_workspace_bytes(M, V), dev)
+        self.acc_ws = B.workspace(B.accept_workspace_bytes(1, V), dev)
+        self.tokens = torch.empty((1, M), dtype=torch.int32, device=dev)
+        self.n_acc = torch.empty(1, dtype=torch.int32, device=dev)
+        self.flags = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def run(self, x, L: int, q, drafts, T: float, top_p: float, seed: int, step: int, stream=None, **out):
+        dec, M, V = self.dec, self.M, self.dec.cfg["V"]
+        logits = dec.forward(x, L, M, stream)
+        B.verify_logits(None, None, None, M, V, dec.cfg["d"], T, top_p, logits, self.stats, self.stat_ws,
+                        stream=stream)
+        B.spec_accept(logits, 0, self.stats, 0, q, 0, drafts, 1, self.D, V, T, seed, step,
+                      out.get("tokens", self.tokens), out.get("n_acc", self.n_acc), out.get("flags", self.flags),
+                      self.acc_ws, stream=stream)
+        return self.tokens, self.n_acc, self.flags
