@@ -105,11 +105,18 @@ def test_forward_matches_oracle_small_decoder():
     print(f"[forward] max rel err {rel.max():.3e}, median {np.median(rel):.3e}", flush=True)
     assert rel.max() < 2e-2
     assert np.median(rel) < 2e-3
-    # the KV rows the verify pass appended agree with the oracle's within bf16
+    # the KV rows the verify pass appended: layer 0 sees identical inputs on
+    # both sides (bit-exact up to rare one-ulp rounding flips); later layers
+    # inherit the flips of earlier ones, so only closeness is required there
     for li in range(cfg["layers"]):
-        kg = host(dec.Kc[li])[:, L:L + M].astype(np.int32)
-        ko = Kh[li][:, L:L + M].astype(np.int32)
-        assert np.mean(kg == ko) > 0.9
+        for gpu_c, ora_c in ((dec.Kc[li], Kh[li]), (dec.Vc[li], Vh[li])):
+            kg = host(gpu_c)[:, L:L + M]
+            ko = ora_c[:, L:L + M]
+            if li == 0:
+                assert np.mean(kg == ko) > 0.95
+            a = synth.bf16_bits_to_f32(kg).astype(np.float64)
+            b = synth.bf16_bits_to_f32(ko).astype(np.float64)
+            assert np.abs(a - b).max() <= 3e-2 * np.sqrt((b ** 2).mean())
 
 
 def _dense_cfg(layers, V):

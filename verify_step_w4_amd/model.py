@@ -162,8 +162,11 @@ class Decoder:
         c = self.cfg
         return c["layers"] * 2 * c["nkv"] * (L + M) * c["hd"] * 2
 
-    def forward(self, x, L: int, M: int, stream=None):
-        """x: int16 (bf16 bits) [M][d] hidden rows; fills self.logits[:M]."""
+    def forward(self, x, L: int, M: int, stream=None, gemm_hook=None):
+        """x: int16 (bf16 bits) [M][d] hidden rows; fills self.logits[:M].
+        gemm_hook(when, name), if given, is called right before ("pre") and
+        after ("post") each W4 GEMM launch (used to time the GEMMs in place)."""
+        hook = gemm_hook or (lambda when, name: None)
         c = self.cfg
         d, nq, nkv, hd, F, eps = c["d"], c["nq"], c["nkv"], c["hd"], c["F"], c["eps"]
         assert 1 <= M <= self.M_max and L + M <= self.Lmax
@@ -175,30 +178,50 @@ class Decoder:
             # attention block
             N, K = self.shapes["qkv"]
             S, ldp = B.gemm_partials_layout(M, N, K)
+            hook("pre", "qkv")
             B.w4_skinny_gemm_partials(h, W["qkv"].packed, W["qkv"].pscales, self.parts["qkv"], M, N, K, stream)
+            hook("post", "qkv")
             B.rope_kv_append(self.parts["qkv"], S, ldp, M, nq, nkv, hd, L, c["theta"], self.q, self.Kc[li],
                              self.Vc[li], self.Lmax, stream)
             B.decode_attn(self.q, self.Kc[li], self.Vc[li], self.Lmax, L, M, nq, nkv, hd, self.attn, self.attn_ws,
                           stream)
             N, K = self.shapes["o"]
             S, ldp = B.gemm_partials_layout(M, N, K)
+            hook("pre", "o")
             B.w4_skinny_gemm_partials(self.attn, W["o"].packed, W["o"].pscales, self.parts["o"], M, N, K, stream)
+            hook("post", "o")
             B.add_rmsnorm(resid, self.parts["o"], S, ldp, W["g2"], eps, M, d, h, stream)
             # FFN block
             N, K = self.shapes["gate_up"]
             S, ldp = B.gemm_partials_layout(M, N, K)
+            hook("pre", "gate_up")
             B.w4_skinny_gemm_partials(h, W["gate_up"].packed, W["gate_up"].pscales, self.parts["gate_up"], M, N, K,
                                       stream)
+            hook("post", "gate_up")
             B.swiglu(self.parts["gate_up"], S, ldp, M, F, self.a, stream)
             N, K = self.shapes["down"]
             S, ldp = B.gemm_partials_layout(M, N, K)
+            hook("pre", "down")
             B.w4_skinny_gemm_partials(self.a, W["down"].packed, W["down"].pscales, self.parts["down"], M, N, K,
                                       stream)
+            hook("post", "down")
             g_next = lay[li + 1]["g1"] if li + 1 < len(lay) else self.final_gamma
             B.add_rmsnorm(resid, self.parts["down"], S, ldp, g_next, eps, M, d, h, stream)
+        hook("pre", "lm_head")
         B.w4_skinny_gemm(h, self.lm_head.packed, self.lm_head.pscales, self.logits[:M], M, c["V"], d,
                          ws=self.lm_ws, stream=stream)
+        hook("post", "lm_head")
         return self.logits[:M]
+
+    def gemm_alg_bytes(self, M: int) -> int:
+        """Algorithmic bytes of one forward's W4 GEMMs: each weight (code +
+        scale) once, activations in, fp32 outputs out."""
+        c = self.cfg
+        tot = 0.0
+        for N, K in self.shapes.values():
+            tot += c["layers"] * (N * K * BYTES_PER_WEIGHT + M * K * 2 + M * N * 4)
+        tot += c["V"] * c["d"] * BYTES_PER_WEIGHT + M * c["d"] * 2 + M * c["V"] * 4
+        return int(tot)
 
 
 class VerifyStep:
@@ -218,9 +241,10 @@ class VerifyStep:
         self.n_acc = torch.empty(1, dtype=torch.int32, device=dev)
         self.flags = torch.empty(1, dtype=torch.int32, device=dev)
 
-    def run(self, x, L: int, q, drafts, T: float, top_p: float, seed: int, step: int, stream=None, **out):
+    def run(self, x, L: int, q, drafts, T: float, top_p: float, seed: int, step: int, stream=None, gemm_hook=None,
+            **out):
         dec, M, V = self.dec, self.M, self.dec.cfg["V"]
-        logits = dec.forward(x, L, M, stream)
+        logits = dec.forward(x, L, M, stream, gemm_hook=gemm_hook)
         B.verify_logits(None, None, None, M, V, dec.cfg["d"], T, top_p, logits, self.stats, self.stat_ws,
                         stream=stream)
         B.spec_accept(logits, 0, self.stats, 0, q, 0, drafts, 1, self.D, V, T, seed, step,
