@@ -23,9 +23,8 @@
  *   - Pointers named *_dev, and every array argument of a compute call, are
  *     device memory owned by the caller.  The library allocates nothing and
  *     keeps no pointer after returning.  Scratch memory comes from a caller
- *     workspace sized by the matching *_workspace_bytes() query; a workspace
- *     must be zero-filled once when it is allocated (the library leaves its
- *     counters at zero after every call, so later calls need no clearing).
+ *     workspace sized by the matching *_workspace_bytes() query (its contents
+ *     need no initialisation and are dead after the call's kernels finish).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
  *     only enqueue work; results are valid once the stream reaches that point.
  *     Calls that share a workspace must not run concurrently.
@@ -182,6 +181,18 @@ VW4_API int verify_logits(const uint16_t* hidden, int64_t ldh, const uint8_t* lm
  * ------------------------------------------------------------------------ */
 VW4_API size_t vw4_accept_workspace_bytes(int32_t B, int32_t V);
 
+/* As spec_accept, but the step of problem 0 is read from device memory
+ * (*step_dev) when the kernels run, so that a captured graph of the verify step
+ * (the pages' compiled-graph cache: hazakura.dev mtplx page,
+ * "4層のアーキテクチャ" Layer 0, GraphBank) draws fresh uniforms on every replay;
+ * vw4_step_advance(step_dev, inc) adds inc to it on the stream. */
+VW4_API int spec_accept_ex(const float* logits, int64_t logits_bstride, const vw4_rowstat* stats,
+                           int64_t stats_bstride, const float* q, int64_t q_bstride, const int32_t* draft, int32_t B,
+                           int32_t D, int32_t V, float temperature, uint64_t seed, const uint64_t* step_dev,
+                           int32_t* out_tokens, int32_t* out_n_acc, uint32_t* out_flags, void* ws, size_t ws_bytes,
+                           void* stream);
+VW4_API int vw4_step_advance(uint64_t* step_dev, uint64_t inc, void* stream);
+
 VW4_API int spec_accept(const float* logits, int64_t logits_bstride, const vw4_rowstat* stats, int64_t stats_bstride,
                 const float* q, int64_t q_bstride, const int32_t* draft, int32_t B, int32_t D, int32_t V,
                 float temperature, uint64_t seed, uint64_t step0, int32_t* out_tokens, int32_t* out_n_acc,
@@ -209,9 +220,11 @@ VW4_API int w4_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_
 
 /* resid[M][D] (bf16, in/out) += sum_s part[s][m][d] (fp32; part may be NULL to
  * skip the add), rounded to bf16; then h = bf16(rmsnorm(resid) * gamma):
- * h = r / sqrt(mean_d(r^2) + eps) * gamma.  D <= 65536. */
+ * h = r / sqrt(mean_d(r^2) + eps) * gamma.  D <= 65536, M <= 64.
+ * Workspace: vw4_norm_workspace_bytes(M, D) (per-chunk sums of squares). */
+VW4_API size_t vw4_norm_workspace_bytes(int32_t M, int32_t D);
 VW4_API int vw4_add_rmsnorm(uint16_t* resid, const float* part, int32_t S, int64_t ldp, const uint16_t* gamma,
-                            float eps, int32_t M, int32_t D, uint16_t* h, void* stream);
+                            float eps, int32_t M, int32_t D, uint16_t* h, void* ws, size_t ws_bytes, void* stream);
 
 /* From the fused q|k|v projection (partials of [M][(nq + 2 nkv) * hd]): rotary
  * embedding (rotate-half, base theta, position L + m) of q and k; q -> q_out

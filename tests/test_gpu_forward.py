@@ -174,3 +174,36 @@ def test_verify_step_deterministic_and_accepts():
     assert outs[0][3].tobytes() == outs[1][3].tobytes()
     n = int(outs[0][1][0])
     assert 0 <= n <= M - 1 and 0 <= int(outs[0][0][0, n]) < cfg["V"]
+
+
+def test_graph_replay_matches_eager_steps():
+    """The verify step captured as a HIP graph: every replay (with eager work in
+    between) equals the eager step with the same Philox step number."""
+    import torch
+    cfg = _dense_cfg(2, 8192)
+    M, L = 4, 300
+    log("graph replay == eager (full width, 2 layers)")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(8)
+    dec = Decoder(cfg, M, L + M + 4, gen=gen)
+    vs = VerifyStep(dec, M)
+    x = dev(synth.activations_bf16(12, M, cfg["d"]))
+    q, drafts = synth.q_and_drafts(13, M - 1, cfg["V"], 1.0, B=1)
+    qd, dd = dev(q), dev(drafts[0])
+    seed, T, top_p = 0x5EED0005, 0.6, 0.95
+    eager = []
+    for k in range(3):
+        tok, nacc, fl = vs.run(x, L, qd, dd, T, top_p, seed, k)
+        torch.cuda.synchronize()
+        eager.append((host(tok).copy(), host(nacc).copy(), host(dec.logits[:M]).copy()))
+    step_dev = torch.zeros(1, dtype=torch.int64, device="cuda")
+    g = vs.capture(x, L, qd, dd, T, top_p, seed, step_dev)   # the warm-up run inside uses step 0
+    step_dev.zero_()
+    torch.cuda.synchronize()
+    for k in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        _ = torch.ones(1000, device="cuda").sum().item()          # eager work between replays
+        assert np.array_equal(host(dec.logits[:M]), eager[k][2]), k
+        assert np.array_equal(host(vs.tokens), eager[k][0]) and np.array_equal(host(vs.n_acc), eager[k][1]), k
+    assert int(step_dev.item()) == 3

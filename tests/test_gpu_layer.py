@@ -42,7 +42,7 @@ def test_add_rmsnorm(M, D, S):
     part = partials(S + D, S, M, D, ldp, 0.5)
     gamma = synth.f32_to_bf16_bits(1.0 + synth.normal_f32(synth.rng(3), (D,), 0.02))
     rd, hd = dev(resid), torch.empty((M, D), dtype=torch.int16, device="cuda")
-    B.add_rmsnorm(rd, dev(part), S, ldp, dev(gamma), 1e-6, M, D, hd)
+    B.add_rmsnorm(rd, dev(part), S, ldp, dev(gamma), 1e-6, M, D, hd, B.workspace(B.norm_workspace_bytes(M, D)))
     torch.cuda.synchronize()
     # oracle: exact sum, one bf16 rounding, then RMSNorm of the rounded residual
     exact = synth.bf16_bits_to_f32(resid).astype(np.float64) + part[:, :, :D].astype(np.float64).sum(axis=0)
@@ -58,7 +58,7 @@ def test_rmsnorm_without_add():
     resid = synth.activations_bf16(5, M, D, 2.0)
     gamma = synth.f32_to_bf16_bits(1.0 + synth.normal_f32(synth.rng(6), (D,), 0.02))
     rd, hd = dev(resid), torch.empty((M, D), dtype=torch.int16, device="cuda")
-    B.add_rmsnorm(rd, None, 1, D, dev(gamma), 1e-6, M, D, hd)
+    B.add_rmsnorm(rd, None, 1, D, dev(gamma), 1e-6, M, D, hd, B.workspace(B.norm_workspace_bytes(M, D)))
     torch.cuda.synchronize()
     assert np.array_equal(host(rd), resid)
     bf16_close(host(hd), oracle.rmsnorm(resid, gamma, 1e-6))

@@ -54,10 +54,14 @@ SIGNATURES = {
     "vw4_accept_workspace_bytes": (_SZ, [_I32, _I32]),
     "spec_accept": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P, _I32, _I32, _I32, _F32, _U64, _U64, _P, _P,
                                    _P, _P, _SZ, _P]),
+    "spec_accept_ex": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P, _I32, _I32, _I32, _F32, _U64, _P, _P, _P,
+                                      _P, _P, _SZ, _P]),
+    "vw4_step_advance": (ctypes.c_int, [_P, _U64, _P]),
     "vw4_gemm_partials_layout": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
                                                 ctypes.POINTER(ctypes.c_int64)]),
     "w4_skinny_gemm_partials": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I32, _I32, _I32, _P]),
-    "vw4_add_rmsnorm": (ctypes.c_int, [_P, _P, _I32, _I64, _P, _F32, _I32, _I32, _P, _P]),
+    "vw4_norm_workspace_bytes": (_SZ, [_I32, _I32]),
+    "vw4_add_rmsnorm": (ctypes.c_int, [_P, _P, _I32, _I64, _P, _F32, _I32, _I32, _P, _P, _SZ, _P]),
     "vw4_rope_kv_append": (ctypes.c_int, [_P, _I32, _I64, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P, _P, _I64, _P]),
     "vw4_swiglu": (ctypes.c_int, [_P, _I32, _I64, _I32, _I32, _P, _P]),
     "vw4_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I64]),
@@ -187,7 +191,7 @@ def w4_quantize_packed(w, stream=None, out=None):
 
 
 # ---------------------------------------------------------------------------
-# workspaces (zero-filled once; the library leaves its counters at zero)
+# workspaces (caller-owned scratch; contents need no initialisation)
 # ---------------------------------------------------------------------------
 def workspace(nbytes: int, device="cuda"):
     import torch
@@ -246,6 +250,20 @@ def spec_accept(logits, logits_bstride: int, stats, stats_bstride: int, q, q_bst
     return out_tokens, out_n_acc, out_flags
 
 
+def spec_accept_ex(logits, logits_bstride: int, stats, stats_bstride: int, q, q_bstride: int, draft, B: int, D: int,
+                   V: int, temperature: float, seed: int, step_dev, out_tokens, out_n_acc, out_flags, ws,
+                   stream=None):
+    _check("spec_accept_ex", lib().spec_accept_ex(_ptr(logits), logits_bstride, _ptr(stats), stats_bstride, _ptr(q),
+                                                  q_bstride, _ptr(draft), B, D, V, float(temperature), int(seed),
+                                                  _ptr(step_dev), _ptr(out_tokens), _ptr(out_n_acc),
+                                                  _ptr(out_flags), _ptr(ws), ws.numel(), _stream(stream)))
+    return out_tokens, out_n_acc, out_flags
+
+
+def step_advance(step_dev, inc: int = 1, stream=None):
+    _check("vw4_step_advance", lib().vw4_step_advance(_ptr(step_dev), int(inc), _stream(stream)))
+
+
 def rowstats_to_numpy(stats_tensor) -> np.ndarray:
     return stats_tensor.detach().cpu().numpy().view(ROWSTAT_DTYPE)
 
@@ -268,9 +286,13 @@ def w4_skinny_gemm_partials(x, w_packed, scales_packed, part, M: int, N: int, K:
     return part
 
 
-def add_rmsnorm(resid, part, S: int, ldp: int, gamma, eps: float, M: int, D: int, h, stream=None):
+def norm_workspace_bytes(M: int, D: int) -> int:
+    return int(lib().vw4_norm_workspace_bytes(M, D))
+
+
+def add_rmsnorm(resid, part, S: int, ldp: int, gamma, eps: float, M: int, D: int, h, ws, stream=None):
     _check("vw4_add_rmsnorm", lib().vw4_add_rmsnorm(_ptr(resid), _ptr(part), S, ldp, _ptr(gamma), float(eps), M, D,
-                                                    _ptr(h), _stream(stream)))
+                                                    _ptr(h), _ptr(ws), ws.numel(), _stream(stream)))
     return resid, h
 
 

@@ -372,7 +372,10 @@ struct AcceptArgs {
     uint32_t* out_flags;
     AcceptPart* parts;
     ProblemState* states;  // per problem, written by workgroup 0 of the chunk kernel
+    const uint64_t* step_dev;  // if set, the first problem's step is read here (graph replays)
 };
+
+__device__ __forceinline__ uint64_t first_step(const AcceptArgs& a) { return a.step_dev ? *a.step_dev : a.step0; }
 
 __device__ __forceinline__ void write_bad(const AcceptArgs& a, int64_t b) {
     if (threadIdx.x <= a.D) a.out_tokens[b * (a.D + 1) + threadIdx.x] = -1;
@@ -399,7 +402,7 @@ __global__ __launch_bounds__(NT) void accept_chunk_kernel(AcceptArgs a) {
     const int32_t* db = a.draft + b * a.D;
     const double T = (double)a.temperature;
     const ProblemState ps =
-        problem_state<NT>(zb, sb, qb, db, a.D, a.V, T, a.seed, a.step0 + (uint64_t)b, s_u, s_st);
+        problem_state<NT>(zb, sb, qb, db, a.D, a.V, T, a.seed, first_step(a) + (uint64_t)b, s_u, s_st);
     if (ps.bad) {
         if (w == 0) write_bad(a, b);
         return;
@@ -447,7 +450,7 @@ __global__ __launch_bounds__(NT) void accept_finish_kernel(AcceptArgs a) {
     if (ps.bad) return;  // outputs written by the chunk kernel
     const int k = ps.k;
     if (threadIdx.x == 0) {
-        uint64_t c[4] = {a.step0 + (uint64_t)b, (uint64_t)k, 0, 0};
+        uint64_t c[4] = {first_step(a) + (uint64_t)b, (uint64_t)k, 0, 0};
         philox4x64_10(a.seed, 0, c);
         s_u[2 * k] = unit53(c[0]);
         s_u[2 * k + 1] = unit53(c[1]);
@@ -461,21 +464,13 @@ __global__ __launch_bounds__(NT) void accept_finish_kernel(AcceptArgs a) {
                        a.out_nacc + b, a.out_flags + b, sh, shi);
 }
 
-}  // namespace vw4
+__global__ void step_advance_kernel(uint64_t* step, uint64_t inc) { *step += inc; }
 
-using namespace vw4;
-
-extern "C" {
-
-size_t vw4_accept_workspace_bytes(int32_t B, int32_t V) {
-    if (B < 1 || B > (1 << 24) || V < 1 || V > (1 << 24)) return 0;
-    return accept_layout(B, V).total;
-}
-
-int spec_accept(const float* logits, int64_t logits_bstride, const vw4_rowstat* stats, int64_t stats_bstride,
-                const float* q, int64_t q_bstride, const int32_t* draft, int32_t B, int32_t D, int32_t V,
-                float temperature, uint64_t seed, uint64_t step0, int32_t* out_tokens, int32_t* out_n_acc,
-                uint32_t* out_flags, void* ws, size_t ws_bytes, void* stream) {
+static int spec_accept_impl(const float* logits, int64_t logits_bstride, const vw4_rowstat* stats,
+                            int64_t stats_bstride, const float* q, int64_t q_bstride, const int32_t* draft, int32_t B,
+                            int32_t D, int32_t V, float temperature, uint64_t seed, uint64_t step0,
+                            const uint64_t* step_dev, int32_t* out_tokens, int32_t* out_n_acc, uint32_t* out_flags,
+                            void* ws, size_t ws_bytes, void* stream) {
     VW4_REQUIRE(B >= 1 && B <= (1 << 24), VW4_EINVAL, "spec_accept: B=%d out of range", B);
     VW4_REQUIRE(D >= 0 && D <= AMAXD, VW4_EINVAL, "spec_accept: D=%d must be in [0, 7]", D);
     VW4_REQUIRE(V >= 1 && V <= (1 << 24), VW4_EINVAL, "spec_accept: V=%d out of range", V);
@@ -496,6 +491,7 @@ int spec_accept(const float* logits, int64_t logits_bstride, const vw4_rowstat* 
     a.out_tokens = out_tokens; a.out_nacc = out_n_acc; a.out_flags = out_flags;
     a.parts = (AcceptPart*)((char*)ws + L.off_part);
     a.states = (ProblemState*)((char*)ws + L.off_state);
+    a.step_dev = step_dev;
     hipStream_t st = (hipStream_t)stream;
     const dim3 grid((unsigned)B, (unsigned)L.P);
     if (L.threads == 64) {
@@ -505,6 +501,42 @@ int spec_accept(const float* logits, int64_t logits_bstride, const vw4_rowstat* 
         if (L.P > 1) hipLaunchKernelGGL(accept_finish_kernel<AT>, dim3((unsigned)B), dim3(AT), 0, st, a);
     }
     return check_launch("spec_accept");
+}
+
+
+}  // namespace vw4
+
+using namespace vw4;
+
+extern "C" {
+
+
+size_t vw4_accept_workspace_bytes(int32_t B, int32_t V) {
+    if (B < 1 || B > (1 << 24) || V < 1 || V > (1 << 24)) return 0;
+    return accept_layout(B, V).total;
+}
+
+int spec_accept(const float* logits, int64_t logits_bstride, const vw4_rowstat* stats, int64_t stats_bstride,
+                const float* q, int64_t q_bstride, const int32_t* draft, int32_t B, int32_t D, int32_t V,
+                float temperature, uint64_t seed, uint64_t step0, int32_t* out_tokens, int32_t* out_n_acc,
+                uint32_t* out_flags, void* ws, size_t ws_bytes, void* stream) {
+    return spec_accept_impl(logits, logits_bstride, stats, stats_bstride, q, q_bstride, draft, B, D, V, temperature,
+                            seed, step0, nullptr, out_tokens, out_n_acc, out_flags, ws, ws_bytes, stream);
+}
+
+int spec_accept_ex(const float* logits, int64_t logits_bstride, const vw4_rowstat* stats, int64_t stats_bstride,
+                   const float* q, int64_t q_bstride, const int32_t* draft, int32_t B, int32_t D, int32_t V,
+                   float temperature, uint64_t seed, const uint64_t* step_dev, int32_t* out_tokens,
+                   int32_t* out_n_acc, uint32_t* out_flags, void* ws, size_t ws_bytes, void* stream) {
+    VW4_REQUIRE(step_dev && aligned(step_dev, 8), VW4_EINVAL, "spec_accept_ex: step_dev must be an 8-byte aligned device pointer");
+    return spec_accept_impl(logits, logits_bstride, stats, stats_bstride, q, q_bstride, draft, B, D, V, temperature,
+                            seed, 0, step_dev, out_tokens, out_n_acc, out_flags, ws, ws_bytes, stream);
+}
+
+int vw4_step_advance(uint64_t* step_dev, uint64_t inc, void* stream) {
+    VW4_REQUIRE(step_dev && aligned(step_dev, 8), VW4_EINVAL, "vw4_step_advance: step_dev must be 8-byte aligned");
+    hipLaunchKernelGGL(step_advance_kernel, dim3(1), dim3(1), 0, (hipStream_t)stream, step_dev, inc);
+    return check_launch("vw4_step_advance");
 }
 
 }  // extern "C"

@@ -19,47 +19,74 @@
 
 namespace vw4 {
 
-// Sum over the S partial slices of element (m, c), slice order.
+// Sum over the S partial slices of element (m, c), slice order.  The loads
+// of 8 slices are issued together (a chain of dependent loads would pay one
+// memory latency per slice).
 __device__ __forceinline__ float sum_parts(const float* __restrict__ part, int S, int M, int64_t ldp, int m,
                                            int64_t c) {
     float s = 0.0f;
-    for (int k = 0; k < S; ++k) s += part[((int64_t)k * M + m) * ldp + c];
+    const int64_t stride = (int64_t)M * ldp;
+    const float* p = part + (int64_t)m * ldp + c;
+    for (int k0 = 0; k0 < S; k0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (k0 + i < S) ? p[(int64_t)(k0 + i) * stride] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (k0 + i < S) s += v[i];
+    }
     return s;
 }
 
 // ---------------------------------------------------------------------------
-// residual add + RMSNorm: one workgroup (1024 threads) per row.
+// residual add + RMSNorm in two launches over many workgroups:
+//   1. grid (ceil(D / NCOL), M): resid += partials (rounded to bf16), and the
+//      chunk's sum of squares of the rounded residual -> ws[m][chunk]
+//   2. grid (ceil(D / NCOL), M): total (chunk order) -> scale, h = bf16(...)
 // ---------------------------------------------------------------------------
-constexpr int NT_NORM = 1024;
+constexpr int NCOL = 256;   // columns per workgroup (one per thread)
+constexpr int NMAXCH = 256; // chunks per row at most (D <= 65536)
 
-__global__ __launch_bounds__(NT_NORM) void add_rmsnorm_kernel(uint16_t* __restrict__ resid,
-                                                              const float* __restrict__ part, int S, int64_t ldp,
-                                                              const uint16_t* __restrict__ gamma, float eps, int M,
-                                                              int D, uint16_t* __restrict__ h) {
-    __shared__ float red[NT_NORM / 64];
-    const int m = blockIdx.x, tid = threadIdx.x;
-    uint16_t* r = resid + (int64_t)m * D;
-    float ss = 0.0f;
-    for (int d = tid; d < D; d += NT_NORM) {
-        float v = bf16_to_f32(r[d]);
+__global__ __launch_bounds__(NCOL) void add_sumsq_kernel(uint16_t* __restrict__ resid, const float* __restrict__ part,
+                                                         int S, int64_t ldp, int M, int D, float* __restrict__ ssq) {
+    __shared__ float red[NCOL / 64];
+    const int ch = blockIdx.x, m = blockIdx.y, d = ch * NCOL + threadIdx.x;
+    float v = 0.0f;
+    if (d < D) {
+        uint16_t* r = resid + (int64_t)m * D + d;
+        v = bf16_to_f32(*r);
         if (part) {
             v += sum_parts(part, S, M, ldp, m, d);
             const uint16_t rb = f32_to_bf16(v);
-            r[d] = rb;
+            *r = rb;
             v = bf16_to_f32(rb);
         }
-        ss += v * v;
     }
-    ss = wave_sum(ss);
-    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    float sq = wave_sum(v * v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sq;
     __syncthreads();
-    float tot = 0.0f;
-    for (int k = 0; k < NT_NORM / 64; ++k) tot += red[k];
-    const float inv = 1.0f / sqrtf(tot / (float)D + eps);
-    for (int d = tid; d < D; d += NT_NORM) {
-        const float v = bf16_to_f32(r[d]);  // this thread wrote r[d] above
-        h[(int64_t)m * D + d] = f32_to_bf16(v * inv * bf16_to_f32(gamma[d]));
+    if (threadIdx.x == 0) ssq[(int64_t)m * gridDim.x + ch] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ __launch_bounds__(NCOL) void rmsnorm_apply_kernel(const uint16_t* __restrict__ resid,
+                                                             const uint16_t* __restrict__ gamma, float eps, int D,
+                                                             const float* __restrict__ ssq, int nch,
+                                                             uint16_t* __restrict__ h) {
+    __shared__ float s_ssq[NMAXCH];
+    __shared__ float s_tot;
+    const int ch = blockIdx.x, m = blockIdx.y, d = ch * NCOL + threadIdx.x;
+    for (int k = threadIdx.x; k < nch; k += NCOL) s_ssq[k] = ssq[(int64_t)m * nch + k];  // loads in parallel
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float tot = 0.0f;
+        for (int k = 0; k < nch; ++k) tot += s_ssq[k];  // chunk order
+        s_tot = tot;
     }
+    __syncthreads();
+    if (d >= D) return;
+    const float inv = 1.0f / sqrtf(s_tot / (float)D + eps);
+    const float r = bf16_to_f32(resid[(int64_t)m * D + d]);
+    h[(int64_t)m * D + d] = f32_to_bf16(r * inv * bf16_to_f32(gamma[d]));
 }
 
 // ---------------------------------------------------------------------------
@@ -270,16 +297,29 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const uint16_t* __restr
 __global__ __launch_bounds__(AHD) void attn_combine_kernel(const float* __restrict__ ws_o,
                                                            const AttnPart* __restrict__ ws_ml, int nparts, int QN, int M,
                                                            int nq, int G, uint16_t* __restrict__ out) {
+    __shared__ float s_f[64], s_l[64];
     const int j = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
     const int64_t base = ((int64_t)h * QN + j) * nparts;
-    float mx = -INFINITY;
-    for (int c = 0; c < nparts; ++c) mx = fmaxf(mx, ws_ml[base + c].m);
+    // chunk maxima and sums: one chunk per thread (nparts <= 64), loads in parallel
+    if (d < 64) {
+        const AttnPart ap = (d < nparts) ? ws_ml[base + d] : AttnPart{-INFINITY, 0.0f};
+        float mx = ap.m;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        s_f[d] = (ap.m == -INFINITY) ? 0.0f : expf(ap.m - mx);
+        s_l[d] = ap.l;
+    }
+    __syncthreads();
+    float o[64];
+#pragma unroll
+    for (int c = 0; c < 64; ++c) o[c] = (c < nparts) ? ws_o[(base + c) * AHD + d] : 0.0f;
     float lt = 0.0f, ot = 0.0f;
-    for (int c = 0; c < nparts; ++c) {
-        const AttnPart ap = ws_ml[base + c];
-        const float f = (ap.m == -INFINITY) ? 0.0f : expf(ap.m - mx);
-        lt += f * ap.l;
-        ot += f * ws_o[(base + c) * AHD + d];
+#pragma unroll
+    for (int c = 0; c < 64; ++c) {
+        if (c < nparts) {
+            lt += s_f[c] * s_l[c];
+            ot += s_f[c] * o[c];
+        }
     }
     const int row = j % M, head = h * G + j / M;
     out[((int64_t)row * nq + head) * AHD + d] = f32_to_bf16(ot / lt);
@@ -314,14 +354,24 @@ using namespace vw4;
 
 extern "C" {
 
+size_t vw4_norm_workspace_bytes(int32_t M, int32_t D) {
+    if (M < 1 || M > 64 || D < 1 || D > 65536) return 0;
+    return ((size_t)M * ((D + NCOL - 1) / NCOL) * sizeof(float) + 255) / 256 * 256;
+}
+
 int vw4_add_rmsnorm(uint16_t* resid, const float* part, int32_t S, int64_t ldp, const uint16_t* gamma, float eps,
-                    int32_t M, int32_t D, uint16_t* h, void* stream) {
+                    int32_t M, int32_t D, uint16_t* h, void* ws, size_t ws_bytes, void* stream) {
     VW4_REQUIRE(resid && gamma && h, VW4_EINVAL, "vw4_add_rmsnorm: null pointer");
     VW4_REQUIRE(M >= 1 && M <= 64 && D >= 1 && D <= 65536, VW4_EINVAL, "vw4_add_rmsnorm: bad shape M=%d D=%d", M, D);
     VW4_REQUIRE(!part || (S >= 1 && ldp >= D), VW4_EINVAL, "vw4_add_rmsnorm: bad partial layout");
     VW4_REQUIRE(eps >= 0.0f, VW4_EINVAL, "vw4_add_rmsnorm: eps must be >= 0");
-    hipLaunchKernelGGL(add_rmsnorm_kernel, dim3(M), dim3(NT_NORM), 0, (hipStream_t)stream, resid, part, S, ldp, gamma,
-                       eps, M, D, h);
+    const size_t need = vw4_norm_workspace_bytes(M, D);
+    VW4_REQUIRE(ws && ws_bytes >= need, VW4_EWORKSPACE, "vw4_add_rmsnorm: needs a workspace of %zu bytes", need);
+    const int nch = (D + NCOL - 1) / NCOL;
+    hipStream_t st = (hipStream_t)stream;
+    hipLaunchKernelGGL(add_sumsq_kernel, dim3(nch, M), dim3(NCOL), 0, st, resid, part, S, ldp, M, D, (float*)ws);
+    hipLaunchKernelGGL(rmsnorm_apply_kernel, dim3(nch, M), dim3(NCOL), 0, st, resid, gamma, eps, D, (const float*)ws,
+                       nch, h);
     return check_launch("vw4_add_rmsnorm");
 }
 

@@ -131,6 +131,7 @@ class Decoder:
             S, ldp = B.gemm_partials_layout(M_max, N, K)
             self.parts[name] = torch.empty(S * M_max * ldp, dtype=torch.float32, device=device)
         self.attn_ws = B.workspace(B.attn_workspace_bytes(M_max, nq, nkv, hd, Lmax), device)
+        self.norm_ws = B.workspace(B.norm_workspace_bytes(M_max, d), device)
         self.logits = torch.empty((M_max, V), dtype=torch.float32, device=device)
         self.lm_ws = B.workspace(B.gemm_workspace_bytes(M_max, V, d), device)
 
@@ -173,7 +174,7 @@ class Decoder:
         resid, h = self.resid[:M], self.h[:M]
         resid.copy_(x[:M])
         lay = self.layers
-        B.add_rmsnorm(resid, None, 1, d, lay[0]["g1"], eps, M, d, h, stream)
+        B.add_rmsnorm(resid, None, 1, d, lay[0]["g1"], eps, M, d, h, self.norm_ws, stream)
         for li, W in enumerate(lay):
             # attention block
             N, K = self.shapes["qkv"]
@@ -190,7 +191,7 @@ class Decoder:
             hook("pre", "o")
             B.w4_skinny_gemm_partials(self.attn, W["o"].packed, W["o"].pscales, self.parts["o"], M, N, K, stream)
             hook("post", "o")
-            B.add_rmsnorm(resid, self.parts["o"], S, ldp, W["g2"], eps, M, d, h, stream)
+            B.add_rmsnorm(resid, self.parts["o"], S, ldp, W["g2"], eps, M, d, h, self.norm_ws, stream)
             # FFN block
             N, K = self.shapes["gate_up"]
             S, ldp = B.gemm_partials_layout(M, N, K)
@@ -206,7 +207,7 @@ class Decoder:
                                       stream)
             hook("post", "down")
             g_next = lay[li + 1]["g1"] if li + 1 < len(lay) else self.final_gamma
-            B.add_rmsnorm(resid, self.parts["down"], S, ldp, g_next, eps, M, d, h, stream)
+            B.add_rmsnorm(resid, self.parts["down"], S, ldp, g_next, eps, M, d, h, self.norm_ws, stream)
         hook("pre", "lm_head")
         B.w4_skinny_gemm(h, self.lm_head.packed, self.lm_head.pscales, self.logits[:M], M, c["V"], d,
                          ws=self.lm_ws, stream=stream)
@@ -240,6 +241,34 @@ class VerifyStep:
         self.tokens = torch.empty((1, M), dtype=torch.int32, device=dev)
         self.n_acc = torch.empty(1, dtype=torch.int32, device=dev)
         self.flags = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def run_graphable(self, x, L: int, q, drafts, T: float, top_p: float, seed: int, step_dev, stream=None):
+        """The same step with the Philox step read from device memory and
+        advanced by one at the end, so the sequence can be captured once and
+        replayed (each replay is a new verify step)."""
+        dec, M, V = self.dec, self.M, self.dec.cfg["V"]
+        logits = dec.forward(x, L, M, stream)
+        B.verify_logits(None, None, None, M, V, dec.cfg["d"], T, top_p, logits, self.stats, self.stat_ws,
+                        stream=stream)
+        B.spec_accept_ex(logits, 0, self.stats, 0, q, 0, drafts, 1, self.D, V, T, seed, step_dev, self.tokens,
+                         self.n_acc, self.flags, self.acc_ws, stream=stream)
+        B.step_advance(step_dev, 1, stream)
+
+    def capture(self, x, L: int, q, drafts, T: float, top_p: float, seed: int, step_dev):
+        """Record the verify step into a HIP graph (torch.cuda.CUDAGraph) on a
+        side stream; replay() then re-issues every kernel with one launch."""
+        import torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.run_graphable(x, L, q, drafts, T, top_p, seed, step_dev)  # warm (plans, code objects)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run_graphable(x, L, q, drafts, T, top_p, seed, step_dev)
+        torch.cuda.synchronize()
+        return g
 
     def run(self, x, L: int, q, drafts, T: float, top_p: float, seed: int, step: int, stream=None, gemm_hook=None,
             **out):
