@@ -89,6 +89,7 @@ def lib():
         L.oracle_rope.argtypes = [_P, _I64, _I64, _F64, _P]
         L.oracle_decode_attn.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]
         L.oracle_moe_route.argtypes = [_P, _I64, _I64, _I64, _P, _P]
+        L.oracle_swiglu_f64.argtypes = [_P, _P, _I64, _P]
         _lib = L
     return _lib
 
@@ -263,11 +264,19 @@ def rmsnorm(x_bf16: np.ndarray, gamma_bf16: np.ndarray, eps: float = 1e-6) -> np
     return y
 
 
-def swiglu(g_bf16: np.ndarray, u_bf16: np.ndarray) -> np.ndarray:
-    g = np.ascontiguousarray(g_bf16, dtype=np.uint16)
-    u = np.ascontiguousarray(u_bf16, dtype=np.uint16)
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """silu(g) * u; uint16 inputs are bf16 bit patterns, anything else is taken as fp64 values."""
+    if np.asarray(g).dtype == np.uint16:
+        g = np.ascontiguousarray(g, dtype=np.uint16)
+        u = np.ascontiguousarray(u, dtype=np.uint16)
+        fn = lib().oracle_swiglu
+    else:
+        g = np.ascontiguousarray(g, dtype=np.float64)
+        u = np.ascontiguousarray(u, dtype=np.float64)
+        fn = lib().oracle_swiglu_f64
+    assert g.shape == u.shape
     y = np.zeros(g.shape, dtype=np.float64)
-    lib().oracle_swiglu(_ptr(g), _ptr(u), g.size, _ptr(y))
+    fn(_ptr(g), _ptr(u), g.size, _ptr(y))
     return y
 
 
@@ -297,3 +306,34 @@ def moe_route(logits: np.ndarray, topk: int):
     wt = np.zeros((M, topk), dtype=np.float64)
     lib().oracle_moe_route(_ptr(lg), M, E, topk, _ptr(ex), _ptr(wt))
     return ex, wt
+
+
+def moe_block(x_bf16: np.ndarray, router_logits: np.ndarray, topk: int, gate_up, down):
+    """Mixture-of-experts FFN of the verify rows, expert by expert in fp64.
+
+    Routing as moe_route (top-k by router logit, softmax weights renormalised
+    over the chosen experts).  Expert e: gate|up = gate_up[e] (codes, scales)
+    of a [2F][K] W4 matrix whose rows [0, F) are the gate and [F, 2F) the up
+    projection; a = bf16(silu(g) * u) on the unrounded products; the expert's
+    output is down[e] (a [D][F] W4 matrix) applied to a.  Row m's output is
+    sum_t w[m][t] * expert_{experts[m][t]}(x_m), in selection order.
+    gate_up / down: (codes [E][N][K/2], scales [E][N][K/64]).
+    Returns (experts [M][topk], weights [M][topk], y float64 [M][D]).
+    (gist.science, "BaseRT: Best-in-Class LLM Inference on Apple Silicon via
+    Native Metal", section "結果": mixture-of-experts models such as
+    Qwen3-30B-A3B, 128 experts with 8 active.)"""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    M = x.shape[0]
+    ex, wt = moe_route(router_logits, topk)
+    gu_c, gu_s = gate_up
+    dn_c, dn_s = down
+    F = gu_c.shape[1] // 2
+    D = dn_c.shape[1]
+    y = np.zeros((M, D), dtype=np.float64)
+    for m in range(M):
+        for t in range(topk):
+            e = int(ex[m, t])
+            gu = w4_gemm(x[m:m + 1], gu_c[e], gu_s[e])
+            a = bf16_round(swiglu(gu[:, :F], gu[:, F:]))
+            y[m] += wt[m, t] * w4_gemm(a, dn_c[e], dn_s[e])[0]
+    return ex, wt, y

@@ -486,11 +486,16 @@ EXPORT void oracle_rmsnorm(const uint16_t* x_bf16, const uint16_t* gamma_bf16, i
 }
 
 /* SwiGLU: silu(g) * u with silu(g) = g / (1 + exp(-g)). */
+static double swiglu1(double g, double u) { return g / (1.0 + exp(-g)) * u; }
+
 EXPORT void oracle_swiglu(const uint16_t* g_bf16, const uint16_t* u_bf16, int64_t n, double* y) {
-    for (int64_t i = 0; i < n; ++i) {
-        double g = bf16_value(g_bf16[i]), u = bf16_value(u_bf16[i]);
-        y[i] = g / (1.0 + exp(-g)) * u;
-    }
+    for (int64_t i = 0; i < n; ++i) y[i] = swiglu1(bf16_value(g_bf16[i]), bf16_value(u_bf16[i]));
+}
+
+/* The same on unrounded gate/up values (a GEMM's fp64 output handed on
+ * without an intermediate bf16 store). */
+EXPORT void oracle_swiglu_f64(const double* g, const double* u, int64_t n, double* y) {
+    for (int64_t i = 0; i < n; ++i) y[i] = swiglu1(g[i], u[i]);
 }
 
 /* Rotary embedding, rotate-half convention (RoFormer), base theta:

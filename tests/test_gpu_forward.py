@@ -75,7 +75,7 @@ def _oracle_forward(cfg, hm, Kc, Vc, x, L):
         resid = oracle.bf16_round(oracle.bf16_value(resid) + o)
         h = oracle.bf16_round(oracle.rmsnorm(resid, l["g2"], eps))
         gu = oracle.w4_gemm(h, *Q["gate_up"])
-        a = oracle.bf16_round(oracle.swiglu(oracle.bf16_round(gu[:, :F]), oracle.bf16_round(gu[:, F:])))
+        a = oracle.bf16_round(oracle.swiglu(gu[:, :F], gu[:, F:]))
         dn = oracle.w4_gemm(a, *Q["down"])
         resid = oracle.bf16_round(oracle.bf16_value(resid) + dn)
     h = oracle.bf16_round(oracle.rmsnorm(resid, hm["final_gamma"], eps))

@@ -36,6 +36,66 @@ def test_swiglu_against_torch():
     np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-300)
 
 
+def test_swiglu_f64_against_torch():
+    g = synth.normal_f32(synth.rng(13), (2048,), 4.0).astype(np.float64) / 3.0
+    u = synth.normal_f32(synth.rng(14), (2048,), 1.0).astype(np.float64) * 1.1
+    y = oracle.swiglu(g, u)
+    ref = (torch.nn.functional.silu(torch.from_numpy(g)) * torch.from_numpy(u)).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-300)
+
+
+def _dequant(codes, scales):
+    """fp64 weights from the canonical format: code c (u - 8) times the fp16 scale of its group."""
+    c = oracle.w4_codes_int(codes).astype(np.float64)
+    s = np.vectorize(oracle.f16_value)(scales).astype(np.float64)
+    return c * np.repeat(s, 64, axis=1)
+
+
+def _moe_bank(seed, E, F, D):
+    gu = [oracle.w4_quantize(synth.linear_weights(seed + e, 2 * F, D)) for e in range(E)]
+    dn = [oracle.w4_quantize(synth.linear_weights(seed + 100 + e, D, F)) for e in range(E)]
+    stack = lambda L: (np.stack([a for a, _ in L]), np.stack([b for _, b in L]))
+    return stack(gu), stack(dn)
+
+
+def test_moe_block_brute_force():
+    """Expert-by-expert against numpy: dequantised fp64 matrices, argsort routing,
+    softmax weights, gate = first F rows, SwiGLU, down projection."""
+    E, F, D, topk, M = 6, 64, 128, 3, 3
+    gate_up, down = _moe_bank(300, E, F, D)
+    x = synth.activations_bf16(301, M, D)
+    lg = synth.synthetic_logits(302, M, E, 1.0)
+    ex, wt, y = oracle.moe_block(x, lg, topk, gate_up, down)
+    xf = synth.bf16_bits_to_f32(x).astype(np.float64)
+    ref = np.zeros((M, D))
+    for m in range(M):
+        order = np.argsort(-lg[m].astype(np.float64), kind="stable")[:topk]
+        p = np.exp(lg[m].astype(np.float64) - lg[m].max())
+        w = p[order] / p[order].sum()
+        for e, we in zip(order, w):
+            W1 = _dequant(gate_up[0][e], gate_up[1][e])
+            h = W1 @ xf[m]
+            g, u = h[:F], h[F:]
+            a = synth.bf16_bits_to_f32(oracle.bf16_round(g / (1 + np.exp(-g)) * u)).astype(np.float64)
+            ref[m] += we * (_dequant(down[0][e], down[1][e]) @ a)
+    np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+    assert (ex == np.stack([np.argsort(-lg[m].astype(np.float64), kind="stable")[:topk] for m in range(M)])).all()
+
+
+def test_moe_block_identical_experts_is_dense():
+    """With every expert equal, the renormalised weights sum to one and the
+    block is the single expert's FFN whatever the routing."""
+    E, F, D, topk, M = 5, 64, 128, 2, 2
+    gate_up, down = _moe_bank(400, 1, F, D)
+    gate_up = tuple(np.repeat(a, E, axis=0) for a in gate_up)
+    down = tuple(np.repeat(a, E, axis=0) for a in down)
+    x = synth.activations_bf16(401, M, D)
+    _, _, y = oracle.moe_block(x, synth.synthetic_logits(402, M, E, 1.0), topk, gate_up, down)
+    _, _, y1 = oracle.moe_block(x, np.zeros((M, 1), np.float32), 1, tuple(a[:1] for a in gate_up),
+                                tuple(a[:1] for a in down))
+    np.testing.assert_allclose(y, y1, rtol=1e-13, atol=1e-15)
+
+
 def test_rope_rotation_properties():
     g = np.random.default_rng(5)
     q = g.standard_normal(128)
