@@ -248,6 +248,57 @@ VW4_API int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_
                             int32_t M, int32_t nq, int32_t nkv, int32_t hd, uint16_t* out, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* ------------------------------------------------------------------------
+ * Mixture-of-experts calls of the MoE-shaped verify step (gist.science,
+ * "BaseRT: Best-in-Class LLM Inference on Apple Silicon via Native Metal",
+ * section "結果": MoE models of the Qwen3-30B-A3B class, 128 experts with 8
+ * active).  Each verify row is routed on its own; the distinct experts chosen
+ * by any row form device-side "slots", so no call reads the routing on the
+ * host and the whole step can be captured as a HIP graph.
+ * ------------------------------------------------------------------------ */
+
+/* Router: per row m of logits [M][E] (fp32), the topk experts with the
+ * largest logits (equal logits: lower index first) -> experts[M][topk] in that
+ * order, and their softmax probabilities renormalised over the chosen ones ->
+ * weights[M][topk] (fp64 arithmetic, stored fp32).  Slots: the distinct
+ * chosen experts in ascending order -> slot_expert[0 .. *n_slots) (at most
+ * min(E, M * topk) entries are written); row_slot[M][topk] = slot of
+ * experts[m][t].  Limits: M <= 16, E <= 1024, topk <= min(E, 64).  Logits are
+ * expected finite; non-finite ones still give valid indices. */
+VW4_API int vw4_moe_route(const float* logits, int32_t M, int32_t E, int32_t topk, int32_t* experts, float* weights,
+                          int32_t* slot_expert, int32_t* n_slots, int32_t* row_slot, void* stream);
+
+/* Grouped W4 GEMM over the slots: for every slot s < *n_slots (device
+ * value; launches cover max_slots slots and the rest exit), expert
+ * e = slot_expert[s], part[s] = split-K partials (as w4_skinny_gemm_partials,
+ * [S][M][ldp] from vw4_grouped_gemm_layout) of x_s . W_e^T with
+ * x_s = x + s * x_sstride ([M][K], row stride ldx, bf16) and W_e the packed W4
+ * matrix at w_bank + e * w_estride bytes with its packed scales at
+ * s_bank + e * s_estride fp16 elements.  Slot s's partials start at
+ * part + s * p_sstride floats, p_sstride >= S * M * ldp.  An [E * N][K] matrix
+ * packed by vw4_w4_pack with N % 64 == 0 is such a bank with
+ * w_estride = N * K / 2 and s_estride = N * K / 64.  x_sstride = 0 gives every
+ * slot the same rows. */
+VW4_API int vw4_grouped_gemm_layout(int32_t M, int32_t N, int32_t K, int32_t max_slots, int32_t* S, int64_t* ldp);
+VW4_API int w4_grouped_gemm(const uint16_t* x, int64_t ldx, int64_t x_sstride, const uint8_t* w_bank,
+                            int64_t w_estride, const uint16_t* s_bank, int64_t s_estride, const int32_t* slot_expert,
+                            const int32_t* n_slots, int32_t max_slots, float* part, int64_t p_sstride, int32_t M,
+                            int32_t N, int32_t K, void* stream);
+
+/* vw4_swiglu per slot: slot s < *n_slots reads partials at
+ * part + s * p_sstride and writes a + s * a_sstride ([M][F] bf16). */
+VW4_API int vw4_grouped_swiglu(const float* part, int32_t S, int64_t ldp, int64_t p_sstride, int32_t M, int32_t F,
+                               uint16_t* a, int64_t a_sstride, const int32_t* n_slots, int32_t max_slots,
+                               void* stream);
+
+/* y[m][d] (fp32, row stride ldy) = sum_t weights[m][t] * (expert output of
+ * row m in slot row_slot[m][t]), the expert output being the sum of the slot's
+ * down-projection partials part[slot][s][m][d] (S slices, row stride ldp,
+ * slots p_sstride floats apart).  Experts in selection order, fp32. */
+VW4_API int vw4_moe_combine(const float* part, int32_t S, int64_t ldp, int64_t p_sstride, const int32_t* row_slot,
+                            const float* weights, int32_t M, int32_t topk, int32_t D, float* y, int64_t ldy,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

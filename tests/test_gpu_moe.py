@@ -1,0 +1,254 @@
+"""GPU parity of the MoE calls (a10) against the oracle: router top-k and
+slot list, grouped W4 GEMM, grouped SwiGLU + down + combine (the whole
+expert layer), and the MoE-shaped verify step.
+
+Routing is integer work and must match bit for bit (experts, slot list);
+the routing weights are fp64 on both sides, stored fp32 (relative 2^-24).
+Expert outputs follow the GEMM bar (1e-3 relative to max(|ref|, row rms));
+the full step's logits follow the forward's looser bar, since a bf16
+rounding flip upstream moves them by about one bf16 ulp."""
+import numpy as np
+import pytest
+
+import oracle
+from verify_step_w4_amd import binding as B
+from verify_step_w4_amd import synth
+from verify_step_w4_amd.model import MOE_30B, ExpertBank, MoEVerify, W4Linear
+
+from helpers import GEMM_RTOL, dev, gemm_rel_err, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _route(lg, topk):
+    import torch
+    M, E = lg.shape
+    ms = min(E, M * topk)
+    ex = torch.empty((M, topk), dtype=torch.int32, device="cuda")
+    wt = torch.empty((M, topk), dtype=torch.float32, device="cuda")
+    se = torch.full((ms,), -7, dtype=torch.int32, device="cuda")
+    ns = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rs = torch.empty((M, topk), dtype=torch.int32, device="cuda")
+    B.moe_route(dev(lg), M, E, topk, ex, wt, se, ns, rs)
+    torch.cuda.synchronize()
+    return host(ex), host(wt), host(se), int(host(ns)[0]), host(rs)
+
+
+def _check_route(lg, topk):
+    ex, wt, se, ns, rs = _route(lg, topk)
+    ex_o, wt_o = oracle.moe_route(lg, topk)
+    assert np.array_equal(ex, ex_o)
+    np.testing.assert_allclose(wt.astype(np.float64), wt_o, rtol=1.2e-7, atol=0)
+    uniq = np.unique(ex_o)
+    assert ns == len(uniq) and np.array_equal(se[:ns], uniq)
+    assert (se[ns:] == -7).all()                      # nothing beyond the live slots is written
+    assert np.array_equal(se[rs], ex)                 # row_slot names the slot of each choice
+    return ns
+
+
+@pytest.mark.parametrize("M,E,topk,seed", [(4, 128, 8, 1), (1, 128, 8, 2), (6, 128, 8, 3), (16, 1024, 64, 4),
+                                           (3, 5, 5, 5), (2, 64, 1, 6)])
+def test_moe_route(M, E, topk, seed):
+    log(f"moe_route M={M} E={E} topk={topk}")
+    lg = synth.synthetic_logits(seed, M, E, 1.0)
+    _check_route(lg, topk)
+
+
+def test_moe_route_ties_and_signed_zero():
+    M, E, topk = 4, 128, 8
+    lg = synth.synthetic_logits(9, M, E, 1.0)
+    lg[0, 10] = lg[0, 3] = lg[0, 77] = lg[0].max() + 0.5     # three-way tie at the top -> 3, 10, 77
+    lg[1] = 0.0
+    lg[1, 5] = -0.0                                           # -0 == +0: index order decides
+    lg[2, :] = np.float32(-1.0)
+    lg[2, 100] = np.float32(-1.0) + np.float32(2.0 ** -23)    # one ulp above the rest
+    lg[3, ::2] = lg[3, 1::2]                                  # pairs of equal logits
+    ns = _check_route(lg, topk)
+    ex, _, _, _, _ = _route(lg, topk)
+    assert list(ex[0, :3]) == [3, 10, 77]
+    assert list(ex[1]) == list(range(8))
+    assert ex[2, 0] == 100 and list(ex[2, 1:]) == list(range(7))
+    assert ns <= M * topk
+
+
+def _host_bank(seed, E, F, d):
+    g = synth.rng(seed)
+    gu = synth.normal_f32(g, (E, 2 * F, d), 0.02)
+    dn = synth.normal_f32(g, (E, d, F), 0.02)
+    return gu, dn
+
+
+def _oracle_bank(gu, dn):
+    q_gu = [oracle.w4_quantize(w) for w in gu]
+    q_dn = [oracle.w4_quantize(w) for w in dn]
+    st = lambda L: (np.stack([a for a, _ in L]), np.stack([b for _, b in L]))
+    return st(q_gu), st(q_dn)
+
+
+@pytest.mark.parametrize("M,N,K,E,slots,max_slots", [(4, 1536, 2048, 6, [5, 0, 3], 5), (1, 192, 320, 4, [3], 1),
+                                                     (6, 2048, 768, 3, [0, 1, 2], 8)])
+def test_grouped_gemm_against_oracle(M, N, K, E, slots, max_slots):
+    """Given slot list: live slots equal the oracle's per-expert GEMM; slots at
+    or beyond n_slots are not written."""
+    import torch
+    log(f"grouped gemm M={M} N={N} K={K} E={E} slots={slots}")
+    w = synth.normal_f32(synth.rng(N + K), (E, N, K), 0.02)
+    bank = W4Linear.from_fp32(dev(w.reshape(E * N, K)))
+    x = synth.activations_bf16(K + M, M, K)
+    S, ldp = B.grouped_gemm_layout(M, N, K, max_slots)
+    sst = S * M * ldp
+    part = torch.full((max_slots * sst,), float("nan"), dtype=torch.float32, device="cuda")
+    se = torch.zeros(max_slots, dtype=torch.int32, device="cuda")
+    se[:len(slots)] = torch.tensor(slots, dtype=torch.int32)
+    ns = torch.tensor([len(slots)], dtype=torch.int32, device="cuda")
+    B.w4_grouped_gemm(dev(x), K, 0, bank.packed, N * K // 2, bank.pscales, N * K // 64, se, ns, max_slots, part, sst,
+                      M, N, K)
+    torch.cuda.synchronize()
+    P = host(part).reshape(max_slots, S, M, ldp)
+    for s, e in enumerate(slots):
+        codes, scales = oracle.w4_quantize(w[e])
+        ref = oracle.w4_gemm(x, codes, scales)
+        y = P[s].astype(np.float64).sum(axis=0)[:, :N]
+        err = gemm_rel_err(y, ref)
+        assert err <= GEMM_RTOL, (s, e, err)
+    assert np.isnan(P[len(slots):]).all()
+
+
+def _moe_device(cfg, M, gu, dn, lm_w, gamma):
+    bank = ExpertBank.from_fp32(dev(gu), dev(dn))
+    mv = MoEVerify(cfg, M, W4Linear.from_fp32(dev(lm_w)), dev(gamma))
+    return bank, mv
+
+
+@pytest.mark.parametrize("E,topk,d,F,M", [(16, 4, 512, 256, 4), (8, 8, 2048, 768, 4), (12, 3, 256, 128, 6),
+                                          (128, 8, 256, 64, 1)])
+def test_moe_layer_against_oracle(E, topk, d, F, M):
+    """Route + grouped gate|up + grouped SwiGLU + grouped down + combine vs the
+    oracle's expert-by-expert block on the same weights and router logits."""
+    import torch
+    log(f"moe layer E={E} topk={topk} d={d} F={F} M={M}")
+    cfg = dict(n_exp=E, topk=topk, d=d, F=F, V=64, eps=1e-6)
+    gu, dn = _host_bank(E + d, E, F, d)
+    lm_w = synth.linear_weights(7, 64, d)
+    gamma = synth.f32_to_bf16_bits(1 + synth.normal_f32(synth.rng(8), (d,), 0.02))
+    bank, mv = _moe_device(cfg, M, gu, dn, lm_w, gamma)
+    x = synth.activations_bf16(E + F, M, d)
+    lg = synth.synthetic_logits(E + M, M, E, 1.0)
+    y = host(mv.moe(dev(x), dev(lg), bank)).astype(np.float64)
+    torch.cuda.synchronize()
+    ex, wt, ref = oracle.moe_block(x, lg, topk, *_oracle_bank(gu, dn))
+    assert np.array_equal(host(mv.experts), ex)
+    err = gemm_rel_err(y, ref)
+    print(f"[moe] n_slots {int(host(mv.n_slots)[0])} rel err {err:.3e}", flush=True)
+    assert err <= 2e-3
+
+
+def test_moe_step_logits_against_oracle():
+    """The whole MoE-shaped forward to the logits: x + moe(x), final RMSNorm, LM head."""
+    import torch
+    E, topk, d, F, M, V = 16, 4, 512, 256, 4, 3000
+    log("moe step logits vs oracle")
+    cfg = dict(n_exp=E, topk=topk, d=d, F=F, V=V, eps=1e-6)
+    gu, dn = _host_bank(31, E, F, d)
+    lm_w = synth.linear_weights(32, V, d)
+    gamma = synth.f32_to_bf16_bits(1 + synth.normal_f32(synth.rng(33), (d,), 0.02))
+    bank, mv = _moe_device(cfg, M, gu, dn, lm_w, gamma)
+    x = synth.activations_bf16(34, M, d)
+    lg = synth.synthetic_logits(35, M, E, 1.0)
+    logits = host(mv.forward(dev(x), dev(lg), bank)).astype(np.float64)
+    torch.cuda.synchronize()
+    _, _, y = oracle.moe_block(x, lg, topk, *_oracle_bank(gu, dn))
+    resid = oracle.bf16_round(synth.bf16_bits_to_f32(x).astype(np.float64) + y)
+    h = oracle.bf16_round(oracle.rmsnorm(resid, gamma, 1e-6))
+    ref = oracle.w4_gemm(h, *oracle.w4_quantize(lm_w))
+    rms = np.sqrt((ref ** 2).mean(axis=1, keepdims=True))
+    rel = np.abs(logits - ref) / np.maximum(np.abs(ref), rms)
+    print(f"[moe step] max rel {rel.max():.3e} median {np.median(rel):.3e}", flush=True)
+    assert rel.max() < 2e-2 and np.median(rel) < 2e-3
+    assert np.mean(host(mv.resid) == resid) > 0.97
+
+
+def _full_moe(seed):
+    import torch
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    c = MOE_30B
+    bank = ExpertBank.random(c["n_exp"], c["d"], c["F"], 0.02, gen)
+    lm = W4Linear.random(c["V"], c["d"], 0.02, gen)
+    gamma = (1 + 0.02 * torch.randn(c["d"], generator=gen, device="cuda")).to(torch.bfloat16).view(torch.int16)
+    return bank, MoEVerify(c, 4, lm, gamma)
+
+
+def test_moe_full_size_grouped_equals_per_expert_dense():
+    """At 128 experts x (2048 -> 768 -> 2048): the grouped expert layer equals
+    the same experts run one by one through the dense W4 GEMM calls and
+    combined on the host in fp64 with the router's weights."""
+    import torch
+    log("moe full size: grouped == per-expert dense")
+    bank, mv = _full_moe(21)
+    c = MOE_30B
+    M, d, F = 4, c["d"], c["F"]
+    x = dev(synth.activations_bf16(22, M, d))
+    lg = synth.synthetic_logits(23, M, c["n_exp"], 1.0)
+    y = host(mv.moe(x, dev(lg), bank)).astype(np.float64)
+    torch.cuda.synchronize()
+    ex_o, wt_o = oracle.moe_route(lg, c["topk"])
+    assert np.array_equal(host(mv.experts), ex_o)
+    ref = np.zeros((M, d))
+    gus, gul = bank.gu_estride
+    dns, dnl = bank.dn_estride
+    a = torch.empty((M, F), dtype=torch.int16, device="cuda")
+    out = torch.empty((M, d), dtype=torch.float32, device="cuda")
+    ws = B.workspace(max(B.gemm_workspace_bytes(M, d, F), 256))
+    for e in sorted(set(ex_o.reshape(-1).tolist())):
+        S, ldp = B.gemm_partials_layout(M, 2 * F, d)
+        part = torch.empty(S * M * ldp, dtype=torch.float32, device="cuda")
+        B.w4_skinny_gemm_partials(x, bank.gate_up.packed[e * gus:(e + 1) * gus],
+                                  bank.gate_up.pscales[e * gul:(e + 1) * gul], part, M, 2 * F, d)
+        B.swiglu(part, S, ldp, M, F, a)
+        B.w4_skinny_gemm(a, bank.down.packed[e * dns:(e + 1) * dns], bank.down.pscales[e * dnl:(e + 1) * dnl], out,
+                         M, d, F, ws=ws)
+        o = host(out).astype(np.float64)
+        for m in range(M):
+            for t in range(c["topk"]):
+                if ex_o[m, t] == e:
+                    ref[m] += wt_o[m, t] * o[m]
+    err = gemm_rel_err(y, ref)
+    print(f"[moe full] rel err {err:.3e}", flush=True)
+    assert err <= GEMM_RTOL
+
+
+def test_moe_step_graph_replay_matches_eager():
+    """Full-size MoE verify step as a HIP graph: new router logits copied into
+    the captured buffer before each replay; tokens and logits equal the eager
+    step with the same inputs and Philox step."""
+    import torch
+    log("moe full size: graph replay == eager")
+    bank, mv = _full_moe(24)
+    c = MOE_30B
+    M = 4
+    x = dev(synth.activations_bf16(25, M, c["d"]))
+    pool = [dev(synth.synthetic_logits(26 + k, M, c["n_exp"], 1.0)) for k in range(3)]
+    q, drafts = synth.q_and_drafts(27, M - 1, c["V"], 3.0, B=1)
+    qd, dd = dev(q), dev(drafts[0])
+    seed, T, top_p = 0x5EED0006, 0.6, 0.95
+    eager = []
+    for k in range(3):
+        tok, nacc, _ = mv.run(x, pool[k], bank, qd, dd, T, top_p, seed, k)
+        torch.cuda.synchronize()
+        eager.append((host(tok).copy(), host(nacc).copy(), host(mv.logits).copy(), int(host(mv.n_slots)[0])))
+    lg_buf = pool[0].clone()
+    step_dev = torch.zeros(1, dtype=torch.int64, device="cuda")
+    g = mv.capture(x, lg_buf, bank, qd, dd, T, top_p, seed, step_dev)
+    step_dev.zero_()
+    torch.cuda.synchronize()
+    for k in range(3):
+        lg_buf.copy_(pool[k])
+        g.replay()
+        torch.cuda.synchronize()
+        _ = torch.ones(1000, device="cuda").sum().item()
+        assert np.array_equal(host(mv.logits), eager[k][2]), k
+        assert np.array_equal(host(mv.tokens), eager[k][0]) and np.array_equal(host(mv.n_acc), eager[k][1]), k
+        assert int(host(mv.n_slots)[0]) == eager[k][3]
+    n = int(eager[0][1][0])
+    assert 0 <= n <= M - 1

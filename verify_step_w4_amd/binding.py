@@ -66,6 +66,13 @@ SIGNATURES = {
     "vw4_swiglu": (ctypes.c_int, [_P, _I32, _I64, _I32, _I32, _P, _P]),
     "vw4_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I64]),
     "vw4_decode_attn": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "vw4_moe_route": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
+    "vw4_grouped_gemm_layout": (ctypes.c_int, [_I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
+                                               ctypes.POINTER(ctypes.c_int64)]),
+    "w4_grouped_gemm": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _I32, _P, _I64, _I32, _I32, _I32,
+                                       _P]),
+    "vw4_grouped_swiglu": (ctypes.c_int, [_P, _I32, _I64, _I64, _I32, _I32, _P, _I64, _P, _I32, _P]),
+    "vw4_moe_combine": (ctypes.c_int, [_P, _I32, _I64, _I64, _P, _P, _I32, _I32, _I32, _P, _I64, _P]),
 }
 
 
@@ -316,3 +323,38 @@ def decode_attn(q, Kc, Vc, Lmax: int, L: int, M: int, nq: int, nkv: int, hd: int
     _check("vw4_decode_attn", lib().vw4_decode_attn(_ptr(q), _ptr(Kc), _ptr(Vc), Lmax, L, M, nq, nkv, hd, _ptr(out),
                                                     _ptr(ws), ws.numel(), _stream(stream)))
     return out
+
+
+def moe_route(logits, M: int, E: int, topk: int, experts, weights, slot_expert, n_slots, row_slot, stream=None):
+    _check("vw4_moe_route", lib().vw4_moe_route(_ptr(logits), M, E, topk, _ptr(experts), _ptr(weights),
+                                                _ptr(slot_expert), _ptr(n_slots), _ptr(row_slot), _stream(stream)))
+
+
+def grouped_gemm_layout(M: int, N: int, K: int, max_slots: int):
+    S = ctypes.c_int32(0)
+    ldp = ctypes.c_int64(0)
+    _check("vw4_grouped_gemm_layout",
+           lib().vw4_grouped_gemm_layout(M, N, K, max_slots, ctypes.byref(S), ctypes.byref(ldp)))
+    return int(S.value), int(ldp.value)
+
+
+def w4_grouped_gemm(x, ldx: int, x_sstride: int, w_bank, w_estride: int, s_bank, s_estride: int, slot_expert,
+                    n_slots, max_slots: int, part, p_sstride: int, M: int, N: int, K: int, stream=None):
+    _check("w4_grouped_gemm", lib().w4_grouped_gemm(_ptr(x), ldx, x_sstride, _ptr(w_bank), w_estride, _ptr(s_bank),
+                                                    s_estride, _ptr(slot_expert), _ptr(n_slots), max_slots,
+                                                    _ptr(part), p_sstride, M, N, K, _stream(stream)))
+    return part
+
+
+def grouped_swiglu(part, S: int, ldp: int, p_sstride: int, M: int, F: int, a, a_sstride: int, n_slots,
+                   max_slots: int, stream=None):
+    _check("vw4_grouped_swiglu", lib().vw4_grouped_swiglu(_ptr(part), S, ldp, p_sstride, M, F, _ptr(a), a_sstride,
+                                                          _ptr(n_slots), max_slots, _stream(stream)))
+    return a
+
+
+def moe_combine(part, S: int, ldp: int, p_sstride: int, row_slot, weights, M: int, topk: int, D: int, y, ldy: int,
+                stream=None):
+    _check("vw4_moe_combine", lib().vw4_moe_combine(_ptr(part), S, ldp, p_sstride, _ptr(row_slot), _ptr(weights), M,
+                                                    topk, D, _ptr(y), ldy, _stream(stream)))
+    return y

@@ -77,4 +77,23 @@ __device__ __forceinline__ T wave_sum(T v) {
     return v;
 }
 
+// Sum over the S partial slices of element (m, c), slice order.  The loads
+// of 8 slices are issued together (a chain of dependent loads would pay one
+// memory latency per slice).
+__device__ __forceinline__ float sum_parts(const float* __restrict__ part, int S, int M, int64_t ldp, int m,
+                                           int64_t c) {
+    float s = 0.0f;
+    const int64_t stride = (int64_t)M * ldp;
+    const float* p = part + (int64_t)m * ldp + c;
+    for (int k0 = 0; k0 < S; k0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (k0 + i < S) ? p[(int64_t)(k0 + i) * stride] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (k0 + i < S) s += v[i];
+    }
+    return s;
+}
+
 }  // namespace vw4

@@ -19,25 +19,6 @@
 
 namespace vw4 {
 
-// Sum over the S partial slices of element (m, c), slice order.  The loads
-// of 8 slices are issued together (a chain of dependent loads would pay one
-// memory latency per slice).
-__device__ __forceinline__ float sum_parts(const float* __restrict__ part, int S, int M, int64_t ldp, int m,
-                                           int64_t c) {
-    float s = 0.0f;
-    const int64_t stride = (int64_t)M * ldp;
-    const float* p = part + (int64_t)m * ldp + c;
-    for (int k0 = 0; k0 < S; k0 += 8) {
-        float v[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (k0 + i < S) ? p[(int64_t)(k0 + i) * stride] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (k0 + i < S) s += v[i];
-    }
-    return s;
-}
-
 // ---------------------------------------------------------------------------
 // residual add + RMSNorm in two launches over many workgroups:
 //   1. grid (ceil(D / NCOL), M): resid += partials (rounded to bf16), and the
@@ -129,10 +110,19 @@ __global__ void rope_kv_kernel(const float* __restrict__ part, int S, int64_t ld
 // ---------------------------------------------------------------------------
 // SwiGLU.  grid = (ceil(F / 256), M), 256 threads.
 // ---------------------------------------------------------------------------
+// Grouped launches (n_slots != NULL): blockIdx.z is a slot with its own
+// partials (p_sstride floats apart) and output (a_sstride elements apart);
+// slots at or beyond *n_slots exit at once.
 __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ part, int S, int64_t ldp, int M, int F,
-                                                     uint16_t* __restrict__ a) {
+                                                     uint16_t* __restrict__ a, int64_t p_sstride, int64_t a_sstride,
+                                                     const int32_t* __restrict__ n_slots) {
     const int j = blockIdx.x * 256 + threadIdx.x, m = blockIdx.y;
     if (j >= F) return;
+    if (n_slots) {
+        if ((int)blockIdx.z >= *n_slots) return;
+        part += (int64_t)blockIdx.z * p_sstride;
+        a += (int64_t)blockIdx.z * a_sstride;
+    }
     const float g = sum_parts(part, S, M, ldp, m, j);
     const float u = sum_parts(part, S, M, ldp, m, (int64_t)F + j);
     const float sg = g / (1.0f + expf(-g));
@@ -393,8 +383,21 @@ int vw4_swiglu(const float* part, int32_t S, int64_t ldp, int32_t M, int32_t F, 
     VW4_REQUIRE(part && a, VW4_EINVAL, "vw4_swiglu: null pointer");
     VW4_REQUIRE(M >= 1 && M <= 64 && F >= 1 && S >= 1 && ldp >= 2 * (int64_t)F, VW4_EINVAL, "vw4_swiglu: bad shape");
     hipLaunchKernelGGL(swiglu_kernel, dim3((F + 255) / 256, M), dim3(256), 0, (hipStream_t)stream, part, S, ldp, M, F,
-                       a);
+                       a, (int64_t)0, (int64_t)0, (const int32_t*)nullptr);
     return check_launch("vw4_swiglu");
+}
+
+int vw4_grouped_swiglu(const float* part, int32_t S, int64_t ldp, int64_t p_sstride, int32_t M, int32_t F,
+                       uint16_t* a, int64_t a_sstride, const int32_t* n_slots, int32_t max_slots, void* stream) {
+    VW4_REQUIRE(part && a && n_slots, VW4_EINVAL, "vw4_grouped_swiglu: null pointer");
+    VW4_REQUIRE(M >= 1 && M <= 64 && F >= 1 && S >= 1 && ldp >= 2 * (int64_t)F, VW4_EINVAL,
+                "vw4_grouped_swiglu: bad shape");
+    VW4_REQUIRE(max_slots >= 1 && max_slots <= 65535 && p_sstride >= (int64_t)S * M * ldp &&
+                    a_sstride >= (int64_t)M * F,
+                VW4_EINVAL, "vw4_grouped_swiglu: bad slot count or strides");
+    hipLaunchKernelGGL(swiglu_kernel, dim3((F + 255) / 256, M, max_slots), dim3(256), 0, (hipStream_t)stream, part, S,
+                       ldp, M, F, a, p_sstride, a_sstride, n_slots);
+    return check_launch("vw4_grouped_swiglu");
 }
 
 size_t vw4_attn_workspace_bytes(int32_t M, int32_t nq, int32_t nkv, int32_t hd, int64_t ctx) {

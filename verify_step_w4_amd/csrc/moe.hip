@@ -1,0 +1,160 @@
+// moe.hip — mixture-of-experts calls of the MoE-shaped verify step: router
+// top-k with slot assignment, and the weighted combine of the expert outputs.
+//
+// gist.science, "BaseRT: Best-in-Class LLM Inference on Apple Silicon via
+// Native Metal", section "結果": mixture-of-experts models (Qwen3-30B-A3B
+// class: 128 experts, 8 active per token) are among the workloads of the
+// decode runtime.  Each verify row is routed on its own: its router logits
+// pick the top-k experts (largest logit first, the lower index first on equal
+// logits), and the softmax weights of the chosen experts are renormalised to
+// sum to one.
+//
+// Device-side slot list.  The distinct experts chosen by any row get slots
+// 0 .. n_slots-1 in ascending expert order; the grouped W4 GEMM and the
+// grouped SwiGLU launch max_slots slots and the ones at or beyond n_slots
+// exit at once, so the host never reads the routing (the step stays
+// capturable as a graph).  Every slot computes all M rows of its expert; the
+// combine reads row m of slot row_slot[m][t] only.
+#include <math.h>
+
+#include "common.h"
+
+namespace vw4 {
+
+constexpr int MOE_MAX_E = 1024;
+constexpr int MOE_MAX_K = 64;
+constexpr int MOE_MAX_M = 16;
+constexpr int MOE_KPL = MOE_MAX_E / 64;  // experts per lane
+
+// One workgroup of 4 wavefronts; wavefront w routes rows w, w + 4, ...
+// Selection: the key (order-preserving fp32 key << 32 | ~index) is unique per
+// expert, so a wavefront maximum names exactly one expert per round.
+__global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ logits, int M, int E, int topk,
+                                                        int32_t* __restrict__ experts, float* __restrict__ weights,
+                                                        int32_t* __restrict__ slot_expert,
+                                                        int32_t* __restrict__ n_slots, int32_t* __restrict__ row_slot) {
+    __shared__ int32_t slot_of[MOE_MAX_E];
+    __shared__ int32_t sel[MOE_MAX_M * MOE_MAX_K];
+    __shared__ int32_t cnt[256];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int e = tid; e < E; e += 256) slot_of[e] = 0;
+    __syncthreads();
+    for (int m = w; m < M; m += 4) {
+        const float* l = logits + (int64_t)m * E;
+        uint64_t key[MOE_KPL];
+#pragma unroll
+        for (int i = 0; i < MOE_KPL; ++i) {
+            const int e = lane + 64 * i;
+            key[i] = e < E ? ((uint64_t)f32_key(l[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e) : 0;
+        }
+        int my_e = 0;
+        for (int t = 0; t < topk; ++t) {
+            uint64_t best = 0;
+#pragma unroll
+            for (int i = 0; i < MOE_KPL; ++i) best = key[i] > best ? key[i] : best;
+            uint64_t wb = best;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const uint64_t o = __shfl_xor(wb, off, 64);
+                wb = o > wb ? o : wb;
+            }
+            const int e = (int)(0xFFFFFFFFu - (uint32_t)wb);
+#pragma unroll
+            for (int i = 0; i < MOE_KPL; ++i)
+                if (key[i] == wb) key[i] = 0;
+            if (lane == t) my_e = e;
+            if (lane == 0) {
+                sel[m * MOE_MAX_K + t] = e;
+                slot_of[e] = 1;
+            }
+        }
+        // weights: exp(l_e - l_top) in fp64 (l_top = the largest logit, chosen
+        // first), normalised over the chosen experts in selection order
+        const double top = (double)l[__shfl(my_e, 0, 64)];
+        const double pe = lane < topk ? exp((double)l[my_e] - top) : 0.0;
+        double den = 0.0;
+        for (int t = 0; t < topk; ++t) den += __shfl(pe, t, 64);
+        if (lane < topk) weights[m * topk + lane] = (float)(pe / den);
+    }
+    __syncthreads();
+    // slots in ascending expert order: thread tid scans experts [e0, e1)
+    const int per = (E + 255) / 256;
+    const int e0 = tid * per < E ? tid * per : E, e1 = e0 + per < E ? e0 + per : E;
+    int c = 0;
+    for (int e = e0; e < e1; ++e) c += slot_of[e];
+    cnt[tid] = c;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const int v = tid >= off ? cnt[tid - off] : 0;
+        __syncthreads();
+        cnt[tid] += v;
+        __syncthreads();
+    }
+    int s = cnt[tid] - c;  // exclusive prefix
+    for (int e = e0; e < e1; ++e)
+        if (slot_of[e]) {
+            slot_expert[s] = e;
+            slot_of[e] = s++;
+        }
+    if (tid == 255) *n_slots = cnt[255];
+    __syncthreads();
+    for (int i = tid; i < M * topk; i += 256) {
+        const int e = sel[(i / topk) * MOE_MAX_K + i % topk];
+        experts[i] = e;
+        row_slot[i] = slot_of[e];
+    }
+}
+
+// y[m][d] = sum_t weights[m][t] * sum_s part[row_slot[m][t]][s][m][d]
+// (experts in selection order, slices in slice order, fp32).
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ part, int S, int64_t ldp,
+                                                          int64_t p_sstride, const int32_t* __restrict__ row_slot,
+                                                          const float* __restrict__ weights, int M, int topk, int D,
+                                                          float* __restrict__ y, int64_t ldy) {
+    const int d = blockIdx.x * 256 + threadIdx.x, m = blockIdx.y;
+    if (d >= D) return;
+    float acc = 0.0f;
+    for (int t0 = 0; t0 < topk; t0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = t0 + i < topk
+                       ? sum_parts(part + (int64_t)row_slot[m * topk + t0 + i] * p_sstride, S, M, ldp, m, d)
+                       : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (t0 + i < topk) acc += weights[m * topk + t0 + i] * v[i];
+    }
+    y[(int64_t)m * ldy + d] = acc;
+}
+
+}  // namespace vw4
+
+using namespace vw4;
+
+extern "C" {
+
+int vw4_moe_route(const float* logits, int32_t M, int32_t E, int32_t topk, int32_t* experts, float* weights,
+                  int32_t* slot_expert, int32_t* n_slots, int32_t* row_slot, void* stream) {
+    VW4_REQUIRE(logits && experts && weights && slot_expert && n_slots && row_slot, VW4_EINVAL,
+                "vw4_moe_route: null pointer");
+    VW4_REQUIRE(M >= 1 && M <= MOE_MAX_M && E >= 1 && E <= MOE_MAX_E && topk >= 1 && topk <= MOE_MAX_K && topk <= E,
+                VW4_EINVAL, "vw4_moe_route: need 1 <= M <= %d, 1 <= topk <= min(E, %d), E <= %d", MOE_MAX_M,
+                MOE_MAX_K, MOE_MAX_E);
+    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, logits, M, E, topk, experts,
+                       weights, slot_expert, n_slots, row_slot);
+    return check_launch("vw4_moe_route");
+}
+
+int vw4_moe_combine(const float* part, int32_t S, int64_t ldp, int64_t p_sstride, const int32_t* row_slot,
+                    const float* weights, int32_t M, int32_t topk, int32_t D, float* y, int64_t ldy, void* stream) {
+    VW4_REQUIRE(part && row_slot && weights && y, VW4_EINVAL, "vw4_moe_combine: null pointer");
+    VW4_REQUIRE(M >= 1 && M <= 64 && topk >= 1 && D >= 1 && S >= 1 && ldp >= D && ldy >= D &&
+                    p_sstride >= (int64_t)S * M * ldp,
+                VW4_EINVAL, "vw4_moe_combine: bad shape or strides");
+    hipLaunchKernelGGL(moe_combine_kernel, dim3((D + 255) / 256, M), dim3(256), 0, (hipStream_t)stream, part, S, ldp,
+                       p_sstride, row_slot, weights, M, topk, D, y, ldy);
+    return check_launch("vw4_moe_combine");
+}
+
+}  // extern "C"

@@ -96,14 +96,37 @@ __device__ __forceinline__ void gemm_group(u32x4 c0, u32x4 c1, uint32_t sbits, c
     }
 }
 
+// Grouped (mixture-of-experts) launches: blockIdx.z is a slot; slots at or
+// beyond *n_slots exit at once; slot s multiplies expert slot_expert[s]
+// (weights at w_estride / s_estride per expert) with the activations at
+// x + s * x_sstride into the partials at part + s * p_sstride.
+struct GemmGroup {
+    const int32_t* slot_expert;
+    const int32_t* n_slots;   // NULL: plain (single-matrix) launch
+    int64_t w_estride;        // u32x4 units
+    int64_t s_estride;        // fp16 units
+    int64_t x_sstride;        // bf16 elements
+    int64_t p_sstride;        // floats
+};
+
 template <int M>
 __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                       const u32x4* __restrict__ wpk,
                                                       const uint16_t* __restrict__ spk, void* __restrict__ y,
                                                       int64_t ldy, int ydt, int N, int G, int S_wg, int S_grid,
                                                       float* __restrict__ part, int64_t Npad, uint32_t kmask,
-                                                      uint32_t kmagic) {
+                                                      uint32_t kmagic, GemmGroup grp) {
     extern __shared__ float lds[];
+    if (grp.n_slots) {
+        const int slot = blockIdx.z;
+        if (slot >= __builtin_amdgcn_readfirstlane(*grp.n_slots)) return;
+        const int e = __builtin_amdgcn_readfirstlane(grp.slot_expert[slot]);
+        wpk += (int64_t)e * grp.w_estride;
+        spk += (int64_t)e * grp.s_estride;
+        x += (int64_t)slot * grp.x_sstride;
+        part += (int64_t)slot * grp.p_sstride;
+        y = part;
+    }
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -253,13 +276,16 @@ struct GemmPlan {
 
 // Split of K over wavefronts: enough wavefronts to cover the 256 CUs several
 // times, at least two groups per wavefront.  Depends on (N, K) only.
-static GemmPlan plan_gemm(int M, int N, int K) {
+// slots: matrices per launch (grouped launches spread the wave target over
+// all of them).
+static GemmPlan plan_gemm(int M, int N, int K, int slots = 1) {
     GemmPlan p;
     p.G = K / 64;
     p.ntiles = (N + 63) / 64;
     p.Npad = (int64_t)p.ntiles * 64;
     const int target_waves = 8192;
-    int S = (target_waves + p.ntiles - 1) / p.ntiles;
+    const int units = p.ntiles * slots;
+    int S = (target_waves + units - 1) / units;
     int maxS = p.G / 2 > 0 ? p.G / 2 : 1;
     if (S > maxS) S = maxS;
     if (S < 1) S = 1;
@@ -285,7 +311,7 @@ static void launch_gemm(const GemmPlan& p, const uint16_t* x, int64_t ldx, const
                         void* y, int64_t ldy, int ydt, int N, float* part, hipStream_t st) {
     hipLaunchKernelGGL(w4_gemm_kernel<M>, dim3(p.ntiles, p.S_grid), dim3(64 * p.S_wg), p.lds_bytes, st, x, ldx,
                        (const u32x4*)w, s, y, ldy, ydt, N, p.G, p.S_wg, p.S_grid, part, p.Npad, 0x000F000Fu,
-                       0x43004300u);
+                       0x43004300u, GemmGroup{});
     if (p.S_grid > 1)
         hipLaunchKernelGGL(w4_gemm_reduce_kernel, dim3(p.ntiles, M), dim3(64), 0, st, part, p.S_grid, M, p.Npad, N,
                            y, ldy, ydt);
@@ -325,9 +351,9 @@ int gemm_dispatch(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16
 }
 
 // Partials form: the main kernel only (no reduction launch); part is the
-// caller's [S_grid][M][Npad] fp32 buffer.
+// caller's [S_grid][M][Npad] fp32 buffer (per slot for grouped launches).
 int gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* s, float* part, int M, int N,
-                  int K, hipStream_t st) {
+                  int K, hipStream_t st, const GemmGroup& grp = GemmGroup{}, int max_slots = 1) {
     VW4_REQUIRE(M >= 1 && M <= GEMM_MAX_M, VW4_EINVAL, "w4_skinny_gemm_partials: M=%d must be in [1, 8]", M);
     VW4_REQUIRE(N >= 1, VW4_EINVAL, "w4_skinny_gemm_partials: N=%d must be >= 1", N);
     VW4_REQUIRE(K >= 64 && K % 64 == 0 && K <= 65536, VW4_EINVAL,
@@ -337,9 +363,7 @@ int gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16
                 "w4_skinny_gemm_partials: x needs ldx >= K, ldx %% 8 == 0 and 16-byte alignment");
     VW4_REQUIRE(aligned(w, 16) && aligned(s, 2) && aligned(part, 4), VW4_EINVAL,
                 "w4_skinny_gemm_partials: misaligned pointer");
-    const GemmPlan p = plan_gemm(M, N, K);
-    GemmPlan q = p;
-    q.ws_bytes = 0;
+    const GemmPlan p = plan_gemm(M, N, K, max_slots);
     // S_grid == 1 writes the product straight into part[0] with row stride Npad
     void* y = part;
     const int64_t ldy = p.Npad;
@@ -347,21 +371,41 @@ int gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16
     switch (M) {
 #define VW4_CASE(MM)                                                                                               \
     case MM:                                                                                                       \
-        hipLaunchKernelGGL(w4_gemm_kernel<MM>, dim3(p.ntiles, p.S_grid), dim3(64 * p.S_wg), p.lds_bytes, st, x, ldx, \
+        hipLaunchKernelGGL(w4_gemm_kernel<MM>, dim3(p.ntiles, p.S_grid, max_slots), dim3(64 * p.S_wg), p.lds_bytes, st, x, ldx, \
                            (const u32x4*)w, s, y, ldy, VW4_F32, N, p.G, p.S_wg, p.S_grid, pp, p.Npad, 0x000F000Fu,   \
-                           0x43004300u);                                                                           \
+                           0x43004300u, grp);                                                                      \
         break;
         VW4_CASE(1) VW4_CASE(2) VW4_CASE(3) VW4_CASE(4) VW4_CASE(5) VW4_CASE(6) VW4_CASE(7) VW4_CASE(8)
 #undef VW4_CASE
     }
-    (void)q;
     return check_launch("w4_skinny_gemm_partials");
 }
 
-int gemm_layout(int M, int N, int K, int* S, int64_t* ldp) {
+int grouped_gemm_partials(const uint16_t* x, int64_t ldx, int64_t x_sstride, const uint8_t* w_bank,
+                          int64_t w_estride_bytes, const uint16_t* s_bank, int64_t s_estride, const int32_t* slot_expert,
+                          const int32_t* n_slots, int max_slots, float* part, int64_t p_sstride, int M, int N, int K,
+                          hipStream_t st) {
+    VW4_REQUIRE(slot_expert && n_slots && max_slots >= 1 && max_slots <= 65535, VW4_EINVAL,
+                "w4_grouped_gemm: bad slot arguments");
+    VW4_REQUIRE(w_estride_bytes % 16 == 0 && w_estride_bytes > 0 && s_estride > 0, VW4_EINVAL,
+                "w4_grouped_gemm: expert strides must be positive, weights 16-byte multiples");
+    VW4_REQUIRE(x_sstride % 8 == 0 && x_sstride >= 0 && p_sstride >= 0, VW4_EINVAL,
+                "w4_grouped_gemm: bad slot strides");
+    GemmGroup g;
+    g.slot_expert = slot_expert;
+    g.n_slots = n_slots;
+    g.w_estride = w_estride_bytes / 16;
+    g.s_estride = s_estride;
+    g.x_sstride = x_sstride;
+    g.p_sstride = p_sstride;
+    return gemm_partials(x, ldx, w_bank, s_bank, part, M, N, K, st, g, max_slots);
+}
+
+int gemm_layout(int M, int N, int K, int* S, int64_t* ldp, int slots = 1) {
     VW4_REQUIRE(M >= 1 && M <= GEMM_MAX_M && N >= 1 && K >= 64 && K % 64 == 0 && K <= 65536, VW4_EINVAL,
                 "vw4_gemm_partials_layout: bad shape M=%d N=%d K=%d", M, N, K);
-    const GemmPlan p = plan_gemm(M, N, K);
+    VW4_REQUIRE(slots >= 1 && slots <= 65535, VW4_EINVAL, "vw4_grouped_gemm_layout: max_slots=%d", slots);
+    const GemmPlan p = plan_gemm(M, N, K, slots);
     if (S) *S = p.S_grid;
     if (ldp) *ldp = p.Npad;
     return VW4_OK;
@@ -383,6 +427,28 @@ int vw4_gemm_partials_layout(int32_t M, int32_t N, int32_t K, int32_t* S, int64_
     int rc = vw4::gemm_layout(M, N, K, &s, ldp);
     if (S) *S = s;
     return rc;
+}
+
+int vw4_grouped_gemm_layout(int32_t M, int32_t N, int32_t K, int32_t max_slots, int32_t* S, int64_t* ldp) {
+    int s = 0;
+    int rc = vw4::gemm_layout(M, N, K, &s, ldp, max_slots);
+    if (S) *S = s;
+    return rc;
+}
+
+int w4_grouped_gemm(const uint16_t* x, int64_t ldx, int64_t x_sstride, const uint8_t* w_bank, int64_t w_estride,
+                    const uint16_t* s_bank, int64_t s_estride, const int32_t* slot_expert, const int32_t* n_slots,
+                    int32_t max_slots, float* part, int64_t p_sstride, int32_t M, int32_t N, int32_t K, void* stream) {
+    if (max_slots >= 1 && max_slots <= 65535 && M >= 1 && M <= vw4::GEMM_MAX_M && N >= 1 && K >= 64 && K % 64 == 0) {
+        int S = 0;
+        int64_t ldp = 0;
+        vw4::gemm_layout(M, N, K, &S, &ldp, max_slots);
+        VW4_REQUIRE(p_sstride >= (int64_t)S * M * ldp, VW4_EINVAL,
+                    "w4_grouped_gemm: p_sstride %lld < S * M * ldp = %lld", (long long)p_sstride,
+                    (long long)((int64_t)S * M * ldp));
+    }
+    return vw4::grouped_gemm_partials(x, ldx, x_sstride, w_bank, w_estride, s_bank, s_estride, slot_expert, n_slots,
+                                      max_slots, part, p_sstride, M, N, K, (hipStream_t)stream);
 }
 
 int w4_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, const uint16_t* scales_packed,

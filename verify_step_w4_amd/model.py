@@ -280,3 +280,153 @@ class VerifyStep:
                       out.get("tokens", self.tokens), out.get("n_acc", self.n_acc), out.get("flags", self.flags),
                       self.acc_ws, stream=stream)
         return self.tokens, self.n_acc, self.flags
+
+
+# ---------------------------------------------------------------------------
+# MoE-shaped verify step (synthetic weights)
+# ---------------------------------------------------------------------------
+MOE_30B = dict(n_exp=128, topk=8, d=2048, F=768, V=151936, eps=1e-6)
+
+
+class ExpertBank:
+    """W4 weights of E SwiGLU experts, each stored as a contiguous slice of two
+    stacked matrices: gate|up [E * 2F][d] (rows [0, F) of an expert are the
+    gate, [F, 2F) the up projection) and down [E * d][F]."""
+
+    def __init__(self, gate_up: W4Linear, down: W4Linear, E: int, d: int, F: int):
+        assert (2 * F) % 64 == 0 and d % 64 == 0 and F % 64 == 0
+        self.gate_up, self.down, self.E, self.d, self.F = gate_up, down, E, d, F
+        self.gu_estride = (2 * F * d // 2, 2 * F * d // 64)   # (bytes, fp16 scales) per expert
+        self.dn_estride = (d * F // 2, d * F // 64)
+
+    @classmethod
+    def random(cls, E: int, d: int, F: int, std: float, gen, device="cuda"):
+        return cls(W4Linear.random(E * 2 * F, d, std, gen, device), W4Linear.random(E * d, F, std, gen, device),
+                   E, d, F)
+
+    @classmethod
+    def from_fp32(cls, gate_up, down):
+        """gate_up: [E][2F][d], down: [E][d][F] fp32 device tensors."""
+        E, F2, d = gate_up.shape
+        return cls(W4Linear.from_fp32(gate_up.reshape(E * F2, d)), W4Linear.from_fp32(down.reshape(E * d, F2 // 2)),
+                   E, d, F2 // 2)
+
+    def expert_bytes(self) -> int:
+        return int(3 * self.d * self.F * BYTES_PER_WEIGHT)
+
+
+class MoEVerify:
+    """Verify step of an MoE-shaped model: the M hidden rows go through one
+    routed SwiGLU expert layer (router top-k, grouped W4 GEMMs over the
+    distinct chosen experts, weighted combine), the residual add and the final
+    RMSNorm, then the LM head, the temperature / top-p statistics and
+    Leviathan–Chen acceptance.  Routing stays on the device (slot list), so the
+    step can be captured as a graph."""
+
+    def __init__(self, cfg: dict, M: int, lm_head: W4Linear, final_gamma, device="cuda"):
+        import torch
+        self.cfg = dict(cfg)
+        E, topk, d, F, V = (cfg[k] for k in ("n_exp", "topk", "d", "F", "V"))
+        self.M, self.D, self.E, self.topk, self.d, self.F, self.V = M, M - 1, E, topk, d, F, V
+        self.lm_head, self.final_gamma, self.device = lm_head, final_gamma, device
+        self.max_slots = min(E, M * topk)
+        i32 = torch.int32
+        self.experts = torch.empty((M, topk), dtype=i32, device=device)
+        self.weights = torch.empty((M, topk), dtype=torch.float32, device=device)
+        self.slot_expert = torch.zeros(self.max_slots, dtype=i32, device=device)
+        self.n_slots = torch.zeros(1, dtype=i32, device=device)
+        self.row_slot = torch.empty((M, topk), dtype=i32, device=device)
+        self.gu_S, self.gu_ldp = B.grouped_gemm_layout(M, 2 * F, d, self.max_slots)
+        self.dn_S, self.dn_ldp = B.grouped_gemm_layout(M, d, F, self.max_slots)
+        self.gu_sstride = self.gu_S * M * self.gu_ldp
+        self.dn_sstride = self.dn_S * M * self.dn_ldp
+        self.part_gu = torch.empty(self.max_slots * self.gu_sstride, dtype=torch.float32, device=device)
+        self.part_dn = torch.empty(self.max_slots * self.dn_sstride, dtype=torch.float32, device=device)
+        self.a = torch.empty((self.max_slots, M, F), dtype=torch.int16, device=device)
+        self.y = torch.empty((M, d), dtype=torch.float32, device=device)
+        self.resid = torch.empty((M, d), dtype=torch.int16, device=device)
+        self.h = torch.empty((M, d), dtype=torch.int16, device=device)
+        self.norm_ws = B.workspace(B.norm_workspace_bytes(M, d), device)
+        self.logits = torch.empty((M, V), dtype=torch.float32, device=device)
+        self.lm_ws = B.workspace(B.gemm_workspace_bytes(M, V, d), device)
+        self.stats = torch.zeros(M * B.ROWSTAT_BYTES, dtype=torch.uint8, device=device)
+        self.stat_ws = B.workspace(B.verify_workspace_bytes(M, V), device)
+        self.acc_ws = B.workspace(B.accept_workspace_bytes(1, V), device)
+        self.tokens = torch.empty((1, M), dtype=i32, device=device)
+        self.n_acc = torch.empty(1, dtype=i32, device=device)
+        self.flags = torch.empty(1, dtype=i32, device=device)
+
+    def moe(self, x, router_logits, bank: ExpertBank, stream=None, gemm_hook=None):
+        """y[M][d] (fp32) = routed SwiGLU experts of the bf16 rows x."""
+        hook = gemm_hook or (lambda when, name: None)
+        M, d, F, ms = self.M, self.d, self.F, self.max_slots
+        B.moe_route(router_logits, M, self.E, self.topk, self.experts, self.weights, self.slot_expert, self.n_slots,
+                    self.row_slot, stream)
+        hook("pre", "gate_up")
+        B.w4_grouped_gemm(x, x.stride(0), 0, bank.gate_up.packed, bank.gu_estride[0], bank.gate_up.pscales,
+                          bank.gu_estride[1], self.slot_expert, self.n_slots, ms, self.part_gu, self.gu_sstride,
+                          M, 2 * F, d, stream)
+        hook("post", "gate_up")
+        B.grouped_swiglu(self.part_gu, self.gu_S, self.gu_ldp, self.gu_sstride, M, F, self.a, M * F, self.n_slots,
+                         ms, stream)
+        hook("pre", "down")
+        B.w4_grouped_gemm(self.a, F, M * F, bank.down.packed, bank.dn_estride[0], bank.down.pscales,
+                          bank.dn_estride[1], self.slot_expert, self.n_slots, ms, self.part_dn, self.dn_sstride,
+                          M, d, F, stream)
+        hook("post", "down")
+        B.moe_combine(self.part_dn, self.dn_S, self.dn_ldp, self.dn_sstride, self.row_slot, self.weights, M,
+                      self.topk, d, self.y, d, stream)
+        return self.y
+
+    def forward(self, x, router_logits, bank: ExpertBank, stream=None, gemm_hook=None):
+        """Logits [M][V] of the M rows: LM head of bf16(rmsnorm(x + moe(x)) * gamma)."""
+        hook = gemm_hook or (lambda when, name: None)
+        M, d = self.M, self.d
+        self.moe(x, router_logits, bank, stream, gemm_hook)
+        self.resid.copy_(x[:M])
+        B.add_rmsnorm(self.resid, self.y, 1, d, self.final_gamma, self.cfg["eps"], M, d, self.h, self.norm_ws, stream)
+        hook("pre", "lm_head")
+        B.w4_skinny_gemm(self.h, self.lm_head.packed, self.lm_head.pscales, self.logits, M, self.V, d, ws=self.lm_ws,
+                         stream=stream)
+        hook("post", "lm_head")
+        return self.logits
+
+    def _accept(self, q, drafts, T, top_p, seed, step=None, step_dev=None, stream=None):
+        B.verify_logits(None, None, None, self.M, self.V, self.d, T, top_p, self.logits, self.stats, self.stat_ws,
+                        stream=stream)
+        if step_dev is None:
+            B.spec_accept(self.logits, 0, self.stats, 0, q, 0, drafts, 1, self.D, self.V, T, seed, step, self.tokens,
+                          self.n_acc, self.flags, self.acc_ws, stream=stream)
+        else:
+            B.spec_accept_ex(self.logits, 0, self.stats, 0, q, 0, drafts, 1, self.D, self.V, T, seed, step_dev,
+                             self.tokens, self.n_acc, self.flags, self.acc_ws, stream=stream)
+            B.step_advance(step_dev, 1, stream)
+
+    def run(self, x, router_logits, bank, q, drafts, T, top_p, seed, step, stream=None, gemm_hook=None):
+        self.forward(x, router_logits, bank, stream, gemm_hook)
+        self._accept(q, drafts, T, top_p, seed, step=step, stream=stream)
+        return self.tokens, self.n_acc, self.flags
+
+    def run_graphable(self, x, router_logits, bank, q, drafts, T, top_p, seed, step_dev, stream=None):
+        self.forward(x, router_logits, bank, stream)
+        self._accept(q, drafts, T, top_p, seed, step_dev=step_dev, stream=stream)
+
+    def capture(self, x, router_logits, bank, q, drafts, T, top_p, seed, step_dev):
+        import torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.run_graphable(x, router_logits, bank, q, drafts, T, top_p, seed, step_dev)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run_graphable(x, router_logits, bank, q, drafts, T, top_p, seed, step_dev)
+        torch.cuda.synchronize()
+        return g
+
+    def step_bytes(self, n_distinct: int) -> int:
+        """Algorithmic HBM bytes of one step with n_distinct experts chosen:
+        each chosen expert's weights and the LM head once (activations and
+        logits are < 0.5 % and left out)."""
+        return int(n_distinct * 3 * self.d * self.F * BYTES_PER_WEIGHT + self.V * self.d * BYTES_PER_WEIGHT)
