@@ -9,6 +9,19 @@ events on the stream it runs on, and the CPU oracle timed on a bounded
 sample of the same workload.
 
 Workloads (synthetic, seeded; the weights are random, drawn on the device):
+  verify27b       (default) the whole verify step of a 27B-shaped dense
+                  decoder: 64 layers (d=5120, GQA 40/8 heads of 128, SwiGLU FFN
+                  17408, all linears W4 group-64), RMSNorm, RoPE, decode
+                  attention of the 4 verify rows over a bf16 KV cache of
+                  --context positions, the W4 LM head [151936][5120],
+                  temperature 0.6 / top_p 0.95 statistics and Leviathan–Chen
+                  acceptance of 3 drafts; captured as one HIP graph.  Also
+                  times the M = 1 autoregressive step on the same state.
+  moe_verify      MoE-shaped verify step: 128 SwiGLU experts (2048 -> 768 ->
+                  2048) with top-8 routing of each row on fresh N(0,1) router
+                  logits, grouped W4 GEMMs over the chosen experts, LM head
+                  [151936][2048], same acceptance; 4 expert banks and LM heads
+                  rotated.
   lm_head_verify  LM-head verify step: hidden rows bf16 ~N(0,1) [4][5120],
                   W4 group-64 LM head [151936][5120] (~N(0,0.02), three copies
                   rotated so the 256 MB Infinity Cache cannot hold the working
@@ -29,10 +42,67 @@ if ROOT not in sys.path:
 
 METRIC = "verify steps/s and achieved HBM GB/s (W4 skinny GEMM, M=4) vs peak"
 HBM_PEAK_GBS = 8000.0
+CALIB_COPY_BYTES = 256 << 20
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4_gemm_hbm_traffic.md")
+
+
+def measured_traffic(workload):
+    """HBM bytes per W4 GEMM launch of a workload's step, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by the plain-copy
+    calibration there), or None if there is none or the GEMM source has
+    changed since the counters were taken."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    src = os.path.join(ROOT, "verify_step_w4_amd", "csrc", "w4_gemm.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    m = re.search(r"w4_gemm\.hip sha256: ([0-9a-f]{64})", text)
+    if not m or m.group(1) != digest:
+        return None
+    m = re.search(r"^\| " + re.escape(workload) + r" \| ([0-9.]+) \| ([0-9.]+) \| ([0-9.]+) \|", text, re.M)
+    if not m:
+        return None
+    return int(float(m.group(3)))
+
+
+def time_graphs(issue_fns, reps):
+    """Capture each issue_fn() (which launches work and returns its launch
+    count) into its own HIP graph, then replay the graphs in turn reps times
+    between two HIP events on the replay stream.  Returns (ms per launch,
+    launches per round)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graphs, n = [], 0
+    with torch.cuda.stream(s):
+        for fn in issue_fns:
+            fn()
+    torch.cuda.synchronize()
+    for fn in issue_fns:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            n += fn()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for g in graphs:
+        g.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for g in graphs:
+            g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * n), n
 
 
 # --------------------------------------------------------------------------
@@ -149,7 +219,7 @@ def verify27b_workload(args):
     import torch
 
     from verify_step_w4_amd import binding as B
-    from verify_step_w4_amd.model import DENSE_27B, Decoder, VerifyStep
+    from verify_step_w4_amd.model import BYTES_PER_WEIGHT, DENSE_27B, Decoder, VerifyStep
 
     cfg = dict(DENSE_27B)
     M, D, L = 4, 3, args.context
@@ -176,10 +246,14 @@ def verify27b_workload(args):
     flag_all = torch.empty(K, dtype=torch.int32, device=dev)
     gemm_events = []
 
+    gemm_names = []
+
     def hook(when, name):
         e = torch.cuda.Event(enable_timing=True)
         e.record()
         gemm_events.append(e)
+        if when == "pre":
+            gemm_names.append(name)
 
     # (a) eager pass: every W4 GEMM launch bracketed by HIP events on its stream
     for i in range(W):
@@ -193,8 +267,12 @@ def verify27b_workload(args):
     e1.record()
     torch.cuda.synchronize()
     eager_ms = e0.elapsed_time(e1) / K
-    gemm_ms = sum(gemm_events[2 * k].elapsed_time(gemm_events[2 * k + 1]) for k in range(len(gemm_events) // 2))
-    n_gemm = len(gemm_events) // 2
+    per_gemm = [gemm_events[2 * k].elapsed_time(gemm_events[2 * k + 1]) for k in range(len(gemm_events) // 2)]
+    gemm_ms = sum(per_gemm)
+    n_gemm = len(per_gemm)
+    by_name = {}
+    for nm, t in zip(gemm_names, per_gemm):
+        by_name.setdefault(nm, []).append(t)
     # (b) the timed region: the verify step captured once as a HIP graph and
     # replayed; each replay is preceded by copying the next step's inputs
     # into the captured buffers (counted in the time)
@@ -236,25 +314,39 @@ def verify27b_workload(args):
     torch.cuda.synchronize()
     ar_ms = a0.elapsed_time(a1) / K
     step_ms = total_ms / K
+    # (d) the W4 GEMM kernel by itself: the 257 GEMM launches of a step, same
+    # shapes, weights and buffers, captured as a graph and replayed
+    ms_launch, n_launch = time_graphs([lambda: dec.gemm_pass(M)], 20)
     alg_gemm = dec.gemm_alg_bytes(M)            # per step, all GEMM launches
-    gemm_launch_us = gemm_ms * 1e3 / n_gemm
-    per_launch_bytes = alg_gemm / (n_gemm / K)
+    gemm_launch_us = ms_launch * 1e3
+    per_launch_bytes = alg_gemm / n_launch
     achieved = per_launch_bytes / (gemm_launch_us * 1e-6) / 1e9
     step_bytes = dec.weight_bytes() + dec.kv_bytes(L, M)
     nacc = nacc_all.cpu().numpy()
     flags = flag_all.cpu().numpy()
+    shapes = dict(dec.shapes)
+    shapes["lm_head"] = (V, d)
+    linears = {}
+    for nm in by_name:
+        N, Kd = shapes[nm]
+        b = N * Kd * BYTES_PER_WEIGHT + M * Kd * 2 + M * N * 4
+        us = time_graphs([lambda nm=nm: dec.gemm_pass(M, names=(nm,))], 20 if nm != "lm_head" else 200)[0] * 1e3
+        linears[nm] = {"N": N, "K": Kd, "avg_us": round(us, 2), "GBs": round(b / (us * 1e-6) / 1e9, 1),
+                       "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     res = dict(
         ms_per_step=step_ms,
         value=K / (total_ms * 1e-3),
         wall_s=wall,
+        w4_gemm_by_linear=linears,
         config={"workload": "verify27b", "layers": 64, "d_model": d, "heads_q_kv_dim": [40, 8, 128],
                 "ffn": cfg["F"], "V": V, "context": L, "M": M, "draft_depth": D, "temperature": T, "top_p": top_p,
                 "weights": "int4 group-64 symmetric, fp16 scales", "kv_cache": "bf16"},
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                  "kernel": "w4_gemm_kernel<4> (all 257 W4 GEMM launches of a step)",
+                  "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("verify27b"),
+                  "kernel": "w4_gemm_kernel<4> (the 257 W4 GEMM launches of a step, replayed as a graph)",
                   "alg_bytes_per_launch": int(per_launch_bytes), "avg_launch_us": round(gemm_launch_us, 2)},
-        stages_us={"w4_gemm_total": round(gemm_ms * 1e3 / K, 1),
+        stages_us={"w4_gemm_total_eager": round(gemm_ms * 1e3 / K, 1),
+                   "w4_gemm_total_graph": round(gemm_launch_us * n_launch, 1),
                    "eager_step": round(eager_ms * 1e3, 1),
                    "rest_of_eager_step": round(eager_ms * 1e3 - gemm_ms * 1e3 / K, 1)},
         m1_ar_step_ms=round(ar_ms, 4),
@@ -266,42 +358,236 @@ def verify27b_workload(args):
     return res
 
 
-def verify27b_cpu_baseline():
-    """The CPU oracle on a bounded sample of the same step: one decoder layer
-    of the 27B-class shapes (4 W4 GEMMs over its 175 MB of weights, fp64),
-    scaled by 64 layers, plus the LM head (sampled 1/16 of the rows, scaled).
-    Attention/glue are O(L * d) and small next to the GEMMs at L = 8192;
-    they are left out of the sample (said so in `sample`)."""
-    import numpy as np
-
+def verify27b_cpu_baseline(reps=16):
+    """The CPU oracle on a bounded sample of the same step: the four W4 GEMMs
+    of one decoder layer at the 27B-class shapes (fp64 over its 175 MB of
+    codes) on `reps` fresh sets of M=4 rows, scaled to 64 layers, plus 1/16 of
+    the LM head rows (reps / 4 times, scaled by 16).  Attention and glue are
+    O(L * d) and small next to the GEMMs at L = 8192; they are left out of the
+    sample (said so in `sample`).  Quantisation is untimed."""
     import oracle
     from verify_step_w4_amd import synth
     g = synth.rng(synth.SEED_BASE + 4)
     shapes = [(7168, 5120), (5120, 5120), (34816, 5120), (5120, 17408)]
-    x = {K: synth.f32_to_bf16_bits(synth.normal_f32(g, (4, K), 1.0)) for _, K in shapes}
-    tot = 0.0
+    layer = 0.0
     for N, K in shapes:
-        w = synth.normal_f32(g, (N, K), 0.02)
-        codes, scales = oracle.w4_quantize(w)
-        del w
-        t0 = time.perf_counter()
-        oracle.w4_gemm(x[K], codes, scales)
-        tot += time.perf_counter() - t0
+        codes, scales = oracle.w4_quantize(synth.normal_f32(g, (N, K), 0.02))
+        for r in range(reps):
+            x = synth.f32_to_bf16_bits(synth.normal_f32(g, (4, K), 1.0))
+            t0 = time.perf_counter()
+            oracle.w4_gemm(x, codes, scales)
+            layer += time.perf_counter() - t0
     V16 = 151936 // 16
-    w = synth.normal_f32(g, (V16, 5120), 0.02)
-    codes, scales = oracle.w4_quantize(w)
-    t0 = time.perf_counter()
-    oracle.w4_gemm(x[5120], codes, scales)
-    lm = (time.perf_counter() - t0) * 16
-    step_s = 64 * tot + lm
+    codes, scales = oracle.w4_quantize(synth.normal_f32(g, (V16, 5120), 0.02))
+    lm = 0.0
+    lreps = max(1, reps // 4)
+    for r in range(lreps):
+        x = synth.f32_to_bf16_bits(synth.normal_f32(g, (4, 5120), 1.0))
+        t0 = time.perf_counter()
+        oracle.w4_gemm(x, codes, scales)
+        lm += time.perf_counter() - t0
+    step_s = 64 * layer / reps + 16 * lm / lreps
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(1.0 / step_s, 5), "unit": "verify steps/s", "cores": cores, "kind": "oracle",
-            "sample": "one 27B-class layer's four W4 GEMMs at M=4 (x64 layers) + 1/16 of the LM head (x16); "
-                      "attention and glue not in the sample"}
+            "sample": f"one 27B-class layer's four W4 GEMMs at M=4 on {reps} row sets (scaled to 64 layers) + "
+                      f"1/16 of the LM head on {lreps} row sets (scaled by 16); timed CPU work "
+                      f"{layer + lm:.1f} s; attention and glue not in the sample"}
+
+# --------------------------------------------------------------------------
+# MoE-shaped verify step
+# --------------------------------------------------------------------------
+def moe_workload(args):
+    import numpy as np
+    import torch
+
+    from verify_step_w4_amd import binding as B
+    from verify_step_w4_amd.model import BYTES_PER_WEIGHT, MOE_30B, ExpertBank, MoEVerify, W4Linear
+
+    cfg = dict(MOE_30B)
+    E, topk, d, F, V = (cfg[k] for k in ("n_exp", "topk", "d", "F", "V"))
+    M, D = 4, 3
+    T, top_p, seed = 0.6, 0.95, 0x5EED0005
+    nrot = 4                      # expert banks and LM heads rotated: 4 x 486 MB working set
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261205)
+    log(f"generating {nrot} expert banks ({E} x SwiGLU {d}->{F}->{d}) and {nrot} LM heads [{V}][{d}], W4")
+    banks = [ExpertBank.random(E, d, F, 0.02, gen) for _ in range(nrot)]
+    heads = [W4Linear.random(V, d, 0.02, gen) for _ in range(nrot)]
+    gamma = (1 + 0.02 * torch.randn(d, generator=gen, device=dev)).to(torch.bfloat16).view(torch.int16)
+    mvs = [MoEVerify(cfg, M, heads[k], gamma) for k in range(nrot)]
+    ar = [MoEVerify(cfg, 1, heads[k], gamma) for k in range(nrot)]
+    K, W = args.steps, args.warmup
+    npool = 8
+    router = torch.randn((K + W, M, E), generator=gen, device=dev, dtype=torch.float32)   # fresh per step
+    xs = torch.randn((npool, M, d), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+    qs = torch.softmax(torch.randn((npool, D, V), generator=gen, device=dev, dtype=torch.float64) * 3.0,
+                       dim=-1).to(torch.float32)
+    drafts = torch.multinomial(qs.reshape(-1, V).double(), 1, generator=gen).reshape(npool, D).to(torch.int32)
+    torch.cuda.synchronize()
+    ev = {"gate_up": [], "down": [], "lm_head": []}
+    cur = {}
+
+    def hook(when, name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        if when == "pre":
+            cur[name] = e
+        else:
+            ev[name].append((cur[name], e))
+
+    # (a) eager pass with the W4 GEMM launches bracketed by events
+    nsl_eager = torch.empty(K, dtype=torch.int32, device=dev)
+    for i in range(W):
+        k, j = i % nrot, i % npool
+        mvs[k].run(xs[j], router[i], banks[k], qs[j], drafts[j], T, top_p, seed, i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(K):
+        k, j = i % nrot, i % npool
+        mvs[k].run(xs[j], router[W + i], banks[k], qs[j], drafts[j], T, top_p, seed, i, gemm_hook=hook)
+        nsl_eager[i:i + 1].copy_(mvs[k].n_slots)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / K
+    t_us = {nm: np.array([a.elapsed_time(b) for a, b in v]) * 1e3 for nm, v in ev.items()}
+    nsl = nsl_eager.cpu().numpy().astype(np.float64)
+    eb_gu = 2 * F * d * BYTES_PER_WEIGHT
+    eb_dn = d * F * BYTES_PER_WEIGHT
+    gu_bytes = nsl * eb_gu + M * d * 2 + nsl * M * 2 * F * 4
+    dn_bytes = nsl * eb_dn + nsl * M * F * 2 + nsl * M * d * 4
+    lm_bytes = V * d * BYTES_PER_WEIGHT + M * d * 2 + M * V * 4
+    grouped = float((gu_bytes + dn_bytes).sum() / ((t_us["gate_up"] + t_us["down"]).sum() * 1e-6) / 1e9)
+    # (b) timed region: one graph per (bank, LM head) pair, replayed in turn;
+    # each replay is preceded by copying the step's inputs into the captured buffers
+    x_s, lg_s, q_s, d_s = xs[0].clone(), router[0].clone(), qs[0].clone(), drafts[0].clone()
+    step_dev = torch.zeros(1, dtype=torch.int64, device=dev)
+    graphs = [mvs[k].capture(x_s, lg_s, banks[k], q_s, d_s, T, top_p, seed, step_dev) for k in range(nrot)]
+    for i in range(W):
+        graphs[i % nrot].replay()
+    step_dev.zero_()
+    tok_all = torch.empty((K, M), dtype=torch.int32, device=dev)
+    nacc_all = torch.empty(K, dtype=torch.int32, device=dev)
+    flag_all = torch.empty(K, dtype=torch.int32, device=dev)
+    nsl_all = torch.empty(K, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        k, j = i % nrot, i % npool
+        x_s.copy_(xs[j])
+        lg_s.copy_(router[W + i])
+        q_s.copy_(qs[j])
+        d_s.copy_(drafts[j])
+        graphs[k].replay()
+        tok_all[i:i + 1].copy_(mvs[k].tokens)
+        nacc_all[i:i + 1].copy_(mvs[k].n_acc)
+        flag_all[i:i + 1].copy_(mvs[k].flags)
+        nsl_all[i:i + 1].copy_(mvs[k].n_slots)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    step_ms = total_ms / K
+    # (c) the M = 1 step (one row, D = 0) on the same weights, same way
+    x1, lg1 = xs[0][:1].clone(), router[0][:1].clone()
+    step1 = torch.zeros(1, dtype=torch.int64, device=dev)
+    g1 = [ar[k].capture(x1, lg1, banks[k], None, None, T, top_p, seed, step1) for k in range(nrot)]
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for i in range(K):
+        x1.copy_(xs[i % npool][:1])
+        lg1.copy_(router[W + i][:1])
+        g1[i % nrot].replay()
+    a1.record()
+    torch.cuda.synchronize()
+    ar_ms = a0.elapsed_time(a1) / K
+    # (d) the W4 GEMM kernel by itself: each bank's 3 GEMM launches on its
+    # last routing, captured as graphs and replayed in turn
+    ms_launch, n_launch = time_graphs([(lambda k=k: mvs[k].gemm_pass(banks[k])) for k in range(nrot)], 50)
+    ns_last = np.array([int(mv.n_slots.item()) for mv in mvs], dtype=np.float64)
+    pass_bytes = float((ns_last * (eb_gu + eb_dn + M * 2 * F * 4 + M * F * 2 + M * d * 4)).sum()
+                       + nrot * (M * d * 2 + lm_bytes))
+    per_launch_bytes = pass_bytes / n_launch
+    achieved = per_launch_bytes / (ms_launch * 1e-3) / 1e9
+    nacc = nacc_all.cpu().numpy()
+    flags = flag_all.cpu().numpy()
+    ns = nsl_all.cpu().numpy()
+    step_bytes = float(np.mean(ns)) * 3 * d * F * BYTES_PER_WEIGHT + V * d * BYTES_PER_WEIGHT
+    return dict(
+        ms_per_step=step_ms,
+        value=K / (total_ms * 1e-3),
+        wall_s=wall,
+        config={"workload": "moe_verify", "experts": E, "top_k": topk, "d_model": d, "expert_ffn": F, "V": V,
+                "M": M, "draft_depth": D, "temperature": T, "top_p": top_p,
+                "weights": "int4 group-64 symmetric, fp16 scales", "rotated_banks": nrot},
+        roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("moe_verify"),
+                  "kernel": "w4_gemm_kernel<4> (grouped gate|up, grouped down, LM head: the 3 W4 GEMM launches "
+                            "of a step, replayed as graphs)",
+                  "alg_bytes_per_launch": int(per_launch_bytes),
+                  "avg_launch_us": round(ms_launch * 1e3, 2)},
+        grouped_gemm_gbs=round(grouped, 1),
+        experts_per_step={"mean": round(float(np.mean(ns)), 2), "min": int(ns.min()), "max": int(ns.max())},
+        stages_us={"grouped_gate_up": round(float(t_us["gate_up"].mean()), 2),
+                   "grouped_down": round(float(t_us["down"].mean()), 2),
+                   "lm_head": round(float(t_us["lm_head"].mean()), 2),
+                   "eager_step": round(eager_ms * 1e3, 1)},
+        m1_ar_step_ms=round(ar_ms, 4),
+        verify_over_ar=round(step_ms / ar_ms, 4),
+        step_hbm_gbs=round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+        accepted_length_hist=np.bincount(np.clip(nacc, 0, D), minlength=D + 1).tolist(),
+        flagged_steps=int(((flags & ~B.FLAG_NONFINITE) != 0).sum()),
+    )
+
+
+def moe_cpu_baseline(nsteps=4):
+    """The CPU oracle on a bounded sample: nsteps whole MoE verify steps
+    (routing, the chosen experts expert by expert in fp64, the full LM head,
+    sorted-vocab top-p and the scalar accept loop).  Weight generation and
+    quantisation are untimed; only the experts a step routes to are built
+    (the router logits are restricted to them, which leaves the choice and the
+    renormalised weights unchanged)."""
+    import numpy as np
+
+    import oracle
+    from verify_step_w4_amd import synth
+    E, topk, d, F, V, M, D = 128, 8, 2048, 768, 151936, 4, 3
+    g = synth.rng(synth.SEED_BASE + 5)
+    lm = oracle.w4_quantize(synth.normal_f32(g, (V, d), 0.02))
+    gamma = synth.f32_to_bf16_bits(1 + synth.normal_f32(g, (d,), 0.02))
+    q, drafts = synth.q_and_drafts(synth.SEED_BASE + 55, D, V, 3.0, B=nsteps)
+    dt = 0.0
+    for s in range(nsteps):
+        x = synth.f32_to_bf16_bits(synth.normal_f32(g, (M, d), 1.0))
+        lg = synth.normal_f32(g, (M, E), 1.0)
+        chosen = np.unique(oracle.moe_route(lg, topk)[0])
+        mask = np.full((M, E), -np.inf, dtype=np.float32)
+        for m, row in enumerate(oracle.moe_route(lg, topk)[0]):
+            mask[m, row] = lg[m, row]
+        sub = np.ascontiguousarray(mask[:, chosen])
+        gu = [oracle.w4_quantize(synth.normal_f32(g, (2 * F, d), 0.02)) for _ in chosen]
+        dn = [oracle.w4_quantize(synth.normal_f32(g, (d, F), 0.02)) for _ in chosen]
+        st = lambda L: (np.stack([a for a, _ in L]), np.stack([b for _, b in L]))
+        t0 = time.perf_counter()
+        _, _, y = oracle.moe_block(x, sub, topk, st(gu), st(dn))
+        resid = oracle.bf16_round(synth.bf16_bits_to_f32(x).astype(np.float64) + y)
+        h = oracle.bf16_round(oracle.rmsnorm(resid, gamma, 1e-6))
+        z = oracle.w4_gemm(h, *lm).astype(np.float32)
+        oracle.spec_accept(z, q, drafts[s], 0.6, 0.95, 0x5EED0005, s)
+        dt += time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(nsteps / dt, 4), "unit": "verify steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nsteps} whole MoE verify steps (128 experts top-8, d=2048, FFN 768, V=151936, M=4); "
+                      "weight generation and quantisation untimed"}
 
 
 WORKLOADS = {"lm_head_verify": (lm_head_workload, lm_head_cpu_baseline),
-             "verify27b": (verify27b_workload, verify27b_cpu_baseline)}
+             "verify27b": (verify27b_workload, verify27b_cpu_baseline),
+             "moe_verify": (moe_workload, moe_cpu_baseline)}
 
 
 def main():
@@ -309,7 +595,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="lm_head_verify", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="verify27b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--context", type=int, default=8192, help="KV context length L of the verify27b workload")
     args = ap.parse_args()
@@ -322,13 +608,21 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     run, cpu = WORKLOADS[args.workload]
+    # A plain copy kernel of known size (256 MiB read, 256 MiB written), run
+    # once before the workload: HBM byte counters read in the same process
+    # are calibrated against it.
+    src = torch.ones(CALIB_COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
     res = run(args)
     out = {"metric": METRIC, "value": round(res["value"], 3), "unit": "verify steps/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic", "config": res["config"], "roofline": res["roofline"]}
-    for k in ("stages_us", "accepted_length_hist", "flagged_steps", "m1_ar_step_ms", "verify_over_ar",
-              "step_hbm_gbs"):
+    for k in ("stages_us", "w4_gemm_by_linear", "accepted_length_hist", "flagged_steps", "m1_ar_step_ms",
+              "verify_over_ar", "step_hbm_gbs", "experts_per_step", "grouped_gemm_gbs"):
         if k in res:
             out[k] = res[k]
     if not args.no_cpu_baseline:

@@ -214,6 +214,25 @@ class Decoder:
         hook("post", "lm_head")
         return self.logits[:M]
 
+    def gemm_pass(self, M: int, stream=None, names=("qkv", "o", "gate_up", "down", "lm_head")):
+        """Only the W4 GEMM launches of one forward (same shapes, weights and
+        buffers, in the same order; optionally only the named linears), for
+        timing the GEMM kernel by itself.  Returns the launch count."""
+        c = self.cfg
+        n = 0
+        for W in self.layers:
+            for name, x in (("qkv", self.h), ("o", self.attn), ("gate_up", self.h), ("down", self.a)):
+                if name in names:
+                    N, K = self.shapes[name]
+                    B.w4_skinny_gemm_partials(x[:M], W[name].packed, W[name].pscales, self.parts[name], M, N, K,
+                                              stream)
+                    n += 1
+        if "lm_head" in names:
+            B.w4_skinny_gemm(self.h[:M], self.lm_head.packed, self.lm_head.pscales, self.logits[:M], M, c["V"],
+                             c["d"], ws=self.lm_ws, stream=stream)
+            n += 1
+        return n
+
     def gemm_alg_bytes(self, M: int) -> int:
         """Algorithmic bytes of one forward's W4 GEMMs: each weight (code +
         scale) once, activations in, fp32 outputs out."""
@@ -377,6 +396,20 @@ class MoEVerify:
         B.moe_combine(self.part_dn, self.dn_S, self.dn_ldp, self.dn_sstride, self.row_slot, self.weights, M,
                       self.topk, d, self.y, d, stream)
         return self.y
+
+    def gemm_pass(self, bank: ExpertBank, stream=None):
+        """Only the W4 GEMM launches of one step (grouped gate|up, grouped
+        down, LM head) on the current routing and buffers."""
+        M, d, F, ms = self.M, self.d, self.F, self.max_slots
+        B.w4_grouped_gemm(self.h, d, 0, bank.gate_up.packed, bank.gu_estride[0], bank.gate_up.pscales,
+                          bank.gu_estride[1], self.slot_expert, self.n_slots, ms, self.part_gu, self.gu_sstride,
+                          M, 2 * F, d, stream)
+        B.w4_grouped_gemm(self.a, F, M * F, bank.down.packed, bank.dn_estride[0], bank.down.pscales,
+                          bank.dn_estride[1], self.slot_expert, self.n_slots, ms, self.part_dn, self.dn_sstride,
+                          M, d, F, stream)
+        B.w4_skinny_gemm(self.h, self.lm_head.packed, self.lm_head.pscales, self.logits, M, self.V, d, ws=self.lm_ws,
+                         stream=stream)
+        return 3
 
     def forward(self, x, router_logits, bank: ExpertBank, stream=None, gemm_hook=None):
         """Logits [M][V] of the M rows: LM head of bf16(rmsnorm(x + moe(x)) * gamma)."""
