@@ -228,10 +228,11 @@ VW4_API int vw4_add_rmsnorm(uint16_t* resid, const float* part, int32_t S, int64
 
 /* From the fused q|k|v projection (partials of [M][(nq + 2 nkv) * hd]): rotary
  * embedding (rotate-half, base theta, position L + m) of q and k; q -> q_out
- * [M][nq][hd]; k and v appended to the caches Kc, Vc [nkv][Lmax][hd] at
- * positions L + m.  hd even, L + M <= Lmax. */
+ * [M][nq][hd]; k appended to the key cache Kc [nkv][Lmax][hd] and v to the
+ * transposed value cache Vt [nkv][hd][Lmax], both at positions L + m.
+ * hd even, L + M <= Lmax. */
 VW4_API int vw4_rope_kv_append(const float* part, int32_t S, int64_t ldp, int32_t M, int32_t nq, int32_t nkv,
-                               int32_t hd, int32_t L, float theta, uint16_t* q_out, uint16_t* Kc, uint16_t* Vc,
+                               int32_t hd, int32_t L, float theta, uint16_t* q_out, uint16_t* Kc, uint16_t* Vt,
                                int64_t Lmax, void* stream);
 
 /* a[M][F] = bf16(silu(g) * u) with g = part[.][m][0:F], u = part[.][m][F:2F]
@@ -240,11 +241,15 @@ VW4_API int vw4_swiglu(const float* part, int32_t S, int64_t ldp, int32_t M, int
 
 /* Grouped-query decode attention for M verify rows: query head h reads KV head
  * h / (nq / nkv); row m attends to positions 0 .. L + m of the cache (causal
- * inside the verify rows); softmax(q k^T / sqrt(hd)) v with fp32 accumulation.
- * q [M][nq][hd]; Kc, Vc [nkv][Lmax][hd]; out [M][nq * hd] bf16.  hd == 128,
- * nq % nkv == 0, (nq / nkv) * M <= 64.  Workspace: vw4_attn_workspace_bytes. */
+ * inside the verify rows); softmax(q k^T / sqrt(hd)) v, computed tile by tile
+ * with an online softmax (gist.science BaseRT summary, "メソドロジー") on the
+ * matrix cores: bf16 products, fp32 accumulation, the probabilities of the
+ * P.V product split into a bf16 head and tail (about 16 significant bits).  q [M][nq][hd]; keys Kc [nkv][Lmax][hd]; values
+ * transposed, Vt [nkv][hd][Lmax]; out [M][nq * hd] bf16.  hd == 128,
+ * nq % nkv == 0, (nq / nkv) * M <= 48, Lmax % 8 == 0, q / Kc / Vt 16-byte
+ * aligned.  Workspace: vw4_attn_workspace_bytes. */
 VW4_API size_t vw4_attn_workspace_bytes(int32_t M, int32_t nq, int32_t nkv, int32_t hd, int64_t ctx);
-VW4_API int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_t* Vc, int64_t Lmax, int64_t L,
+VW4_API int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_t* Vt, int64_t Lmax, int64_t L,
                             int32_t M, int32_t nq, int32_t nkv, int32_t hd, uint16_t* out, void* ws, size_t ws_bytes,
                             void* stream);
 

@@ -75,7 +75,7 @@ def test_rope_kv_append(M, L, S):
     part = partials(L + S, S, M, N, ldp)
     qd = torch.empty((M, nq, hd), dtype=torch.int16, device="cuda")
     Kc = torch.zeros((nkv, Lmax, hd), dtype=torch.int16, device="cuda")
-    Vc = torch.zeros((nkv, Lmax, hd), dtype=torch.int16, device="cuda")
+    Vc = torch.zeros((nkv, hd, Lmax), dtype=torch.int16, device="cuda")      # values transposed
     B.rope_kv_append(dev(part), S, ldp, M, nq, nkv, hd, L, 10000.0, qd, Kc, Vc, Lmax)
     torch.cuda.synchronize()
     x = part.astype(np.float64).sum(axis=0)          # exact sum of the partials
@@ -88,7 +88,7 @@ def test_rope_kv_append(M, L, S):
             k_ref[m, h] = oracle.rope(x[m, (nq + h) * hd:(nq + h + 1) * hd], L + m)
     v_ref = x[:, (nq + nkv) * hd:].reshape(M, nkv, hd)
     bf16_close(host(qd), q_ref)
-    Kh, Vh = host(Kc), host(Vc)
+    Kh, Vh = host(Kc), host(Vc).transpose(0, 2, 1)
     bf16_close(np.stack([Kh[:, L + m] for m in range(M)]), k_ref)
     bf16_close(np.stack([Vh[:, L + m] for m in range(M)]), v_ref)
     # nothing else of the cache is touched
@@ -112,25 +112,39 @@ def test_swiglu(M, F, S):
     bf16_close(host(ad), ref)
 
 
-def _attn_case(M, nq, nkv, L, seed):
+def _vt(Vc):
+    """Host [nkv][Lmax][hd] values -> the kernel's transposed [nkv][hd][Lmax] layout."""
+    return np.ascontiguousarray(Vc.transpose(0, 2, 1))
+
+
+def _attn_case(M, nq, nkv, L, seed, Lmax=None):
     import torch
     hd = 128
-    Lmax = L + M + 5
+    Lmax = Lmax or (L + M + 5 + 7) // 8 * 8
     q = synth.activations_bf16(seed, M * nq, hd).reshape(M, nq, hd)
     Kc = synth.activations_bf16(seed + 1, nkv * Lmax, hd).reshape(nkv, Lmax, hd)
     Vc = synth.activations_bf16(seed + 2, nkv * Lmax, hd).reshape(nkv, Lmax, hd)
     out = torch.empty((M, nq * hd), dtype=torch.int16, device="cuda")
     ws = B.workspace(B.attn_workspace_bytes(M, nq, nkv, hd, L + M))
-    B.decode_attn(dev(q), dev(Kc), dev(Vc), Lmax, L, M, nq, nkv, hd, out, ws)
+    B.decode_attn(dev(q), dev(Kc), dev(_vt(Vc)), Lmax, L, M, nq, nkv, hd, out, ws)
     torch.cuda.synchronize()
     return q, Kc, Vc, host(out).reshape(M, nq, hd)
 
 
 @pytest.mark.parametrize("M,nq,nkv,L", [(4, 40, 8, 0), (4, 40, 8, 100), (1, 40, 8, 1023), (4, 40, 8, 1024),
-                                        (2, 8, 2, 777), (6, 10, 2, 300), (4, 40, 8, 8192)])
+                                        (2, 8, 2, 777), (6, 10, 2, 300), (4, 40, 8, 8192), (8, 40, 8, 777),
+                                        (3, 40, 8, 31), (6, 40, 8, 2049), (1, 40, 8, 0), (4, 40, 8, 32764)])
 def test_decode_attn(M, nq, nkv, L):
     log(f"attn M={M} nq={nq} nkv={nkv} L={L}")
     q, Kc, Vc, out = _attn_case(M, nq, nkv, L, 1000 + L + M)
+    ref = oracle.decode_attn(synth.bf16_bits_to_f32(q).astype(np.float64), Kc, Vc, L)
+    bf16_close(out, ref)
+
+
+def test_decode_attn_context_ends_at_cache_end():
+    """L + M == Lmax: the last tile's rows run past the cache and must be masked."""
+    M, nq, nkv, L = 4, 40, 8, 1020
+    q, Kc, Vc, out = _attn_case(M, nq, nkv, L, 55, Lmax=1024)
     ref = oracle.decode_attn(synth.bf16_bits_to_f32(q).astype(np.float64), Kc, Vc, L)
     bf16_close(out, ref)
 
@@ -146,7 +160,7 @@ def test_decode_attn_causal_rows():
     Vc2[:, L + 1:] = 0
     out2 = torch.empty((M, nq * hd), dtype=torch.int16, device="cuda")
     ws = B.workspace(B.attn_workspace_bytes(M, nq, nkv, hd, L + M))
-    B.decode_attn(dev(q), dev(Kc2), dev(Vc2), Lmax, L, M, nq, nkv, hd, out2, ws)
+    B.decode_attn(dev(q), dev(Kc2), dev(_vt(Vc2)), Lmax, L, M, nq, nkv, hd, out2, ws)
     torch.cuda.synchronize()
     o2 = host(out2).reshape(M, nq, hd)
     assert np.array_equal(o2[0], out[0])

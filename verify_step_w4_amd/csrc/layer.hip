@@ -1,6 +1,6 @@
 // layer.hip — decoder-layer calls of the verify forward: residual add +
 // RMSNorm, rotary embedding + KV-cache append, SwiGLU, grouped-query decode
-// attention for the M verify rows.
+// attention for the M verify rows (matrix cores).
 //
 // hazakura.dev, "mtplx——M5 Maxで63tok/s…", section "4層のアーキテクチャ", Layer 1:
 // target and drafter share one checkpoint and its KV cache, and all drafts are
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(NCOL) void rmsnorm_apply_kernel(const uint16_t* __r
 // ---------------------------------------------------------------------------
 __global__ void rope_kv_kernel(const float* __restrict__ part, int S, int64_t ldp, int M, int nq, int nkv, int hd,
                                int L, double theta, uint16_t* __restrict__ q_out, uint16_t* __restrict__ Kc,
-                               uint16_t* __restrict__ Vc, int64_t Lmax) {
+                               uint16_t* __restrict__ Vt, int64_t Lmax) {
     const int hh = blockIdx.x, m = blockIdx.y, d = threadIdx.x, half = hd / 2;
     const int64_t c0 = (int64_t)hh * hd;
     const float a = sum_parts(part, S, M, ldp, m, c0 + d);
@@ -83,9 +83,9 @@ __global__ void rope_kv_kernel(const float* __restrict__ part, int S, int64_t ld
     const int64_t pos = (int64_t)L + m;
     if (hh >= nq + nkv) {  // value head: append as is
         const int kv = hh - nq - nkv;
-        uint16_t* dst = Vc + ((int64_t)kv * Lmax + pos) * hd;
-        dst[d] = f32_to_bf16(a);
-        dst[d + half] = f32_to_bf16(b);
+        uint16_t* dst = Vt + (int64_t)kv * hd * Lmax + pos;     // transposed: [kv][dim][position]
+        dst[(int64_t)d * Lmax] = f32_to_bf16(a);
+        dst[(int64_t)(d + half) * Lmax] = f32_to_bf16(b);
         return;
     }
     // angle = pos * theta^(-2d/hd), in fp64 so that large positions keep their
@@ -130,157 +130,306 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ p
 }
 
 // ---------------------------------------------------------------------------
-// Grouped-query decode attention.
+// Grouped-query decode attention on the matrix cores.
 //
-// grid = (nkv, nchunks), 256 threads (4 wavefronts).  Workgroup (h, c) owns
-// context positions [c * CP, (c + 1) * CP) of KV head h and all QN = G * M
-// queries that read it (G = nq / nkv query heads, M rows); query j is head
-// h * G + j / M, row j % M.  Per 64-position tile, a wavefront:
-//   1. lane = position: loads its key row (16 x 16 B) and forms the QN scores
-//      with v_dot2_f32_bf16, the query rows coming through scalar loads
-//      (identical for all lanes);
-//   2. masks positions > L + row, takes the tile max per query (wave
-//      reduction), p = exp(s - max), and stores p to LDS;
-//   3. lane = pair of dims: accumulates p * v over the tile's positions, the p
-//      row of each position read back from LDS as a broadcast;
-// with an online softmax across the wavefront's tiles.  The 4 wavefronts'
-// (max, sum, o) are merged in LDS and the workgroup writes one partial per
-// query; attn_combine_kernel merges the chunks (log-sum-exp weights, chunk
-// order).
+// KV cache layout: K [nkv][Lmax][128] (a position is one 256-byte row) and V
+// transposed, Vt [nkv][128][Lmax] (a head dimension is one row of positions),
+// so that both contractions read 16-byte runs straight into MFMA operands.
+//
+// grid = (nkv, nparts), 4 wavefronts.  Workgroup (h, c) owns a contiguous
+// range of 32-position tiles of KV head h and all QN = G * M queries that read
+// it (query j: head h * G + j / M, row j % M; row m sees positions
+// 0 .. L + m).  Wavefront w takes tiles w, w + 4, ... of the range; the next
+// tile's K rows are requested once the scores have consumed the current ones,
+// its V rows once P.V has.  Per tile, with
+// v_mfma_f32_16x16x32_bf16 (A: lane l = row l % 16, k 8 (l / 16) .. +8;
+// B: lane l = column l % 16, same k; D: lane l = column l % 16, rows
+// 4 (l / 16) .. +4):
+//   S^T[pos][query] = K[pos][:] . Q[query][:]   (A = K rows, B = queries),
+//     the 16 A rows of block b being positions 8 (i / 4) + 4 b + i % 4, so
+//     that lane (g, i) ends up holding query i at positions 8 g .. 8 g + 7;
+//   online softmax in base 2 (scores pre-scaled by log2(e) / sqrt(128));
+//   O[query][dim] += P[query][pos] . V[pos][dim]  (A = those 8 probabilities
+//     as a bf16 head plus a bf16 tail, two products, so P keeps about 16
+//     bits; B = 16 bytes of a Vt row).
+// The four wavefronts merge pairwise in LDS ((w0 + w2) + (w1 + w3)), and the
+// workgroup writes one partial (m, l, o) per query; attn_combine_kernel
+// merges the partials in chunk order.
 // ---------------------------------------------------------------------------
 constexpr int AHD = 128;       // head dim handled
-constexpr int AQN = 64;        // max queries per KV head (G * M)
-constexpr int ATILE = 64;      // positions per wavefront tile
+constexpr int AQN = 48;        // max queries per KV head (G * M)
+constexpr int AT = 32;         // positions per tile
+constexpr int AWV = 4;         // wavefronts per workgroup
 
-typedef const __attribute__((address_space(4))) uint32_t acu32;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4v;
 
-__device__ __forceinline__ acu32* uniform_ptr_a(acu32* p) {
-    const uint64_t a = (uint64_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    return (acu32*)(((uint64_t)hi << 32) | lo);
-}
-
-__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-
-struct AttnPart {   // per (kv head, chunk, query): max, sum, then o[AHD]
+struct AttnPart {   // per (kv head, query, chunk): max (base 2), sum
     float m, l;
 };
 
-template <int QN>
-__global__ __launch_bounds__(256) void attn_chunk_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
-                                                         const uint16_t* __restrict__ Vc, int64_t Lmax, int64_t L, int M,
-                                                         int nq, int G, int CP, float scale, float* __restrict__ ws_o,
-                                                         AttnPart* __restrict__ ws_ml) {
-    // p values of the current tile per wavefront during the loop; the
-    // wavefronts' o accumulators at the merge (same storage)
-    constexpr int PSZ = 4 * ATILE * QN, WSZ = 4 * QN * AHD;
-    __shared__ float smem[PSZ > WSZ ? PSZ : WSZ];
-    __shared__ float Wm[4][QN], Wl[4][QN];
-    float(*P)[ATILE][QN] = (float(*)[ATILE][QN])smem;
-    float(*Wo)[QN][AHD] = (float(*)[QN][AHD])smem;
-    const int h = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int64_t ctx = L + M;                                  // filled cache positions
-    const int64_t p0 = (int64_t)c * CP, p1 = min(ctx, p0 + CP);
+__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
+    return __builtin_bit_cast(bf16x8, *(const u32x4v*)p);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+struct AttnTile {
+    bf16x8 k[2][4];   // K rows of the two 16-position blocks, 4 steps of 32 dims
+    bf16x8 v[8];      // Vt rows of the 8 16-dim blocks, positions 8 g .. +8
+};
+
+__device__ __forceinline__ void attn_load_k(AttnTile& T, const uint16_t* Kh, int64_t ctx, int64_t t0, int g, int i) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        int64_t pos = t0 + 8 * (i >> 2) + 4 * b + (i & 3);
+        pos = pos < ctx ? pos : ctx - 1;               // rows past the context are masked later
+#pragma unroll
+        for (int s = 0; s < 4; ++s) T.k[b][s] = ld_bf16x8(Kh + pos * AHD + 32 * s + 8 * g);
+    }
+}
+
+__device__ __forceinline__ void attn_load_v(AttnTile& T, const uint16_t* Vh, int64_t Lmax, int64_t ctx, int64_t t0,
+                                            int g, int i) {
+    const int64_t p8 = t0 + 8 * g;
+    if (p8 + 8 <= ctx) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) T.v[db] = ld_bf16x8(Vh + (int64_t)(db * 16 + i) * Lmax + p8);
+    } else {
+        // the context ends inside these 8 positions: zeros past it (their
+        // probabilities are 0, and 0 * NaN would not be)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            uint16_t e8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) e8[e] = (p8 + e < ctx) ? Vh[(int64_t)(db * 16 + i) * Lmax + p8 + e] : 0;
+            T.v[db] = __builtin_bit_cast(bf16x8, e8);
+        }
+    }
+}
+
+// One tile: scores from T.k, then (once T.k is consumed) the next tile's K
+// rows are requested; softmax; P.V from T.v, then the next tile's V rows.
+template <int NQB>
+__device__ __forceinline__ void attn_tile(AttnTile& T, const bf16x8 (&qop)[NQB][4], const int64_t (&lim)[NQB],
+                                          int64_t t0, int g, int i, float sl2e, float (&mrun)[NQB], float (&lrun)[NQB],
+                                          f32x4 (&o)[NQB][8], bool more, int64_t tn0, const uint16_t* Kh,
+                                          const uint16_t* Vh, int64_t Lmax, int64_t ctx) {
+    f32x4 sc[NQB][2];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        sc[qb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sc[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            sc[qb][0] = mfma16(T.k[0][s], qop[qb][s], sc[qb][0]);
+            sc[qb][1] = mfma16(T.k[1][s], qop[qb][s], sc[qb][1]);
+        }
+    }
+    if (more) attn_load_k(T, Kh, ctx, tn0, g, i);
+    bf16x8 pv[NQB], pw[NQB];   // p = pv + pw to about 2^-17 (bf16 head and tail)
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        float v[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            v[r] = sc[qb][0][r] * sl2e;
+            v[4 + r] = sc[qb][1][r] * sl2e;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (t0 + 8 * g + e > lim[qb]) v[e] = -INFINITY;
+            mx = fmaxf(mx, v[e]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(mrun[qb], mx);
+        const float mu = (mnew == -INFINITY) ? 0.0f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(mrun[qb] - mu);
+        float ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(v[e] - mu);
+            ps += p;
+            const __bf16 hi = (__bf16)p;
+            pv[qb][e] = hi;
+            pw[qb][e] = (__bf16)(p - (float)hi);
+        }
+        lrun[qb] = lrun[qb] * alpha + ps;
+        mrun[qb] = mnew;
+        // O rows are queries 4 g + r; their factor lives in lane 16 g + 4 g + r
+        float a4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a4[r] = __shfl(alpha, 20 * g + r, 64);
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[qb][db][r] *= a4[r];
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+            o[qb][db] = mfma16(pv[qb], T.v[db], o[qb][db]);
+            o[qb][db] = mfma16(pw[qb], T.v[db], o[qb][db]);
+        }
+    if (more) attn_load_v(T, Vh, Lmax, ctx, tn0, g, i);
+}
+
+// Merge another wavefront's state (LDS slot) into this one's registers.
+template <int NQB>
+__device__ __forceinline__ void attn_merge(const float* Wo, const float* Wm, const float* Wl, int lane, int g, int i,
+                                           float (&mrun)[NQB], float (&lrun)[NQB], f32x4 (&o)[NQB][8]) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const float mb = Wm[qb * 16 + i], lb = Wl[qb * 16 + i];
+        const float mx = fmaxf(mrun[qb], mb);
+        const float mu = (mx == -INFINITY) ? 0.0f : mx;
+        const float fa = __builtin_amdgcn_exp2f(mrun[qb] - mu), fb = __builtin_amdgcn_exp2f(mb - mu);
+        lrun[qb] = fa * lrun[qb] + fb * lb;
+        mrun[qb] = mx;
+        float fa4[4], fb4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            fa4[r] = __shfl(fa, 20 * g + r, 64);
+            fb4[r] = __shfl(fb, 20 * g + r, 64);
+        }
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                o[qb][db][r] = fa4[r] * o[qb][db][r] + fb4[r] * Wo[((qb * 8 + db) * 4 + r) * 64 + lane];
+    }
+}
+
+template <int NQB>
+__device__ __forceinline__ void attn_store(float* Wo, float* Wm, float* Wl, int lane, int g, int i,
+                                           const float (&mrun)[NQB], const float (&lrun)[NQB],
+                                           const f32x4 (&o)[NQB][8]) {
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        if (g == 0) {
+            Wm[qb * 16 + i] = mrun[qb];
+            Wl[qb * 16 + i] = lrun[qb];
+        }
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Wo[((qb * 8 + db) * 4 + r) * 64 + lane] = o[qb][db][r];
+    }
+}
+
+template <int NQB>
+__device__ __forceinline__ void attn_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
+                                          const uint16_t* __restrict__ Vt, int64_t Lmax, int64_t L, int M, int nq,
+                                          int G, int ntiles, float sl2e, float* __restrict__ ws_o,
+                                          AttnPart* __restrict__ ws_ml) {
+    constexpr int OSZ = NQB * 8 * 4 * 64;                  // one wavefront's o, lane-major
+    __shared__ float Wo[2][OSZ];
+    __shared__ float Wm[2][NQB * 16], Wl[2][NQB * 16];
+    const int QN = G * M;
+    const int h = blockIdx.x, c = blockIdx.y, nparts = gridDim.y;
+    const int tid = threadIdx.x;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, i = lane & 15;
+    const int64_t ctx = L + M;
+    const int tb = (int)((int64_t)c * ntiles / nparts), te = (int)((int64_t)(c + 1) * ntiles / nparts);
     const uint16_t* Kh = Kc + (int64_t)h * Lmax * AHD;
-    const uint16_t* Vh = Vc + (int64_t)h * Lmax * AHD;
+    const uint16_t* Vh = Vt + (int64_t)h * AHD * Lmax;
 
-    float mrun[QN], lrun[QN], o0[QN], o1[QN];
+    bf16x8 qop[NQB][4];
+    int64_t lim[NQB];
 #pragma unroll
-    for (int j = 0; j < QN; ++j) { mrun[j] = -INFINITY; lrun[j] = 0.0f; o0[j] = 0.0f; o1[j] = 0.0f; }
-
-    for (int64_t t0 = p0 + (int64_t)wv * ATILE; t0 < p1; t0 += 4 * ATILE) {
-        const int64_t pos = t0 + lane;
-        const bool valid = pos < p1;
-        // 1. scores for this lane's position
-        uint32_t kr[AHD / 2];
-        const uint4* kp = (const uint4*)(Kh + (valid ? pos : p0) * AHD);
-#pragma unroll
-        for (int v = 0; v < AHD / 8; ++v) {
-            const uint4 w = kp[v];
-            kr[4 * v] = w.x; kr[4 * v + 1] = w.y; kr[4 * v + 2] = w.z; kr[4 * v + 3] = w.w;
-        }
-        float s[QN];
-#pragma unroll
-        for (int j = 0; j < QN; ++j) {
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int j = qb * 16 + i;
+        if (j < QN) {
             const int row = j % M, head = h * G + j / M;
-            acu32* qp = uniform_ptr_a((acu32*)(q + ((int64_t)row * nq + head) * AHD));
-            float acc = 0.0f;
+            const uint16_t* qp = q + ((int64_t)row * nq + head) * AHD;
 #pragma unroll
-            for (int t = 0; t < AHD / 2; ++t) acc = dot2bf(kr[t], qp[t], acc);
-            const bool vis = valid && pos <= L + row;
-            s[j] = vis ? acc * scale : -INFINITY;
+            for (int s = 0; s < 4; ++s) qop[qb][s] = ld_bf16x8(qp + 32 * s + 8 * g);
+            lim[qb] = L + row;
+        } else {
+            const bf16x8 z = {};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) qop[qb][s] = z;
+            lim[qb] = -1;
         }
-        // 2. tile max, probabilities, online-softmax rescale
+    }
+    float mrun[NQB], lrun[NQB];
+    f32x4 o[NQB][8];
 #pragma unroll
-        for (int j = 0; j < QN; ++j) {
-            float mx = s[j];
+    for (int qb = 0; qb < NQB; ++qb) {
+        mrun[qb] = -INFINITY;
+        lrun[qb] = 0.0f;
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-            const float mnew = fmaxf(mrun[j], mx);
-            const float pj = (s[j] == -INFINITY) ? 0.0f : expf(s[j] - mnew);
-            const float alpha = (mrun[j] == -INFINITY) ? 0.0f : expf(mrun[j] - mnew);
-            float ls = pj;
+        for (int db = 0; db < 8; ++db) o[qb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    // one tile of registers: the next tile's K (V) rows are requested as soon
+    // as the current ones have been consumed
+    AttnTile T;
+    int t = tb + wv;
+    if (t < te) {
+        attn_load_k(T, Kh, ctx, (int64_t)t * AT, g, i);
+        attn_load_v(T, Vh, Lmax, ctx, (int64_t)t * AT, g, i);
+    }
+    for (; t < te; t += AWV) {
+        const int tn = t + AWV;
+        attn_tile<NQB>(T, qop, lim, (int64_t)t * AT, g, i, sl2e, mrun, lrun, o, tn < te, (int64_t)tn * AT, Kh, Vh,
+                       Lmax, ctx);
+    }
+    // row sums over the four lanes that share a query
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off, 64);
-            lrun[j] = lrun[j] * alpha + ls;
-            o0[j] *= alpha;
-            o1[j] *= alpha;
-            mrun[j] = mnew;
-            P[wv][lane][j] = pj;
+    for (int qb = 0; qb < NQB; ++qb) {
+        lrun[qb] += __shfl_xor(lrun[qb], 16, 64);
+        lrun[qb] += __shfl_xor(lrun[qb], 32, 64);
+    }
+    // (w0 + w2) and (w1 + w3), then their sum, in wavefront 0
+    if (wv >= 2) attn_store<NQB>(Wo[wv - 2], Wm[wv - 2], Wl[wv - 2], lane, g, i, mrun, lrun, o);
+    __syncthreads();
+    if (wv < 2) attn_merge<NQB>(Wo[wv], Wm[wv], Wl[wv], lane, g, i, mrun, lrun, o);
+    __syncthreads();
+    if (wv == 1) attn_store<NQB>(Wo[0], Wm[0], Wl[0], lane, g, i, mrun, lrun, o);
+    __syncthreads();
+    if (wv != 0) return;
+    attn_merge<NQB>(Wo[0], Wm[0], Wl[0], lane, g, i, mrun, lrun, o);
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int j = qb * 16 + i;
+        if (g == 0 && j < QN) {
+            AttnPart ap;
+            ap.m = mrun[qb];
+            ap.l = lrun[qb];
+            ws_ml[((int64_t)h * QN + j) * nparts + c] = ap;
         }
-        // (LDS accesses of one wavefront execute in order: its reads below see
-        // the writes above without a workgroup barrier)
-        __builtin_amdgcn_wave_barrier();
-        // 3. p * v with lane = dims (2 * lane, 2 * lane + 1); V rows loaded 8 at a time
-        const int ntile = (int)min((int64_t)ATILE, p1 - t0);
-        for (int u0 = 0; u0 < ntile; u0 += 8) {
-            uint32_t vv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                vv[e] = (u0 + e < ntile) ? *((const uint32_t*)(Vh + (t0 + u0 + e) * AHD) + lane) : 0u;
+        for (int r = 0; r < 4; ++r) {
+            const int jr = qb * 16 + 4 * g + r;
+            if (jr < QN) {
+                float* dst = ws_o + (((int64_t)h * QN + jr) * nparts + c) * AHD + i;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if (u0 + e >= ntile) break;
-                const float v0 = bf16_to_f32((uint16_t)(vv[e] & 0xffffu)), v1 = bf16_to_f32((uint16_t)(vv[e] >> 16));
-#pragma unroll
-                for (int j = 0; j < QN; ++j) {
-                    const float pj = P[wv][u0 + e][j];
-                    o0[j] = fmaf(pj, v0, o0[j]);
-                    o1[j] = fmaf(pj, v1, o1[j]);
-                }
+                for (int db = 0; db < 8; ++db) dst[db * 16] = o[qb][db][r];
             }
         }
-        __builtin_amdgcn_wave_barrier();
     }
-    __syncthreads();  // every wavefront is done with P before it is reused as Wo
-    // merge the 4 wavefronts of the workgroup
-#pragma unroll
-    for (int j = 0; j < QN; ++j) {
-        if (lane == 0) { Wm[wv][j] = mrun[j]; Wl[wv][j] = lrun[j]; }
-        Wo[wv][j][2 * lane] = o0[j];
-        Wo[wv][j][2 * lane + 1] = o1[j];
-    }
-    __syncthreads();
-    const int nparts = gridDim.y;
-    for (int idx = tid; idx < QN * AHD; idx += 256) {
-        const int j = idx / AHD, d = idx % AHD;
-        float mx = -INFINITY;
-        for (int w = 0; w < 4; ++w) mx = fmaxf(mx, Wm[w][j]);
-        float lt = 0.0f, ot = 0.0f;
-        for (int w = 0; w < 4; ++w) {
-            const float f = (Wm[w][j] == -INFINITY) ? 0.0f : expf(Wm[w][j] - mx);
-            lt += f * Wl[w][j];
-            ot += f * Wo[w][j][d];
-        }
-        const int64_t pi = ((int64_t)h * QN + j) * nparts + c;
-        ws_o[pi * AHD + d] = ot;
-        if (d == 0) { AttnPart ap; ap.m = mx; ap.l = lt; ws_ml[pi] = ap; }
-    }
+}
+
+// Up to 32 queries per KV head: two workgroups per CU (no more than 256
+// registers per lane).  More queries: one workgroup per CU, no spills.
+template <int NQB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vt, int64_t Lmax,
+    int64_t L, int M, int nq, int G, int ntiles, float sl2e, float* __restrict__ ws_o, AttnPart* __restrict__ ws_ml) {
+    attn_body<NQB>(q, Kc, Vt, Lmax, L, M, nq, G, ntiles, sl2e, ws_o, ws_ml);
+}
+
+__global__ __launch_bounds__(256) void attn_mfma_wide_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vt, int64_t Lmax,
+    int64_t L, int M, int nq, int G, int ntiles, float sl2e, float* __restrict__ ws_o, AttnPart* __restrict__ ws_ml) {
+    attn_body<3>(q, Kc, Vt, Lmax, L, M, nq, G, ntiles, sl2e, ws_o, ws_ml);
 }
 
 // Merge the chunk partials of one (kv head, query): grid = (QN, nkv), AHD threads.
@@ -296,7 +445,7 @@ __global__ __launch_bounds__(AHD) void attn_combine_kernel(const float* __restri
         float mx = ap.m;
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-        s_f[d] = (ap.m == -INFINITY) ? 0.0f : expf(ap.m - mx);
+        s_f[d] = (ap.m == -INFINITY) ? 0.0f : exp2f(ap.m - mx);
         s_l[d] = ap.l;
     }
     __syncthreads();
@@ -316,18 +465,18 @@ __global__ __launch_bounds__(AHD) void attn_combine_kernel(const float* __restri
 }
 
 struct AttnPlan {
-    int QN, CP, nparts;
+    int QN, ntiles, nparts;
     size_t off_o, off_ml, total;
 };
 
+// 32-position tiles split evenly over nparts workgroups per KV head: about 8
+// tiles (two per wavefront) per workgroup, at most 64 partials per query.
 static AttnPlan attn_plan(int M, int nq, int nkv, int64_t ctx) {
     AttnPlan p;
     p.QN = (nq / nkv) * M;
-    // chunks of >= 256 positions, at most 64 per KV head
-    int64_t cp = 256;
-    while ((ctx + cp - 1) / cp > 64) cp += 256;
-    p.CP = (int)cp;
-    p.nparts = (int)((ctx + cp - 1) / cp);
+    p.ntiles = (int)((ctx + AT - 1) / AT);
+    int np = (p.ntiles + 7) / 8;
+    p.nparts = np < 1 ? 1 : (np > 64 ? 64 : np);
     size_t o = 0;
     p.off_o = o;
     o += (size_t)nkv * p.QN * p.nparts * AHD * sizeof(float);
@@ -366,16 +515,16 @@ int vw4_add_rmsnorm(uint16_t* resid, const float* part, int32_t S, int64_t ldp, 
 }
 
 int vw4_rope_kv_append(const float* part, int32_t S, int64_t ldp, int32_t M, int32_t nq, int32_t nkv, int32_t hd,
-                       int32_t L, float theta, uint16_t* q_out, uint16_t* Kc, uint16_t* Vc, int64_t Lmax,
+                       int32_t L, float theta, uint16_t* q_out, uint16_t* Kc, uint16_t* Vt, int64_t Lmax,
                        void* stream) {
-    VW4_REQUIRE(part && q_out && Kc && Vc, VW4_EINVAL, "vw4_rope_kv_append: null pointer");
+    VW4_REQUIRE(part && q_out && Kc && Vt, VW4_EINVAL, "vw4_rope_kv_append: null pointer");
     VW4_REQUIRE(M >= 1 && M <= 64 && nq >= 1 && nkv >= 1 && hd >= 2 && hd % 2 == 0 && hd <= 2048, VW4_EINVAL,
                 "vw4_rope_kv_append: bad shape");
     VW4_REQUIRE(S >= 1 && ldp >= (int64_t)(nq + 2 * nkv) * hd, VW4_EINVAL, "vw4_rope_kv_append: bad partial layout");
     VW4_REQUIRE(L >= 0 && (int64_t)L + M <= Lmax, VW4_EINVAL, "vw4_rope_kv_append: L + M exceeds the cache");
     VW4_REQUIRE(theta > 0.0f, VW4_EINVAL, "vw4_rope_kv_append: theta must be > 0");
     hipLaunchKernelGGL(rope_kv_kernel, dim3(nq + 2 * nkv, M), dim3(hd / 2), 0, (hipStream_t)stream, part, S, ldp, M,
-                       nq, nkv, hd, L, (double)theta, q_out, Kc, Vc, Lmax);
+                       nq, nkv, hd, L, (double)theta, q_out, Kc, Vt, Lmax);
     return check_launch("vw4_rope_kv_append");
 }
 
@@ -405,38 +554,39 @@ size_t vw4_attn_workspace_bytes(int32_t M, int32_t nq, int32_t nkv, int32_t hd, 
     return attn_plan(M, nq, nkv, ctx).total;
 }
 
-int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_t* Vc, int64_t Lmax, int64_t L, int32_t M,
+int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_t* Vt, int64_t Lmax, int64_t L, int32_t M,
                     int32_t nq, int32_t nkv, int32_t hd, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
-    VW4_REQUIRE(q && Kc && Vc && out, VW4_EINVAL, "vw4_decode_attn: null pointer");
+    VW4_REQUIRE(q && Kc && Vt && out, VW4_EINVAL, "vw4_decode_attn: null pointer");
     VW4_REQUIRE(hd == AHD, VW4_EUNSUPPORTED, "vw4_decode_attn: head dim %d (only 128 is built)", hd);
     VW4_REQUIRE(M >= 1 && nq >= 1 && nkv >= 1 && nq % nkv == 0, VW4_EINVAL, "vw4_decode_attn: bad head counts");
     const int QN = (nq / nkv) * M;
     VW4_REQUIRE(QN <= AQN, VW4_EUNSUPPORTED, "vw4_decode_attn: (nq/nkv)*M = %d > %d", QN, AQN);
     VW4_REQUIRE(L >= 0 && L + M <= Lmax, VW4_EINVAL, "vw4_decode_attn: L + M exceeds the cache");
-    VW4_REQUIRE(aligned(Kc, 16) && aligned(Vc, 16) && aligned(q, 4), VW4_EINVAL, "vw4_decode_attn: misaligned");
+    VW4_REQUIRE(Lmax % 8 == 0, VW4_EINVAL, "vw4_decode_attn: Lmax must be a multiple of 8");
+    VW4_REQUIRE(aligned(Kc, 16) && aligned(Vt, 16) && aligned(q, 16), VW4_EINVAL, "vw4_decode_attn: misaligned");
     const AttnPlan p = attn_plan(M, nq, nkv, L + M);
     VW4_REQUIRE(ws && ws_bytes >= p.total && aligned(ws, 256), VW4_EWORKSPACE,
                 "vw4_decode_attn: needs a 256-byte aligned workspace of %zu bytes", p.total);
     hipStream_t st = (hipStream_t)stream;
     float* wo = (float*)((char*)ws + p.off_o);
     AttnPart* wml = (AttnPart*)((char*)ws + p.off_ml);
-    const float scale = 1.0f / sqrtf((float)hd);
+    const float sl2e = 1.4426950408889634f / sqrtf((float)hd);
     const int G = nq / nkv;
     const dim3 grid(nkv, p.nparts);
-#define VW4_ATTN(QQ)                                                                                              \
-    case QQ:                                                                                                      \
-        hipLaunchKernelGGL(attn_chunk_kernel<QQ>, grid, dim3(256), 0, st, q, Kc, Vc, Lmax, L, M, nq, G, p.CP, scale, \
-                           wo, wml);                                                                              \
-        break;
-    switch (QN) {
-        VW4_ATTN(1) VW4_ATTN(2) VW4_ATTN(3) VW4_ATTN(4) VW4_ATTN(5) VW4_ATTN(6) VW4_ATTN(8) VW4_ATTN(10)
-        VW4_ATTN(12) VW4_ATTN(15) VW4_ATTN(16) VW4_ATTN(20) VW4_ATTN(24) VW4_ATTN(25) VW4_ATTN(30) VW4_ATTN(32)
-        VW4_ATTN(35) VW4_ATTN(40)
+    switch ((QN + 15) / 16) {
+        case 1:
+            hipLaunchKernelGGL(attn_mfma_kernel<1>, grid, dim3(256), 0, st, q, Kc, Vt, Lmax, L, M, nq, G, p.ntiles,
+                               sl2e, wo, wml);
+            break;
+        case 2:
+            hipLaunchKernelGGL(attn_mfma_kernel<2>, grid, dim3(256), 0, st, q, Kc, Vt, Lmax, L, M, nq, G, p.ntiles,
+                               sl2e, wo, wml);
+            break;
         default:
-            set_error("vw4_decode_attn: G*M = %d has no compiled variant", QN);
-            return VW4_EUNSUPPORTED;
+            hipLaunchKernelGGL(attn_mfma_wide_kernel, grid, dim3(256), 0, st, q, Kc, Vt, Lmax, L, M, nq, G, p.ntiles,
+                               sl2e, wo, wml);
+            break;
     }
-#undef VW4_ATTN
     hipLaunchKernelGGL(attn_combine_kernel, dim3(QN, nkv), dim3(AHD), 0, st, wo, wml, p.nparts, QN, M, nq, G, out);
     return check_launch("vw4_decode_attn");
 }
