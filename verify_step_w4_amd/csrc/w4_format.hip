@@ -8,16 +8,19 @@
 //     c_k   = clamp(rint(w_k / scale), -7, 7)  with the *rounded* scale, half-even
 //     an all-zero (or fp16-underflowing) group gets scale 0 and codes 0.
 //
-// Packed layout (what w4_skinny_gemm streams).  Rows are padded to a multiple
-// of 64 and grouped in tiles of 64 rows; tile t, group g, half c (k/32 within
-// the group) and row l of the tile own 16 bytes at
-//     ((t * G + g) * 2 + c) * 1024 + l * 16,
-// so one wavefront (lane = row) reads 1 KiB of contiguous memory per load.
-// Within those 16 bytes, dword d covers k = 64g + 32c + 8d + j (j = 0..7) with
-// code nibble u = c + 8 at bit 4*(j/2) for even j and bit 16 + 4*(j/2) for
-// odd j: ((word >> 4i) & 0x000F000F) is the pair (k0 + 2i, k0 + 2i + 1), one
-// per 16-bit half, matching a dword of consecutive bf16 activations.
-// Scales: f16 [t][g][64].
+// Packed layout (what w4_skinny_gemm streams), built for the matrix-core
+// GEMM: rows are padded to a multiple of 64 and grouped in tiles of 64 rows;
+// tile t and K-group g own a 2 KiB block at (t * G + g) * 2048 bytes.  Lane
+// l = 16 kq + i (kq, i = 0..3, 0..15) of a wavefront owns 8 dwords of it,
+// dword d = 2 nb + s at byte ((t * G + g) * 2 + d / 4) * 1024 + l * 16 +
+// (d % 4) * 4 (so each of the lane's two 16-byte loads is part of one
+// contiguous 1 KiB wavefront load); that dword holds row t * 64 + 16 nb + i,
+// k = 64 g + 32 s + 8 kq + j (j = 0..7), which is exactly one 8-element
+// operand of v_mfma_f32_16x16x32_bf16 for lane l.  Inside the dword the code
+// nibble u = c + 8 of element j sits at bit 4 * (j / 2) for even j and
+// 16 + 4 * (j / 2) for odd j, so ((dword >> 4i) & 0x000F000F) is the element
+// pair (2i, 2i + 1), one per 16-bit half.
+// Scales: fp16 [t][g][i][nb] (lane l reads its four row scales as 8 bytes).
 #include <math.h>
 #include <stdarg.h>
 
@@ -71,6 +74,20 @@ __host__ __device__ __forceinline__ int packed_nibble_shift(int j) {
     return (j & 1) ? 16 + 4 * (j >> 1) : 4 * (j >> 1);
 }
 
+// Dword index (in the packed codes) holding row n, k = 8 * (k / 8) .. +8.
+__host__ __device__ __forceinline__ int64_t packed_dword(int64_t n, int64_t k, int64_t G) {
+    const int64_t t = n >> 6, g = k >> 6;
+    const int nb = (int)((n >> 4) & 3), i = (int)(n & 15);
+    const int s = (int)((k >> 5) & 1), kq = (int)((k >> 3) & 3);
+    const int lane = kq * 16 + i, d = nb * 2 + s;
+    return ((((t * G + g) * 2 + (d >> 2)) * 1024 + lane * 16) >> 2) + (d & 3);
+}
+
+// Index (in fp16 units) of the scale of row n, group g.
+__host__ __device__ __forceinline__ int64_t packed_scale(int64_t n, int64_t g, int64_t G) {
+    return (((n >> 6) * G + g) * 16 + (n & 15)) * 4 + ((n >> 4) & 3);
+}
+
 __global__ __launch_bounds__(256) void quantize_canonical_kernel(const float* __restrict__ w, int64_t N,
                                                                  int64_t K, uint8_t* __restrict__ codes,
                                                                  uint16_t* __restrict__ scales) {
@@ -107,13 +124,8 @@ __global__ __launch_bounds__(256) void quantize_packed_kernel(const float* __res
     uint32_t word = u;
 #pragma unroll
     for (int off = 1; off < 8; off <<= 1) word |= __shfl_xor(word, off, 64);
-    const int64_t t = n >> 6, l = n & 63;
-    if ((lane & 7) == 0) {
-        const int half = lane >> 5, d = (lane >> 3) & 3;
-        const int64_t off = (((t * G + g) * 2 + half) * 1024 + l * 16) / 4 + d;
-        packed[off] = word;
-    }
-    if (lane == 0) pscales[(t * G + g) * 64 + l] = sb;
+    if ((lane & 7) == 0) packed[packed_dword(n, g * 64 + lane, G)] = word;
+    if (lane == 0) pscales[packed_scale(n, g, G)] = sb;
 }
 
 // One thread per (padded row, group): canonical 32 bytes + scale -> packed.
@@ -124,24 +136,22 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ c
     const int64_t G = K / 64;
     const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (id >= Npad * G) return;
-    const int64_t n = id / G, g = id % G, t = n >> 6, l = n & 63;
+    const int64_t n = id / G, g = id % G;
     const uint8_t* src = codes + n * (K / 2) + g * 32;
-    for (int half = 0; half < 2; ++half) {
-        for (int d = 0; d < 4; ++d) {
-            uint32_t word = 0;
-            for (int j = 0; j < 8; ++j) {
-                const int k = half * 32 + d * 8 + j;  // k within the group
-                uint32_t u = 8;
-                if (n < N) {
-                    const uint8_t b = src[k >> 1];
-                    u = (k & 1) ? (b >> 4) : (b & 15u);
-                }
-                word |= u << packed_nibble_shift(j);
+    for (int o = 0; o < 8; ++o) {          // the 8 runs of 8 k of the group
+        uint32_t word = 0;
+        for (int j = 0; j < 8; ++j) {
+            const int k = o * 8 + j;       // k within the group
+            uint32_t u = 8;
+            if (n < N) {
+                const uint8_t b = src[k >> 1];
+                u = (k & 1) ? (b >> 4) : (b & 15u);
             }
-            packed[(((t * G + g) * 2 + half) * 1024 + l * 16) / 4 + d] = word;
+            word |= u << packed_nibble_shift(j);
         }
+        packed[packed_dword(n, g * 64 + o * 8, G)] = word;
     }
-    pscales[(t * G + g) * 64 + l] = (n < N) ? scales[n * G + g] : (uint16_t)0;
+    pscales[packed_scale(n, g, G)] = (n < N) ? scales[n * G + g] : (uint16_t)0;
 }
 
 __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict__ packed,
@@ -150,19 +160,17 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict_
     const int64_t G = K / 64;
     const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (id >= N * G) return;
-    const int64_t n = id / G, g = id % G, t = n >> 6, l = n & 63;
+    const int64_t n = id / G, g = id % G;
     uint8_t* dst = codes + n * (K / 2) + g * 32;
-    for (int half = 0; half < 2; ++half) {
-        for (int d = 0; d < 4; ++d) {
-            const uint32_t word = packed[(((t * G + g) * 2 + half) * 1024 + l * 16) / 4 + d];
-            for (int jp = 0; jp < 4; ++jp) {
-                const uint32_t lo = (word >> packed_nibble_shift(2 * jp)) & 15u;
-                const uint32_t hi = (word >> packed_nibble_shift(2 * jp + 1)) & 15u;
-                dst[half * 16 + d * 4 + jp] = (uint8_t)(lo | (hi << 4));
-            }
+    for (int o = 0; o < 8; ++o) {
+        const uint32_t word = packed[packed_dword(n, g * 64 + o * 8, G)];
+        for (int jp = 0; jp < 4; ++jp) {
+            const uint32_t lo = (word >> packed_nibble_shift(2 * jp)) & 15u;
+            const uint32_t hi = (word >> packed_nibble_shift(2 * jp + 1)) & 15u;
+            dst[o * 4 + jp] = (uint8_t)(lo | (hi << 4));
         }
     }
-    scales[n * G + g] = pscales[(t * G + g) * 64 + l];
+    scales[n * G + g] = pscales[packed_scale(n, g, G)];
 }
 
 static int check_shape(int64_t N, int64_t K) {

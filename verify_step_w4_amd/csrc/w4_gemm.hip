@@ -7,24 +7,33 @@
 //
 // y[m][n] = sum_g scale[n][g] * sum_{k in g} x[m][k] * c[n][k]
 //
-// MI355X design (bandwidth-bound: each weight byte is used M times at most):
-//  * lane = output row.  A wavefront owns a tile of 64 rows and a slice of the
-//    K groups; each lane streams its row's codes with 16-byte loads, and the
-//    packed layout makes every wavefront load 1 KiB of contiguous HBM.
-//  * The activations x are identical for all 64 lanes, so they are read with
-//    scalar loads into SGPRs and feed v_dot2_f32_bf16 directly: no LDS traffic
-//    and no cross-lane reduction in the inner loop.
-//  * Dequantisation in registers: ((word >> 4i) & 0x000F000F) | 0x43004300 is a
-//    pair of bf16 values 128 + u = 136 + c.  The constant 136 is removed once
-//    per group by starting the group's accumulator at -136 * sum_{k in g} x[m][k]
-//    (computed per workgroup in fp64 and rounded once), so the inner loop is
-//    one AND-OR (plus a shift) per pair and M dot2 per pair.
+// MI355X design.  The op is bound by HBM: every weight byte is read once and
+// used by M <= 8 rows.  On gfx950, though, forming those products on the
+// vector ALU (v_dot2_f32_bf16, 2 MACs per lane-op) plus the dequantisation
+// costs about 24 lane-ops per 4 bytes of weights at M = 4, more than the
+// chip issues at full HBM speed.  So the multiplies go to the matrix cores
+// and the vector ALU only dequantises:
+//  * A wavefront owns a tile of 64 rows and a slice of the K groups.  Per
+//    64-element group, lane l = 16 kq + i loads 32 bytes (two 16-byte loads,
+//    each part of a contiguous 1 KiB wavefront load): the 8 code nibbles of
+//    rows 16 nb + i (nb = 0..3) at k = 32 s + 8 kq .. +8 (s = 0, 1), exactly
+//    its B operand (W^T, column = row of W) of v_mfma_f32_16x16x32_bf16.
+//  * The A operand is the activations: lane l supplies x[i][32 s + 8 kq .. +8]
+//    (for i >= M any valid row: those output rows are not stored), read once
+//    per group from L2.  D[m][n] lands in
+//    lane (kq, i) as rows m = 4 kq .. +4, column n = 16 nb + i.
+//  * Dequantisation in registers: ((word >> 4j) & 0x000F000F) | 0x43004300 is
+//    a pair of bf16 values 128 + u = 136 + c (one v_bitop3 per pair).  The
+//    constant is removed by one more product per group: the C input of the
+//    four row blocks' products is x . (-136), which the matrix cores form from
+//    the same A operand.  Then acc += scale[n] * D, per row.
 //  * Split K: S_wg wavefronts of a workgroup take consecutive K slices of the
 //    same tile and are reduced through LDS; when the tiles are too few to fill
-//    the chip, S_grid workgroups per tile write fp32 partials to the workspace
-//    and a second launch sums them in slice order.  The summation order
-//    depends only on (N, K), never on M or on timing, so results are bitwise
-//    reproducible and row m of an M-row call equals the one-row call.
+//    the chip, S_grid workgroups per tile write fp32 partials and the consumer
+//    (or a second launch) sums them in slice order.  Every summation order
+//    depends only on (N, K): results are bitwise reproducible and row m of an
+//    M-row call equals the one-row call (the matrix core computes each output
+//    from its own row of A).
 #include <stdlib.h>
 
 #include "common.h"
@@ -33,24 +42,10 @@ namespace vw4 {
 
 constexpr int GEMM_MAX_M = 8;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-// Constant address space: uniform loads through it become scalar (SGPR) loads.
-typedef const __attribute__((address_space(4))) uint32_t cu32;
-constexpr float GEMM_OFFSET = 136.0f;  // bf16 magic 128 plus the code bias 8
-constexpr int PF = 4;                  // weight groups in flight per lane
-
-// Marks an address as wavefront-uniform so that loads through it are scalar.
-__device__ __forceinline__ cu32* uniform_ptr(cu32* p) {
-    const uint64_t a = (uint64_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-    return (cu32*)(((uint64_t)hi << 32) | lo);
-}
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c,
-                                           false);
-}
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+constexpr int PF = 4;                  // groups in flight per lane
+constexpr uint32_t NEG136_PAIR = 0xC308C308u;  // two bf16 -136.0
 
 // (v & mask) | magic in one instruction: gfx950's three-input bitwise op with
 // truth table 0xEA = (A & B) | C.  gfx9 VOP3 encodings take no literal
@@ -60,40 +55,42 @@ __device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask_s, uint32_t
     return __builtin_amdgcn_bitop3_b32(v, mask_s, magic_v, 0xEA);
 }
 
-template <int M>
-__device__ __forceinline__ void gemm_dword(uint32_t word, cu32* const* xg, int xoff, uint32_t kmask,
-                                           uint32_t kmagic, float (&ag)[M]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t pair = and_or(word >> (4 * i), kmask, kmagic);
-#pragma unroll
-        for (int m = 0; m < M; ++m) ag[m] = dot2_bf16(pair, xg[m][xoff + i], ag[m]);
-    }
+// 8 code nibbles -> the 8 bf16 values 128 + u of one MFMA operand.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t w, uint32_t kmask, uint32_t magic_v) {
+    u32x4 r;
+    r.x = and_or(w, kmask, magic_v);
+    r.y = and_or(w >> 4, kmask, magic_v);
+    r.z = and_or(w >> 8, kmask, magic_v);
+    r.w = and_or(w >> 12, kmask, magic_v);
+    return __builtin_bit_cast(bf16x8, r);
 }
 
-// One 64-element group of one row per lane: M partial sums started at
-// -136 * sum(x) (xsg[m * ng]), 8 code dwords, then acc += scale * partial.
-// Advances the activation pointers by one group.
-template <int M>
-__device__ __forceinline__ void gemm_group(u32x4 c0, u32x4 c1, uint32_t sbits, cu32** xp, const float* xsg, int ng,
-                                           uint32_t kmask, uint32_t magic_v, float (&acc)[M]) {
-    float ag[M];
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One K-group of one tile: wa / wb = the lane's two 16-byte code loads (row
+// blocks 0, 1 and 2, 3), xa / xb = its activations for k halves 0 / 1, sc =
+// its four row scales (fp16 pairs).
+__device__ __forceinline__ void gemm_group(u32x4 wa, u32x4 wb, u32x4 xa, u32x4 xb, uint2 sc, uint32_t kmask,
+                                           uint32_t magic_v, f32x4 (&acc)[4]) {
+    const bf16x8 a0 = __builtin_bit_cast(bf16x8, xa), a1 = __builtin_bit_cast(bf16x8, xb);
+    const u32x4 nq = {NEG136_PAIR, NEG136_PAIR, NEG136_PAIR, NEG136_PAIR};
+    const bf16x8 neg = __builtin_bit_cast(bf16x8, nq);
+    f32x4 off = {0.f, 0.f, 0.f, 0.f};
+    off = mfma16(a0, neg, off);
+    off = mfma16(a1, neg, off);
+    f32x4 d[4];
+    d[0] = mfma16(a1, dequant8(wa.y, kmask, magic_v), mfma16(a0, dequant8(wa.x, kmask, magic_v), off));
+    d[1] = mfma16(a1, dequant8(wa.w, kmask, magic_v), mfma16(a0, dequant8(wa.z, kmask, magic_v), off));
+    d[2] = mfma16(a1, dequant8(wb.y, kmask, magic_v), mfma16(a0, dequant8(wb.x, kmask, magic_v), off));
+    d[3] = mfma16(a1, dequant8(wb.w, kmask, magic_v), mfma16(a0, dequant8(wb.z, kmask, magic_v), off));
+    const float f[4] = {f16_bits_to_f32((uint16_t)(sc.x & 0xffffu)), f16_bits_to_f32((uint16_t)(sc.x >> 16)),
+                        f16_bits_to_f32((uint16_t)(sc.y & 0xffffu)), f16_bits_to_f32((uint16_t)(sc.y >> 16))};
 #pragma unroll
-    for (int m = 0; m < M; ++m) ag[m] = xsg[m * ng];
-    gemm_dword<M>(c0.x, xp, 0, kmask, magic_v, ag);
-    gemm_dword<M>(c0.y, xp, 4, kmask, magic_v, ag);
-    gemm_dword<M>(c0.z, xp, 8, kmask, magic_v, ag);
-    gemm_dword<M>(c0.w, xp, 12, kmask, magic_v, ag);
-    gemm_dword<M>(c1.x, xp, 16, kmask, magic_v, ag);
-    gemm_dword<M>(c1.y, xp, 20, kmask, magic_v, ag);
-    gemm_dword<M>(c1.z, xp, 24, kmask, magic_v, ag);
-    gemm_dword<M>(c1.w, xp, 28, kmask, magic_v, ag);
-    const float sc = f16_bits_to_f32((uint16_t)sbits);
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-        acc[m] = fmaf(sc, ag[m], acc[m]);
-        xp[m] += 32;
-    }
+        for (int r = 0; r < 4; ++r) acc[nb][r] = fmaf(f[nb], d[nb][r], acc[nb][r]);
 }
 
 // Grouped (mixture-of-experts) launches: blockIdx.z is a slot; slots at or
@@ -109,14 +106,13 @@ struct GemmGroup {
     int64_t p_sstride;        // floats
 };
 
-template <int M>
 __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                       const u32x4* __restrict__ wpk,
                                                       const uint16_t* __restrict__ spk, void* __restrict__ y,
-                                                      int64_t ldy, int ydt, int N, int G, int S_wg, int S_grid,
-                                                      float* __restrict__ part, int64_t Npad, uint32_t kmask,
-                                                      uint32_t kmagic, GemmGroup grp) {
-    extern __shared__ float lds[];
+                                                      int64_t ldy, int ydt, int M, int N, int G, int S_wg,
+                                                      int S_grid, float* __restrict__ part, int64_t Npad,
+                                                      uint32_t kmask, uint32_t kmagic, GemmGroup grp) {
+    __shared__ float red[4][16][64];     // [wavefront][4 nb + r][lane]
     if (grp.n_slots) {
         const int slot = blockIdx.z;
         if (slot >= __builtin_amdgcn_readfirstlane(*grp.n_slots)) return;
@@ -129,121 +125,102 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
     }
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63;
+    const int lane = tid & 63, kq = lane >> 4, i = lane & 15;
     const int t = blockIdx.x;
     const int S = S_wg * S_grid;
-    const int sw0 = blockIdx.y * S_wg;
-    const int gw0 = (int)((int64_t)sw0 * G / S);
-    const int gw1 = (int)((int64_t)(sw0 + S_wg) * G / S);
-    const int ng = gw1 - gw0;
-    float* xs = lds;                     // [M][ng]: -136 * sum of the group's x
-    float* red = lds + M * ng;           // [S_wg][M][64]
-
-    // Prologue: group sums of x for every group this workgroup touches.
-    for (int i = tid; i < M * ng; i += blockDim.x) {
-        const int m = i / ng, gg = i - m * ng;
-        const uint4* xr = (const uint4*)(x + m * ldx + (int64_t)(gw0 + gg) * 64);
-        double s = 0.0;
-#pragma unroll 1
-        for (int v = 0; v < 8; ++v) {
-            const uint4 q = xr[v];
-            const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                s += (double)bf16_to_f32((uint16_t)(w4[e] & 0xffffu));
-                s += (double)bf16_to_f32((uint16_t)(w4[e] >> 16));
-            }
-        }
-        xs[m * ng + gg] = (float)(-(double)GEMM_OFFSET * s);
-    }
-    __syncthreads();
-
-    const int s_idx = sw0 + wv;
+    const int s_idx = blockIdx.y * S_wg + wv;
     const int g0 = (int)((int64_t)s_idx * G / S);
     const int g1 = (int)((int64_t)(s_idx + 1) * G / S);
-
-    // Activation rows of the current group, advanced by one group (32 dwords)
-    // per iteration; kept wavefront-uniform so every x load is an s_load.
-    cu32* xp[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) xp[m] = uniform_ptr((cu32*)(x + m * ldx) + g0 * 32);
     const uint32_t magic_v = kmagic;  // lives in a VGPR for and_or()
 
-    float acc[M];
+    // per-lane streams, advanced by one group per step
+    const u32x4* wbase = wpk + (int64_t)t * G * 128 + lane;                  // + g * 128 (+ 64: second half)
+    const uint2* sbase = (const uint2*)spk + (int64_t)t * G * 16 + i;         // + g * 16
+    // A rows i >= M only feed output rows that are never stored (each output
+    // row depends on its own A row alone), so those lanes re-read a valid row
+    // instead of branching around the load
+    const u32x4* xbase = (const u32x4*)(x + (int64_t)(i < M ? i : M - 1) * ldx) + kq;   // + g * 8 (+ 4: k half 1)
+
+    f32x4 acc[4];
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] = 0.0f;
+    for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // PF groups in flight per lane, each in its own registers: the main loop
-    // consumes buffer i and refills it with the group PF further on (clamped to
+    // consumes buffer j and refills it with the group PF further on (clamped to
     // the slice's last group, so every load address is valid and the loop body
     // has no branches); the last < PF groups are consumed after the loop.
-    const u32x4* wbase = wpk + (int64_t)t * G * 128 + lane;
-    const uint16_t* sbase = spk + (int64_t)t * G * 64 + lane;
     const int glast = g1 - 1;
     if (g0 < g1) {
-        u32x4 b0[PF], b1[PF];
-        uint32_t bs[PF];  // fp16 scale bits, one register each (packing two would force early waits)
+        u32x4 bw0[PF], bw1[PF], bx0[PF], bx1[PF];
+        uint2 bs[PF];
 #pragma unroll
-        for (int i = 0; i < PF; ++i) {
-            const int gi = min(g0 + i, glast);
-            b0[i] = __builtin_nontemporal_load(wbase + (int64_t)gi * 128);
-            b1[i] = __builtin_nontemporal_load(wbase + (int64_t)gi * 128 + 64);
-            bs[i] = sbase[(int64_t)gi * 64];
+        for (int j = 0; j < PF; ++j) {
+            const int gi = min(g0 + j, glast);
+            bw0[j] = __builtin_nontemporal_load(wbase + (int64_t)gi * 128);
+            bw1[j] = __builtin_nontemporal_load(wbase + (int64_t)gi * 128 + 64);
+            bx0[j] = xbase[(int64_t)gi * 8];
+            bx1[j] = xbase[(int64_t)gi * 8 + 4];
+            bs[j] = sbase[(int64_t)gi * 16];
         }
         int g = g0;
         for (; g + PF <= g1; g += PF) {
 #pragma unroll
-            for (int i = 0; i < PF; ++i) {
-                gemm_group<M>(b0[i], b1[i], bs[i], xp, xs + (g + i - gw0), ng, kmask, magic_v, acc);
-                const int gn = min(g + i + PF, glast);
+            for (int j = 0; j < PF; ++j) {
+                gemm_group(bw0[j], bw1[j], bx0[j], bx1[j], bs[j], kmask, magic_v, acc);
+                const int gn = min(g + j + PF, glast);
                 // keep the refill right after its buffer's last use: the
                 // scheduler would otherwise sink all refills to the loop end
                 __builtin_amdgcn_sched_barrier(0);
-                b0[i] = __builtin_nontemporal_load(wbase + (int64_t)gn * 128);
-                b1[i] = __builtin_nontemporal_load(wbase + (int64_t)gn * 128 + 64);
-                bs[i] = sbase[(int64_t)gn * 64];
+                bw0[j] = __builtin_nontemporal_load(wbase + (int64_t)gn * 128);
+                bw1[j] = __builtin_nontemporal_load(wbase + (int64_t)gn * 128 + 64);
+                bx0[j] = xbase[(int64_t)gn * 8];
+                bx1[j] = xbase[(int64_t)gn * 8 + 4];
+                bs[j] = sbase[(int64_t)gn * 16];
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
-        for (int i = 0; i < PF - 1; ++i)
-            if (g + i < g1) gemm_group<M>(b0[i], b1[i], bs[i], xp, xs + (g + i - gw0), ng, kmask, magic_v, acc);
+        for (int j = 0; j < PF - 1; ++j)
+            if (g + j < g1) gemm_group(bw0[j], bw1[j], bx0[j], bx1[j], bs[j], kmask, magic_v, acc);
     }
 
     // Reduce the S_wg slices of this workgroup in slice order.
-    float v[M];
     if (S_wg > 1) {
 #pragma unroll
-        for (int m = 0; m < M; ++m) red[(wv * M + m) * 64 + lane] = acc[m];
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wv][nb * 4 + r][lane] = acc[nb][r];
         __syncthreads();
-        if (wv == 0) {
+        if (wv != 0) return;
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                float s = red[m * 64 + lane];
-                for (int w = 1; w < S_wg; ++w) s += red[(w * M + m) * 64 + lane];
-                v[m] = s;
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = red[0][nb * 4 + r][lane];
+                for (int w = 1; w < S_wg; ++w) v += red[w][nb * 4 + r][lane];
+                acc[nb][r] = v;
             }
-        }
-    } else {
-#pragma unroll
-        for (int m = 0; m < M; ++m) v[m] = acc[m];
     }
 
-    const int n = t * 64 + lane;
-    if (wv != 0) return;
-    if (S_grid == 1) {
-        if (n < N) {
+    // lane (kq, i) holds rows m = 4 kq + r of columns n = 64 t + 16 nb + i
 #pragma unroll
-            for (int m = 0; m < M; ++m) {
-                if (ydt == VW4_F32) ((float*)y)[m * ldy + n] = v[m];
-                else ((uint16_t*)y)[m * ldy + n] = f32_to_bf16(v[m]);
+    for (int r = 0; r < 4; ++r) {
+        const int m = 4 * kq + r;
+        if (m >= M) break;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int n = t * 64 + nb * 16 + i;
+            if (S_grid == 1) {
+                if (n < N) {
+                    if (ydt == VW4_F32) ((float*)y)[m * ldy + n] = acc[nb][r];
+                    else ((uint16_t*)y)[m * ldy + n] = f32_to_bf16(acc[nb][r]);
+                }
+            } else {
+                // split across workgroups: fp32 partials, summed by the consumer
+                part[((int64_t)blockIdx.y * M + m) * Npad + n] = acc[nb][r];
             }
         }
-        return;
     }
-    // Split across workgroups: fp32 partials; w4_gemm_reduce_kernel sums them.
-#pragma unroll
-    for (int m = 0; m < M; ++m) part[((int64_t)blockIdx.y * M + m) * Npad + n] = v[m];
 }
 
 // Sum of the S_grid partials of each output in slice order (a separate launch:
@@ -271,26 +248,30 @@ struct GemmPlan {
     int ntiles, G, S_wg, S_grid;
     int64_t Npad;
     size_t ws_bytes;
-    size_t lds_bytes;
 };
 
-// Split of K over wavefronts: enough wavefronts to cover the 256 CUs several
-// times, at least two groups per wavefront.  Depends on (N, K) only.
-// slots: matrices per launch (grouped launches spread the wave target over
-// all of them).
+// Split of K over wavefronts: about 2048 wavefronts (two per SIMD), at least
+// four groups per wavefront and at most 16 partial slices; one wavefront per
+// workgroup, except that very wide matrices (one slice) pair two wavefronts
+// per tile through LDS.  Measured on MI355X over the 27B-class shapes: more
+// wavefronts only add per-wavefront start-up and partial traffic.  Depends on
+// (N, K) only.  slots: matrices per launch (grouped launches spread the
+// wavefront target over all of them).
 static GemmPlan plan_gemm(int M, int N, int K, int slots = 1) {
     GemmPlan p;
     p.G = K / 64;
     p.ntiles = (N + 63) / 64;
     p.Npad = (int64_t)p.ntiles * 64;
-    const int target_waves = 8192;
+    const int target_waves = 2048;
     const int units = p.ntiles * slots;
     int S = (target_waves + units - 1) / units;
-    int maxS = p.G / 2 > 0 ? p.G / 2 : 1;
+    int maxS = p.G / 4 < 16 ? p.G / 4 : 16;
+    if (maxS < 1) maxS = 1;
     if (S > maxS) S = maxS;
     if (S < 1) S = 1;
-    p.S_wg = S < 4 ? S : 4;
-    p.S_grid = (S + p.S_wg - 1) / p.S_wg;
+    p.S_wg = 1;
+    p.S_grid = S;
+    if (S == 1 && units >= 1024 && p.G >= 8) p.S_wg = 2;
     if (const char* e = getenv("VW4_GEMM_SPLIT")) {
         int a = 0, b = 0;
         if (sscanf(e, "%d,%d", &a, &b) == 2 && a >= 1 && a <= 4 && b >= 1 && a * b <= p.G) {
@@ -298,20 +279,15 @@ static GemmPlan plan_gemm(int M, int N, int K, int slots = 1) {
             p.S_grid = b;
         }
     }
-    const int S_all = p.S_wg * p.S_grid;
-    const int ng_max = (int)(((int64_t)p.S_wg * p.G + S_all - 1) / S_all) + 1;
-    p.lds_bytes = (size_t)M * ng_max * 4 + (p.S_wg > 1 ? (size_t)p.S_wg * M * 64 * 4 : 0);
     p.ws_bytes = 0;
     if (p.S_grid > 1) p.ws_bytes = ((size_t)p.S_grid * M * p.Npad * 4 + 255) / 256 * 256;
     return p;
 }
 
-template <int M>
 static void launch_gemm(const GemmPlan& p, const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* s,
-                        void* y, int64_t ldy, int ydt, int N, float* part, hipStream_t st) {
-    hipLaunchKernelGGL(w4_gemm_kernel<M>, dim3(p.ntiles, p.S_grid), dim3(64 * p.S_wg), p.lds_bytes, st, x, ldx,
-                       (const u32x4*)w, s, y, ldy, ydt, N, p.G, p.S_wg, p.S_grid, part, p.Npad, 0x000F000Fu,
-                       0x43004300u, GemmGroup{});
+                        void* y, int64_t ldy, int ydt, int M, int N, float* part, hipStream_t st) {
+    hipLaunchKernelGGL(w4_gemm_kernel, dim3(p.ntiles, p.S_grid), dim3(64 * p.S_wg), 0, st, x, ldx, (const u32x4*)w, s,
+                       y, ldy, ydt, M, N, p.G, p.S_wg, p.S_grid, part, p.Npad, 0x000F000Fu, 0x43004300u, GemmGroup{});
     if (p.S_grid > 1)
         hipLaunchKernelGGL(w4_gemm_reduce_kernel, dim3(p.ntiles, M), dim3(64), 0, st, part, p.S_grid, M, p.Npad, N,
                            y, ldy, ydt);
@@ -326,7 +302,8 @@ int gemm_dispatch(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16
     VW4_REQUIRE(x && w && s && y, VW4_EINVAL, "w4_skinny_gemm: null pointer");
     VW4_REQUIRE(ldx >= K && ldx % 8 == 0 && aligned(x, 16), VW4_EINVAL,
                 "w4_skinny_gemm: x needs ldx >= K, ldx %% 8 == 0 and 16-byte alignment");
-    VW4_REQUIRE(aligned(w, 16) && aligned(s, 2), VW4_EINVAL, "w4_skinny_gemm: packed weights must be 16-byte aligned");
+    VW4_REQUIRE(aligned(w, 16) && aligned(s, 8), VW4_EINVAL,
+                "w4_skinny_gemm: packed codes must be 16-byte and packed scales 8-byte aligned");
     VW4_REQUIRE(ldy >= N, VW4_EINVAL, "w4_skinny_gemm: ldy=%lld < N=%d", (long long)ldy, N);
     VW4_REQUIRE(ydt == VW4_F32 || ydt == VW4_BF16, VW4_EINVAL, "w4_skinny_gemm: y_dtype must be VW4_F32 or VW4_BF16");
     VW4_REQUIRE(aligned(y, ydt == VW4_F32 ? 4 : 2), VW4_EINVAL, "w4_skinny_gemm: y misaligned");
@@ -337,16 +314,7 @@ int gemm_dispatch(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16
                     "w4_skinny_gemm: needs a 256-byte aligned workspace of %zu bytes", p.ws_bytes);
         part = (float*)ws;
     }
-    switch (M) {
-        case 1: launch_gemm<1>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
-        case 2: launch_gemm<2>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
-        case 3: launch_gemm<3>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
-        case 4: launch_gemm<4>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
-        case 5: launch_gemm<5>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
-        case 6: launch_gemm<6>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
-        case 7: launch_gemm<7>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
-        default: launch_gemm<8>(p, x, ldx, w, s, y, ldy, ydt, N, part, st); break;
-    }
+    launch_gemm(p, x, ldx, w, s, y, ldy, ydt, M, N, part, st);
     return check_launch("w4_skinny_gemm");
 }
 
@@ -361,23 +329,16 @@ int gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16
     VW4_REQUIRE(x && w && s && part, VW4_EINVAL, "w4_skinny_gemm_partials: null pointer");
     VW4_REQUIRE(ldx >= K && ldx % 8 == 0 && aligned(x, 16), VW4_EINVAL,
                 "w4_skinny_gemm_partials: x needs ldx >= K, ldx %% 8 == 0 and 16-byte alignment");
-    VW4_REQUIRE(aligned(w, 16) && aligned(s, 2) && aligned(part, 4), VW4_EINVAL,
+    VW4_REQUIRE(aligned(w, 16) && aligned(s, 8) && aligned(part, 4), VW4_EINVAL,
                 "w4_skinny_gemm_partials: misaligned pointer");
     const GemmPlan p = plan_gemm(M, N, K, max_slots);
     // S_grid == 1 writes the product straight into part[0] with row stride Npad
     void* y = part;
     const int64_t ldy = p.Npad;
     float* pp = part;
-    switch (M) {
-#define VW4_CASE(MM)                                                                                               \
-    case MM:                                                                                                       \
-        hipLaunchKernelGGL(w4_gemm_kernel<MM>, dim3(p.ntiles, p.S_grid, max_slots), dim3(64 * p.S_wg), p.lds_bytes, st, x, ldx, \
-                           (const u32x4*)w, s, y, ldy, VW4_F32, N, p.G, p.S_wg, p.S_grid, pp, p.Npad, 0x000F000Fu,   \
-                           0x43004300u, grp);                                                                      \
-        break;
-        VW4_CASE(1) VW4_CASE(2) VW4_CASE(3) VW4_CASE(4) VW4_CASE(5) VW4_CASE(6) VW4_CASE(7) VW4_CASE(8)
-#undef VW4_CASE
-    }
+    hipLaunchKernelGGL(w4_gemm_kernel, dim3(p.ntiles, p.S_grid, max_slots), dim3(64 * p.S_wg), 0, st, x, ldx,
+                       (const u32x4*)w, s, y, ldy, VW4_F32, M, N, p.G, p.S_wg, p.S_grid, pp, p.Npad, 0x000F000Fu,
+                       0x43004300u, grp);
     return check_launch("w4_skinny_gemm_partials");
 }
 
@@ -387,8 +348,8 @@ int grouped_gemm_partials(const uint16_t* x, int64_t ldx, int64_t x_sstride, con
                           hipStream_t st) {
     VW4_REQUIRE(slot_expert && n_slots && max_slots >= 1 && max_slots <= 65535, VW4_EINVAL,
                 "w4_grouped_gemm: bad slot arguments");
-    VW4_REQUIRE(w_estride_bytes % 16 == 0 && w_estride_bytes > 0 && s_estride > 0, VW4_EINVAL,
-                "w4_grouped_gemm: expert strides must be positive, weights 16-byte multiples");
+    VW4_REQUIRE(w_estride_bytes % 16 == 0 && w_estride_bytes > 0 && s_estride > 0 && s_estride % 4 == 0, VW4_EINVAL,
+                "w4_grouped_gemm: expert strides must be positive, weights 16-byte and scales 8-byte multiples");
     VW4_REQUIRE(x_sstride % 8 == 0 && x_sstride >= 0 && p_sstride >= 0, VW4_EINVAL,
                 "w4_grouped_gemm: bad slot strides");
     GemmGroup g;
