@@ -329,7 +329,7 @@ def verify27b_workload(args):
     linears = {}
     for nm in by_name:
         N, Kd = shapes[nm]
-        b = N * Kd * BYTES_PER_WEIGHT + M * Kd * 2 + M * N * 4
+        b = N * Kd * BYTES_PER_WEIGHT + M * Kd * 2 + (M * (N // 2) * 2 if nm == "gate_up" else M * N * 4)
         us = time_graphs([lambda nm=nm: dec.gemm_pass(M, names=(nm,))], 20 if nm != "lm_head" else 200)[0] * 1e3
         linears[nm] = {"N": N, "K": Kd, "avg_us": round(us, 2), "GBs": round(b / (us * 1e-6) / 1e9, 1),
                        "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -455,7 +455,7 @@ def moe_workload(args):
     nsl = nsl_eager.cpu().numpy().astype(np.float64)
     eb_gu = 2 * F * d * BYTES_PER_WEIGHT
     eb_dn = d * F * BYTES_PER_WEIGHT
-    gu_bytes = nsl * eb_gu + M * d * 2 + nsl * M * 2 * F * 4
+    gu_bytes = nsl * eb_gu + M * d * 2 + nsl * M * F * 2
     dn_bytes = nsl * eb_dn + nsl * M * F * 2 + nsl * M * d * 4
     lm_bytes = V * d * BYTES_PER_WEIGHT + M * d * 2 + M * V * 4
     grouped = float((gu_bytes + dn_bytes).sum() / ((t_us["gate_up"] + t_us["down"]).sum() * 1e-6) / 1e9)
@@ -509,7 +509,7 @@ def moe_workload(args):
     # last routing, captured as graphs and replayed in turn
     ms_launch, n_launch = time_graphs([(lambda k=k: mvs[k].gemm_pass(banks[k])) for k in range(nrot)], 50)
     ns_last = np.array([int(mv.n_slots.item()) for mv in mvs], dtype=np.float64)
-    pass_bytes = float((ns_last * (eb_gu + eb_dn + M * 2 * F * 4 + M * F * 2 + M * d * 4)).sum()
+    pass_bytes = float((ns_last * (eb_gu + eb_dn + M * F * 2 + M * F * 2 + M * d * 4)).sum()
                        + nrot * (M * d * 2 + lm_bytes))
     per_launch_bytes = pass_bytes / n_launch
     achieved = per_launch_bytes / (ms_launch * 1e-3) / 1e9

@@ -226,6 +226,41 @@ VW4_API size_t vw4_norm_workspace_bytes(int32_t M, int32_t D);
 VW4_API int vw4_add_rmsnorm(uint16_t* resid, const float* part, int32_t S, int64_t ldp, const uint16_t* gamma,
                             float eps, int32_t M, int32_t D, uint16_t* h, void* ws, size_t ws_bytes, void* stream);
 
+/* The first half of vw4_add_rmsnorm alone: resid += sum_s part (bf16), and the
+ * per-chunk sums of squares of the rounded rows into ws ([M][ceil(D / 256)]
+ * floats, chunk order), for a GEMM that normalises its own activations. */
+VW4_API int vw4_add_sumsq(uint16_t* resid, const float* part, int32_t S, int64_t ldp, int32_t M, int32_t D,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* w4_skinny_gemm_partials with the RMSNorm folded into the activation load
+ * (gist.science BaseRT summary, "メソドロジー": operator sequences fused so
+ * that short kernels do not pay an extra round trip): the activations are
+ * h = bf16(resid / sqrt(mean(resid^2) + eps) * gamma), computed per
+ * workgroup from resid [M][K] bf16, gamma [K] bf16 and the sums of squares
+ * vw4_add_sumsq left in norm_ws; h is bitwise what vw4_add_rmsnorm writes.
+ * Partials layout as vw4_gemm_partials_layout(M, N, K). */
+VW4_API int w4_skinny_gemm_rmsnorm_partials(const uint16_t* resid, const uint16_t* gamma, const void* norm_ws,
+                                            float eps, const uint8_t* w_packed, const uint16_t* scales_packed,
+                                            float* part, int32_t M, int32_t N, int32_t K, void* stream);
+
+/* Gate|up projection with the SwiGLU in its epilogue, on given bf16
+ * activations x [M][K] (row stride ldx): a[m][f] = bf16(silu(g) * u), the
+ * matrix packed gate/up-interleaved as for w4_skinny_gemm_rmsnorm_swiglu. */
+VW4_API int w4_skinny_gemm_swiglu(const uint16_t* x, int64_t ldx, const uint8_t* w_packed,
+                                  const uint16_t* scales_packed, uint16_t* a, int64_t lda, int32_t M, int32_t F,
+                                  int32_t K, void* stream);
+
+/* Fused gate|up projection with the SwiGLU in its epilogue:
+ * a[m][f] = bf16(silu(g) * u) (row stride lda >= F), g and u being rows of
+ * one W4 matrix of 2F rows packed in gate/up-interleaved order: rows
+ * 64 t .. 64 t + 31 are the gate rows of features 32 t .. 32 t + 31 and rows
+ * 64 t + 32 .. 64 t + 63 the up rows of the same features (F % 32 == 0).
+ * The activations are normalised as in w4_skinny_gemm_rmsnorm_partials (each
+ * workgroup covers all of K here, so this pays off for small K only). */
+VW4_API int w4_skinny_gemm_rmsnorm_swiglu(const uint16_t* resid, const uint16_t* gamma, const void* norm_ws,
+                                          float eps, const uint8_t* w_packed, const uint16_t* scales_packed,
+                                          uint16_t* a, int64_t lda, int32_t M, int32_t F, int32_t K, void* stream);
+
 /* From the fused q|k|v projection (partials of [M][(nq + 2 nkv) * hd]): rotary
  * embedding (rotate-half, base theta, position L + m) of q and k; q -> q_out
  * [M][nq][hd]; k appended to the key cache Kc [nkv][Lmax][hd] and v to the
@@ -289,6 +324,16 @@ VW4_API int w4_grouped_gemm(const uint16_t* x, int64_t ldx, int64_t x_sstride, c
                             int64_t w_estride, const uint16_t* s_bank, int64_t s_estride, const int32_t* slot_expert,
                             const int32_t* n_slots, int32_t max_slots, float* part, int64_t p_sstride, int32_t M,
                             int32_t N, int32_t K, void* stream);
+
+/* Grouped gate|up projection with the SwiGLU in its epilogue: for every
+ * slot s < *n_slots, a + s * a_sstride ([M][F] bf16) = bf16(silu(g) * u) of
+ * expert slot_expert[s], whose [2F][K] matrix is packed gate/up-interleaved
+ * as for w4_skinny_gemm_rmsnorm_swiglu; x, strides and banks as
+ * w4_grouped_gemm. */
+VW4_API int w4_grouped_gemm_swiglu(const uint16_t* x, int64_t ldx, int64_t x_sstride, const uint8_t* w_bank,
+                                   int64_t w_estride, const uint16_t* s_bank, int64_t s_estride,
+                                   const int32_t* slot_expert, const int32_t* n_slots, int32_t max_slots, uint16_t* a,
+                                   int64_t a_sstride, int32_t M, int32_t F, int32_t K, void* stream);
 
 /* vw4_swiglu per slot: slot s < *n_slots reads partials at
  * part + s * p_sstride and writes a + s * a_sstride ([M][F] bf16). */

@@ -44,8 +44,15 @@ def _host_model(cfg, seed):
 def _device_weights(hm):
     layers = []
     for l in hm["layers"]:
-        layers.append({k: (W4Linear.from_fp32(dev(l[k])) if k not in ("g1", "g2") else dev(l[k]))
-                       for k in l})
+        d = {}
+        for k, v in l.items():
+            if k in ("g1", "g2"):
+                d[k] = dev(v)
+            elif k == "gate_up":   # the fused SwiGLU GEMM takes gate/up-interleaved rows
+                d[k] = W4Linear.from_fp32(dev(B.interleave_gate_up(v)))
+            else:
+                d[k] = W4Linear.from_fp32(dev(v))
+        layers.append(d)
     return dict(layers=layers, final_gamma=dev(hm["final_gamma"]), lm_head=W4Linear.from_fp32(dev(hm["lm_head"])))
 
 

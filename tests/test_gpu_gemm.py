@@ -146,3 +146,96 @@ def test_lm_head_large_vocab_sampled():
     rms = np.sqrt((y.astype(np.float64) ** 2).mean(axis=1, keepdims=True))
     err = np.abs(y[:, cols] - ref) / np.maximum(np.abs(ref), rms)
     assert err.max() <= GEMM_RTOL, err.max()
+
+
+def _rmsnorm_inputs(M, K, seed):
+    resid = synth.activations_bf16(seed, M, K, 2.0)
+    gamma = synth.f32_to_bf16_bits(1.0 + synth.normal_f32(synth.rng(seed + 1), (K,), 0.02))
+    return resid, gamma
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 7168, 5120), (1, 100, 320), (6, 333, 1024), (8, 64, 5120), (3, 5120, 17408)])
+def test_rmsnorm_gemm_equals_norm_then_gemm(M, N, K):
+    """The GEMM that normalises its own activations gives bitwise the partials
+    of vw4_add_rmsnorm followed by the plain GEMM, and those match the oracle."""
+    import torch
+    log(f"rmsnorm gemm M={M} N={N} K={K}")
+    resid, gamma = _rmsnorm_inputs(M, K, N + K)
+    w = _weights(3 * N + K, N, K)
+    packed, pscales = B.w4_quantize_packed(dev(w))
+    S, ldp = B.gemm_partials_layout(M, N, K)
+    rd, gd = dev(resid), dev(gamma)
+    nws = B.workspace(B.norm_workspace_bytes(M, K))
+    h = torch.empty((M, K), dtype=torch.int16, device="cuda")
+    B.add_rmsnorm(rd, None, 1, K, gd, 1e-6, M, K, h, nws)
+    p_ref = torch.empty(S * M * ldp, dtype=torch.float32, device="cuda")
+    B.w4_skinny_gemm_partials(h, packed, pscales, p_ref, M, N, K)
+    nws2 = B.workspace(B.norm_workspace_bytes(M, K))
+    B.add_sumsq(rd, None, 1, K, M, K, nws2)
+    p = torch.empty(S * M * ldp, dtype=torch.float32, device="cuda")
+    B.w4_skinny_gemm_rmsnorm_partials(rd, gd, nws2, 1e-6, packed, pscales, p, M, N, K)
+    torch.cuda.synchronize()
+    # the defined part of the partials (columns past N are padding)
+    assert torch.equal(p.view(S, M, ldp)[:, :, :N], p_ref.view(S, M, ldp)[:, :, :N])
+    hh = host(h)
+    assert np.array_equal(hh, oracle.bf16_round(oracle.rmsnorm(resid, gamma, 1e-6))) or \
+        np.mean(hh == oracle.bf16_round(oracle.rmsnorm(resid, gamma, 1e-6))) > 0.999
+    y = host(p).reshape(S, M, ldp).astype(np.float64).sum(axis=0)[:, :N]
+    oc, os_ = oracle.w4_quantize(w)
+    assert gemm_rel_err(y, oracle.w4_gemm(hh, oc, os_)) <= GEMM_RTOL
+
+
+def _swiglu_ref(h_bits, w_gu, F):
+    """Oracle: gate|up products of h (natural row order), SwiGLU on the unrounded sums, bf16."""
+    oc, os_ = oracle.w4_quantize(w_gu)
+    gu = oracle.w4_gemm(h_bits, oc, os_)
+    return oracle.swiglu(gu[:, :F], gu[:, F:])
+
+
+@pytest.mark.parametrize("M,F,K", [(4, 512, 1024), (1, 96, 320), (6, 2176, 5120), (8, 256, 5120), (4, 17408, 5120)])
+def test_rmsnorm_swiglu_gemm_against_oracle(M, F, K):
+    """Fused gate|up projection of rmsnorm(resid) * gamma with the SwiGLU in the
+    epilogue (gate/up-interleaved weights) against the oracle composition."""
+    import torch
+    from test_gpu_layer import bf16_close
+    log(f"rmsnorm+swiglu gemm M={M} F={F} K={K}")
+    resid, gamma = _rmsnorm_inputs(M, K, F + K)
+    w = _weights(5 * F + K, 2 * F, K)
+    packed, pscales = B.w4_quantize_packed(dev(B.interleave_gate_up(w)))
+    rd, gd = dev(resid), dev(gamma)
+    nws = B.workspace(B.norm_workspace_bytes(M, K))
+    B.add_sumsq(rd, None, 1, K, M, K, nws)
+    a = torch.full((M, F + 8), -1, dtype=torch.int16, device="cuda")
+    B.w4_skinny_gemm_rmsnorm_swiglu(rd, gd, nws, 1e-6, packed, pscales, a, F + 8, M, F, K)
+    torch.cuda.synchronize()
+    ah = host(a)
+    assert (ah[:, F:] == 0xFFFF).all()                  # nothing past F in each row
+    h = oracle.bf16_round(oracle.rmsnorm(resid, gamma, 1e-6))
+    if F * K > 20_000_000:                              # full-size FFN: a sample of features
+        cols = np.unique(np.random.default_rng(F).integers(0, F, 96))
+        wsel = np.ascontiguousarray(np.concatenate([w[cols], w[F + cols]]))
+        ref = _swiglu_ref(h, wsel, len(cols))
+        bf16_close(np.ascontiguousarray(ah[:, cols]), ref, min_exact=0.9)
+    else:
+        bf16_close(np.ascontiguousarray(ah[:, :F]), _swiglu_ref(h, w, F), min_exact=0.9)
+
+
+@pytest.mark.parametrize("M,F,K", [(4, 17408, 5120), (1, 96, 320), (6, 544, 1024)])
+def test_swiglu_gemm_against_oracle(M, F, K):
+    """Gate|up GEMM on given activations with the SwiGLU epilogue."""
+    import torch
+    from test_gpu_layer import bf16_close
+    log(f"swiglu gemm M={M} F={F} K={K}")
+    x = synth.activations_bf16(F + 3, M, K)
+    w = _weights(7 * F + K, 2 * F, K)
+    packed, pscales = B.w4_quantize_packed(dev(B.interleave_gate_up(w)))
+    a = torch.empty((M, F), dtype=torch.int16, device="cuda")
+    B.w4_skinny_gemm_swiglu(dev(x), packed, pscales, a, F, M, F, K)
+    torch.cuda.synchronize()
+    ah = host(a)
+    if F * K > 20_000_000:
+        cols = np.unique(np.random.default_rng(F + 1).integers(0, F, 96))
+        wsel = np.ascontiguousarray(np.concatenate([w[cols], w[F + cols]]))
+        bf16_close(np.ascontiguousarray(ah[:, cols]), _swiglu_ref(x, wsel, len(cols)), min_exact=0.9)
+    else:
+        bf16_close(ah, _swiglu_ref(x, w, F), min_exact=0.9)

@@ -1,6 +1,6 @@
 """GPU parity of the MoE calls (a10) against the oracle: router top-k and
-slot list, grouped W4 GEMM, grouped SwiGLU + down + combine (the whole
-expert layer), and the MoE-shaped verify step.
+slot list, grouped W4 GEMM, grouped gate|up GEMM with the SwiGLU epilogue,
+down + combine (the whole expert layer), and the MoE-shaped verify step.
 
 Routing is integer work and must match bit for bit (experts, slot list);
 the routing weights are fp64 on both sides, stored fp32 (relative 2^-24).
@@ -114,6 +114,32 @@ def test_grouped_gemm_against_oracle(M, N, K, E, slots, max_slots):
     assert np.isnan(P[len(slots):]).all()
 
 
+@pytest.mark.parametrize("M,F,K,E,slots,max_slots", [(4, 768, 2048, 5, [4, 1, 2], 6), (1, 96, 320, 3, [2], 1)])
+def test_grouped_gemm_swiglu_against_oracle(M, F, K, E, slots, max_slots):
+    """Grouped gate|up projection with the SwiGLU in the epilogue: live slots
+    equal the oracle's per-expert composition, the others are not written."""
+    import torch
+    from test_gpu_layer import bf16_close
+    log(f"grouped gemm+swiglu M={M} F={F} K={K} slots={slots}")
+    w = synth.normal_f32(synth.rng(F + K + 1), (E, 2 * F, K), 0.02)
+    wi = np.stack([B.interleave_gate_up(w[e]) for e in range(E)])
+    bank = W4Linear.from_fp32(dev(wi.reshape(E * 2 * F, K)))
+    x = synth.activations_bf16(K + M + 1, M, K)
+    a = torch.full((max_slots, M, F), -1, dtype=torch.int16, device="cuda")
+    se = torch.zeros(max_slots, dtype=torch.int32, device="cuda")
+    se[:len(slots)] = torch.tensor(slots, dtype=torch.int32)
+    ns = torch.tensor([len(slots)], dtype=torch.int32, device="cuda")
+    B.w4_grouped_gemm_swiglu(dev(x), K, 0, bank.packed, 2 * F * K // 2, bank.pscales, 2 * F * K // 64, se, ns,
+                             max_slots, a, M * F, M, F, K)
+    torch.cuda.synchronize()
+    ah = host(a)
+    for s, e in enumerate(slots):
+        oc, os_ = oracle.w4_quantize(w[e])
+        gu = oracle.w4_gemm(x, oc, os_)
+        bf16_close(np.ascontiguousarray(ah[s]), oracle.swiglu(gu[:, :F], gu[:, F:]), min_exact=0.9)
+    assert (ah[len(slots):] == 0xFFFF).all()
+
+
 def _moe_device(cfg, M, gu, dn, lm_w, gamma):
     bank = ExpertBank.from_fp32(dev(gu), dev(dn))
     mv = MoEVerify(cfg, M, W4Linear.from_fp32(dev(lm_w)), dev(gamma))
@@ -200,12 +226,16 @@ def test_moe_full_size_grouped_equals_per_expert_dense():
     a = torch.empty((M, F), dtype=torch.int16, device="cuda")
     out = torch.empty((M, d), dtype=torch.float32, device="cuda")
     ws = B.workspace(max(B.gemm_workspace_bytes(M, d, F), 256))
+    # gate/up-interleaved rows -> columns [gate f | up f] for the unfused SwiGLU
+    inter = B.interleave_gate_up(np.arange(2 * F).reshape(2 * F, 1))[:, 0]
+    natural = torch.as_tensor(np.argsort(inter), device="cuda")
     for e in sorted(set(ex_o.reshape(-1).tolist())):
         S, ldp = B.gemm_partials_layout(M, 2 * F, d)
         part = torch.empty(S * M * ldp, dtype=torch.float32, device="cuda")
         B.w4_skinny_gemm_partials(x, bank.gate_up.packed[e * gus:(e + 1) * gus],
                                   bank.gate_up.pscales[e * gul:(e + 1) * gul], part, M, 2 * F, d)
-        B.swiglu(part, S, ldp, M, F, a)
+        pn = part.view(S, M, ldp)[:, :, :2 * F][:, :, natural].contiguous()
+        B.swiglu(pn, S, 2 * F, M, F, a)
         B.w4_skinny_gemm(a, bank.down.packed[e * dns:(e + 1) * dns], bank.down.pscales[e * dnl:(e + 1) * dnl], out,
                          M, d, F, ws=ws)
         o = host(out).astype(np.float64)

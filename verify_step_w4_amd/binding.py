@@ -66,6 +66,12 @@ SIGNATURES = {
     "vw4_swiglu": (ctypes.c_int, [_P, _I32, _I64, _I32, _I32, _P, _P]),
     "vw4_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I64]),
     "vw4_decode_attn": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "vw4_add_sumsq": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _I32, _P, _SZ, _P]),
+    "w4_skinny_gemm_rmsnorm_partials": (ctypes.c_int, [_P, _P, _P, _F32, _P, _P, _P, _I32, _I32, _I32, _P]),
+    "w4_skinny_gemm_rmsnorm_swiglu": (ctypes.c_int, [_P, _P, _P, _F32, _P, _P, _P, _I64, _I32, _I32, _I32, _P]),
+    "w4_skinny_gemm_swiglu": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I64, _I32, _I32, _I32, _P]),
+    "w4_grouped_gemm_swiglu": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _I32, _P, _I64, _I32,
+                                              _I32, _I32, _P]),
     "vw4_moe_route": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "vw4_grouped_gemm_layout": (ctypes.c_int, [_I32, _I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
                                                ctypes.POINTER(ctypes.c_int64)]),
@@ -358,3 +364,59 @@ def moe_combine(part, S: int, ldp: int, p_sstride: int, row_slot, weights, M: in
     _check("vw4_moe_combine", lib().vw4_moe_combine(_ptr(part), S, ldp, p_sstride, _ptr(row_slot), _ptr(weights), M,
                                                     topk, D, _ptr(y), ldy, _stream(stream)))
     return y
+
+
+def add_sumsq(resid, part, S: int, ldp: int, M: int, D: int, ws, stream=None):
+    _check("vw4_add_sumsq", lib().vw4_add_sumsq(_ptr(resid), _ptr(part), S, ldp, M, D, _ptr(ws), ws.numel(),
+                                                _stream(stream)))
+
+
+def w4_skinny_gemm_rmsnorm_partials(resid, gamma, norm_ws, eps: float, w_packed, scales_packed, part, M: int, N: int,
+                                    K: int, stream=None):
+    _check("w4_skinny_gemm_rmsnorm_partials",
+           lib().w4_skinny_gemm_rmsnorm_partials(_ptr(resid), _ptr(gamma), _ptr(norm_ws), eps, _ptr(w_packed),
+                                                 _ptr(scales_packed), _ptr(part), M, N, K, _stream(stream)))
+    return part
+
+
+def w4_skinny_gemm_rmsnorm_swiglu(resid, gamma, norm_ws, eps: float, w_packed, scales_packed, a, lda: int, M: int,
+                                  F: int, K: int, stream=None):
+    _check("w4_skinny_gemm_rmsnorm_swiglu",
+           lib().w4_skinny_gemm_rmsnorm_swiglu(_ptr(resid), _ptr(gamma), _ptr(norm_ws), eps, _ptr(w_packed),
+                                               _ptr(scales_packed), _ptr(a), lda, M, F, K, _stream(stream)))
+    return a
+
+
+def w4_grouped_gemm_swiglu(x, ldx: int, x_sstride: int, w_bank, w_estride: int, s_bank, s_estride: int, slot_expert,
+                           n_slots, max_slots: int, a, a_sstride: int, M: int, F: int, K: int, stream=None):
+    _check("w4_grouped_gemm_swiglu",
+           lib().w4_grouped_gemm_swiglu(_ptr(x), ldx, x_sstride, _ptr(w_bank), w_estride, _ptr(s_bank), s_estride,
+                                        _ptr(slot_expert), _ptr(n_slots), max_slots, _ptr(a), a_sstride, M, F, K,
+                                        _stream(stream)))
+    return a
+
+
+def interleave_gate_up(w):
+    """[2F][K] gate|up rows (gate rows 0..F-1, up rows F..2F-1; numpy or torch)
+    -> the gate/up-interleaved row order of the fused SwiGLU GEMM: rows
+    64 t .. +32 = gate rows 32 t .. +32, rows 64 t + 32 .. +32 = up rows
+    32 t .. +32."""
+    F = w.shape[0] // 2
+    assert w.shape[0] == 2 * F and F % 32 == 0
+    import numpy as _np
+    order = _np.empty(2 * F, dtype=_np.int64)
+    for t in range(F // 32):
+        order[64 * t:64 * t + 32] = _np.arange(32 * t, 32 * t + 32)
+        order[64 * t + 32:64 * t + 64] = F + _np.arange(32 * t, 32 * t + 32)
+    if isinstance(w, _np.ndarray):
+        return _np.ascontiguousarray(w[order])
+    import torch
+    return w[torch.as_tensor(order, device=w.device)].contiguous()
+
+
+def w4_skinny_gemm_swiglu(x, w_packed, scales_packed, a, lda: int, M: int, F: int, K: int, stream=None,
+                          ldx: int | None = None):
+    ldx = x.stride(0) if ldx is None else ldx
+    _check("w4_skinny_gemm_swiglu", lib().w4_skinny_gemm_swiglu(_ptr(x), ldx, _ptr(w_packed), _ptr(scales_packed),
+                                                                _ptr(a), lda, M, F, K, _stream(stream)))
+    return a

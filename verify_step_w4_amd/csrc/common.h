@@ -69,6 +69,10 @@ __device__ __forceinline__ float key_f32(uint32_t k) {
     return __uint_as_float(u);
 }
 
+// RMSNorm sums of squares are kept per chunk of NORM_CHUNK columns
+// ([M][ceil(D / NORM_CHUNK)] floats, summed in chunk order by every consumer).
+constexpr int NORM_CHUNK = 256;
+
 // Wavefront (64-lane) reductions via cross-lane moves.
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {

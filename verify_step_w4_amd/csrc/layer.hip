@@ -25,7 +25,7 @@ namespace vw4 {
 //      chunk's sum of squares of the rounded residual -> ws[m][chunk]
 //   2. grid (ceil(D / NCOL), M): total (chunk order) -> scale, h = bf16(...)
 // ---------------------------------------------------------------------------
-constexpr int NCOL = 256;   // columns per workgroup (one per thread)
+constexpr int NCOL = NORM_CHUNK;   // columns per workgroup (one per thread)
 constexpr int NMAXCH = 256; // chunks per row at most (D <= 65536)
 
 __global__ __launch_bounds__(NCOL) void add_sumsq_kernel(uint16_t* __restrict__ resid, const float* __restrict__ part,
@@ -512,6 +512,19 @@ int vw4_add_rmsnorm(uint16_t* resid, const float* part, int32_t S, int64_t ldp, 
     hipLaunchKernelGGL(rmsnorm_apply_kernel, dim3(nch, M), dim3(NCOL), 0, st, resid, gamma, eps, D, (const float*)ws,
                        nch, h);
     return check_launch("vw4_add_rmsnorm");
+}
+
+int vw4_add_sumsq(uint16_t* resid, const float* part, int32_t S, int64_t ldp, int32_t M, int32_t D, void* ws,
+                  size_t ws_bytes, void* stream) {
+    VW4_REQUIRE(resid, VW4_EINVAL, "vw4_add_sumsq: null pointer");
+    VW4_REQUIRE(M >= 1 && M <= 64 && D >= 1 && D <= 65536, VW4_EINVAL, "vw4_add_sumsq: bad shape M=%d D=%d", M, D);
+    VW4_REQUIRE(!part || (S >= 1 && ldp >= D), VW4_EINVAL, "vw4_add_sumsq: bad partial layout");
+    const size_t need = vw4_norm_workspace_bytes(M, D);
+    VW4_REQUIRE(ws && ws_bytes >= need, VW4_EWORKSPACE, "vw4_add_sumsq: needs a workspace of %zu bytes", need);
+    const int nch = (D + NCOL - 1) / NCOL;
+    hipLaunchKernelGGL(add_sumsq_kernel, dim3(nch, M), dim3(NCOL), 0, (hipStream_t)stream, resid, part, S, ldp, M, D,
+                       (float*)ws);
+    return check_launch("vw4_add_sumsq");
 }
 
 int vw4_rope_kv_append(const float* part, int32_t S, int64_t ldp, int32_t M, int32_t nq, int32_t nkv, int32_t hd,

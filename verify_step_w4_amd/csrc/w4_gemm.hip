@@ -96,7 +96,8 @@ __device__ __forceinline__ void gemm_group(u32x4 wa, u32x4 wb, u32x4 xa, u32x4 x
 // Grouped (mixture-of-experts) launches: blockIdx.z is a slot; slots at or
 // beyond *n_slots exit at once; slot s multiplies expert slot_expert[s]
 // (weights at w_estride / s_estride per expert) with the activations at
-// x + s * x_sstride into the partials at part + s * p_sstride.
+// x + s * x_sstride into the partials at part + s * p_sstride (SwiGLU
+// epilogue: into y + s * y_sstride).
 struct GemmGroup {
     const int32_t* slot_expert;
     const int32_t* n_slots;   // NULL: plain (single-matrix) launch
@@ -104,15 +105,37 @@ struct GemmGroup {
     int64_t s_estride;        // fp16 units
     int64_t x_sstride;        // bf16 elements
     int64_t p_sstride;        // floats
+    int64_t y_sstride;        // bf16 elements (SwiGLU epilogue)
 };
 
+// RMSNorm folded into the activation load: A = h = bf16(r * inv * gamma), with
+// inv = 1 / sqrt(sum(ssq) / K + eps) from the per-chunk sums of squares of the
+// residual rows (the same arithmetic, in the same order, as the standalone
+// normalisation, so h is bitwise the same).
+struct NormIn {
+    const uint16_t* resid;    // [M][K] bf16
+    const uint16_t* gamma;    // [K] bf16
+    const float* ssq;         // [M][nch]
+    int nch;
+    float eps;
+};
+
+// Modes: NORM = activations are rmsnorm(resid) * gamma, computed per
+// workgroup for its K range into LDS (dynamic shared memory [M][kw]);
+// SWIGLU = the matrix holds gate and up rows interleaved per 64-row tile
+// (rows 64 t .. +32: gate features 32 t .. +32; rows 64 t + 32 .. +32: the up
+// rows of the same features) and the workgroup, which then covers all of K
+// (S_grid == 1), writes y[m][f] = bf16(silu(gate) * up) directly.
+template <bool NORM, bool SWIGLU>
 __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                       const u32x4* __restrict__ wpk,
                                                       const uint16_t* __restrict__ spk, void* __restrict__ y,
                                                       int64_t ldy, int ydt, int M, int N, int G, int S_wg,
                                                       int S_grid, float* __restrict__ part, int64_t Npad,
-                                                      uint32_t kmask, uint32_t kmagic, GemmGroup grp) {
+                                                      uint32_t kmask, uint32_t kmagic, GemmGroup grp, NormIn nrm) {
+    extern __shared__ uint16_t hs[];     // NORM: this workgroup's rows of h, [M][kw]
     __shared__ float red[4][16][64];     // [wavefront][4 nb + r][lane]
+    __shared__ float s_inv[GEMM_MAX_M];
     if (grp.n_slots) {
         const int slot = blockIdx.z;
         if (slot >= __builtin_amdgcn_readfirstlane(*grp.n_slots)) return;
@@ -121,25 +144,25 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
         spk += (int64_t)e * grp.s_estride;
         x += (int64_t)slot * grp.x_sstride;
         part += (int64_t)slot * grp.p_sstride;
-        y = part;
+        y = SWIGLU ? (void*)((uint16_t*)y + (int64_t)slot * grp.y_sstride) : (void*)part;
     }
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, kq = lane >> 4, i = lane & 15;
     const int t = blockIdx.x;
     const int S = S_wg * S_grid;
-    const int s_idx = blockIdx.y * S_wg + wv;
+    const int sw0 = blockIdx.y * S_wg;
+    const int gw0 = (int)((int64_t)sw0 * G / S);
+    const int s_idx = sw0 + wv;
     const int g0 = (int)((int64_t)s_idx * G / S);
     const int g1 = (int)((int64_t)(s_idx + 1) * G / S);
     const uint32_t magic_v = kmagic;  // lives in a VGPR for and_or()
+    const int xr = i < M ? i : M - 1;  // A rows i >= M feed output rows that are never stored
 
     // per-lane streams, advanced by one group per step
     const u32x4* wbase = wpk + (int64_t)t * G * 128 + lane;                  // + g * 128 (+ 64: second half)
     const uint2* sbase = (const uint2*)spk + (int64_t)t * G * 16 + i;         // + g * 16
-    // A rows i >= M only feed output rows that are never stored (each output
-    // row depends on its own A row alone), so those lanes re-read a valid row
-    // instead of branching around the load
-    const u32x4* xbase = (const u32x4*)(x + (int64_t)(i < M ? i : M - 1) * ldx) + kq;   // + g * 8 (+ 4: k half 1)
+    const u32x4* xbase = (const u32x4*)(x + (int64_t)xr * ldx) + kq;          // + g * 8 (+ 4: k half 1)
 
     f32x4 acc[4];
 #pragma unroll
@@ -148,24 +171,102 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
     // PF groups in flight per lane, each in its own registers: the main loop
     // consumes buffer j and refills it with the group PF further on (clamped to
     // the slice's last group, so every load address is valid and the loop body
-    // has no branches); the last < PF groups are consumed after the loop.
-    const int glast = g1 - 1;
+    // has no branches); the last < PF groups are consumed after the loop.  The
+    // first loads are issued before the NORM prologue so they overlap it.
+    const int glast = g1 > g0 ? g1 - 1 : g0;
+    u32x4 bw0[PF], bw1[PF], bx0[PF], bx1[PF];
+    uint2 bs[PF];
     if (g0 < g1) {
-        u32x4 bw0[PF], bw1[PF], bx0[PF], bx1[PF];
-        uint2 bs[PF];
 #pragma unroll
         for (int j = 0; j < PF; ++j) {
             const int gi = min(g0 + j, glast);
             bw0[j] = __builtin_nontemporal_load(wbase + (int64_t)gi * 128);
             bw1[j] = __builtin_nontemporal_load(wbase + (int64_t)gi * 128 + 64);
-            bx0[j] = xbase[(int64_t)gi * 8];
-            bx1[j] = xbase[(int64_t)gi * 8 + 4];
+            if (!NORM) {
+                bx0[j] = xbase[(int64_t)gi * 8];
+                bx1[j] = xbase[(int64_t)gi * 8 + 4];
+            }
             bs[j] = sbase[(int64_t)gi * 16];
         }
+    }
+
+    int kw = 0;
+    if (NORM) {
+        // One round trip: the sums of squares (wavefront 0, one chunk per
+        // lane) and this thread's first column of every row are requested
+        // together; the chunk sums are then added in chunk order.
+        const int gw1 = (int)((int64_t)(sw0 + S_wg) * G / S);
+        kw = (gw1 - gw0) * 64;
+        const int K = G * 64, nv = kw / 8;
+        const int bs_ = blockDim.x;
+        u32x4 gv = {0u, 0u, 0u, 0u}, rv[GEMM_MAX_M];
+        int c = tid;
+        if (c < nv) {
+            const int64_t k = (int64_t)gw0 * 64 + c * 8;
+            gv = *(const u32x4*)(nrm.gamma + k);
+#pragma unroll
+            for (int m = 0; m < GEMM_MAX_M; ++m)
+                if (m < M) rv[m] = *(const u32x4*)(nrm.resid + (int64_t)m * K + k);
+        }
+        if (wv == 0) {
+            float tot[GEMM_MAX_M];
+#pragma unroll
+            for (int m = 0; m < GEMM_MAX_M; ++m) tot[m] = 0.0f;
+            for (int cb = 0; cb < nrm.nch; cb += 64) {
+                float sv[GEMM_MAX_M];
+#pragma unroll
+                for (int m = 0; m < GEMM_MAX_M; ++m)
+                    sv[m] = (m < M && cb + lane < nrm.nch) ? nrm.ssq[(int64_t)m * nrm.nch + cb + lane] : 0.0f;
+                const int ne = nrm.nch - cb < 64 ? nrm.nch - cb : 64;
+                for (int e = 0; e < ne; ++e)
+#pragma unroll
+                    for (int m = 0; m < GEMM_MAX_M; ++m)
+                        tot[m] += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv[m]), e));
+            }
+#pragma unroll
+            for (int m = 0; m < GEMM_MAX_M; ++m)
+                if (lane == 0 && m < M) s_inv[m] = 1.0f / sqrtf(tot[m] / (float)K + nrm.eps);
+        }
+        __syncthreads();
+        for (; c < nv; c += bs_) {
+            const int64_t k = (int64_t)gw0 * 64 + c * 8;
+            if (c != tid) {                          // columns past the first: load now
+                gv = *(const u32x4*)(nrm.gamma + k);
+#pragma unroll
+                for (int m = 0; m < GEMM_MAX_M; ++m)
+                    if (m < M) rv[m] = *(const u32x4*)(nrm.resid + (int64_t)m * K + k);
+            }
+#pragma unroll
+            for (int m = 0; m < GEMM_MAX_M; ++m) {
+                if (m >= M) break;
+                const float inv = s_inv[m];
+                u32x4 hv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t rw = rv[m][e], gw = gv[e];
+                    const uint16_t lo = f32_to_bf16(bf16_to_f32((uint16_t)(rw & 0xffffu)) * inv *
+                                                    bf16_to_f32((uint16_t)(gw & 0xffffu)));
+                    const uint16_t hi = f32_to_bf16(bf16_to_f32((uint16_t)(rw >> 16)) * inv *
+                                                    bf16_to_f32((uint16_t)(gw >> 16)));
+                    hv[e] = (uint32_t)lo | ((uint32_t)hi << 16);
+                }
+                *(u32x4*)(hs + (int64_t)m * kw + c * 8) = hv;
+            }
+        }
+        __syncthreads();
+    }
+    // NORM: lane's activations of group g, k half s, from LDS
+    const u32x4* hrow = (const u32x4*)(hs + (int64_t)xr * kw) + kq;        // + (g - gw0) * 8 (+ 4)
+
+    if (g0 < g1) {
         int g = g0;
         for (; g + PF <= g1; g += PF) {
 #pragma unroll
             for (int j = 0; j < PF; ++j) {
+                if (NORM) {
+                    bx0[j] = hrow[(g + j - gw0) * 8];
+                    bx1[j] = hrow[(g + j - gw0) * 8 + 4];
+                }
                 gemm_group(bw0[j], bw1[j], bx0[j], bx1[j], bs[j], kmask, magic_v, acc);
                 const int gn = min(g + j + PF, glast);
                 // keep the refill right after its buffer's last use: the
@@ -173,15 +274,23 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
                 __builtin_amdgcn_sched_barrier(0);
                 bw0[j] = __builtin_nontemporal_load(wbase + (int64_t)gn * 128);
                 bw1[j] = __builtin_nontemporal_load(wbase + (int64_t)gn * 128 + 64);
-                bx0[j] = xbase[(int64_t)gn * 8];
-                bx1[j] = xbase[(int64_t)gn * 8 + 4];
+                if (!NORM) {
+                    bx0[j] = xbase[(int64_t)gn * 8];
+                    bx1[j] = xbase[(int64_t)gn * 8 + 4];
+                }
                 bs[j] = sbase[(int64_t)gn * 16];
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
         for (int j = 0; j < PF - 1; ++j)
-            if (g + j < g1) gemm_group(bw0[j], bw1[j], bx0[j], bx1[j], bs[j], kmask, magic_v, acc);
+            if (g + j < g1) {
+                if (NORM) {
+                    bx0[j] = hrow[(g + j - gw0) * 8];
+                    bx1[j] = hrow[(g + j - gw0) * 8 + 4];
+                }
+                gemm_group(bw0[j], bw1[j], bx0[j], bx1[j], bs[j], kmask, magic_v, acc);
+            }
     }
 
     // Reduce the S_wg slices of this workgroup in slice order.
@@ -203,6 +312,22 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
     }
 
     // lane (kq, i) holds rows m = 4 kq + r of columns n = 64 t + 16 nb + i
+    if (SWIGLU) {
+        const int F = N / 2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int m = 4 * kq + r;
+            if (m >= M) break;
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const int f = t * 32 + nb * 16 + i;
+                const float gt = acc[nb][r], up = acc[nb + 2][r];
+                const float sg = gt / (1.0f + expf(-gt));
+                if (f < F) ((uint16_t*)y)[m * ldy + f] = f32_to_bf16(sg * up);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int m = 4 * kq + r;
@@ -251,7 +376,7 @@ struct GemmPlan {
 };
 
 // Split of K over wavefronts: about 2048 wavefronts (two per SIMD), at least
-// four groups per wavefront and at most 16 partial slices; one wavefront per
+// four groups per wavefront and at most 8 partial slices; one wavefront per
 // workgroup, except that very wide matrices (one slice) pair two wavefronts
 // per tile through LDS.  Measured on MI355X over the 27B-class shapes: more
 // wavefronts only add per-wavefront start-up and partial traffic.  Depends on
@@ -265,7 +390,7 @@ static GemmPlan plan_gemm(int M, int N, int K, int slots = 1) {
     const int target_waves = 2048;
     const int units = p.ntiles * slots;
     int S = (target_waves + units - 1) / units;
-    int maxS = p.G / 4 < 16 ? p.G / 4 : 16;
+    int maxS = p.G / 4 < 8 ? p.G / 4 : 8;
     if (maxS < 1) maxS = 1;
     if (S > maxS) S = maxS;
     if (S < 1) S = 1;
@@ -284,13 +409,42 @@ static GemmPlan plan_gemm(int M, int N, int K, int slots = 1) {
     return p;
 }
 
-static void launch_gemm(const GemmPlan& p, const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* s,
-                        void* y, int64_t ldy, int ydt, int M, int N, float* part, hipStream_t st) {
-    hipLaunchKernelGGL(w4_gemm_kernel, dim3(p.ntiles, p.S_grid), dim3(64 * p.S_wg), 0, st, x, ldx, (const u32x4*)w, s,
-                       y, ldy, ydt, M, N, p.G, p.S_wg, p.S_grid, part, p.Npad, 0x000F000Fu, 0x43004300u, GemmGroup{});
-    if (p.S_grid > 1)
-        hipLaunchKernelGGL(w4_gemm_reduce_kernel, dim3(p.ntiles, M), dim3(64), 0, st, part, p.S_grid, M, p.Npad, N,
-                           y, ldy, ydt);
+// Dynamic LDS beyond the default 64 KiB needs a per-kernel opt-in (gfx950 has
+// 160 KiB per workgroup); set once per kernel variant.
+template <bool NORM, bool SWIGLU>
+static int kernel_lds_optin(size_t lds) {
+    static size_t granted = 65536;
+    if (lds > granted) {
+        const hipError_t e = hipFuncSetAttribute((const void*)w4_gemm_kernel<NORM, SWIGLU>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) {
+            set_error("w4 GEMM: cannot raise the dynamic LDS limit to %zu bytes: %s", lds, hipGetErrorString(e));
+            return VW4_EHIP;
+        }
+        granted = lds;
+    }
+    return VW4_OK;
+}
+
+template <bool NORM, bool SWIGLU>
+static int launch_kernel(const GemmPlan& p, int slots, hipStream_t st, const uint16_t* x, int64_t ldx,
+                         const uint8_t* w, const uint16_t* s, void* y, int64_t ldy, int ydt, int M, int N, float* part,
+                         const GemmGroup& grp, const NormIn& nrm) {
+    size_t lds = 0;
+    if (NORM) {
+        const int S = p.S_wg * p.S_grid;
+        const int kw = (p.S_wg * p.G + S - 1) / S * 64;   // the widest workgroup K range
+        lds = (size_t)M * kw * 2;
+        // 160 KiB per workgroup, less the static reduction buffer
+        VW4_REQUIRE(lds <= 160 * 1024 - 17 * 1024, VW4_EUNSUPPORTED,
+                    "w4 GEMM: normalised rows need %zu bytes of LDS", lds);
+        const int rc = kernel_lds_optin<NORM, SWIGLU>(lds);
+        if (rc) return rc;
+    }
+    hipLaunchKernelGGL((w4_gemm_kernel<NORM, SWIGLU>), dim3(p.ntiles, p.S_grid, slots), dim3(64 * p.S_wg), lds, st,
+                       x, ldx, (const u32x4*)w, s, y, ldy, ydt, M, N, p.G, p.S_wg, p.S_grid, part, p.Npad,
+                       0x000F000Fu, 0x43004300u, grp, nrm);
+    return VW4_OK;
 }
 
 int gemm_dispatch(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* s, void* y, int64_t ldy,
@@ -314,7 +468,12 @@ int gemm_dispatch(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16
                     "w4_skinny_gemm: needs a 256-byte aligned workspace of %zu bytes", p.ws_bytes);
         part = (float*)ws;
     }
-    launch_gemm(p, x, ldx, w, s, y, ldy, ydt, M, N, part, st);
+    const int rc = launch_kernel<false, false>(p, 1, st, x, ldx, w, s, y, ldy, ydt, M, N, part, GemmGroup{},
+                                               NormIn{});
+    if (rc) return rc;
+    if (p.S_grid > 1)
+        hipLaunchKernelGGL(w4_gemm_reduce_kernel, dim3(p.ntiles, M), dim3(64), 0, st, part, p.S_grid, M, p.Npad, N,
+                           y, ldy, ydt);
     return check_launch("w4_skinny_gemm");
 }
 
@@ -333,13 +492,67 @@ int gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16
                 "w4_skinny_gemm_partials: misaligned pointer");
     const GemmPlan p = plan_gemm(M, N, K, max_slots);
     // S_grid == 1 writes the product straight into part[0] with row stride Npad
-    void* y = part;
-    const int64_t ldy = p.Npad;
-    float* pp = part;
-    hipLaunchKernelGGL(w4_gemm_kernel, dim3(p.ntiles, p.S_grid, max_slots), dim3(64 * p.S_wg), 0, st, x, ldx,
-                       (const u32x4*)w, s, y, ldy, VW4_F32, M, N, p.G, p.S_wg, p.S_grid, pp, p.Npad, 0x000F000Fu,
-                       0x43004300u, grp);
+    const int rc = launch_kernel<false, false>(p, max_slots, st, x, ldx, w, s, part, p.Npad, VW4_F32, M, N, part,
+                                               grp, NormIn{});
+    if (rc) return rc;
     return check_launch("w4_skinny_gemm_partials");
+}
+
+// The partials form with the activations normalised on the fly:
+// h = bf16(rmsnorm(resid) * gamma) (sums of squares from vw4_add_sumsq).
+int gemm_rmsnorm_partials(const uint16_t* resid, const uint16_t* gamma, const float* ssq, float eps,
+                          const uint8_t* w, const uint16_t* s, float* part, int M, int N, int K, hipStream_t st) {
+    VW4_REQUIRE(M >= 1 && M <= GEMM_MAX_M && N >= 1 && K >= 64 && K % 64 == 0 && K <= 65536, VW4_EINVAL,
+                "w4_skinny_gemm_rmsnorm_partials: bad shape M=%d N=%d K=%d", M, N, K);
+    VW4_REQUIRE(resid && gamma && ssq && w && s && part, VW4_EINVAL, "w4_skinny_gemm_rmsnorm_partials: null pointer");
+    VW4_REQUIRE(aligned(resid, 16) && aligned(gamma, 16) && aligned(w, 16) && aligned(s, 8) && aligned(part, 4),
+                VW4_EINVAL, "w4_skinny_gemm_rmsnorm_partials: misaligned pointer");
+    VW4_REQUIRE(eps >= 0.0f, VW4_EINVAL, "w4_skinny_gemm_rmsnorm_partials: eps must be >= 0");
+    const GemmPlan p = plan_gemm(M, N, K);
+    const NormIn nrm{resid, gamma, ssq, (K + NORM_CHUNK - 1) / NORM_CHUNK, eps};
+    const int rc = launch_kernel<true, false>(p, 1, st, nullptr, K, w, s, part, p.Npad, VW4_F32, M, N, part,
+                                              GemmGroup{}, nrm);
+    if (rc) return rc;
+    return check_launch("w4_skinny_gemm_rmsnorm_partials");
+}
+
+// SwiGLU epilogue: one slice of K per tile, S_wg wavefronts per workgroup.
+static GemmPlan plan_swiglu(int N, int K, int slots) {
+    GemmPlan p;
+    p.G = K / 64;
+    p.ntiles = (N + 63) / 64;
+    p.Npad = (int64_t)p.ntiles * 64;
+    const int units = p.ntiles * slots;
+    int swg = (2048 + units - 1) / units;
+    if (swg > 4) swg = 4;
+    if (swg > p.G) swg = p.G;
+    p.S_wg = swg < 1 ? 1 : swg;
+    p.S_grid = 1;
+    p.ws_bytes = 0;
+    return p;
+}
+
+int gemm_swiglu(const uint16_t* x, int64_t ldx, const NormIn* nrm, const uint8_t* w, const uint16_t* s, uint16_t* a,
+                int64_t lda, int M, int F, int K, hipStream_t st, const GemmGroup& grp, int slots) {
+    VW4_REQUIRE(M >= 1 && M <= GEMM_MAX_M && F >= 32 && F % 32 == 0 && K >= 64 && K % 64 == 0 && K <= 65536,
+                VW4_EINVAL, "w4 GEMM + SwiGLU: bad shape M=%d F=%d K=%d (F must be a multiple of 32)", M, F, K);
+    VW4_REQUIRE(w && s && a && lda >= F, VW4_EINVAL, "w4 GEMM + SwiGLU: bad output or null pointer");
+    VW4_REQUIRE(aligned(w, 16) && aligned(s, 8) && aligned(a, 2), VW4_EINVAL, "w4 GEMM + SwiGLU: misaligned pointer");
+    const GemmPlan p = plan_swiglu(2 * F, K, slots);
+    int rc;
+    if (nrm) {
+        VW4_REQUIRE(nrm->resid && nrm->gamma && nrm->ssq && aligned(nrm->resid, 16) && aligned(nrm->gamma, 16),
+                    VW4_EINVAL, "w4 GEMM + SwiGLU: bad normalisation inputs");
+        rc = launch_kernel<true, true>(p, slots, st, nullptr, K, w, s, a, lda, VW4_BF16, M, 2 * F, nullptr, grp,
+                                       *nrm);
+    } else {
+        VW4_REQUIRE(x && ldx >= K && ldx % 8 == 0 && aligned(x, 16), VW4_EINVAL,
+                    "w4 GEMM + SwiGLU: x needs ldx >= K, ldx %% 8 == 0 and 16-byte alignment");
+        rc = launch_kernel<false, true>(p, slots, st, x, ldx, w, s, a, lda, VW4_BF16, M, 2 * F, nullptr, grp,
+                                        NormIn{});
+    }
+    if (rc) return rc;
+    return check_launch("w4 GEMM + SwiGLU");
 }
 
 int grouped_gemm_partials(const uint16_t* x, int64_t ldx, int64_t x_sstride, const uint8_t* w_bank,
@@ -352,7 +565,7 @@ int grouped_gemm_partials(const uint16_t* x, int64_t ldx, int64_t x_sstride, con
                 "w4_grouped_gemm: expert strides must be positive, weights 16-byte and scales 8-byte multiples");
     VW4_REQUIRE(x_sstride % 8 == 0 && x_sstride >= 0 && p_sstride >= 0, VW4_EINVAL,
                 "w4_grouped_gemm: bad slot strides");
-    GemmGroup g;
+    GemmGroup g{};
     g.slot_expert = slot_expert;
     g.n_slots = n_slots;
     g.w_estride = w_estride_bytes / 16;
@@ -410,6 +623,48 @@ int w4_grouped_gemm(const uint16_t* x, int64_t ldx, int64_t x_sstride, const uin
     }
     return vw4::grouped_gemm_partials(x, ldx, x_sstride, w_bank, w_estride, s_bank, s_estride, slot_expert, n_slots,
                                       max_slots, part, p_sstride, M, N, K, (hipStream_t)stream);
+}
+
+int w4_skinny_gemm_rmsnorm_partials(const uint16_t* resid, const uint16_t* gamma, const void* norm_ws, float eps,
+                                    const uint8_t* w_packed, const uint16_t* scales_packed, float* part, int32_t M,
+                                    int32_t N, int32_t K, void* stream) {
+    return vw4::gemm_rmsnorm_partials(resid, gamma, (const float*)norm_ws, eps, w_packed, scales_packed, part, M, N,
+                                      K, (hipStream_t)stream);
+}
+
+int w4_skinny_gemm_rmsnorm_swiglu(const uint16_t* resid, const uint16_t* gamma, const void* norm_ws, float eps,
+                                  const uint8_t* w_packed, const uint16_t* scales_packed, uint16_t* a, int64_t lda,
+                                  int32_t M, int32_t F, int32_t K, void* stream) {
+    const vw4::NormIn nrm{resid, gamma, (const float*)norm_ws, (K + vw4::NORM_CHUNK - 1) / vw4::NORM_CHUNK, eps};
+    VW4_REQUIRE(eps >= 0.0f, VW4_EINVAL, "w4_skinny_gemm_rmsnorm_swiglu: eps must be >= 0");
+    return vw4::gemm_swiglu(nullptr, K, &nrm, w_packed, scales_packed, a, lda, M, F, K, (hipStream_t)stream,
+                            vw4::GemmGroup{}, 1);
+}
+
+int w4_skinny_gemm_swiglu(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, const uint16_t* scales_packed,
+                          uint16_t* a, int64_t lda, int32_t M, int32_t F, int32_t K, void* stream) {
+    return vw4::gemm_swiglu(x, ldx, nullptr, w_packed, scales_packed, a, lda, M, F, K, (hipStream_t)stream,
+                            vw4::GemmGroup{}, 1);
+}
+
+int w4_grouped_gemm_swiglu(const uint16_t* x, int64_t ldx, int64_t x_sstride, const uint8_t* w_bank,
+                           int64_t w_estride, const uint16_t* s_bank, int64_t s_estride, const int32_t* slot_expert,
+                           const int32_t* n_slots, int32_t max_slots, uint16_t* a, int64_t a_sstride, int32_t M,
+                           int32_t F, int32_t K, void* stream) {
+    VW4_REQUIRE(slot_expert && n_slots && max_slots >= 1 && max_slots <= 65535, VW4_EINVAL,
+                "w4_grouped_gemm_swiglu: bad slot arguments");
+    VW4_REQUIRE(w_estride % 16 == 0 && w_estride > 0 && s_estride > 0 && s_estride % 4 == 0, VW4_EINVAL,
+                "w4_grouped_gemm_swiglu: expert strides must be positive, weights 16-byte and scales 8-byte multiples");
+    VW4_REQUIRE(x_sstride % 8 == 0 && x_sstride >= 0 && a_sstride >= (int64_t)M * F, VW4_EINVAL,
+                "w4_grouped_gemm_swiglu: bad slot strides");
+    vw4::GemmGroup g{};
+    g.slot_expert = slot_expert;
+    g.n_slots = n_slots;
+    g.w_estride = w_estride / 16;
+    g.s_estride = s_estride;
+    g.x_sstride = x_sstride;
+    g.y_sstride = a_sstride;
+    return vw4::gemm_swiglu(x, ldx, nullptr, w_bank, s_bank, a, F, M, F, K, (hipStream_t)stream, g, max_slots);
 }
 
 int w4_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, const uint16_t* scales_packed,

@@ -90,7 +90,8 @@ DENSE_27B = dict(d=5120, nq=40, nkv=8, hd=128, F=17408, layers=64, V=151936, eps
 
 class Decoder:
     """Pre-norm dense decoder with GQA attention and a SwiGLU FFN, every linear
-    a W4 skinny GEMM.  One call of ``forward`` scores M rows at positions
+    a W4 skinny GEMM (the gate|up matrix in the gate/up-interleaved row order
+    of B.interleave_gate_up, with the SwiGLU in that GEMM's epilogue).  One call of ``forward`` scores M rows at positions
     L .. L+M-1 (the verify pass); M = 1 is an autoregressive step.  Weights,
     KV caches and activation buffers are allocated once (device-resident)."""
 
@@ -194,14 +195,11 @@ class Decoder:
             B.w4_skinny_gemm_partials(self.attn, W["o"].packed, W["o"].pscales, self.parts["o"], M, N, K, stream)
             hook("post", "o")
             B.add_rmsnorm(resid, self.parts["o"], S, ldp, W["g2"], eps, M, d, h, self.norm_ws, stream)
-            # FFN block
+            # FFN block: gate|up with the SwiGLU in the GEMM epilogue
             N, K = self.shapes["gate_up"]
-            S, ldp = B.gemm_partials_layout(M, N, K)
             hook("pre", "gate_up")
-            B.w4_skinny_gemm_partials(h, W["gate_up"].packed, W["gate_up"].pscales, self.parts["gate_up"], M, N, K,
-                                      stream)
+            B.w4_skinny_gemm_swiglu(h, W["gate_up"].packed, W["gate_up"].pscales, self.a, F, M, F, K, stream)
             hook("post", "gate_up")
-            B.swiglu(self.parts["gate_up"], S, ldp, M, F, self.a, stream)
             N, K = self.shapes["down"]
             S, ldp = B.gemm_partials_layout(M, N, K)
             hook("pre", "down")
@@ -221,14 +219,20 @@ class Decoder:
         buffers, in the same order; optionally only the named linears), for
         timing the GEMM kernel by itself.  Returns the launch count."""
         c = self.cfg
+        eps, F = c["eps"], c["F"]
         n = 0
         for W in self.layers:
-            for name, x in (("qkv", self.h), ("o", self.attn), ("gate_up", self.h), ("down", self.a)):
-                if name in names:
-                    N, K = self.shapes[name]
+            for name in ("qkv", "o", "gate_up", "down"):
+                if name not in names:
+                    continue
+                N, K = self.shapes[name]
+                if name == "gate_up":
+                    B.w4_skinny_gemm_swiglu(self.h[:M], W[name].packed, W[name].pscales, self.a, F, M, F, K, stream)
+                else:
+                    x = {"qkv": self.h, "o": self.attn, "down": self.a}[name]
                     B.w4_skinny_gemm_partials(x[:M], W[name].packed, W[name].pscales, self.parts[name], M, N, K,
                                               stream)
-                    n += 1
+                n += 1
         if "lm_head" in names:
             B.w4_skinny_gemm(self.h[:M], self.lm_head.packed, self.lm_head.pscales, self.logits[:M], M, c["V"],
                              c["d"], ws=self.lm_ws, stream=stream)
@@ -240,8 +244,9 @@ class Decoder:
         scale) once, activations in, fp32 outputs out."""
         c = self.cfg
         tot = 0.0
-        for N, K in self.shapes.values():
-            tot += c["layers"] * (N * K * BYTES_PER_WEIGHT + M * K * 2 + M * N * 4)
+        for name, (N, K) in self.shapes.items():
+            out = M * (N // 2) * 2 if name == "gate_up" else M * N * 4    # SwiGLU output (bf16) / fp32 partial sums
+            tot += c["layers"] * (N * K * BYTES_PER_WEIGHT + M * K * 2 + out)
         tot += c["V"] * c["d"] * BYTES_PER_WEIGHT + M * c["d"] * 2 + M * c["V"] * 4
         return int(tot)
 
@@ -311,8 +316,8 @@ MOE_30B = dict(n_exp=128, topk=8, d=2048, F=768, V=151936, eps=1e-6)
 
 class ExpertBank:
     """W4 weights of E SwiGLU experts, each stored as a contiguous slice of two
-    stacked matrices: gate|up [E * 2F][d] (rows [0, F) of an expert are the
-    gate, [F, 2F) the up projection) and down [E * d][F]."""
+    stacked matrices: gate|up [E * 2F][d] (each expert's 2F rows in the
+    gate/up-interleaved order of B.interleave_gate_up) and down [E * d][F]."""
 
     def __init__(self, gate_up: W4Linear, down: W4Linear, E: int, d: int, F: int):
         assert (2 * F) % 64 == 0 and d % 64 == 0 and F % 64 == 0
@@ -329,7 +334,9 @@ class ExpertBank:
     def from_fp32(cls, gate_up, down):
         """gate_up: [E][2F][d], down: [E][d][F] fp32 device tensors."""
         E, F2, d = gate_up.shape
-        return cls(W4Linear.from_fp32(gate_up.reshape(E * F2, d)), W4Linear.from_fp32(down.reshape(E * d, F2 // 2)),
+        gu = B.interleave_gate_up(gate_up.reshape(E, F2, d).permute(1, 0, 2).reshape(F2, E * d))
+        gu = gu.reshape(F2, E, d).permute(1, 0, 2).contiguous()     # per expert, gate/up-interleaved rows
+        return cls(W4Linear.from_fp32(gu.reshape(E * F2, d)), W4Linear.from_fp32(down.reshape(E * d, F2 // 2)),
                    E, d, F2 // 2)
 
     def expert_bytes(self) -> int:
@@ -357,11 +364,8 @@ class MoEVerify:
         self.slot_expert = torch.zeros(self.max_slots, dtype=i32, device=device)
         self.n_slots = torch.zeros(1, dtype=i32, device=device)
         self.row_slot = torch.empty((M, topk), dtype=i32, device=device)
-        self.gu_S, self.gu_ldp = B.grouped_gemm_layout(M, 2 * F, d, self.max_slots)
         self.dn_S, self.dn_ldp = B.grouped_gemm_layout(M, d, F, self.max_slots)
-        self.gu_sstride = self.gu_S * M * self.gu_ldp
         self.dn_sstride = self.dn_S * M * self.dn_ldp
-        self.part_gu = torch.empty(self.max_slots * self.gu_sstride, dtype=torch.float32, device=device)
         self.part_dn = torch.empty(self.max_slots * self.dn_sstride, dtype=torch.float32, device=device)
         self.a = torch.empty((self.max_slots, M, F), dtype=torch.int16, device=device)
         self.y = torch.empty((M, d), dtype=torch.float32, device=device)
@@ -384,12 +388,10 @@ class MoEVerify:
         B.moe_route(router_logits, M, self.E, self.topk, self.experts, self.weights, self.slot_expert, self.n_slots,
                     self.row_slot, stream)
         hook("pre", "gate_up")
-        B.w4_grouped_gemm(x, x.stride(0), 0, bank.gate_up.packed, bank.gu_estride[0], bank.gate_up.pscales,
-                          bank.gu_estride[1], self.slot_expert, self.n_slots, ms, self.part_gu, self.gu_sstride,
-                          M, 2 * F, d, stream)
+        B.w4_grouped_gemm_swiglu(x, x.stride(0), 0, bank.gate_up.packed, bank.gu_estride[0], bank.gate_up.pscales,
+                                 bank.gu_estride[1], self.slot_expert, self.n_slots, ms, self.a, M * F, M, F, d,
+                                 stream)
         hook("post", "gate_up")
-        B.grouped_swiglu(self.part_gu, self.gu_S, self.gu_ldp, self.gu_sstride, M, F, self.a, M * F, self.n_slots,
-                         ms, stream)
         hook("pre", "down")
         B.w4_grouped_gemm(self.a, F, M * F, bank.down.packed, bank.dn_estride[0], bank.down.pscales,
                           bank.dn_estride[1], self.slot_expert, self.n_slots, ms, self.part_dn, self.dn_sstride,
@@ -403,9 +405,9 @@ class MoEVerify:
         """Only the W4 GEMM launches of one step (grouped gate|up, grouped
         down, LM head) on the current routing and buffers."""
         M, d, F, ms = self.M, self.d, self.F, self.max_slots
-        B.w4_grouped_gemm(self.h, d, 0, bank.gate_up.packed, bank.gu_estride[0], bank.gate_up.pscales,
-                          bank.gu_estride[1], self.slot_expert, self.n_slots, ms, self.part_gu, self.gu_sstride,
-                          M, 2 * F, d, stream)
+        B.w4_grouped_gemm_swiglu(self.h, d, 0, bank.gate_up.packed, bank.gu_estride[0], bank.gate_up.pscales,
+                                 bank.gu_estride[1], self.slot_expert, self.n_slots, ms, self.a, M * F, M, F, d,
+                                 stream)
         B.w4_grouped_gemm(self.a, F, M * F, bank.down.packed, bank.dn_estride[0], bank.down.pscales,
                           bank.dn_estride[1], self.slot_expert, self.n_slots, ms, self.part_dn, self.dn_sstride,
                           M, d, F, stream)
