@@ -14,6 +14,7 @@
 // launch of its own.  Rounding points: activations are stored as bf16 after
 // every op (round to nearest even), arithmetic is fp32.
 #include <math.h>
+#include <stdlib.h>
 
 #include "common.h"
 
@@ -469,13 +470,20 @@ struct AttnPlan {
     size_t off_o, off_ml, total;
 };
 
-// 32-position tiles split evenly over nparts workgroups per KV head: about 8
-// tiles (two per wavefront) per workgroup, at most 64 partials per query.
+// 32-position tiles split evenly over nparts workgroups per KV head: about 4
+// tiles (one per wavefront) per workgroup, at most 64 partials per query
+// (measured on MI355X at 1k / 8k / 32k context: one tile in flight per
+// wavefront across many workgroups beats longer per-wavefront loops).
 static AttnPlan attn_plan(int M, int nq, int nkv, int64_t ctx) {
     AttnPlan p;
     p.QN = (nq / nkv) * M;
     p.ntiles = (int)((ctx + AT - 1) / AT);
-    int np = (p.ntiles + 7) / 8;
+    int tpw = 4;                                     // tiles per workgroup (tuning override below)
+    if (const char* e = getenv("VW4_ATTN_TILES")) {
+        const int v = atoi(e);
+        if (v >= 1 && v <= 1024) tpw = v;
+    }
+    int np = (p.ntiles + tpw - 1) / tpw;
     p.nparts = np < 1 ? 1 : (np > 64 ? 64 : np);
     size_t o = 0;
     p.off_o = o;
