@@ -177,7 +177,7 @@ def lm_head_workload(args):
                 "top_p": top_p, "weights": "int4 group-64 symmetric, fp16 scales", "lm_head_copies": ncopies},
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                  "kernel": "w4_gemm_kernel<4>", "alg_bytes_per_launch": int(alg_bytes),
+                  "kernel": "w4_gemm_kernel (M=4)", "alg_bytes_per_launch": int(alg_bytes),
                   "avg_launch_us": round(gemm_avg * 1e3, 2)},
         stages_us={"w4_gemm_lm_head": round(gemm_avg * 1e3, 2),
                    "stats_and_accept": round(total_ms / K * 1e3 - gemm_avg * 1e3, 2)},
@@ -343,7 +343,7 @@ def verify27b_workload(args):
                 "weights": "int4 group-64 symmetric, fp16 scales", "kv_cache": "bf16"},
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("verify27b"),
-                  "kernel": "w4_gemm_kernel<4> (the 257 W4 GEMM launches of a step, replayed as a graph)",
+                  "kernel": "w4_gemm_kernel (the 257 W4 GEMM launches of a step at M=4, replayed as a graph)",
                   "alg_bytes_per_launch": int(per_launch_bytes), "avg_launch_us": round(gemm_launch_us, 2)},
         stages_us={"w4_gemm_total_eager": round(gemm_ms * 1e3 / K, 1),
                    "w4_gemm_total_graph": round(gemm_launch_us * n_launch, 1),
@@ -526,7 +526,7 @@ def moe_workload(args):
                 "weights": "int4 group-64 symmetric, fp16 scales", "rotated_banks": nrot},
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("moe_verify"),
-                  "kernel": "w4_gemm_kernel<4> (grouped gate|up, grouped down, LM head: the 3 W4 GEMM launches "
+                  "kernel": "w4_gemm_kernel (grouped gate|up + SwiGLU, grouped down, LM head: the 3 W4 GEMM launches "
                             "of a step, replayed as graphs)",
                   "alg_bytes_per_launch": int(per_launch_bytes),
                   "avg_launch_us": round(ms_launch * 1e3, 2)},
