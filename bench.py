@@ -358,6 +358,24 @@ def verify27b_workload(args):
     return res
 
 
+def verify27b_cpu_baseline_layer(reps=8):
+    """The CPU oracle on the four linears of one layer at M=4 (fp64), reps row sets."""
+    import oracle
+    from verify_step_w4_amd import synth
+    g = synth.rng(synth.SEED_BASE + 2)
+    tot = 0.0
+    for N, K in [(7168, 5120), (5120, 5120), (34816, 5120), (5120, 17408)]:
+        codes, scales = oracle.w4_quantize(synth.normal_f32(g, (N, K), 0.02))
+        for r in range(reps):
+            x = synth.f32_to_bf16_bits(synth.normal_f32(g, (4, K), 1.0))
+            t0 = time.perf_counter()
+            oracle.w4_gemm(x, codes, scales)
+            tot += time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(reps / tot, 4), "unit": "layer passes/s", "cores": cores, "kind": "oracle",
+            "sample": f"one 27B-class layer's four W4 GEMMs at M=4 on {reps} row sets; quantisation untimed"}
+
+
 def verify27b_cpu_baseline(reps=16):
     """The CPU oracle on a bounded sample of the same step: the four W4 GEMMs
     of one decoder layer at the 27B-class shapes (fp64 over its 175 MB of
@@ -585,9 +603,161 @@ def moe_cpu_baseline(nsteps=4):
                       "weight generation and quantisation untimed"}
 
 
+# --------------------------------------------------------------------------
+# One 27B-class decoder layer's linears, M swept
+# --------------------------------------------------------------------------
+def layer_linears_workload(args):
+    """The fused qkv [7168][5120], o [5120][5120], gate|up [34816][5120] (SwiGLU
+    epilogue) and down [5120][17408] W4 GEMMs of one layer; 8 layers' weights
+    rotated (1.4 GB).  A step is one pass over a layer's four linears at M=4;
+    the M sweep times the same passes at M = 1, 2, 3, 4, 6."""
+    import numpy as np
+    import torch
+
+    from verify_step_w4_amd import binding as B
+    from verify_step_w4_amd.model import BYTES_PER_WEIGHT, W4Linear
+
+    d, F, nqkv = 5120, 17408, 7168
+    nlay = 8
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261202)
+    log(f"generating {nlay} layers of W4 linears (175.5 MB each)")
+    layers = [dict(qkv=W4Linear.random(nqkv, d, 0.02, gen), o=W4Linear.random(d, d, 0.02, gen),
+                   gate_up=W4Linear.random(2 * F, d, 0.02, gen), down=W4Linear.random(d, F, 0.02, gen))
+              for _ in range(nlay)]
+    Mmax = 6
+    xs = {K: torch.randn((Mmax, K), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+          for K in (d, F)}
+    parts = {nm: torch.empty(8 * Mmax * (N + 64), dtype=torch.float32, device="cuda")
+             for nm, N in (("qkv", nqkv), ("o", d), ("down", d))}
+    a = torch.empty((Mmax, F), dtype=torch.int16, device="cuda")
+    shapes = {"qkv": (nqkv, d), "o": (d, d), "gate_up": (2 * F, d), "down": (d, F)}
+
+    def issue(M, names=("qkv", "o", "gate_up", "down")):
+        n = 0
+        for L in layers:
+            for nm in names:
+                N, K = shapes[nm]
+                if nm == "gate_up":
+                    B.w4_skinny_gemm_swiglu(xs[K][:M], L[nm].packed, L[nm].pscales, a, F, M, F, K)
+                else:
+                    B.w4_skinny_gemm_partials(xs[K][:M], L[nm].packed, L[nm].pscales, parts[nm], M, N, K)
+                n += 1
+        return n
+
+    def alg(M, nm):
+        N, K = shapes[nm]
+        out = M * (N // 2) * 2 if nm == "gate_up" else M * N * 4
+        return N * K * BYTES_PER_WEIGHT + M * K * 2 + out
+
+    reps = max(1, args.steps // nlay)
+    sweep = {}
+    for M in (1, 2, 3, 4, 6):
+        ms_launch, n_launch = time_graphs([lambda M=M: issue(M)], reps)
+        per_layer_us = ms_launch * 1e3 * 4
+        layer_bytes = sum(alg(M, nm) for nm in shapes)
+        sweep[M] = {"layer_us": round(per_layer_us, 2),
+                    "layer_GBs": round(layer_bytes / (per_layer_us * 1e-6) / 1e9, 1)}
+        for nm in shapes:
+            us = time_graphs([lambda M=M, nm=nm: issue(M, (nm,))], reps)[0] * 1e3
+            sweep[M][nm + "_GBs"] = round(alg(M, nm) / (us * 1e-6) / 1e9, 1)
+        log(f"M={M}: {sweep[M]}")
+    s4 = sweep[4]
+    ms4 = s4["layer_us"] * 1e-3
+    layer_bytes4 = sum(alg(4, nm) for nm in shapes)
+    return dict(
+        ms_per_step=ms4,
+        value=1.0 / (ms4 * 1e-3),
+        config={"workload": "layer_linears", "d_model": d, "qkv": [nqkv, d], "o": [d, d], "gate_up": [2 * F, d],
+                "down": [d, F], "M": 4, "rotated_layers": nlay,
+                "weights": "int4 group-64 symmetric, fp16 scales"},
+        roofline={"bound": "hbm", "achieved": round(layer_bytes4 / 4 / (ms4 / 4 * 1e-3) / 1e9, 1),
+                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(layer_bytes4 / (ms4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                  "kernel": "w4_gemm_kernel (the four linears of a layer at M=4, replayed as a graph)",
+                  "alg_bytes_per_launch": int(layer_bytes4 / 4), "avg_launch_us": round(s4["layer_us"] / 4, 2)},
+        m_sweep=sweep,
+        unit_note="value = layer passes (four W4 GEMM launches) per second at M=4",
+    )
+
+
+# --------------------------------------------------------------------------
+# Single small LM-head verify step (d=1024, V=8192)
+# --------------------------------------------------------------------------
+def lm_small_workload(args):
+    """x [4][1024] -> W4 LM head [8192][1024] -> temperature 0.6 / top_p 0.95
+    statistics -> acceptance of 3 drafts from q = softmax(N(0, 2)); 240 copies
+    of the 4.46 MB head rotated (1.07 GB), one copy per step."""
+    import numpy as np
+    import torch
+
+    from verify_step_w4_amd import binding as B
+    from verify_step_w4_amd.model import BYTES_PER_WEIGHT, LMHeadVerify, W4Linear
+
+    V, d, M, D = 8192, 1024, 4, 3
+    T, top_p, seed = 0.6, 0.95, 0x5EED0001
+    ncopy = 240
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261201)
+    log(f"generating {ncopy} W4 LM heads [{V}][{d}]")
+    heads = [W4Linear.random(V, d, 0.02, gen) for _ in range(ncopy)]
+    npool = 64
+    xs = torch.randn((npool, M, d), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+    qs = torch.softmax(torch.randn((npool, D, V), generator=gen, device="cuda", dtype=torch.float64) * 2.0,
+                       dim=-1).to(torch.float32)
+    drafts = torch.multinomial(qs.reshape(-1, V).double(), 1, generator=gen).reshape(npool, D).to(torch.int32)
+    vs = LMHeadVerify(V, d, M)
+    step_dev = torch.zeros(1, dtype=torch.int64, device="cuda")
+
+    def issue_step(k):
+        j = k % npool
+        vs.gemm(xs[j], heads[k % ncopy])
+        B.verify_logits(None, None, None, M, V, d, T, top_p, vs.logits, vs.stats, vs.stat_ws)
+        B.spec_accept_ex(vs.logits, 0, vs.stats, 0, qs[j], 0, drafts[j], 1, D, V, T, seed, step_dev, vs.tokens,
+                         vs.n_acc, vs.flags, vs.acc_ws)
+        B.step_advance(step_dev, 1)
+
+    # one graph per group of 240 steps (all copies once), replayed
+    ms_step, n = time_graphs([lambda: [issue_step(k) for k in range(ncopy)] and ncopy], max(1, args.steps // ncopy))
+    gemm_ms, _ = time_graphs([lambda: [vs.gemm(xs[k % npool], heads[k]) for k in range(ncopy)] and ncopy], 2)
+    alg = V * d * BYTES_PER_WEIGHT + M * d * 2 + M * V * 4
+    return dict(
+        ms_per_step=ms_step,
+        value=1.0 / (ms_step * 1e-3),
+        config={"workload": "lm_small", "d": d, "V": V, "M": M, "draft_depth": D, "temperature": T, "top_p": top_p,
+                "weights": "int4 group-64 symmetric, fp16 scales", "lm_head_copies": ncopy},
+        roofline={"bound": "hbm", "achieved": round(alg / (gemm_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                  "unit": "GB/s", "frac": round(alg / (gemm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                  "kernel": "w4_gemm_kernel (M=4, 4.46 MB head: launch-latency bound)",
+                  "alg_bytes_per_launch": int(alg), "avg_launch_us": round(gemm_ms * 1e3, 2)},
+        stages_us={"w4_gemm": round(gemm_ms * 1e3, 2), "stats_and_accept": round((ms_step - gemm_ms) * 1e3, 2)},
+    )
+
+
+def lm_small_cpu_baseline(nsteps=200):
+    """The CPU oracle on nsteps whole small LM-head verify steps."""
+    import oracle
+    from verify_step_w4_amd import synth
+    V, d, D = 8192, 1024, 3
+    g = synth.rng(synth.SEED_BASE + 1)
+    codes, scales = oracle.w4_quantize(synth.normal_f32(g, (V, d), 0.02))
+    q, drafts = synth.q_and_drafts(synth.SEED_BASE + 11, D, V, 2.0, B=nsteps)
+    xs = [synth.f32_to_bf16_bits(synth.normal_f32(g, (D + 1, d), 1.0)) for _ in range(nsteps)]
+    t0 = time.perf_counter()
+    for s in range(nsteps):
+        z = oracle.w4_gemm(xs[s], codes, scales).astype("float32")
+        oracle.spec_accept(z, q, drafts[s], 0.6, 0.95, 0x5EED0001, s)
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(nsteps / dt, 3), "unit": "verify steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nsteps} whole small LM-head verify steps (d=1024, V=8192, M=4)"}
+
+
 WORKLOADS = {"lm_head_verify": (lm_head_workload, lm_head_cpu_baseline),
              "verify27b": (verify27b_workload, verify27b_cpu_baseline),
-             "moe_verify": (moe_workload, moe_cpu_baseline)}
+             "moe_verify": (moe_workload, moe_cpu_baseline),
+             "layer_linears": (layer_linears_workload, lambda: verify27b_cpu_baseline_layer()),
+             "lm_small": (lm_small_workload, lm_small_cpu_baseline)}
 
 
 def main():
@@ -617,12 +787,13 @@ def main():
     torch.cuda.synchronize()
     del src, dst
     res = run(args)
-    out = {"metric": METRIC, "value": round(res["value"], 3), "unit": "verify steps/s", "n_gpus": 1,
+    out = {"metric": METRIC, "value": round(res["value"], 3),
+           "unit": "layer passes/s" if args.workload == "layer_linears" else "verify steps/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic", "config": res["config"], "roofline": res["roofline"]}
     for k in ("stages_us", "w4_gemm_by_linear", "accepted_length_hist", "flagged_steps", "m1_ar_step_ms",
-              "verify_over_ar", "step_hbm_gbs", "experts_per_step", "grouped_gemm_gbs"):
+              "verify_over_ar", "step_hbm_gbs", "experts_per_step", "grouped_gemm_gbs", "m_sweep", "unit_note"):
         if k in res:
             out[k] = res[k]
     if not args.no_cpu_baseline:

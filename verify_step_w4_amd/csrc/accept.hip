@@ -67,7 +67,7 @@ static AcceptLayout accept_layout(int B, int V) {
     o += (size_t)B * L.P * sizeof(AcceptPart);
     o = (o + 255) / 256 * 256;
     L.off_state = o;
-    o += (size_t)B * 16;
+    o += (size_t)B * 64;
     L.total = (o + 255) / 256 * 256;
     return L;
 }
@@ -160,7 +160,16 @@ struct ProblemState {
     uint32_t flags;
     bool bad;
 };
-static_assert(sizeof(ProblemState) <= 16, "ProblemState slot is 16 bytes");
+// What the finishing workgroup needs from the chunk kernel, in one load:
+// the decision state, the statistics of the resampled row k and its uniform.
+struct ProblemSlot {
+    ProblemState ps;
+    int32_t pad0;
+    vw4_rowstat sk;
+    double u_res;
+    double pad1;
+};
+static_assert(sizeof(ProblemSlot) == 64, "ProblemSlot is 64 bytes");
 
 template <int NT>
 __device__ __forceinline__ ProblemState problem_state(const float* __restrict__ zb, const vw4_rowstat* __restrict__ sb,
@@ -281,6 +290,35 @@ __device__ void finish_problem(const float* __restrict__ zk, const vw4_rowstat& 
         const int a0 = wc * chunk, a1 = min(V, a0 + chunk);
         const int per = (a1 - a0 + NT - 1) / NT;
         const int j0 = a0 + threadIdx.x * per, j1 = min(a1, j0 + per);
+        int cand = 0x7fffffff;
+        double cp = 0.0, cc = 0.0;
+        if (per <= AU) {
+            // the whole run in registers: one load, the masses computed once
+            float zv[AU], qv[AU];
+#pragma unroll
+            for (int u = 0; u < AU; ++u) {
+                zv[u] = (j0 + u < j1) ? zk[j0 + u] : 0.0f;
+                qv[u] = (resid && j0 + u < j1) ? qk[j0 + u] : 0.0f;
+            }
+            double rv[AU];
+            double mine = 0.0;
+#pragma unroll
+            for (int u = 0; u < AU; ++u) {
+                rv[u] = 0.0;
+                if (j0 + u < j1) {
+                    const double pj = p_val(zv[u], sk, T, j0 + u);
+                    rv[u] = resid ? fmax(0.0, pj - (double)qv[u]) : pj;
+                    mine += rv[u];
+                }
+            }
+            double run = before + blk_prefix_excl<NT>(mine, sh);
+            for (int u = 0; u < AU; ++u) {
+                if (j0 + u >= j1) break;
+                const double nxt = run + rv[u];
+                if (nxt > target) { cand = j0 + u; cp = run; cc = nxt; break; }
+                run = nxt;
+            }
+        } else {
         // this thread's residual masses, computed once (runs of up to AU per pass)
         double mine = 0.0;
         for (int t0 = j0; t0 < j1; t0 += AU) {
@@ -298,8 +336,6 @@ __device__ void finish_problem(const float* __restrict__ zk, const vw4_rowstat& 
             }
         }
         double run = before + blk_prefix_excl<NT>(mine, sh);
-        int cand = 0x7fffffff;
-        double cp = 0.0, cc = 0.0;
         for (int t0 = j0; t0 < j1 && cand == 0x7fffffff; t0 += AU) {
             float zv[AU], qv[AU];
 #pragma unroll
@@ -315,6 +351,7 @@ __device__ void finish_problem(const float* __restrict__ zk, const vw4_rowstat& 
                 if (nxt > target) { cand = t0 + u; cp = run; cc = nxt; break; }
                 run = nxt;
             }
+        }
         }
         int best = cand;
         for (int off = 32; off > 0; off >>= 1) best = min(best, __shfl_xor(best, off, 64));
@@ -371,7 +408,7 @@ struct AcceptArgs {
     int32_t* out_nacc;
     uint32_t* out_flags;
     AcceptPart* parts;
-    ProblemState* states;  // per problem, written by workgroup 0 of the chunk kernel
+    ProblemSlot* states;   // per problem, written by workgroup 0 of the chunk kernel
     const uint64_t* step_dev;  // if set, the first problem's step is read here (graph replays)
 };
 
@@ -416,7 +453,15 @@ __global__ __launch_bounds__(NT) void accept_chunk_kernel(AcceptArgs a) {
     if (a.P > 1) {
         if (threadIdx.x == 0) {
             a.parts[b * a.P + w] = part;
-            if (w == 0) a.states[b] = ps;
+            if (w == 0) {
+                ProblemSlot slot;
+                slot.ps = ps;
+                slot.pad0 = 0;
+                slot.sk = sk;
+                slot.u_res = s_u[2 * k + 1];
+                slot.pad1 = 0.0;
+                a.states[b] = slot;
+            }
         }
         return;
     }
@@ -439,26 +484,20 @@ __global__ __launch_bounds__(NT) void accept_finish_kernel(AcceptArgs a) {
     const float* qb = a.q ? a.q + b * a.qstride : nullptr;
     const int32_t* db = a.draft + b * a.D;
     const double T = (double)a.temperature;
-    __shared__ ProblemState s_ps;
-    __shared__ vw4_rowstat s_sk;
-    // the accept decisions were taken by the chunk kernel; only the residual
-    // row's uniform is needed here
-    if (threadIdx.x == 0) s_ps = a.states[b];
+    __shared__ ProblemSlot s_slot;
+    // the accept decisions, the resampled row's statistics and its uniform
+    // come from the chunk kernel, loaded together with the chunk sums
+    if (threadIdx.x == 0) s_slot = a.states[b];
     for (int c = threadIdx.x; c < a.P; c += NT) sp[c] = a.parts[b * a.P + c];
     __syncthreads();
-    const ProblemState ps = s_ps;
+    const ProblemState ps = s_slot.ps;
     if (ps.bad) return;  // outputs written by the chunk kernel
     const int k = ps.k;
-    if (threadIdx.x == 0) {
-        uint64_t c[4] = {first_step(a) + (uint64_t)b, (uint64_t)k, 0, 0};
-        philox4x64_10(a.seed, 0, c);
-        s_u[2 * k] = unit53(c[0]);
-        s_u[2 * k + 1] = unit53(c[1]);
-        s_sk = sb[k];
-    }
+    if (threadIdx.x == 0) s_u[2 * k + 1] = s_slot.u_res;
     __syncthreads();
+    (void)sb;
     const float* zk = zb + (int64_t)k * a.V;
-    const vw4_rowstat sk = s_sk;
+    const vw4_rowstat sk = s_slot.sk;
     const float* qk = (k < a.D) ? qb + (int64_t)k * a.V : nullptr;
     finish_problem<NT>(zk, sk, qk, db, sp, a.P, a.chunk, a.D, a.V, T, ps, s_u, a.out_tokens + b * (a.D + 1),
                        a.out_nacc + b, a.out_flags + b, sh, shi);
@@ -490,7 +529,7 @@ static int spec_accept_impl(const float* logits, int64_t logits_bstride, const v
     a.chunk = L.chunk; a.P = L.P;
     a.out_tokens = out_tokens; a.out_nacc = out_n_acc; a.out_flags = out_flags;
     a.parts = (AcceptPart*)((char*)ws + L.off_part);
-    a.states = (ProblemState*)((char*)ws + L.off_state);
+    a.states = (ProblemSlot*)((char*)ws + L.off_state);
     a.step_dev = step_dev;
     hipStream_t st = (hipStream_t)stream;
     const dim3 grid((unsigned)B, (unsigned)L.P);

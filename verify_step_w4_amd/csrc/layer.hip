@@ -57,6 +57,11 @@ __global__ __launch_bounds__(NCOL) void rmsnorm_apply_kernel(const uint16_t* __r
     __shared__ float s_ssq[NMAXCH];
     __shared__ float s_tot;
     const int ch = blockIdx.x, m = blockIdx.y, d = ch * NCOL + threadIdx.x;
+    // this thread's row value and gain are requested together with the chunk
+    // sums (one memory round trip)
+    const bool live = d < D;
+    const float r = live ? bf16_to_f32(resid[(int64_t)m * D + d]) : 0.0f;
+    const float gm = live ? bf16_to_f32(gamma[d]) : 0.0f;
     for (int k = threadIdx.x; k < nch; k += NCOL) s_ssq[k] = ssq[(int64_t)m * nch + k];  // loads in parallel
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -65,10 +70,9 @@ __global__ __launch_bounds__(NCOL) void rmsnorm_apply_kernel(const uint16_t* __r
         s_tot = tot;
     }
     __syncthreads();
-    if (d >= D) return;
+    if (!live) return;
     const float inv = 1.0f / sqrtf(s_tot / (float)D + eps);
-    const float r = bf16_to_f32(resid[(int64_t)m * D + d]);
-    h[(int64_t)m * D + d] = f32_to_bf16(r * inv * bf16_to_f32(gamma[d]));
+    h[(int64_t)m * D + d] = f32_to_bf16(r * inv * gm);
 }
 
 // ---------------------------------------------------------------------------
@@ -440,6 +444,11 @@ __global__ __launch_bounds__(AHD) void attn_combine_kernel(const float* __restri
     __shared__ float s_f[64], s_l[64];
     const int j = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
     const int64_t base = ((int64_t)h * QN + j) * nparts;
+    // the partial outputs are requested first, together with the chunk maxima
+    // and sums (one memory round trip)
+    float o[64];
+#pragma unroll
+    for (int c = 0; c < 64; ++c) o[c] = (c < nparts) ? ws_o[(base + c) * AHD + d] : 0.0f;
     // chunk maxima and sums: one chunk per thread (nparts <= 64), loads in parallel
     if (d < 64) {
         const AttnPart ap = (d < nparts) ? ws_ml[base + d] : AttnPart{-INFINITY, 0.0f};
@@ -450,9 +459,6 @@ __global__ __launch_bounds__(AHD) void attn_combine_kernel(const float* __restri
         s_l[d] = ap.l;
     }
     __syncthreads();
-    float o[64];
-#pragma unroll
-    for (int c = 0; c < 64; ++c) o[c] = (c < nparts) ? ws_o[(base + c) * AHD + d] : 0.0f;
     float lt = 0.0f, ot = 0.0f;
 #pragma unroll
     for (int c = 0; c < 64; ++c) {

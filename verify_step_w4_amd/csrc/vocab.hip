@@ -207,19 +207,24 @@ __device__ __forceinline__ double combine_E(const ChunkPart* sp, int P, float m,
     return E;
 }
 
-// Descend nb combined bins (ascending key, HB/VT = 8 per thread): the largest
-// bin b with above + sum_{b' >= b} H[b'] >= target.  Returns -1 if none.
-__device__ int descend(const double* __restrict__ H, int nb, double above, double target, double* new_above,
+// Descend nb combined bins (ascending key, HB/VT = 8 per thread, this
+// thread's slice in h): the largest bin b with
+// above + sum_{b' >= b} H[b'] >= target.  Returns -1 if none.
+// This thread's slice of a combined histogram (requested early, so that it
+// travels together with the kernel's other loads).
+__device__ __forceinline__ void load_slice(const double* __restrict__ H, int nb, double (&h)[HB / VT]) {
+    const int b0 = threadIdx.x * (HB / VT);
+#pragma unroll
+    for (int i = 0; i < HB / VT; ++i) h[i] = (b0 + i < nb) ? H[b0 + i] : 0.0;
+}
+
+__device__ int descend(const double (&h)[HB / VT], int nb, double above, double target, double* new_above,
                        double* sh, int* shi) {
     const int per = HB / VT;
     const int b0 = threadIdx.x * per;
-    double h[HB / VT];
     double mine = 0.0;
 #pragma unroll
-    for (int i = 0; i < per; ++i) {
-        h[i] = (b0 + i < nb) ? H[b0 + i] : 0.0;
-        mine += h[i];
-    }
+    for (int i = 0; i < per; ++i) mine += h[i];
     const double later = block_suffix_excl_f64(mine, sh);
     if (threadIdx.x == 0) *shi = -1;
     __syncthreads();
@@ -276,9 +281,18 @@ __global__ __launch_bounds__(VT) void vs_chunk_kernel(const float* __restrict__ 
     float lm = -INFINITY, lmn = INFINITY;
     int li = 0x7fffffff;
     uint32_t bad = 0;
+    // the first tile (the whole chunk unless V is huge) stays in registers for
+    // both passes
+    float v0[VU];
+    load_tile(z, c0, c1, v0);
     for (int base = c0; base < c1; base += VT * VU) {
         float v[VU];
-        load_tile(z, base, c1, v);
+        if (base == c0) {
+#pragma unroll
+            for (int u = 0; u < VU; ++u) v[u] = v0[u];
+        } else {
+            load_tile(z, base, c1, v);
+        }
 #pragma unroll
         for (int u = 0; u < VU; ++u) {
             const int j = base + u * VT + tid;
@@ -314,7 +328,12 @@ __global__ __launch_bounds__(VT) void vs_chunk_kernel(const float* __restrict__ 
         double es = 0.0;
         for (int base = c0; base < c1; base += VT * VU) {
             float v[VU];
-            load_tile(z, base, c1, v);
+            if (base == c0) {
+#pragma unroll
+                for (int u = 0; u < VU; ++u) v[u] = v0[u];
+            } else {
+                load_tile(z, base, c1, v);
+            }
 #pragma unroll
             for (int u = 0; u < VU; ++u) {
                 const int j = base + u * VT + tid;
@@ -378,6 +397,15 @@ __global__ __launch_bounds__(VT) void vs_level2_kernel(const float* __restrict__
     __shared__ double f[VMAXP];
     const int w = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
     const RowView rv = row_view(ws, L, r);
+    const float* z = logits + (int64_t)r * L.V;
+    const int c0 = w * L.chunk, c1 = min(L.V, c0 + L.chunk);
+    // every independent load first (one memory round trip): the chunk's first
+    // tile of logits and e, this thread's level-1 slice, the chunk parts
+    float v0[VU];
+    double e0[VU], h1[HB / VT];
+    load_tile(z, c0, c1, v0);
+    load_tile((const double*)rv.e, c0, c1, e0);
+    load_slice(rv.h1, HB, h1);
     stage_parts(rv.part, L.P, sp);
     const RowMax mx = combine_max(sp, L.P);
     if (mx.bad || !(temperature > 0.0f)) return;
@@ -385,9 +413,7 @@ __global__ __launch_bounds__(VT) void vs_level2_kernel(const float* __restrict__
     const double E = combine_E(sp, L.P, mx.m, T, f);
     const double target = (double)top_p * E;
     double above1;
-    int b1 = descend(rv.h1, HB, 0.0, target, &above1, shd, shi);
-    const float* z = logits + (int64_t)r * L.V;
-    const int c0 = w * L.chunk, c1 = min(L.V, c0 + L.chunk);
+    int b1 = descend(h1, HB, 0.0, target, &above1, shd, shi);
     const double fw = f[w];
     for (int b = tid; b < HB; b += VT) hist[b] = 0.0;
     __syncthreads();
@@ -395,8 +421,13 @@ __global__ __launch_bounds__(VT) void vs_level2_kernel(const float* __restrict__
         for (int base = c0; base < c1; base += VT * VU) {
             float v[VU];
             double ev[VU];
-            load_tile(z, base, c1, v);
-            load_tile((const double*)rv.e, base, c1, ev);
+            if (base == c0) {
+#pragma unroll
+                for (int u = 0; u < VU; ++u) { v[u] = v0[u]; ev[u] = e0[u]; }
+            } else {
+                load_tile(z, base, c1, v);
+                load_tile((const double*)rv.e, base, c1, ev);
+            }
 #pragma unroll
             for (int u = 0; u < VU; ++u) {
                 if (base + u * VT + tid >= c1) break;
@@ -421,6 +452,15 @@ __global__ __launch_bounds__(VT) void vs_level3_kernel(const float* __restrict__
     __shared__ double f[VMAXP];
     const int w = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
     const RowView rv = row_view(ws, L, r);
+    const float* z = logits + (int64_t)r * L.V;
+    const int c0 = w * L.chunk, c1 = min(L.V, c0 + L.chunk);
+    // every independent load first (one memory round trip)
+    float v0[VU];
+    double e0[VU], h1[HB / VT], h2[HB / VT];
+    load_tile(z, c0, c1, v0);
+    load_tile((const double*)rv.e, c0, c1, e0);
+    load_slice(rv.h1, HB, h1);
+    load_slice(rv.h2, HB, h2);
     stage_parts(rv.part, L.P, sp);
     const RowMax mx = combine_max(sp, L.P);
     if (mx.bad || !(temperature > 0.0f)) return;
@@ -428,10 +468,8 @@ __global__ __launch_bounds__(VT) void vs_level3_kernel(const float* __restrict__
     const double E = combine_E(sp, L.P, mx.m, T, f);
     const double target = (double)top_p * E;
     double above1, above2 = 0.0;
-    int b1 = descend(rv.h1, HB, 0.0, target, &above1, shd, shi);
-    int b2 = (b1 >= 0) ? descend(rv.h2, HB, above1, target, &above2, shd, shi) : -1;
-    const float* z = logits + (int64_t)r * L.V;
-    const int c0 = w * L.chunk, c1 = min(L.V, c0 + L.chunk);
+    int b1 = descend(h1, HB, 0.0, target, &above1, shd, shi);
+    int b2 = (b1 >= 0) ? descend(h2, HB, above1, target, &above2, shd, shi) : -1;
     const double fw = f[w];
     for (int b = tid; b < HB3; b += VT) cnt[b] = 0u;
     __syncthreads();
@@ -444,8 +482,13 @@ __global__ __launch_bounds__(VT) void vs_level3_kernel(const float* __restrict__
     for (int base = c0; base < c1; base += VT * VU) {
         float v[VU];
         double ev[VU];
-        load_tile(z, base, c1, v);
-        load_tile((const double*)rv.e, base, c1, ev);
+        if (base == c0) {
+#pragma unroll
+            for (int u = 0; u < VU; ++u) { v[u] = v0[u]; ev[u] = e0[u]; }
+        } else {
+            load_tile(z, base, c1, v);
+            load_tile((const double*)rv.e, base, c1, ev);
+        }
 #pragma unroll
         for (int u = 0; u < VU; ++u) {
             if (base + u * VT + tid >= c1) break;
@@ -476,8 +519,17 @@ __global__ __launch_bounds__(HB3) void vs_finish_kernel(float temperature, float
     __shared__ ChunkSums ss[VMAXP];
     const int r = blockIdx.x, tid = threadIdx.x;
     const RowView rv = row_view(ws, L, r);
-    stage_parts(rv.part, L.P, sp);
-    for (int k = tid; k < L.P; k += blockDim.x) ss[k] = rv.sums[k];
+    // every independent load first (one memory round trip): this thread's
+    // level-3 bin over all chunks, the chunk parts and sums
+    uint32_t c3v[VMAXP];
+    if (top_p < 1.0f && temperature > 0.0f) {
+#pragma unroll
+        for (int i = 0; i < VMAXP; ++i) c3v[i] = (i < L.P) ? rv.c3[(int64_t)i * HB3 + tid] : 0u;
+    }
+    for (int k = tid; k < L.P; k += blockDim.x) {
+        sp[k] = rv.part[k];
+        ss[k] = rv.sums[k];
+    }
     __syncthreads();
     const RowMax mx = combine_max(sp, L.P);
     const double T = (double)temperature;
@@ -515,13 +567,8 @@ __global__ __launch_bounds__(HB3) void vs_finish_kernel(float temperature, float
     const uint32_t prefix = ss[0].pad;
     // level-3 bin b (thread b): one float value, mass = count * e(value)
     uint32_t c = 0;
-    {
-        uint32_t v[VMAXP];
 #pragma unroll
-        for (int i = 0; i < VMAXP; ++i) v[i] = (i < L.P) ? rv.c3[(int64_t)i * HB3 + tid] : 0u;
-#pragma unroll
-        for (int i = 0; i < VMAXP; ++i) c += v[i];
-    }
+    for (int i = 0; i < VMAXP; ++i) c += c3v[i];
     const float zb = key_f32((prefix << L3BITS) | (uint32_t)tid);
     const double eb = (c && prefix != 0x3fffffu) ? exp(((double)zb - (double)mx.m) / T) : 0.0;
     const double mass = (double)c * eb;
