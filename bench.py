@@ -228,8 +228,11 @@ def verify27b_workload(args):
     gen = torch.Generator(device=dev)
     gen.manual_seed(20261204)
     t0 = time.perf_counter()
-    log(f"generating the 64-layer W4 decoder (d=5120, GQA 40/8x128, FFN 17408) + LM head, KV context L={L}")
-    dec = Decoder(cfg, M, L + M + 8, gen=gen)
+    sweep_L = [] if args.no_context_sweep else [c for c in (1024, 8192, 32768) if c != L]
+    Lcap = max([L] + sweep_L)
+    log(f"generating the 64-layer W4 decoder (d=5120, GQA 40/8x128, FFN 17408) + LM head, KV cache for {Lcap} "
+        f"positions, timed context L={L}")
+    dec = Decoder(cfg, M, Lcap + M + 8, gen=gen)
     torch.cuda.synchronize()
     log(f"weights ready in {time.perf_counter() - t0:.1f} s ({dec.weight_bytes() / 1e9:.2f} GB W4)")
     V, d = cfg["V"], cfg["d"]
@@ -322,6 +325,38 @@ def verify27b_workload(args):
     per_launch_bytes = alg_gemm / n_launch
     achieved = per_launch_bytes / (gemm_launch_us * 1e-6) / 1e9
     step_bytes = dec.weight_bytes() + dec.kv_bytes(L, M)
+    # (e) the same step (graph, inputs copied in) and the M = 1 step at the
+    # other context lengths of the workload
+    ctx_sweep = {}
+    for Ls in sweep_L:
+        gs = vs.capture(x_s, Ls, q_s, d_s, T, top_p, seed, step_dev)
+        g1s = ar.capture(x1, Ls, None, None, T, top_p, seed, step1)
+        Ks = max(10, K // 4)
+        res_ms = []
+        for g_, one in ((gs, False), (g1s, True)):
+            for i in range(3):
+                g_.replay()
+            torch.cuda.synchronize()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            for i in range(Ks):
+                j = i % npool
+                if one:
+                    x1.copy_(xs[j][:1])
+                else:
+                    x_s.copy_(xs[j])
+                    q_s.copy_(qs[j])
+                    d_s.copy_(drafts[j])
+                g_.replay()
+            c1.record()
+            torch.cuda.synchronize()
+            res_ms.append(c0.elapsed_time(c1) / Ks)
+        sb = dec.weight_bytes() + dec.kv_bytes(Ls, M)
+        ctx_sweep[Ls] = {"ms_per_step": round(res_ms[0], 4), "steps_per_s": round(1e3 / res_ms[0], 2),
+                         "m1_ar_step_ms": round(res_ms[1], 4), "verify_over_ar": round(res_ms[0] / res_ms[1], 4),
+                         "step_hbm_gbs": round(sb / (res_ms[0] * 1e-3) / 1e9, 1)}
+        log(f"context {Ls}: {ctx_sweep[Ls]}")
+        del gs, g1s
     nacc = nacc_all.cpu().numpy()
     flags = flag_all.cpu().numpy()
     shapes = dict(dec.shapes)
@@ -354,6 +389,7 @@ def verify27b_workload(args):
         step_hbm_gbs=round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
         accepted_length_hist=np.bincount(np.clip(nacc, 0, D), minlength=D + 1).tolist(),
         flagged_steps=int(((flags & ~B.FLAG_NONFINITE) != 0).sum()),
+        context_sweep=ctx_sweep,
     )
     return res
 
@@ -768,6 +804,8 @@ def main():
     ap.add_argument("--workload", default="verify27b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--context", type=int, default=8192, help="KV context length L of the verify27b workload")
+    ap.add_argument("--no-context-sweep", action="store_true",
+                    help="verify27b: skip the extra timings at the other context lengths (1024, 8192, 32768)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -793,7 +831,8 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic", "config": res["config"], "roofline": res["roofline"]}
     for k in ("stages_us", "w4_gemm_by_linear", "accepted_length_hist", "flagged_steps", "m1_ar_step_ms",
-              "verify_over_ar", "step_hbm_gbs", "experts_per_step", "grouped_gemm_gbs", "m_sweep", "unit_note"):
+              "verify_over_ar", "step_hbm_gbs", "experts_per_step", "grouped_gemm_gbs", "m_sweep", "unit_note",
+              "context_sweep"):
         if k in res:
             out[k] = res[k]
     if not args.no_cpu_baseline:
