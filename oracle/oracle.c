@@ -93,6 +93,7 @@ EXPORT uint16_t oracle_bf16_round(double v) {
     uint16_t sign = (uint16_t)(signbit(v) ? 0x8000u : 0u);
     double x = fabs(v);
     if (isnan(v)) return (uint16_t)(sign | 0x7fc0u);
+    if (isinf(v)) return (uint16_t)(sign | 0x7f80u);   /* infinities are exact */
     if (x == 0.0) return sign;
     if (x < ldexp(1.0, -126)) {                    /* subnormal, ulp 2^-133 */
         double q = rint(x * ldexp(1.0, 133));      /* 0 .. 128 (128 = min normal) */

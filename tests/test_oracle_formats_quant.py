@@ -175,10 +175,25 @@ def test_bf16_rounding_matches_torch_on_fp32_values():
     hi = ((b + 1) << 16).view(np.float32).astype(np.float64)
     ties = ((lo + hi) / 2).astype(np.float32)
     sub = (np.arange(1, 300, dtype=np.uint32) << 13).view(np.float32)
-    allv = np.concatenate([vals, ties, sub, -vals[:100], np.array([0.0, 1.0, 3.389e38], np.float32)])
+    special = np.array([0.0, 1.0, 3.389e38, np.inf, -np.inf, np.finfo(np.float32).max,
+                        -np.finfo(np.float32).max], np.float32)
+    allv = np.concatenate([vals, ties, sub, -vals[:100], special])
     want = torch.from_numpy(allv).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     got = oracle.bf16_round(allv.astype(np.float64))
     assert np.array_equal(got, want)
+
+
+def test_bf16_rounding_of_random_fp32_words():
+    """One rounding to nearest, ties to even, on random binary32 words (every
+    exponent, both signs, infinities; NaN excluded), against torch's cast."""
+    import torch
+    g = np.random.default_rng(7)
+    u = g.integers(0, 2 ** 32, 200_000, dtype=np.uint64).astype(np.uint32)
+    u = np.concatenate([u, np.array([0x7f800000, 0xff800000, 0x7f7fffff, 0x7f7f8000], np.uint32)])
+    f = u.view(np.float32)
+    f = f[~np.isnan(f)]
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.bf16_round(f.astype(np.float64)), want)
 
 
 def test_bf16_double_rounding_case():
