@@ -235,9 +235,10 @@ VW4_API int vw4_add_sumsq(uint16_t* resid, const float* part, int32_t S, int64_t
 /* w4_skinny_gemm_partials with the RMSNorm folded into the activation load
  * (gist.science BaseRT summary, "メソドロジー": operator sequences fused so
  * that short kernels do not pay an extra round trip): the activations are
- * h = bf16(resid / sqrt(mean(resid^2) + eps) * gamma), computed per
- * workgroup from resid [M][K] bf16, gamma [K] bf16 and the sums of squares
- * vw4_add_sumsq left in norm_ws; h is bitwise what vw4_add_rmsnorm writes.
+ * h = bf16(resid / sqrt(mean(resid^2) + eps) * gamma), formed in registers
+ * as each group of 64 columns is consumed, from resid [M][K] bf16, gamma [K]
+ * bf16 and the sums of squares vw4_add_sumsq left in norm_ws; h is bitwise
+ * what vw4_add_rmsnorm writes.  K <= 16384 (at most 64 chunk sums per row).
  * Partials layout as vw4_gemm_partials_layout(M, N, K). */
 VW4_API int w4_skinny_gemm_rmsnorm_partials(const uint16_t* resid, const uint16_t* gamma, const void* norm_ws,
                                             float eps, const uint8_t* w_packed, const uint16_t* scales_packed,
@@ -255,8 +256,8 @@ VW4_API int w4_skinny_gemm_swiglu(const uint16_t* x, int64_t ldx, const uint8_t*
  * one W4 matrix of 2F rows packed in gate/up-interleaved order: rows
  * 64 t .. 64 t + 31 are the gate rows of features 32 t .. 32 t + 31 and rows
  * 64 t + 32 .. 64 t + 63 the up rows of the same features (F % 32 == 0).
- * The activations are normalised as in w4_skinny_gemm_rmsnorm_partials (each
- * workgroup covers all of K here, so this pays off for small K only). */
+ * The activations are normalised as in w4_skinny_gemm_rmsnorm_partials
+ * (K <= 16384). */
 VW4_API int w4_skinny_gemm_rmsnorm_swiglu(const uint16_t* resid, const uint16_t* gamma, const void* norm_ws,
                                           float eps, const uint8_t* w_packed, const uint16_t* scales_packed,
                                           uint16_t* a, int64_t lda, int32_t M, int32_t F, int32_t K, void* stream);
@@ -279,10 +280,12 @@ VW4_API int vw4_swiglu(const float* part, int32_t S, int64_t ldp, int32_t M, int
  * inside the verify rows); softmax(q k^T / sqrt(hd)) v, computed tile by tile
  * with an online softmax (gist.science BaseRT summary, "メソドロジー") on the
  * matrix cores: bf16 products, fp32 accumulation, the probabilities of the
- * P.V product split into a bf16 head and tail (about 16 significant bits).  q [M][nq][hd]; keys Kc [nkv][Lmax][hd]; values
+ * P.V product split into a bf16 head and tail (about 16 significant bits);
+ * the fewer than 32 positions past the last whole 32-position tile are added
+ * in the merge pass, in fp32.  q [M][nq][hd]; keys Kc [nkv][Lmax][hd]; values
  * transposed, Vt [nkv][hd][Lmax]; out [M][nq * hd] bf16.  hd == 128,
- * nq % nkv == 0, (nq / nkv) * M <= 48, Lmax % 8 == 0, q / Kc / Vt 16-byte
- * aligned.  Workspace: vw4_attn_workspace_bytes. */
+ * nq % nkv == 0, (nq / nkv) * M <= 48, Lmax % 8 == 0, L + M < 2^29, q / Kc /
+ * Vt 16-byte aligned.  Workspace: vw4_attn_workspace_bytes. */
 VW4_API size_t vw4_attn_workspace_bytes(int32_t M, int32_t nq, int32_t nkv, int32_t hd, int64_t ctx);
 VW4_API int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_t* Vt, int64_t Lmax, int64_t L,
                             int32_t M, int32_t nq, int32_t nkv, int32_t hd, uint16_t* out, void* ws, size_t ws_bytes,

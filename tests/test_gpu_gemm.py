@@ -154,7 +154,7 @@ def _rmsnorm_inputs(M, K, seed):
     return resid, gamma
 
 
-@pytest.mark.parametrize("M,N,K", [(4, 7168, 5120), (1, 100, 320), (6, 333, 1024), (8, 64, 5120), (3, 5120, 17408)])
+@pytest.mark.parametrize("M,N,K", [(4, 7168, 5120), (1, 100, 320), (6, 333, 1024), (8, 64, 5120), (3, 5120, 16384)])
 def test_rmsnorm_gemm_equals_norm_then_gemm(M, N, K):
     """The GEMM that normalises its own activations gives bitwise the partials
     of vw4_add_rmsnorm followed by the plain GEMM, and those match the oracle."""
@@ -183,6 +183,24 @@ def test_rmsnorm_gemm_equals_norm_then_gemm(M, N, K):
     y = host(p).reshape(S, M, ldp).astype(np.float64).sum(axis=0)[:, :N]
     oc, os_ = oracle.w4_quantize(w)
     assert gemm_rel_err(y, oracle.w4_gemm(hh, oc, os_)) <= GEMM_RTOL
+
+
+def test_rmsnorm_gemm_rejects_more_than_64_chunks():
+    """The normalising GEMMs take at most 64 chunk sums per row (K <= 16384):
+    K = 16448 is refused on the host, before any launch."""
+    import torch
+    M, N, K = 2, 64, 16448
+    resid = torch.zeros((M, K), dtype=torch.int16, device="cuda")
+    gamma = torch.zeros(K, dtype=torch.int16, device="cuda")
+    nws = B.workspace(B.norm_workspace_bytes(M, K))
+    packed = torch.zeros(N * K // 2, dtype=torch.uint8, device="cuda")
+    pscales = torch.zeros(N * K // 64, dtype=torch.int16, device="cuda")
+    part = torch.zeros(8 * M * (N + 64), dtype=torch.float32, device="cuda")
+    a = torch.zeros((M, 32), dtype=torch.int16, device="cuda")
+    with pytest.raises(B.VW4Error, match="K <= 16384"):
+        B.w4_skinny_gemm_rmsnorm_partials(resid, gamma, nws, 1e-6, packed, pscales, part, M, N, K)
+    with pytest.raises(B.VW4Error, match="K <= 16384"):
+        B.w4_skinny_gemm_rmsnorm_swiglu(resid, gamma, nws, 1e-6, packed, pscales, a, 32, M, 32, K)
 
 
 def _swiglu_ref(h_bits, w_gu, F):

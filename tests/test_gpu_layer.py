@@ -52,6 +52,37 @@ def test_add_rmsnorm(M, D, S):
     bf16_close(host(hd), h_ref)
 
 
+def test_bf16_rounding_of_fp32_bit_patterns():
+    """The kernels' fp32 -> bf16 conversion is round to nearest even: with a
+    zero residual and one partial, vw4_add_sumsq stores bf16(0 + p) = bf16(p).
+    2^20 patterns: random words plus ties (low half 0x8000, both parities),
+    carries into the exponent, overflow to infinity, subnormals and NaNs; each
+    finite one against the oracle's rounding of the same value, NaN -> NaN."""
+    import torch
+    M, D = 16, 65536
+    g = np.random.default_rng(20261203)
+    u = g.integers(0, 2 ** 32, size=M * D, dtype=np.uint64).astype(np.uint32)
+    hi = g.integers(0, 2 ** 16, size=M * D // 8, dtype=np.uint64).astype(np.uint32)
+    n = len(hi)
+    u[:n] = (hi << 16) | 0x8000                           # exact ties
+    u[n:2 * n] = (hi << 16) | g.integers(0x7f00, 0x8100, n).astype(np.uint32)   # near ties
+    u[2 * n:3 * n] = g.integers(0, 0x00800000, n).astype(np.uint32) | (hi & 0x8000) << 16   # subnormals
+    special = np.array([0x7f7fffff, 0x7f7f8000, 0x7f7f7fff, 0xff7fffff, 0x7f800000, 0xff800000, 0x7fc00000,
+                        0x7f800001, 0xffffffff, 0x00000001, 0x00008000, 0x00018000, 0x3f808000, 0x3f818000,
+                        0x3fffffff, 0x00000000], dtype=np.uint32)
+    u[3 * n:3 * n + len(special)] = special
+    u[u == 0x80000000] = 0                               # -0 + (+0) is +0: left out
+    f = u.view(np.float32).reshape(M, D)
+    resid = torch.zeros((M, D), dtype=torch.int16, device="cuda")
+    B.add_sumsq(resid, dev(f.reshape(1, M, D)), 1, D, M, D, B.workspace(B.norm_workspace_bytes(M, D)))
+    torch.cuda.synchronize()
+    got = host(resid).view(np.uint16).reshape(-1)
+    nan = np.isnan(f.reshape(-1))
+    assert np.all(((got & 0x7fff) > 0x7f80)[nan])
+    ref = oracle.bf16_round(f.reshape(-1)[~nan].astype(np.float64)).view(np.uint16)
+    assert np.array_equal(got[~nan], ref), int((got[~nan] != ref).sum())
+
+
 def test_rmsnorm_without_add():
     import torch
     M, D = 3, 5120
@@ -133,7 +164,8 @@ def _attn_case(M, nq, nkv, L, seed, Lmax=None):
 
 @pytest.mark.parametrize("M,nq,nkv,L", [(4, 40, 8, 0), (4, 40, 8, 100), (1, 40, 8, 1023), (4, 40, 8, 1024),
                                         (2, 8, 2, 777), (6, 10, 2, 300), (4, 40, 8, 8192), (8, 40, 8, 777),
-                                        (3, 40, 8, 31), (6, 40, 8, 2049), (1, 40, 8, 0), (4, 40, 8, 32764)])
+                                        (3, 40, 8, 31), (6, 40, 8, 2049), (1, 40, 8, 0), (4, 40, 8, 32764),
+                                        (4, 40, 8, 1051), (1, 40, 8, 30)])
 def test_decode_attn(M, nq, nkv, L):
     log(f"attn M={M} nq={nq} nkv={nkv} L={L}")
     q, Kc, Vc, out = _attn_case(M, nq, nkv, L, 1000 + L + M)
@@ -147,6 +179,24 @@ def test_decode_attn_context_ends_at_cache_end():
     q, Kc, Vc, out = _attn_case(M, nq, nkv, L, 55, Lmax=1024)
     ref = oracle.decode_attn(synth.bf16_bits_to_f32(q).astype(np.float64), Kc, Vc, L)
     bf16_close(out, ref)
+
+
+def test_decode_attn_ignores_cache_past_context():
+    """NaN in every cache position at or past L + M (stale memory) changes
+    nothing: 31 positions past the last whole tile (merge pass) and a partial
+    8-position piece."""
+    import torch
+    M, nq, nkv, L, hd = 4, 40, 8, 1051, 128
+    q, Kc, Vc, out = _attn_case(M, nq, nkv, L, 17)
+    Lmax = Kc.shape[1]
+    Kc2, Vc2 = Kc.copy(), Vc.copy()
+    Kc2[:, L + M:] = 0x7fc0
+    Vc2[:, L + M:] = 0xffc0
+    out2 = torch.empty((M, nq * hd), dtype=torch.int16, device="cuda")
+    ws = B.workspace(B.attn_workspace_bytes(M, nq, nkv, hd, L + M))
+    B.decode_attn(dev(q), dev(Kc2), dev(_vt(Vc2)), Lmax, L, M, nq, nkv, hd, out2, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out2).reshape(M, nq, hd), out)
 
 
 def test_decode_attn_causal_rows():

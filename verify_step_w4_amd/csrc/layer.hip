@@ -141,7 +141,11 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ p
 // transposed, Vt [nkv][128][Lmax] (a head dimension is one row of positions),
 // so that both contractions read 16-byte runs straight into MFMA operands.
 //
-// grid = (nkv, nparts), 4 wavefronts.  Workgroup (h, c) owns a contiguous
+// grid = (nkv, nparts), 4 wavefronts.  The context is cut into whole
+// 32-position tiles; the fewer than 32 positions past the last whole tile are
+// left to attn_combine_kernel, so that a context just past a multiple of the
+// tile count does not give one wavefront a second tile (measured: about 2 us
+// per launch).  Workgroup (h, c) owns a contiguous
 // range of 32-position tiles of KV head h and all QN = G * M queries that read
 // it (query j: head h * G + j / M, row j % M; row m sees positions
 // 0 .. L + m).  Wavefront w takes tiles w, w + 4, ... of the range; the next
@@ -159,7 +163,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ p
 //     bits; B = 16 bytes of a Vt row).
 // The four wavefronts merge pairwise in LDS ((w0 + w2) + (w1 + w3)), and the
 // workgroup writes one partial (m, l, o) per query; attn_combine_kernel
-// merges the partials in chunk order.
+// merges the partials in chunk order, then the remainder positions.
 // ---------------------------------------------------------------------------
 constexpr int AHD = 128;       // head dim handled
 constexpr int AQN = 48;        // max queries per KV head (G * M)
@@ -204,14 +208,23 @@ __device__ __forceinline__ void attn_load_v(AttnTile& T, const uint16_t* Vh, int
 #pragma unroll
         for (int db = 0; db < 8; ++db) T.v[db] = ld_bf16x8(Vh + (int64_t)(db * 16 + i) * Lmax + p8);
     } else {
-        // the context ends inside these 8 positions: zeros past it (their
-        // probabilities are 0, and 0 * NaN would not be)
+        // The context ends inside (or before) these 8 positions.  The 16 bytes
+        // are read from an 8-aligned start at most (ctx - 1) rounded down, which
+        // lies inside the row (Lmax % 8 == 0), and the positions at or past ctx
+        // are zeroed in registers (their probabilities are 0, and 0 * NaN would
+        // not be).
+        const int64_t last8 = (ctx - 1) & ~(int64_t)7;
+        const int64_t pl = p8 < last8 ? p8 : last8;
+        const int64_t nv64 = ctx - p8;
+        const int nv = nv64 < 0 ? 0 : (int)nv64;
+        u32x4v keep;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            keep[w] = (2 * w < nv ? 0x0000ffffu : 0u) | (2 * w + 1 < nv ? 0xffff0000u : 0u);
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-            uint16_t e8[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) e8[e] = (p8 + e < ctx) ? Vh[(int64_t)(db * 16 + i) * Lmax + p8 + e] : 0;
-            T.v[db] = __builtin_bit_cast(bf16x8, e8);
+            const u32x4v raw = *(const u32x4v*)(Vh + (int64_t)(db * 16 + i) * Lmax + pl);
+            T.v[db] = __builtin_bit_cast(bf16x8, raw & keep);
         }
     }
 }
@@ -341,7 +354,7 @@ __device__ __forceinline__ void attn_body(const uint16_t* __restrict__ q, const 
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, g = lane >> 4, i = lane & 15;
     const int64_t ctx = L + M;
-    const int tb = (int)((int64_t)c * ntiles / nparts), te = (int)((int64_t)(c + 1) * ntiles / nparts);
+    const int tb = c * ntiles / nparts, te = (c + 1) * ntiles / nparts;   // ntiles < 2^24: 32-bit division
     const uint16_t* Kh = Kc + (int64_t)h * Lmax * AHD;
     const uint16_t* Vh = Vt + (int64_t)h * AHD * Lmax;
 
@@ -437,26 +450,103 @@ __global__ __launch_bounds__(256) void attn_mfma_wide_kernel(
     attn_body<3>(q, Kc, Vt, Lmax, L, M, nq, G, ntiles, sl2e, ws_o, ws_ml);
 }
 
-// Merge the chunk partials of one (kv head, query): grid = (QN, nkv), AHD threads.
-__global__ __launch_bounds__(AHD) void attn_combine_kernel(const float* __restrict__ ws_o,
-                                                           const AttnPart* __restrict__ ws_ml, int nparts, int QN, int M,
-                                                           int nq, int G, uint16_t* __restrict__ out) {
-    __shared__ float s_f[64], s_l[64];
+// Merge the chunk partials of one (kv head, query) and add the positions
+// past the last whole tile (r0 .. ctx - 1, fewer than 32), which the tile
+// kernel leaves out so that its workgroups stay balanced: grid = (QN, nkv),
+// AHD threads.  The remainder is one more partial (scores and softmax in
+// fp32, base 2), merged after the chunks in position order.
+__global__ __launch_bounds__(AHD) void attn_combine_kernel(
+    const float* __restrict__ ws_o, const AttnPart* __restrict__ ws_ml, int nparts, int QN, int M, int nq, int G,
+    uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
+    const uint16_t* __restrict__ Vt, int64_t Lmax, int64_t L, int64_t r0, int64_t ctx, float sl2e) {
+    __shared__ float s_f[64], s_l[64], s_sc[AT];
+    __shared__ float s_mr;
     const int j = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+    const int row = j % M, head = h * G + j / M;
+    const int64_t lim = L + row;                      // last position this query sees
+    const int nr = (int)(ctx - r0);                   // 0 .. AT - 1
     const int64_t base = ((int64_t)h * QN + j) * nparts;
-    // the partial outputs are requested first, together with the chunk maxima
-    // and sums (one memory round trip)
+    // One memory round trip: the remainder's operands first (so that its
+    // scores can be formed while the rest is in flight), then the partial
+    // outputs and the chunk maxima and sums.
+    // Remainder scores: thread 4 k + qt takes dims 32 qt .. +32 of position
+    // r0 + k.  Its value-cache row d, positions r0 .. r0 + 31, comes in
+    // 8-position pieces whose start is clamped to the last 8-aligned start
+    // before ctx (inside the row: Lmax % 8 == 0); positions at or past ctx
+    // are never used.
+    // Every address is clamped to a valid one instead of the load being
+    // predicated, so that no branch separates the loads and each wait covers
+    // only the loads it needs.
+    const int k = d >> 2, qt = d & 3;
+    u32x4v kv[4], qv[4], vv[4];
+    {
+        const int64_t pk = r0 + k < ctx ? r0 + k : ctx - 1;
+        const u32x4v* kp = (const u32x4v*)(Kc + ((int64_t)h * Lmax + pk) * AHD + 32 * qt);
+        const u32x4v* qp = (const u32x4v*)(q + ((int64_t)row * nq + head) * AHD + 32 * qt);
+        const int64_t last8 = (ctx - 1) & ~(int64_t)7;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            kv[e] = kp[e];
+            qv[e] = qp[e];
+            const int64_t p8 = r0 + 8 * e < last8 ? r0 + 8 * e : last8;
+            vv[e] = *(const u32x4v*)(Vt + ((int64_t)h * AHD + d) * Lmax + p8);
+        }
+    }
+    // (then 40 of the partial outputs: the wait counter counts at most 63
+    // loads, so the remainder's scores are formed before the last 24 issue)
+    __builtin_amdgcn_sched_barrier(0);
+    // lanes d >= nparts repeat the last chunk: the maximum is unchanged and
+    // the sums below stop at nparts
+    const AttnPart ap = ws_ml[base + (d < nparts ? d : nparts - 1)];
     float o[64];
 #pragma unroll
-    for (int c = 0; c < 64; ++c) o[c] = (c < nparts) ? ws_o[(base + c) * AHD + d] : 0.0f;
-    // chunk maxima and sums: one chunk per thread (nparts <= 64), loads in parallel
+    for (int c = 0; c < 40; ++c) o[c] = ws_o[(base + (c < nparts ? c : nparts - 1)) * AHD + d];
+    __builtin_amdgcn_sched_barrier(0);
+    // (unconditional: with nr == 0 every score is -inf and nothing is added;
+    // a branch here would let the compiler sink the loads above into it)
+    float mr = -INFINITY, lr = 0.0f, orr = 0.0f;
+    {
+        float sc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                sc = fmaf(__uint_as_float(qv[e][w] << 16), __uint_as_float(kv[e][w] << 16), sc);
+                sc = fmaf(__uint_as_float(qv[e][w] & 0xffff0000u), __uint_as_float(kv[e][w] & 0xffff0000u), sc);
+            }
+        sc += __shfl_xor(sc, 1, 64);
+        sc += __shfl_xor(sc, 2, 64);
+        if (qt == 0) s_sc[k] = (k < nr && r0 + k <= lim) ? sc * sl2e : -INFINITY;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 40; c < 64; ++c) o[c] = ws_o[(base + (c < nparts ? c : nparts - 1)) * AHD + d];
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        for (int e = 0; e < nr; ++e) mr = fmaxf(mr, s_sc[e]);
+        const float mru = (mr == -INFINITY) ? 0.0f : mr;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int e = 8 * c + 2 * w + hf;
+                    if (e < nr) {
+                        const float p = __builtin_amdgcn_exp2f(s_sc[e] - mru);
+                        const float v = __uint_as_float(hf ? (vv[c][w] & 0xffff0000u) : (vv[c][w] << 16));
+                        lr += p;
+                        orr = fmaf(p, v, orr);
+                    }
+                }
+    }
+    // chunk maxima and sums: one chunk per thread (nparts <= 64)
     if (d < 64) {
-        const AttnPart ap = (d < nparts) ? ws_ml[base + d] : AttnPart{-INFINITY, 0.0f};
-        float mx = ap.m;
+        float mx = fmaxf(ap.m, mr);
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
         s_f[d] = (ap.m == -INFINITY) ? 0.0f : exp2f(ap.m - mx);
         s_l[d] = ap.l;
+        if (d == 0) s_mr = (mr == -INFINITY) ? 0.0f : exp2f(mr - mx);
     }
     __syncthreads();
     float lt = 0.0f, ot = 0.0f;
@@ -467,7 +557,9 @@ __global__ __launch_bounds__(AHD) void attn_combine_kernel(const float* __restri
             ot += s_f[c] * o[c];
         }
     }
-    const int row = j % M, head = h * G + j / M;
+    const float fr = s_mr;
+    lt += fr * lr;
+    ot += fr * orr;
     out[((int64_t)row * nq + head) * AHD + d] = f32_to_bf16(ot / lt);
 }
 
@@ -476,27 +568,46 @@ struct AttnPlan {
     size_t off_o, off_ml, total;
 };
 
-// 32-position tiles split evenly over nparts workgroups per KV head: about 4
-// tiles (one per wavefront) per workgroup, at most 64 partials per query
-// (measured on MI355X at 1k / 8k / 32k context: one tile in flight per
-// wavefront across many workgroups beats longer per-wavefront loops).
+// Compute units of the current device (cached per device).
+static int device_cus() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+constexpr int ATTN_MAX_PARTS = 64;
+
+// Whole 32-position tiles split evenly over nparts workgroups per KV head:
+// about one workgroup per compute unit over all KV heads, and at least two
+// tiles per workgroup (measured on MI355X from 512 to 32768 positions, M = 1
+// and 4: one workgroup per CU beats two, and fewer partials make the merge
+// cheaper).  The workspace is sized for ATTN_MAX_PARTS partials, so that its
+// size does not depend on the device or the tuning.
 static AttnPlan attn_plan(int M, int nq, int nkv, int64_t ctx) {
     AttnPlan p;
     p.QN = (nq / nkv) * M;
-    p.ntiles = (int)((ctx + AT - 1) / AT);
-    int tpw = 4;                                     // tiles per workgroup (tuning override below)
-    if (const char* e = getenv("VW4_ATTN_TILES")) {
+    p.ntiles = (int)(ctx / AT);                     // whole tiles; the rest goes to the combine
+    int np = (p.ntiles + 1) / 2;
+    int cap = device_cus() / nkv;
+    cap = cap < 1 ? 1 : (cap > ATTN_MAX_PARTS ? ATTN_MAX_PARTS : cap);
+    np = np > cap ? cap : np;
+    if (const char* e = getenv("VW4_ATTN_TILES")) {  // tuning override: tiles per workgroup
         const int v = atoi(e);
-        if (v >= 1 && v <= 1024) tpw = v;
+        if (v >= 1 && v <= 1 << 20) np = (p.ntiles + v - 1) / v;
     }
-    int np = (p.ntiles + tpw - 1) / tpw;
-    p.nparts = np < 1 ? 1 : (np > 64 ? 64 : np);
+    p.nparts = np < 1 ? 1 : (np > ATTN_MAX_PARTS ? ATTN_MAX_PARTS : np);
     size_t o = 0;
     p.off_o = o;
-    o += (size_t)nkv * p.QN * p.nparts * AHD * sizeof(float);
+    o += (size_t)nkv * p.QN * ATTN_MAX_PARTS * AHD * sizeof(float);
     o = (o + 255) / 256 * 256;
     p.off_ml = o;
-    o += (size_t)nkv * p.QN * p.nparts * sizeof(AttnPart);
+    o += (size_t)nkv * p.QN * ATTN_MAX_PARTS * sizeof(AttnPart);
     p.total = (o + 255) / 256 * 256;
     return p;
 }
@@ -589,6 +700,7 @@ int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_t* Vt, i
     const int QN = (nq / nkv) * M;
     VW4_REQUIRE(QN <= AQN, VW4_EUNSUPPORTED, "vw4_decode_attn: (nq/nkv)*M = %d > %d", QN, AQN);
     VW4_REQUIRE(L >= 0 && L + M <= Lmax, VW4_EINVAL, "vw4_decode_attn: L + M exceeds the cache");
+    VW4_REQUIRE(L + M < ((int64_t)1 << 29), VW4_EUNSUPPORTED, "vw4_decode_attn: context of 2^29 or more positions");
     VW4_REQUIRE(Lmax % 8 == 0, VW4_EINVAL, "vw4_decode_attn: Lmax must be a multiple of 8");
     VW4_REQUIRE(aligned(Kc, 16) && aligned(Vt, 16) && aligned(q, 16), VW4_EINVAL, "vw4_decode_attn: misaligned");
     const AttnPlan p = attn_plan(M, nq, nkv, L + M);
@@ -614,7 +726,8 @@ int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_t* Vt, i
                                sl2e, wo, wml);
             break;
     }
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(QN, nkv), dim3(AHD), 0, st, wo, wml, p.nparts, QN, M, nq, G, out);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(QN, nkv), dim3(AHD), 0, st, wo, wml, p.nparts, QN, M, nq, G, out, q,
+                       Kc, Vt, Lmax, L, (int64_t)p.ntiles * AT, L + M, sl2e);
     return check_launch("vw4_decode_attn");
 }
 

@@ -45,6 +45,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr int PF = 4;                  // groups in flight per lane
+constexpr int NORM_MAX_K = 64 * NORM_CHUNK;  // NORM mode: at most 64 chunk sums per row
 constexpr uint32_t NEG136_PAIR = 0xC308C308u;  // two bf16 -136.0
 
 // (v & mask) | magic in one instruction: gfx950's three-input bitwise op with
@@ -93,6 +94,19 @@ __device__ __forceinline__ void gemm_group(u32x4 wa, u32x4 wb, u32x4 xa, u32x4 x
         for (int r = 0; r < 4; ++r) acc[nb][r] = fmaf(f[nb], d[nb][r], acc[nb][r]);
 }
 
+// Eight activations of one row: h = bf16((r * inv) * gamma) per element, the
+// standalone normalisation's arithmetic in its order.
+__device__ __forceinline__ u32x4 norm8(u32x4 r, u32x4 g, float inv) {
+    u32x4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float rl = __uint_as_float(r[e] << 16), rh = __uint_as_float(r[e] & 0xffff0000u);
+        const float gl = __uint_as_float(g[e] << 16), gh = __uint_as_float(g[e] & 0xffff0000u);
+        h[e] = f32x2_to_bf16x2(rl * inv * gl, rh * inv * gh);
+    }
+    return h;
+}
+
 // Grouped (mixture-of-experts) launches: blockIdx.z is a slot; slots at or
 // beyond *n_slots exit at once; slot s multiplies expert slot_expert[s]
 // (weights at w_estride / s_estride per expert) with the activations at
@@ -120,8 +134,8 @@ struct NormIn {
     float eps;
 };
 
-// Modes: NORM = activations are rmsnorm(resid) * gamma, computed per
-// workgroup for its K range into LDS (dynamic shared memory [M][kw]);
+// Modes: NORM = the activations are h = bf16(rmsnorm(resid) * gamma), formed
+// in registers from the residual rows and gamma as each group is consumed;
 // SWIGLU = the matrix holds gate and up rows interleaved per 64-row tile
 // (rows 64 t .. +32: gate features 32 t .. +32; rows 64 t + 32 .. +32: the up
 // rows of the same features) and the workgroup, which then covers all of K
@@ -133,9 +147,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
                                                       int64_t ldy, int ydt, int M, int N, int G, int S_wg,
                                                       int S_grid, float* __restrict__ part, int64_t Npad,
                                                       uint32_t kmask, uint32_t kmagic, GemmGroup grp, NormIn nrm) {
-    extern __shared__ uint16_t hs[];     // NORM: this workgroup's rows of h, [M][kw]
     __shared__ float red[4][16][64];     // [wavefront][4 nb + r][lane]
-    __shared__ float s_inv[GEMM_MAX_M];
     if (grp.n_slots) {
         const int slot = blockIdx.z;
         if (slot >= __builtin_amdgcn_readfirstlane(*grp.n_slots)) return;
@@ -151,146 +163,104 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(const uint16_t* __restrict
     const int lane = tid & 63, kq = lane >> 4, i = lane & 15;
     const int t = blockIdx.x;
     const int S = S_wg * S_grid;
-    const int sw0 = blockIdx.y * S_wg;
-    const int gw0 = (int)((int64_t)sw0 * G / S);
-    const int s_idx = sw0 + wv;
-    const int g0 = (int)((int64_t)s_idx * G / S);
-    const int g1 = (int)((int64_t)(s_idx + 1) * G / S);
+    const int s_idx = blockIdx.y * S_wg + wv;
+    const int g0 = s_idx * G / S;               // S * G < 2^31: 32-bit division
+    const int g1 = (s_idx + 1) * G / S;
+    const int K = G * 64;
     const uint32_t magic_v = kmagic;  // lives in a VGPR for and_or()
     const int xr = i < M ? i : M - 1;  // A rows i >= M feed output rows that are never stored
+    if (NORM) {                        // A rows: the residual rows (row stride K)
+        x = nrm.resid;
+        ldx = K;
+    }
 
     // per-lane streams, advanced by one group per step
     const u32x4* wbase = wpk + (int64_t)t * G * 128 + lane;                  // + g * 128 (+ 64: second half)
     const uint2* sbase = (const uint2*)spk + (int64_t)t * G * 16 + i;         // + g * 16
     const u32x4* xbase = (const u32x4*)(x + (int64_t)xr * ldx) + kq;          // + g * 8 (+ 4: k half 1)
+    const u32x4* gbase = (const u32x4*)nrm.gamma + kq;                        // NORM: + g * 8 (+ 4)
 
     f32x4 acc[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // NORM, part 1: the per-chunk sums of squares of the residual rows (chunk
+    // = lane; row and chunk indexes clamped rather than the loads predicated,
+    // so that no branch separates them from their use) are requested before
+    // the weights.  Loads complete in issue order: waiting for these does not
+    // wait for the weight stream behind them.
+    float sv[GEMM_MAX_M];
+    if (NORM) {
+        const int lc = lane < nrm.nch ? lane : nrm.nch - 1;
+#pragma unroll
+        for (int m = 0; m < GEMM_MAX_M; ++m) sv[m] = nrm.ssq[(int64_t)(m < M ? m : M - 1) * nrm.nch + lc];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
     // PF groups in flight per lane, each in its own registers: the main loop
     // consumes buffer j and refills it with the group PF further on (clamped to
     // the slice's last group, so every load address is valid and the loop body
-    // has no branches); the last < PF groups are consumed after the loop.  The
-    // first loads are issued before the NORM prologue so they overlap it.
+    // has no branches); the last < PF groups are consumed after the loop.
     const int glast = g1 > g0 ? g1 - 1 : g0;
-    u32x4 bw0[PF], bw1[PF], bx0[PF], bx1[PF];
+    u32x4 bw0[PF], bw1[PF], bx0[PF], bx1[PF], bg0[PF], bg1[PF];
     uint2 bs[PF];
-    if (g0 < g1) {
-#pragma unroll
-        for (int j = 0; j < PF; ++j) {
-            const int gi = min(g0 + j, glast);
-            bw0[j] = __builtin_nontemporal_load(wbase + (int64_t)gi * 128);
-            bw1[j] = __builtin_nontemporal_load(wbase + (int64_t)gi * 128 + 64);
-            if (!NORM) {
-                bx0[j] = xbase[(int64_t)gi * 8];
-                bx1[j] = xbase[(int64_t)gi * 8 + 4];
-            }
-            bs[j] = sbase[(int64_t)gi * 16];
+    auto issue = [&](int j, int gi) {
+        bw0[j] = __builtin_nontemporal_load(wbase + (int64_t)gi * 128);
+        bw1[j] = __builtin_nontemporal_load(wbase + (int64_t)gi * 128 + 64);
+        bx0[j] = xbase[(int64_t)gi * 8];
+        bx1[j] = xbase[(int64_t)gi * 8 + 4];
+        if (NORM) {
+            bg0[j] = gbase[(int64_t)gi * 8];
+            bg1[j] = gbase[(int64_t)gi * 8 + 4];
         }
-    }
+        bs[j] = sbase[(int64_t)gi * 16];
+    };
+    // g0 < G always (S <= G), so these addresses are valid even for an empty slice
+#pragma unroll
+    for (int j = 0; j < PF; ++j) issue(j, min(g0 + j, glast));
+    __builtin_amdgcn_sched_barrier(0);
 
-    int kw = 0;
+    // NORM, part 2: the chunk sums (at most 64: K <= 64 * NORM_CHUNK) added in
+    // chunk order (lane values read back one by one), then this lane's row
+    // factor, computed as the standalone normalisation computes it
+    float inv = 1.0f;
     if (NORM) {
-        // One round trip: the sums of squares (wavefront 0, one chunk per
-        // lane) and this thread's first column of every row are requested
-        // together; the chunk sums are then added in chunk order.
-        const int gw1 = (int)((int64_t)(sw0 + S_wg) * G / S);
-        kw = (gw1 - gw0) * 64;
-        const int K = G * 64, nv = kw / 8;
-        const int bs_ = blockDim.x;
-        u32x4 gv = {0u, 0u, 0u, 0u}, rv[GEMM_MAX_M];
-        int c = tid;
-        if (c < nv) {
-            const int64_t k = (int64_t)gw0 * 64 + c * 8;
-            gv = *(const u32x4*)(nrm.gamma + k);
+        float tot[GEMM_MAX_M];
+#pragma unroll
+        for (int m = 0; m < GEMM_MAX_M; ++m) tot[m] = 0.0f;
+        for (int e = 0; e < nrm.nch; ++e)
 #pragma unroll
             for (int m = 0; m < GEMM_MAX_M; ++m)
-                if (m < M) rv[m] = *(const u32x4*)(nrm.resid + (int64_t)m * K + k);
-        }
-        if (wv == 0) {
-            float tot[GEMM_MAX_M];
+                tot[m] += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv[m]), e));
+        float tr = tot[0];
 #pragma unroll
-            for (int m = 0; m < GEMM_MAX_M; ++m) tot[m] = 0.0f;
-            for (int cb = 0; cb < nrm.nch; cb += 64) {
-                float sv[GEMM_MAX_M];
-#pragma unroll
-                for (int m = 0; m < GEMM_MAX_M; ++m)
-                    sv[m] = (m < M && cb + lane < nrm.nch) ? nrm.ssq[(int64_t)m * nrm.nch + cb + lane] : 0.0f;
-                const int ne = nrm.nch - cb < 64 ? nrm.nch - cb : 64;
-                for (int e = 0; e < ne; ++e)
-#pragma unroll
-                    for (int m = 0; m < GEMM_MAX_M; ++m)
-                        tot[m] += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sv[m]), e));
-            }
-#pragma unroll
-            for (int m = 0; m < GEMM_MAX_M; ++m)
-                if (lane == 0 && m < M) s_inv[m] = 1.0f / sqrtf(tot[m] / (float)K + nrm.eps);
-        }
-        __syncthreads();
-        for (; c < nv; c += bs_) {
-            const int64_t k = (int64_t)gw0 * 64 + c * 8;
-            if (c != tid) {                          // columns past the first: load now
-                gv = *(const u32x4*)(nrm.gamma + k);
-#pragma unroll
-                for (int m = 0; m < GEMM_MAX_M; ++m)
-                    if (m < M) rv[m] = *(const u32x4*)(nrm.resid + (int64_t)m * K + k);
-            }
-#pragma unroll
-            for (int m = 0; m < GEMM_MAX_M; ++m) {
-                if (m >= M) break;
-                const float inv = s_inv[m];
-                u32x4 hv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t rw = rv[m][e], gw = gv[e];
-                    const uint16_t lo = f32_to_bf16(bf16_to_f32((uint16_t)(rw & 0xffffu)) * inv *
-                                                    bf16_to_f32((uint16_t)(gw & 0xffffu)));
-                    const uint16_t hi = f32_to_bf16(bf16_to_f32((uint16_t)(rw >> 16)) * inv *
-                                                    bf16_to_f32((uint16_t)(gw >> 16)));
-                    hv[e] = (uint32_t)lo | ((uint32_t)hi << 16);
-                }
-                *(u32x4*)(hs + (int64_t)m * kw + c * 8) = hv;
-            }
-        }
-        __syncthreads();
+        for (int m = 1; m < GEMM_MAX_M; ++m) tr = xr == m ? tot[m] : tr;
+        inv = 1.0f / sqrtf(tr / (float)K + nrm.eps);
     }
-    // NORM: lane's activations of group g, k half s, from LDS
-    const u32x4* hrow = (const u32x4*)(hs + (int64_t)xr * kw) + kq;        // + (g - gw0) * 8 (+ 4)
 
+    auto consume = [&](int j) {
+        if (NORM) {
+            bx0[j] = norm8(bx0[j], bg0[j], inv);
+            bx1[j] = norm8(bx1[j], bg1[j], inv);
+        }
+        gemm_group(bw0[j], bw1[j], bx0[j], bx1[j], bs[j], kmask, magic_v, acc);
+    };
     if (g0 < g1) {
         int g = g0;
         for (; g + PF <= g1; g += PF) {
 #pragma unroll
             for (int j = 0; j < PF; ++j) {
-                if (NORM) {
-                    bx0[j] = hrow[(g + j - gw0) * 8];
-                    bx1[j] = hrow[(g + j - gw0) * 8 + 4];
-                }
-                gemm_group(bw0[j], bw1[j], bx0[j], bx1[j], bs[j], kmask, magic_v, acc);
-                const int gn = min(g + j + PF, glast);
+                consume(j);
                 // keep the refill right after its buffer's last use: the
                 // scheduler would otherwise sink all refills to the loop end
                 __builtin_amdgcn_sched_barrier(0);
-                bw0[j] = __builtin_nontemporal_load(wbase + (int64_t)gn * 128);
-                bw1[j] = __builtin_nontemporal_load(wbase + (int64_t)gn * 128 + 64);
-                if (!NORM) {
-                    bx0[j] = xbase[(int64_t)gn * 8];
-                    bx1[j] = xbase[(int64_t)gn * 8 + 4];
-                }
-                bs[j] = sbase[(int64_t)gn * 16];
+                issue(j, min(g + j + PF, glast));
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
         for (int j = 0; j < PF - 1; ++j)
-            if (g + j < g1) {
-                if (NORM) {
-                    bx0[j] = hrow[(g + j - gw0) * 8];
-                    bx1[j] = hrow[(g + j - gw0) * 8 + 4];
-                }
-                gemm_group(bw0[j], bw1[j], bx0[j], bx1[j], bs[j], kmask, magic_v, acc);
-            }
+            if (g + j < g1) consume(j);
     }
 
     // Reduce the S_wg slices of this workgroup in slice order.
@@ -409,39 +379,11 @@ static GemmPlan plan_gemm(int M, int N, int K, int slots = 1) {
     return p;
 }
 
-// Dynamic LDS beyond the default 64 KiB needs a per-kernel opt-in (gfx950 has
-// 160 KiB per workgroup); set once per kernel variant.
-template <bool NORM, bool SWIGLU>
-static int kernel_lds_optin(size_t lds) {
-    static size_t granted = 65536;
-    if (lds > granted) {
-        const hipError_t e = hipFuncSetAttribute((const void*)w4_gemm_kernel<NORM, SWIGLU>,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) {
-            set_error("w4 GEMM: cannot raise the dynamic LDS limit to %zu bytes: %s", lds, hipGetErrorString(e));
-            return VW4_EHIP;
-        }
-        granted = lds;
-    }
-    return VW4_OK;
-}
-
 template <bool NORM, bool SWIGLU>
 static int launch_kernel(const GemmPlan& p, int slots, hipStream_t st, const uint16_t* x, int64_t ldx,
                          const uint8_t* w, const uint16_t* s, void* y, int64_t ldy, int ydt, int M, int N, float* part,
                          const GemmGroup& grp, const NormIn& nrm) {
-    size_t lds = 0;
-    if (NORM) {
-        const int S = p.S_wg * p.S_grid;
-        const int kw = (p.S_wg * p.G + S - 1) / S * 64;   // the widest workgroup K range
-        lds = (size_t)M * kw * 2;
-        // 160 KiB per workgroup, less the static reduction buffer
-        VW4_REQUIRE(lds <= 160 * 1024 - 17 * 1024, VW4_EUNSUPPORTED,
-                    "w4 GEMM: normalised rows need %zu bytes of LDS", lds);
-        const int rc = kernel_lds_optin<NORM, SWIGLU>(lds);
-        if (rc) return rc;
-    }
-    hipLaunchKernelGGL((w4_gemm_kernel<NORM, SWIGLU>), dim3(p.ntiles, p.S_grid, slots), dim3(64 * p.S_wg), lds, st,
+    hipLaunchKernelGGL((w4_gemm_kernel<NORM, SWIGLU>), dim3(p.ntiles, p.S_grid, slots), dim3(64 * p.S_wg), 0, st,
                        x, ldx, (const u32x4*)w, s, y, ldy, ydt, M, N, p.G, p.S_wg, p.S_grid, part, p.Npad,
                        0x000F000Fu, 0x43004300u, grp, nrm);
     return VW4_OK;
@@ -502,8 +444,8 @@ int gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16
 // h = bf16(rmsnorm(resid) * gamma) (sums of squares from vw4_add_sumsq).
 int gemm_rmsnorm_partials(const uint16_t* resid, const uint16_t* gamma, const float* ssq, float eps,
                           const uint8_t* w, const uint16_t* s, float* part, int M, int N, int K, hipStream_t st) {
-    VW4_REQUIRE(M >= 1 && M <= GEMM_MAX_M && N >= 1 && K >= 64 && K % 64 == 0 && K <= 65536, VW4_EINVAL,
-                "w4_skinny_gemm_rmsnorm_partials: bad shape M=%d N=%d K=%d", M, N, K);
+    VW4_REQUIRE(M >= 1 && M <= GEMM_MAX_M && N >= 1 && K >= 64 && K % 64 == 0 && K <= NORM_MAX_K, VW4_EINVAL,
+                "w4_skinny_gemm_rmsnorm_partials: bad shape M=%d N=%d K=%d (K <= %d)", M, N, K, NORM_MAX_K);
     VW4_REQUIRE(resid && gamma && ssq && w && s && part, VW4_EINVAL, "w4_skinny_gemm_rmsnorm_partials: null pointer");
     VW4_REQUIRE(aligned(resid, 16) && aligned(gamma, 16) && aligned(w, 16) && aligned(s, 8) && aligned(part, 4),
                 VW4_EINVAL, "w4_skinny_gemm_rmsnorm_partials: misaligned pointer");
@@ -543,6 +485,7 @@ int gemm_swiglu(const uint16_t* x, int64_t ldx, const NormIn* nrm, const uint8_t
     if (nrm) {
         VW4_REQUIRE(nrm->resid && nrm->gamma && nrm->ssq && aligned(nrm->resid, 16) && aligned(nrm->gamma, 16),
                     VW4_EINVAL, "w4 GEMM + SwiGLU: bad normalisation inputs");
+        VW4_REQUIRE(K <= NORM_MAX_K, VW4_EINVAL, "w4 GEMM + SwiGLU: normalised rows need K <= %d", NORM_MAX_K);
         rc = launch_kernel<true, true>(p, slots, st, nullptr, K, w, s, a, lda, VW4_BF16, M, 2 * F, nullptr, grp,
                                        *nrm);
     } else {
