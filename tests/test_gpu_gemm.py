@@ -130,6 +130,19 @@ def test_gemm_layer_shapes_sampled(name):
     assert err.max() <= GEMM_RTOL, err.max()
 
 
+@pytest.mark.parametrize("M,N,K", [(3, 65600, 576), (4, 66000, 640), (1, 70000, 512)])
+def test_gemm_many_tiles_split_inside_workgroup(M, N, K):
+    """More than 1024 tiles of 64 rows: each workgroup splits K over several
+    wavefronts (3 here) and reduces in LDS; every output against the oracle."""
+    log(f"gemm many tiles M={M} N={N} K={K}")
+    w = _weights(11 * N + K, N, K)
+    x = synth.activations_bf16(M * 7 + N, M, K)
+    packed, pscales = B.w4_quantize_packed(dev(w))
+    y = host(_gemm(x, packed, pscales, M, N, K))
+    oc, os_ = oracle.w4_quantize(w)
+    assert gemm_rel_err(y, oracle.w4_gemm(x, oc, os_)) <= GEMM_RTOL
+
+
 @pytest.mark.slow
 def test_lm_head_large_vocab_sampled():
     """d=5120, V=151936 LM head at M=4, sampled outputs against the oracle."""

@@ -568,19 +568,6 @@ struct AttnPlan {
     size_t off_o, off_ml, total;
 };
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
-    static int cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] <= 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev] = n;
-    }
-    return cache[dev];
-}
-
 constexpr int ATTN_MAX_PARTS = 64;
 
 // Whole 32-position tiles split evenly over nparts workgroups per KV head:
