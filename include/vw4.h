@@ -226,6 +226,19 @@ VW4_API size_t vw4_norm_workspace_bytes(int32_t M, int32_t D);
 VW4_API int vw4_add_rmsnorm(uint16_t* resid, const float* part, int32_t S, int64_t ldp, const uint16_t* gamma,
                             float eps, int32_t M, int32_t D, uint16_t* h, void* ws, size_t ws_bytes, void* stream);
 
+/* vw4_add_rmsnorm in one launch, out of place: resid_out = bf16(resid_in +
+ * sum_s part) (part may be NULL: resid_out = resid_in) and h = bf16(
+ * rmsnorm(resid_out) * gamma), bitwise what vw4_add_rmsnorm gives.  Every
+ * workgroup forms its row's sums of squares itself (the same chunk sums, in
+ * the same order), so no second launch is needed; that is why the residual is
+ * written to another buffer (other workgroups still read resid_in).
+ * D % 4 == 0, 4 <= D <= 8192, M <= 64, S <= 8, ldp % 4 == 0; part 16-byte
+ * aligned, the rest 8-byte aligned; resid_in, resid_out and h must not
+ * overlap.  No workspace. */
+VW4_API int vw4_add_rmsnorm_out(const uint16_t* resid_in, const float* part, int32_t S, int64_t ldp,
+                                const uint16_t* gamma, float eps, int32_t M, int32_t D, uint16_t* resid_out,
+                                uint16_t* h, void* stream);
+
 /* The first half of vw4_add_rmsnorm alone: resid += sum_s part (bf16), and the
  * per-chunk sums of squares of the rounded rows into ws ([M][ceil(D / 256)]
  * floats, chunk order), for a GEMM that normalises its own activations. */

@@ -83,6 +83,54 @@ def test_bf16_rounding_of_fp32_bit_patterns():
     assert np.array_equal(got[~nan], ref), int((got[~nan] != ref).sum())
 
 
+@pytest.mark.parametrize("M,D,S", [(4, 5120, 8), (1, 5120, 1), (6, 1000, 3), (4, 2048, 0), (3, 8192, 8),
+                                   (2, 4, 1), (64, 260, 2)])
+def test_add_rmsnorm_out_equals_two_launch_path(M, D, S):
+    """The one-launch, out-of-place add + RMSNorm gives bitwise the residual
+    and h of vw4_add_rmsnorm (same chunk sums, same order), and matches the
+    oracle; resid_in is left unchanged."""
+    import torch
+    log(f"add_rmsnorm_out M={M} D={D} S={S}")
+    ldp = (D + 63) // 64 * 64
+    resid = synth.activations_bf16(M * 3 + D, M, D)
+    part = partials(S + D + 1, max(S, 1), M, D, ldp, 0.5)
+    gamma = synth.f32_to_bf16_bits(1.0 + synth.normal_f32(synth.rng(D + 5), (D,), 0.02))
+    pd = dev(part) if S else None
+    r1, h1 = dev(resid), torch.empty((M, D), dtype=torch.int16, device="cuda")
+    B.add_rmsnorm(r1, pd, max(S, 1), ldp, dev(gamma), 1e-6, M, D, h1, B.workspace(B.norm_workspace_bytes(M, D)))
+    rin = dev(resid)
+    r2, h2 = torch.full((M, D), 7, dtype=torch.int16, device="cuda"), torch.empty((M, D), dtype=torch.int16,
+                                                                                   device="cuda")
+    B.add_rmsnorm_out(rin, pd, max(S, 1), ldp, dev(gamma), 1e-6, M, D, r2, h2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(rin), resid)
+    assert np.array_equal(host(r2), host(r1))
+    assert np.array_equal(host(h2), host(h1))
+    exact = synth.bf16_bits_to_f32(resid).astype(np.float64)
+    if S:
+        exact = exact + part[:, :, :D].astype(np.float64).sum(axis=0)
+    bf16_close(host(r2), exact)
+    bf16_close(host(h2), oracle.rmsnorm(oracle.bf16_round(exact), gamma, 1e-6))
+
+
+def test_add_rmsnorm_out_rejects_bad_arguments():
+    import torch
+    M, D = 2, 1024
+    a = torch.zeros((M, 8200), dtype=torch.int16, device="cuda")
+    b = torch.zeros((M, 8200), dtype=torch.int16, device="cuda")
+    hh = torch.zeros((M, 8200), dtype=torch.int16, device="cuda")
+    g = torch.zeros(8200, dtype=torch.int16, device="cuda")
+    p = torch.zeros(9 * M * 8256, dtype=torch.float32, device="cuda")
+    with pytest.raises(B.VW4Error, match="D % 4 == 0"):
+        B.add_rmsnorm_out(a, None, 1, 1024, g, 1e-6, M, 1022, b, hh)
+    with pytest.raises(B.VW4Error, match="D <= 8192"):
+        B.add_rmsnorm_out(a, None, 1, 8196, g, 1e-6, M, 8196, b, hh)
+    with pytest.raises(B.VW4Error, match="S <= 8"):
+        B.add_rmsnorm_out(a, p, 9, 1024, g, 1e-6, M, D, b, hh)
+    with pytest.raises(B.VW4Error, match="must not overlap"):
+        B.add_rmsnorm_out(a, p, 1, 1024, g, 1e-6, M, D, a, hh)
+
+
 def test_rmsnorm_without_add():
     import torch
     M, D = 3, 5120

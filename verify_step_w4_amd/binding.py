@@ -67,6 +67,7 @@ SIGNATURES = {
     "vw4_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I64]),
     "vw4_decode_attn": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "vw4_add_sumsq": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _I32, _P, _SZ, _P]),
+    "vw4_add_rmsnorm_out": (ctypes.c_int, [_P, _P, _I32, _I64, _P, _F32, _I32, _I32, _P, _P, _P]),
     "w4_skinny_gemm_rmsnorm_partials": (ctypes.c_int, [_P, _P, _P, _F32, _P, _P, _P, _I32, _I32, _I32, _P]),
     "w4_skinny_gemm_rmsnorm_swiglu": (ctypes.c_int, [_P, _P, _P, _F32, _P, _P, _P, _I64, _I32, _I32, _I32, _P]),
     "w4_skinny_gemm_swiglu": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I64, _I32, _I32, _I32, _P]),
@@ -364,6 +365,14 @@ def moe_combine(part, S: int, ldp: int, p_sstride: int, row_slot, weights, M: in
     _check("vw4_moe_combine", lib().vw4_moe_combine(_ptr(part), S, ldp, p_sstride, _ptr(row_slot), _ptr(weights), M,
                                                     topk, D, _ptr(y), ldy, _stream(stream)))
     return y
+
+
+def add_rmsnorm_out(resid_in, part, S: int, ldp: int, gamma, eps: float, M: int, D: int, resid_out, h,
+                    stream=None):
+    _check("vw4_add_rmsnorm_out", lib().vw4_add_rmsnorm_out(_ptr(resid_in), _ptr(part), S, ldp, _ptr(gamma),
+                                                            float(eps), M, D, _ptr(resid_out), _ptr(h),
+                                                            _stream(stream)))
+    return resid_out, h
 
 
 def add_sumsq(resid, part, S: int, ldp: int, M: int, D: int, ws, stream=None):

@@ -20,34 +20,122 @@
 
 namespace vw4 {
 
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4v;
+
 // ---------------------------------------------------------------------------
-// residual add + RMSNorm in two launches over many workgroups:
-//   1. grid (ceil(D / NCOL), M): resid += partials (rounded to bf16), and the
-//      chunk's sum of squares of the rounded residual -> ws[m][chunk]
-//   2. grid (ceil(D / NCOL), M): total (chunk order) -> scale, h = bf16(...)
+// residual add + RMSNorm.  Chunk sums of squares: a chunk is NCOL = 256
+// columns; lane l of one wavefront holds columns 4 l .. 4 l + 3 (zero past
+// D), its value is v0^2 + v1^2 + v2^2 + v3^2 as the explicit fma chain below,
+// and the wavefront adds the 64 lane values (wave_sum).  The total is the sum
+// of the chunk sums in chunk order.  Every kernel forms them this way, so all
+// paths give bitwise the same h:
+//   - add_sumsq_kernel: resid += partials (bf16), chunk sums -> ws[m][chunk];
+//     then rmsnorm_apply_kernel (or the W4 GEMM's NORM mode) applies them;
+//   - add_rmsnorm_fused_kernel: one launch, out of place; every workgroup
+//     forms all of its row's chunk sums itself (reading the whole row, mostly
+//     from L2) and writes its own chunk of resid_out and h.
 // ---------------------------------------------------------------------------
-constexpr int NCOL = NORM_CHUNK;   // columns per workgroup (one per thread)
+constexpr int NCOL = NORM_CHUNK;   // columns per chunk
 constexpr int NMAXCH = 256; // chunks per row at most (D <= 65536)
 
-__global__ __launch_bounds__(NCOL) void add_sumsq_kernel(uint16_t* __restrict__ resid, const float* __restrict__ part,
-                                                         int S, int64_t ldp, int M, int D, float* __restrict__ ssq) {
-    __shared__ float red[NCOL / 64];
-    const int ch = blockIdx.x, m = blockIdx.y, d = ch * NCOL + threadIdx.x;
-    float v = 0.0f;
-    if (d < D) {
-        uint16_t* r = resid + (int64_t)m * D + d;
-        v = bf16_to_f32(*r);
-        if (part) {
-            v += sum_parts(part, S, M, ldp, m, d);
-            const uint16_t rb = f32_to_bf16(v);
-            *r = rb;
-            v = bf16_to_f32(rb);
+__device__ __forceinline__ float chunk_sumsq(const float (&v)[4]) {
+    return wave_sum(fmaf(v[3], v[3], fmaf(v[2], v[2], fmaf(v[1], v[1], v[0] * v[0]))));
+}
+
+// grid (ceil(D / NCOL), M), one wavefront per chunk.
+__global__ __launch_bounds__(64) void add_sumsq_kernel(uint16_t* __restrict__ resid, const float* __restrict__ part,
+                                                       int S, int64_t ldp, int M, int D, float* __restrict__ ssq) {
+    const int ch = blockIdx.x, m = blockIdx.y, lane = threadIdx.x;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int d = ch * NCOL + 4 * lane + e;
+        v[e] = 0.0f;
+        if (d < D) {
+            uint16_t* r = resid + (int64_t)m * D + d;
+            v[e] = bf16_to_f32(*r);
+            if (part) {
+                v[e] += sum_parts(part, S, M, ldp, m, d);
+                const uint16_t rb = f32_to_bf16(v[e]);
+                *r = rb;
+                v[e] = bf16_to_f32(rb);
+            }
         }
     }
-    float sq = wave_sum(v * v);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sq;
+    const float q = chunk_sumsq(v);
+    if (lane == 0) ssq[(int64_t)m * gridDim.x + ch] = q;
+}
+
+// One launch: resid_out = bf16(resid_in + sum_s part) and h for chunk
+// blockIdx.x of row blockIdx.y.  FN_WAVES wavefronts; wavefront w forms the
+// sums of chunks w, w + FN_WAVES, ... (at most FN_CPW each: nch <= 32).  All
+// loads are issued before any is used (row and slice indexes clamped, no
+// branches between them).  SS = number of partial slices (0: no add).
+constexpr int FN_WAVES = 8, FN_CPW = 4;
+template <int SS>
+__global__ __launch_bounds__(FN_WAVES * 64) void add_rmsnorm_fused_kernel(
+    const uint16_t* __restrict__ rin, const float* __restrict__ part, int64_t ldp, const uint16_t* __restrict__ gamma,
+    float eps, int M, int D, uint16_t* __restrict__ rout, uint16_t* __restrict__ h) {
+    __shared__ float s_ssq[FN_WAVES * FN_CPW];
+    const int ch = blockIdx.x, m = blockIdx.y, nch = gridDim.x;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int own_j = ch / FN_WAVES, own_w = ch % FN_WAVES;
+    uint2 rr[FN_CPW];
+    f32x4 pp[FN_CPW][SS > 0 ? SS : 1];
+    // gamma of this workgroup's own chunk (used by its owner wavefront)
+    const int gcol = ch * NCOL + 4 * lane < D ? ch * NCOL + 4 * lane : D - 4;
+    const uint2 gg = *(const uint2*)(gamma + gcol);
+#pragma unroll
+    for (int j = 0; j < FN_CPW; ++j) {
+        int c = w + FN_WAVES * j;
+        c = c < nch ? c : nch - 1;
+        int col = c * NCOL + 4 * lane;
+        col = col < D ? col : D - 4;                      // D % 4 == 0
+        rr[j] = *(const uint2*)(rin + (int64_t)m * D + col);
+#pragma unroll
+        for (int s = 0; s < SS; ++s) pp[j][s] = *(const f32x4*)(part + ((int64_t)s * M + m) * ldp + col);
+    }
+    float own[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < FN_CPW; ++j) {
+        const int c = w + FN_WAVES * j;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float x = bf16_to_f32((uint16_t)((e < 2 ? rr[j].x : rr[j].y) >> (16 * (e & 1))));
+            if (SS > 0) {
+                float sp = 0.0f;
+#pragma unroll
+                for (int s = 0; s < SS; ++s) sp += pp[j][s][e];
+                x = bf16_to_f32(f32_to_bf16(x + sp));
+            }
+            v[e] = (c < nch && c * NCOL + 4 * lane + e < D) ? x : 0.0f;
+        }
+        const float q = chunk_sumsq(v);
+        if (c < nch && lane == 0) s_ssq[c] = q;
+        if (j == own_j && w == own_w) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) own[e] = v[e];
+        }
+    }
     __syncthreads();
-    if (threadIdx.x == 0) ssq[(int64_t)m * gridDim.x + ch] = (red[0] + red[1]) + (red[2] + red[3]);
+    if (w != own_w) return;
+    float tot = 0.0f;
+    for (int c = 0; c < nch; ++c) tot += s_ssq[c];      // chunk order
+    const float inv = 1.0f / sqrtf(tot / (float)D + eps);
+    const int col = ch * NCOL + 4 * lane;
+    if (col >= D) return;
+    const float g[4] = {bf16_to_f32((uint16_t)(gg.x & 0xffffu)), bf16_to_f32((uint16_t)(gg.x >> 16)),
+                        bf16_to_f32((uint16_t)(gg.y & 0xffffu)), bf16_to_f32((uint16_t)(gg.y >> 16))};
+    uint2 ro, ho;
+    ro.x = f32x2_to_bf16x2(own[0], own[1]);
+    ro.y = f32x2_to_bf16x2(own[2], own[3]);
+    ho.x = f32x2_to_bf16x2(own[0] * inv * g[0], own[1] * inv * g[1]);
+    ho.y = f32x2_to_bf16x2(own[2] * inv * g[2], own[3] * inv * g[3]);
+    *(uint2*)(rout + (int64_t)m * D + col) = ro;
+    *(uint2*)(h + (int64_t)m * D + col) = ho;
 }
 
 __global__ __launch_bounds__(NCOL) void rmsnorm_apply_kernel(const uint16_t* __restrict__ resid,
@@ -170,9 +258,6 @@ constexpr int AQN = 48;        // max queries per KV head (G * M)
 constexpr int AT = 32;         // positions per tile
 constexpr int AWV = 4;         // wavefronts per workgroup
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4v;
 
 struct AttnPart {   // per (kv head, query, chunk): max (base 2), sum
     float m, l;
@@ -620,7 +705,7 @@ int vw4_add_rmsnorm(uint16_t* resid, const float* part, int32_t S, int64_t ldp, 
     VW4_REQUIRE(ws && ws_bytes >= need, VW4_EWORKSPACE, "vw4_add_rmsnorm: needs a workspace of %zu bytes", need);
     const int nch = (D + NCOL - 1) / NCOL;
     hipStream_t st = (hipStream_t)stream;
-    hipLaunchKernelGGL(add_sumsq_kernel, dim3(nch, M), dim3(NCOL), 0, st, resid, part, S, ldp, M, D, (float*)ws);
+    hipLaunchKernelGGL(add_sumsq_kernel, dim3(nch, M), dim3(64), 0, st, resid, part, S, ldp, M, D, (float*)ws);
     hipLaunchKernelGGL(rmsnorm_apply_kernel, dim3(nch, M), dim3(NCOL), 0, st, resid, gamma, eps, D, (const float*)ws,
                        nch, h);
     return check_launch("vw4_add_rmsnorm");
@@ -634,9 +719,45 @@ int vw4_add_sumsq(uint16_t* resid, const float* part, int32_t S, int64_t ldp, in
     const size_t need = vw4_norm_workspace_bytes(M, D);
     VW4_REQUIRE(ws && ws_bytes >= need, VW4_EWORKSPACE, "vw4_add_sumsq: needs a workspace of %zu bytes", need);
     const int nch = (D + NCOL - 1) / NCOL;
-    hipLaunchKernelGGL(add_sumsq_kernel, dim3(nch, M), dim3(NCOL), 0, (hipStream_t)stream, resid, part, S, ldp, M, D,
+    hipLaunchKernelGGL(add_sumsq_kernel, dim3(nch, M), dim3(64), 0, (hipStream_t)stream, resid, part, S, ldp, M, D,
                        (float*)ws);
     return check_launch("vw4_add_sumsq");
+}
+
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const char *pa = (const char*)a, *pb = (const char*)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+int vw4_add_rmsnorm_out(const uint16_t* resid_in, const float* part, int32_t S, int64_t ldp, const uint16_t* gamma,
+                        float eps, int32_t M, int32_t D, uint16_t* resid_out, uint16_t* h, void* stream) {
+    VW4_REQUIRE(resid_in && gamma && resid_out && h, VW4_EINVAL, "vw4_add_rmsnorm_out: null pointer");
+    VW4_REQUIRE(M >= 1 && M <= 64 && D >= 4 && D % 4 == 0 && D <= FN_WAVES * FN_CPW * NCOL, VW4_EINVAL,
+                "vw4_add_rmsnorm_out: need 1 <= M <= 64, D %% 4 == 0, 4 <= D <= %d (M=%d D=%d)",
+                FN_WAVES * FN_CPW * NCOL, M, D);
+    VW4_REQUIRE(!part || (S >= 1 && S <= 8 && ldp >= D && ldp % 4 == 0 && aligned(part, 16)), VW4_EINVAL,
+                "vw4_add_rmsnorm_out: partials need 1 <= S <= 8, ldp >= D, ldp %% 4 == 0, 16-byte alignment");
+    VW4_REQUIRE(aligned(resid_in, 8) && aligned(resid_out, 8) && aligned(h, 8) && aligned(gamma, 8), VW4_EINVAL,
+                "vw4_add_rmsnorm_out: resid_in, resid_out, h and gamma need 8-byte alignment");
+    VW4_REQUIRE(eps >= 0.0f, VW4_EINVAL, "vw4_add_rmsnorm_out: eps must be >= 0");
+    const size_t nb = (size_t)M * D * 2;
+    VW4_REQUIRE(!overlaps(resid_in, nb, resid_out, nb) && !overlaps(resid_in, nb, h, nb) &&
+                    !overlaps(resid_out, nb, h, nb),
+                VW4_EINVAL, "vw4_add_rmsnorm_out: resid_in, resid_out and h must not overlap");
+    const dim3 grid((D + NCOL - 1) / NCOL, M), blk(FN_WAVES * 64);
+    hipStream_t st = (hipStream_t)stream;
+    const int ss = part ? S : 0;
+    switch (ss) {
+#define VW4_FN_CASE(n)                                                                                         \
+    case n:                                                                                                  \
+        hipLaunchKernelGGL(add_rmsnorm_fused_kernel<n>, grid, blk, 0, st, resid_in, part, ldp, gamma, eps, M, D, \
+                           resid_out, h);                                                                    \
+        break;
+        VW4_FN_CASE(0) VW4_FN_CASE(1) VW4_FN_CASE(2) VW4_FN_CASE(3) VW4_FN_CASE(4) VW4_FN_CASE(5) VW4_FN_CASE(6)
+        VW4_FN_CASE(7) VW4_FN_CASE(8)
+#undef VW4_FN_CASE
+    }
+    return check_launch("vw4_add_rmsnorm_out");
 }
 
 int vw4_rope_kv_append(const float* part, int32_t S, int64_t ldp, int32_t M, int32_t nq, int32_t nkv, int32_t hd,

@@ -124,7 +124,10 @@ class Decoder:
             self.Vc.append(v)
         # activation buffers
         i16 = torch.int16
+        # two residual buffers: the one-launch add + RMSNorm writes the new
+        # residual out of place
         self.resid = torch.empty((M_max, d), dtype=i16, device=device)
+        self.resid2 = torch.empty((M_max, d), dtype=i16, device=device)
         self.h = torch.empty((M_max, d), dtype=i16, device=device)
         self.q = torch.empty((M_max, nq, hd), dtype=i16, device=device)
         self.attn = torch.empty((M_max, nq * hd), dtype=i16, device=device)
@@ -174,10 +177,22 @@ class Decoder:
         c = self.cfg
         d, nq, nkv, hd, F, eps = c["d"], c["nq"], c["nkv"], c["hd"], c["F"], c["eps"]
         assert 1 <= M <= self.M_max and L + M <= self.Lmax
-        resid, h = self.resid[:M], self.h[:M]
-        resid.copy_(x[:M])
+        h = self.h[:M]
+        bufs = (self.resid[:M], self.resid2[:M])
+        cur = [x[:M], 0]                 # current residual rows, next output buffer
+
+        def add_norm(part, S, ldp, gamma):
+            """resid <- resid + sum of the partials; h <- rmsnorm(resid) * gamma."""
+            out = bufs[cur[1]]
+            if d % 4 == 0 and d <= 8192 and (part is None or (S <= 8 and ldp % 4 == 0)):
+                B.add_rmsnorm_out(cur[0], part, S, ldp, gamma, eps, M, d, out, h, stream)
+            else:
+                out.copy_(cur[0])
+                B.add_rmsnorm(out, part, S, ldp, gamma, eps, M, d, h, self.norm_ws, stream)
+            cur[0], cur[1] = out, 1 - cur[1]
+
         lay = self.layers
-        B.add_rmsnorm(resid, None, 1, d, lay[0]["g1"], eps, M, d, h, self.norm_ws, stream)
+        add_norm(None, 1, d, lay[0]["g1"])
         for li, W in enumerate(lay):
             # attention block
             N, K = self.shapes["qkv"]
@@ -194,7 +209,7 @@ class Decoder:
             hook("pre", "o")
             B.w4_skinny_gemm_partials(self.attn, W["o"].packed, W["o"].pscales, self.parts["o"], M, N, K, stream)
             hook("post", "o")
-            B.add_rmsnorm(resid, self.parts["o"], S, ldp, W["g2"], eps, M, d, h, self.norm_ws, stream)
+            add_norm(self.parts["o"], S, ldp, W["g2"])
             # FFN block: gate|up with the SwiGLU in the GEMM epilogue
             N, K = self.shapes["gate_up"]
             hook("pre", "gate_up")
@@ -207,7 +222,7 @@ class Decoder:
                                       stream)
             hook("post", "down")
             g_next = lay[li + 1]["g1"] if li + 1 < len(lay) else self.final_gamma
-            B.add_rmsnorm(resid, self.parts["down"], S, ldp, g_next, eps, M, d, h, self.norm_ws, stream)
+            add_norm(self.parts["down"], S, ldp, g_next)
         hook("pre", "lm_head")
         B.w4_skinny_gemm(h, self.lm_head.packed, self.lm_head.pscales, self.logits[:M], M, c["V"], d,
                          ws=self.lm_ws, stream=stream)
@@ -420,8 +435,7 @@ class MoEVerify:
         hook = gemm_hook or (lambda when, name: None)
         M, d = self.M, self.d
         self.moe(x, router_logits, bank, stream, gemm_hook)
-        self.resid.copy_(x[:M])
-        B.add_rmsnorm(self.resid, self.y, 1, d, self.final_gamma, self.cfg["eps"], M, d, self.h, self.norm_ws, stream)
+        B.add_rmsnorm_out(x[:M], self.y, 1, d, self.final_gamma, self.cfg["eps"], M, d, self.resid, self.h, stream)
         hook("pre", "lm_head")
         B.w4_skinny_gemm(self.h, self.lm_head.packed, self.lm_head.pscales, self.logits, M, self.V, d, ws=self.lm_ws,
                          stream=stream)
