@@ -560,8 +560,13 @@ def moe_workload(args):
     torch.cuda.synchronize()
     ar_ms = a0.elapsed_time(a1) / K
     # (d) the W4 GEMM kernel by itself: each bank's 3 GEMM launches on its
-    # last routing, captured as graphs and replayed in turn
-    ms_launch, n_launch = time_graphs([(lambda k=k: mvs[k].gemm_pass(banks[k])) for k in range(nrot)], 50)
+    # last routing, banks in turn, four rounds, captured as one graph (so that
+    # the per-replay cost of a graph is spread over many launches) and replayed
+    def gemm_rounds(rounds=4):
+        return sum(mvs[k].gemm_pass(banks[k]) for _ in range(rounds) for k in range(nrot))
+
+    ms_launch, n_launch = time_graphs([gemm_rounds], 12)
+    n_launch //= 4
     ns_last = np.array([int(mv.n_slots.item()) for mv in mvs], dtype=np.float64)
     pass_bytes = float((ns_last * (eb_gu + eb_dn + M * F * 2 + M * F * 2 + M * d * 4)).sum()
                        + nrot * (M * d * 2 + lm_bytes))
