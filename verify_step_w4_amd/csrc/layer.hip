@@ -520,8 +520,9 @@ __device__ __forceinline__ void attn_body(const uint16_t* __restrict__ q, const 
     }
 }
 
-// Up to 32 queries per KV head: two workgroups per CU (no more than 256
-// registers per lane).  More queries: one workgroup per CU, no spills.
+// Up to 32 queries per KV head: at most 256 registers per lane, so that two
+// workgroups could share a CU (the plan launches about one per CU).  More
+// queries: one workgroup per CU, no spills.
 template <int NQB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vt, int64_t Lmax,

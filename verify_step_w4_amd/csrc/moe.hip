@@ -27,76 +27,107 @@ constexpr int MOE_MAX_M = 16;
 constexpr int MOE_KPL = MOE_MAX_E / 64;  // experts per lane
 
 // One workgroup of 4 wavefronts; wavefront w routes rows w, w + 4, ...
-// Selection: the key (order-preserving fp32 key << 32 | ~index) is unique per
-// expert, so a wavefront maximum names exactly one expert per round.
+// Selection key: the order-preserving fp32 key << 32 | ~index, unique per
+// expert, so the top-k are the k largest keys and their order is the
+// selection order.  With E <= MOE_RANK_E the keys go to LDS and every expert
+// counts the keys above its own (its rank) in parallel; otherwise k rounds of
+// a wavefront maximum pick them one by one.
+constexpr int MOE_RANK_E = 256;
 __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ logits, int M, int E, int topk,
                                                         int32_t* __restrict__ experts, float* __restrict__ weights,
                                                         int32_t* __restrict__ slot_expert,
                                                         int32_t* __restrict__ n_slots, int32_t* __restrict__ row_slot) {
     __shared__ int32_t slot_of[MOE_MAX_E];
     __shared__ int32_t sel[MOE_MAX_M * MOE_MAX_K];
-    __shared__ int32_t cnt[256];
+    __shared__ uint64_t s_key[4][MOE_RANK_E];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     for (int e = tid; e < E; e += 256) slot_of[e] = 0;
-    __syncthreads();
-    for (int m = w; m < M; m += 4) {
-        const float* l = logits + (int64_t)m * E;
+    const bool by_rank = E <= MOE_RANK_E;
+    // every wavefront runs the same number of row rounds (barriers inside)
+    for (int m0 = 0; m0 < M; m0 += 4) {
+        const int m = m0 + w;
+        const bool live = m < M;
+        const float* l = logits + (int64_t)(live ? m : 0) * E;
         uint64_t key[MOE_KPL];
 #pragma unroll
         for (int i = 0; i < MOE_KPL; ++i) {
             const int e = lane + 64 * i;
             key[i] = e < E ? ((uint64_t)f32_key(l[e]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e) : 0;
         }
-        int my_e = 0;
-        for (int t = 0; t < topk; ++t) {
-            uint64_t best = 0;
+        if (by_rank) {
 #pragma unroll
-            for (int i = 0; i < MOE_KPL; ++i) best = key[i] > best ? key[i] : best;
-            uint64_t wb = best;
+            for (int i = 0; i < MOE_RANK_E / 64; ++i)
+                if (lane + 64 * i < E) s_key[w][lane + 64 * i] = key[i];
+        }
+        __syncthreads();
+        if (live && by_rank) {
+            int r[MOE_RANK_E / 64];
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                const uint64_t o = __shfl_xor(wb, off, 64);
-                wb = o > wb ? o : wb;
+            for (int i = 0; i < MOE_RANK_E / 64; ++i) r[i] = 0;
+            for (int e2 = 0; e2 < E; ++e2) {
+                const uint64_t k2 = s_key[w][e2];
+#pragma unroll
+                for (int i = 0; i < MOE_RANK_E / 64; ++i) r[i] += k2 > key[i] ? 1 : 0;
             }
-            const int e = (int)(0xFFFFFFFFu - (uint32_t)wb);
 #pragma unroll
-            for (int i = 0; i < MOE_KPL; ++i)
-                if (key[i] == wb) key[i] = 0;
-            if (lane == t) my_e = e;
-            if (lane == 0) {
-                sel[m * MOE_MAX_K + t] = e;
-                slot_of[e] = 1;
+            for (int i = 0; i < MOE_RANK_E / 64; ++i) {
+                const int e = lane + 64 * i;
+                if (e < E && r[i] < topk) {
+                    sel[m * MOE_MAX_K + r[i]] = e;
+                    slot_of[e] = 1;
+                }
+            }
+        } else if (live) {
+            for (int t = 0; t < topk; ++t) {
+                uint64_t best = 0;
+#pragma unroll
+                for (int i = 0; i < MOE_KPL; ++i) best = key[i] > best ? key[i] : best;
+                uint64_t wb = best;
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) {
+                    const uint64_t o = __shfl_xor(wb, off, 64);
+                    wb = o > wb ? o : wb;
+                }
+                const int e = (int)(0xFFFFFFFFu - (uint32_t)wb);
+#pragma unroll
+                for (int i = 0; i < MOE_KPL; ++i)
+                    if (key[i] == wb) key[i] = 0;
+                if (lane == 0) {
+                    sel[m * MOE_MAX_K + t] = e;
+                    slot_of[e] = 1;
+                }
             }
         }
-        // weights: exp(l_e - l_top) in fp64 (l_top = the largest logit, chosen
-        // first), normalised over the chosen experts in selection order
-        const double top = (double)l[__shfl(my_e, 0, 64)];
-        const double pe = lane < topk ? exp((double)l[my_e] - top) : 0.0;
-        double den = 0.0;
-        for (int t = 0; t < topk; ++t) den += __shfl(pe, t, 64);
-        if (lane < topk) weights[m * topk + lane] = (float)(pe / den);
-    }
-    __syncthreads();
-    // slots in ascending expert order: thread tid scans experts [e0, e1)
-    const int per = (E + 255) / 256;
-    const int e0 = tid * per < E ? tid * per : E, e1 = e0 + per < E ? e0 + per : E;
-    int c = 0;
-    for (int e = e0; e < e1; ++e) c += slot_of[e];
-    cnt[tid] = c;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        const int v = tid >= off ? cnt[tid - off] : 0;
         __syncthreads();
-        cnt[tid] += v;
-        __syncthreads();
-    }
-    int s = cnt[tid] - c;  // exclusive prefix
-    for (int e = e0; e < e1; ++e)
-        if (slot_of[e]) {
-            slot_expert[s] = e;
-            slot_of[e] = s++;
+        if (live) {
+            // weights: exp(l_e - l_top) in fp64 (l_top = the largest logit,
+            // chosen first), normalised over the chosen experts in selection order
+            const int my_e = lane < topk ? sel[m * MOE_MAX_K + lane] : sel[m * MOE_MAX_K];
+            const double top = (double)l[sel[m * MOE_MAX_K]];
+            const double pe = lane < topk ? exp((double)l[my_e] - top) : 0.0;
+            double den = 0.0;
+            for (int t = 0; t < topk; ++t) den += __shfl(pe, t, 64);
+            if (lane < topk) weights[m * topk + lane] = (float)(pe / den);
         }
-    if (tid == 255) *n_slots = cnt[255];
+    }
+    __syncthreads();
+    // slots in ascending expert order: wavefront 0 counts the chosen experts
+    // 64 at a time (ballot + popcount)
+    if (w == 0) {
+        int base = 0;
+        for (int e0 = 0; e0 < E; e0 += 64) {
+            const int e = e0 + lane;
+            const bool chosen = e < E && slot_of[e] != 0;
+            const uint64_t mask = __ballot(chosen);
+            if (chosen) {
+                const int s = base + __popcll(mask & ((1ull << lane) - 1ull));
+                slot_expert[s] = e;
+                slot_of[e] = s;
+            }
+            base += __popcll(mask);
+        }
+        if (lane == 0) *n_slots = base;
+    }
     __syncthreads();
     for (int i = tid; i < M * topk; i += 256) {
         const int e = sel[(i / topk) * MOE_MAX_K + i % topk];
