@@ -33,16 +33,18 @@ constexpr int MOE_KPL = MOE_MAX_E / 64;  // experts per lane
 // counts the keys above its own (its rank) in parallel; otherwise k rounds of
 // a wavefront maximum pick them one by one.
 constexpr int MOE_RANK_E = 256;
+template <int KR>   // keys per lane ranked: E <= 64 * KR (rank path), 0: wavefront-maximum rounds
 __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ logits, int M, int E, int topk,
                                                         int32_t* __restrict__ experts, float* __restrict__ weights,
                                                         int32_t* __restrict__ slot_expert,
                                                         int32_t* __restrict__ n_slots, int32_t* __restrict__ row_slot) {
     __shared__ int32_t slot_of[MOE_MAX_E];
     __shared__ int32_t sel[MOE_MAX_M * MOE_MAX_K];
+    __shared__ float sel_l[MOE_MAX_M * MOE_MAX_K];   // their logits (from the keys)
     __shared__ uint64_t s_key[4][MOE_RANK_E];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     for (int e = tid; e < E; e += 256) slot_of[e] = 0;
-    const bool by_rank = E <= MOE_RANK_E;
+    constexpr bool by_rank = KR > 0;
     // every wavefront runs the same number of row rounds (barriers inside)
     for (int m0 = 0; m0 < M; m0 += 4) {
         const int m = m0 + w;
@@ -56,24 +58,30 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
         }
         if (by_rank) {
 #pragma unroll
-            for (int i = 0; i < MOE_RANK_E / 64; ++i)
+            for (int i = 0; i < KR; ++i)
                 if (lane + 64 * i < E) s_key[w][lane + 64 * i] = key[i];
         }
         __syncthreads();
         if (live && by_rank) {
-            int r[MOE_RANK_E / 64];
+            int r[KR > 0 ? KR : 1];
 #pragma unroll
-            for (int i = 0; i < MOE_RANK_E / 64; ++i) r[i] = 0;
-            for (int e2 = 0; e2 < E; ++e2) {
-                const uint64_t k2 = s_key[w][e2];
+            for (int i = 0; i < KR; ++i) r[i] = 0;
+            int e2 = 0;
+            for (; e2 + 2 <= E; e2 += 2) {     // two keys per LDS read
+                const uint64_t k2a = s_key[w][e2], k2b = s_key[w][e2 + 1];
 #pragma unroll
-                for (int i = 0; i < MOE_RANK_E / 64; ++i) r[i] += k2 > key[i] ? 1 : 0;
+                for (int i = 0; i < KR; ++i) r[i] += (k2a > key[i] ? 1 : 0) + (k2b > key[i] ? 1 : 0);
+            }
+            if (e2 < E) {
+#pragma unroll
+                for (int i = 0; i < KR; ++i) r[i] += s_key[w][e2] > key[i] ? 1 : 0;
             }
 #pragma unroll
-            for (int i = 0; i < MOE_RANK_E / 64; ++i) {
+            for (int i = 0; i < KR; ++i) {
                 const int e = lane + 64 * i;
                 if (e < E && r[i] < topk) {
                     sel[m * MOE_MAX_K + r[i]] = e;
+                    sel_l[m * MOE_MAX_K + r[i]] = key_f32((uint32_t)(key[i] >> 32));
                     slot_of[e] = 1;
                 }
             }
@@ -94,6 +102,7 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
                     if (key[i] == wb) key[i] = 0;
                 if (lane == 0) {
                     sel[m * MOE_MAX_K + t] = e;
+                    sel_l[m * MOE_MAX_K + t] = key_f32((uint32_t)(wb >> 32));
                     slot_of[e] = 1;
                 }
             }
@@ -102,9 +111,8 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
         if (live) {
             // weights: exp(l_e - l_top) in fp64 (l_top = the largest logit,
             // chosen first), normalised over the chosen experts in selection order
-            const int my_e = lane < topk ? sel[m * MOE_MAX_K + lane] : sel[m * MOE_MAX_K];
-            const double top = (double)l[sel[m * MOE_MAX_K]];
-            const double pe = lane < topk ? exp((double)l[my_e] - top) : 0.0;
+            const double top = (double)sel_l[m * MOE_MAX_K];
+            const double pe = lane < topk ? exp((double)sel_l[m * MOE_MAX_K + lane] - top) : 0.0;
             double den = 0.0;
             for (int t = 0; t < topk; ++t) den += __shfl(pe, t, 64);
             if (lane < topk) weights[m * topk + lane] = (float)(pe / den);
@@ -172,8 +180,19 @@ int vw4_moe_route(const float* logits, int32_t M, int32_t E, int32_t topk, int32
     VW4_REQUIRE(M >= 1 && M <= MOE_MAX_M && E >= 1 && E <= MOE_MAX_E && topk >= 1 && topk <= MOE_MAX_K && topk <= E,
                 VW4_EINVAL, "vw4_moe_route: need 1 <= M <= %d, 1 <= topk <= min(E, %d), E <= %d", MOE_MAX_M,
                 MOE_MAX_K, MOE_MAX_E);
-    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, logits, M, E, topk, experts,
-                       weights, slot_expert, n_slots, row_slot);
+    hipStream_t st = (hipStream_t)stream;
+    if (E <= 64)
+        hipLaunchKernelGGL(moe_route_kernel<1>, dim3(1), dim3(256), 0, st, logits, M, E, topk, experts, weights,
+                           slot_expert, n_slots, row_slot);
+    else if (E <= 128)
+        hipLaunchKernelGGL(moe_route_kernel<2>, dim3(1), dim3(256), 0, st, logits, M, E, topk, experts, weights,
+                           slot_expert, n_slots, row_slot);
+    else if (E <= MOE_RANK_E)
+        hipLaunchKernelGGL(moe_route_kernel<4>, dim3(1), dim3(256), 0, st, logits, M, E, topk, experts, weights,
+                           slot_expert, n_slots, row_slot);
+    else
+        hipLaunchKernelGGL(moe_route_kernel<0>, dim3(1), dim3(256), 0, st, logits, M, E, topk, experts, weights,
+                           slot_expert, n_slots, row_slot);
     return check_launch("vw4_moe_route");
 }
 
