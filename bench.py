@@ -169,6 +169,54 @@ def lm_head_workload(args):
     nacc = nacc_all.cpu().numpy()
     flags = flag_all.cpu().numpy()
     hist = np.bincount(np.clip(nacc, 0, D), minlength=D + 1).tolist()
+    # the statistics + acceptance stage at every (temperature, top_p) of the
+    # workload: its time as a replayed graph (verify_logits, spec_accept_ex,
+    # step advance on one set of logits, q and drafts), and the accepted-length
+    # histogram of 256 steps with fresh inputs (logits of the rotated heads)
+    sweep = {}
+    step_dev = torch.zeros(1, dtype=torch.int64, device=dev)
+    for Ts in (0.0, 0.6, 1.0):
+        for ps in (0.95, 1.0):
+            vs.gemm(xs[0], heads[0])
+            s_ = torch.cuda.Stream()
+            s_.wait_stream(torch.cuda.current_stream())
+
+            def stage(Ts=Ts, ps=ps):
+                B.verify_logits(None, None, None, M, V, d, Ts, ps, vs.logits, vs.stats, vs.stat_ws)
+                B.spec_accept_ex(vs.logits, 0, vs.stats, 0, qs[0], 0, drafts[0], 1, D, V, Ts, seed, step_dev,
+                                 vs.tokens, vs.n_acc, vs.flags, vs.acc_ws)
+                B.step_advance(step_dev, 1)
+
+            with torch.cuda.stream(s_):
+                stage()
+            torch.cuda.current_stream().wait_stream(s_)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                stage()
+            for _ in range(5):
+                g.replay()
+            torch.cuda.synchronize()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record()
+            for _ in range(50):
+                g.replay()
+            a1.record()
+            torch.cuda.synchronize()
+            us = a0.elapsed_time(a1) / 50 * 1e3
+            na = torch.empty(256, dtype=torch.int32, device=dev)
+            fl = torch.empty(256, dtype=torch.int32, device=dev)
+            for i in range(256):
+                j = i % nsteps_inputs
+                vs.gemm(xs[j], heads[i % ncopies])
+                vs.stats_and_accept(qs[j], drafts[j], Ts, ps, seed + 1, i, n_acc=na[i:i + 1], flags=fl[i:i + 1])
+            nh = na.cpu().numpy()
+            flh = fl.cpu().numpy()
+            sweep[f"T={Ts},top_p={ps}"] = {
+                "stats_and_accept_us": round(us, 2),
+                "accepted_length_hist_256": np.bincount(np.clip(nh, 0, D), minlength=D + 1).tolist(),
+                "flagged_steps": int(((flh & ~B.FLAG_NONFINITE) != 0).sum())}
+            log(f"T={Ts} top_p={ps}: {sweep[f'T={Ts},top_p={ps}']}")
     res = dict(
         ms_per_step=total_ms / K,
         value=K / (total_ms * 1e-3),
@@ -183,6 +231,7 @@ def lm_head_workload(args):
                    "stats_and_accept": round(total_ms / K * 1e3 - gemm_avg * 1e3, 2)},
         accepted_length_hist=hist,
         flagged_steps=int(((flags & ~B.FLAG_NONFINITE) != 0).sum()),
+        stats_accept_sweep=sweep,
     )
     return res
 
@@ -837,7 +886,7 @@ def main():
            "data": "synthetic", "config": res["config"], "roofline": res["roofline"]}
     for k in ("stages_us", "w4_gemm_by_linear", "accepted_length_hist", "flagged_steps", "m1_ar_step_ms",
               "verify_over_ar", "step_hbm_gbs", "experts_per_step", "grouped_gemm_gbs", "m_sweep", "unit_note",
-              "context_sweep"):
+              "context_sweep", "stats_accept_sweep"):
         if k in res:
             out[k] = res[k]
     if not args.no_cpu_baseline:
