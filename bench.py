@@ -171,7 +171,8 @@ def lm_head_workload(args):
     hist = np.bincount(np.clip(nacc, 0, D), minlength=D + 1).tolist()
     # the statistics + acceptance stage at every (temperature, top_p) of the
     # workload: its time as a replayed graph (verify_logits, spec_accept_ex,
-    # step advance on one set of logits, q and drafts), and the accepted-length
+    # step advance on one set of logits, q and drafts; 8 stages per graph),
+    # and the accepted-length
     # histogram of 256 steps with fresh inputs (logits of the rotated heads)
     sweep = {}
     step_dev = torch.zeros(1, dtype=torch.int64, device=dev)
@@ -191,19 +192,22 @@ def lm_head_workload(args):
                 stage()
             torch.cuda.current_stream().wait_stream(s_)
             torch.cuda.synchronize()
+            # 8 stages per graph, so that the cost of launching a graph from
+            # the host does not show in the per-stage time
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                stage()
-            for _ in range(5):
+                for _ in range(8):
+                    stage()
+            for _ in range(3):
                 g.replay()
             torch.cuda.synchronize()
             a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a0.record()
-            for _ in range(50):
+            for _ in range(10):
                 g.replay()
             a1.record()
             torch.cuda.synchronize()
-            us = a0.elapsed_time(a1) / 50 * 1e3
+            us = a0.elapsed_time(a1) / 80 * 1e3
             na = torch.empty(256, dtype=torch.int32, device=dev)
             fl = torch.empty(256, dtype=torch.int32, device=dev)
             for i in range(256):

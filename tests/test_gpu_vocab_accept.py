@@ -117,7 +117,7 @@ def run_accept(z, q, drafts, T, top_p, seed, step0, shared=False):
 @pytest.mark.parametrize("V,D,T,top_p", [
     (16, 3, 0.6, 0.95), (1000, 3, 0.6, 0.95), (8192, 3, 0.6, 0.95), (8192, 1, 1.0, 1.0),
     (8192, 3, 0.0, 0.95), (151936, 3, 0.6, 0.95), (151936, 3, 1.0, 0.95), (151936, 0, 0.6, 0.95),
-    (5000, 7, 1.0, 0.95),
+    (5000, 7, 1.0, 0.95), (151936, 3, 0.0, 0.95), (1000, 7, 0.0, 1.0),
 ])
 def test_accept_matches_oracle(V, D, T, top_p):
     Bn = 48 if V > 10000 else 200
@@ -131,6 +131,10 @@ def test_accept_matches_oracle(V, D, T, top_p):
     ql[: Bn // 2, :, :] = z[: Bn // 2, :max(D, 1), :] / np.float32(max(T, 0.6))
     q = synth.softmax_f32(ql)[:, :D, :] if D else np.zeros((Bn, 0, V), np.float32)
     drafts = np.stack([synth.sample_drafts(g, q[b], 1)[0] for b in range(Bn)]) if D else np.zeros((Bn, 0), np.int32)
+    if T == 0.0 and D:
+        # greedy targets: half of the problems draft the argmax, so that
+        # acceptances occur whatever q is
+        drafts[: Bn // 2] = np.argmax(z[: Bn // 2, :D, :], axis=2).astype(np.int32)
     seed, step0 = synth.PHILOX_SEED_BASE + 3, 1000
     tok, nacc, fl = run_accept(z, q, drafts, T, top_p, seed, step0)
     mism = 0
@@ -169,6 +173,32 @@ def test_accept_special_cases():
     tok, nacc, fl = run_accept(z, qu, drafts2, 0.0, 0.95, 7, 0, shared=True)
     assert np.all(nacc[:32] == D) and np.all(nacc[32:] == 1)
     assert np.all(tok[:32] == am) and np.all(tok[32:, :2] == am[:2])
+
+
+def test_accept_greedy_residual_zero_and_cdf_ends():
+    """T = 0 (one-hot targets): a rejected draft whose row's q puts all its mass
+    on the argmax leaves R = 0, so the token falls back to the argmax with the
+    R-zero flag; the same step without that q gives the argmax unflagged.
+    Both against the oracle."""
+    V, D = 64, 2
+    M = D + 1
+    z = synth.synthetic_logits(11, M, V, 1.0)
+    am = np.argmax(z, axis=1)
+    q = np.zeros((D, V), dtype=np.float32)
+    q[0, am[0]] = 1.0
+    q[1, am[1]] = 1.0                               # all of row 1's mass on its argmax
+    drafts = np.tile(np.array([am[0], (am[1] + 5) % V], dtype=np.int32), (16, 1))
+    tok, nacc, fl = run_accept(z, q, drafts, 0.0, 0.95, 21, 0, shared=True)
+    assert np.all(nacc == 1)
+    assert np.all(tok[:, 0] == am[0]) and np.all(tok[:, 1] == am[1]) and np.all(tok[:, 2] == -1)
+    assert np.all(fl & B.FLAG_R_ZERO)
+    qu = np.full((D, V), 1.0 / V, dtype=np.float32)
+    tok2, nacc2, fl2 = run_accept(z, qu, drafts, 0.0, 0.95, 21, 0, shared=True)
+    assert np.all(nacc2 == 1) and np.all(tok2[:, 1] == am[1])
+    assert not np.any(fl2 & B.FLAG_R_ZERO)
+    for b in range(16):
+        otok, onacc, ofl, _ = oracle.spec_accept(z, q, drafts[b], 0.0, 0.95, 21, b)
+        assert onacc == int(nacc[b]) and list(otok) == list(tok[b]) and ofl == int(fl[b])
 
 
 def test_accept_non_finite_rows():

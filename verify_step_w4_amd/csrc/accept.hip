@@ -23,7 +23,8 @@
 // it with a block-wide fp64 prefix sum in index order and writes the tokens.
 // Kernel boundaries, not device-wide atomics, separate the phases (an atomic
 // counter costs tens of ns per arriving workgroup on this part).  Vocabularies
-// of at most 1024 entries use one 64-lane workgroup per problem and one launch.
+// of at most 1024 entries use one 64-lane workgroup per problem and one launch;
+// so does T == 0, whose outcome needs no pass over the vocabulary.
 #include <math.h>
 
 #include "common.h"
@@ -503,6 +504,49 @@ __global__ __launch_bounds__(NT) void accept_finish_kernel(AcceptArgs a) {
                        a.out_nacc + b, a.out_flags + b, sh, shi);
 }
 
+// T == 0: every target row is one-hot at its argmax a_i, so the outcome of the
+// general algorithm is known without a pass over the vocabulary.  Draft i is
+// accepted iff it is a_i (u * q < 1 always holds there); the residual row
+// k < D is max(0, 1 - q_k(a_k)) at a_k and 0 elsewhere (R == 0 falls back to
+// p_k, the same token); the bonus row samples a_D.  The CDF-boundary flag of
+// the general path reduces to u_res * R within 1e-9 * R of 0 or of R, the two
+// ends of the only nonzero mass.  grid (B), one wavefront per problem.
+__global__ __launch_bounds__(64) void accept_greedy_kernel(AcceptArgs a) {
+    __shared__ double s_u[2 * (AMAXD + 1)];
+    __shared__ vw4_rowstat s_st[AMAXD + 1];
+    const int64_t b = blockIdx.x;
+    const float* zb = a.logits + b * a.lstride;
+    const vw4_rowstat* sb = a.stats + b * a.sstride;
+    const float* qb = a.q ? a.q + b * a.qstride : nullptr;
+    const int32_t* db = a.draft + b * a.D;
+    const ProblemState ps =
+        problem_state<64>(zb, sb, qb, db, a.D, a.V, 0.0, a.seed, first_step(a) + (uint64_t)b, s_u, s_st);
+    if (ps.bad) {
+        write_bad(a, b);
+        return;
+    }
+    if (threadIdx.x != 0) return;
+    const int k = ps.k;
+    const int32_t y = s_st[k].argmax;
+    uint32_t flags = ps.flags;
+    double R = 1.0;
+    if (k < a.D) {
+        R = fmax(0.0, 1.0 - (double)qb[(int64_t)k * a.V + y]);
+        if (!(R > 0.0)) {
+            flags |= VW4_FLAG_R_ZERO;
+            R = 1.0;
+        }
+    }
+    const double target = s_u[2 * k + 1] * R;
+    if (fabs(target) < 1e-9 * R || fabs(target - R) < 1e-9 * R) flags |= VW4_FLAG_CDF_TIE;
+    int32_t* tb = a.out_tokens + b * (a.D + 1);
+    for (int i = 0; i < k; ++i) tb[i] = db[i];
+    tb[k] = y;
+    for (int i = k + 1; i <= a.D; ++i) tb[i] = -1;
+    a.out_nacc[b] = k;
+    a.out_flags[b] = flags;
+}
+
 __global__ void step_advance_kernel(uint64_t* step, uint64_t inc) { *step += inc; }
 
 static int spec_accept_impl(const float* logits, int64_t logits_bstride, const vw4_rowstat* stats,
@@ -532,6 +576,10 @@ static int spec_accept_impl(const float* logits, int64_t logits_bstride, const v
     a.states = (ProblemSlot*)((char*)ws + L.off_state);
     a.step_dev = step_dev;
     hipStream_t st = (hipStream_t)stream;
+    if (temperature == 0.0f) {
+        hipLaunchKernelGGL(accept_greedy_kernel, dim3((unsigned)B), dim3(64), 0, st, a);
+        return check_launch("spec_accept");
+    }
     const dim3 grid((unsigned)B, (unsigned)L.P);
     if (L.threads == 64) {
         hipLaunchKernelGGL(accept_chunk_kernel<64>, grid, dim3(64), 0, st, a);
