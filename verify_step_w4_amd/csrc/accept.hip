@@ -23,8 +23,9 @@
 // it with a block-wide fp64 prefix sum in index order and writes the tokens.
 // Kernel boundaries, not device-wide atomics, separate the phases (an atomic
 // counter costs tens of ns per arriving workgroup on this part).  Vocabularies
-// of at most 1024 entries use one 64-lane workgroup per problem and one launch;
-// so does T == 0, whose outcome needs no pass over the vocabulary.
+// of at most 1024 entries use one 64-lane workgroup per problem, up to 16384
+// one 512-lane workgroup, each in one launch; so does T == 0, whose outcome
+// needs no pass over the vocabulary.
 #include <math.h>
 
 #include "common.h"
@@ -32,6 +33,8 @@
 namespace vw4 {
 
 constexpr int AT = 256;          // threads per workgroup for large vocabularies
+constexpr int AT1 = 512;         // one workgroup per problem up to AT1 * 32 entries
+constexpr int ASH = AT1 / 64 + 4;  // block-reduction scratch
 constexpr int ACHUNK = 4096;     // vocabulary entries per workgroup
 constexpr int AMAXP = 64;
 constexpr int AMAXD = 7;
@@ -54,6 +57,10 @@ static AcceptLayout accept_layout(int B, int V) {
         L.P = 1;
         L.chunk = V;
         L.threads = 64;
+    } else if (V <= AT1 * 32) {
+        L.P = 1;
+        L.chunk = V;
+        L.threads = AT1;
     } else {
         L.threads = AT;
         L.chunk = ACHUNK;
@@ -366,15 +373,15 @@ __device__ void finish_problem(const float* __restrict__ zk, const vw4_rowstat& 
         __syncthreads();
         if (cand != 0x7fffffff && cand == best) {
             s_y = cand;
-            sh[6] = cp;
-            sh[7] = cc;
+            sh[NT / 64 + 1] = cp;
+            sh[NT / 64 + 2] = cc;
         }
         __syncthreads();
         if (s_y != 0x7fffffff) {
             found = true;
             y = s_y;
-            cprev = sh[6];
-            cy = sh[7];
+            cprev = sh[NT / 64 + 1];
+            cy = sh[NT / 64 + 2];
         }
     }
     if (threadIdx.x != 0) return;
@@ -427,8 +434,8 @@ __device__ __forceinline__ void write_bad(const AcceptArgs& a, int64_t b) {
 // otherwise it stores its chunk sums for accept_finish_kernel.
 template <int NT>
 __global__ __launch_bounds__(NT) void accept_chunk_kernel(AcceptArgs a) {
-    __shared__ double sh[8];
-    __shared__ int shi[8];
+    __shared__ double sh[ASH];
+    __shared__ int shi[ASH];
     __shared__ double s_u[2 * (AMAXD + 1)];
     __shared__ AcceptPart s_part;
     __shared__ vw4_rowstat s_st[AMAXD + 1];
@@ -475,8 +482,8 @@ __global__ __launch_bounds__(NT) void accept_chunk_kernel(AcceptArgs a) {
 // grid (B): combine the P chunk sums of problem b and sample its token.
 template <int NT>
 __global__ __launch_bounds__(NT) void accept_finish_kernel(AcceptArgs a) {
-    __shared__ double sh[8];
-    __shared__ int shi[8];
+    __shared__ double sh[ASH];
+    __shared__ int shi[ASH];
     __shared__ double s_u[2 * (AMAXD + 1)];
     __shared__ AcceptPart sp[AMAXP];
     const int64_t b = blockIdx.x;
@@ -583,6 +590,8 @@ static int spec_accept_impl(const float* logits, int64_t logits_bstride, const v
     const dim3 grid((unsigned)B, (unsigned)L.P);
     if (L.threads == 64) {
         hipLaunchKernelGGL(accept_chunk_kernel<64>, grid, dim3(64), 0, st, a);
+    } else if (L.threads == AT1) {
+        hipLaunchKernelGGL(accept_chunk_kernel<AT1>, grid, dim3(AT1), 0, st, a);
     } else {
         hipLaunchKernelGGL(accept_chunk_kernel<AT>, grid, dim3(AT), 0, st, a);
         if (L.P > 1) hipLaunchKernelGGL(accept_finish_kernel<AT>, dim3((unsigned)B), dim3(AT), 0, st, a);

@@ -630,6 +630,263 @@ __global__ __launch_bounds__(HB3) void vs_finish_kernel(float temperature, float
     stats[r] = s;
 }
 
+// ---------------------------------------------------------------------------
+// V <= RT * RU: one workgroup per row does every phase in LDS (one launch).
+// The arithmetic is that of the chunked path with a single chunk: e relative
+// to the row max, fixed-order block sums, the same three-level descent and
+// the same finish and flags.
+// ---------------------------------------------------------------------------
+constexpr int RT = 1024, RNW = RT / 64, RU = 16;
+constexpr int RHPT = HB / RT;            // level-1/2 bins per thread
+
+__device__ __forceinline__ double row_sum_f64(double v, double* sh) {
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double s = 0.0;
+#pragma unroll
+    for (int k = 0; k < RNW; ++k) s += sh[k];           // wavefront order
+    __syncthreads();
+    return s;
+}
+
+__device__ __forceinline__ uint32_t row_sum_u32(uint32_t v, uint32_t* sh) {
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint32_t s = 0;
+#pragma unroll
+    for (int k = 0; k < RNW; ++k) s += sh[k];
+    __syncthreads();
+    return s;
+}
+
+// Exclusive suffix sum over the RT threads (fixed order).
+__device__ __forceinline__ double row_suffix_excl(double v, double* sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    double s = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double t = __shfl_down(s, off, 64);
+        if (lane + off < 64) s += t;
+    }
+    if (lane == 0) sh[w] = s;
+    __syncthreads();
+    double later = 0.0;
+    for (int w2 = RNW - 1; w2 > w; --w2) later += sh[w2];
+    double ex = __shfl_down(s, 1, 64);
+    if (lane == 63) ex = 0.0;
+    __syncthreads();
+    return ex + later;
+}
+
+// Descend the HB bins in hist (LDS; thread t owns bins RHPT t .. +RHPT): the
+// largest bin b with above + sum_{b' >= b} H[b'] >= target, -1 if none (then
+// the lowest non-empty bin, as in the chunked path).
+__device__ int row_descend(const double* hist, double above, double target, double* new_above, double* sh,
+                           int* shi) {
+    const int b0 = threadIdx.x * RHPT;
+    double h[RHPT], mine = 0.0;
+#pragma unroll
+    for (int i = 0; i < RHPT; ++i) {
+        h[i] = hist[b0 + i];
+        mine += h[i];
+    }
+    const double later = row_suffix_excl(mine, sh);
+    if (threadIdx.x == 0) shi[0] = -1;
+    __syncthreads();
+    double cum = above + later;
+#pragma unroll
+    for (int i = RHPT - 1; i >= 0; --i) {
+        if (cum < target && cum + h[i] >= target) {
+            shi[0] = b0 + i;
+            sh[RNW] = cum;
+        }
+        cum += h[i];
+    }
+    __syncthreads();
+    int b = shi[0];
+    double na = (b >= 0) ? sh[RNW] : above;
+    __syncthreads();
+    if (b < 0) {
+        if (threadIdx.x == 0) shi[0] = 0x7fffffff;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < RHPT; ++i)
+            if (h[i] > 0.0) atomicMin(&shi[0], b0 + i);
+        __syncthreads();
+        b = shi[0];
+        if (b == 0x7fffffff) b = -1;
+        double mass_above = 0.0;
+#pragma unroll
+        for (int i = 0; i < RHPT; ++i)
+            if (b0 + i > b) mass_above += h[i];
+        na = above + row_sum_f64(mass_above, sh);
+    }
+    *new_above = na;
+    return b;
+}
+
+__global__ __launch_bounds__(RT) void vs_row_kernel(const float* __restrict__ logits, float temperature, float top_p,
+                                                    int V, vw4_rowstat* __restrict__ stats) {
+    __shared__ double hist[HB];
+    __shared__ uint32_t cnt[HB3];
+    __shared__ double sh[RNW + 4];
+    __shared__ float shf[2 * RNW];
+    __shared__ int shi[RNW + 4];
+    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const float* z = logits + (int64_t)r * V;
+    float v[RU];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+        const int j = u * RT + tid;
+        v[u] = (j < V) ? z[j] : 0.0f;
+    }
+    // max (lowest index on ties), min, non-finite
+    float lm = -INFINITY, lmn = INFINITY;
+    int li = 0x7fffffff;
+    uint32_t bad = 0;
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+        const int j = u * RT + tid;
+        if (j >= V) break;
+        if (!isfinite(v[u])) bad = 1;
+        lmn = fminf(lmn, v[u]);
+        if (v[u] > lm || (v[u] == lm && j < li)) { lm = v[u]; li = j; }
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        const float om = __shfl_xor(lm, off, 64);
+        const int oi = __shfl_xor(li, off, 64);
+        if (om > lm || (om == lm && oi < li)) { lm = om; li = oi; }
+        lmn = fminf(lmn, __shfl_xor(lmn, off, 64));
+    }
+    if (lane == 0) { shf[wv] = lm; shi[wv] = li; shf[RNW + wv] = lmn; }
+    __syncthreads();
+    float m = shf[0], mn = shf[RNW];
+    int am = shi[0];
+    for (int k = 1; k < RNW; ++k) {
+        if (shf[k] > m || (shf[k] == m && shi[k] < am)) { m = shf[k]; am = shi[k]; }
+        mn = fminf(mn, shf[RNW + k]);
+    }
+    __syncthreads();
+    const bool isbad = row_sum_u32(bad, (uint32_t*)shi) != 0;
+    const double T = (double)temperature;
+    vw4_rowstat s;
+    s.max_logit = m;
+    s.argmax = am;
+    s.pad = 0;
+    if (isbad || !(T > 0.0)) {
+        if (tid == 0) {
+            s.max_logit = isbad ? NAN : m;
+            s.tau = s.max_logit;
+            s.log_z = 0.0;
+            s.argmax = isbad ? -1 : am;
+            s.n_kept = isbad ? 0 : 1;
+            s.flags = isbad ? VW4_FLAG_NONFINITE : 0u;
+            stats[r] = s;
+        }
+        return;
+    }
+    double e[RU], es = 0.0;
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+        e[u] = (u * RT + tid < V) ? exp(((double)v[u] - (double)m) / T) : 0.0;
+        es += e[u];
+    }
+    const double E = row_sum_f64(es, sh);
+    if (!(top_p < 1.0f)) {
+        if (tid == 0) {
+            s.tau = mn;
+            s.log_z = log(E);
+            s.n_kept = V;
+            s.flags = 0;
+            stats[r] = s;
+        }
+        return;
+    }
+    const double target = (double)top_p * E;
+    // level 1
+    for (int b = tid; b < HB; b += RT) hist[b] = 0.0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < RU; ++u)
+        if (u * RT + tid < V) atomicAdd(&hist[f32_key(v[u]) >> (32 - L1BITS)], e[u]);
+    __syncthreads();
+    double above1, above2 = 0.0;
+    const int b1 = row_descend(hist, 0.0, target, &above1, sh, shi);
+    // level 2
+    for (int b = tid; b < HB; b += RT) hist[b] = 0.0;
+    __syncthreads();
+    if (b1 >= 0) {
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+            if (u * RT + tid >= V) break;
+            const uint32_t k = f32_key(v[u]);
+            if ((k >> (32 - L1BITS)) == (uint32_t)b1) atomicAdd(&hist[(k >> L3BITS) & (HB - 1)], e[u]);
+        }
+    }
+    __syncthreads();
+    const int b2 = (b1 >= 0) ? row_descend(hist, above1, target, &above2, sh, shi) : -1;
+    const uint32_t prefix = (b1 >= 0 && b2 >= 0) ? (((uint32_t)b1 << L2BITS) | (uint32_t)b2) : 0x3fffffu;
+    // level 3: counts inside the prefix, mass and count above it
+    for (int b = tid; b < HB3; b += RT) cnt[b] = 0u;
+    __syncthreads();
+    double sa = 0.0;
+    uint32_t na = 0;
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+        if (u * RT + tid >= V) break;
+        const uint32_t k = f32_key(v[u]);
+        const uint32_t hi = k >> L3BITS;
+        if (hi > prefix) { sa += e[u]; ++na; }
+        else if (hi == prefix) atomicAdd(&cnt[k & (HB3 - 1)], 1u);
+    }
+    const double above = row_sum_f64(sa, sh);
+    const uint32_t n_above = row_sum_u32(na, (uint32_t*)shi);
+    // finish (thread b = level-3 bin b): one float value per bin, mass = count * e(value)
+    static_assert(RT == HB3, "one thread per level-3 bin");
+    const uint32_t c = cnt[tid];
+    const float zb = key_f32((prefix << L3BITS) | (uint32_t)tid);
+    const double eb = (c && prefix != 0x3fffffu) ? exp(((double)zb - (double)m) / T) : 0.0;
+    const double mass = (double)c * eb;
+    const double cum_above = above + row_suffix_excl(mass, sh);  // mass of every key above this bin
+    __shared__ int s_b;
+    __shared__ double s_cum;
+    if (tid == 0) s_b = -1;
+    __syncthreads();
+    if (c && cum_above < target && cum_above + mass >= target) { s_b = tid; s_cum = cum_above; }
+    __syncthreads();
+    uint32_t flags = 0;
+    int b3 = s_b;
+    double G = s_cum;
+    if (b3 < 0) {
+        // steering missed the boundary by rounding: keep the nearest bin and flag it
+        flags |= VW4_FLAG_TOPP_TIE;
+        __shared__ int s_lo, s_hi;
+        if (tid == 0) { s_lo = 0x7fffffff; s_hi = -1; }
+        __syncthreads();
+        if (c) { atomicMin(&s_lo, tid); atomicMax(&s_hi, tid); }
+        __syncthreads();
+        b3 = (above >= target) ? s_hi : s_lo;
+        if (b3 < 0 || b3 >= HB3) b3 = 0;
+        G = 0.0;
+    }
+    __syncthreads();
+    // Z = mass above + bins >= b3 (block sum in wavefront order)
+    const double Zin = row_sum_f64((tid >= b3) ? mass : 0.0, sh);
+    const uint32_t nin = row_sum_u32((tid >= b3) ? c : 0u, (uint32_t*)shi);
+    if (tid != 0) return;
+    const double Z = above + Zin;
+    if (!(flags & VW4_FLAG_TOPP_TIE)) {
+        if (fabs(Z - target) < 1e-9 * E || fabs(G - target) < 1e-9 * E) flags |= VW4_FLAG_TOPP_TIE;
+    }
+    s.tau = key_f32((prefix << L3BITS) | (uint32_t)b3);
+    s.log_z = log(Z);
+    s.n_kept = (int32_t)(n_above + nin);
+    s.flags = flags;
+    stats[r] = s;
+}
+
 int gemm_dispatch(const uint16_t* x, int64_t ldx, const uint8_t* w, const uint16_t* s, void* y, int64_t ldy, int ydt,
                   int M, int N, int K, void* ws, size_t ws_bytes, hipStream_t st);
 size_t gemm_ws_bytes(int M, int N, int K);
@@ -667,6 +924,10 @@ int verify_logits(const uint16_t* hidden, int64_t ldh, const uint8_t* lm_packed,
         int rc = gemm_dispatch(hidden, ldh, lm_packed, lm_scales, logits, V, VW4_F32, rows, V, d,
                                gws ? (char*)ws + L.total : nullptr, gws, st);
         if (rc) return rc;
+    }
+    if (V <= RT * RU) {
+        hipLaunchKernelGGL(vs_row_kernel, dim3(rows), dim3(RT), 0, st, logits, temperature, top_p, V, stats);
+        return check_launch("verify_logits");
     }
     char* w = (char*)ws;
     const dim3 grid(L.P, rows), cgrid(HB / CB, rows);
