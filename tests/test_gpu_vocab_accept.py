@@ -42,7 +42,7 @@ def check_stats(z, T, top_p):
     return flagged
 
 
-@pytest.mark.parametrize("V", [1, 16, 1000, 8192, 151936])
+@pytest.mark.parametrize("V", [1, 16, 1000, 8192, 16384, 16385, 151936])
 @pytest.mark.parametrize("T,top_p", [(0.0, 0.95), (0.6, 0.95), (1.0, 0.95), (0.6, 1.0), (1.0, 0.5)])
 def test_stats_match_oracle(V, T, top_p):
     log(f"stats V={V} T={T} top_p={top_p}")
@@ -117,7 +117,7 @@ def run_accept(z, q, drafts, T, top_p, seed, step0, shared=False):
 @pytest.mark.parametrize("V,D,T,top_p", [
     (16, 3, 0.6, 0.95), (1000, 3, 0.6, 0.95), (8192, 3, 0.6, 0.95), (8192, 1, 1.0, 1.0),
     (8192, 3, 0.0, 0.95), (151936, 3, 0.6, 0.95), (151936, 3, 1.0, 0.95), (151936, 0, 0.6, 0.95),
-    (5000, 7, 1.0, 0.95), (151936, 3, 0.0, 0.95), (1000, 7, 0.0, 1.0),
+    (5000, 7, 1.0, 0.95), (151936, 3, 0.0, 0.95), (1000, 7, 0.0, 1.0), (16384, 3, 0.6, 0.95), (16385, 2, 1.0, 0.95),
 ])
 def test_accept_matches_oracle(V, D, T, top_p):
     Bn = 48 if V > 10000 else 200
