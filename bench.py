@@ -105,6 +105,135 @@ def time_graphs(issue_fns, reps):
     return e0.elapsed_time(e1) / (reps * n), n
 
 
+class Telemetry:
+    """Samples the GPU's clocks, temperatures and power through amdsmi in a
+    background thread (every `period` s) while the GPU works.  summary()
+    gives min / median / max of each metric and the change of the firmware's
+    throttle-residency counters over the run; if amdsmi is unavailable it
+    says why instead."""
+
+    FIELDS = (("gfxclk_mhz", "current_gfxclk", "current_gfxclks"), ("uclk_mhz", "current_uclk", None),
+              ("hotspot_c", "temperature_hotspot", None), ("hbm_c", "temperature_mem", None),
+              ("socket_power_w", "current_socket_power", None))
+    RESIDENCY = ("prochot_residency_acc", "ppt_residency_acc", "socket_thm_residency_acc",
+                 "vr_thm_residency_acc", "hbm_thm_residency_acc")
+
+    def __init__(self, period=0.25):
+        import threading
+        self.period, self.samples, self.error = period, [], None
+        self.first = self.last = None
+        self.stop_evt = threading.Event()
+        self.thread = None
+        try:
+            import amdsmi
+            import torch
+            amdsmi.amdsmi_init()
+            self.smi = amdsmi
+            handles = amdsmi.amdsmi_get_processor_handles()
+            p = torch.cuda.get_device_properties(0)
+            want = f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}"
+            self.handle = next((h for h in handles
+                                if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(want)), None)
+            if self.handle is None:
+                raise RuntimeError(f"no amdsmi device at PCI {want}")
+            self.first = self.last = amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        except Exception as e:  # telemetry is a report, never a reason to fail the bench
+            self.error = f"{type(e).__name__}: {e}"
+
+    @staticmethod
+    def _num(v):
+        if isinstance(v, (list, tuple)):
+            vals = [x for x in (Telemetry._num(y) for y in v) if x is not None]
+            return max(vals) if vals else None
+        return float(v) if isinstance(v, (int, float)) else None
+
+    def _run(self):
+        while not self.stop_evt.wait(self.period):
+            try:
+                m = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self.last = m
+            row = {}
+            for name, key, alt in self.FIELDS:
+                v = self._num(m.get(key))
+                if v is None and alt:
+                    v = self._num(m.get(alt))
+                row[name] = v
+            self.samples.append(row)
+
+    def start(self):
+        import threading
+        if self.error is None:
+            self.thread = threading.Thread(target=self._run, daemon=True)
+            self.thread.start()
+        return self
+
+    def stop(self):
+        if self.thread is not None:
+            self.stop_evt.set()
+            self.thread.join()
+        return self
+
+    def summary(self):
+        if not self.samples:
+            return {"unavailable": self.error or "no samples"}
+        import statistics
+        out = {"samples": len(self.samples), "period_s": self.period}
+        for name, _, _ in self.FIELDS:
+            vals = [s[name] for s in self.samples if s[name] is not None]
+            if vals:
+                out[name] = {"min": min(vals), "median": statistics.median(vals), "max": max(vals)}
+        n0, n1 = self._num(self.first.get("accumulation_counter")), self._num(self.last.get("accumulation_counter"))
+        if n0 is not None and n1 is not None and n1 > n0:
+            res = {}
+            for key in self.RESIDENCY:
+                a, b = self._num(self.first.get(key)), self._num(self.last.get(key))
+                if a is not None and b is not None:
+                    res[key.replace("_residency_acc", "")] = round((b - a) / (n1 - n0), 4)
+            out["throttle_residency_frac"] = res
+        if self.error:
+            out["error"] = self.error
+        return out
+
+
+def sustained_run(issue_step, ms_per_step, seconds, group=2):
+    """Replay one step (issue_step(i) enqueues step i) back to back for at
+    least `seconds` on the current stream while Telemetry samples the GPU.
+    A HIP event after every `group` steps gives samples of >= 10 ms each;
+    returns the median, p10 and p90 of ms per step over those samples, the
+    step rate of the first and last second, and the telemetry summary."""
+    import numpy as np
+    import torch
+    n = max(group * 30, int(np.ceil(seconds * 1e3 / ms_per_step / group)) * group)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n // group + 1)]
+    tel = Telemetry().start()
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(n):
+        issue_step(i)
+        if (i + 1) % group == 0:
+            evs[(i + 1) // group].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    tel.stop()
+    ms = np.array([evs[k].elapsed_time(evs[k + 1]) / group for k in range(len(evs) - 1)])
+    t_end = np.cumsum(ms * group)  # ms since the start, at the end of each sample
+
+    def rate(lo, hi):
+        sel = (t_end > lo) & (t_end <= hi)
+        return round(float(group * sel.sum() / (ms[sel] * group).sum() * 1e3), 2) if sel.any() else None
+
+    total = float(t_end[-1])
+    return {"steps": n, "seconds": round(total / 1e3, 2), "wall_s": round(wall, 2),
+            "ms_per_step": {"median": round(float(np.median(ms)), 4), "p10": round(float(np.percentile(ms, 10)), 4),
+                            "p90": round(float(np.percentile(ms, 90)), 4), "samples": len(ms),
+                            "steps_per_sample": group},
+            "steps_per_s_first_second": rate(0, 1000), "steps_per_s_last_second": rate(total - 1000, total),
+            "gpu_telemetry": tel.summary()}
+
+
 # --------------------------------------------------------------------------
 # LM-head verify workload
 # --------------------------------------------------------------------------
@@ -354,6 +483,20 @@ def verify27b_workload(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
+    sustained = None
+    if args.sustain > 0:
+        # the same replays for >= args.sustain seconds: spread of the step
+        # time, and the GPU's clocks / temperatures / power meanwhile
+
+        def issue(i):
+            j = i % npool
+            x_s.copy_(xs[j])
+            q_s.copy_(qs[j])
+            d_s.copy_(drafts[j])
+            graph.replay()
+
+        sustained = sustained_run(issue, total_ms / K, args.sustain)
+        log(f"sustained: {sustained}")
     # (c) the M = 1 autoregressive step on the same weights and context, same way
     x1 = xs[0][:1].clone()
     step1 = torch.zeros(1, dtype=torch.int64, device=dev)
@@ -444,6 +587,8 @@ def verify27b_workload(args):
         flagged_steps=int(((flags & ~B.FLAG_NONFINITE) != 0).sum()),
         context_sweep=ctx_sweep,
     )
+    if sustained is not None:
+        res["sustained"] = sustained
     return res
 
 
@@ -847,6 +992,21 @@ def lm_small_cpu_baseline(nsteps=200):
             "sample": f"{nsteps} whole small LM-head verify steps (d=1024, V=8192, M=4)"}
 
 
+def oracle_one_core(fn_name, **kw):
+    """Run the CPU-oracle baseline `fn_name(**kw)` of this file in a child
+    process limited to one host thread (OMP_NUM_THREADS=1); the child touches
+    no GPU.  Returns its result, or a note of why there is none."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    code = f"import json, bench; print(json.dumps(bench.{fn_name}(**{kw!r})))"
+    try:
+        r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                           timeout=600)
+        return json.loads(r.stdout.strip().splitlines()[-1])
+    except Exception as e:
+        return {"unavailable": f"{type(e).__name__}: {e}"}
+
+
 WORKLOADS = {"lm_head_verify": (lm_head_workload, lm_head_cpu_baseline),
              "verify27b": (verify27b_workload, verify27b_cpu_baseline),
              "moe_verify": (moe_workload, moe_cpu_baseline),
@@ -864,6 +1024,9 @@ def main():
     ap.add_argument("--context", type=int, default=8192, help="KV context length L of the verify27b workload")
     ap.add_argument("--no-context-sweep", action="store_true",
                     help="verify27b: skip the extra timings at the other context lengths (1024, 8192, 32768)")
+    ap.add_argument("--sustain", type=float, default=10.0,
+                    help="verify27b: seconds of back-to-back steps sampled for the step-time spread and the GPU's "
+                         "clocks / temperatures / power (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -890,12 +1053,17 @@ def main():
            "data": "synthetic", "config": res["config"], "roofline": res["roofline"]}
     for k in ("stages_us", "w4_gemm_by_linear", "accepted_length_hist", "flagged_steps", "m1_ar_step_ms",
               "verify_over_ar", "step_hbm_gbs", "experts_per_step", "grouped_gemm_gbs", "m_sweep", "unit_note",
-              "context_sweep", "stats_accept_sweep"):
+              "context_sweep", "stats_accept_sweep", "sustained"):
         if k in res:
             out[k] = res[k]
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu()
+        if args.workload == "verify27b":
+            log("timing the CPU oracle on one host thread")
+            one = oracle_one_core("verify27b_cpu_baseline", reps=1)
+            out["cpu_baseline"]["one_core"] = {k: one[k] for k in ("value", "cores", "sample", "unavailable")
+                                               if k in one}
     print(json.dumps(out), flush=True)
 
 
