@@ -69,27 +69,29 @@ __global__ __launch_bounds__(64) void add_sumsq_kernel(uint16_t* __restrict__ re
 }
 
 // One launch: resid_out = bf16(resid_in + sum_s part) and h for chunk
-// blockIdx.x of row blockIdx.y.  FN_WAVES wavefronts; wavefront w forms the
-// sums of chunks w, w + FN_WAVES, ... (at most FN_CPW each: nch <= 32).  All
-// loads are issued before any is used (row and slice indexes clamped, no
-// branches between them).  SS = number of partial slices (0: no add).
-constexpr int FN_WAVES = 8, FN_CPW = 4;
-template <int SS>
-__global__ __launch_bounds__(FN_WAVES * 64) void add_rmsnorm_fused_kernel(
+// blockIdx.x of row blockIdx.y.  nw = blockDim.x / 64 wavefronts, nw * CPW >=
+// nch (at most CPW - 1 idle slots in all); wavefront w forms the sums of
+// chunks w, w + nw, ... (CPW each).  All loads are issued before any is used
+// (row and slice indexes clamped, no branches between them).  SS = number of
+// partial slices (0: no add).
+constexpr int FN_MAXW = 11, FN_MAXCH = 32;
+template <int SS, int CPW>
+__global__ __launch_bounds__(FN_MAXW * 64) void add_rmsnorm_fused_kernel(
     const uint16_t* __restrict__ rin, const float* __restrict__ part, int64_t ldp, const uint16_t* __restrict__ gamma,
     float eps, int M, int D, uint16_t* __restrict__ rout, uint16_t* __restrict__ h) {
-    __shared__ float s_ssq[FN_WAVES * FN_CPW];
+    __shared__ float s_ssq[FN_MAXCH];
     const int ch = blockIdx.x, m = blockIdx.y, nch = gridDim.x;
+    const int nw = blockDim.x >> 6;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int own_j = ch / FN_WAVES, own_w = ch % FN_WAVES;
-    uint2 rr[FN_CPW];
-    f32x4 pp[FN_CPW][SS > 0 ? SS : 1];
+    const int own_j = ch / nw, own_w = ch % nw;
+    uint2 rr[CPW];
+    f32x4 pp[CPW][SS > 0 ? SS : 1];
     // gamma of this workgroup's own chunk (used by its owner wavefront)
     const int gcol = ch * NCOL + 4 * lane < D ? ch * NCOL + 4 * lane : D - 4;
     const uint2 gg = *(const uint2*)(gamma + gcol);
 #pragma unroll
-    for (int j = 0; j < FN_CPW; ++j) {
-        int c = w + FN_WAVES * j;
+    for (int j = 0; j < CPW; ++j) {
+        int c = w + nw * j;
         c = c < nch ? c : nch - 1;
         int col = c * NCOL + 4 * lane;
         col = col < D ? col : D - 4;                      // D % 4 == 0
@@ -99,8 +101,8 @@ __global__ __launch_bounds__(FN_WAVES * 64) void add_rmsnorm_fused_kernel(
     }
     float own[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < FN_CPW; ++j) {
-        const int c = w + FN_WAVES * j;
+    for (int j = 0; j < CPW; ++j) {
+        const int c = w + nw * j;
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -733,9 +735,9 @@ static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 int vw4_add_rmsnorm_out(const uint16_t* resid_in, const float* part, int32_t S, int64_t ldp, const uint16_t* gamma,
                         float eps, int32_t M, int32_t D, uint16_t* resid_out, uint16_t* h, void* stream) {
     VW4_REQUIRE(resid_in && gamma && resid_out && h, VW4_EINVAL, "vw4_add_rmsnorm_out: null pointer");
-    VW4_REQUIRE(M >= 1 && M <= 64 && D >= 4 && D % 4 == 0 && D <= FN_WAVES * FN_CPW * NCOL, VW4_EINVAL,
-                "vw4_add_rmsnorm_out: need 1 <= M <= 64, D %% 4 == 0, 4 <= D <= %d (M=%d D=%d)",
-                FN_WAVES * FN_CPW * NCOL, M, D);
+    VW4_REQUIRE(M >= 1 && M <= 64 && D >= 4 && D % 4 == 0 && D <= FN_MAXCH * NCOL, VW4_EINVAL,
+                "vw4_add_rmsnorm_out: need 1 <= M <= 64, D %% 4 == 0, 4 <= D <= %d (M=%d D=%d)", FN_MAXCH * NCOL,
+                M, D);
     VW4_REQUIRE(!part || (S >= 1 && S <= 8 && ldp >= D && ldp % 4 == 0 && aligned(part, 16)), VW4_EINVAL,
                 "vw4_add_rmsnorm_out: partials need 1 <= S <= 8, ldp >= D, ldp %% 4 == 0, 16-byte alignment");
     VW4_REQUIRE(aligned(resid_in, 8) && aligned(resid_out, 8) && aligned(h, 8) && aligned(gamma, 8), VW4_EINVAL,
@@ -745,14 +747,29 @@ int vw4_add_rmsnorm_out(const uint16_t* resid_in, const float* part, int32_t S, 
     VW4_REQUIRE(!overlaps(resid_in, nb, resid_out, nb) && !overlaps(resid_in, nb, h, nb) &&
                     !overlaps(resid_out, nb, h, nb),
                 VW4_EINVAL, "vw4_add_rmsnorm_out: resid_in, resid_out and h must not overlap");
-    const dim3 grid((D + NCOL - 1) / NCOL, M), blk(FN_WAVES * 64);
+    // Chunks per wavefront: 1 up to 8 chunks, 2 up to 16, then 3 (at most 11
+    // wavefronts).  Measured at D = 5120 (20 chunks) after the o and down
+    // GEMMs: 7 wavefronts of 3 chunks beat 10 of 2 and 5 of 4, and 8 of 4
+    // (12 clamped duplicate slots) by 0.7-0.9 us.
+    const int nch = (D + NCOL - 1) / NCOL;
+    const int cpw = nch <= 8 ? 1 : (nch <= 16 ? 2 : 3);
+    const int nw = (nch + cpw - 1) / cpw;
+    const dim3 grid(nch, M), blk(nw * 64);
     hipStream_t st = (hipStream_t)stream;
     const int ss = part ? S : 0;
-    switch (ss) {
-#define VW4_FN_CASE(n)                                                                                         \
-    case n:                                                                                                  \
-        hipLaunchKernelGGL(add_rmsnorm_fused_kernel<n>, grid, blk, 0, st, resid_in, part, ldp, gamma, eps, M, D, \
-                           resid_out, h);                                                                    \
+    switch (ss * 3 + (cpw - 1)) {
+#define VW4_FN_CASE(n)                                                                                        \
+    case 3 * n:                                                                                             \
+        hipLaunchKernelGGL((add_rmsnorm_fused_kernel<n, 1>), grid, blk, 0, st, resid_in, part, ldp, gamma, eps, M, \
+                           D, resid_out, h);                                                                \
+        break;                                                                                              \
+    case 3 * n + 1:                                                                                         \
+        hipLaunchKernelGGL((add_rmsnorm_fused_kernel<n, 2>), grid, blk, 0, st, resid_in, part, ldp, gamma, eps, M, \
+                           D, resid_out, h);                                                                \
+        break;                                                                                              \
+    case 3 * n + 2:                                                                                         \
+        hipLaunchKernelGGL((add_rmsnorm_fused_kernel<n, 3>), grid, blk, 0, st, resid_in, part, ldp, gamma, eps, M, \
+                           D, resid_out, h);                                                                \
         break;
         VW4_FN_CASE(0) VW4_FN_CASE(1) VW4_FN_CASE(2) VW4_FN_CASE(3) VW4_FN_CASE(4) VW4_FN_CASE(5) VW4_FN_CASE(6)
         VW4_FN_CASE(7) VW4_FN_CASE(8)
