@@ -113,11 +113,12 @@ __device__ __forceinline__ float sum_parts(const float* __restrict__ part, int S
     const float* p = part + (int64_t)m * ldp + c;
     for (int k0 = 0; k0 < S; k0 += 8) {
         float v[8];
+        // slice index clamped instead of the load predicated: no branch
+        // separates the loads (a branch would make the compiler wait for each)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (k0 + i < S) ? p[(int64_t)(k0 + i) * stride] : 0.0f;
+        for (int i = 0; i < 8; ++i) v[i] = p[(int64_t)(k0 + i < S ? k0 + i : S - 1) * stride];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (k0 + i < S) s += v[i];
+        for (int i = 0; i < 8; ++i) s += (k0 + i < S) ? v[i] : 0.0f;
     }
     return s;
 }

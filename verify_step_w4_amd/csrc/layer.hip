@@ -173,21 +173,47 @@ __global__ void rope_kv_kernel(const float* __restrict__ part, int S, int64_t ld
                                uint16_t* __restrict__ Vt, int64_t Lmax) {
     const int hh = blockIdx.x, m = blockIdx.y, d = threadIdx.x, half = hd / 2;
     const int64_t c0 = (int64_t)hh * hd;
-    const float a = sum_parts(part, S, M, ldp, m, c0 + d);
-    const float b = sum_parts(part, S, M, ldp, m, c0 + d + half);
     const int64_t pos = (int64_t)L + m;
-    if (hh >= nq + nkv) {  // value head: append as is
+    const bool vhead = hh >= nq + nkv;
+    // With S <= 8 the 2 S partial loads are all issued (slice index clamped,
+    // no branch between them) before the angle is computed, so the fp64 math
+    // runs while they are in flight; the sums are in slice order either way.
+    float pa[8], pb[8];
+    const float* p = part + (int64_t)m * ldp + c0 + d;
+    const int64_t pst = (int64_t)M * ldp;
+    if (S <= 8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t k = i < S ? i : S - 1;
+            pa[i] = p[k * pst];
+            pb[i] = p[k * pst + half];
+        }
+    }
+    // angle = pos * theta^(-2d/hd), in fp64 so that large positions keep their
+    // accuracy; the rotation itself in fp32 (value heads need none)
+    double sd = 0.0, cd = 1.0;
+    if (!vhead) {
+        const double ang = (double)pos * pow(theta, -2.0 * (double)d / (double)hd);
+        sincos(ang, &sd, &cd);
+    }
+    float a = 0.0f, b = 0.0f;
+    if (S <= 8) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            a += i < S ? pa[i] : 0.0f;
+            b += i < S ? pb[i] : 0.0f;
+        }
+    } else {
+        a = sum_parts(part, S, M, ldp, m, c0 + d);
+        b = sum_parts(part, S, M, ldp, m, c0 + d + half);
+    }
+    if (vhead) {  // value head: append as is
         const int kv = hh - nq - nkv;
         uint16_t* dst = Vt + (int64_t)kv * hd * Lmax + pos;     // transposed: [kv][dim][position]
         dst[(int64_t)d * Lmax] = f32_to_bf16(a);
         dst[(int64_t)(d + half) * Lmax] = f32_to_bf16(b);
         return;
     }
-    // angle = pos * theta^(-2d/hd), in fp64 so that large positions keep their
-    // accuracy; the rotation itself in fp32
-    const double ang = (double)pos * pow(theta, -2.0 * (double)d / (double)hd);
-    double sd, cd;
-    sincos(ang, &sd, &cd);
     const float c = (float)cd, s = (float)sd;
     const float ra = a * c - b * s, rb = b * c + a * s;
     if (hh < nq) {
