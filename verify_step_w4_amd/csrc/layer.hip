@@ -568,7 +568,9 @@ __global__ __launch_bounds__(256) void attn_mfma_wide_kernel(
 // past the last whole tile (r0 .. ctx - 1, fewer than 32), which the tile
 // kernel leaves out so that its workgroups stay balanced: grid = (QN, nkv),
 // AHD threads.  The remainder is one more partial (scores and softmax in
-// fp32, base 2), merged after the chunks in position order.
+// fp32, base 2), merged after the chunks in position order.  NPM >= nparts
+// is the number of partial slots each thread loads (16, 32 or 64).
+template <int NPM>
 __global__ __launch_bounds__(AHD) void attn_combine_kernel(
     const float* __restrict__ ws_o, const AttnPart* __restrict__ ws_ml, int nparts, int QN, int M, int nq, int G,
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
@@ -606,15 +608,17 @@ __global__ __launch_bounds__(AHD) void attn_combine_kernel(
             vv[e] = *(const u32x4v*)(Vt + ((int64_t)h * AHD + d) * Lmax + p8);
         }
     }
-    // (then 40 of the partial outputs: the wait counter counts at most 63
-    // loads, so the remainder's scores are formed before the last 24 issue)
+    // (then up to 40 of the partial outputs: the wait counter counts at most
+    // 63 loads, so with NPM = 64 the remainder's scores are formed before the
+    // last 24 issue)
+    constexpr int NP1 = NPM < 40 ? NPM : 40;
     __builtin_amdgcn_sched_barrier(0);
     // lanes d >= nparts repeat the last chunk: the maximum is unchanged and
     // the sums below stop at nparts
     const AttnPart ap = ws_ml[base + (d < nparts ? d : nparts - 1)];
-    float o[64];
+    float o[NPM];
 #pragma unroll
-    for (int c = 0; c < 40; ++c) o[c] = ws_o[(base + (c < nparts ? c : nparts - 1)) * AHD + d];
+    for (int c = 0; c < NP1; ++c) o[c] = ws_o[(base + (c < nparts ? c : nparts - 1)) * AHD + d];
     __builtin_amdgcn_sched_barrier(0);
     // (unconditional: with nr == 0 every score is -inf and nothing is added;
     // a branch here would let the compiler sink the loads above into it)
@@ -633,7 +637,7 @@ __global__ __launch_bounds__(AHD) void attn_combine_kernel(
         if (qt == 0) s_sc[k] = (k < nr && r0 + k <= lim) ? sc * sl2e : -INFINITY;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 40; c < 64; ++c) o[c] = ws_o[(base + (c < nparts ? c : nparts - 1)) * AHD + d];
+        for (int c = NP1; c < NPM; ++c) o[c] = ws_o[(base + (c < nparts ? c : nparts - 1)) * AHD + d];
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
         for (int e = 0; e < nr; ++e) mr = fmaxf(mr, s_sc[e]);
@@ -665,7 +669,7 @@ __global__ __launch_bounds__(AHD) void attn_combine_kernel(
     __syncthreads();
     float lt = 0.0f, ot = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 64; ++c) {
+    for (int c = 0; c < NPM; ++c) {
         if (c < nparts) {
             lt += s_f[c] * s_l[c];
             ot += s_f[c] * o[c];
@@ -878,8 +882,17 @@ int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_t* Vt, i
                                sl2e, wo, wml);
             break;
     }
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(QN, nkv), dim3(AHD), 0, st, wo, wml, p.nparts, QN, M, nq, G, out, q,
-                       Kc, Vt, Lmax, L, (int64_t)p.ntiles * AT, L + M, sl2e);
+    // the merge loads only as many partial slots as the plan can produce
+    const int64_t r0 = (int64_t)p.ntiles * AT;
+    if (p.nparts <= 16)
+        hipLaunchKernelGGL(attn_combine_kernel<16>, dim3(QN, nkv), dim3(AHD), 0, st, wo, wml, p.nparts, QN, M, nq, G,
+                           out, q, Kc, Vt, Lmax, L, r0, L + M, sl2e);
+    else if (p.nparts <= 32)
+        hipLaunchKernelGGL(attn_combine_kernel<32>, dim3(QN, nkv), dim3(AHD), 0, st, wo, wml, p.nparts, QN, M, nq, G,
+                           out, q, Kc, Vt, Lmax, L, r0, L + M, sl2e);
+    else
+        hipLaunchKernelGGL(attn_combine_kernel<ATTN_MAX_PARTS>, dim3(QN, nkv), dim3(AHD), 0, st, wo, wml, p.nparts,
+                           QN, M, nq, G, out, q, Kc, Vt, Lmax, L, r0, L + M, sl2e);
     return check_launch("vw4_decode_attn");
 }
 
