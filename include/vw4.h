@@ -278,10 +278,11 @@ VW4_API int w4_skinny_gemm_rmsnorm_swiglu(const uint16_t* resid, const uint16_t*
 /* From the fused q|k|v projection (partials of [M][(nq + 2 nkv) * hd]): rotary
  * embedding (rotate-half, base theta, position L + m) of q and k; q -> q_out
  * [M][nq][hd]; k appended to the key cache Kc [nkv][Lmax][hd] and v to the
- * transposed value cache Vt [nkv][hd][Lmax], both at positions L + m.
- * hd even, L + M <= Lmax. */
+ * blocked value cache Vb [nkv][Lmax / 32][hd][32] (position p, dimension d at
+ * [p / 32][d][p % 32]), both at positions L + m.  hd even, L + M <= Lmax,
+ * Lmax % 32 == 0. */
 VW4_API int vw4_rope_kv_append(const float* part, int32_t S, int64_t ldp, int32_t M, int32_t nq, int32_t nkv,
-                               int32_t hd, int32_t L, float theta, uint16_t* q_out, uint16_t* Kc, uint16_t* Vt,
+                               int32_t hd, int32_t L, float theta, uint16_t* q_out, uint16_t* Kc, uint16_t* Vb,
                                int64_t Lmax, void* stream);
 
 /* a[M][F] = bf16(silu(g) * u) with g = part[.][m][0:F], u = part[.][m][F:2F]
@@ -296,11 +297,12 @@ VW4_API int vw4_swiglu(const float* part, int32_t S, int64_t ldp, int32_t M, int
  * P.V product split into a bf16 head and tail (about 16 significant bits);
  * the fewer than 32 positions past the last whole 32-position tile are added
  * in the merge pass, in fp32.  q [M][nq][hd]; keys Kc [nkv][Lmax][hd]; values
- * transposed, Vt [nkv][hd][Lmax]; out [M][nq * hd] bf16.  hd == 128,
- * nq % nkv == 0, (nq / nkv) * M <= 48, Lmax % 8 == 0, L + M < 2^29, q / Kc /
- * Vt 16-byte aligned.  Workspace: vw4_attn_workspace_bytes. */
+ * in 32-position blocks, Vb [nkv][Lmax / 32][hd][32] (as vw4_rope_kv_append
+ * writes them); out [M][nq * hd] bf16.  hd == 128, nq % nkv == 0,
+ * (nq / nkv) * M <= 48, Lmax % 32 == 0, L + M < 2^29, q / Kc / Vb 16-byte
+ * aligned.  Workspace: vw4_attn_workspace_bytes. */
 VW4_API size_t vw4_attn_workspace_bytes(int32_t M, int32_t nq, int32_t nkv, int32_t hd, int64_t ctx);
-VW4_API int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_t* Vt, int64_t Lmax, int64_t L,
+VW4_API int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_t* Vb, int64_t Lmax, int64_t L,
                             int32_t M, int32_t nq, int32_t nkv, int32_t hd, uint16_t* out, void* ws, size_t ws_bytes,
                             void* stream);
 

@@ -26,6 +26,19 @@ def host(t) -> np.ndarray:
     return a.numpy()
 
 
+def vb_from_rows(v: np.ndarray) -> np.ndarray:
+    """Values [nkv][Lmax][hd] -> the blocked value cache the kernels use,
+    [nkv][Lmax / 32][hd][32] (position p, dimension d at [p / 32][d][p % 32])."""
+    nkv, lmax, hd = v.shape
+    return np.ascontiguousarray(v.reshape(nkv, lmax // 32, 32, hd).transpose(0, 1, 3, 2))
+
+
+def rows_from_vb(vb: np.ndarray) -> np.ndarray:
+    """The blocked value cache [nkv][Lmax / 32][hd][32] -> values [nkv][Lmax][hd]."""
+    nkv, nb, hd, _ = vb.shape
+    return np.ascontiguousarray(vb.transpose(0, 1, 3, 2).reshape(nkv, nb * 32, hd))
+
+
 def gemm_rel_err(y: np.ndarray, ref: np.ndarray) -> float:
     """max |y - ref| / max(|ref|, rms of ref's row): the fp32-logit parity metric
     (the floor keeps near-zero outputs from dominating)."""

@@ -19,7 +19,7 @@ from verify_step_w4_amd import binding as B
 from verify_step_w4_amd import synth
 from verify_step_w4_amd.model import DENSE_27B, Decoder, VerifyStep, W4Linear
 
-from helpers import dev, host, log
+from helpers import dev, host, log, rows_from_vb, vb_from_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -92,7 +92,7 @@ def _oracle_forward(cfg, hm, Kc, Vc, x, L):
 def test_forward_matches_oracle_small_decoder():
     cfg = TINY
     M, L = 4, 37
-    Lmax = L + M + 7                                    # 48: a multiple of 8, as the value cache needs
+    Lmax = 64                                           # >= L + M, a multiple of 32 (blocked value cache)
     log("forward vs oracle, small decoder")
     hm = _host_model(cfg, 4242)
     dec = Decoder(cfg, M, Lmax, weights=_device_weights(hm), kv_fill=False)
@@ -101,7 +101,7 @@ def test_forward_matches_oracle_small_decoder():
     Vh = [synth.f32_to_bf16_bits(synth.normal_f32(g, (cfg["nkv"], Lmax, cfg["hd"]), 1.0)) for _ in range(cfg["layers"])]
     for li in range(cfg["layers"]):
         dec.Kc[li].copy_(dev(Kh[li]))
-        dec.Vc[li].copy_(dev(np.ascontiguousarray(Vh[li].transpose(0, 2, 1))))   # values transposed
+        dec.Vc[li].copy_(dev(vb_from_rows(Vh[li])).view(dec.Vc[li].shape))   # blocked values
     x = synth.activations_bf16(78, M, cfg["d"])
     import torch
     logits = host(dec.forward(dev(x), L, M))
@@ -116,7 +116,7 @@ def test_forward_matches_oracle_small_decoder():
     # both sides (bit-exact up to rare one-ulp rounding flips); later layers
     # inherit the flips of earlier ones, so only closeness is required there
     for li in range(cfg["layers"]):
-        for gpu_c, ora_c in ((host(dec.Kc[li]), Kh[li]), (host(dec.Vc[li]).transpose(0, 2, 1), Vh[li])):
+        for gpu_c, ora_c in ((host(dec.Kc[li]), Kh[li]), (rows_from_vb(host(dec.Vc[li])), Vh[li])):
             kg = gpu_c[:, L:L + M]
             ko = ora_c[:, L:L + M]
             if li == 0:

@@ -11,7 +11,7 @@ import oracle
 from verify_step_w4_amd import binding as B
 from verify_step_w4_amd import synth
 
-from helpers import dev, host, log
+from helpers import dev, host, log, rows_from_vb, vb_from_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -149,12 +149,12 @@ def test_rope_kv_append(M, L, S):
     nq, nkv, hd = 40, 8, 128
     N = (nq + 2 * nkv) * hd
     ldp = N
-    Lmax = L + M + 3
+    Lmax = (L + M + 3 + 31) // 32 * 32                # the value cache is kept in 32-position blocks
     log(f"rope_kv M={M} L={L} S={S}")
     part = partials(L + S, S, M, N, ldp)
     qd = torch.empty((M, nq, hd), dtype=torch.int16, device="cuda")
     Kc = torch.zeros((nkv, Lmax, hd), dtype=torch.int16, device="cuda")
-    Vc = torch.zeros((nkv, hd, Lmax), dtype=torch.int16, device="cuda")      # values transposed
+    Vc = torch.zeros((nkv, Lmax // 32, hd, 32), dtype=torch.int16, device="cuda")   # blocked values
     B.rope_kv_append(dev(part), S, ldp, M, nq, nkv, hd, L, 10000.0, qd, Kc, Vc, Lmax)
     torch.cuda.synchronize()
     x = part.astype(np.float64).sum(axis=0)          # exact sum of the partials
@@ -167,7 +167,7 @@ def test_rope_kv_append(M, L, S):
             k_ref[m, h] = oracle.rope(x[m, (nq + h) * hd:(nq + h + 1) * hd], L + m)
     v_ref = x[:, (nq + nkv) * hd:].reshape(M, nkv, hd)
     bf16_close(host(qd), q_ref)
-    Kh, Vh = host(Kc), host(Vc).transpose(0, 2, 1)
+    Kh, Vh = host(Kc), rows_from_vb(host(Vc))
     bf16_close(np.stack([Kh[:, L + m] for m in range(M)]), k_ref)
     bf16_close(np.stack([Vh[:, L + m] for m in range(M)]), v_ref)
     # nothing else of the cache is touched
@@ -191,21 +191,16 @@ def test_swiglu(M, F, S):
     bf16_close(host(ad), ref)
 
 
-def _vt(Vc):
-    """Host [nkv][Lmax][hd] values -> the kernel's transposed [nkv][hd][Lmax] layout."""
-    return np.ascontiguousarray(Vc.transpose(0, 2, 1))
-
-
 def _attn_case(M, nq, nkv, L, seed, Lmax=None):
     import torch
     hd = 128
-    Lmax = Lmax or (L + M + 5 + 7) // 8 * 8
+    Lmax = Lmax or (L + M + 5 + 31) // 32 * 32
     q = synth.activations_bf16(seed, M * nq, hd).reshape(M, nq, hd)
     Kc = synth.activations_bf16(seed + 1, nkv * Lmax, hd).reshape(nkv, Lmax, hd)
     Vc = synth.activations_bf16(seed + 2, nkv * Lmax, hd).reshape(nkv, Lmax, hd)
     out = torch.empty((M, nq * hd), dtype=torch.int16, device="cuda")
     ws = B.workspace(B.attn_workspace_bytes(M, nq, nkv, hd, L + M))
-    B.decode_attn(dev(q), dev(Kc), dev(_vt(Vc)), Lmax, L, M, nq, nkv, hd, out, ws)
+    B.decode_attn(dev(q), dev(Kc), dev(vb_from_rows(Vc)), Lmax, L, M, nq, nkv, hd, out, ws)
     torch.cuda.synchronize()
     return q, Kc, Vc, host(out).reshape(M, nq, hd)
 
@@ -242,7 +237,7 @@ def test_decode_attn_ignores_cache_past_context():
     Vc2[:, L + M:] = 0xffc0
     out2 = torch.empty((M, nq * hd), dtype=torch.int16, device="cuda")
     ws = B.workspace(B.attn_workspace_bytes(M, nq, nkv, hd, L + M))
-    B.decode_attn(dev(q), dev(Kc2), dev(_vt(Vc2)), Lmax, L, M, nq, nkv, hd, out2, ws)
+    B.decode_attn(dev(q), dev(Kc2), dev(vb_from_rows(Vc2)), Lmax, L, M, nq, nkv, hd, out2, ws)
     torch.cuda.synchronize()
     assert np.array_equal(host(out2).reshape(M, nq, hd), out)
 
@@ -258,7 +253,7 @@ def test_decode_attn_causal_rows():
     Vc2[:, L + 1:] = 0
     out2 = torch.empty((M, nq * hd), dtype=torch.int16, device="cuda")
     ws = B.workspace(B.attn_workspace_bytes(M, nq, nkv, hd, L + M))
-    B.decode_attn(dev(q), dev(Kc2), dev(_vt(Vc2)), Lmax, L, M, nq, nkv, hd, out2, ws)
+    B.decode_attn(dev(q), dev(Kc2), dev(vb_from_rows(Vc2)), Lmax, L, M, nq, nkv, hd, out2, ws)
     torch.cuda.synchronize()
     o2 = host(out2).reshape(M, nq, hd)
     assert np.array_equal(o2[0], out[0])

@@ -170,7 +170,7 @@ __global__ __launch_bounds__(NCOL) void rmsnorm_apply_kernel(const uint16_t* __r
 // ---------------------------------------------------------------------------
 __global__ void rope_kv_kernel(const float* __restrict__ part, int S, int64_t ldp, int M, int nq, int nkv, int hd,
                                int L, double theta, uint16_t* __restrict__ q_out, uint16_t* __restrict__ Kc,
-                               uint16_t* __restrict__ Vt, int64_t Lmax) {
+                               uint16_t* __restrict__ Vb, int64_t Lmax) {
     const int hh = blockIdx.x, m = blockIdx.y, d = threadIdx.x, half = hd / 2;
     const int64_t c0 = (int64_t)hh * hd;
     const int64_t pos = (int64_t)L + m;
@@ -209,9 +209,10 @@ __global__ void rope_kv_kernel(const float* __restrict__ part, int S, int64_t ld
     }
     if (vhead) {  // value head: append as is
         const int kv = hh - nq - nkv;
-        uint16_t* dst = Vt + (int64_t)kv * hd * Lmax + pos;     // transposed: [kv][dim][position]
-        dst[(int64_t)d * Lmax] = f32_to_bf16(a);
-        dst[(int64_t)(d + half) * Lmax] = f32_to_bf16(b);
+        // blocked: [kv][position / 32][dim][position % 32]
+        uint16_t* dst = Vb + (int64_t)kv * hd * Lmax + (pos >> 5) * hd * 32 + (pos & 31);
+        dst[(int64_t)d * 32] = f32_to_bf16(a);
+        dst[(int64_t)(d + half) * 32] = f32_to_bf16(b);
         return;
     }
     const float c = (float)cd, s = (float)sd;
@@ -254,8 +255,12 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ p
 // Grouped-query decode attention on the matrix cores.
 //
 // KV cache layout: K [nkv][Lmax][128] (a position is one 256-byte row) and V
-// transposed, Vt [nkv][128][Lmax] (a head dimension is one row of positions),
-// so that both contractions read 16-byte runs straight into MFMA operands.
+// in 32-position blocks, transposed inside each block: Vb [nkv][Lmax / 32]
+// [128][32] (a block is 8 KiB, one row of 32 positions per head dimension).
+// Both contractions read 16-byte runs straight into MFMA operands, and a
+// 32-position tile of K or V is one contiguous 8 KiB run (measured: a fully
+// transposed V [128][Lmax], whose tile is 128 pieces of 64 bytes 2 * Lmax
+// bytes apart, costs 8-9% of the kernel's time at 8k-32k positions).
 //
 // grid = (nkv, nparts), 4 wavefronts.  The context is cut into whole
 // 32-position tiles; the fewer than 32 positions past the last whole tile are
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ p
 //   online softmax in base 2 (scores pre-scaled by log2(e) / sqrt(128));
 //   O[query][dim] += P[query][pos] . V[pos][dim]  (A = those 8 probabilities
 //     as a bf16 head plus a bf16 tail, two products, so P keeps about 16
-//     bits; B = 16 bytes of a Vt row).
+//     bits; B = 16 bytes of a Vb row).
 // The four wavefronts merge pairwise in LDS ((w0 + w2) + (w1 + w3)), and the
 // workgroup writes one partial (m, l, o) per query; attn_combine_kernel
 // merges the partials in chunk order, then the remainder positions.
@@ -301,7 +306,7 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 
 struct AttnTile {
     bf16x8 k[2][4];   // K rows of the two 16-position blocks, 4 steps of 32 dims
-    bf16x8 v[8];      // Vt rows of the 8 16-dim blocks, positions 8 g .. +8
+    bf16x8 v[8];      // Vb rows of the 8 16-dim blocks, positions 8 g .. +8
 };
 
 __device__ __forceinline__ void attn_load_k(AttnTile& T, const uint16_t* Kh, int64_t ctx, int64_t t0, int g, int i) {
@@ -314,18 +319,24 @@ __device__ __forceinline__ void attn_load_k(AttnTile& T, const uint16_t* Kh, int
     }
 }
 
+// Element (position p, dimension dim) of one KV head's blocked value cache;
+// 8 positions from an 8-aligned p are 16 contiguous bytes.
+__device__ __forceinline__ int64_t vb_at(int64_t p, int dim) {
+    return ((p >> 5) * AHD + dim) * 32 + (p & 31);
+}
+
 __device__ __forceinline__ void attn_load_v(AttnTile& T, const uint16_t* Vh, int64_t Lmax, int64_t ctx, int64_t t0,
                                             int g, int i) {
     const int64_t p8 = t0 + 8 * g;
     if (p8 + 8 <= ctx) {
 #pragma unroll
-        for (int db = 0; db < 8; ++db) T.v[db] = ld_bf16x8(Vh + (int64_t)(db * 16 + i) * Lmax + p8);
+        for (int db = 0; db < 8; ++db) T.v[db] = ld_bf16x8(Vh + vb_at(p8, db * 16 + i));
     } else {
         // The context ends inside (or before) these 8 positions.  The 16 bytes
         // are read from an 8-aligned start at most (ctx - 1) rounded down, which
-        // lies inside the row (Lmax % 8 == 0), and the positions at or past ctx
-        // are zeroed in registers (their probabilities are 0, and 0 * NaN would
-        // not be).
+        // lies inside the cache (Lmax % 32 == 0), and the positions at or past
+        // ctx are zeroed in registers (their probabilities are 0, and 0 * NaN
+        // would not be).
         const int64_t last8 = (ctx - 1) & ~(int64_t)7;
         const int64_t pl = p8 < last8 ? p8 : last8;
         const int64_t nv64 = ctx - p8;
@@ -336,7 +347,7 @@ __device__ __forceinline__ void attn_load_v(AttnTile& T, const uint16_t* Vh, int
             keep[w] = (2 * w < nv ? 0x0000ffffu : 0u) | (2 * w + 1 < nv ? 0xffff0000u : 0u);
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-            const u32x4v raw = *(const u32x4v*)(Vh + (int64_t)(db * 16 + i) * Lmax + pl);
+            const u32x4v raw = *(const u32x4v*)(Vh + vb_at(pl, db * 16 + i));
             T.v[db] = __builtin_bit_cast(bf16x8, raw & keep);
         }
     }
@@ -456,7 +467,7 @@ __device__ __forceinline__ void attn_store(float* Wo, float* Wm, float* Wl, int 
 
 template <int NQB>
 __device__ __forceinline__ void attn_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
-                                          const uint16_t* __restrict__ Vt, int64_t Lmax, int64_t L, int M, int nq,
+                                          const uint16_t* __restrict__ Vb, int64_t Lmax, int64_t L, int M, int nq,
                                           int G, int ntiles, float sl2e, float* __restrict__ ws_o,
                                           AttnPart* __restrict__ ws_ml) {
     constexpr int OSZ = NQB * 8 * 4 * 64;                  // one wavefront's o, lane-major
@@ -469,7 +480,7 @@ __device__ __forceinline__ void attn_body(const uint16_t* __restrict__ q, const 
     const int64_t ctx = L + M;
     const int tb = c * ntiles / nparts, te = (c + 1) * ntiles / nparts;   // ntiles < 2^24: 32-bit division
     const uint16_t* Kh = Kc + (int64_t)h * Lmax * AHD;
-    const uint16_t* Vh = Vt + (int64_t)h * AHD * Lmax;
+    const uint16_t* Vh = Vb + (int64_t)h * AHD * Lmax;
 
     bf16x8 qop[NQB][4];
     int64_t lim[NQB];
@@ -553,15 +564,15 @@ __device__ __forceinline__ void attn_body(const uint16_t* __restrict__ q, const 
 // queries: one workgroup per CU, no spills.
 template <int NQB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vt, int64_t Lmax,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vb, int64_t Lmax,
     int64_t L, int M, int nq, int G, int ntiles, float sl2e, float* __restrict__ ws_o, AttnPart* __restrict__ ws_ml) {
-    attn_body<NQB>(q, Kc, Vt, Lmax, L, M, nq, G, ntiles, sl2e, ws_o, ws_ml);
+    attn_body<NQB>(q, Kc, Vb, Lmax, L, M, nq, G, ntiles, sl2e, ws_o, ws_ml);
 }
 
 __global__ __launch_bounds__(256) void attn_mfma_wide_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vt, int64_t Lmax,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc, const uint16_t* __restrict__ Vb, int64_t Lmax,
     int64_t L, int M, int nq, int G, int ntiles, float sl2e, float* __restrict__ ws_o, AttnPart* __restrict__ ws_ml) {
-    attn_body<3>(q, Kc, Vt, Lmax, L, M, nq, G, ntiles, sl2e, ws_o, ws_ml);
+    attn_body<3>(q, Kc, Vb, Lmax, L, M, nq, G, ntiles, sl2e, ws_o, ws_ml);
 }
 
 // Merge the chunk partials of one (kv head, query) and add the positions
@@ -574,7 +585,7 @@ template <int NPM>
 __global__ __launch_bounds__(AHD) void attn_combine_kernel(
     const float* __restrict__ ws_o, const AttnPart* __restrict__ ws_ml, int nparts, int QN, int M, int nq, int G,
     uint16_t* __restrict__ out, const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
-    const uint16_t* __restrict__ Vt, int64_t Lmax, int64_t L, int64_t r0, int64_t ctx, float sl2e) {
+    const uint16_t* __restrict__ Vb, int64_t Lmax, int64_t L, int64_t r0, int64_t ctx, float sl2e) {
     __shared__ float s_f[64], s_l[64], s_sc[AT];
     __shared__ float s_mr;
     const int j = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
@@ -586,9 +597,9 @@ __global__ __launch_bounds__(AHD) void attn_combine_kernel(
     // scores can be formed while the rest is in flight), then the partial
     // outputs and the chunk maxima and sums.
     // Remainder scores: thread 4 k + qt takes dims 32 qt .. +32 of position
-    // r0 + k.  Its value-cache row d, positions r0 .. r0 + 31, comes in
+    // r0 + k.  Its values of dimension d, positions r0 .. r0 + 31, come in
     // 8-position pieces whose start is clamped to the last 8-aligned start
-    // before ctx (inside the row: Lmax % 8 == 0); positions at or past ctx
+    // before ctx (inside the cache: Lmax % 32 == 0); positions at or past ctx
     // are never used.
     // Every address is clamped to a valid one instead of the load being
     // predicated, so that no branch separates the loads and each wait covers
@@ -605,7 +616,7 @@ __global__ __launch_bounds__(AHD) void attn_combine_kernel(
             kv[e] = kp[e];
             qv[e] = qp[e];
             const int64_t p8 = r0 + 8 * e < last8 ? r0 + 8 * e : last8;
-            vv[e] = *(const u32x4v*)(Vt + ((int64_t)h * AHD + d) * Lmax + p8);
+            vv[e] = *(const u32x4v*)(Vb + (int64_t)h * AHD * Lmax + vb_at(p8, d));
         }
     }
     // (then up to 40 of the partial outputs: the wait counter counts at most
@@ -809,16 +820,17 @@ int vw4_add_rmsnorm_out(const uint16_t* resid_in, const float* part, int32_t S, 
 }
 
 int vw4_rope_kv_append(const float* part, int32_t S, int64_t ldp, int32_t M, int32_t nq, int32_t nkv, int32_t hd,
-                       int32_t L, float theta, uint16_t* q_out, uint16_t* Kc, uint16_t* Vt, int64_t Lmax,
+                       int32_t L, float theta, uint16_t* q_out, uint16_t* Kc, uint16_t* Vb, int64_t Lmax,
                        void* stream) {
-    VW4_REQUIRE(part && q_out && Kc && Vt, VW4_EINVAL, "vw4_rope_kv_append: null pointer");
+    VW4_REQUIRE(part && q_out && Kc && Vb, VW4_EINVAL, "vw4_rope_kv_append: null pointer");
     VW4_REQUIRE(M >= 1 && M <= 64 && nq >= 1 && nkv >= 1 && hd >= 2 && hd % 2 == 0 && hd <= 2048, VW4_EINVAL,
                 "vw4_rope_kv_append: bad shape");
     VW4_REQUIRE(S >= 1 && ldp >= (int64_t)(nq + 2 * nkv) * hd, VW4_EINVAL, "vw4_rope_kv_append: bad partial layout");
     VW4_REQUIRE(L >= 0 && (int64_t)L + M <= Lmax, VW4_EINVAL, "vw4_rope_kv_append: L + M exceeds the cache");
+    VW4_REQUIRE(Lmax % 32 == 0, VW4_EINVAL, "vw4_rope_kv_append: Lmax must be a multiple of 32");
     VW4_REQUIRE(theta > 0.0f, VW4_EINVAL, "vw4_rope_kv_append: theta must be > 0");
     hipLaunchKernelGGL(rope_kv_kernel, dim3(nq + 2 * nkv, M), dim3(hd / 2), 0, (hipStream_t)stream, part, S, ldp, M,
-                       nq, nkv, hd, L, (double)theta, q_out, Kc, Vt, Lmax);
+                       nq, nkv, hd, L, (double)theta, q_out, Kc, Vb, Lmax);
     return check_launch("vw4_rope_kv_append");
 }
 
@@ -848,17 +860,17 @@ size_t vw4_attn_workspace_bytes(int32_t M, int32_t nq, int32_t nkv, int32_t hd, 
     return attn_plan(M, nq, nkv, ctx).total;
 }
 
-int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_t* Vt, int64_t Lmax, int64_t L, int32_t M,
+int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_t* Vb, int64_t Lmax, int64_t L, int32_t M,
                     int32_t nq, int32_t nkv, int32_t hd, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
-    VW4_REQUIRE(q && Kc && Vt && out, VW4_EINVAL, "vw4_decode_attn: null pointer");
+    VW4_REQUIRE(q && Kc && Vb && out, VW4_EINVAL, "vw4_decode_attn: null pointer");
     VW4_REQUIRE(hd == AHD, VW4_EUNSUPPORTED, "vw4_decode_attn: head dim %d (only 128 is built)", hd);
     VW4_REQUIRE(M >= 1 && nq >= 1 && nkv >= 1 && nq % nkv == 0, VW4_EINVAL, "vw4_decode_attn: bad head counts");
     const int QN = (nq / nkv) * M;
     VW4_REQUIRE(QN <= AQN, VW4_EUNSUPPORTED, "vw4_decode_attn: (nq/nkv)*M = %d > %d", QN, AQN);
     VW4_REQUIRE(L >= 0 && L + M <= Lmax, VW4_EINVAL, "vw4_decode_attn: L + M exceeds the cache");
     VW4_REQUIRE(L + M < ((int64_t)1 << 29), VW4_EUNSUPPORTED, "vw4_decode_attn: context of 2^29 or more positions");
-    VW4_REQUIRE(Lmax % 8 == 0, VW4_EINVAL, "vw4_decode_attn: Lmax must be a multiple of 8");
-    VW4_REQUIRE(aligned(Kc, 16) && aligned(Vt, 16) && aligned(q, 16), VW4_EINVAL, "vw4_decode_attn: misaligned");
+    VW4_REQUIRE(Lmax % 32 == 0, VW4_EINVAL, "vw4_decode_attn: Lmax must be a multiple of 32");
+    VW4_REQUIRE(aligned(Kc, 16) && aligned(Vb, 16) && aligned(q, 16), VW4_EINVAL, "vw4_decode_attn: misaligned");
     const AttnPlan p = attn_plan(M, nq, nkv, L + M);
     VW4_REQUIRE(ws && ws_bytes >= p.total && aligned(ws, 256), VW4_EWORKSPACE,
                 "vw4_decode_attn: needs a 256-byte aligned workspace of %zu bytes", p.total);
@@ -870,15 +882,15 @@ int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_t* Vt, i
     const dim3 grid(nkv, p.nparts);
     switch ((QN + 15) / 16) {
         case 1:
-            hipLaunchKernelGGL(attn_mfma_kernel<1>, grid, dim3(256), 0, st, q, Kc, Vt, Lmax, L, M, nq, G, p.ntiles,
+            hipLaunchKernelGGL(attn_mfma_kernel<1>, grid, dim3(256), 0, st, q, Kc, Vb, Lmax, L, M, nq, G, p.ntiles,
                                sl2e, wo, wml);
             break;
         case 2:
-            hipLaunchKernelGGL(attn_mfma_kernel<2>, grid, dim3(256), 0, st, q, Kc, Vt, Lmax, L, M, nq, G, p.ntiles,
+            hipLaunchKernelGGL(attn_mfma_kernel<2>, grid, dim3(256), 0, st, q, Kc, Vb, Lmax, L, M, nq, G, p.ntiles,
                                sl2e, wo, wml);
             break;
         default:
-            hipLaunchKernelGGL(attn_mfma_wide_kernel, grid, dim3(256), 0, st, q, Kc, Vt, Lmax, L, M, nq, G, p.ntiles,
+            hipLaunchKernelGGL(attn_mfma_wide_kernel, grid, dim3(256), 0, st, q, Kc, Vb, Lmax, L, M, nq, G, p.ntiles,
                                sl2e, wo, wml);
             break;
     }
@@ -886,13 +898,13 @@ int vw4_decode_attn(const uint16_t* q, const uint16_t* Kc, const uint16_t* Vt, i
     const int64_t r0 = (int64_t)p.ntiles * AT;
     if (p.nparts <= 16)
         hipLaunchKernelGGL(attn_combine_kernel<16>, dim3(QN, nkv), dim3(AHD), 0, st, wo, wml, p.nparts, QN, M, nq, G,
-                           out, q, Kc, Vt, Lmax, L, r0, L + M, sl2e);
+                           out, q, Kc, Vb, Lmax, L, r0, L + M, sl2e);
     else if (p.nparts <= 32)
         hipLaunchKernelGGL(attn_combine_kernel<32>, dim3(QN, nkv), dim3(AHD), 0, st, wo, wml, p.nparts, QN, M, nq, G,
-                           out, q, Kc, Vt, Lmax, L, r0, L + M, sl2e);
+                           out, q, Kc, Vb, Lmax, L, r0, L + M, sl2e);
     else
         hipLaunchKernelGGL(attn_combine_kernel<ATTN_MAX_PARTS>, dim3(QN, nkv), dim3(AHD), 0, st, wo, wml, p.nparts,
-                           QN, M, nq, G, out, q, Kc, Vt, Lmax, L, r0, L + M, sl2e);
+                           QN, M, nq, G, out, q, Kc, Vb, Lmax, L, r0, L + M, sl2e);
     return check_launch("vw4_decode_attn");
 }
 

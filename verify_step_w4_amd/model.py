@@ -100,7 +100,7 @@ class Decoder:
         import torch
         self.cfg = dict(cfg)
         c = self.cfg
-        Lmax = (Lmax + 7) // 8 * 8                     # the value cache rows are read 16 bytes at a time
+        Lmax = (Lmax + 31) // 32 * 32                  # the value cache is stored in 32-position blocks
         self.M_max, self.Lmax, self.device = M_max, Lmax, device
         d, nq, nkv, hd, F, nl, V = c["d"], c["nq"], c["nkv"], c["hd"], c["F"], c["layers"], c["V"]
         self.nqkv = (nq + 2 * nkv) * hd
@@ -110,16 +110,17 @@ class Decoder:
         self.layers = weights["layers"]
         self.final_gamma = weights["final_gamma"]
         self.lm_head = weights["lm_head"]
-        # KV caches bf16: keys [layer][nkv][Lmax][hd], values transposed
-        # [layer][nkv][hd][Lmax]; synthetic N(0,1) context
+        # KV caches bf16: keys [layer][nkv][Lmax][hd], values in 32-position
+        # blocks [layer][nkv][Lmax / 32][hd][32]; synthetic N(0,1) context
         self.Kc, self.Vc = [], []
         for _ in range(nl):
             if kv_fill:
                 k = torch.randn((nkv, Lmax, hd), generator=gen, device=device).to(torch.bfloat16).view(torch.int16)
-                v = torch.randn((nkv, hd, Lmax), generator=gen, device=device).to(torch.bfloat16).view(torch.int16)
+                v = torch.randn((nkv, Lmax // 32, hd, 32), generator=gen,
+                                device=device).to(torch.bfloat16).view(torch.int16)
             else:
                 k = torch.zeros((nkv, Lmax, hd), dtype=torch.int16, device=device)
-                v = torch.zeros((nkv, hd, Lmax), dtype=torch.int16, device=device)
+                v = torch.zeros((nkv, Lmax // 32, hd, 32), dtype=torch.int16, device=device)
             self.Kc.append(k)
             self.Vc.append(v)
         # activation buffers
