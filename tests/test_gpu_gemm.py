@@ -251,7 +251,7 @@ def test_rmsnorm_swiglu_gemm_against_oracle(M, F, K):
         bf16_close(np.ascontiguousarray(ah[:, :F]), _swiglu_ref(h, w, F), min_exact=0.9)
 
 
-@pytest.mark.parametrize("M,F,K", [(4, 17408, 5120), (1, 96, 320), (6, 544, 1024)])
+@pytest.mark.parametrize("M,F,K", [(4, 17408, 5120), (1, 96, 320), (6, 544, 1024), (2, 3200, 512)])
 def test_swiglu_gemm_against_oracle(M, F, K):
     """Gate|up GEMM on given activations with the SwiGLU epilogue."""
     import torch

@@ -44,11 +44,14 @@ def test_add_rmsnorm(M, D, S):
     rd, hd = dev(resid), torch.empty((M, D), dtype=torch.int16, device="cuda")
     B.add_rmsnorm(rd, dev(part), S, ldp, dev(gamma), 1e-6, M, D, hd, B.workspace(B.norm_workspace_bytes(M, D)))
     torch.cuda.synchronize()
-    # oracle: exact sum, one bf16 rounding, then RMSNorm of the rounded residual
+    # oracle: exact sum and one bf16 rounding for the residual; h is the
+    # RMSNorm of the residual as stored (the kernels sum the partials in fp32,
+    # so a residual within 1e-7 of a bf16 rounding midpoint may land one ulp
+    # from the exact rounding; the residual check covers that ulp, and h is
+    # judged on the residual it was computed from)
     exact = synth.bf16_bits_to_f32(resid).astype(np.float64) + part[:, :, :D].astype(np.float64).sum(axis=0)
-    r_ref_bits = oracle.bf16_round(exact)
     bf16_close(host(rd), exact)
-    h_ref = oracle.rmsnorm(r_ref_bits, gamma, 1e-6)
+    h_ref = oracle.rmsnorm(host(rd), gamma, 1e-6)
     bf16_close(host(hd), h_ref)
 
 
@@ -84,7 +87,7 @@ def test_bf16_rounding_of_fp32_bit_patterns():
 
 
 @pytest.mark.parametrize("M,D,S", [(4, 5120, 8), (1, 5120, 1), (6, 1000, 3), (4, 2048, 0), (3, 8192, 8),
-                                   (2, 4, 1), (64, 260, 2)])
+                                   (2, 4, 1), (64, 260, 2), (4, 3072, 4), (5, 2304, 8), (2, 4100, 5)])
 def test_add_rmsnorm_out_equals_two_launch_path(M, D, S):
     """The one-launch, out-of-place add + RMSNorm gives bitwise the residual
     and h of vw4_add_rmsnorm (same chunk sums, same order), and matches the
@@ -110,7 +113,7 @@ def test_add_rmsnorm_out_equals_two_launch_path(M, D, S):
     if S:
         exact = exact + part[:, :, :D].astype(np.float64).sum(axis=0)
     bf16_close(host(r2), exact)
-    bf16_close(host(h2), oracle.rmsnorm(oracle.bf16_round(exact), gamma, 1e-6))
+    bf16_close(host(h2), oracle.rmsnorm(host(r2), gamma, 1e-6))   # h of the stored residual
 
 
 def test_add_rmsnorm_out_rejects_bad_arguments():
@@ -208,7 +211,7 @@ def _attn_case(M, nq, nkv, L, seed, Lmax=None):
 @pytest.mark.parametrize("M,nq,nkv,L", [(4, 40, 8, 0), (4, 40, 8, 100), (1, 40, 8, 1023), (4, 40, 8, 1024),
                                         (2, 8, 2, 777), (6, 10, 2, 300), (4, 40, 8, 8192), (8, 40, 8, 777),
                                         (3, 40, 8, 31), (6, 40, 8, 2049), (1, 40, 8, 0), (4, 40, 8, 32764),
-                                        (4, 40, 8, 1051), (1, 40, 8, 30)])
+                                        (4, 40, 8, 1051), (1, 40, 8, 30), (4, 40, 4, 4000), (2, 8, 2, 6000)])
 def test_decode_attn(M, nq, nkv, L):
     log(f"attn M={M} nq={nq} nkv={nkv} L={L}")
     q, Kc, Vc, out = _attn_case(M, nq, nkv, L, 1000 + L + M)
