@@ -564,11 +564,28 @@ def verify27b_workload(args):
         us = time_graphs([lambda nm=nm: dec.gemm_pass(M, names=(nm,))], 20 if nm != "lm_head" else 200)[0] * 1e3
         linears[nm] = {"N": N, "K": Kd, "avg_us": round(us, 2), "GBs": round(b / (us * 1e-6) / 1e9, 1),
                        "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    # (f) the decode attention (tile kernel + merge) by itself, one call per
+    # layer over that layer's cache, captured as a graph and replayed, at each
+    # context of the workload: K and V of L + M positions read once
+    attention = {}
+    nq, nkv, hd = 40, 8, 128
+    for Ls in sorted(set([L] + sweep_L)):
+
+        def attn_pass(Ls=Ls):
+            for li in range(cfg["layers"]):
+                B.decode_attn(dec.q, dec.Kc[li], dec.Vc[li], dec.Lmax, Ls, M, nq, nkv, hd, dec.attn, dec.attn_ws)
+            return cfg["layers"]
+
+        us = time_graphs([attn_pass], 10)[0] * 1e3
+        kv = 2 * nkv * (Ls + M) * hd * 2
+        attention[Ls] = {"us_per_layer": round(us, 2), "kv_bytes": kv, "GBs": round(kv / (us * 1e-6) / 1e9, 1),
+                         "frac": round(kv / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     res = dict(
         ms_per_step=step_ms,
         value=K / (total_ms * 1e-3),
         wall_s=wall,
         w4_gemm_by_linear=linears,
+        attention_by_context=attention,
         config={"workload": "verify27b", "layers": 64, "d_model": d, "heads_q_kv_dim": [40, 8, 128],
                 "ffn": cfg["F"], "V": V, "context": L, "M": M, "draft_depth": D, "temperature": T, "top_p": top_p,
                 "weights": "int4 group-64 symmetric, fp16 scales", "kv_cache": "bf16"},
@@ -1053,7 +1070,7 @@ def main():
            "data": "synthetic", "config": res["config"], "roofline": res["roofline"]}
     for k in ("stages_us", "w4_gemm_by_linear", "accepted_length_hist", "flagged_steps", "m1_ar_step_ms",
               "verify_over_ar", "step_hbm_gbs", "experts_per_step", "grouped_gemm_gbs", "m_sweep", "unit_note",
-              "context_sweep", "stats_accept_sweep", "sustained"):
+              "context_sweep", "stats_accept_sweep", "sustained", "attention_by_context"):
         if k in res:
             out[k] = res[k]
     if not args.no_cpu_baseline:
