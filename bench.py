@@ -105,6 +105,39 @@ def time_graphs(issue_fns, reps):
     return e0.elapsed_time(e1) / (reps * n), n
 
 
+class InputStage:
+    """The per-step inputs of a captured step packed in one device byte
+    buffer: views into `stage` are what the graph reads, and `pool` holds
+    npool input sets in the same layout, so one copy (pool[j] -> stage)
+    refreshes every input of a step.  specs: (name, shape, torch dtype)."""
+
+    def __init__(self, specs, npool, device="cuda"):
+        import torch
+        self.offs, off = {}, 0
+        for name, shape, dt in specs:
+            n = int(torch.tensor([], dtype=dt).element_size())
+            for v in shape:
+                n *= v
+            self.offs[name] = (off, n, tuple(shape), dt)
+            off += (n + 255) // 256 * 256
+        self.nbytes = off
+        self.stage = torch.empty(off, dtype=torch.uint8, device=device)
+        self.pool = torch.empty((npool, off), dtype=torch.uint8, device=device)
+
+    def _view(self, buf, name):
+        off, n, shape, dt = self.offs[name]
+        return buf[off:off + n].view(dt).view(shape)
+
+    def view(self, name):
+        return self._view(self.stage, name)
+
+    def slot(self, j, name):
+        return self._view(self.pool[j], name)
+
+    def load(self, j):
+        self.stage.copy_(self.pool[j])
+
+
 class Telemetry:
     """Samples the GPU's clocks, temperatures and power through amdsmi in a
     background thread (every `period` s) while the GPU works.  summary()
@@ -426,9 +459,8 @@ def verify27b_workload(args):
     vs = VerifyStep(dec, M)
     ar = VerifyStep(dec, 1)
     K, W = args.steps, args.warmup
-    nacc_all = torch.empty(K, dtype=torch.int32, device=dev)
-    tok_all = torch.empty((K, M), dtype=torch.int32, device=dev)
-    flag_all = torch.empty(K, dtype=torch.int32, device=dev)
+    out_all = torch.empty((K, M + 2), dtype=torch.int32, device=dev)   # tokens, n_acc, flags per step
+    nacc_all, flag_all = out_all[:, M], out_all[:, M + 1]
     gemm_events = []
 
     gemm_names = []
@@ -461,7 +493,13 @@ def verify27b_workload(args):
     # (b) the timed region: the verify step captured once as a HIP graph and
     # replayed; each replay is preceded by copying the next step's inputs
     # into the captured buffers (counted in the time)
-    x_s, q_s, d_s = xs[0].clone(), qs[0].clone(), drafts[0].clone()
+    stage = InputStage([("x", (M, d), torch.int16), ("q", (D, V), torch.float32), ("d", (D,), torch.int32)], npool)
+    for j in range(npool):
+        stage.slot(j, "x").copy_(xs[j])
+        stage.slot(j, "q").copy_(qs[j])
+        stage.slot(j, "d").copy_(drafts[j])
+    stage.load(0)
+    x_s, q_s, d_s = stage.view("x"), stage.view("q"), stage.view("d")
     step_dev = torch.zeros(1, dtype=torch.int64, device=dev)
     graph = vs.capture(x_s, L, q_s, d_s, T, top_p, seed, step_dev)
     for i in range(W):
@@ -471,14 +509,9 @@ def verify27b_workload(args):
     t0 = time.perf_counter()
     start.record()
     for i in range(K):
-        j = i % npool
-        x_s.copy_(xs[j])
-        q_s.copy_(qs[j])
-        d_s.copy_(drafts[j])
+        stage.load(i % npool)
         graph.replay()
-        tok_all[i:i + 1].copy_(vs.tokens)
-        nacc_all[i:i + 1].copy_(vs.n_acc)
-        flag_all[i:i + 1].copy_(vs.flags)
+        out_all[i].copy_(vs.outputs)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -489,10 +522,7 @@ def verify27b_workload(args):
         # time, and the GPU's clocks / temperatures / power meanwhile
 
         def issue(i):
-            j = i % npool
-            x_s.copy_(xs[j])
-            q_s.copy_(qs[j])
-            d_s.copy_(drafts[j])
+            stage.load(i % npool)
             graph.replay()
 
         sustained = sustained_run(issue, total_ms / K, args.sustain)
@@ -540,9 +570,7 @@ def verify27b_workload(args):
                 if one:
                     x1.copy_(xs[j][:1])
                 else:
-                    x_s.copy_(xs[j])
-                    q_s.copy_(qs[j])
-                    d_s.copy_(drafts[j])
+                    stage.load(j)
                 g_.replay()
             c1.record()
             torch.cuda.synchronize()
@@ -729,47 +757,57 @@ def moe_workload(args):
     lm_bytes = V * d * BYTES_PER_WEIGHT + M * d * 2 + M * V * 4
     grouped = float((gu_bytes + dn_bytes).sum() / ((t_us["gate_up"] + t_us["down"]).sum() * 1e-6) / 1e9)
     # (b) timed region: one graph per (bank, LM head) pair, replayed in turn;
-    # each replay is preceded by copying the step's inputs into the captured buffers
-    x_s, lg_s, q_s, d_s = xs[0].clone(), router[0].clone(), qs[0].clone(), drafts[0].clone()
+    # each replay is preceded by one copy of the step's inputs (packed: rows,
+    # router logits, q, drafts) into the captured buffers
+    stage = InputStage([("x", (M, d), torch.int16), ("lg", (M, E), torch.float32), ("q", (D, V), torch.float32),
+                        ("d", (D,), torch.int32)], K)
+    for i in range(K):
+        j = i % npool
+        stage.slot(i, "x").copy_(xs[j])
+        stage.slot(i, "lg").copy_(router[W + i])
+        stage.slot(i, "q").copy_(qs[j])
+        stage.slot(i, "d").copy_(drafts[j])
+    stage.stage.zero_()
+    stage.view("x").copy_(xs[0])
+    stage.view("lg").copy_(router[0])
+    stage.view("q").copy_(qs[0])
+    stage.view("d").copy_(drafts[0])
+    x_s, lg_s, q_s, d_s = stage.view("x"), stage.view("lg"), stage.view("q"), stage.view("d")
     step_dev = torch.zeros(1, dtype=torch.int64, device=dev)
     graphs = [mvs[k].capture(x_s, lg_s, banks[k], q_s, d_s, T, top_p, seed, step_dev) for k in range(nrot)]
     for i in range(W):
         graphs[i % nrot].replay()
     step_dev.zero_()
-    tok_all = torch.empty((K, M), dtype=torch.int32, device=dev)
-    nacc_all = torch.empty(K, dtype=torch.int32, device=dev)
-    flag_all = torch.empty(K, dtype=torch.int32, device=dev)
-    nsl_all = torch.empty(K, dtype=torch.int32, device=dev)
+    out_all = torch.empty((K, M + 3), dtype=torch.int32, device=dev)   # tokens, n_acc, flags, experts per step
+    nacc_all, flag_all, nsl_all = out_all[:, M], out_all[:, M + 1], out_all[:, M + 2]
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record()
     for i in range(K):
-        k, j = i % nrot, i % npool
-        x_s.copy_(xs[j])
-        lg_s.copy_(router[W + i])
-        q_s.copy_(qs[j])
-        d_s.copy_(drafts[j])
+        k = i % nrot
+        stage.load(i)
         graphs[k].replay()
-        tok_all[i:i + 1].copy_(mvs[k].tokens)
-        nacc_all[i:i + 1].copy_(mvs[k].n_acc)
-        flag_all[i:i + 1].copy_(mvs[k].flags)
-        nsl_all[i:i + 1].copy_(mvs[k].n_slots)
+        out_all[i].copy_(mvs[k].outputs)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
     step_ms = total_ms / K
     # (c) the M = 1 step (one row, D = 0) on the same weights, same way
-    x1, lg1 = xs[0][:1].clone(), router[0][:1].clone()
+    stage1 = InputStage([("x", (1, d), torch.int16), ("lg", (1, E), torch.float32)], K)
+    for i in range(K):
+        stage1.slot(i, "x").copy_(xs[i % npool][:1])
+        stage1.slot(i, "lg").copy_(router[W + i][:1])
+    stage1.load(0)
+    x1, lg1 = stage1.view("x"), stage1.view("lg")
     step1 = torch.zeros(1, dtype=torch.int64, device=dev)
     g1 = [ar[k].capture(x1, lg1, banks[k], None, None, T, top_p, seed, step1) for k in range(nrot)]
     torch.cuda.synchronize()
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a0.record()
     for i in range(K):
-        x1.copy_(xs[i % npool][:1])
-        lg1.copy_(router[W + i][:1])
+        stage1.load(i)
         g1[i % nrot].replay()
     a1.record()
     torch.cuda.synchronize()

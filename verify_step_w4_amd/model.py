@@ -280,9 +280,12 @@ class VerifyStep:
         self.stats = torch.zeros(M * B.ROWSTAT_BYTES, dtype=torch.uint8, device=dev)
         self.stat_ws = B.workspace(B.verify_workspace_bytes(M, V), dev)
         self.acc_ws = B.workspace(B.accept_workspace_bytes(1, V), dev)
-        self.tokens = torch.empty((1, M), dtype=torch.int32, device=dev)
-        self.n_acc = torch.empty(1, dtype=torch.int32, device=dev)
-        self.flags = torch.empty(1, dtype=torch.int32, device=dev)
+        # tokens [1][M], n_acc and flags in one int32 block: one copy reads a
+        # step's outputs
+        self.outputs = torch.empty(M + 2, dtype=torch.int32, device=dev)
+        self.tokens = self.outputs[:M].view(1, M)
+        self.n_acc = self.outputs[M:M + 1]
+        self.flags = self.outputs[M + 1:M + 2]
 
     def run_graphable(self, x, L: int, q, drafts, T: float, top_p: float, seed: int, step_dev, stream=None):
         """The same step with the Philox step read from device memory and
@@ -378,7 +381,10 @@ class MoEVerify:
         self.experts = torch.empty((M, topk), dtype=i32, device=device)
         self.weights = torch.empty((M, topk), dtype=torch.float32, device=device)
         self.slot_expert = torch.zeros(self.max_slots, dtype=i32, device=device)
-        self.n_slots = torch.zeros(1, dtype=i32, device=device)
+        # tokens [1][M], n_acc, flags and the routed slot count in one int32
+        # block: one copy reads a step's outputs
+        self.outputs = torch.zeros(M + 3, dtype=i32, device=device)
+        self.n_slots = self.outputs[M + 2:M + 3]
         self.row_slot = torch.empty((M, topk), dtype=i32, device=device)
         self.dn_S, self.dn_ldp = B.grouped_gemm_layout(M, d, F, self.max_slots)
         self.dn_sstride = self.dn_S * M * self.dn_ldp
@@ -393,9 +399,9 @@ class MoEVerify:
         self.stats = torch.zeros(M * B.ROWSTAT_BYTES, dtype=torch.uint8, device=device)
         self.stat_ws = B.workspace(B.verify_workspace_bytes(M, V), device)
         self.acc_ws = B.workspace(B.accept_workspace_bytes(1, V), device)
-        self.tokens = torch.empty((1, M), dtype=i32, device=device)
-        self.n_acc = torch.empty(1, dtype=i32, device=device)
-        self.flags = torch.empty(1, dtype=i32, device=device)
+        self.tokens = self.outputs[:M].view(1, M)
+        self.n_acc = self.outputs[M:M + 1]
+        self.flags = self.outputs[M + 1:M + 2]
 
     def moe(self, x, router_logits, bank: ExpertBank, stream=None, gemm_hook=None):
         """y[M][d] (fp32) = routed SwiGLU experts of the bf16 rows x."""
