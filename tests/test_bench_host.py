@@ -1,0 +1,82 @@
+"""Host logic of bench.py (no GPU): the packed per-step input buffer, the
+telemetry summary and the lookup of the committed HBM-traffic figures."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_input_stage_layout_and_copy():
+    import torch
+    specs = [("x", (4, 5120), torch.int16), ("q", (3, 1001), torch.float32), ("d", (3,), torch.int32)]
+    st = bench.InputStage(specs, npool=5, device="cpu")
+    # 256-byte aligned offsets, in spec order, each region large enough
+    offs = [st.offs[n][0] for n, _, _ in specs]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert offs[1] >= 4 * 5120 * 2 and offs[2] >= offs[1] + 3 * 1001 * 4
+    assert st.nbytes % 256 == 0 and st.nbytes >= offs[2] + 12
+    # views alias the staging bytes and have the requested shapes and types
+    for name, shape, dt in specs:
+        v = st.view(name)
+        assert tuple(v.shape) == shape and v.dtype == dt
+        assert v.data_ptr() == st.stage.data_ptr() + st.offs[name][0]
+    # one load copies every input of a slot
+    g = torch.Generator().manual_seed(3)
+    for j in range(5):
+        st.slot(j, "x").copy_(torch.randint(-2**15, 2**15, (4, 5120), generator=g, dtype=torch.int16))
+        st.slot(j, "q").copy_(torch.rand((3, 1001), generator=g))
+        st.slot(j, "d").copy_(torch.tensor([j, j + 1, j + 2], dtype=torch.int32))
+    st.load(3)
+    for name, _, _ in specs:
+        assert torch.equal(st.view(name), st.slot(3, name))
+    assert st.view("d").tolist() == [3, 4, 5]
+
+
+def test_telemetry_summary_from_samples():
+    t = bench.Telemetry.__new__(bench.Telemetry)
+    t.period, t.error = 0.25, None
+    t.samples = [{"gfxclk_mhz": 2400.0, "uclk_mhz": 2000.0, "hotspot_c": 50.0, "hbm_c": 48.0, "socket_power_w": p}
+                 for p in (800.0, 900.0, 850.0)]
+    t.first = {"accumulation_counter": 100, "ppt_residency_acc": 10, "socket_thm_residency_acc": 0}
+    t.last = {"accumulation_counter": 300, "ppt_residency_acc": 60, "socket_thm_residency_acc": 0}
+    s = t.summary()
+    assert s["samples"] == 3 and s["socket_power_w"] == {"min": 800.0, "median": 850.0, "max": 900.0}
+    assert s["gfxclk_mhz"]["median"] == 2400.0
+    assert s["throttle_residency_frac"]["ppt"] == 0.25 and s["throttle_residency_frac"]["socket_thm"] == 0.0
+    # a list-valued clock (one per partition) reads as its maximum; "N/A" as missing
+    assert bench.Telemetry._num([2100, "N/A", 2390]) == 2390.0
+    assert bench.Telemetry._num("N/A") is None
+    empty = bench.Telemetry.__new__(bench.Telemetry)
+    empty.samples, empty.error = [], "no device"
+    assert empty.summary() == {"unavailable": "no device"}
+
+
+def test_measured_traffic_follows_the_committed_digest():
+    text = open(bench.TRAFFIC_FILE).read()
+    import re
+    m = re.search(r"^\| verify27b \| ([0-9]+) \| ([0-9]+) \| ([0-9]+) \|", text, re.M)
+    assert m, "the traffic summary lists verify27b"
+    # the reported figure is the per-launch total while the GEMM source has
+    # the digest the counters were taken with, and None otherwise
+    import hashlib
+    src = os.path.join(ROOT, "verify_step_w4_amd", "csrc", "w4_gemm.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    recorded = re.search(r"w4_gemm\.hip sha256: ([0-9a-f]{64})", text).group(1)
+    got = bench.measured_traffic("verify27b")
+    assert got == (int(m.group(3)) if digest == recorded else None)
+    assert bench.measured_traffic("no_such_workload") is None
+
+
+@pytest.mark.parametrize("argv", [["--gpus", "2"]])
+def test_more_than_one_gpu_is_refused(argv, monkeypatch):
+    monkeypatch.setattr(sys, "argv", ["bench.py"] + argv)
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert e.value.code == 2
