@@ -133,6 +133,39 @@ def _dense_cfg(layers, V):
     return c
 
 
+def test_full_size_layer_matches_oracle():
+    """One decoder layer at the 27B shapes (d 5120, GQA 40/8 x 128, FFN 17408)
+    over a context of 8192 positions at M = 4 -- the launch configuration of
+    the benchmark -- against the oracle's composition of the same layer (LM
+    head cut to 2048 rows; it is tested at full width elsewhere)."""
+    import torch
+    cfg = _dense_cfg(1, 2048)
+    M, L = 4, 8192
+    Lmax = L + M + 28                                   # a multiple of 32
+    log("full-size layer vs oracle (L=8192, M=4)")
+    hm = _host_model(cfg, 4343)
+    dec = Decoder(cfg, M, Lmax, weights=_device_weights(hm), kv_fill=False)
+    g = synth.rng(79)
+    Kh = [synth.f32_to_bf16_bits(synth.normal_f32(g, (cfg["nkv"], Lmax, cfg["hd"]), 1.0))]
+    Vh = [synth.f32_to_bf16_bits(synth.normal_f32(g, (cfg["nkv"], Lmax, cfg["hd"]), 1.0))]
+    dec.Kc[0].copy_(dev(Kh[0]))
+    dec.Vc[0].copy_(dev(vb_from_rows(Vh[0])).view(dec.Vc[0].shape))
+    x = synth.activations_bf16(80, M, cfg["d"])
+    logits = host(dec.forward(dev(x), L, M))
+    torch.cuda.synchronize()
+    ref = _oracle_forward(cfg, hm, Kh, Vh, x, L)
+    rms = np.sqrt((ref ** 2).mean(axis=1, keepdims=True))
+    rel = np.abs(logits - ref) / np.maximum(np.abs(ref), rms)
+    print(f"[full-size layer] max rel err {rel.max():.3e}, median {np.median(rel):.3e}", flush=True)
+    assert rel.max() < 2e-2
+    assert np.median(rel) < 2e-3
+    # the K and V rows the pass appended (identical inputs on both sides:
+    # bit-exact up to rare one-ulp rounding flips)
+    for gpu_c, ora_c in ((host(dec.Kc[0]), Kh[0]), (rows_from_vb(host(dec.Vc[0])), Vh[0])):
+        assert np.mean(gpu_c[:, L:L + M] == ora_c[:, L:L + M]) > 0.95
+        assert np.array_equal(gpu_c[:, :L], ora_c[:, :L])          # the context is untouched
+
+
 def test_verify_rows_equal_autoregressive_steps():
     import torch
     cfg = _dense_cfg(2, 4096)
