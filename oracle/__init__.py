@@ -90,6 +90,12 @@ def lib():
         L.oracle_decode_attn.argtypes = [_P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]
         L.oracle_moe_route.argtypes = [_P, _I64, _I64, _I64, _P, _P]
         L.oracle_swiglu_f64.argtypes = [_P, _P, _I64, _P]
+        L.oracle_mtp_input.argtypes = [_P, _P, _P, _P, _I64, _F64, _P]
+        L.oracle_embed_rows.argtypes = [_P, _I64, _I64, _P, _I64, _P]
+        L.oracle_draft_uniform.argtypes = [_U64, _U64, _I32]
+        L.oracle_draft_uniform.restype = _F64
+        L.oracle_draft_sample.argtypes = [_P, _I64, _F32, _F32, _U64, _U64, _I32, _P, ctypes.POINTER(WarpStat),
+                                          _P, _P]
         _lib = L
     return _lib
 
@@ -337,3 +343,46 @@ def moe_block(x_bf16: np.ndarray, router_logits: np.ndarray, topk: int, gate_up,
             a = bf16_round(swiglu(gu[:, :F], gu[:, F:]))
             y[m] += wt[m, t] * w4_gemm(a, dn_c[e], dn_s[e])[0]
     return ex, wt, y
+
+
+# --------------------------------------------------------------------------
+# the draft side of the cycle (the MTP head; NEXT row 1 of the hot path)
+# --------------------------------------------------------------------------
+def mtp_input(h_bf16: np.ndarray, e_bf16: np.ndarray, gamma_h: np.ndarray, gamma_e: np.ndarray,
+              eps: float = 1e-6) -> np.ndarray:
+    """[rmsnorm(h) * gamma_h ; rmsnorm(e) * gamma_e] in fp64; h, e, gammas: bf16 bits [d]."""
+    h = np.ascontiguousarray(h_bf16, dtype=np.uint16).reshape(-1)
+    e = np.ascontiguousarray(e_bf16, dtype=np.uint16).reshape(-1)
+    d = h.shape[0]
+    assert e.shape[0] == d
+    out = np.zeros(2 * d, dtype=np.float64)
+    lib().oracle_mtp_input(_ptr(h), _ptr(e), _ptr(np.ascontiguousarray(gamma_h, dtype=np.uint16)),
+                           _ptr(np.ascontiguousarray(gamma_e, dtype=np.uint16)), d, float(eps), _ptr(out))
+    return out
+
+
+def embed_rows(E: np.ndarray, tokens) -> np.ndarray:
+    """Rows E[tokens] of a bf16 [V][d] table; ids outside [0, V) give zero rows."""
+    E = np.ascontiguousarray(E, dtype=np.uint16)
+    V, d = E.shape
+    t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+    out = np.zeros((t.shape[0], d), dtype=np.uint16)
+    lib().oracle_embed_rows(_ptr(E), V, d, _ptr(t), t.shape[0], _ptr(out))
+    return out
+
+
+def draft_uniform(seed: int, step: int, depth: int) -> float:
+    return float(lib().oracle_draft_uniform(int(seed), int(step), int(depth)))
+
+
+def draft_sample(z: np.ndarray, temperature: float, top_p: float, seed: int, step: int, depth: int):
+    """One draft from logits z [V]: (token, q float32 [V], warp stats, flags)."""
+    z = np.ascontiguousarray(z, dtype=np.float32).reshape(-1)
+    V = z.shape[0]
+    q = np.zeros(V, dtype=np.float32)
+    st = WarpStat()
+    tok = np.zeros(1, dtype=np.int32)
+    fl = np.zeros(1, dtype=np.uint32)
+    lib().oracle_draft_sample(_ptr(z), V, float(temperature), float(top_p), int(seed), int(step), int(depth),
+                              _ptr(q), ctypes.byref(st), _ptr(tok), _ptr(fl))
+    return int(tok[0]), q, st, int(fl[0])

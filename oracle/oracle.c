@@ -580,3 +580,63 @@ EXPORT void oracle_moe_route(const float* logits, int64_t M, int64_t E, int64_t 
         free(used);
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* The draft side of the cycle.  [mtplx/4層] Layer 1: the drafter is the MTP   */
+/* head inside the same checkpoint; Layer 0: it has a 4-bit LM head of its    */
+/* own; Layer 2: each cycle drafts, then verifies.  The pages do not describe */
+/* the head's inside.  Reading (the common MTP head): the hidden row h of the */
+/* last processed position and the embedding e of the next token are each    */
+/* RMS-normalised with a gain of their own, concatenated [h ; e], projected   */
+/* back to d by a W4 matrix, passed through one decoder layer, the final norm */
+/* and the (shared, W4) LM head; D drafts apply the head D times, each time   */
+/* feeding its own output row and the token it just drew.                     */
+/* ------------------------------------------------------------------------ */
+
+/* Projection input of one draft: [rmsnorm(h) * gamma_h ; rmsnorm(e) * gamma_e],
+ * the exact fp64 values (the caller rounds to bfloat16). */
+EXPORT void oracle_mtp_input(const uint16_t* h_bf16, const uint16_t* e_bf16, const uint16_t* gamma_h,
+                             const uint16_t* gamma_e, int64_t d, double eps, double* out /* [2d] */) {
+    oracle_rmsnorm(h_bf16, gamma_h, 1, d, eps, out);
+    oracle_rmsnorm(e_bf16, gamma_e, 1, d, eps, out + d);
+}
+
+/* Token embedding rows: out[i] = E[tokens[i]]; an id outside [0, V) gives a
+ * row of zeros. */
+EXPORT void oracle_embed_rows(const uint16_t* E, int64_t V, int64_t d, const int32_t* tokens, int64_t n,
+                              uint16_t* out /* [n][d] */) {
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t t = tokens[i];
+        if (t >= 0 && t < V) memcpy(out + i * d, E + t * d, (size_t)d * sizeof(uint16_t));
+        else memset(out + i * d, 0, (size_t)d * sizeof(uint16_t));
+    }
+}
+
+/* Uniform of draft depth `depth` in cycle `step`: Philox4x64-10 with key
+ * (seed, 0) and counter (step, depth, 1, 0) -- the third word 1 keeps the
+ * draft stream apart from the verify's, whose third word is 0 -- second
+ * output word, 53 bits. */
+EXPORT double oracle_draft_uniform(uint64_t seed, uint64_t step, int32_t depth) {
+    const uint64_t key[2] = {seed, 0};
+    uint64_t ctr[4] = {step, (uint64_t)depth, 1, 0}, out[4];
+    oracle_philox4x64_10(key, ctr, out);
+    return u53(out[1]);
+}
+
+/* One draft: q = the warped distribution of the draft logits z (the same
+ * temperature / top-p reading as a verify row), written as binary32 for the
+ * verify's ratio test; the token is drawn from that distribution (fp64, index
+ * order, the inverse CDF of the acceptance step's sampler) at the draft
+ * uniform.  Reading: the drafter samples with the target's temperature and
+ * top-p. */
+EXPORT void oracle_draft_sample(const float* z, int64_t V, float temperature, float top_p, uint64_t seed,
+                                uint64_t step, int32_t depth, float* q_out /* nullable, [V] */,
+                                oracle_warp_t* st, int32_t* token, uint32_t* flags) {
+    double* p = (double*)calloc((size_t)V, sizeof(double));
+    oracle_warp(z, V, temperature, top_p, st, p);
+    if (q_out) for (int64_t j = 0; j < V; ++j) q_out[j] = (float)p[j];
+    const double u_acc = 0.0, u_res = oracle_draft_uniform(seed, step, depth);
+    int32_t n_acc;
+    oracle_accept_with_uniforms(z, st, NULL, NULL, 0, V, temperature, &u_acc, &u_res, token, &n_acc, flags);
+    free(p);
+}
