@@ -367,6 +367,52 @@ VW4_API int vw4_moe_combine(const float* part, int32_t S, int64_t ldp, int64_t p
                             const float* weights, int32_t M, int32_t topk, int32_t D, float* y, int64_t ldy,
                             void* stream);
 
+/* ------------------------------------------------------------------------
+ * The draft side of the cycle (hazakura.dev mtplx page, section
+ * "4層のアーキテクチャ": Layer 1, the drafter is the MTP head inside the same
+ * checkpoint; Layer 0, it has a 4-bit LM head; Layer 2, Draft -> Verify ->
+ * ratio acceptance -> residual correction -> bonus token).  The pages do not
+ * describe the head's inside; the common MTP head is built: the last hidden
+ * row and the next token's embedding, each RMS-normalised with its own gain,
+ * concatenated, projected back to d (a W4 GEMM), one decoder layer, the final
+ * norm and the LM head.  All pointers are device memory owned by the caller.
+ * ------------------------------------------------------------------------ */
+
+/* out[i][0:d] (row stride ldo) = E[tokens[i]][0:d] (E: [V][d] bf16, row
+ * stride lde), for i < n; an id outside [0, V) gives a row of zeros (ids are
+ * read on the device, so a captured graph can take new ones).  d % 8 == 0,
+ * strides multiples of 8, E and out 16-byte aligned, 1 <= n <= 65535. */
+VW4_API int vw4_embed_rows(const uint16_t* E, int64_t lde, int32_t V, int32_t d, const int32_t* tokens, int32_t n,
+                           uint16_t* out, int64_t ldo, void* stream);
+
+/* Projection input of one draft, out[0:2d] (bf16):
+ *   out[0:d]  = bf16(h_r * (1 / sqrt(mean(h_r^2) + eps)) * gamma_h), r = *h_row
+ *               (0 if h_row is NULL; clamped to [0, h_rows)), h_r = h + r * ldh;
+ *   out[d:2d] = the same of the embedding row E[*token] with gamma_e (a zero
+ *               row for an id outside [0, V)).
+ * Sums of squares in fp32.  8 <= d <= 8192, d % 8 == 0, strides multiples of
+ * 8, h, E, gains and out 16-byte aligned. */
+VW4_API int vw4_mtp_input(const uint16_t* h, int64_t ldh, int32_t h_rows, const int32_t* h_row, const uint16_t* E,
+                          int64_t lde, int32_t V, const int32_t* token, const uint16_t* gamma_h,
+                          const uint16_t* gamma_e, float eps, int32_t d, uint16_t* out, void* stream);
+
+/* One draft token from draft logits [V] (fp32) and their rowstat (from
+ * verify_logits with the target's temperature and top-p):
+ *   q_out (nullable) [V] = p(j) as binary32, p the warped distribution (the
+ *     q row the verify's spec_accept reads for this draft);
+ *   *token_out = min{ j : C_j > u * R } (inverse CDF of p in index order, fp64),
+ *     u = (r1 >> 11) 2^-53 of Philox4x64-10 with key (seed, 0) and counter
+ *     (step, depth, 1, 0): the third word 1 keeps drafts apart from the verify's
+ *     uniforms, whose third word is 0; step = *step_dev if step_dev is not NULL
+ *     (read when the kernels run), else the step argument;
+ *   *flags_out: VW4_FLAG_* bits (a non-finite row gives token -1).
+ * T == 0 is greedy (argmax, q one-hot).  1 <= V <= 2^24, 0 <= depth <= 1023.
+ * Workspace: vw4_draft_workspace_bytes(V), 256-byte aligned. */
+VW4_API size_t vw4_draft_workspace_bytes(int32_t V);
+VW4_API int draft_sample(const float* logits, const vw4_rowstat* stats, int32_t V, float temperature, uint64_t seed,
+                         const uint64_t* step_dev, uint64_t step, int32_t depth, float* q_out, int32_t* token_out,
+                         uint32_t* flags_out, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

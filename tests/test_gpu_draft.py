@@ -1,0 +1,237 @@
+"""The draft side of the cycle and the closed loop on the GPU.
+
+* Embedding rows and the MTP projection input against the oracle (bit-exact
+  rows; the normalised halves up to rare one-ulp bf16 flips).
+* draft_sample against the oracle on the same logits: the token bit-exact
+  outside the CDF-boundary flag, q within binary32 rounding; the device-step
+  form equals the host-step form.
+* One MTP-head draft step (projection, one decoder layer, final norm, LM head)
+  against the oracle's composition on a small model.
+* The closed loop at T = 0 emits exactly the greedy autoregressive sequence,
+  with the head's drafts (mostly rejected on random weights) and with drafts
+  that are the greedy continuation (all accepted); at T = 0.6 it is
+  deterministic and every cycle emits 1 .. D + 1 tokens.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from verify_step_w4_amd import binding as B
+from verify_step_w4_amd import synth
+from verify_step_w4_amd.model import DENSE_27B, Decoder, MTPHead, SpecLoop, W4Linear
+
+from helpers import dev, host, log, rows_from_vb, vb_from_rows
+from test_gpu_forward import TINY, _device_weights, _host_model, _oracle_forward
+
+pytestmark = pytest.mark.gpu
+SEED = 0x5EED0007
+
+
+def _stats_dev(logits_dev, T, top_p):
+    import torch
+    rows, V = logits_dev.shape
+    st = torch.zeros(rows * B.ROWSTAT_BYTES, dtype=torch.uint8, device="cuda")
+    ws = B.workspace(B.verify_workspace_bytes(rows, V), "cuda")
+    B.verify_logits(None, None, None, rows, V, 64, T, top_p, logits_dev, st, ws)
+    return st
+
+
+def test_embed_rows_match_oracle():
+    import torch
+    V, d = 1000, 256
+    E = synth.f32_to_bf16_bits(synth.normal_f32(synth.rng(5), (V, d), 1.0))
+    tok = np.array([3, 0, V - 1, -1, V, 3, 517], dtype=np.int32)
+    out = torch.zeros((len(tok), d), dtype=torch.int16, device="cuda")
+    log("embed rows")
+    B.embed_rows(dev(E), dev(tok), len(tok), out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out), oracle.embed_rows(E, tok))
+
+
+@pytest.mark.parametrize("d", [256, 5120, 8192])
+@pytest.mark.parametrize("row,token", [(2, 7), (-1, 0), (9, -3), (3, 999)])
+def test_mtp_input_matches_oracle(d, row, token):
+    import torch
+    V, rows = 1000, 4
+    g = synth.rng(d + 17)
+    E = synth.f32_to_bf16_bits(synth.normal_f32(g, (V, d), 1.0))
+    h = synth.f32_to_bf16_bits(synth.normal_f32(g, (rows, d), 3.0))
+    gh = synth.f32_to_bf16_bits(1 + synth.normal_f32(g, (d,), 0.02))
+    ge = synth.f32_to_bf16_bits(1 + synth.normal_f32(g, (d,), 0.02))
+    out = torch.zeros((1, 2 * d), dtype=torch.int16, device="cuda")
+    log(f"mtp input d={d} row={row} token={token}")
+    B.mtp_input(dev(h), rows, dev(np.array([row], np.int32)), dev(E), dev(np.array([token], np.int32)), dev(gh),
+                dev(ge), 1e-6, out)
+    torch.cuda.synchronize()
+    r = min(max(row, 0), rows - 1)
+    e = oracle.embed_rows(E, [token])[0]
+    ref = oracle.bf16_round(oracle.mtp_input(h[r], e, gh, ge, 1e-6))
+    got = host(out)[0]
+    a = synth.bf16_bits_to_f32(got).astype(np.float64)
+    b = synth.bf16_bits_to_f32(ref).astype(np.float64)
+    assert np.mean(got == ref) > 0.99
+    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 1e-30)       # at most one bf16 ulp apart
+    if not 0 <= token < V:
+        assert not got[d:].any()                                      # zero embedding row
+
+
+@pytest.mark.parametrize("V", [1000, 151936])
+@pytest.mark.parametrize("T,top_p", [(0.0, 0.95), (0.6, 0.95), (1.0, 1.0), (0.6, 0.5)])
+def test_draft_sample_matches_oracle(V, T, top_p):
+    import torch
+    z = synth.normal_f32(synth.rng(V + int(10 * T)), (V,), 3.0)
+    zd = dev(z.reshape(1, V))
+    st = _stats_dev(zd, T, top_p)
+    ws = B.workspace(B.draft_workspace_bytes(V), "cuda")
+    q = torch.zeros(V, dtype=torch.float32, device="cuda")
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    step_dev = torch.zeros(1, dtype=torch.int64, device="cuda")
+    log(f"draft_sample V={V} T={T} top_p={top_p}")
+    mism = flagged = 0
+    for step, depth in [(0, 0), (1, 0), (5, 2), (2 ** 33 + 1, 6), (77, 1), (78, 1), (79, 3), (1000, 0)]:
+        B.draft_sample(zd, st, V, T, SEED, step, depth, q, tok, fl, ws)
+        torch.cuda.synchronize()
+        t_ref, q_ref, _, f_ref = oracle.draft_sample(z, T, top_p, SEED, step, depth)
+        if (int(host(fl)[0]) | f_ref) & 8:
+            flagged += 1
+        elif int(host(tok)[0]) != t_ref:
+            mism += 1
+        np.testing.assert_allclose(host(q).astype(np.float64), q_ref.astype(np.float64), rtol=1e-6, atol=0)
+        # the device-step form draws the same token
+        step_dev.fill_(step)
+        tok2 = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+        B.draft_sample(zd, st, V, T, SEED, 0, depth, None, tok2, fl, ws, step_dev=step_dev)
+        torch.cuda.synchronize()
+        assert int(host(tok2)[0]) == int(host(tok)[0])
+    assert mism == 0 and flagged <= 1
+
+
+def _head_host(cfg, seed):
+    g = synth.rng(seed)
+    d = cfg["d"]
+    lay = _host_model(dict(cfg, layers=1), seed + 1)["layers"][0]
+    return dict(proj=synth.normal_f32(g, (d, 2 * d), 0.02), layer=lay,
+                gamma_h=synth.f32_to_bf16_bits(1 + synth.normal_f32(g, (d,), 0.02)),
+                gamma_e=synth.f32_to_bf16_bits(1 + synth.normal_f32(g, (d,), 0.02)),
+                final_gamma=synth.f32_to_bf16_bits(1 + synth.normal_f32(g, (d,), 0.02)))
+
+
+def test_mtp_draft_step_matches_oracle():
+    import torch
+    cfg = TINY
+    d, V, Lmax, pos = cfg["d"], cfg["V"], 64, 29
+    log("MTP head draft step vs oracle, small model")
+    hm = _host_model(cfg, 4242)
+    target = Decoder(cfg, 4, Lmax, weights=_device_weights(hm), kv_fill=False)
+    E = synth.f32_to_bf16_bits(synth.normal_f32(synth.rng(91), (V, d), 1.0))
+    hh = _head_host(cfg, 93)
+    dl = _device_weights(dict(layers=[hh["layer"]], final_gamma=hh["final_gamma"], lm_head=hm["lm_head"]))
+    head = MTPHead(target, dev(E), kv_fill=False,
+                   weights=dict(gamma_h=dev(hh["gamma_h"]), gamma_e=dev(hh["gamma_e"]),
+                                final_gamma=dl["final_gamma"], layer=dl["layers"][0],
+                                proj=W4Linear.from_fp32(dev(hh["proj"]))))
+    g = synth.rng(95)
+    Kh = synth.f32_to_bf16_bits(synth.normal_f32(g, (cfg["nkv"], Lmax, cfg["hd"]), 1.0))
+    Vh = synth.f32_to_bf16_bits(synth.normal_f32(g, (cfg["nkv"], Lmax, cfg["hd"]), 1.0))
+    head.block.Kc[0].copy_(dev(Kh))
+    head.block.Vc[0].copy_(dev(vb_from_rows(Vh)).view(head.block.Vc[0].shape))
+    h = synth.activations_bf16(96, 3, d)
+    token = 411
+    q = torch.zeros(V, dtype=torch.float32, device="cuda")
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    T, top_p = 0.6, 0.95
+    logits = host(head.draft(dev(h), 3, dev(np.array([1], np.int32)), dev(np.array([token], np.int32)), pos, T,
+                             top_p, SEED, 12, 2, q, tok)).copy()
+    torch.cuda.synchronize()
+    # oracle: projection input, projection, then the one-layer decoder composition
+    inp = oracle.bf16_round(oracle.mtp_input(h[1], E[token], hh["gamma_h"], hh["gamma_e"], cfg["eps"]))
+    x = oracle.bf16_round(oracle.w4_gemm(inp.reshape(1, -1), *oracle.w4_quantize(hh["proj"])))
+    bm = dict(layers=[hh["layer"]], final_gamma=hh["final_gamma"], lm_head=hm["lm_head"])
+    ref = _oracle_forward(dict(cfg, layers=1), bm, [Kh.copy()], [Vh.copy()], x, pos)
+    rms = np.sqrt((ref ** 2).mean(axis=1, keepdims=True))
+    rel = np.abs(logits - ref) / np.maximum(np.abs(ref), rms)
+    print(f"[mtp draft] max rel err {rel.max():.3e}, median {np.median(rel):.3e}", flush=True)
+    assert rel.max() < 2e-2 and np.median(rel) < 2e-3
+    # the draw, from the GPU's own logits, is the oracle's
+    t_ref, q_ref, _, f_ref = oracle.draft_sample(logits[0], T, top_p, SEED, 12, 2)
+    assert (f_ref & 8) or int(host(tok)[0]) == t_ref
+    np.testing.assert_allclose(host(q).astype(np.float64), q_ref.astype(np.float64), rtol=1e-6, atol=0)
+
+
+def _loop_setup(seed, D, L0):
+    import torch
+    cfg = dict(DENSE_27B, layers=2, V=4096)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    target = Decoder(cfg, D + 1, L0 + 64, gen=gen)
+    E = torch.randn((cfg["V"], cfg["d"]), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
+    head = MTPHead(target, E, gen=gen)
+    kv = ([k.clone() for k in target.Kc], [v.clone() for v in target.Vc],
+          [k.clone() for k in head.block.Kc], [v.clone() for v in head.block.Vc])
+    return target, head, kv
+
+
+def _reset(target, head, kv):
+    for dst, src in zip((target.Kc, target.Vc, head.block.Kc, head.block.Vc), kv):
+        for a, b in zip(dst, src):
+            a.copy_(b)
+
+
+def _ar_sequence(target, head, kv, L0, t0, n, T, top_p):
+    _reset(target, head, kv)
+    loop = SpecLoop(target, head, 1)
+    seq = [loop.start(L0, t0, T, top_p, SEED, 0)]
+    while len(seq) < n:
+        loop.tokens_in[:1].fill_(seq[-1])
+        B.embed_rows(head.embed, loop.tokens_in, 1, loop.x)
+        tok, _, _ = loop.ar_vs.run(loop.x, loop.L, None, None, T, top_p, SEED, len(seq))
+        seq.append(int(tok.view(-1)[0].item()))
+        loop.L += 1
+    return seq
+
+
+def test_spec_loop_greedy_equals_autoregressive():
+    import torch
+    D, L0, t0, n = 3, 700, 123, 14
+    log("closed loop at T = 0 vs greedy AR (2 layers, full width)")
+    target, head, kv = _loop_setup(21, D, L0)
+    ar = _ar_sequence(target, head, kv, L0, t0, n + D + 1, 0.0, 0.95)
+    # the head's drafts
+    _reset(target, head, kv)
+    loop = SpecLoop(target, head, D)
+    seq = [loop.start(L0, t0, 0.0, 0.95, SEED, 0)]
+    cycles = 0
+    while len(seq) < n:
+        seq += loop.cycle(0.0, 0.95, SEED, cycles + 1)
+        cycles += 1
+    assert seq[:n] == ar[:n], (seq, ar)
+    assert loop.L == L0 + len(seq)
+    # drafts that are the greedy continuation: every cycle accepts all D
+    _reset(target, head, kv)
+    loop = SpecLoop(target, head, D)
+    seq = [loop.start(L0, t0, 0.0, 0.95, SEED, 0)]
+    while len(seq) + D + 1 <= len(ar):
+        drafts = torch.tensor(ar[len(seq):len(seq) + D], dtype=torch.int32, device="cuda")
+        out = loop.cycle(0.0, 0.95, SEED, len(seq), drafts=drafts)
+        assert len(out) == D + 1
+        seq += out
+    assert seq == ar[:len(seq)] and len(seq) >= n
+
+
+def test_spec_loop_sampling_deterministic():
+    D, L0, t0 = 3, 500, 77
+    log("closed loop at T = 0.6: determinism and cycle invariants")
+    target, head, kv = _loop_setup(22, D, L0)
+    runs = []
+    for rep in range(2):
+        _reset(target, head, kv)
+        loop = SpecLoop(target, head, D)
+        seq = [loop.start(L0, t0, 0.6, 0.95, SEED, 0)]
+        for c in range(6):
+            out = loop.cycle(0.6, 0.95, SEED, c + 1)
+            assert 1 <= len(out) <= D + 1 and all(0 <= t < 4096 for t in out)
+            seq += out
+        assert loop.L == L0 + len(seq)
+        runs.append(seq)
+    assert runs[0] == runs[1]

@@ -57,6 +57,10 @@ SIGNATURES = {
     "spec_accept_ex": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _I64, _P, _I32, _I32, _I32, _F32, _U64, _P, _P, _P,
                                       _P, _P, _SZ, _P]),
     "vw4_step_advance": (ctypes.c_int, [_P, _U64, _P]),
+    "vw4_embed_rows": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I32, _P, _I64, _P]),
+    "vw4_mtp_input": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _I64, _I32, _P, _P, _P, ctypes.c_float, _I32, _P, _P]),
+    "vw4_draft_workspace_bytes": (_SZ, [_I32]),
+    "draft_sample": (ctypes.c_int, [_P, _P, _I32, ctypes.c_float, _U64, _P, _U64, _I32, _P, _P, _P, _P, _SZ, _P]),
     "vw4_gemm_partials_layout": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
                                                 ctypes.POINTER(ctypes.c_int64)]),
     "w4_skinny_gemm_partials": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I32, _I32, _I32, _P]),
@@ -276,6 +280,32 @@ def spec_accept_ex(logits, logits_bstride: int, stats, stats_bstride: int, q, q_
 
 def step_advance(step_dev, inc: int = 1, stream=None):
     _check("vw4_step_advance", lib().vw4_step_advance(_ptr(step_dev), int(inc), _stream(stream)))
+
+
+def embed_rows(E, tokens, n: int, out, stream=None):
+    """out[i] = E[tokens[i]] for i < n (bf16 bit tensors; tokens int32 on the device)."""
+    V, d = E.shape
+    _check("vw4_embed_rows", lib().vw4_embed_rows(_ptr(E), E.stride(0), V, d, _ptr(tokens), n, _ptr(out),
+                                                  out.stride(0), _stream(stream)))
+
+
+def mtp_input(h, h_rows: int, h_row, E, token, gamma_h, gamma_e, eps: float, out, stream=None):
+    """out[0:2d] = [rmsnorm(h[*h_row]) * gamma_h ; rmsnorm(E[*token]) * gamma_e] (bf16)."""
+    V, d = E.shape
+    _check("vw4_mtp_input", lib().vw4_mtp_input(_ptr(h), h.stride(0), h_rows, _ptr(h_row), _ptr(E), E.stride(0), V,
+                                                _ptr(token), _ptr(gamma_h), _ptr(gamma_e), float(eps), d, _ptr(out),
+                                                _stream(stream)))
+
+
+def draft_workspace_bytes(V: int) -> int:
+    return int(lib().vw4_draft_workspace_bytes(V))
+
+
+def draft_sample(logits, stats, V: int, temperature: float, seed: int, step: int, depth: int, q_out, token_out,
+                 flags_out, ws, step_dev=None, stream=None):
+    _check("draft_sample", lib().draft_sample(_ptr(logits), _ptr(stats), V, float(temperature), int(seed),
+                                              _ptr(step_dev), int(step), int(depth), _ptr(q_out), _ptr(token_out),
+                                              _ptr(flags_out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def rowstats_to_numpy(stats_tensor) -> np.ndarray:

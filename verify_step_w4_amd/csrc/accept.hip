@@ -183,14 +183,15 @@ template <int NT>
 __device__ __forceinline__ ProblemState problem_state(const float* __restrict__ zb, const vw4_rowstat* __restrict__ sb,
                                                       const float* __restrict__ qb, const int32_t* __restrict__ db,
                                                       int D, int V, double T, uint64_t seed, uint64_t step,
-                                                      double* s_u, vw4_rowstat* s_st) {
+                                                      uint64_t row0, uint64_t cstream, double* s_u,
+                                                      vw4_rowstat* s_st) {
     __shared__ double s_p[AMAXD + 1], s_q[AMAXD + 1];
     __shared__ int s_ok[AMAXD + 1];
     // thread i (<= D): row i's uniforms, statistics, and p_i(x_i), q_i(x_i) --
     // all rows' loads in flight together
     if (threadIdx.x <= D) {
         const int i = threadIdx.x;
-        uint64_t c[4] = {step, (uint64_t)i, 0, 0};
+        uint64_t c[4] = {step, row0 + (uint64_t)i, cstream, 0};
         philox4x64_10(seed, 0, c);
         s_u[2 * i] = unit53(c[0]);
         s_u[2 * i + 1] = unit53(c[1]);
@@ -418,6 +419,7 @@ struct AcceptArgs {
     AcceptPart* parts;
     ProblemSlot* states;   // per problem, written by workgroup 0 of the chunk kernel
     const uint64_t* step_dev;  // if set, the first problem's step is read here (graph replays)
+    uint64_t row0, cstream;    // Philox counter words 1 (row offset) and 2 (stream): 0 for verify
 };
 
 __device__ __forceinline__ uint64_t first_step(const AcceptArgs& a) { return a.step_dev ? *a.step_dev : a.step0; }
@@ -447,7 +449,7 @@ __global__ __launch_bounds__(NT) void accept_chunk_kernel(AcceptArgs a) {
     const int32_t* db = a.draft + b * a.D;
     const double T = (double)a.temperature;
     const ProblemState ps =
-        problem_state<NT>(zb, sb, qb, db, a.D, a.V, T, a.seed, first_step(a) + (uint64_t)b, s_u, s_st);
+        problem_state<NT>(zb, sb, qb, db, a.D, a.V, T, a.seed, first_step(a) + (uint64_t)b, a.row0, a.cstream, s_u, s_st);
     if (ps.bad) {
         if (w == 0) write_bad(a, b);
         return;
@@ -527,7 +529,7 @@ __global__ __launch_bounds__(64) void accept_greedy_kernel(AcceptArgs a) {
     const float* qb = a.q ? a.q + b * a.qstride : nullptr;
     const int32_t* db = a.draft + b * a.D;
     const ProblemState ps =
-        problem_state<64>(zb, sb, qb, db, a.D, a.V, 0.0, a.seed, first_step(a) + (uint64_t)b, s_u, s_st);
+        problem_state<64>(zb, sb, qb, db, a.D, a.V, 0.0, a.seed, first_step(a) + (uint64_t)b, a.row0, a.cstream, s_u, s_st);
     if (ps.bad) {
         write_bad(a, b);
         return;
@@ -560,7 +562,7 @@ static int spec_accept_impl(const float* logits, int64_t logits_bstride, const v
                             int64_t stats_bstride, const float* q, int64_t q_bstride, const int32_t* draft, int32_t B,
                             int32_t D, int32_t V, float temperature, uint64_t seed, uint64_t step0,
                             const uint64_t* step_dev, int32_t* out_tokens, int32_t* out_n_acc, uint32_t* out_flags,
-                            void* ws, size_t ws_bytes, void* stream) {
+                            void* ws, size_t ws_bytes, void* stream, uint64_t row0 = 0, uint64_t cstream = 0) {
     VW4_REQUIRE(B >= 1 && B <= (1 << 24), VW4_EINVAL, "spec_accept: B=%d out of range", B);
     VW4_REQUIRE(D >= 0 && D <= AMAXD, VW4_EINVAL, "spec_accept: D=%d must be in [0, 7]", D);
     VW4_REQUIRE(V >= 1 && V <= (1 << 24), VW4_EINVAL, "spec_accept: V=%d out of range", V);
@@ -582,6 +584,7 @@ static int spec_accept_impl(const float* logits, int64_t logits_bstride, const v
     a.parts = (AcceptPart*)((char*)ws + L.off_part);
     a.states = (ProblemSlot*)((char*)ws + L.off_state);
     a.step_dev = step_dev;
+    a.row0 = row0; a.cstream = cstream;
     hipStream_t st = (hipStream_t)stream;
     if (temperature == 0.0f) {
         hipLaunchKernelGGL(accept_greedy_kernel, dim3((unsigned)B), dim3(64), 0, st, a);
@@ -599,6 +602,17 @@ static int spec_accept_impl(const float* logits, int64_t logits_bstride, const v
     return check_launch("spec_accept");
 }
 
+
+// q[j] = p(j) of one warped row as binary32 (the draft distribution the
+// verify's ratio test reads); grid over V, 256 threads.
+__global__ __launch_bounds__(256) void draft_q_kernel(const float* __restrict__ z, const vw4_rowstat* __restrict__ st,
+                                                      int V, double T, float* __restrict__ q) {
+    const vw4_rowstat s = *st;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j < V) q[j] = (float)p_val(z[j], s, T, j);
+}
+
+static size_t draft_ws_tail(int V) { return (accept_layout(1, V).total + 255) / 256 * 256; }
 
 }  // namespace vw4
 
@@ -627,6 +641,34 @@ int spec_accept_ex(const float* logits, int64_t logits_bstride, const vw4_rowsta
     VW4_REQUIRE(step_dev && aligned(step_dev, 8), VW4_EINVAL, "spec_accept_ex: step_dev must be an 8-byte aligned device pointer");
     return spec_accept_impl(logits, logits_bstride, stats, stats_bstride, q, q_bstride, draft, B, D, V, temperature,
                             seed, 0, step_dev, out_tokens, out_n_acc, out_flags, ws, ws_bytes, stream);
+}
+
+size_t vw4_draft_workspace_bytes(int32_t V) {
+    if (V < 1 || V > (1 << 24)) return 0;
+    return draft_ws_tail(V) + 256;
+}
+
+int draft_sample(const float* logits, const vw4_rowstat* stats, int32_t V, float temperature, uint64_t seed,
+                 const uint64_t* step_dev, uint64_t step, int32_t depth, float* q_out, int32_t* token_out,
+                 uint32_t* flags_out, void* ws, size_t ws_bytes, void* stream) {
+    VW4_REQUIRE(logits && stats && token_out && flags_out, VW4_EINVAL, "draft_sample: null pointer");
+    VW4_REQUIRE(V >= 1 && V <= (1 << 24), VW4_EINVAL, "draft_sample: V=%d out of range", V);
+    VW4_REQUIRE(depth >= 0 && depth <= 1023, VW4_EINVAL, "draft_sample: depth=%d out of range", depth);
+    VW4_REQUIRE(!step_dev || aligned(step_dev, 8), VW4_EINVAL, "draft_sample: step_dev must be 8-byte aligned");
+    VW4_REQUIRE(isfinite(temperature) && temperature >= 0.0f, VW4_EINVAL, "draft_sample: temperature must be >= 0");
+    const size_t tail = draft_ws_tail(V);
+    VW4_REQUIRE(ws && ws_bytes >= tail + 256 && aligned(ws, 256), VW4_EWORKSPACE,
+                "draft_sample: needs a 256-byte aligned workspace of %zu bytes", tail + 256);
+    hipStream_t st = (hipStream_t)stream;
+    if (q_out) {
+        hipLaunchKernelGGL(draft_q_kernel, dim3((unsigned)ceil_div(V, 256)), dim3(256), 0, st, logits, stats, V,
+                           (double)temperature, q_out);
+        const int rc = check_launch("draft_sample");
+        if (rc != VW4_OK) return rc;
+    }
+    int32_t* n_acc = (int32_t*)((char*)ws + tail);
+    return spec_accept_impl(logits, 0, stats, 0, nullptr, 0, nullptr, 1, 0, V, temperature, seed, step, step_dev,
+                            token_out, n_acc, flags_out, ws, tail, stream, (uint64_t)depth, 1);
 }
 
 int vw4_step_advance(uint64_t* step_dev, uint64_t inc, void* stream) {

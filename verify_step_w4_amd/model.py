@@ -224,6 +224,7 @@ class Decoder:
             hook("post", "down")
             g_next = lay[li + 1]["g1"] if li + 1 < len(lay) else self.final_gamma
             add_norm(self.parts["down"], S, ldp, g_next)
+        self.last_resid = cur[0]         # residual rows after the last layer (before the final norm)
         hook("pre", "lm_head")
         B.w4_skinny_gemm(h, self.lm_head.packed, self.lm_head.pscales, self.logits[:M], M, c["V"], d,
                          ws=self.lm_ws, stream=stream)
@@ -325,6 +326,142 @@ class VerifyStep:
                       out.get("tokens", self.tokens), out.get("n_acc", self.n_acc), out.get("flags", self.flags),
                       self.acc_ws, stream=stream)
         return self.tokens, self.n_acc, self.flags
+
+
+# ---------------------------------------------------------------------------
+# The draft side and the closed cycle: MTP head -> verify -> accept
+# ---------------------------------------------------------------------------
+class MTPHead:
+    """The drafter: the MTP head of the same checkpoint (hazakura.dev mtplx page,
+    section "4層のアーキテクチャ", Layers 0-2).  The pages do not describe its
+    inside; this is the common MTP head: the hidden row h of the last processed
+    position and the embedding of the next token, each RMS-normalised with its
+    own gain and concatenated, a W4 projection from 2d back to d, one decoder
+    layer (own KV cache), the final norm and the target's W4 LM head.  One
+    ``draft`` call is one depth: its output row and drawn token feed the next."""
+
+    def __init__(self, target: "Decoder", embed, gen=None, weights=None, kv_fill: bool = True):
+        import torch
+        cfg = dict(target.cfg, layers=1)
+        d, V = cfg["d"], cfg["V"]
+        dev = target.device
+        if weights is None:
+            weights = self.random_weights(cfg, gen, dev)
+        self.cfg, self.embed = cfg, embed
+        self.gamma_h, self.gamma_e, self.proj = weights["gamma_h"], weights["gamma_e"], weights["proj"]
+        self.block = Decoder(cfg, 1, target.Lmax, gen=gen, device=dev, kv_fill=kv_fill,
+                             weights=dict(layers=[weights["layer"]], final_gamma=weights["final_gamma"],
+                                          lm_head=target.lm_head))
+        self.inp = torch.empty((1, 2 * d), dtype=torch.int16, device=dev)
+        self.x = torch.empty((1, d), dtype=torch.int16, device=dev)
+        self.proj_ws = B.workspace(B.gemm_workspace_bytes(1, d, 2 * d), dev)
+        self.stats = torch.zeros(B.ROWSTAT_BYTES, dtype=torch.uint8, device=dev)
+        self.stat_ws = B.workspace(B.verify_workspace_bytes(1, V), dev)
+        self.ws = B.workspace(B.draft_workspace_bytes(V), dev)
+        self.flags = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    @staticmethod
+    def random_weights(cfg: dict, gen, device="cuda"):
+        import torch
+        d = cfg["d"]
+
+        def gamma():
+            return (1.0 + 0.02 * torch.randn(d, generator=gen, device=device)).to(torch.bfloat16).view(torch.int16)
+
+        lay = Decoder.random_weights(dict(cfg, layers=1, V=1), gen, device)["layers"][0]
+        return dict(gamma_h=gamma(), gamma_e=gamma(), final_gamma=gamma(), layer=lay,
+                    proj=W4Linear.random(d, 2 * d, 0.02, gen, device))
+
+    def draft(self, h, h_rows: int, h_row, token, pos: int, T: float, top_p: float, seed: int, step, depth: int,
+              q_out, token_out, stream=None):
+        """One depth at position pos: h [h_rows][d] (row *h_row, or 0 if h_row is
+        None), token (int32 on the device) -> q_out [V] (fp32 draft distribution)
+        and token_out (the drawn draft).  step: an int, or an int64 device
+        tensor read when the kernels run."""
+        c = self.cfg
+        d, V = c["d"], c["V"]
+        B.mtp_input(h, h_rows, h_row, self.embed, token, self.gamma_h, self.gamma_e, c["eps"], self.inp, stream)
+        B.w4_skinny_gemm(self.inp, self.proj.packed, self.proj.pscales, self.x, 1, d, 2 * d, ws=self.proj_ws,
+                         stream=stream)
+        logits = self.block.forward(self.x, pos, 1, stream)
+        B.verify_logits(None, None, None, 1, V, d, T, top_p, logits, self.stats, self.stat_ws, stream=stream)
+        dev_step = step if hasattr(step, "data_ptr") else None
+        B.draft_sample(logits, self.stats, V, T, seed, 0 if dev_step is not None else step, depth, q_out,
+                       token_out, self.flags, self.ws, step_dev=dev_step, stream=stream)
+        return logits
+
+
+class SpecLoop:
+    """The closed cycle (hazakura.dev mtplx page, "4層のアーキテクチャ" Layer 2):
+    D drafts from the MTP head, one verify pass of the target over M = D + 1
+    rows, Leviathan–Chen acceptance with residual / bonus sampling.  State
+    between cycles: L positions processed (0 .. L-1 in the KV caches), the
+    target's residual row h of position L-1 and the next token y (position L,
+    not processed yet).  A cycle emits the accepted drafts and the corrected or
+    bonus token; rejected positions need no rollback beyond L, whose rows the
+    next cycle overwrites.  The verify rows are the embedding rows of
+    [y, x_0 .. x_{D-1}] at positions L .. L+D."""
+
+    def __init__(self, target: "Decoder", head: MTPHead, D: int):
+        import torch
+        assert 1 <= D <= 7 and D + 1 <= target.M_max
+        dev = target.device
+        V, d = target.cfg["V"], target.cfg["d"]
+        self.target, self.head, self.D = target, head, D
+        self.vs = VerifyStep(target, D + 1)
+        self.tokens_in = torch.zeros(D + 1, dtype=torch.int32, device=dev)     # y, x_0 .. x_{D-1}
+        self.q = torch.zeros((D, V), dtype=torch.float32, device=dev)
+        self.x = torch.empty((D + 1, d), dtype=torch.int16, device=dev)
+        self.h_row = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.h_src, self.h_rows = None, 1
+        self.ar_vs = VerifyStep(target, 1)
+        self.L = 0
+
+    def start(self, L0: int, t0: int, T: float, top_p: float, seed: int, step: int):
+        """Process token t0 at position L0 (an autoregressive step) and draw y."""
+        self.tokens_in[:1].fill_(int(t0))
+        B.embed_rows(self.head.embed, self.tokens_in, 1, self.x)
+        tok, n_acc, flags = self.ar_vs.run(self.x, L0, None, None, T, top_p, seed, step)
+        self.tokens_in[:1].copy_(tok.view(-1)[:1])
+        self.h_src, self.h_rows = self.target.last_resid, 1
+        self.h_row.zero_()
+        self.L = L0 + 1
+        return int(tok.view(-1)[0].item())
+
+    def draft(self, T: float, top_p: float, seed: int, step):
+        """D head steps from (h, y) at positions L-1 .. L+D-2; fills q and x_0 ..."""
+        head, D = self.head, self.D
+        h, rows, row = self.h_src, self.h_rows, self.h_row
+        for i in range(D):
+            head.draft(h, rows, row, self.tokens_in[i:i + 1], self.L - 1 + i, T, top_p, seed, step, i, self.q[i],
+                       self.tokens_in[i + 1:i + 2])
+            h, rows, row = head.block.last_resid, 1, None
+
+    def verify(self, T: float, top_p: float, seed: int, step: int):
+        D, M = self.D, self.D + 1
+        B.embed_rows(self.head.embed, self.tokens_in, M, self.x)
+        return self.vs.run(self.x, self.L, self.q, self.tokens_in[1:], T, top_p, seed, step)
+
+    def cycle(self, T: float, top_p: float, seed: int, step: int, drafts=None):
+        """One cycle; returns the emitted tokens (host list).  drafts (int32
+        device [D]) replaces the head's drafts (with one-hot q): any other
+        drafter can drive the same verify."""
+        if drafts is None:
+            self.draft(T, top_p, seed, step)
+        else:
+            self.tokens_in[1:].copy_(drafts)
+            self.q.zero_()
+            self.q.scatter_(1, drafts.view(-1, 1).long(), 1.0)
+        tok, n_acc, flags = self.verify(T, top_p, seed, step)
+        k = int(n_acc.item())
+        out = tok.view(-1)[:k + 1].tolist()
+        if k < 0:
+            raise RuntimeError("verify rows were not finite")
+        self.tokens_in[:1].copy_(tok.view(-1)[k:k + 1])
+        self.h_src, self.h_rows = self.target.last_resid, self.D + 1
+        self.h_row.fill_(k)
+        self.L += k + 1
+        return out
 
 
 # ---------------------------------------------------------------------------
