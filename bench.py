@@ -637,6 +637,119 @@ def verify27b_workload(args):
     return res
 
 
+def tokens_per_cycle(alpha: float, D: int) -> float:
+    """Expected tokens a cycle emits when each of the D drafts is accepted
+    with probability alpha independently (Leviathan, Kalman, Matias, ICML
+    2023): the accepted prefix plus the corrected or bonus token,
+    (1 - alpha^(D+1)) / (1 - alpha)."""
+    return D + 1.0 if alpha >= 1.0 else (1.0 - alpha ** (D + 1)) / (1.0 - alpha)
+
+
+def spec_loop_workload(args):
+    """The closed cycle on the 27B-shaped model: D drafts of the MTP head (one
+    decoder layer + projection + the shared W4 LM head each), one verify pass
+    over D + 1 rows, acceptance.  Each cycle (and the M = 1 AR step) is
+    captured as a HIP graph at context L and replayed; acceptance is measured
+    on an eager run of real cycles (random weights: the head's drafts are
+    independent of the target, so few are accepted), and the tokens/s of each
+    depth follow for per-draft acceptance rates alpha from
+    E[tokens per cycle] = (1 - alpha^(D+1)) / (1 - alpha)."""
+    import numpy as np
+    import torch
+
+    from verify_step_w4_amd import binding as B
+    from verify_step_w4_amd.model import DENSE_27B, Decoder, MTPHead, SpecLoop
+
+    cfg = dict(DENSE_27B)
+    L = args.context
+    T, top_p, seed = 0.6, 0.95, 0x5EED0008
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20261208)
+    V, d = cfg["V"], cfg["d"]
+    log(f"generating the 64-layer W4 decoder, the MTP head and a {V} x {d} bf16 embedding table; context {L}")
+    dec = Decoder(cfg, 4, L + 72, gen=gen)
+    E = torch.randn((V, d), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+    head = MTPHead(dec, E, gen=gen)
+    torch.cuda.synchronize()
+    K, W = max(10, args.steps // 4), max(3, args.warmup // 4)
+
+    def time_graph(g, reps):
+        for _ in range(W):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    depths = {}
+    step_dev = torch.zeros(1, dtype=torch.int64, device=dev)
+    for D in (1, 2, 3):
+        loop = SpecLoop(dec, head, D)
+        loop.start(L - 1, 123, T, top_p, seed, 0)
+        g_cycle = loop.capture(lambda: loop.run_graphable(T, top_p, seed, step_dev))
+        g_draft = loop.capture(lambda: loop.draft(T, top_p, seed, step_dev))
+        t_cycle, t_draft = time_graph(g_cycle, K), time_graph(g_draft, K)
+        depths[D] = {"cycle_ms": round(t_cycle, 4), "draft_ms": round(t_draft, 4),
+                     "verify_ms": round(t_cycle - t_draft, 4), "draft_ms_per_depth": round(t_draft / D, 4)}
+        log(f"D={D}: {depths[D]}")
+        del g_cycle, g_draft
+    ar_loop = SpecLoop(dec, head, 1)
+    ar_loop.start(L - 1, 123, T, top_p, seed, 0)
+
+    def ar_step():
+        B.embed_rows(E, ar_loop.tokens_in, 1, ar_loop.x)
+        ar_loop.ar_vs.run_graphable(ar_loop.x, ar_loop.L, None, None, T, top_p, seed, step_dev)
+
+    t_ar = time_graph(ar_loop.capture(ar_step), K)
+    # real cycles, eagerly launched (one host sync per cycle for n_acc)
+    D = 3
+    loop = SpecLoop(dec, head, D)
+    emitted = [loop.start(L - 1, 123, T, top_p, seed, 0)]
+    ncyc = 8
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    acc = []
+    for c in range(ncyc):
+        out = loop.cycle(T, top_p, seed, c + 1)
+        acc.append(len(out) - 1)
+        emitted += out
+    eager_s = (time.perf_counter() - t0) / ncyc
+    alpha_meas = float(np.mean(acc)) / D
+
+    model = {}
+    for a in (round(alpha_meas, 4), 0.5, 0.6, 0.7, 0.8, 0.9):
+        row = {"ar": round(1e3 / t_ar, 2)}
+        for D_, r in depths.items():
+            row[f"D{D_}"] = round(tokens_per_cycle(a, D_) * 1e3 / r["cycle_ms"], 2)
+        best = max(row, key=row.get)
+        model[str(a)] = {"tokens_per_s": row, "autotune_pick": best}
+    # the dominant kernel: the W4 GEMM launches of the verify pass at M = 4
+    ms_launch, n_launch = time_graphs([lambda: dec.gemm_pass(4)], 10)
+    per_launch = dec.gemm_alg_bytes(4) / n_launch
+    achieved = per_launch / (ms_launch * 1e-3) / 1e9
+    t3 = depths[3]["cycle_ms"]
+    return dict(
+        ms_per_step=t3,
+        value=1e3 / t3,
+        unit="spec cycles/s",
+        config={"workload": "spec_loop_27b", "layers": 64, "d_model": d, "V": V, "context": L, "draft_depth": 3,
+                "mtp_head": "rmsnorm(h) | rmsnorm(embed) -> W4 2d->d -> 1 decoder layer -> final norm -> W4 LM head",
+                "temperature": T, "top_p": top_p},
+        roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("verify27b"),
+                  "kernel": "w4_gemm_kernel (the W4 GEMM launches of the verify pass at M=4, replayed as a graph)",
+                  "alg_bytes_per_launch": int(per_launch), "avg_launch_us": round(ms_launch * 1e3, 2)},
+        spec_loop={"by_depth": depths, "m1_ar_step_ms": round(t_ar, 4), "eager_cycle_ms": round(eager_s * 1e3, 2),
+                   "measured_accepted_per_cycle": acc, "measured_alpha": round(alpha_meas, 4),
+                   "tokens_per_s_by_alpha": model},
+    )
+
+
 def verify27b_cpu_baseline_layer(reps=8):
     """The CPU oracle on the four linears of one layer at M=4 (fp64), reps row sets."""
     import oracle
@@ -1066,7 +1179,8 @@ WORKLOADS = {"lm_head_verify": (lm_head_workload, lm_head_cpu_baseline),
              "verify27b": (verify27b_workload, verify27b_cpu_baseline),
              "moe_verify": (moe_workload, moe_cpu_baseline),
              "layer_linears": (layer_linears_workload, lambda: verify27b_cpu_baseline_layer()),
-             "lm_small": (lm_small_workload, lm_small_cpu_baseline)}
+             "lm_small": (lm_small_workload, lm_small_cpu_baseline),
+             "spec_loop_27b": (spec_loop_workload, lambda: verify27b_cpu_baseline())}
 
 
 def main():
@@ -1102,13 +1216,14 @@ def main():
     del src, dst
     res = run(args)
     out = {"metric": METRIC, "value": round(res["value"], 3),
-           "unit": "layer passes/s" if args.workload == "layer_linears" else "verify steps/s", "n_gpus": 1,
+           "unit": res.get("unit", "layer passes/s" if args.workload == "layer_linears" else "verify steps/s"),
+           "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic", "config": res["config"], "roofline": res["roofline"]}
     for k in ("stages_us", "w4_gemm_by_linear", "accepted_length_hist", "flagged_steps", "m1_ar_step_ms",
               "verify_over_ar", "step_hbm_gbs", "experts_per_step", "grouped_gemm_gbs", "m_sweep", "unit_note",
-              "context_sweep", "stats_accept_sweep", "sustained", "attention_by_context"):
+              "context_sweep", "stats_accept_sweep", "sustained", "attention_by_context", "spec_loop"):
         if k in res:
             out[k] = res[k]
     if not args.no_cpu_baseline:

@@ -80,3 +80,12 @@ def test_more_than_one_gpu_is_refused(argv, monkeypatch):
     with pytest.raises(SystemExit) as e:
         bench.main()
     assert e.value.code == 2
+
+
+@pytest.mark.parametrize("D", [1, 2, 3, 7])
+@pytest.mark.parametrize("alpha", [0.0, 0.3, 0.7, 0.95, 1.0])
+def test_tokens_per_cycle_by_enumeration(alpha, D):
+    # P(k drafts accepted) = alpha^k (1 - alpha) for k < D, alpha^D for k = D;
+    # the cycle emits k + 1 tokens
+    e = sum((k + 1) * alpha ** k * (1 - alpha) for k in range(D)) + (D + 1) * alpha ** D
+    assert abs(bench.tokens_per_cycle(alpha, D) - e) < 1e-12

@@ -442,6 +442,28 @@ class SpecLoop:
         B.embed_rows(self.head.embed, self.tokens_in, M, self.x)
         return self.vs.run(self.x, self.L, self.q, self.tokens_in[1:], T, top_p, seed, step)
 
+    def run_graphable(self, T: float, top_p: float, seed: int, step_dev):
+        """A cycle at the current L with the Philox step read from device memory
+        (drafts and verify draw with the same step; the verify advances it)."""
+        self.draft(T, top_p, seed, step_dev)
+        B.embed_rows(self.head.embed, self.tokens_in, self.D + 1, self.x)
+        self.vs.run_graphable(self.x, self.L, self.q, self.tokens_in[1:], T, top_p, seed, step_dev)
+
+    def capture(self, fn):
+        """Record fn() (launches only) into a HIP graph on a side stream."""
+        import torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()                                    # warm (plans, code objects)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
     def cycle(self, T: float, top_p: float, seed: int, step: int, drafts=None):
         """One cycle; returns the emitted tokens (host list).  drafts (int32
         device [D]) replaces the head's drafts (with one-hot q): any other
