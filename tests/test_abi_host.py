@@ -118,3 +118,28 @@ def test_spec_accept_rejects_bad_arguments():
     a = list(args(1, 3, 100))
     a[4] = None  # q missing with D > 0
     assert _call("spec_accept", *a) == B.VW4_EINVAL
+
+
+def test_draft_side_rejects_bad_arguments():
+    fake = ctypes.c_void_p(0x100000)   # 256-byte aligned, never dereferenced: validation fails first
+    assert B.lib().vw4_draft_workspace_bytes(0) == 0
+    assert B.draft_workspace_bytes(151936) > B.accept_workspace_bytes(1, 151936)
+    ws = B.draft_workspace_bytes(1000)
+    ds = lambda V, T, depth, ws_bytes, tok=fake: _call("draft_sample", fake, fake, V, T, 1, None, 0, depth, fake, tok,
+                                                       fake, fake, ws_bytes, None)
+    assert ds(0, 0.6, 0, ws) == B.VW4_EINVAL
+    assert ds(1000, -0.5, 0, ws) == B.VW4_EINVAL
+    assert ds(1000, 0.6, 1024, ws) == B.VW4_EINVAL
+    assert ds(1000, 0.6, 0, ws, tok=None) == B.VW4_EINVAL
+    assert ds(1000, 0.6, 0, 64) == B.VW4_EWORKSPACE
+    mi = lambda d, ldh, eps=1e-6: _call("vw4_mtp_input", fake, ldh, 2, None, fake, d, 100, fake, fake, fake, eps, d,
+                                        fake, None)
+    assert mi(12, 16) == B.VW4_EINVAL          # d % 8
+    assert mi(8200, 8200) == B.VW4_EINVAL      # d > 8192
+    assert mi(256, 128) == B.VW4_EINVAL        # ldh < d
+    assert mi(256, 256, eps=-1.0) == B.VW4_EINVAL
+    assert "vw4_mtp_input" in B.last_error()
+    er = lambda d, n: _call("vw4_embed_rows", fake, d, 100, d, fake, n, fake, d, None)
+    assert er(256, 0) == B.VW4_EINVAL
+    assert er(12, 1) == B.VW4_EINVAL
+    assert "vw4_embed_rows" in B.last_error()

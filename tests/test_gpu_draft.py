@@ -48,7 +48,7 @@ def test_embed_rows_match_oracle():
     assert np.array_equal(host(out), oracle.embed_rows(E, tok))
 
 
-@pytest.mark.parametrize("d", [256, 5120, 8192])
+@pytest.mark.parametrize("d", [8, 264, 256, 5120, 8192])
 @pytest.mark.parametrize("row,token", [(2, 7), (-1, 0), (9, -3), (3, 999)])
 def test_mtp_input_matches_oracle(d, row, token):
     import torch
@@ -105,6 +105,22 @@ def test_draft_sample_matches_oracle(V, T, top_p):
         torch.cuda.synchronize()
         assert int(host(tok2)[0]) == int(host(tok)[0])
     assert mism == 0 and flagged <= 1
+
+
+def test_draft_sample_single_token_vocab_and_max_depth():
+    import torch
+    V = 1
+    zd = dev(np.array([[0.25]], dtype=np.float32))
+    st = _stats_dev(zd, 0.6, 0.95)
+    ws = B.workspace(B.draft_workspace_bytes(V), "cuda")
+    q = torch.zeros(V, dtype=torch.float32, device="cuda")
+    tok = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    fl = torch.zeros(1, dtype=torch.int32, device="cuda")
+    log("draft_sample V=1, depth 1023")
+    B.draft_sample(zd, st, V, 0.6, SEED, 3, 1023, q, tok, fl, ws)
+    torch.cuda.synchronize()
+    assert int(host(tok)[0]) == 0 and host(q).tolist() == [1.0]
+    assert oracle.draft_sample(np.array([0.25], np.float32), 0.6, 0.95, SEED, 3, 1023)[0] == 0
 
 
 def _head_host(cfg, seed):
