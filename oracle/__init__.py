@@ -91,6 +91,8 @@ def lib():
         L.oracle_moe_route.argtypes = [_P, _I64, _I64, _I64, _P, _P]
         L.oracle_swiglu_f64.argtypes = [_P, _P, _I64, _P]
         L.oracle_mtp_input.argtypes = [_P, _P, _P, _P, _I64, _F64, _P]
+        L.oracle_w8_quantize.argtypes = [_P, _I64, _I64, _P, _P]
+        L.oracle_w8_gemm.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P]
         L.oracle_embed_rows.argtypes = [_P, _I64, _I64, _P, _I64, _P]
         L.oracle_draft_uniform.argtypes = [_U64, _U64, _I32]
         L.oracle_draft_uniform.restype = _F64
@@ -386,3 +388,29 @@ def draft_sample(z: np.ndarray, temperature: float, top_p: float, seed: int, ste
     lib().oracle_draft_sample(_ptr(z), V, float(temperature), float(top_p), int(seed), int(step), int(depth),
                               _ptr(q), ctypes.byref(st), _ptr(tok), _ptr(fl))
     return int(tok[0]), q, st, int(fl[0])
+
+
+# --------------------------------------------------------------------------
+# the W8 weight format (a second format for the skinny GEMM)
+# --------------------------------------------------------------------------
+def w8_quantize(w: np.ndarray):
+    """w: float32 [N][K] (K % 64 == 0) -> (codes u8 [N][K] holding c + 128, scales u16 [N][K/64])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    assert K % 64 == 0
+    codes = np.zeros((N, K), dtype=np.uint8)
+    scales = np.zeros((N, K // 64), dtype=np.uint16)
+    lib().oracle_w8_quantize(_ptr(w), N, K, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def w8_gemm(x_bf16: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """x_bf16: uint16 [M][K]; codes u8 [N][K]; returns float64 [M][N]."""
+    x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    M, K = x_bf16.shape
+    N = codes.shape[0]
+    assert codes.shape == (N, K) and scales.shape == (N, K // 64)
+    y = np.zeros((M, N), dtype=np.float64)
+    lib().oracle_w8_gemm(_ptr(x_bf16), M, K, _ptr(np.ascontiguousarray(codes)), _ptr(np.ascontiguousarray(scales)),
+                         N, _ptr(y))
+    return y
