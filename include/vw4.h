@@ -413,6 +413,38 @@ VW4_API int draft_sample(const float* logits, const vw4_rowstat* stats, int32_t 
                          const uint64_t* step_dev, uint64_t step, int32_t depth, float* q_out, int32_t* token_out,
                          uint32_t* flags_out, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * A second weight format for the skinny GEMM: W8 (gist.science, "BaseRT: Best-
+ * in-Class LLM Inference on Apple Silicon via Native Metal", section
+ * "メソドロジー": the GEMV reads several quantisation formats, Q8 among them;
+ * no layout is given).  Per row n and 64-element group g along K:
+ *     scale = fp16_rne(absmax / 127);  c_k = clamp(rint(w_k / scale), -127, 127)
+ * with the rounded scale, half-even; an all-zero group gets scale 0 and codes 0.
+ * Canonical storage: u8 codes[N][K] holding u = c + 128, fp16 scales[N][K/64].
+ * Kernel storage: the high and the low nibble of u as two planes, each in the
+ * W4 packed layout (vw4_w4_packed_bytes(N, K) bytes per plane) with the W4
+ * packed scales.
+ * ------------------------------------------------------------------------ */
+
+/* Host quantiser (host memory): w [N][K] fp32 -> codes [N][K], scales [N][K/64]. */
+VW4_API int vw4_w8_quantize_host(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales);
+
+/* Canonical codes and scales (device) -> the two packed nibble planes hi, lo
+ * (16-byte aligned, vw4_w4_packed_bytes(N, K) bytes each) and the packed
+ * scales; rows are padded to a multiple of 64 with code 0 and scale 0. */
+VW4_API int vw4_w8_pack(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, uint8_t* hi,
+                        uint8_t* lo, uint16_t* packed_scales, void* stream);
+
+/* y[M][N] (fp32 or bf16, row stride ldy) = x[M][K] (bf16, row stride ldx) .
+ * deq(W8)^T, W8 given as its packed planes and scales.  1 <= M <= 8,
+ * K % 64 == 0, K <= 65536; x 16-byte aligned with ldx % 8 == 0.  Workspace:
+ * vw4_w8_workspace_bytes(M, N, K) (0: none needed), 256-byte aligned.
+ * Sums are fp32 in an order fixed by (N, K). */
+VW4_API size_t vw4_w8_workspace_bytes(int32_t M, int32_t N, int32_t K);
+VW4_API int w8_skinny_gemm(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, const uint8_t* w_lo,
+                           const uint16_t* scales_packed, void* y, int64_t ldy, int32_t y_dtype, int32_t M, int32_t N,
+                           int32_t K, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -143,3 +143,27 @@ def test_draft_side_rejects_bad_arguments():
     assert er(256, 0) == B.VW4_EINVAL
     assert er(12, 1) == B.VW4_EINVAL
     assert "vw4_embed_rows" in B.last_error()
+
+
+def test_w8_host_quantizer_matches_oracle():
+    rng = np.random.default_rng(12)
+    w = rng.normal(0.0, 0.02, (45, 384)).astype(np.float32)
+    w[2, :64] = 0.0
+    w[4, 64:128] = 1e-9
+    w[6, 200] = -5.0
+    c1, s1 = B.w8_quantize_host(w)
+    c2, s2 = oracle.w8_quantize(w)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+def test_w8_gemm_rejects_bad_arguments():
+    fake = ctypes.c_void_p(0x100000)
+    g = lambda M, N, K, ldx, ydt: _call("w8_skinny_gemm", fake, ldx, fake, fake, fake, fake, N, ydt, M, N, K, None, 0,
+                                        None)
+    assert g(0, 64, 64, 64, 0) == B.VW4_EINVAL
+    assert g(9, 64, 64, 64, 0) == B.VW4_EINVAL
+    assert g(1, 64, 100, 128, 0) == B.VW4_EINVAL
+    assert g(1, 64, 64, 60, 0) == B.VW4_EINVAL
+    assert g(1, 64, 64, 64, 5) == B.VW4_EINVAL
+    assert g(4, 5120, 5120, 5120, 0) == B.VW4_EWORKSPACE      # split-K plan, no workspace
+    assert B.w8_workspace_bytes(4, 5120, 5120) > 0 and B.lib().vw4_w8_workspace_bytes(0, 64, 64) == 0

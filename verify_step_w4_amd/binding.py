@@ -60,6 +60,10 @@ SIGNATURES = {
     "vw4_embed_rows": (ctypes.c_int, [_P, _I64, _I32, _I32, _P, _I32, _P, _I64, _P]),
     "vw4_mtp_input": (ctypes.c_int, [_P, _I64, _I32, _P, _P, _I64, _I32, _P, _P, _P, ctypes.c_float, _I32, _P, _P]),
     "vw4_draft_workspace_bytes": (_SZ, [_I32]),
+    "vw4_w8_quantize_host": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
+    "vw4_w8_pack": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P, _P]),
+    "vw4_w8_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "w8_skinny_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
     "draft_sample": (ctypes.c_int, [_P, _P, _I32, ctypes.c_float, _U64, _P, _U64, _I32, _P, _P, _P, _P, _SZ, _P]),
     "vw4_gemm_partials_layout": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
                                                 ctypes.POINTER(ctypes.c_int64)]),
@@ -306,6 +310,40 @@ def draft_sample(logits, stats, V: int, temperature: float, seed: int, step: int
     _check("draft_sample", lib().draft_sample(_ptr(logits), _ptr(stats), V, float(temperature), int(seed),
                                               _ptr(step_dev), int(step), int(depth), _ptr(q_out), _ptr(token_out),
                                               _ptr(flags_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def w8_quantize_host(w: np.ndarray):
+    """fp32 [N][K] host array -> (codes u8 [N][K] holding c + 128, scales u16 [N][K/64])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    codes = np.zeros((N, K), dtype=np.uint8)
+    scales = np.zeros((N, K // 64), dtype=np.uint16)
+    _check("vw4_w8_quantize_host", lib().vw4_w8_quantize_host(w.ctypes.data_as(ctypes.c_void_p), N, K,
+                                                              codes.ctypes.data_as(ctypes.c_void_p),
+                                                              scales.ctypes.data_as(ctypes.c_void_p)))
+    return codes, scales
+
+
+def w8_pack(codes, scales, N: int, K: int, hi, lo, pscales, stream=None):
+    _check("vw4_w8_pack", lib().vw4_w8_pack(_ptr(codes), _ptr(scales), N, K, _ptr(hi), _ptr(lo), _ptr(pscales),
+                                            _stream(stream)))
+
+
+def w8_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().vw4_w8_workspace_bytes(M, N, K))
+
+
+def w8_skinny_gemm(x, w_hi, w_lo, scales_packed, y, M: int, N: int, K: int, ws=None, stream=None,
+                   ldx: int | None = None, ldy: int | None = None):
+    """y[M][N] (fp32 or bf16 tensor) = x[M][K] (bf16 bits) @ W8^T."""
+    import torch
+    ydt = VW4_F32 if y.dtype == torch.float32 else VW4_BF16
+    ldx = x.stride(0) if ldx is None else ldx
+    ldy = y.stride(0) if ldy is None else ldy
+    nbytes = ws.numel() if ws is not None else 0
+    _check("w8_skinny_gemm", lib().w8_skinny_gemm(_ptr(x), ldx, _ptr(w_hi), _ptr(w_lo), _ptr(scales_packed), _ptr(y),
+                                                  ldy, ydt, M, N, K, _ptr(ws), nbytes, _stream(stream)))
+    return y
 
 
 def rowstats_to_numpy(stats_tensor) -> np.ndarray:

@@ -154,6 +154,32 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ c
     pscales[packed_scale(n, g, G)] = (n < N) ? scales[n * G + g] : (uint16_t)0;
 }
 
+// W8: one u8 code u = c + 128 per element (row n, k at codes[n * K + k]).
+// The high and low nibbles of u go to two planes, each in the W4 packed
+// layout above; padding rows get u = 128 (code 0) and scale 0.
+__global__ __launch_bounds__(256) void pack8_kernel(const uint8_t* __restrict__ codes,
+                                                    const uint16_t* __restrict__ scales, int64_t N, int64_t K,
+                                                    int64_t Npad, uint32_t* __restrict__ hi, uint32_t* __restrict__ lo,
+                                                    uint16_t* __restrict__ pscales) {
+    const int64_t G = K / 64;
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= Npad * G) return;
+    const int64_t n = id / G, g = id % G;
+    const uint8_t* src = codes + n * K + g * 64;
+    for (int o = 0; o < 8; ++o) {
+        uint32_t wh = 0, wl = 0;
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t u = (n < N) ? src[o * 8 + j] : 128u;
+            wh |= (u >> 4) << packed_nibble_shift(j);
+            wl |= (u & 15u) << packed_nibble_shift(j);
+        }
+        const int64_t d = packed_dword(n, g * 64 + o * 8, G);
+        hi[d] = wh;
+        lo[d] = wl;
+    }
+    pscales[packed_scale(n, g, G)] = (n < N) ? scales[n * G + g] : (uint16_t)0;
+}
+
 __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict__ packed,
                                                      const uint16_t* __restrict__ pscales, int64_t N, int64_t K,
                                                      uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
@@ -254,6 +280,40 @@ int vw4_w4_quantize_host(const float* w, int64_t N, int64_t K, uint8_t* codes, u
         }
     }
     return VW4_OK;
+}
+
+int vw4_w8_quantize_host(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales) {
+    int rc = check_shape(N, K);
+    if (rc) return rc;
+    VW4_REQUIRE(w && codes && scales, VW4_EINVAL, "null pointer");
+    const int64_t G = K / 64;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < G; ++g) {
+            const float* wg = w + n * K + g * 64;
+            float a = 0.0f;
+            for (int k = 0; k < 64; ++k) a = fmaxf(a, fabsf(wg[k]));
+            const uint16_t s16 = host_f32_to_f16(a / 127.0f);
+            const float sf = host_f16_to_f32(s16);
+            scales[n * G + g] = s16;
+            for (int k = 0; k < 64; ++k) {
+                const int c = sf != 0.0f ? (int)fminf(fmaxf(rintf(wg[k] / sf), -127.0f), 127.0f) : 0;
+                codes[n * K + g * 64 + k] = (uint8_t)(c + 128);
+            }
+        }
+    }
+    return VW4_OK;
+}
+
+int vw4_w8_pack(const uint8_t* codes_dev, const uint16_t* scales_dev, int64_t N, int64_t K, uint8_t* hi_dev,
+                uint8_t* lo_dev, uint16_t* packed_scales_dev, void* stream) {
+    int rc = check_shape(N, K);
+    if (rc) return rc;
+    VW4_REQUIRE(codes_dev && scales_dev && hi_dev && lo_dev && packed_scales_dev, VW4_EINVAL, "null pointer");
+    VW4_REQUIRE(aligned(hi_dev, 16) && aligned(lo_dev, 16), VW4_EINVAL, "packed planes must be 16-byte aligned");
+    const int64_t Np = pad64(N), total = Np * (K / 64);
+    hipLaunchKernelGGL(pack8_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                       codes_dev, scales_dev, N, K, Np, (uint32_t*)hi_dev, (uint32_t*)lo_dev, packed_scales_dev);
+    return check_launch("vw4_w8_pack");
 }
 
 int vw4_w4_quantize(const float* w_dev, int64_t N, int64_t K, uint8_t* codes_dev, uint16_t* scales_dev,

@@ -49,6 +49,45 @@ class W4Linear:
         return int(self.N * self.K * BYTES_PER_WEIGHT)
 
 
+class W8Linear:
+    """A [N][K] matrix in the W8 format (int8 codes, fp16 scale per 64 K), kept
+    as its two packed nibble planes and the packed scales."""
+
+    def __init__(self, hi, lo, pscales, N: int, K: int):
+        self.hi, self.lo, self.pscales, self.N, self.K = hi, lo, pscales, N, K
+
+    @classmethod
+    def from_codes(cls, codes, scales, stream=None):
+        """codes: uint8 device [N][K] (c + 128); scales: int16 device [N][K/64] (fp16 bits)."""
+        import torch
+        N, K = codes.shape
+        cb, sb = B.packed_sizes(N, K)
+        hi = torch.empty(cb, dtype=torch.uint8, device=codes.device)
+        lo = torch.empty(cb, dtype=torch.uint8, device=codes.device)
+        ps = torch.empty(sb // 2, dtype=torch.int16, device=codes.device)
+        B.w8_pack(codes, scales, N, K, hi, lo, ps, stream)
+        return cls(hi, lo, ps, N, K)
+
+    @classmethod
+    def from_fp32(cls, w, device="cuda"):
+        """w: fp32 [N][K] (numpy or torch); quantised by the library's host quantiser."""
+        import torch
+        wn = w.detach().cpu().numpy() if hasattr(w, "detach") else w
+        codes, scales = B.w8_quantize_host(wn)
+        return cls.from_codes(torch.from_numpy(codes).to(device), torch.from_numpy(scales.view("int16")).to(device))
+
+    @classmethod
+    def random(cls, N: int, K: int, gen, device="cuda"):
+        """Uniform codes in [-127, 127] and fp16 scales in [1e-4, 3e-4] (timing inputs)."""
+        import torch
+        codes = torch.randint(1, 256, (N, K), generator=gen, device=device, dtype=torch.int32).to(torch.uint8)
+        scales = (1e-4 + 2e-4 * torch.rand((N, K // 64), generator=gen, device=device)).to(torch.float16)
+        return cls.from_codes(codes, scales.view(torch.int16))
+
+    def nbytes(self) -> int:
+        return self.N * self.K + self.N * (self.K // 64) * 2
+
+
 class LMHeadVerify:
     """One verify step on an LM head: W4 GEMM of the M rows, temperature/top-p
     statistics, Leviathan–Chen acceptance.  All buffers are allocated once."""
