@@ -1088,6 +1088,67 @@ def layer_linears_workload(args):
     )
 
 
+def layer_linears_w8_workload(args):
+    """The same four linears of one 27B-shaped layer in the W8 format (int8
+    codes, fp16 scale per 64 K: 1.03125 bytes per weight, 351 MB per layer),
+    plain GEMM outputs (gate|up as one [34816][5120] product); 4 layers'
+    weights rotated (1.4 GB).  A step is one pass over a layer's four linears
+    at M = 4."""
+    import torch
+
+    from verify_step_w4_amd import binding as B
+    from verify_step_w4_amd.model import W8Linear
+
+    d, F, nqkv = 5120, 17408, 7168
+    nlay = 4
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261209)
+    shapes = {"qkv": (nqkv, d), "o": (d, d), "gate_up": (2 * F, d), "down": (d, F)}
+    log(f"generating {nlay} layers of W8 linears (351 MB each)")
+    layers = [{nm: W8Linear.random(N, K, gen) for nm, (N, K) in shapes.items()} for _ in range(nlay)]
+    M = 4
+    xs = {K: torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16) for K in (d, F)}
+    ys = {nm: torch.empty((M, N), dtype=torch.float32, device="cuda") for nm, (N, K) in shapes.items()}
+    ws = {nm: B.workspace(max(B.w8_workspace_bytes(M, N, K), 256)) for nm, (N, K) in shapes.items()}
+
+    def issue(names=tuple(shapes)):
+        n = 0
+        for L in layers:
+            for nm in names:
+                N, K = shapes[nm]
+                B.w8_skinny_gemm(xs[K], L[nm].hi, L[nm].lo, L[nm].pscales, ys[nm], M, N, K, ws=ws[nm])
+                n += 1
+        return n
+
+    def alg(nm):
+        N, K = shapes[nm]
+        return N * K + N * (K // 64) * 2 + M * K * 2 + M * N * 4
+
+    reps = max(1, args.steps // nlay)
+    ms_launch, n_launch = time_graphs([issue], reps)
+    layer_us = ms_launch * 1e3 * 4
+    per = {}
+    for nm in shapes:
+        us = time_graphs([lambda nm=nm: issue((nm,))], reps)[0] * 1e3
+        per[nm] = {"avg_us": round(us, 2), "GBs": round(alg(nm) / (us * 1e-6) / 1e9, 1),
+                   "frac": round(alg(nm) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"W8 layer {layer_us:.2f} us: {per}")
+    lb = sum(alg(nm) for nm in shapes)
+    return dict(
+        ms_per_step=layer_us * 1e-3,
+        value=1.0 / (layer_us * 1e-6),
+        unit="layer passes/s",
+        config={"workload": "layer_linears_w8", "d_model": d, "qkv": [nqkv, d], "o": [d, d], "gate_up": [2 * F, d],
+                "down": [d, F], "M": M, "rotated_layers": nlay,
+                "weights": "int8 group-64 symmetric, fp16 scales (two nibble planes)"},
+        roofline={"bound": "hbm", "achieved": round(lb / (layer_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                  "unit": "GB/s", "frac": round(lb / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                  "kernel": "w8_gemm_kernel (+ w8_reduce_kernel; the four linears of a layer at M=4, graph-replayed)",
+                  "alg_bytes_per_launch": int(lb / 4), "avg_launch_us": round(layer_us / 4, 2)},
+        w8_gemm_by_linear=per,
+    )
+
+
 # --------------------------------------------------------------------------
 # Single small LM-head verify step (d=1024, V=8192)
 # --------------------------------------------------------------------------
@@ -1180,7 +1241,8 @@ WORKLOADS = {"lm_head_verify": (lm_head_workload, lm_head_cpu_baseline),
              "moe_verify": (moe_workload, moe_cpu_baseline),
              "layer_linears": (layer_linears_workload, lambda: verify27b_cpu_baseline_layer()),
              "lm_small": (lm_small_workload, lm_small_cpu_baseline),
-             "spec_loop_27b": (spec_loop_workload, lambda: verify27b_cpu_baseline())}
+             "spec_loop_27b": (spec_loop_workload, lambda: verify27b_cpu_baseline()),
+             "layer_linears_w8": (layer_linears_w8_workload, lambda: verify27b_cpu_baseline_layer())}
 
 
 def main():
@@ -1223,7 +1285,8 @@ def main():
            "data": "synthetic", "config": res["config"], "roofline": res["roofline"]}
     for k in ("stages_us", "w4_gemm_by_linear", "accepted_length_hist", "flagged_steps", "m1_ar_step_ms",
               "verify_over_ar", "step_hbm_gbs", "experts_per_step", "grouped_gemm_gbs", "m_sweep", "unit_note",
-              "context_sweep", "stats_accept_sweep", "sustained", "attention_by_context", "spec_loop"):
+              "context_sweep", "stats_accept_sweep", "sustained", "attention_by_context", "spec_loop",
+              "w8_gemm_by_linear"):
         if k in res:
             out[k] = res[k]
     if not args.no_cpu_baseline:
