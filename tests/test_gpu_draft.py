@@ -207,10 +207,11 @@ def _ar_sequence(target, head, kv, L0, t0, n, T, top_p):
     return seq
 
 
-def test_spec_loop_greedy_equals_autoregressive():
+@pytest.mark.parametrize("D", [1, 3, 5])
+def test_spec_loop_greedy_equals_autoregressive(D):
     import torch
-    D, L0, t0, n = 3, 700, 123, 14
-    log("closed loop at T = 0 vs greedy AR (2 layers, full width)")
+    L0, t0, n = 700, 123, 14
+    log(f"closed loop at T = 0 vs greedy AR (2 layers, full width), D = {D}")
     target, head, kv = _loop_setup(21, D, L0)
     ar = _ar_sequence(target, head, kv, L0, t0, n + D + 1, 0.0, 0.95)
     # the head's drafts
