@@ -445,11 +445,13 @@ def verify27b_workload(args):
     t0 = time.perf_counter()
     sweep_L = [] if args.no_context_sweep else [c for c in (1024, 8192, 32768) if c != L]
     Lcap = max([L] + sweep_L)
-    log(f"generating the 64-layer W4 decoder (d=5120, GQA 40/8x128, FFN 17408) + LM head, KV cache for {Lcap} "
-        f"positions, timed context L={L}")
-    dec = Decoder(cfg, M, Lcap + M + 8, gen=gen)
+    fmt = args.weights
+    log(f"generating the 64-layer {fmt.upper()} decoder (d=5120, GQA 40/8x128, FFN 17408) + LM head, KV cache for "
+        f"{Lcap} positions, timed context L={L}")
+    dec = Decoder(cfg, M, Lcap + M + 8, gen=gen, fmt=fmt)
+    bpw = BYTES_PER_WEIGHT if fmt == "w4" else 1.03125
     torch.cuda.synchronize()
-    log(f"weights ready in {time.perf_counter() - t0:.1f} s ({dec.weight_bytes() / 1e9:.2f} GB W4)")
+    log(f"weights ready in {time.perf_counter() - t0:.1f} s ({dec.weight_bytes() / 1e9:.2f} GB {fmt.upper()})")
     V, d = cfg["V"], cfg["d"]
     npool = 8
     xs = torch.randn((npool, M, d), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
@@ -588,7 +590,7 @@ def verify27b_workload(args):
     linears = {}
     for nm in by_name:
         N, Kd = shapes[nm]
-        b = N * Kd * BYTES_PER_WEIGHT + M * Kd * 2 + (M * (N // 2) * 2 if nm == "gate_up" else M * N * 4)
+        b = N * Kd * bpw + M * Kd * 2 + (M * (N // 2) * 2 if (nm == "gate_up" and fmt == "w4") else M * N * 4)
         us = time_graphs([lambda nm=nm: dec.gemm_pass(M, names=(nm,))], 20 if nm != "lm_head" else 200)[0] * 1e3
         linears[nm] = {"N": N, "K": Kd, "avg_us": round(us, 2), "GBs": round(b / (us * 1e-6) / 1e9, 1),
                        "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
@@ -616,10 +618,13 @@ def verify27b_workload(args):
         attention_by_context=attention,
         config={"workload": "verify27b", "layers": 64, "d_model": d, "heads_q_kv_dim": [40, 8, 128],
                 "ffn": cfg["F"], "V": V, "context": L, "M": M, "draft_depth": D, "temperature": T, "top_p": top_p,
-                "weights": "int4 group-64 symmetric, fp16 scales", "kv_cache": "bf16"},
+                "weights": ("int4" if fmt == "w4" else "int8") + " group-64 symmetric, fp16 scales",
+                "kv_cache": "bf16"},
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("verify27b"),
-                  "kernel": "w4_gemm_kernel (the 257 W4 GEMM launches of a step at M=4, replayed as a graph)",
+                  "frac": round(achieved / HBM_PEAK_GBS, 4),
+                  "traffic": measured_traffic("verify27b") if fmt == "w4" else None,
+                  "kernel": f"{fmt}_gemm_kernel (the 257 {fmt.upper()} GEMM launches of a step at M=4, replayed "
+                            "as a graph)",
                   "alg_bytes_per_launch": int(per_launch_bytes), "avg_launch_us": round(gemm_launch_us, 2)},
         stages_us={"w4_gemm_total_eager": round(gemm_ms * 1e3 / K, 1),
                    "w4_gemm_total_graph": round(gemm_launch_us * n_launch, 1),
@@ -1252,6 +1257,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="verify27b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--weights", default="w4", choices=("w4", "w8"),
+                    help="verify27b: weight format of the decoder's linears and LM head")
     ap.add_argument("--context", type=int, default=8192, help="KV context length L of the verify27b workload")
     ap.add_argument("--no-context-sweep", action="store_true",
                     help="verify27b: skip the extra timings at the other context lengths (1024, 8192, 32768)")

@@ -445,6 +445,16 @@ VW4_API int w8_skinny_gemm(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, 
                            const uint16_t* scales_packed, void* y, int64_t ldy, int32_t y_dtype, int32_t M, int32_t N,
                            int32_t K, void* ws, size_t ws_bytes, void* stream);
 
+/* The product as fp32 split-K partials for a consumer that sums them (the
+ * decoder's RoPE, add + RMSNorm and SwiGLU calls take (part, S, ldp)):
+ * part[s][m][n] (s < S, row stride ldp), S and ldp from
+ * vw4_w8_partials_layout(M, N, K); columns n >= N of a row are padding.
+ * part is caller-owned, S * M * ldp floats, 16-byte aligned. */
+VW4_API int vw4_w8_partials_layout(int32_t M, int32_t N, int32_t K, int32_t* S, int64_t* ldp);
+VW4_API int w8_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, const uint8_t* w_lo,
+                                    const uint16_t* scales_packed, float* part, int32_t M, int32_t N, int32_t K,
+                                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,7 @@ import pytest
 import oracle
 from verify_step_w4_amd import binding as B
 from verify_step_w4_amd import synth
-from verify_step_w4_amd.model import DENSE_27B, Decoder, VerifyStep, W4Linear
+from verify_step_w4_amd.model import DENSE_27B, Decoder, VerifyStep, W4Linear, W8Linear
 
 from helpers import dev, host, log, rows_from_vb, vb_from_rows
 
@@ -41,34 +41,39 @@ def _host_model(cfg, seed):
                 lm_head=synth.normal_f32(g, (V, d), 0.02))
 
 
-def _device_weights(hm):
+def _device_weights(hm, fmt="w4"):
     layers = []
     for l in hm["layers"]:
         d = {}
         for k, v in l.items():
             if k in ("g1", "g2"):
                 d[k] = dev(v)
+            elif fmt == "w8":      # W8: natural gate|up order (the SwiGLU runs on the partials)
+                d[k] = W8Linear.from_fp32(v)
             elif k == "gate_up":   # the fused SwiGLU GEMM takes gate/up-interleaved rows
                 d[k] = W4Linear.from_fp32(dev(B.interleave_gate_up(v)))
             else:
                 d[k] = W4Linear.from_fp32(dev(v))
         layers.append(d)
-    return dict(layers=layers, final_gamma=dev(hm["final_gamma"]), lm_head=W4Linear.from_fp32(dev(hm["lm_head"])))
+    lm = W8Linear.from_fp32(hm["lm_head"]) if fmt == "w8" else W4Linear.from_fp32(dev(hm["lm_head"]))
+    return dict(layers=layers, final_gamma=dev(hm["final_gamma"]), lm_head=lm)
 
 
-def _oracle_forward(cfg, hm, Kc, Vc, x, L):
+def _oracle_forward(cfg, hm, Kc, Vc, x, L, quant=None, gemm=None):
     """Oracle composition of the layer ops; Kc/Vc: per-layer uint16 arrays (modified)."""
     d, nq, nkv, hd, F, eps = (cfg[k] for k in ("d", "nq", "nkv", "hd", "F", "eps"))
+    quant = quant or oracle.w4_quantize
+    gemm = gemm or oracle.w4_gemm
     M = x.shape[0]
     q4 = {}
     for li, l in enumerate(hm["layers"]):
-        q4[li] = {k: oracle.w4_quantize(l[k]) for k in ("qkv", "o", "gate_up", "down")}
-    lm = oracle.w4_quantize(hm["lm_head"])
+        q4[li] = {k: quant(l[k]) for k in ("qkv", "o", "gate_up", "down")}
+    lm = quant(hm["lm_head"])
     resid = x.copy()
     for li, l in enumerate(hm["layers"]):
         Q = q4[li]
         h = oracle.bf16_round(oracle.rmsnorm(resid, l["g1"], eps))
-        qkv = oracle.w4_gemm(h, *Q["qkv"])
+        qkv = gemm(h, *Q["qkv"])
         q = np.zeros((M, nq, hd))
         for m in range(M):
             for hh in range(nq):
@@ -78,15 +83,15 @@ def _oracle_forward(cfg, hm, Kc, Vc, x, L):
                 Kc[li][hh, L + m] = oracle.bf16_round(kk)
                 Vc[li][hh, L + m] = oracle.bf16_round(qkv[m, (nq + nkv + hh) * hd:(nq + nkv + hh + 1) * hd])
         att = oracle.bf16_round(oracle.decode_attn(q, Kc[li], Vc[li], L).reshape(M, nq * hd))
-        o = oracle.w4_gemm(att, *Q["o"])
+        o = gemm(att, *Q["o"])
         resid = oracle.bf16_round(oracle.bf16_value(resid) + o)
         h = oracle.bf16_round(oracle.rmsnorm(resid, l["g2"], eps))
-        gu = oracle.w4_gemm(h, *Q["gate_up"])
+        gu = gemm(h, *Q["gate_up"])
         a = oracle.bf16_round(oracle.swiglu(gu[:, :F], gu[:, F:]))
-        dn = oracle.w4_gemm(a, *Q["down"])
+        dn = gemm(a, *Q["down"])
         resid = oracle.bf16_round(oracle.bf16_value(resid) + dn)
     h = oracle.bf16_round(oracle.rmsnorm(resid, hm["final_gamma"], eps))
-    return oracle.w4_gemm(h, *lm)
+    return gemm(h, *lm)
 
 
 def test_forward_matches_oracle_small_decoder():
@@ -131,6 +136,44 @@ def _dense_cfg(layers, V):
     c["layers"] = layers
     c["V"] = V
     return c
+
+
+@pytest.mark.parametrize("fmt", ["w8"])
+def test_forward_matches_oracle_small_decoder_other_format(fmt):
+    """The same small decoder with W8 linears and LM head (gate|up partials
+    through the standalone SwiGLU) against the oracle's W8 composition."""
+    import torch
+    cfg = TINY
+    M, L, Lmax = 4, 37, 64
+    log(f"forward vs oracle, small decoder, {fmt}")
+    hm = _host_model(cfg, 4243)
+    dec = Decoder(cfg, M, Lmax, weights=_device_weights(hm, fmt), kv_fill=False)
+    g = synth.rng(79)
+    Kh = [synth.f32_to_bf16_bits(synth.normal_f32(g, (cfg["nkv"], Lmax, cfg["hd"]), 1.0)) for _ in range(cfg["layers"])]
+    Vh = [synth.f32_to_bf16_bits(synth.normal_f32(g, (cfg["nkv"], Lmax, cfg["hd"]), 1.0)) for _ in range(cfg["layers"])]
+    for li in range(cfg["layers"]):
+        dec.Kc[li].copy_(dev(Kh[li]))
+        dec.Vc[li].copy_(dev(vb_from_rows(Vh[li])).view(dec.Vc[li].shape))
+    x = synth.activations_bf16(80, M, cfg["d"])
+    logits = host(dec.forward(dev(x), L, M)).copy()
+    torch.cuda.synchronize()
+    ref = _oracle_forward(cfg, hm, Kh, Vh, x, L, quant=oracle.w8_quantize, gemm=oracle.w8_gemm)
+    rms = np.sqrt((ref ** 2).mean(axis=1, keepdims=True))
+    rel = np.abs(logits - ref) / np.maximum(np.abs(ref), rms)
+    print(f"[forward {fmt}] max rel err {rel.max():.3e}, median {np.median(rel):.3e}", flush=True)
+    assert rel.max() < 2e-2
+    assert np.median(rel) < 2e-3
+    # verify rows equal the one-row steps bit for bit in this format too
+    for li in range(cfg["layers"]):
+        dec.Kc[li].copy_(dev(Kh[li]))
+        dec.Vc[li].copy_(dev(vb_from_rows(Vh[li])).view(dec.Vc[li].shape))
+    xd = dev(x)
+    verify = host(dec.forward(xd, L, M)).copy()
+    for li in range(cfg["layers"]):
+        dec.Kc[li].copy_(dev(Kh[li]))
+        dec.Vc[li].copy_(dev(vb_from_rows(Vh[li])).view(dec.Vc[li].shape))
+    for i in range(M):
+        assert np.array_equal(host(dec.forward(xd[i:i + 1], L + i, 1))[0], verify[i]), i
 
 
 def test_full_size_layer_matches_oracle():

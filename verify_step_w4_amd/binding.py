@@ -64,6 +64,9 @@ SIGNATURES = {
     "vw4_w8_pack": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P, _P]),
     "vw4_w8_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "w8_skinny_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+    "vw4_w8_partials_layout": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
+                                              ctypes.POINTER(ctypes.c_int64)]),
+    "w8_skinny_gemm_partials": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
     "draft_sample": (ctypes.c_int, [_P, _P, _I32, ctypes.c_float, _U64, _P, _U64, _I32, _P, _P, _P, _P, _SZ, _P]),
     "vw4_gemm_partials_layout": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
                                                 ctypes.POINTER(ctypes.c_int64)]),
@@ -344,6 +347,20 @@ def w8_skinny_gemm(x, w_hi, w_lo, scales_packed, y, M: int, N: int, K: int, ws=N
     _check("w8_skinny_gemm", lib().w8_skinny_gemm(_ptr(x), ldx, _ptr(w_hi), _ptr(w_lo), _ptr(scales_packed), _ptr(y),
                                                   ldy, ydt, M, N, K, _ptr(ws), nbytes, _stream(stream)))
     return y
+
+
+def w8_partials_layout(M: int, N: int, K: int):
+    S, ldp = ctypes.c_int32(0), ctypes.c_int64(0)
+    _check("vw4_w8_partials_layout", lib().vw4_w8_partials_layout(M, N, K, ctypes.byref(S), ctypes.byref(ldp)))
+    return int(S.value), int(ldp.value)
+
+
+def w8_skinny_gemm_partials(x, w_hi, w_lo, scales_packed, part, M: int, N: int, K: int, stream=None,
+                            ldx: int | None = None):
+    ldx = x.stride(0) if ldx is None else ldx
+    _check("w8_skinny_gemm_partials", lib().w8_skinny_gemm_partials(_ptr(x), ldx, _ptr(w_hi), _ptr(w_lo),
+                                                                    _ptr(scales_packed), _ptr(part), M, N, K,
+                                                                    _stream(stream)))
 
 
 def rowstats_to_numpy(stats_tensor) -> np.ndarray:

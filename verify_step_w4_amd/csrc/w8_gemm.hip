@@ -77,7 +77,7 @@ __global__ __launch_bounds__(64) void w8_gemm_kernel(const uint16_t* __restrict_
                                                      const w8u32x4* __restrict__ wlo,
                                                      const uint16_t* __restrict__ spk, void* __restrict__ y,
                                                      int64_t ldy, int ydt, int M, int N, int G, int S_grid,
-                                                     float* __restrict__ part, int64_t Npad) {
+                                                     float* __restrict__ part, int64_t Npad, int to_part) {
     const int lane = threadIdx.x, kq = lane >> 4, i = lane & 15;
     const int t = blockIdx.x, s_idx = blockIdx.y;
     const int g0 = s_idx * G / S_grid, g1 = (s_idx + 1) * G / S_grid;
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(64) void w8_gemm_kernel(const uint16_t* __restrict_
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
             const int n = t * 64 + nb * 16 + i;
-            if (S_grid == 1) {
+            if (S_grid == 1 && !to_part) {
                 if (n < N) {
                     if (ydt == VW4_F32) ((float*)y)[m * ldy + n] = acc[nb][r];
                     else ((uint16_t*)y)[m * ldy + n] = f32_to_bf16(acc[nb][r]);
@@ -213,11 +213,37 @@ int w8_skinny_gemm(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, const ui
     }
     hipStream_t st = (hipStream_t)stream;
     hipLaunchKernelGGL(w8_gemm_kernel, dim3(p.ntiles, p.S_grid), dim3(64), 0, st, x, ldx, (const w8u32x4*)w_hi,
-                       (const w8u32x4*)w_lo, scales_packed, y, ldy, y_dtype, M, N, p.G, p.S_grid, part, p.Npad);
+                       (const w8u32x4*)w_lo, scales_packed, y, ldy, y_dtype, M, N, p.G, p.S_grid, part, p.Npad, 0);
     if (p.S_grid > 1)
         hipLaunchKernelGGL(w8_reduce_kernel, dim3(p.ntiles, M), dim3(64), 0, st, part, p.S_grid, M, p.Npad, N, y, ldy,
                            y_dtype);
     return check_launch("w8_skinny_gemm");
+}
+
+int vw4_w8_partials_layout(int32_t M, int32_t N, int32_t K, int32_t* S, int64_t* ldp) {
+    VW4_REQUIRE(M >= 1 && M <= W8_MAX_M && N >= 1 && K >= 64 && K % 64 == 0 && K <= 65536, VW4_EINVAL,
+                "vw4_w8_partials_layout: bad shape M=%d N=%d K=%d", M, N, K);
+    const W8Plan p = w8_plan(M, N, K);
+    if (S) *S = p.S_grid;
+    if (ldp) *ldp = p.Npad;
+    return VW4_OK;
+}
+
+int w8_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, const uint8_t* w_lo,
+                            const uint16_t* scales_packed, float* part, int32_t M, int32_t N, int32_t K,
+                            void* stream) {
+    VW4_REQUIRE(M >= 1 && M <= W8_MAX_M && N >= 1 && K >= 64 && K % 64 == 0 && K <= 65536, VW4_EINVAL,
+                "w8_skinny_gemm_partials: bad shape M=%d N=%d K=%d", M, N, K);
+    VW4_REQUIRE(x && w_hi && w_lo && scales_packed && part, VW4_EINVAL, "w8_skinny_gemm_partials: null pointer");
+    VW4_REQUIRE(ldx >= K && ldx % 8 == 0 && aligned(x, 16), VW4_EINVAL,
+                "w8_skinny_gemm_partials: x needs ldx >= K, ldx %% 8 == 0 and 16-byte alignment");
+    VW4_REQUIRE(aligned(w_hi, 16) && aligned(w_lo, 16) && aligned(scales_packed, 8) && aligned(part, 16),
+                VW4_EINVAL, "w8_skinny_gemm_partials: misaligned pointer");
+    const W8Plan p = w8_plan(M, N, K);
+    hipLaunchKernelGGL(w8_gemm_kernel, dim3(p.ntiles, p.S_grid), dim3(64), 0, (hipStream_t)stream, x, ldx,
+                       (const w8u32x4*)w_hi, (const w8u32x4*)w_lo, scales_packed, (void*)part, p.Npad, VW4_F32, M, N,
+                       p.G, p.S_grid, part, p.Npad, 1);
+    return check_launch("w8_skinny_gemm_partials");
 }
 
 }  // extern "C"

@@ -135,7 +135,7 @@ class Decoder:
     KV caches and activation buffers are allocated once (device-resident)."""
 
     def __init__(self, cfg: dict, M_max: int, Lmax: int, gen=None, device="cuda", weights=None,
-                 kv_fill: bool = True):
+                 kv_fill: bool = True, fmt: str = "w4"):
         import torch
         self.cfg = dict(cfg)
         c = self.cfg
@@ -145,7 +145,7 @@ class Decoder:
         self.nqkv = (nq + 2 * nkv) * hd
         self.shapes = {"qkv": (self.nqkv, d), "o": (d, nq * hd), "gate_up": (2 * F, d), "down": (d, F)}
         if weights is None:
-            weights = self.random_weights(cfg, gen, device)
+            weights = self.random_weights(cfg, gen, device, fmt)
         self.layers = weights["layers"]
         self.final_gamma = weights["final_gamma"]
         self.lm_head = weights["lm_head"]
@@ -175,16 +175,19 @@ class Decoder:
         self.parts = {}
         for name, (N, K) in self.shapes.items():
             S, ldp = B.gemm_partials_layout(M_max, N, K)
-            self.parts[name] = torch.empty(S * M_max * ldp, dtype=torch.float32, device=device)
+            S8, ldp8 = B.w8_partials_layout(M_max, N, K)
+            self.parts[name] = torch.empty(max(S * ldp, S8 * ldp8) * M_max, dtype=torch.float32, device=device)
         self.attn_ws = B.workspace(B.attn_workspace_bytes(M_max, nq, nkv, hd, Lmax), device)
         self.norm_ws = B.workspace(B.norm_workspace_bytes(M_max, d), device)
         self.logits = torch.empty((M_max, V), dtype=torch.float32, device=device)
-        self.lm_ws = B.workspace(B.gemm_workspace_bytes(M_max, V, d), device)
+        self.lm_ws = B.workspace(max(B.gemm_workspace_bytes(M_max, V, d), B.w8_workspace_bytes(M_max, V, d)), device)
 
     @staticmethod
-    def random_weights(cfg: dict, gen, device="cuda"):
-        """~N(0, 0.02) fp32 weights drawn on the device and quantised to W4;
-        RMSNorm gains ~N(1, 0.02) in bf16."""
+    def random_weights(cfg: dict, gen, device="cuda", fmt: str = "w4"):
+        """W4: ~N(0, 0.02) fp32 weights drawn on the device and quantised; W8:
+        uniform int8 codes with fp16 scales in [1e-4, 3e-4] (the same spread).
+        RMSNorm gains ~N(1, 0.02) in bf16.  In W8 the gate|up matrix keeps its
+        natural row order (the SwiGLU runs on its partials)."""
         import torch
         d, nq, nkv, hd, F, nl, V = (cfg[k] for k in ("d", "nq", "nkv", "hd", "F", "layers", "V"))
         nqkv = (nq + 2 * nkv) * hd
@@ -192,14 +195,16 @@ class Decoder:
         def gamma():
             return (1.0 + 0.02 * torch.randn(d, generator=gen, device=device)).to(torch.bfloat16).view(torch.int16)
 
+        def lin(N, K):
+            if fmt == "w8":
+                return W8Linear.random(N, K, gen, device)
+            return W4Linear.random(N, K, 0.02, gen, device)
+
         layers = []
         for _ in range(nl):
-            layers.append(dict(qkv=W4Linear.random(nqkv, d, 0.02, gen, device),
-                               o=W4Linear.random(d, nq * hd, 0.02, gen, device),
-                               gate_up=W4Linear.random(2 * F, d, 0.02, gen, device),
-                               down=W4Linear.random(d, F, 0.02, gen, device),
+            layers.append(dict(qkv=lin(nqkv, d), o=lin(d, nq * hd), gate_up=lin(2 * F, d), down=lin(d, F),
                                g1=gamma(), g2=gamma()))
-        return dict(layers=layers, final_gamma=gamma(), lm_head=W4Linear.random(V, d, 0.02, gen, device))
+        return dict(layers=layers, final_gamma=gamma(), lm_head=lin(V, d))
 
     def weight_bytes(self) -> int:
         n = sum(l[k].nbytes() for l in self.layers for k in ("qkv", "o", "gate_up", "down"))
@@ -236,39 +241,55 @@ class Decoder:
         for li, W in enumerate(lay):
             # attention block
             N, K = self.shapes["qkv"]
-            S, ldp = B.gemm_partials_layout(M, N, K)
             hook("pre", "qkv")
-            B.w4_skinny_gemm_partials(h, W["qkv"].packed, W["qkv"].pscales, self.parts["qkv"], M, N, K, stream)
+            S, ldp = self._partials(W, "qkv", h, M, stream)
             hook("post", "qkv")
             B.rope_kv_append(self.parts["qkv"], S, ldp, M, nq, nkv, hd, L, c["theta"], self.q, self.Kc[li],
                              self.Vc[li], self.Lmax, stream)
             B.decode_attn(self.q, self.Kc[li], self.Vc[li], self.Lmax, L, M, nq, nkv, hd, self.attn, self.attn_ws,
                           stream)
-            N, K = self.shapes["o"]
-            S, ldp = B.gemm_partials_layout(M, N, K)
             hook("pre", "o")
-            B.w4_skinny_gemm_partials(self.attn, W["o"].packed, W["o"].pscales, self.parts["o"], M, N, K, stream)
+            S, ldp = self._partials(W, "o", self.attn[:M], M, stream)
             hook("post", "o")
             add_norm(self.parts["o"], S, ldp, W["g2"])
             # FFN block: gate|up with the SwiGLU in the GEMM epilogue
             N, K = self.shapes["gate_up"]
             hook("pre", "gate_up")
-            B.w4_skinny_gemm_swiglu(h, W["gate_up"].packed, W["gate_up"].pscales, self.a, F, M, F, K, stream)
+            if isinstance(W["gate_up"], W8Linear):
+                S, ldp = self._partials(W, "gate_up", h, M, stream)
+                B.swiglu(self.parts["gate_up"], S, ldp, M, F, self.a, stream)
+            else:
+                B.w4_skinny_gemm_swiglu(h, W["gate_up"].packed, W["gate_up"].pscales, self.a, F, M, F, K, stream)
             hook("post", "gate_up")
-            N, K = self.shapes["down"]
-            S, ldp = B.gemm_partials_layout(M, N, K)
             hook("pre", "down")
-            B.w4_skinny_gemm_partials(self.a, W["down"].packed, W["down"].pscales, self.parts["down"], M, N, K,
-                                      stream)
+            S, ldp = self._partials(W, "down", self.a[:M], M, stream)
             hook("post", "down")
             g_next = lay[li + 1]["g1"] if li + 1 < len(lay) else self.final_gamma
             add_norm(self.parts["down"], S, ldp, g_next)
         self.last_resid = cur[0]         # residual rows after the last layer (before the final norm)
         hook("pre", "lm_head")
-        B.w4_skinny_gemm(h, self.lm_head.packed, self.lm_head.pscales, self.logits[:M], M, c["V"], d,
-                         ws=self.lm_ws, stream=stream)
+        self._lm_head(h, M, stream)
         hook("post", "lm_head")
         return self.logits[:M]
+
+    def _partials(self, W, name, x, M, stream):
+        """Split-K partial sums of linear `name` into self.parts[name]; returns (S, ldp)."""
+        lin = W[name]
+        N, K = self.shapes[name]
+        if isinstance(lin, W8Linear):
+            B.w8_skinny_gemm_partials(x, lin.hi, lin.lo, lin.pscales, self.parts[name], M, N, K, stream)
+            return B.w8_partials_layout(M, N, K)
+        B.w4_skinny_gemm_partials(x, lin.packed, lin.pscales, self.parts[name], M, N, K, stream)
+        return B.gemm_partials_layout(M, N, K)
+
+    def _lm_head(self, h, M, stream):
+        c, lm = self.cfg, self.lm_head
+        if isinstance(lm, W8Linear):
+            B.w8_skinny_gemm(h, lm.hi, lm.lo, lm.pscales, self.logits[:M], M, c["V"], c["d"], ws=self.lm_ws,
+                             stream=stream)
+        else:
+            B.w4_skinny_gemm(h, lm.packed, lm.pscales, self.logits[:M], M, c["V"], c["d"], ws=self.lm_ws,
+                             stream=stream)
 
     def gemm_pass(self, M: int, stream=None, names=("qkv", "o", "gate_up", "down", "lm_head")):
         """Only the W4 GEMM launches of one forward (same shapes, weights and
@@ -282,16 +303,14 @@ class Decoder:
                 if name not in names:
                     continue
                 N, K = self.shapes[name]
-                if name == "gate_up":
+                if name == "gate_up" and not isinstance(W[name], W8Linear):
                     B.w4_skinny_gemm_swiglu(self.h[:M], W[name].packed, W[name].pscales, self.a, F, M, F, K, stream)
                 else:
-                    x = {"qkv": self.h, "o": self.attn, "down": self.a}[name]
-                    B.w4_skinny_gemm_partials(x[:M], W[name].packed, W[name].pscales, self.parts[name], M, N, K,
-                                              stream)
+                    x = {"qkv": self.h, "o": self.attn, "gate_up": self.h, "down": self.a}[name]
+                    self._partials(W, name, x[:M], M, stream)
                 n += 1
         if "lm_head" in names:
-            B.w4_skinny_gemm(self.h[:M], self.lm_head.packed, self.lm_head.pscales, self.logits[:M], M, c["V"],
-                             c["d"], ws=self.lm_ws, stream=stream)
+            self._lm_head(self.h[:M], M, stream)
             n += 1
         return n
 
@@ -301,9 +320,11 @@ class Decoder:
         c = self.cfg
         tot = 0.0
         for name, (N, K) in self.shapes.items():
-            out = M * (N // 2) * 2 if name == "gate_up" else M * N * 4    # SwiGLU output (bf16) / fp32 partial sums
-            tot += c["layers"] * (N * K * BYTES_PER_WEIGHT + M * K * 2 + out)
-        tot += c["V"] * c["d"] * BYTES_PER_WEIGHT + M * c["d"] * 2 + M * c["V"] * 4
+            w8 = isinstance(self.layers[0][name], W8Linear)
+            # SwiGLU epilogue output (bf16), or fp32 partial sums
+            out = M * (N // 2) * 2 if (name == "gate_up" and not w8) else M * N * 4
+            tot += sum(l[name].nbytes() for l in self.layers) + c["layers"] * (M * K * 2 + out)
+        tot += self.lm_head.nbytes() + M * c["d"] * 2 + M * c["V"] * 4
         return int(tot)
 
 
