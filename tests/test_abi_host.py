@@ -167,3 +167,17 @@ def test_w8_gemm_rejects_bad_arguments():
     assert g(1, 64, 64, 64, 5) == B.VW4_EINVAL
     assert g(4, 5120, 5120, 5120, 0) == B.VW4_EWORKSPACE      # split-K plan, no workspace
     assert B.w8_workspace_bytes(4, 5120, 5120) > 0 and B.lib().vw4_w8_workspace_bytes(0, 64, 64) == 0
+
+
+def test_w8_partials_layout_and_validation():
+    # the layout does not depend on M (so verify rows equal one-row steps), and
+    # never exceeds the 8 slices the decoder's consumers read
+    for N, K in ((7168, 5120), (5120, 5120), (34816, 5120), (5120, 17408), (151936, 5120)):
+        lay = {M: B.w8_partials_layout(M, N, K) for M in (1, 4, 8)}
+        assert len(set(lay.values())) == 1
+        S, ldp = lay[1]
+        assert 1 <= S <= 8 and ldp % 64 == 0 and ldp >= N
+    fake = ctypes.c_void_p(0x100000)
+    assert _call("w8_skinny_gemm_partials", fake, 60, fake, fake, fake, fake, 1, 64, 64, None) == B.VW4_EINVAL
+    assert _call("w8_skinny_gemm_partials", fake, 64, fake, fake, fake, fake, 9, 64, 64, None) == B.VW4_EINVAL
+    assert _call("w8_skinny_gemm_partials", fake, 64, fake, fake, fake, None, 1, 64, 64, None) == B.VW4_EINVAL
