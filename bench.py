@@ -614,7 +614,6 @@ def verify27b_workload(args):
         ms_per_step=step_ms,
         value=K / (total_ms * 1e-3),
         wall_s=wall,
-        w4_gemm_by_linear=linears,
         attention_by_context=attention,
         config={"workload": "verify27b", "layers": 64, "d_model": d, "heads_q_kv_dim": [40, 8, 128],
                 "ffn": cfg["F"], "V": V, "context": L, "M": M, "draft_depth": D, "temperature": T, "top_p": top_p,
@@ -637,6 +636,7 @@ def verify27b_workload(args):
         flagged_steps=int(((flags & ~B.FLAG_NONFINITE) != 0).sum()),
         context_sweep=ctx_sweep,
     )
+    res[f"{fmt}_gemm_by_linear"] = linears
     if sustained is not None:
         res["sustained"] = sustained
     return res
