@@ -773,6 +773,24 @@ def verify27b_cpu_baseline_layer(reps=8):
             "sample": f"one 27B-class layer's four W4 GEMMs at M=4 on {reps} row sets; quantisation untimed"}
 
 
+def layer_linears_w8_cpu_baseline(reps=4):
+    """The CPU oracle's W8 GEMM on the four linears of one layer at M=4 (fp64), reps row sets."""
+    import oracle
+    from verify_step_w4_amd import synth
+    g = synth.rng(synth.SEED_BASE + 9)
+    tot = 0.0
+    for N, K in [(7168, 5120), (5120, 5120), (34816, 5120), (5120, 17408)]:
+        codes, scales = oracle.w8_quantize(synth.normal_f32(g, (N, K), 0.02))
+        for r in range(reps):
+            x = synth.f32_to_bf16_bits(synth.normal_f32(g, (4, K), 1.0))
+            t0 = time.perf_counter()
+            oracle.w8_gemm(x, codes, scales)
+            tot += time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(reps / tot, 4), "unit": "layer passes/s", "cores": cores, "kind": "oracle",
+            "sample": f"one 27B-class layer's four W8 GEMMs at M=4 on {reps} row sets; quantisation untimed"}
+
+
 def verify27b_cpu_baseline(reps=16):
     """The CPU oracle on a bounded sample of the same step: the four W4 GEMMs
     of one decoder layer at the 27B-class shapes (fp64 over its 175 MB of
@@ -1247,7 +1265,7 @@ WORKLOADS = {"lm_head_verify": (lm_head_workload, lm_head_cpu_baseline),
              "layer_linears": (layer_linears_workload, lambda: verify27b_cpu_baseline_layer()),
              "lm_small": (lm_small_workload, lm_small_cpu_baseline),
              "spec_loop_27b": (spec_loop_workload, lambda: verify27b_cpu_baseline()),
-             "layer_linears_w8": (layer_linears_w8_workload, lambda: verify27b_cpu_baseline_layer())}
+             "layer_linears_w8": (layer_linears_w8_workload, lambda: layer_linears_w8_cpu_baseline())}
 
 
 def main():
