@@ -175,12 +175,12 @@ def test_mtp_draft_step_matches_oracle():
     np.testing.assert_allclose(host(q).astype(np.float64), q_ref.astype(np.float64), rtol=1e-6, atol=0)
 
 
-def _loop_setup(seed, D, L0):
+def _loop_setup(seed, D, L0, fmt="w4"):
     import torch
     cfg = dict(DENSE_27B, layers=2, V=4096)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(seed)
-    target = Decoder(cfg, D + 1, L0 + 64, gen=gen)
+    target = Decoder(cfg, D + 1, L0 + 64, gen=gen, fmt=fmt)
     E = torch.randn((cfg["V"], cfg["d"]), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
     head = MTPHead(target, E, gen=gen)
     kv = ([k.clone() for k in target.Kc], [v.clone() for v in target.Vc],
@@ -207,12 +207,12 @@ def _ar_sequence(target, head, kv, L0, t0, n, T, top_p):
     return seq
 
 
-@pytest.mark.parametrize("D", [1, 3, 5])
-def test_spec_loop_greedy_equals_autoregressive(D):
+@pytest.mark.parametrize("D,fmt", [(1, "w4"), (3, "w4"), (5, "w4"), (3, "w8")])
+def test_spec_loop_greedy_equals_autoregressive(D, fmt):
     import torch
     L0, t0, n = 700, 123, 14
-    log(f"closed loop at T = 0 vs greedy AR (2 layers, full width), D = {D}")
-    target, head, kv = _loop_setup(21, D, L0)
+    log(f"closed loop at T = 0 vs greedy AR (2 layers, full width), D = {D}, {fmt} target")
+    target, head, kv = _loop_setup(21, D, L0, fmt)
     ar = _ar_sequence(target, head, kv, L0, t0, n + D + 1, 0.0, 0.95)
     # the head's drafts
     _reset(target, head, kv)
@@ -252,3 +252,25 @@ def test_spec_loop_sampling_deterministic():
         assert loop.L == L0 + len(seq)
         runs.append(seq)
     assert runs[0] == runs[1]
+
+
+@pytest.mark.parametrize("fmt", ["w4", "w8"])
+def test_gemm_pass_counts_and_bytes(fmt):
+    """The GEMM-only pass the bench times issues one launch per linear plus the
+    LM head, and its algorithmic bytes are the weights' bytes plus activations."""
+    import torch
+    cfg = dict(DENSE_27B, layers=2, V=4096)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(31)
+    log(f"gemm pass counts, {fmt}")
+    dec = Decoder(cfg, 4, 128, gen=gen, fmt=fmt)
+    n = dec.gemm_pass(4)
+    torch.cuda.synchronize()
+    assert n == 4 * cfg["layers"] + 1
+    wb = dec.weight_bytes()
+    alg = dec.gemm_alg_bytes(4)
+    assert wb < alg < wb * 1.01
+    per_w = 0.53125 if fmt == "w4" else 1.03125
+    d, F, nqkv = cfg["d"], cfg["F"], (cfg["nq"] + 2 * cfg["nkv"]) * cfg["hd"]
+    nw = cfg["layers"] * (nqkv * d + d * d + 2 * F * d + d * F) + cfg["V"] * d
+    assert wb == int(round(nw * per_w))
