@@ -663,7 +663,7 @@ def spec_loop_workload(args):
     import torch
 
     from verify_step_w4_amd import binding as B
-    from verify_step_w4_amd.model import DENSE_27B, Decoder, MTPHead, SpecLoop
+    from verify_step_w4_amd.model import DENSE_27B, Decoder, MTPHead, SpecLoop, W4Linear
 
     cfg = dict(DENSE_27B)
     L = args.context
@@ -672,10 +672,15 @@ def spec_loop_workload(args):
     gen = torch.Generator(device=dev)
     gen.manual_seed(20261208)
     V, d = cfg["V"], cfg["d"]
-    log(f"generating the 64-layer W4 decoder, the MTP head and a {V} x {d} bf16 embedding table; context {L}")
-    dec = Decoder(cfg, 4, L + 72, gen=gen)
+    fmt = args.weights
+    log(f"generating the 64-layer {fmt.upper()} decoder, the MTP head and a {V} x {d} bf16 embedding table; "
+        f"context {L}")
+    dec = Decoder(cfg, 4, L + 72, gen=gen, fmt=fmt)
     E = torch.randn((V, d), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
-    head = MTPHead(dec, E, gen=gen)
+    # a W8 target drafts with a draft-only W4 LM head (the pages' design); its
+    # shared-head cost is timed too
+    draft_lm = W4Linear.random(V, d, 0.02, gen) if fmt == "w8" else None
+    head = MTPHead(dec, E, gen=gen, lm_head=draft_lm)
     torch.cuda.synchronize()
     K, W = max(10, args.steps // 4), max(3, args.warmup // 4)
 
@@ -703,6 +708,17 @@ def spec_loop_workload(args):
                      "verify_ms": round(t_cycle - t_draft, 4), "draft_ms_per_depth": round(t_draft / D, 4)}
         log(f"D={D}: {depths[D]}")
         del g_cycle, g_draft
+    shared = None
+    if draft_lm is not None:
+        # the same drafts through the target's own (W8) LM head, for comparison
+        head_shared = MTPHead(dec, E, gen=gen)
+        loop_s = SpecLoop(dec, head_shared, 3)
+        loop_s.start(L - 1, 123, T, top_p, seed, 0)
+        t_s = time_graph(loop_s.capture(lambda: loop_s.draft(T, top_p, seed, step_dev)), K)
+        shared = {"draft_ms_d3_shared_target_head": round(t_s, 4),
+                  "draft_only_head_speedup": round(t_s / depths[3]["draft_ms"], 3)}
+        log(f"drafts with the target's W8 head: {shared}")
+        del loop_s, head_shared
     ar_loop = SpecLoop(dec, head, 1)
     ar_loop.start(L - 1, 123, T, top_p, seed, 0)
 
@@ -743,15 +759,17 @@ def spec_loop_workload(args):
         value=1e3 / t3,
         unit="spec cycles/s",
         config={"workload": "spec_loop_27b", "layers": 64, "d_model": d, "V": V, "context": L, "draft_depth": 3,
+                "weights": fmt, "draft_lm_head": "w4 (draft-only)" if draft_lm is not None else "shared",
                 "mtp_head": "rmsnorm(h) | rmsnorm(embed) -> W4 2d->d -> 1 decoder layer -> final norm -> W4 LM head",
                 "temperature": T, "top_p": top_p},
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                  "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("verify27b"),
-                  "kernel": "w4_gemm_kernel (the W4 GEMM launches of the verify pass at M=4, replayed as a graph)",
+                  "frac": round(achieved / HBM_PEAK_GBS, 4),
+                  "traffic": measured_traffic("verify27b") if fmt == "w4" else None,
+                  "kernel": f"{fmt}_gemm_kernel (the GEMM launches of the verify pass at M=4, replayed as a graph)",
                   "alg_bytes_per_launch": int(per_launch), "avg_launch_us": round(ms_launch * 1e3, 2)},
         spec_loop={"by_depth": depths, "m1_ar_step_ms": round(t_ar, 4), "eager_cycle_ms": round(eager_s * 1e3, 2),
                    "measured_accepted_per_cycle": acc, "measured_alpha": round(alpha_meas, 4),
-                   "tokens_per_s_by_alpha": model},
+                   "tokens_per_s_by_alpha": model, "draft_only_head": shared},
     )
 
 

@@ -182,7 +182,9 @@ def _loop_setup(seed, D, L0, fmt="w4"):
     gen.manual_seed(seed)
     target = Decoder(cfg, D + 1, L0 + 64, gen=gen, fmt=fmt)
     E = torch.randn((cfg["V"], cfg["d"]), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
-    head = MTPHead(target, E, gen=gen)
+    # a W8 target gets a draft-only W4 LM head
+    lm = W4Linear.random(cfg["V"], cfg["d"], 0.02, gen) if fmt == "w8" else None
+    head = MTPHead(target, E, gen=gen, lm_head=lm)
     kv = ([k.clone() for k in target.Kc], [v.clone() for v in target.Vc],
           [k.clone() for k in head.block.Kc], [v.clone() for v in head.block.Vc])
     return target, head, kv

@@ -397,10 +397,12 @@ class MTPHead:
     inside; this is the common MTP head: the hidden row h of the last processed
     position and the embedding of the next token, each RMS-normalised with its
     own gain and concatenated, a W4 projection from 2d back to d, one decoder
-    layer (own KV cache), the final norm and the target's W4 LM head.  One
-    ``draft`` call is one depth: its output row and drawn token feed the next."""
+    layer (own KV cache), the final norm and the target's LM head -- or, with
+    ``lm_head`` given, a draft-only head (the pages' draft-only 4-bit LM head
+    beside a higher-precision target head).  One ``draft`` call is one depth:
+    its output row and drawn token feed the next."""
 
-    def __init__(self, target: "Decoder", embed, gen=None, weights=None, kv_fill: bool = True):
+    def __init__(self, target: "Decoder", embed, gen=None, weights=None, kv_fill: bool = True, lm_head=None):
         import torch
         cfg = dict(target.cfg, layers=1)
         d, V = cfg["d"], cfg["V"]
@@ -411,7 +413,7 @@ class MTPHead:
         self.gamma_h, self.gamma_e, self.proj = weights["gamma_h"], weights["gamma_e"], weights["proj"]
         self.block = Decoder(cfg, 1, target.Lmax, gen=gen, device=dev, kv_fill=kv_fill,
                              weights=dict(layers=[weights["layer"]], final_gamma=weights["final_gamma"],
-                                          lm_head=target.lm_head))
+                                          lm_head=target.lm_head if lm_head is None else lm_head))
         self.inp = torch.empty((1, 2 * d), dtype=torch.int16, device=dev)
         self.x = torch.empty((1, d), dtype=torch.int16, device=dev)
         self.proj_ws = B.workspace(B.gemm_workspace_bytes(1, d, 2 * d), dev)
