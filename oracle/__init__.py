@@ -93,6 +93,8 @@ def lib():
         L.oracle_mtp_input.argtypes = [_P, _P, _P, _P, _I64, _F64, _P]
         L.oracle_w8_quantize.argtypes = [_P, _I64, _I64, _P, _P]
         L.oracle_w8_gemm.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P]
+        L.oracle_w6_quantize.argtypes = [_P, _I64, _I64, _P, _P]
+        L.oracle_w6_gemm.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P]
         L.oracle_embed_rows.argtypes = [_P, _I64, _I64, _P, _I64, _P]
         L.oracle_draft_uniform.argtypes = [_U64, _U64, _I32]
         L.oracle_draft_uniform.restype = _F64
@@ -412,5 +414,28 @@ def w8_gemm(x_bf16: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> np.nda
     assert codes.shape == (N, K) and scales.shape == (N, K // 64)
     y = np.zeros((M, N), dtype=np.float64)
     lib().oracle_w8_gemm(_ptr(x_bf16), M, K, _ptr(np.ascontiguousarray(codes)), _ptr(np.ascontiguousarray(scales)),
+                         N, _ptr(y))
+    return y
+
+
+def w6_quantize(w: np.ndarray):
+    """w: float32 [N][K] (K % 64 == 0) -> (codes u8 [N][K] holding c + 32, scales u16 [N][K/64])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    assert K % 64 == 0
+    codes = np.zeros((N, K), dtype=np.uint8)
+    scales = np.zeros((N, K // 64), dtype=np.uint16)
+    lib().oracle_w6_quantize(_ptr(w), N, K, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def w6_gemm(x_bf16: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """x_bf16: uint16 [M][K]; codes u8 [N][K] (c + 32); returns float64 [M][N]."""
+    x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    M, K = x_bf16.shape
+    N = codes.shape[0]
+    assert codes.shape == (N, K) and scales.shape == (N, K // 64)
+    y = np.zeros((M, N), dtype=np.float64)
+    lib().oracle_w6_gemm(_ptr(x_bf16), M, K, _ptr(np.ascontiguousarray(codes)), _ptr(np.ascontiguousarray(scales)),
                          N, _ptr(y))
     return y
