@@ -455,6 +455,32 @@ VW4_API int w8_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_
                                     const uint16_t* scales_packed, float* part, int32_t M, int32_t N, int32_t K,
                                     void* stream);
 
+/* ------------------------------------------------------------------------
+ * A third weight format: W6 (the same BaseRT section lists Q2 ... Q8; no
+ * layout).  Per row n and 64-element group g: scale = fp16_rne(absmax / 31),
+ * c_k = clamp(rint(w_k / scale), -31, 31) with the rounded scale, half-even;
+ * an all-zero group gets scale 0 and codes 0.  Canonical storage: u8
+ * codes[N][K] holding u = c + 32, fp16 scales[N][K/64].  Kernel storage: the
+ * low 4 bits of u in the W4 packed layout (vw4_w4_packed_bytes(N, K) bytes),
+ * the high 2 bits in a 2-bit plane of vw4_w6_hi_plane_bytes(N, K) bytes (per
+ * 64-row tile and K-group 1 KiB; lane l = 16 kq + i owns 16 bytes, dword nb
+ * holding row 16 nb + i at k = 32 s + 8 kq + j in bits 8 s + 2 (j / 2) +
+ * 16 (j % 2)), and the W4 packed scales.
+ * ------------------------------------------------------------------------ */
+VW4_API int vw4_w6_quantize_host(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales);
+VW4_API size_t vw4_w6_hi_plane_bytes(int64_t N, int64_t K);
+VW4_API int vw4_w6_pack(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, uint8_t* hi,
+                        uint8_t* lo, uint16_t* packed_scales, void* stream);
+/* As w8_skinny_gemm / w8_skinny_gemm_partials / vw4_w8_*_bytes, for W6 planes. */
+VW4_API size_t vw4_w6_workspace_bytes(int32_t M, int32_t N, int32_t K);
+VW4_API int w6_skinny_gemm(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, const uint8_t* w_lo,
+                           const uint16_t* scales_packed, void* y, int64_t ldy, int32_t y_dtype, int32_t M, int32_t N,
+                           int32_t K, void* ws, size_t ws_bytes, void* stream);
+VW4_API int vw4_w6_partials_layout(int32_t M, int32_t N, int32_t K, int32_t* S, int64_t* ldp);
+VW4_API int w6_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, const uint8_t* w_lo,
+                                    const uint16_t* scales_packed, float* part, int32_t M, int32_t N, int32_t K,
+                                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -67,6 +67,14 @@ SIGNATURES = {
     "vw4_w8_partials_layout": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
                                               ctypes.POINTER(ctypes.c_int64)]),
     "w8_skinny_gemm_partials": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
+    "vw4_w6_quantize_host": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
+    "vw4_w6_hi_plane_bytes": (_SZ, [_I64, _I64]),
+    "vw4_w6_pack": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P, _P]),
+    "vw4_w6_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "w6_skinny_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+    "vw4_w6_partials_layout": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
+                                              ctypes.POINTER(ctypes.c_int64)]),
+    "w6_skinny_gemm_partials": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
     "draft_sample": (ctypes.c_int, [_P, _P, _I32, ctypes.c_float, _U64, _P, _U64, _I32, _P, _P, _P, _P, _SZ, _P]),
     "vw4_gemm_partials_layout": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
                                                 ctypes.POINTER(ctypes.c_int64)]),
@@ -361,6 +369,40 @@ def w8_skinny_gemm_partials(x, w_hi, w_lo, scales_packed, part, M: int, N: int, 
     _check("w8_skinny_gemm_partials", lib().w8_skinny_gemm_partials(_ptr(x), ldx, _ptr(w_hi), _ptr(w_lo),
                                                                     _ptr(scales_packed), _ptr(part), M, N, K,
                                                                     _stream(stream)))
+
+
+def w6_quantize_host(w: np.ndarray):
+    """fp32 [N][K] host array -> (codes u8 [N][K] holding c + 32, scales u16 [N][K/64])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    codes = np.zeros((N, K), dtype=np.uint8)
+    scales = np.zeros((N, K // 64), dtype=np.uint16)
+    _check("vw4_w6_quantize_host", lib().vw4_w6_quantize_host(w.ctypes.data_as(ctypes.c_void_p), N, K,
+                                                              codes.ctypes.data_as(ctypes.c_void_p),
+                                                              scales.ctypes.data_as(ctypes.c_void_p)))
+    return codes, scales
+
+
+def w6_pack(codes, scales, N: int, K: int, hi, lo, pscales, stream=None):
+    _check("vw4_w6_pack", lib().vw4_w6_pack(_ptr(codes), _ptr(scales), N, K, _ptr(hi), _ptr(lo), _ptr(pscales),
+                                            _stream(stream)))
+
+
+def w6_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().vw4_w6_workspace_bytes(M, N, K))
+
+
+def w6_skinny_gemm(x, w_hi, w_lo, scales_packed, y, M: int, N: int, K: int, ws=None, stream=None,
+                   ldx: int | None = None, ldy: int | None = None):
+    """y[M][N] (fp32 or bf16 tensor) = x[M][K] (bf16 bits) @ W6^T."""
+    import torch
+    ydt = VW4_F32 if y.dtype == torch.float32 else VW4_BF16
+    ldx = x.stride(0) if ldx is None else ldx
+    ldy = y.stride(0) if ldy is None else ldy
+    nbytes = ws.numel() if ws is not None else 0
+    _check("w6_skinny_gemm", lib().w6_skinny_gemm(_ptr(x), ldx, _ptr(w_hi), _ptr(w_lo), _ptr(scales_packed), _ptr(y),
+                                                  ldy, ydt, M, N, K, _ptr(ws), nbytes, _stream(stream)))
+    return y
 
 
 def rowstats_to_numpy(stats_tensor) -> np.ndarray:

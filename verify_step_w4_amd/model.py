@@ -88,6 +88,45 @@ class W8Linear:
         return self.N * self.K + self.N * (self.K // 64) * 2
 
 
+class W6Linear:
+    """A [N][K] matrix in the W6 format (6-bit codes, fp16 scale per 64 K): the
+    2-bit high plane, the 4-bit low plane (W4 layout) and the packed scales."""
+
+    def __init__(self, hi, lo, pscales, N: int, K: int):
+        self.hi, self.lo, self.pscales, self.N, self.K = hi, lo, pscales, N, K
+
+    @classmethod
+    def from_codes(cls, codes, scales, stream=None):
+        """codes: uint8 device [N][K] (c + 32); scales: int16 device [N][K/64] (fp16 bits)."""
+        import torch
+        N, K = codes.shape
+        cb, sb = B.packed_sizes(N, K)
+        hb = int(B.lib().vw4_w6_hi_plane_bytes(N, K))
+        hi = torch.empty(hb, dtype=torch.uint8, device=codes.device)
+        lo = torch.empty(cb, dtype=torch.uint8, device=codes.device)
+        ps = torch.empty(sb // 2, dtype=torch.int16, device=codes.device)
+        B.w6_pack(codes, scales, N, K, hi, lo, ps, stream)
+        return cls(hi, lo, ps, N, K)
+
+    @classmethod
+    def from_fp32(cls, w, device="cuda"):
+        import torch
+        wn = w.detach().cpu().numpy() if hasattr(w, "detach") else w
+        codes, scales = B.w6_quantize_host(wn)
+        return cls.from_codes(torch.from_numpy(codes).to(device), torch.from_numpy(scales.view("int16")).to(device))
+
+    @classmethod
+    def random(cls, N: int, K: int, gen, device="cuda"):
+        """Uniform codes in [-31, 31] and fp16 scales in [4e-4, 1.2e-3] (timing inputs)."""
+        import torch
+        codes = torch.randint(1, 64, (N, K), generator=gen, device=device, dtype=torch.int32).to(torch.uint8)
+        scales = (4e-4 + 8e-4 * torch.rand((N, K // 64), generator=gen, device=device)).to(torch.float16)
+        return cls.from_codes(codes, scales.view(torch.int16))
+
+    def nbytes(self) -> int:
+        return self.N * self.K * 3 // 4 + self.N * (self.K // 64) * 2
+
+
 class LMHeadVerify:
     """One verify step on an LM head: W4 GEMM of the M rows, temperature/top-p
     statistics, Leviathan–Chen acceptance.  All buffers are allocated once."""
