@@ -791,22 +791,24 @@ def verify27b_cpu_baseline_layer(reps=8):
             "sample": f"one 27B-class layer's four W4 GEMMs at M=4 on {reps} row sets; quantisation untimed"}
 
 
-def layer_linears_w8_cpu_baseline(reps=4):
-    """The CPU oracle's W8 GEMM on the four linears of one layer at M=4 (fp64), reps row sets."""
+def layer_linears_w8_cpu_baseline(reps=4, fmt="w8"):
+    """The CPU oracle's W8 (or W6) GEMM on the four linears of one layer at M=4 (fp64), reps row sets."""
     import oracle
     from verify_step_w4_amd import synth
+    quant, gemm = (oracle.w8_quantize, oracle.w8_gemm) if fmt == "w8" else (oracle.w6_quantize, oracle.w6_gemm)
     g = synth.rng(synth.SEED_BASE + 9)
     tot = 0.0
     for N, K in [(7168, 5120), (5120, 5120), (34816, 5120), (5120, 17408)]:
-        codes, scales = oracle.w8_quantize(synth.normal_f32(g, (N, K), 0.02))
+        codes, scales = quant(synth.normal_f32(g, (N, K), 0.02))
         for r in range(reps):
             x = synth.f32_to_bf16_bits(synth.normal_f32(g, (4, K), 1.0))
             t0 = time.perf_counter()
-            oracle.w8_gemm(x, codes, scales)
+            gemm(x, codes, scales)
             tot += time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(reps / tot, 4), "unit": "layer passes/s", "cores": cores, "kind": "oracle",
-            "sample": f"one 27B-class layer's four W8 GEMMs at M=4 on {reps} row sets; quantisation untimed"}
+            "sample": f"one 27B-class layer's four {fmt.upper()} GEMMs at M=4 on {reps} row sets; "
+                      "quantisation untimed"}
 
 
 def verify27b_cpu_baseline(reps=16):
@@ -1129,7 +1131,11 @@ def layer_linears_workload(args):
     )
 
 
-def layer_linears_w8_workload(args):
+def layer_linears_w6_workload(args):
+    return layer_linears_w8_workload(args, fmt="w6")
+
+
+def layer_linears_w8_workload(args, fmt="w8"):
     """The same four linears of one 27B-shaped layer in the W8 format (int8
     codes, fp16 scale per 64 K: 1.03125 bytes per weight, 351 MB per layer),
     plain GEMM outputs (gate|up as one [34816][5120] product); 4 layers'
@@ -1138,32 +1144,36 @@ def layer_linears_w8_workload(args):
     import torch
 
     from verify_step_w4_amd import binding as B
-    from verify_step_w4_amd.model import W8Linear
+    from verify_step_w4_amd.model import W6Linear, W8Linear
 
     d, F, nqkv = 5120, 17408, 7168
     nlay = 4
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20261209)
     shapes = {"qkv": (nqkv, d), "o": (d, d), "gate_up": (2 * F, d), "down": (d, F)}
-    log(f"generating {nlay} layers of W8 linears (351 MB each)")
-    layers = [{nm: W8Linear.random(N, K, gen) for nm, (N, K) in shapes.items()} for _ in range(nlay)]
+    Lin = W8Linear if fmt == "w8" else W6Linear
+    code_bytes = 1.0 if fmt == "w8" else 0.75
+    gemm = B.w8_skinny_gemm if fmt == "w8" else B.w6_skinny_gemm
+    wsb = B.w8_workspace_bytes if fmt == "w8" else B.w6_workspace_bytes
+    log(f"generating {nlay} layers of {fmt.upper()} linears")
+    layers = [{nm: Lin.random(N, K, gen) for nm, (N, K) in shapes.items()} for _ in range(nlay)]
     M = 4
     xs = {K: torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16) for K in (d, F)}
     ys = {nm: torch.empty((M, N), dtype=torch.float32, device="cuda") for nm, (N, K) in shapes.items()}
-    ws = {nm: B.workspace(max(B.w8_workspace_bytes(M, N, K), 256)) for nm, (N, K) in shapes.items()}
+    ws = {nm: B.workspace(max(wsb(M, N, K), 256)) for nm, (N, K) in shapes.items()}
 
     def issue(names=tuple(shapes)):
         n = 0
         for L in layers:
             for nm in names:
                 N, K = shapes[nm]
-                B.w8_skinny_gemm(xs[K], L[nm].hi, L[nm].lo, L[nm].pscales, ys[nm], M, N, K, ws=ws[nm])
+                gemm(xs[K], L[nm].hi, L[nm].lo, L[nm].pscales, ys[nm], M, N, K, ws=ws[nm])
                 n += 1
         return n
 
     def alg(nm):
         N, K = shapes[nm]
-        return N * K + N * (K // 64) * 2 + M * K * 2 + M * N * 4
+        return int(N * K * code_bytes) + N * (K // 64) * 2 + M * K * 2 + M * N * 4
 
     reps = max(1, args.steps // nlay)
     ms_launch, n_launch = time_graphs([issue], reps)
@@ -1173,20 +1183,22 @@ def layer_linears_w8_workload(args):
         us = time_graphs([lambda nm=nm: issue((nm,))], reps)[0] * 1e3
         per[nm] = {"avg_us": round(us, 2), "GBs": round(alg(nm) / (us * 1e-6) / 1e9, 1),
                    "frac": round(alg(nm) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-    log(f"W8 layer {layer_us:.2f} us: {per}")
+    log(f"{fmt.upper()} layer {layer_us:.2f} us: {per}")
     lb = sum(alg(nm) for nm in shapes)
     return dict(
         ms_per_step=layer_us * 1e-3,
         value=1.0 / (layer_us * 1e-6),
         unit="layer passes/s",
-        config={"workload": "layer_linears_w8", "d_model": d, "qkv": [nqkv, d], "o": [d, d], "gate_up": [2 * F, d],
+        config={"workload": f"layer_linears_{fmt}", "d_model": d, "qkv": [nqkv, d], "o": [d, d], "gate_up": [2 * F, d],
                 "down": [d, F], "M": M, "rotated_layers": nlay,
-                "weights": "int8 group-64 symmetric, fp16 scales (two nibble planes)"},
+                "weights": ("int8 group-64 symmetric, fp16 scales (two nibble planes)" if fmt == "w8" else
+                            "6-bit group-64 symmetric, fp16 scales (2-bit + 4-bit planes)")},
         roofline={"bound": "hbm", "achieved": round(lb / (layer_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
                   "unit": "GB/s", "frac": round(lb / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
-                  "kernel": "w8_gemm_kernel (+ w8_reduce_kernel; the four linears of a layer at M=4, graph-replayed)",
+                  "kernel": f"{fmt}_gemm_kernel (+ {fmt}_reduce_kernel; the four linears of a layer at M=4, "
+                            "graph-replayed)",
                   "alg_bytes_per_launch": int(lb / 4), "avg_launch_us": round(layer_us / 4, 2)},
-        w8_gemm_by_linear=per,
+        **{f"{fmt}_gemm_by_linear": per},
     )
 
 
@@ -1283,7 +1295,8 @@ WORKLOADS = {"lm_head_verify": (lm_head_workload, lm_head_cpu_baseline),
              "layer_linears": (layer_linears_workload, lambda: verify27b_cpu_baseline_layer()),
              "lm_small": (lm_small_workload, lm_small_cpu_baseline),
              "spec_loop_27b": (spec_loop_workload, lambda: verify27b_cpu_baseline()),
-             "layer_linears_w8": (layer_linears_w8_workload, lambda: layer_linears_w8_cpu_baseline())}
+             "layer_linears_w8": (layer_linears_w8_workload, lambda: layer_linears_w8_cpu_baseline()),
+             "layer_linears_w6": (layer_linears_w6_workload, lambda: layer_linears_w8_cpu_baseline(fmt="w6"))}
 
 
 def main():
@@ -1329,7 +1342,7 @@ def main():
     for k in ("stages_us", "w4_gemm_by_linear", "accepted_length_hist", "flagged_steps", "m1_ar_step_ms",
               "verify_over_ar", "step_hbm_gbs", "experts_per_step", "grouped_gemm_gbs", "m_sweep", "unit_note",
               "context_sweep", "stats_accept_sweep", "sustained", "attention_by_context", "spec_loop",
-              "w8_gemm_by_linear"):
+              "w8_gemm_by_linear", "w6_gemm_by_linear"):
         if k in res:
             out[k] = res[k]
     if not args.no_cpu_baseline:
