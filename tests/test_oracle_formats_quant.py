@@ -106,6 +106,38 @@ def test_quant_invariants_random():
             assert abs(cg[j]) == 7 and np.sign(cg[j]) == np.sign(wg[j])
 
 
+def _numpy_w4(w):
+    """The quantiser recipe in numpy's IEEE arithmetic: scale = fp16(absmax / 7)
+    (binary32 division, binary16 rounding), codes = clamp(round-half-even(w /
+    scale), -7, 7) against the rounded scale, zero codes for a zero scale,
+    canonical nibbles c + 8 with even k low."""
+    N, K = w.shape
+    G = K // 64
+    wg = w.reshape(N, G, 64)
+    a = np.abs(wg).max(axis=2)
+    s16 = (a / np.float32(7.0)).astype(np.float32).astype(np.float16)
+    sf = s16.astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.rint(wg / sf[:, :, None])
+    c = np.where(sf[:, :, None] != 0, np.clip(r, -7, 7), 0).astype(np.int64).reshape(N, K)
+    u = (c + 8).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8), s16.view(np.uint16)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_quant_matches_numpy_reimplementation(seed):
+    rng = np.random.default_rng(100 + seed)
+    w = rng.normal(0.0, 0.02, (41, 320)).astype(np.float32)
+    w[2, 64:128] = 0.0                         # zero group
+    w[4, :64] = 1e-9                           # scale underflows to a subnormal fp16 / zero
+    w[6, 200] = 2.5                            # one outlier
+    w[8, 0:64] = np.float32(7 * 2.0 ** -7) * rng.integers(-1, 2, 64).astype(np.float32)   # ties at +-0.5 ulp
+    c1, s1 = oracle.w4_quantize(w)
+    c2, s2 = _numpy_w4(w)
+    assert np.array_equal(s1, s2)
+    assert np.array_equal(c1, c2)
+
+
 def test_quant_exactly_representable_roundtrip():
     # w = c * 2^-7 with +-7 present in every group: scale must be 2^-7, codes c
     g = np.random.default_rng(3)

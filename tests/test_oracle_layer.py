@@ -107,11 +107,39 @@ def test_rope_rotation_properties():
     d1 = oracle.rope(q, 1030) @ oracle.rope(k, 1000)
     d2 = oracle.rope(q, 40) @ oracle.rope(k, 10)
     assert abs(d1 - d2) < 1e-9
-    # lowest frequency pair rotates by exactly pos radians
+    # pair d = 0 (the highest frequency) rotates by exactly pos radians
     e = np.zeros(128)
     e[0] = 1.0
     r = oracle.rope(e, 3)
     assert abs(r[0] - np.cos(3)) < 1e-15 and abs(r[64] - np.sin(3)) < 1e-15
+
+
+def test_rope_frequency_schedule_hand_values():
+    """Pair d of a head of H dims turns by pos * theta^(-2d/H): at H = 128 and
+    theta = 10000 that is pos * 10^(-d/16), so pair 16 turns by pos / 10,
+    pair 32 by pos / 100 and pair 48 by pos / 1000 (rotate-half: dims d and
+    d + H/2).  These values hold for no other exponent (theta^(-d/H) would
+    give pos / 10^(d/32)), so a wrong schedule fails here."""
+    H = 128
+    cases = [(32, 100, 1.0), (16, 10, 1.0), (48, 2500, 2.5), (8, 4, 4 * 10 ** -0.5), (63, 7, 7 * 10 ** (-63 / 16))]
+    for d, pos, ang in cases:
+        e = np.zeros(H)
+        e[d] = 1.0
+        r = oracle.rope(e, pos)
+        assert abs(r[d] - np.cos(ang)) < 1e-12 and abs(r[d + H // 2] - np.sin(ang)) < 1e-12, (d, pos)
+        # every other entry stays zero: the pair turns only within itself
+        rest = np.delete(r, [d, d + H // 2])
+        assert np.all(rest == 0.0)
+        # the second half of the pair turns the other way round: (0, 1) -> (-sin, cos)
+        f = np.zeros(H)
+        f[d + H // 2] = 1.0
+        r2 = oracle.rope(f, pos)
+        assert abs(r2[d] + np.sin(ang)) < 1e-12 and abs(r2[d + H // 2] - np.cos(ang)) < 1e-12, (d, pos)
+    # another head size and base: H = 64, theta = 1e6, pair 16 turns by pos / 1000
+    e = np.zeros(64)
+    e[16] = 1.0
+    r = oracle.rope(e, 1000, theta=1e6)
+    assert abs(r[16] - np.cos(1.0)) < 1e-12 and abs(r[48] - np.sin(1.0)) < 1e-12
 
 
 def _kv(seed, Hkv, Lc, Dh):
