@@ -663,7 +663,7 @@ def spec_loop_workload(args):
     import torch
 
     from verify_step_w4_amd import binding as B
-    from verify_step_w4_amd.model import DENSE_27B, Decoder, MTPHead, SpecLoop, W4Linear
+    from verify_step_w4_amd.model import DENSE_27B, Decoder, DepthTuner, MTPHead, SpecLoop, W4Linear
 
     cfg = dict(DENSE_27B)
     L = args.context
@@ -742,13 +742,23 @@ def spec_loop_workload(args):
     eager_s = (time.perf_counter() - t0) / ncyc
     alpha_meas = float(np.mean(acc)) / D
 
+    # the draft-depth autotune: every depth and the AR step measured on the
+    # device (graph-timed cycles, real cycles for the yield), the best locked
+    tuner = DepthTuner(dec, head, (1, 2, 3))
+    tune = tuner.tune(L - 1, 123, T, top_p, seed, cycles=8, reps=K)
+    autotune = {"pick": tune["pick"], "tokens_per_s": {k: round(v, 2) for k, v in tune["tokens_per_s"].items()},
+                "ms": {k: round(v, 4) for k, v in tune["ms"].items()},
+                "tokens_per_cycle": {k: round(v, 4) for k, v in tune["tokens_per_cycle"].items()}}
+    log(f"autotune: {autotune}")
+    # the same rule on modelled yields, for acceptance rates the random head cannot reach
     model = {}
     for a in (round(alpha_meas, 4), 0.5, 0.6, 0.7, 0.8, 0.9):
-        row = {"ar": round(1e3 / t_ar, 2)}
+        tps = {0: 1e3 / t_ar}
         for D_, r in depths.items():
-            row[f"D{D_}"] = round(tokens_per_cycle(a, D_) * 1e3 / r["cycle_ms"], 2)
-        best = max(row, key=row.get)
-        model[str(a)] = {"tokens_per_s": row, "autotune_pick": best}
+            tps[D_] = tokens_per_cycle(a, D_) * 1e3 / r["cycle_ms"]
+        pick = DepthTuner.choose(tps)
+        model[str(a)] = {"tokens_per_s": {("ar" if k == 0 else f"D{k}"): round(v, 2) for k, v in tps.items()},
+                         "autotune_pick": "ar" if pick == 0 else f"D{pick}"}
     # the dominant kernel: the W4 GEMM launches of the verify pass at M = 4
     ms_launch, n_launch = time_graphs([lambda: dec.gemm_pass(4)], 10)
     per_launch = dec.gemm_alg_bytes(4) / n_launch
@@ -769,7 +779,7 @@ def spec_loop_workload(args):
                   "alg_bytes_per_launch": int(per_launch), "avg_launch_us": round(ms_launch * 1e3, 2)},
         spec_loop={"by_depth": depths, "m1_ar_step_ms": round(t_ar, 4), "eager_cycle_ms": round(eager_s * 1e3, 2),
                    "measured_accepted_per_cycle": acc, "measured_alpha": round(alpha_meas, 4),
-                   "tokens_per_s_by_alpha": model, "draft_only_head": shared},
+                   "autotune": autotune, "tokens_per_s_by_alpha": model, "draft_only_head": shared},
     )
 
 

@@ -89,3 +89,14 @@ def test_tokens_per_cycle_by_enumeration(alpha, D):
     # the cycle emits k + 1 tokens
     e = sum((k + 1) * alpha ** k * (1 - alpha) for k in range(D)) + (D + 1) * alpha ** D
     assert abs(bench.tokens_per_cycle(alpha, D) - e) < 1e-12
+
+
+def test_depth_choice_rule():
+    """The autotune's decision: the most tokens per second wins, AR (depth 0)
+    is kept on ties and whenever no depth beats it."""
+    from verify_step_w4_amd.model import DepthTuner
+    assert DepthTuner.choose({0: 216.0, 1: 201.6, 2: 186.6, 3: 173.0}) == 0      # alpha ~ 0: AR
+    assert DepthTuner.choose({0: 216.0, 1: 343.0, 2: 409.0, 3: 438.0}) == 3      # alpha 0.7
+    assert DepthTuner.choose({0: 216.0, 1: 303.0, 2: 327.0, 3: 324.0}) == 2      # alpha 0.5
+    assert DepthTuner.choose({0: 300.0, 1: 300.0, 2: 299.0}) == 0                # tie: the smaller depth
+    assert DepthTuner.choose({0: 100.0, 2: 150.0, 3: 150.0}) == 2

@@ -21,6 +21,7 @@ from verify_step_w4_amd import synth
 from verify_step_w4_amd.model import DENSE_27B, Decoder, MTPHead, SpecLoop, W4Linear
 
 from helpers import dev, host, log, rows_from_vb, vb_from_rows
+from layer_parity import DecoderCapture, bf16_close, check_decoder_ops, end_to_end
 from test_gpu_forward import TINY, _device_weights, _host_model, _oracle_forward
 
 pytestmark = pytest.mark.gpu
@@ -157,18 +158,27 @@ def test_mtp_draft_step_matches_oracle():
     q = torch.zeros(V, dtype=torch.float32, device="cuda")
     tok = torch.zeros(1, dtype=torch.int32, device="cuda")
     T, top_p = 0.6, 0.95
+    cap = DecoderCapture(head.block, 1)
     logits = host(head.draft(dev(h), 3, dev(np.array([1], np.int32)), dev(np.array([token], np.int32)), pos, T,
-                             top_p, SEED, 12, 2, q, tok)).copy()
+                             top_p, SEED, 12, 2, q, tok, gemm_hook=cap)).copy()
     torch.cuda.synchronize()
-    # oracle: projection input, projection, then the one-layer decoder composition
+    # teacher forced, op by op: the projection input, the projection (bf16
+    # output) from the GPU's input, then every op of the head's decoder layer
+    # and the LM head from the GPU's own inputs (tests/layer_parity.py)
+    inp_gpu = host(head.inp).reshape(1, -1)
+    bf16_close(inp_gpu[0], oracle.mtp_input(h[1], E[token], hh["gamma_h"], hh["gamma_e"], cfg["eps"]),
+               min_exact=0.99, what="projection input")
+    x_gpu = host(head.x).reshape(1, -1).copy()
+    bf16_close(x_gpu, oracle.w4_gemm(inp_gpu, *oracle.w4_quantize(hh["proj"])), what="projection")
+    bm = dict(layers=[hh["layer"]], final_gamma=hh["final_gamma"], lm_head=hm["lm_head"])
+    worst, ident = check_decoder_ops(cap, bm, dict(cfg, layers=1), x_gpu, pos)
+    # end to end from the oracle's own chain: a statistic
     inp = oracle.bf16_round(oracle.mtp_input(h[1], E[token], hh["gamma_h"], hh["gamma_e"], cfg["eps"]))
     x = oracle.bf16_round(oracle.w4_gemm(inp.reshape(1, -1), *oracle.w4_quantize(hh["proj"])))
-    bm = dict(layers=[hh["layer"]], final_gamma=hh["final_gamma"], lm_head=hm["lm_head"])
     ref = _oracle_forward(dict(cfg, layers=1), bm, [Kh.copy()], [Vh.copy()], x, pos)
-    rms = np.sqrt((ref ** 2).mean(axis=1, keepdims=True))
-    rel = np.abs(logits - ref) / np.maximum(np.abs(ref), rms)
-    print(f"[mtp draft] max rel err {rel.max():.3e}, median {np.median(rel):.3e}", flush=True)
-    assert rel.max() < 2e-2 and np.median(rel) < 2e-3
+    mx, med = end_to_end(logits, ref)
+    print(f"[mtp draft] per op: worst fp32 rel {worst:.2e}, bf16 identical >= {ident:.4f}; "
+          f"end to end (statistic): max rel {mx:.3e}, median {med:.3e}", flush=True)
     # the draw, from the GPU's own logits, is the oracle's
     t_ref, q_ref, _, f_ref = oracle.draft_sample(logits[0], T, top_p, SEED, 12, 2)
     assert (f_ref & 8) or int(host(tok)[0]) == t_ref
@@ -276,3 +286,52 @@ def test_gemm_pass_counts_and_bytes(fmt):
     d, F, nqkv = cfg["d"], cfg["F"], (cfg["nq"] + 2 * cfg["nkv"]) * cfg["hd"]
     nw = cfg["layers"] * (nqkv * d + d * d + 2 * F * d + d * F) + cfg["V"] * d
     assert wb == int(round(nw * per_w))
+
+
+def test_depth_autotune():
+    """The draft-depth autotune (DepthTuner) on the 2-layer full-width model:
+    * random weights at T = 0.6: the head's drafts are independent of the
+      target and almost never accepted, so every depth emits about one token
+      per cycle at a higher cost than the AR step -- AR is locked;
+    * T = 0 with drafts that are the target's greedy continuation: every
+      draft is accepted (D + 1 tokens per cycle, alpha = 1), and the pick is
+      the depth with the most (D + 1) / cycle time among the measured ones;
+    * at T = 0 the sequence decode() emits equals greedy autoregressive
+      decoding token for token whatever depth is locked (AR, 1, 2, 3)."""
+    import torch
+    from verify_step_w4_amd.model import DepthTuner
+    L0, t0 = 600, 321
+    log("draft-depth autotune (2 layers, full width)")
+    target, head, kv = _loop_setup(23, 3, L0)
+    tuner = DepthTuner(target, head, (1, 2, 3))
+    _reset(target, head, kv)
+    rep = tuner.tune(L0, t0, 0.6, 0.95, SEED, cycles=6, reps=5)
+    print(f"[autotune, random head] {rep}", flush=True)
+    assert rep["depth"] == 0 and rep["pick"] == "ar"
+    assert all(1.0 <= rep["tokens_per_cycle"][f"D{D}"] <= D + 1 for D in (1, 2, 3))
+    # greedy continuation drafts: alpha = 1
+    cycles = 4
+    ar = _ar_sequence(target, head, kv, L0, t0, cycles * 4 + 4, 0.0, 0.95)
+
+    def greedy_drafts(loop, emitted):
+        return torch.tensor(ar[len(emitted):len(emitted) + loop.D], dtype=torch.int32, device="cuda")
+
+    _reset(target, head, kv)
+    rep = tuner.tune(L0, t0, 0.0, 0.95, SEED, cycles=cycles, reps=5, drafts_fn=greedy_drafts)
+    print(f"[autotune, greedy drafts] {rep}", flush=True)
+    for D in (1, 2, 3):
+        assert rep["tokens_per_cycle"][f"D{D}"] == D + 1
+    tps = rep["tokens_per_s"]
+    for D in (1, 2, 3):
+        assert abs(tps[f"D{D}"] - (D + 1) * 1e3 / rep["ms"][f"D{D}"]) < 1e-9 * tps[f"D{D}"]
+    assert abs(tps["ar"] - 1e3 / rep["ms"]["ar"]) < 1e-9 * tps["ar"]
+    want = DepthTuner.choose({0: tps["ar"], 1: tps["D1"], 2: tps["D2"], 3: tps["D3"]})
+    assert rep["depth"] == want and want == max((0, 1, 2, 3), key=lambda D: (tps["ar" if D == 0 else f"D{D}"], -D))
+    # whatever depth is locked, T = 0 decoding is greedy decoding
+    n = 13
+    for D in (0, 1, 2, 3):
+        _reset(target, head, kv)
+        tuner.depth = D
+        seq, loop = tuner.decode(L0, t0, n, 0.0, 0.95, SEED)
+        assert seq[:n] == ar[:n], (D, seq, ar)
+        assert loop.L == L0 + len(seq)

@@ -15,17 +15,7 @@ from helpers import dev, host, log, rows_from_vb, vb_from_rows
 
 pytestmark = pytest.mark.gpu
 
-BF16_REL = 2.0 ** -8
-
-
-def bf16_close(gpu_bits, ref, rms_axis=-1, min_exact=0.97):
-    g = synth.bf16_bits_to_f32(gpu_bits).astype(np.float64)
-    ref = np.asarray(ref, dtype=np.float64)
-    rms = np.sqrt((ref ** 2).mean(axis=rms_axis, keepdims=True))
-    err = np.abs(g - ref)
-    assert np.all(err <= BF16_REL * np.abs(ref) + 1e-3 * rms), float((err / (np.abs(ref) + rms)).max())
-    exact = (gpu_bits == oracle.bf16_round(ref)).mean()
-    assert exact >= min_exact, exact
+from layer_parity import BF16_REL, bf16_close  # noqa: F401  (the bf16 bar, shared with the composed tests)
 
 
 def partials(seed, S, M, N, ldp, std=1.0):

@@ -32,12 +32,54 @@ def _run(x, lin, M, N, K):
 
 
 @pytest.mark.parametrize("N,K", [(1, 64), (100, 320), (257, 1024), (1000, 2048), (5120, 5120), (64, 17408)])
-@pytest.mark.parametrize("M", [1, 4, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_w6_gemm_matches_oracle(M, N, K):
     log(f"w6 gemm M={M} N={N} K={K}")
     codes, scales, lin = _w6(13 * N + K, N, K)
     x = synth.activations_bf16(M * 100 + N + 1, M, K)
     err = gemm_rel_err(_run(dev(x), lin, M, N, K), oracle.w6_gemm(x, codes, scales))
+    assert err <= GEMM_RTOL, err
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 1000, 2048), (1, 257, 1024), (6, 5120, 5120)])
+def test_w6_gemm_bf16_output(M, N, K):
+    """bf16 output: the round-to-nearest-even of the call's own fp32 result,
+    and within the bf16 bar of the oracle's exact product."""
+    import torch
+    from layer_parity import bf16_close
+    log(f"w6 gemm bf16 out M={M} N={N} K={K}")
+    codes, scales, lin = _w6(17 * N + K, N, K)
+    x = dev(synth.activations_bf16(M + N + 3, M, K))
+    y32 = _run(x, lin, M, N, K)
+    y16 = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    ws = B.workspace(max(B.w6_workspace_bytes(M, N, K), 256))
+    B.w6_skinny_gemm(x, lin.hi, lin.lo, lin.pscales, y16, M, N, K, ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y16), oracle.bf16_round(y32.astype(np.float64)))
+    bf16_close(host(y16), oracle.w6_gemm(host(x), codes, scales), min_exact=0.9)
+
+
+@pytest.mark.parametrize("M,N,K", [(4, 5120, 5120), (1, 7168, 5120), (8, 5120, 17408), (3, 100, 320),
+                                   (6, 34816, 5120)])
+def test_w6_partials_sum_to_the_product(M, N, K):
+    """The partials form: at most 8 slices, a layout that does not depend on M,
+    and the S slices summed in slice order give the oracle's product."""
+    import torch
+    log(f"w6 partials M={M} N={N} K={K}")
+    S, ldp = B.w6_partials_layout(M, N, K)
+    assert 1 <= S <= 8 and ldp >= N
+    assert all(B.w6_partials_layout(m, N, K) == (S, ldp) for m in range(1, 9))
+    codes, scales, lin = _w6(19 * N + K, N, K)
+    x = synth.activations_bf16(M + 2 * N, M, K)
+    part = torch.full((S * M * ldp,), float("nan"), dtype=torch.float32, device="cuda")
+    B.w6_skinny_gemm_partials(dev(x), lin.hi, lin.lo, lin.pscales, part, M, N, K)
+    torch.cuda.synchronize()
+    P = host(part).reshape(S, M, ldp)[:, :, :N]
+    s = np.zeros((M, N), np.float32)
+    for k in range(S):
+        s = (s + P[k]).astype(np.float32)
+    assert np.isfinite(s).all()
+    err = gemm_rel_err(s, oracle.w6_gemm(x, codes, scales))
     assert err <= GEMM_RTOL, err
 
 

@@ -392,6 +392,20 @@ def w6_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(lib().vw4_w6_workspace_bytes(M, N, K))
 
 
+def w6_partials_layout(M: int, N: int, K: int):
+    S, ldp = ctypes.c_int32(0), ctypes.c_int64(0)
+    _check("vw4_w6_partials_layout", lib().vw4_w6_partials_layout(M, N, K, ctypes.byref(S), ctypes.byref(ldp)))
+    return int(S.value), int(ldp.value)
+
+
+def w6_skinny_gemm_partials(x, w_hi, w_lo, scales_packed, part, M: int, N: int, K: int, stream=None,
+                            ldx: int | None = None):
+    ldx = x.stride(0) if ldx is None else ldx
+    _check("w6_skinny_gemm_partials", lib().w6_skinny_gemm_partials(_ptr(x), ldx, _ptr(w_hi), _ptr(w_lo),
+                                                                    _ptr(scales_packed), _ptr(part), M, N, K,
+                                                                    _stream(stream)))
+
+
 def w6_skinny_gemm(x, w_hi, w_lo, scales_packed, y, M: int, N: int, K: int, ws=None, stream=None,
                    ldx: int | None = None, ldy: int | None = None):
     """y[M][N] (fp32 or bf16 tensor) = x[M][K] (bf16 bits) @ W6^T."""

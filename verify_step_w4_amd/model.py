@@ -474,17 +474,18 @@ class MTPHead:
                     proj=W4Linear.random(d, 2 * d, 0.02, gen, device))
 
     def draft(self, h, h_rows: int, h_row, token, pos: int, T: float, top_p: float, seed: int, step, depth: int,
-              q_out, token_out, stream=None):
+              q_out, token_out, stream=None, gemm_hook=None):
         """One depth at position pos: h [h_rows][d] (row *h_row, or 0 if h_row is
         None), token (int32 on the device) -> q_out [V] (fp32 draft distribution)
         and token_out (the drawn draft).  step: an int, or an int64 device
-        tensor read when the kernels run."""
+        tensor read when the kernels run.  gemm_hook: passed to the block's
+        forward (see Decoder.forward)."""
         c = self.cfg
         d, V = c["d"], c["V"]
         B.mtp_input(h, h_rows, h_row, self.embed, token, self.gamma_h, self.gamma_e, c["eps"], self.inp, stream)
         B.w4_skinny_gemm(self.inp, self.proj.packed, self.proj.pscales, self.x, 1, d, 2 * d, ws=self.proj_ws,
                          stream=stream)
-        logits = self.block.forward(self.x, pos, 1, stream)
+        logits = self.block.forward(self.x, pos, 1, stream, gemm_hook=gemm_hook)
         B.verify_logits(None, None, None, 1, V, d, T, top_p, logits, self.stats, self.stat_ws, stream=stream)
         dev_step = step if hasattr(step, "data_ptr") else None
         B.draft_sample(logits, self.stats, V, T, seed, 0 if dev_step is not None else step, depth, q_out,
@@ -543,6 +544,26 @@ class SpecLoop:
         B.embed_rows(self.head.embed, self.tokens_in, M, self.x)
         return self.vs.run(self.x, self.L, self.q, self.tokens_in[1:], T, top_p, seed, step)
 
+    def ar_graphable(self, T: float, top_p: float, seed: int, step_dev):
+        """One autoregressive step of the pending token at the current L (no
+        drafts: D = 0 sampling), Philox step from device memory."""
+        B.embed_rows(self.head.embed, self.tokens_in, 1, self.x)
+        self.ar_vs.run_graphable(self.x, self.L, None, None, T, top_p, seed, step_dev)
+
+    def ar_step(self, T: float, top_p: float, seed: int, step: int):
+        """The same eagerly: processes the pending token at L, returns the next
+        one (host int) and makes it the pending token."""
+        B.embed_rows(self.head.embed, self.tokens_in, 1, self.x)
+        tok, _, _ = self.ar_vs.run(self.x, self.L, None, None, T, top_p, seed, step)
+        self.tokens_in[:1].copy_(tok.view(-1)[:1])
+        self.h_src, self.h_rows = self.target.last_resid, 1
+        self.h_row.zero_()
+        self.L += 1
+        t = int(tok.view(-1)[0].item())
+        if t < 0:
+            raise RuntimeError("the autoregressive row was not finite")
+        return t
+
     def run_graphable(self, T: float, top_p: float, seed: int, step_dev):
         """A cycle at the current L with the Philox step read from device memory
         (drafts and verify draw with the same step; the verify advances it)."""
@@ -585,6 +606,109 @@ class SpecLoop:
         self.h_row.fill_(k)
         self.L += k + 1
         return out
+
+
+def _graph_ms(g, reps: int, warm: int = 2) -> float:
+    """Mean time of one replay of a captured graph, from HIP events on the
+    current stream (where replay() launches)."""
+    import torch
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+class DepthTuner:
+    """Draft-depth autotune with the autoregressive fallback (devtrends.cc,
+    "Apple Silicon上でローカルLLMを最大2倍高速化するMTPLX", section "主な機能":
+    the tool tries draft depths 1 to 3 on the machine itself, keeps the
+    fastest, and leaves drafting off where plain decoding is faster).
+
+    Each candidate is measured on the device, from the same start state:
+    * cost: one cycle of depth D (D head steps, the verify of D + 1 rows and
+      the acceptance) captured as a HIP graph at the current context and
+      replayed; D = 0 is the one-row autoregressive step, timed the same way;
+    * yield: the tokens that real cycles of depth D emit (accepted drafts plus
+      the corrected or bonus token), averaged over `cycles` cycles; D = 0
+      emits one token per step.
+    The depth with the most tokens per second is locked (a tie goes to the
+    smaller depth, so AR wins ties).  ``decode`` then generates with it."""
+
+    def __init__(self, target: "Decoder", head: MTPHead, depths=(1, 2, 3)):
+        assert all(1 <= D <= 7 and D + 1 <= target.M_max for D in depths)
+        self.target, self.head, self.depths = target, head, tuple(sorted(depths))
+        self.depth = None
+        self.report = None
+
+    @staticmethod
+    def choose(tokens_per_s: dict) -> int:
+        """The depth with the most tokens per second; depth 0 (AR) is the
+        default, and a tie keeps the smaller depth."""
+        best = 0
+        for D in sorted(tokens_per_s):
+            if tokens_per_s[D] > tokens_per_s.get(best, float("-inf")):
+                best = D
+        return best
+
+    def tune(self, L0: int, t0: int, T: float, top_p: float, seed: int, cycles: int = 8, reps: int = 10,
+             drafts_fn=None):
+        """Measure every candidate and lock the best.  drafts_fn(loop, emitted),
+        if given, returns the int32 device drafts of the next cycle (None: the
+        head drafts); emitted is the token list so far, starting with the token
+        that follows t0."""
+        import torch
+        dev = self.target.device
+        step_dev = torch.zeros(1, dtype=torch.int64, device=dev)
+        ms, per_cycle = {}, {}
+        ar = SpecLoop(self.target, self.head, self.depths[0])
+        ar.start(L0, t0, T, top_p, seed, 0)
+        ms[0] = _graph_ms(ar.capture(lambda: ar.ar_graphable(T, top_p, seed, step_dev)), reps)
+        per_cycle[0] = 1.0
+        for D in self.depths:
+            loop = SpecLoop(self.target, self.head, D)
+            loop.start(L0, t0, T, top_p, seed, 0)
+            ms[D] = _graph_ms(loop.capture(lambda: loop.run_graphable(T, top_p, seed, step_dev)), reps)
+            # real cycles from the same start state (rows past L are overwritten)
+            emitted = [loop.start(L0, t0, T, top_p, seed, 0)]
+            n = 0
+            for c in range(cycles):
+                drafts = drafts_fn(loop, emitted) if drafts_fn is not None else None
+                out = loop.cycle(T, top_p, seed, c + 1, drafts=drafts)
+                n += len(out)
+                emitted += out
+            per_cycle[D] = n / cycles
+        tps = {D: per_cycle[D] * 1e3 / ms[D] for D in ms}
+        best = self.choose(tps)
+        self.depth = best
+        self.report = {"pick": "ar" if best == 0 else f"D{best}", "depth": best,
+                       "ms": {("ar" if D == 0 else f"D{D}"): v for D, v in ms.items()},
+                       "tokens_per_cycle": {f"D{D}": per_cycle[D] for D in self.depths},
+                       "tokens_per_s": {("ar" if D == 0 else f"D{D}"): v for D, v in tps.items()},
+                       "alpha": {f"D{D}": round((per_cycle[D] - 1.0) / D, 4) for D in self.depths}}
+        return self.report
+
+    def decode(self, L0: int, t0: int, n: int, T: float, top_p: float, seed: int):
+        """At least n tokens after t0 (processed at L0) with the locked depth:
+        autoregressive steps for depth 0, else draft -> verify -> accept cycles.
+        Returns (tokens, the loop)."""
+        assert self.depth is not None, "tune() first"
+        D = self.depth
+        loop = SpecLoop(self.target, self.head, D if D else self.depths[0])
+        seq = [loop.start(L0, t0, T, top_p, seed, 0)]
+        k = 1
+        while len(seq) < n:
+            if D == 0:
+                seq.append(loop.ar_step(T, top_p, seed, k))
+            else:
+                seq += loop.cycle(T, top_p, seed, k)
+            k += 1
+        return seq, loop
 
 
 # ---------------------------------------------------------------------------
