@@ -140,6 +140,26 @@ VW4_API int w4_skinny_gemm(const uint16_t* x, int64_t ldx, const uint8_t* w_pack
                    void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * w4_skinny_gemm without a workspace, for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, kernels and results as w4_skinny_gemm (bit for
+ * bit); the split-K partial sums go to a static device array of
+ * VW4_NOALLOC_SCRATCH_BYTES (8 MiB) that each GPU the library runs on holds
+ * until the process ends.  The call allocates nothing (no hipMalloc, no
+ * library allocator).  Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (different streams, or host threads) race and give
+ * undefined results; serialise them.  Nothing in the array needs to start at
+ * zero.  Returns VW4_EWORKSPACE if a shape's partials exceed the array (no
+ * shape with M <= 8 does), VW4_EHIP if the array's device address cannot be
+ * obtained, else as w4_skinny_gemm.
+ * ------------------------------------------------------------------------ */
+#define VW4_NOALLOC_SCRATCH_BYTES (8u << 20)
+VW4_API size_t vw4_noalloc_scratch_bytes(void);
+VW4_API int w4_skinny_gemm_noalloc(const uint16_t* x, int64_t ldx, const uint8_t* w_packed,
+                                   const uint16_t* scales_packed, void* y, int64_t ldy, int32_t y_dtype, int32_t M,
+                                   int32_t N, int32_t K, void* stream);
+
+/* ------------------------------------------------------------------------
  * verify_logits: LM head of the verify rows, then the temperature / top-p
  * statistics of every row (devtrends.cc MTPLX page, section
  * "2つ目のモデル不要！MTPの裏技": sampling at temperature 0.6, top_p 0.95).

@@ -49,6 +49,8 @@ SIGNATURES = {
     "vw4_w4_quantize_packed": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "vw4_gemm_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
     "w4_skinny_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+    "w4_skinny_gemm_noalloc": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P]),
+    "vw4_noalloc_scratch_bytes": (_SZ, []),
     "vw4_workspace_bytes": (_SZ, [_I32, _I32]),
     "verify_logits": (ctypes.c_int, [_P, _I64, _P, _P, _I32, _I32, _I32, _F32, _F32, _P, _P, _P, _SZ, _P]),
     "vw4_accept_workspace_bytes": (_SZ, [_I32, _I32]),
@@ -259,6 +261,19 @@ def w4_skinny_gemm(x, w_packed, scales_packed, y, M: int, N: int, K: int, ws=Non
     nbytes = ws.numel() if ws is not None else 0
     _check("w4_skinny_gemm", lib().w4_skinny_gemm(_ptr(x), ldx, _ptr(w_packed), _ptr(scales_packed), _ptr(y), ldy,
                                                   ydt, M, N, K, _ptr(ws), nbytes, _stream(stream)))
+    return y
+
+
+def w4_skinny_gemm_noalloc(x, w_packed, scales_packed, y, M: int, N: int, K: int, stream=None,
+                           ldx: int | None = None, ldy: int | None = None):
+    """w4_skinny_gemm with its partial sums in the library's static scratch
+    array (no workspace, nothing allocated); calls on one GPU must not overlap."""
+    import torch
+    ydt = VW4_F32 if y.dtype == torch.float32 else VW4_BF16
+    ldx = x.stride(0) if ldx is None else ldx
+    ldy = y.stride(0) if ldy is None else ldy
+    _check("w4_skinny_gemm_noalloc", lib().w4_skinny_gemm_noalloc(_ptr(x), ldx, _ptr(w_packed), _ptr(scales_packed),
+                                                                  _ptr(y), ldy, ydt, M, N, K, _stream(stream)))
     return y
 
 

@@ -36,6 +36,8 @@
 //    from its own row of A).
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace vw4 {
@@ -646,6 +648,68 @@ int w4_skinny_gemm(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, cons
                    void* stream) {
     return vw4::gemm_dispatch(x, ldx, w_packed, scales_packed, y, ldy, y_dtype, M, N, K, ws, ws_bytes,
                               (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The allocation-free form of w4_skinny_gemm.  Its split-K partial sums live
+// in a file-scope device array instead of a caller workspace: every GPU the
+// library runs on holds one copy of VW4_NOALLOC_SCRATCH_BYTES until the
+// process ends.  The largest split-K workspace the plan asks for at M <= 8 is
+// 8 * 8 * 32768 * 4 bytes (S * Npad stays below 4096 * 64), so every shape
+// the plan produces fits.  Host code never passes the array's name to a
+// kernel: it is a host-side stand-in; the device address of each GPU's copy
+// comes from hipGetSymbolAddress, taken once per device on the first call
+// made with that device current.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[VW4_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex noalloc_mu;
+void* noalloc_ptr[NOALLOC_MAX_DEVICES];
+
+// Device address of the current device's scratch copy, or nullptr (with the
+// error message set) if it cannot be had.
+void* noalloc_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) {
+        vw4::set_error("w4_skinny_gemm_noalloc: no current device (or device index >= %d)", NOALLOC_MAX_DEVICES);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(noalloc_mu);
+    if (!noalloc_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            vw4::set_error("w4_skinny_gemm_noalloc: hipGetSymbolAddress of the scratch array failed on device %d: %s",
+                           dev, hipGetErrorString(e));
+            return nullptr;
+        }
+        noalloc_ptr[dev] = p;
+    }
+    return noalloc_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+size_t vw4_noalloc_scratch_bytes(void) { return VW4_NOALLOC_SCRATCH_BYTES; }
+
+int w4_skinny_gemm_noalloc(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, const uint16_t* scales_packed,
+                           void* y, int64_t ldy, int32_t y_dtype, int32_t M, int32_t N, int32_t K, void* stream) {
+    const size_t need = vw4::gemm_ws_bytes(M, N, K);
+    VW4_REQUIRE(need <= VW4_NOALLOC_SCRATCH_BYTES, VW4_EWORKSPACE,
+                "w4_skinny_gemm_noalloc: the split-K partials need %zu bytes, more than the %zu-byte scratch array",
+                need, (size_t)VW4_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need) {
+        ws = noalloc_scratch();
+        if (!ws) return VW4_EHIP;
+    }
+    return vw4::gemm_dispatch(x, ldx, w_packed, scales_packed, y, ldy, y_dtype, M, N, K, ws,
+                              need ? (size_t)VW4_NOALLOC_SCRATCH_BYTES : 0, (hipStream_t)stream);
 }
 
 }  // extern "C"
