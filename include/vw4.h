@@ -501,6 +501,18 @@ VW4_API int w6_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_
                                     const uint16_t* scales_packed, float* part, int32_t M, int32_t N, int32_t K,
                                     void* stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement: the plain streaming-read ceiling of the part (gist.science
+ * BaseRT summary, "結果": decode is bound by memory bandwidth; the W4 GEMM's
+ * achieved bandwidth is reported against it beside the published peak).
+ * Reads `bytes` (a multiple of 16) at device pointer src with 16-byte
+ * non-temporal loads, blocks workgroups of 256 threads in a grid-stride loop;
+ * sink[b] (device, `blocks` words, caller-owned) receives the XOR of the
+ * 32-bit words workgroup b read, so the XOR of all sink words equals the XOR
+ * of the buffer's words.  1 <= blocks <= 2^20.  Enqueues only.
+ * ------------------------------------------------------------------------ */
+VW4_API int vw4_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

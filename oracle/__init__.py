@@ -20,20 +20,34 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "_build", "liboracle.so")
+# VW4_ORACLE_LIB selects another build of the same source (the sanitizer build
+# that tests/test_host_sanitizers.py runs the oracle pins against)
+_LIB_PATH = os.environ.get("VW4_ORACLE_LIB") or os.path.join(_HERE, "_build", "liboracle.so")
+
+_FLAGS = ["-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-fno-fast-math", "-ffp-contract=off"]
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=all"]
 
 
 def build(force: bool = True) -> str:
     """Compile oracle.c with gcc into oracle/_build/liboracle.so."""
-    if not force and os.path.exists(_LIB_PATH):
-        return _LIB_PATH
-    os.makedirs(os.path.dirname(_LIB_PATH), exist_ok=True)
-    tmp = _LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
-           "-fno-fast-math", "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    path = os.path.join(_HERE, "_build", "liboracle.so")
+    if not force and os.path.exists(path):
+        return path
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    tmp = path + ".tmp"
+    subprocess.run(["gcc", "-O2", *_FLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+    os.replace(tmp, path)
+    return path
+
+
+def build_sanitized(path: str) -> str:
+    """The same source with AddressSanitizer and UndefinedBehaviorSanitizer
+    (gcc; any report aborts).  Load it only in a process that preloads gcc's
+    libasan first."""
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    subprocess.run(["gcc", *SANITIZE_FLAGS, *_FLAGS, "-o", path, _SRC, "-lm"], check=True)
+    return path
 
 
 class WarpStat(ctypes.Structure):
@@ -59,7 +73,7 @@ _F64 = ctypes.c_double
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        if not os.path.exists(_LIB_PATH) and not os.environ.get("VW4_ORACLE_LIB"):
             build()
         L = ctypes.CDLL(_LIB_PATH)
         L.oracle_f32_to_f16.argtypes = [_F32]

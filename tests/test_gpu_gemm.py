@@ -276,3 +276,19 @@ def test_swiglu_gemm_against_oracle(M, F, K):
         bf16_close(np.ascontiguousarray(ah[:, cols]), _swiglu_ref(x, wsel, len(cols)), min_exact=0.9)
     else:
         bf16_close(ah, _swiglu_ref(x, w, F), min_exact=0.9)
+
+
+@pytest.mark.parametrize("nbytes,blocks", [(16, 1), (4096 * 16 + 16, 7), (10 << 20, 2048), ((3 << 20) + 48, 300)])
+def test_stream_read_reads_every_word(nbytes, blocks):
+    """The read-ceiling kernel reads the whole buffer: the XOR of its
+    per-workgroup words equals the XOR of the buffer's 32-bit words."""
+    import torch
+    log(f"stream_read bytes={nbytes} blocks={blocks}")
+    words = np.random.default_rng(nbytes % 1000 + blocks).integers(0, 2 ** 32, nbytes // 4, dtype=np.uint64)
+    buf = torch.from_numpy(words.astype(np.uint32).view(np.int32)).cuda()
+    sink = torch.full((blocks + 3,), 12345, dtype=torch.int32, device="cuda")
+    B.stream_read(buf, sink, blocks)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(host(sink)[:blocks].view(np.uint32))
+    assert int(got) == int(np.bitwise_xor.reduce(words.astype(np.uint32)))
+    assert (host(sink)[blocks:] == 12345).all()

@@ -14,7 +14,9 @@ import os
 import numpy as np
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libvw4.so")
+# VW4_LIB selects another build of the same sources (the host-sanitizer build
+# that tests/test_host_sanitizers.py runs the host-side ABI checks against)
+LIB_PATH = os.environ.get("VW4_LIB") or os.path.join(PKG, "libvw4.so")
 
 VW4_OK = 0
 VW4_EINVAL = -1
@@ -51,6 +53,7 @@ SIGNATURES = {
     "w4_skinny_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
     "w4_skinny_gemm_noalloc": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P]),
     "vw4_noalloc_scratch_bytes": (_SZ, []),
+    "vw4_stream_read": (ctypes.c_int, [_P, _SZ, _P, _I32, _P]),
     "vw4_workspace_bytes": (_SZ, [_I32, _I32]),
     "verify_logits": (ctypes.c_int, [_P, _I64, _P, _P, _I32, _I32, _I32, _F32, _F32, _P, _P, _P, _SZ, _P]),
     "vw4_accept_workspace_bytes": (_SZ, [_I32, _I32]),
@@ -275,6 +278,13 @@ def w4_skinny_gemm_noalloc(x, w_packed, scales_packed, y, M: int, N: int, K: int
     _check("w4_skinny_gemm_noalloc", lib().w4_skinny_gemm_noalloc(_ptr(x), ldx, _ptr(w_packed), _ptr(scales_packed),
                                                                   _ptr(y), ldy, ydt, M, N, K, _stream(stream)))
     return y
+
+
+def stream_read(src, sink, blocks: int, nbytes: int | None = None, stream=None):
+    """Read nbytes (default: all) of device tensor src; sink: int32/uint32
+    device tensor of >= blocks words (per-workgroup XOR of what was read)."""
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check("vw4_stream_read", lib().vw4_stream_read(_ptr(src), n, _ptr(sink), blocks, _stream(stream)))
 
 
 def verify_logits(hidden, lm_packed, lm_scales, rows: int, V: int, d: int, temperature: float, top_p: float,
