@@ -55,7 +55,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4_gemm_hbm_traffic.md")
 def measured_traffic(workload):
     """HBM bytes per W4 GEMM launch of a workload's step, from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by the plain-copy
-    calibration there), or None if there is none or the GEMM source has
+    calibration there), or None if there is none or the GEMM sources have
     changed since the counters were taken."""
     import hashlib
     import re
@@ -63,9 +63,11 @@ def measured_traffic(workload):
         text = open(TRAFFIC_FILE).read()
     except OSError:
         return None
-    src = os.path.join(ROOT, "verify_step_w4_amd", "csrc", "w4_gemm.hip")
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    m = re.search(r"w4_gemm\.hip sha256: ([0-9a-f]{64})", text)
+    h = hashlib.sha256()
+    for name in ("w4_gemm.hip", "skinny_gemm.h"):
+        h.update(open(os.path.join(ROOT, "verify_step_w4_amd", "csrc", name), "rb").read())
+    digest = h.hexdigest()
+    m = re.search(r"W4 GEMM sources sha256 \(w4_gemm\.hip, then skinny_gemm\.h\): ([0-9a-f]{64})", text)
     if not m or m.group(1) != digest:
         return None
     m = re.search(r"^\| " + re.escape(workload) + r" \| ([0-9.]+) \| ([0-9.]+) \| ([0-9.]+) \|", text, re.M)

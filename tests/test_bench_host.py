@@ -63,12 +63,15 @@ def test_measured_traffic_follows_the_committed_digest():
     import re
     m = re.search(r"^\| verify27b \| ([0-9]+) \| ([0-9]+) \| ([0-9]+) \|", text, re.M)
     assert m, "the traffic summary lists verify27b"
-    # the reported figure is the per-launch total while the GEMM source has
+    # the reported figure is the per-launch total while the GEMM sources have
     # the digest the counters were taken with, and None otherwise
     import hashlib
-    src = os.path.join(ROOT, "verify_step_w4_amd", "csrc", "w4_gemm.hip")
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    recorded = re.search(r"w4_gemm\.hip sha256: ([0-9a-f]{64})", text).group(1)
+    h = hashlib.sha256()
+    for name in ("w4_gemm.hip", "skinny_gemm.h"):
+        h.update(open(os.path.join(ROOT, "verify_step_w4_amd", "csrc", name), "rb").read())
+    digest = h.hexdigest()
+    recorded = re.search(r"W4 GEMM sources sha256 \(w4_gemm\.hip, then skinny_gemm\.h\): ([0-9a-f]{64})",
+                         text).group(1)
     got = bench.measured_traffic("verify27b")
     assert got == (int(m.group(3)) if digest == recorded else None)
     assert bench.measured_traffic("no_such_workload") is None
