@@ -233,23 +233,29 @@ __device__ __forceinline__ AcceptPart chunk_sums(const float* __restrict__ zk, c
     double sr = 0.0, sp = 0.0;
     int lr = -1, lp = -1;
     for (int base = c0; base < c1; base += NT * AU) {
+        // all loads of the tile issued together (clamped indices, no branches);
+        // slots past the chunk end are masked below
         float zv[AU], qv[AU];
 #pragma unroll
-        for (int u = 0; u < AU; ++u) {
-            const int j = base + u * NT + threadIdx.x;
-            zv[u] = (j < c1) ? zk[j] : 0.0f;
-            qv[u] = (qk && j < c1) ? qk[j] : 0.0f;
+        for (int u = 0; u < AU; ++u) zv[u] = zk[min(base + u * NT + (int)threadIdx.x, c1 - 1)];
+        if (qk) {
+#pragma unroll
+            for (int u = 0; u < AU; ++u) qv[u] = qk[min(base + u * NT + (int)threadIdx.x, c1 - 1)];
+        } else {
+#pragma unroll
+            for (int u = 0; u < AU; ++u) qv[u] = 0.0f;
         }
 #pragma unroll
         for (int u = 0; u < AU; ++u) {
             const int j = base + u * NT + threadIdx.x;
-            if (j >= c1) break;
-            const double pj = p_val(zv[u], sk, T, j);
-            const double rj = qk ? fmax(0.0, pj - (double)qv[u]) : pj;
-            sr += rj;
-            sp += pj;
-            if (rj > 0.0) lr = j;
-            if (pj > 0.0) lp = j;
+            if (j < c1) {
+                const double pj = p_val(zv[u], sk, T, j);
+                const double rj = qk ? fmax(0.0, pj - (double)qv[u]) : pj;
+                sr += rj;
+                sp += pj;
+                if (rj > 0.0) lr = j;
+                if (pj > 0.0) lp = j;
+            }
         }
     }
     AcceptPart a;
@@ -268,28 +274,45 @@ __device__ void finish_problem(const float* __restrict__ zk, const vw4_rowstat& 
                                double T, const ProblemState& ps, const double* s_u, int32_t* __restrict__ tb,
                                int32_t* __restrict__ nacc_b, uint32_t* __restrict__ flags_b, double* sh, int* shi) {
     __shared__ int s_y;
+    __shared__ double s_R, s_before;
+    __shared__ int s_wc, s_last, s_usep;
     const int k = ps.k;
     uint32_t flags = ps.flags;
-    bool use_p = false;
-    double R = 0.0;
-    for (int c = 0; c < P; ++c) R += pb[c].r;
-    if (!(R > 0.0)) {
-        use_p = true;
-        flags |= VW4_FLAG_R_ZERO;
-        R = 0.0;
-        for (int c = 0; c < P; ++c) R += pb[c].p;
+    // R and the chunk holding u * R, by wavefront 0 (lane c holds part c,
+    // P <= 64): the same sums and comparisons in chunk order, operands taken
+    // lane by lane, instead of every wavefront reading all P parts from LDS
+    if (threadIdx.x < 64) {
+        const AcceptPart& q = pb[min((int)threadIdx.x, P - 1)];
+        double R = 0.0;
+        for (int c = 0; c < P; ++c) R += readlane_f64(q.r, c);
+        const bool use_p = !(R > 0.0);
+        if (use_p) {
+            R = 0.0;
+            for (int c = 0; c < P; ++c) R += readlane_f64(q.p, c);
+        }
+        const double target = s_u[2 * k + 1] * R;
+        const double mq = use_p ? q.p : q.r;
+        const int lq = use_p ? q.last_p : q.last_r;
+        int wc = -1, last_any = -1;
+        double before = 0.0, cum = 0.0;
+        for (int c = 0; c < P; ++c) {
+            const double m = readlane_f64(mq, c);
+            const int lst = __builtin_amdgcn_readlane(lq, c);
+            if (lst >= 0) last_any = lst;
+            if (wc < 0 && cum + m > target) { wc = c; before = cum; }
+            cum += m;
+        }
+        if (threadIdx.x == 0) {
+            s_R = R; s_before = before; s_wc = wc; s_last = last_any; s_usep = use_p;
+        }
     }
+    __syncthreads();
+    const bool use_p = s_usep;
+    if (use_p) flags |= VW4_FLAG_R_ZERO;
+    const double R = s_R;
     const double target = s_u[2 * k + 1] * R;
-    int wc = -1;
-    double before = 0.0, cum = 0.0;
-    int last_any = -1;
-    for (int c = 0; c < P; ++c) {
-        const double m = use_p ? pb[c].p : pb[c].r;
-        const int lst = use_p ? pb[c].last_p : pb[c].last_r;
-        if (lst >= 0) last_any = lst;
-        if (wc < 0 && cum + m > target) { wc = c; before = cum; }
-        cum += m;
-    }
+    const int wc = s_wc, last_any = s_last;
+    const double before = s_before;
     const bool resid = !use_p && qk != nullptr;
     int y = -1;
     double cprev = 0.0, cy = 0.0;

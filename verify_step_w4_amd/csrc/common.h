@@ -80,6 +80,15 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
 
 // Order-preserving key of a binary32 (ascending floats -> ascending keys);
 // -0.0 is folded onto +0.0 so that equal floats share one key.
+// Lane k's value of v, for every lane (k uniform): one wavefront walking a
+// per-lane array in order without a round trip through LDS.
+__device__ __forceinline__ double readlane_f64(double v, int k) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, k);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), k);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 __device__ __forceinline__ uint32_t f32_key(float f) {
     uint32_t u = __float_as_uint(f);
     if (u == 0x80000000u) u = 0u;

@@ -26,7 +26,9 @@
 //      histogram of the next 11 key bits inside it
 //   4. combine level 2
 //   5. per chunk: descend both levels; fixed-order mass and count above the
-//      22-bit key prefix of the cutoff; counts of the last 10 key bits inside it
+//      22-bit key prefix of the cutoff; counts of the last 10 key bits inside it,
+//      published as a short list of the non-empty bins (the dense counts only
+//      when the list overflows its 256-byte record)
 //   6. per row: with the 10-bit counts every bin is one float value, so its mass
 //      is count * exp((z - m)/T) exactly; finish the descent, tau, Z, n_kept.
 // The LDS histogram atomics only steer steps 3 and 5; the final decision in
@@ -57,12 +59,20 @@ struct ChunkPart {   // per-workgroup results of phase 1
 struct ChunkSums {   // per-workgroup results of phase 5
     double above;    // mass of keys above the 22-bit cutoff prefix
     uint32_t n_above;
-    uint32_t pad;
+    uint32_t pad;    // the 22-bit prefix
 };
+
+// Phase-5 record of one chunk (REC uint32 words, 256 bytes): its ChunkSums
+// (words 0-3), the number nz of non-empty level-3 bins (word 4), and the
+// first REC_CAP of them as (count << 10 | bin) entries.  When nz > REC_CAP
+// the chunk's dense counts are written as well.  A chunk holds at most
+// 2^18 logits (V <= 2^24 over at most 64 chunks), so a count fits 22 bits.
+constexpr int REC = 64, REC_HEAD = 5, REC_CAP = REC - REC_HEAD;
+static_assert(sizeof(ChunkSums) == 16, "ChunkSums fills record words 0-3");
 
 struct VocabLayout {
     int P, chunk, V, rows;
-    size_t off_part, off_e, off_h1p, off_h1, off_h2p, off_h2, off_sums, off_c3, total;
+    size_t off_part, off_e, off_h1p, off_h1, off_h2p, off_h2, off_rec, off_c3, total;
 };
 
 static size_t al256(size_t o) { return (o + 255) / 256 * 256; }
@@ -86,7 +96,7 @@ static VocabLayout vocab_layout(int rows, int V) {
     L.off_h1 = o;   o = al256(o + (size_t)rows * HB * sizeof(double));
     L.off_h2p = o;  o = al256(o + (size_t)rows * P * HB * sizeof(double));
     L.off_h2 = o;   o = al256(o + (size_t)rows * HB * sizeof(double));
-    L.off_sums = o; o = al256(o + (size_t)rows * P * sizeof(ChunkSums));
+    L.off_rec = o;  o = al256(o + (size_t)rows * P * REC * sizeof(uint32_t));
     L.off_c3 = o;   o = al256(o + (size_t)rows * P * HB3 * sizeof(uint32_t));
     L.total = o;
     return L;
@@ -99,7 +109,7 @@ struct RowView {     // pointers of one row inside the workspace
     double* h1;
     double* h2p;
     double* h2;
-    ChunkSums* sums;
+    uint32_t* rec;
     uint32_t* c3;
 };
 
@@ -111,7 +121,7 @@ __device__ __forceinline__ RowView row_view(char* ws, const VocabLayout& L, int 
     v.h1 = (double*)(ws + L.off_h1) + (int64_t)r * HB;
     v.h2p = (double*)(ws + L.off_h2p) + (int64_t)r * L.P * HB;
     v.h2 = (double*)(ws + L.off_h2) + (int64_t)r * HB;
-    v.sums = (ChunkSums*)(ws + L.off_sums) + (int64_t)r * L.P;
+    v.rec = (uint32_t*)(ws + L.off_rec) + (int64_t)r * L.P * REC;
     v.c3 = (uint32_t*)(ws + L.off_c3) + (int64_t)r * L.P * HB3;
     return v;
 }
@@ -207,6 +217,45 @@ __device__ __forceinline__ double combine_E(const ChunkPart* sp, int P, float m,
     return E;
 }
 
+// Row header by one wavefront, lane k holding chunk part k (P <= 64), for
+// the 1024-thread finishing kernel, where the whole-block loops over the parts
+// cost one LDS round trip per part in each of 16 wavefronts.  The max, its
+// argmax and the non-finite flag come from a lane reduction: a pure selection,
+// exact, with ties to the lowest chunk as in the scan in chunk order (only
+// non-finite rows, whose header is not used, could differ).  The minimum and
+// E = sum_k f_k E_k are the scan's own chains in chunk order (fminf, and one
+// fused multiply-add per chunk), operands taken lane by lane.
+__device__ __forceinline__ RowMax wave_combine_max(const ChunkPart* sp, int P) {
+    const int lane = threadIdx.x & 63;
+    const bool in = lane < P;
+    const ChunkPart& q = sp[in ? lane : 0];
+    float m = in ? q.m : -INFINITY;
+    int32_t a = in ? q.argmax : 0, k = in ? lane : 0x7fffffff;
+    uint32_t bad = in ? q.bad : 0u;
+    for (int off = 32; off > 0; off >>= 1) {
+        const float om = __shfl_xor(m, off, 64);
+        const int32_t ok = __shfl_xor(k, off, 64), oa = __shfl_xor(a, off, 64);
+        if (om > m || (om == m && ok < k)) { m = om; k = ok; a = oa; }
+        bad |= __shfl_xor(bad, off, 64);
+    }
+    // the minimum folded in chunk order (fminf of signed zeros may depend on order)
+    const int32_t mnl = __float_as_int(q.mn);
+    float mn = INFINITY;
+    for (int c = 0; c < P; ++c) mn = fminf(mn, __int_as_float(__builtin_amdgcn_readlane(mnl, c)));
+    RowMax r;
+    r.m = m; r.mn = mn; r.argmax = a; r.bad = bad;
+    return r;
+}
+
+__device__ __forceinline__ double wave_combine_E(const ChunkPart* sp, int P, float m, double T) {
+    const int lane = threadIdx.x & 63;
+    const ChunkPart& q = sp[lane < P ? lane : 0];
+    const double f = exp(((double)q.m - (double)m) / T), e = q.E;
+    double E = 0.0;
+    for (int k = 0; k < P; ++k) E = fma(readlane_f64(f, k), readlane_f64(e, k), E);
+    return E;
+}
+
 // Descend nb combined bins (ascending key, HB/VT = 8 per thread, this
 // thread's slice in h): the largest bin b with
 // above + sum_{b' >= b} H[b'] >= target.  Returns -1 if none.
@@ -296,10 +345,11 @@ __global__ __launch_bounds__(VT) void vs_chunk_kernel(const float* __restrict__ 
 #pragma unroll
         for (int u = 0; u < VU; ++u) {
             const int j = base + u * VT + tid;
-            if (j >= c1) break;
-            if (!isfinite(v[u])) bad = 1;
-            lmn = fminf(lmn, v[u]);
-            if (v[u] > lm || (v[u] == lm && j < li)) { lm = v[u]; li = j; }
+            if (j < c1) {
+                if (!isfinite(v[u])) bad = 1;
+                lmn = fminf(lmn, v[u]);
+                if (v[u] > lm || (v[u] == lm && j < li)) { lm = v[u]; li = j; }
+            }
         }
     }
     for (int off = 32; off > 0; off >>= 1) {
@@ -337,12 +387,13 @@ __global__ __launch_bounds__(VT) void vs_chunk_kernel(const float* __restrict__ 
 #pragma unroll
             for (int u = 0; u < VU; ++u) {
                 const int j = base + u * VT + tid;
-                if (j >= c1) break;
-                const double e = exp(((double)v[u] - (double)m_w) / T);
-                es += e;
-                if (hist_on) {
-                    rv.e[j] = e;
-                    atomicAdd(&hist[f32_key(v[u]) >> (32 - L1BITS)], e);
+                if (j < c1) {
+                    const double e = exp(((double)v[u] - (double)m_w) / T);
+                    es += e;
+                    if (hist_on) {
+                        rv.e[j] = e;
+                        atomicAdd(&hist[f32_key(v[u]) >> (32 - L1BITS)], e);
+                    }
                 }
             }
         }
@@ -430,9 +481,10 @@ __global__ __launch_bounds__(VT) void vs_level2_kernel(const float* __restrict__
             }
 #pragma unroll
             for (int u = 0; u < VU; ++u) {
-                if (base + u * VT + tid >= c1) break;
-                const uint32_t k = f32_key(v[u]);
-                if ((k >> (32 - L1BITS)) == (uint32_t)b1) atomicAdd(&hist[(k >> L3BITS) & (HB - 1)], ev[u] * fw);
+                if (base + u * VT + tid < c1) {
+                    const uint32_t k = f32_key(v[u]);
+                    if ((k >> (32 - L1BITS)) == (uint32_t)b1) atomicAdd(&hist[(k >> L3BITS) & (HB - 1)], ev[u] * fw);
+                }
             }
         }
     }
@@ -450,6 +502,7 @@ __global__ __launch_bounds__(VT) void vs_level3_kernel(const float* __restrict__
     __shared__ int shi[4];
     __shared__ ChunkPart sp[VMAXP];
     __shared__ double f[VMAXP];
+    __shared__ uint32_t s_nz;
     const int w = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
     const RowView rv = row_view(ws, L, r);
     const float* z = logits + (int64_t)r * L.V;
@@ -472,6 +525,7 @@ __global__ __launch_bounds__(VT) void vs_level3_kernel(const float* __restrict__
     int b2 = (b1 >= 0) ? descend(h2, HB, above1, target, &above2, shd, shi) : -1;
     const double fw = f[w];
     for (int b = tid; b < HB3; b += VT) cnt[b] = 0u;
+    if (tid == 0) s_nz = 0u;
     __syncthreads();
     // without a usable steering bin (only rounding can cause this) the prefix
     // is placed above every key: nothing is "above", all counts land in bins
@@ -491,20 +545,35 @@ __global__ __launch_bounds__(VT) void vs_level3_kernel(const float* __restrict__
         }
 #pragma unroll
         for (int u = 0; u < VU; ++u) {
-            if (base + u * VT + tid >= c1) break;
-            const uint32_t k = f32_key(v[u]);
-            const uint32_t hi = k >> L3BITS;
-            if (hi > prefix) { sa += ev[u] * fw; ++na; }
-            else if (hi == prefix) atomicAdd(&cnt[k & (HB3 - 1)], 1u);
+            if (base + u * VT + tid < c1) {
+                const uint32_t k = f32_key(v[u]);
+                const uint32_t hi = k >> L3BITS;
+                if (hi > prefix) { sa += ev[u] * fw; ++na; }
+                else if (hi == prefix) atomicAdd(&cnt[k & (HB3 - 1)], 1u);
+            }
         }
     }
     sa = block_sum_f64(sa, shd);
     na = block_sum_u32(na, shu);
-    for (int b = tid; b < HB3; b += VT) rv.c3[(int64_t)w * HB3 + b] = cnt[b];
+    // the non-empty bins into the chunk's record (slots taken in any order:
+    // the finishing pass only adds integer counts per bin)
+    uint32_t* rec = rv.rec + (int64_t)w * REC;
+    for (int b = tid; b < HB3; b += VT) {
+        const uint32_t c = cnt[b];
+        if (c) {
+            const uint32_t slot = atomicAdd(&s_nz, 1u);
+            if (slot < (uint32_t)REC_CAP) rec[REC_HEAD + slot] = (c << 10) | (uint32_t)b;
+        }
+    }
+    __syncthreads();
+    const uint32_t nz = s_nz;
+    if (nz > (uint32_t)REC_CAP)
+        for (int b = tid; b < HB3; b += VT) rv.c3[(int64_t)w * HB3 + b] = cnt[b];
     if (tid == 0) {
         ChunkSums s;
         s.above = sa; s.n_above = na; s.pad = prefix;
-        rv.sums[w] = s;
+        *(ChunkSums*)rec = s;
+        rec[4] = nz;
     }
 }
 
@@ -515,24 +584,70 @@ __global__ __launch_bounds__(HB3) void vs_finish_kernel(float temperature, float
     __shared__ int s_b;
     __shared__ double s_cum;
     __shared__ ChunkPart sp[VMAXP];
-    __shared__ double f[VMAXP];
-    __shared__ ChunkSums ss[VMAXP];
+    __shared__ __align__(16) uint32_t s_rec[VMAXP * REC];
+    __shared__ uint32_t s_cnt[HB3];
     const int r = blockIdx.x, tid = threadIdx.x;
     const RowView rv = row_view(ws, L, r);
-    // every independent load first (one memory round trip): this thread's
-    // level-3 bin over all chunks, the chunk parts and sums
-    uint32_t c3v[VMAXP];
-    if (top_p < 1.0f && temperature > 0.0f) {
+    // every independent load first (one memory round trip): the chunk parts
+    // and the chunks' phase-5 records (at most VMAXP * REC / HB3 = 4 words per
+    // thread, clamped loads issued together)
+    const bool topp = top_p < 1.0f && temperature > 0.0f;
+    if (topp) {
+        const int nrec = L.P * REC;
+        uint32_t rw[VMAXP * REC / HB3];
 #pragma unroll
-        for (int i = 0; i < VMAXP; ++i) c3v[i] = (i < L.P) ? rv.c3[(int64_t)i * HB3 + tid] : 0u;
+        for (int u = 0; u < VMAXP * REC / HB3; ++u) rw[u] = rv.rec[min(tid + u * HB3, nrec - 1)];
+#pragma unroll
+        for (int u = 0; u < VMAXP * REC / HB3; ++u)
+            if (tid + u * HB3 < nrec) s_rec[tid + u * HB3] = rw[u];
+        s_cnt[tid] = 0u;
     }
-    for (int k = tid; k < L.P; k += blockDim.x) {
-        sp[k] = rv.part[k];
-        ss[k] = rv.sums[k];
+    for (int k = tid; k < L.P; k += blockDim.x) sp[k] = rv.part[k];
+    __syncthreads();
+    const double T = (double)temperature;
+    // the level-3 counts of all chunks, bin by bin: the record entries, or the
+    // dense counts of a chunk whose record overflowed (rare: its 22-bit prefix
+    // bin then holds more than REC_CAP distinct values).  Records of a row
+    // that stopped early (non-finite, T == 0) are never used.
+    if (topp) {
+        bool dense = false;
+        for (int i = tid; i < L.P * REC; i += HB3) {
+            const int k = i / REC, j = i % REC;
+            const uint32_t nz = s_rec[k * REC + 4];
+            if (j >= REC_HEAD && (uint32_t)(j - REC_HEAD) < nz) {
+                if (nz <= (uint32_t)REC_CAP) atomicAdd(&s_cnt[s_rec[i] & (HB3 - 1)], s_rec[i] >> 10);
+                else dense = true;
+            }
+        }
+        if (__syncthreads_or(dense)) {
+            for (int k = 0; k < L.P; ++k)
+                if (s_rec[k * REC + 4] > (uint32_t)REC_CAP)
+                    atomicAdd(&s_cnt[tid], rv.c3[(int64_t)k * HB3 + tid]);
+        }
+    }
+    // the row header, by wavefront 0: max, E, and the mass and count above the
+    // cutoff prefix summed over the chunks in chunk order
+    __shared__ RowMax s_mx;
+    __shared__ double s_E, s_above;
+    __shared__ uint32_t s_na;
+    if (tid < 64) {
+        const RowMax h = wave_combine_max(sp, L.P);
+        double E = 0.0, above = 0.0;
+        uint32_t na = 0;
+        if (!h.bad && T > 0.0) {
+            E = wave_combine_E(sp, L.P, h.m, T);
+            if (topp) {
+                const ChunkSums* sk = (const ChunkSums*)&s_rec[min(tid, L.P - 1) * REC];
+                const double a = sk->above;
+                for (int k = 0; k < L.P; ++k) above += readlane_f64(a, k);
+                na = (tid < L.P) ? sk->n_above : 0u;
+                for (int off = 32; off > 0; off >>= 1) na += __shfl_xor(na, off, 64);
+            }
+        }
+        if (tid == 0) { s_mx = h; s_E = E; s_above = above; s_na = na; }
     }
     __syncthreads();
-    const RowMax mx = combine_max(sp, L.P);
-    const double T = (double)temperature;
+    const RowMax mx = s_mx;
     vw4_rowstat s;
     s.max_logit = mx.m;
     s.argmax = mx.argmax;
@@ -549,7 +664,7 @@ __global__ __launch_bounds__(HB3) void vs_finish_kernel(float temperature, float
         }
         return;
     }
-    const double E = combine_E(sp, L.P, mx.m, T, f);
+    const double E = s_E;
     if (!(top_p < 1.0f)) {
         if (tid == 0) {
             s.tau = mx.mn;
@@ -561,14 +676,11 @@ __global__ __launch_bounds__(HB3) void vs_finish_kernel(float temperature, float
         return;
     }
     const double target = (double)top_p * E;
-    double above = 0.0;
-    uint32_t n_above = 0;
-    for (int k = 0; k < L.P; ++k) { above += ss[k].above; n_above += ss[k].n_above; }
-    const uint32_t prefix = ss[0].pad;
+    const double above = s_above;
+    const uint32_t n_above = s_na;
+    const uint32_t prefix = ((const ChunkSums*)&s_rec[0])->pad;
     // level-3 bin b (thread b): one float value, mass = count * e(value)
-    uint32_t c = 0;
-#pragma unroll
-    for (int i = 0; i < VMAXP; ++i) c += c3v[i];
+    const uint32_t c = s_cnt[tid];
     const float zb = key_f32((prefix << L3BITS) | (uint32_t)tid);
     const double eb = (c && prefix != 0x3fffffu) ? exp(((double)zb - (double)mx.m) / T) : 0.0;
     const double mass = (double)c * eb;
@@ -749,10 +861,11 @@ __global__ __launch_bounds__(RT) void vs_row_kernel(const float* __restrict__ lo
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
         const int j = u * RT + tid;
-        if (j >= V) break;
-        if (!isfinite(v[u])) bad = 1;
-        lmn = fminf(lmn, v[u]);
-        if (v[u] > lm || (v[u] == lm && j < li)) { lm = v[u]; li = j; }
+        if (j < V) {
+            if (!isfinite(v[u])) bad = 1;
+            lmn = fminf(lmn, v[u]);
+            if (v[u] > lm || (v[u] == lm && j < li)) { lm = v[u]; li = j; }
+        }
     }
     for (int off = 32; off > 0; off >>= 1) {
         const float om = __shfl_xor(lm, off, 64);
@@ -820,9 +933,10 @@ __global__ __launch_bounds__(RT) void vs_row_kernel(const float* __restrict__ lo
     if (b1 >= 0) {
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
-            if (u * RT + tid >= V) break;
-            const uint32_t k = f32_key(v[u]);
-            if ((k >> (32 - L1BITS)) == (uint32_t)b1) atomicAdd(&hist[(k >> L3BITS) & (HB - 1)], e[u]);
+            if (u * RT + tid < V) {
+                const uint32_t k = f32_key(v[u]);
+                if ((k >> (32 - L1BITS)) == (uint32_t)b1) atomicAdd(&hist[(k >> L3BITS) & (HB - 1)], e[u]);
+            }
         }
     }
     __syncthreads();
@@ -835,11 +949,12 @@ __global__ __launch_bounds__(RT) void vs_row_kernel(const float* __restrict__ lo
     uint32_t na = 0;
 #pragma unroll
     for (int u = 0; u < RU; ++u) {
-        if (u * RT + tid >= V) break;
-        const uint32_t k = f32_key(v[u]);
-        const uint32_t hi = k >> L3BITS;
-        if (hi > prefix) { sa += e[u]; ++na; }
-        else if (hi == prefix) atomicAdd(&cnt[k & (HB3 - 1)], 1u);
+        if (u * RT + tid < V) {
+            const uint32_t k = f32_key(v[u]);
+            const uint32_t hi = k >> L3BITS;
+            if (hi > prefix) { sa += e[u]; ++na; }
+            else if (hi == prefix) atomicAdd(&cnt[k & (HB3 - 1)], 1u);
+        }
     }
     const double above = row_sum_f64(sa, sh);
     const uint32_t n_above = row_sum_u32(na, (uint32_t*)shi);
