@@ -274,45 +274,28 @@ __device__ void finish_problem(const float* __restrict__ zk, const vw4_rowstat& 
                                double T, const ProblemState& ps, const double* s_u, int32_t* __restrict__ tb,
                                int32_t* __restrict__ nacc_b, uint32_t* __restrict__ flags_b, double* sh, int* shi) {
     __shared__ int s_y;
-    __shared__ double s_R, s_before;
-    __shared__ int s_wc, s_last, s_usep;
     const int k = ps.k;
     uint32_t flags = ps.flags;
-    // R and the chunk holding u * R, by wavefront 0 (lane c holds part c,
-    // P <= 64): the same sums and comparisons in chunk order, operands taken
-    // lane by lane, instead of every wavefront reading all P parts from LDS
-    if (threadIdx.x < 64) {
-        const AcceptPart& q = pb[min((int)threadIdx.x, P - 1)];
-        double R = 0.0;
-        for (int c = 0; c < P; ++c) R += readlane_f64(q.r, c);
-        const bool use_p = !(R > 0.0);
-        if (use_p) {
-            R = 0.0;
-            for (int c = 0; c < P; ++c) R += readlane_f64(q.p, c);
-        }
-        const double target = s_u[2 * k + 1] * R;
-        const double mq = use_p ? q.p : q.r;
-        const int lq = use_p ? q.last_p : q.last_r;
-        int wc = -1, last_any = -1;
-        double before = 0.0, cum = 0.0;
-        for (int c = 0; c < P; ++c) {
-            const double m = readlane_f64(mq, c);
-            const int lst = __builtin_amdgcn_readlane(lq, c);
-            if (lst >= 0) last_any = lst;
-            if (wc < 0 && cum + m > target) { wc = c; before = cum; }
-            cum += m;
-        }
-        if (threadIdx.x == 0) {
-            s_R = R; s_before = before; s_wc = wc; s_last = last_any; s_usep = use_p;
-        }
+    bool use_p = false;
+    double R = 0.0;
+    for (int c = 0; c < P; ++c) R += pb[c].r;
+    if (!(R > 0.0)) {
+        use_p = true;
+        flags |= VW4_FLAG_R_ZERO;
+        R = 0.0;
+        for (int c = 0; c < P; ++c) R += pb[c].p;
     }
-    __syncthreads();
-    const bool use_p = s_usep;
-    if (use_p) flags |= VW4_FLAG_R_ZERO;
-    const double R = s_R;
     const double target = s_u[2 * k + 1] * R;
-    const int wc = s_wc, last_any = s_last;
-    const double before = s_before;
+    int wc = -1;
+    double before = 0.0, cum = 0.0;
+    int last_any = -1;
+    for (int c = 0; c < P; ++c) {
+        const double m = use_p ? pb[c].p : pb[c].r;
+        const int lst = use_p ? pb[c].last_p : pb[c].last_r;
+        if (lst >= 0) last_any = lst;
+        if (wc < 0 && cum + m > target) { wc = c; before = cum; }
+        cum += m;
+    }
     const bool resid = !use_p && qk != nullptr;
     int y = -1;
     double cprev = 0.0, cy = 0.0;
