@@ -694,6 +694,57 @@ EXPORT void oracle_w8_gemm(const uint16_t* x_bf16, int64_t M, int64_t K, const u
 }
 
 /* ------------------------------------------------------------------------ */
+/* A fourth weight format: W5 (the same BaseRT section lists Q2 ... Q8 among  */
+/* the GEMV's formats; no layout).  Reading: the W4 recipe with 5-bit codes -- */
+/* codes in [-15, 15]; scale = fp16(absmax / 15) rounded to nearest-even;     */
+/* codes use the rounded scale, half-even, clamped; an all-zero group gets    */
+/* scale 0 and codes 0.  Canonical storage: u8 codes[N][K] holding u = c + 16; */
+/* f16 scales[N][K/64].                                                       */
+/* ------------------------------------------------------------------------ */
+EXPORT void oracle_w5_quantize(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales) {
+    const int64_t G = K / 64;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < G; ++g) {
+            const float* wg = w + n * K + g * 64;
+            float a = 0.0f;
+            for (int k = 0; k < 64; ++k) {
+                float v = fabsf(wg[k]);
+                if (v > a) a = v;
+            }
+            uint16_t s16 = oracle_f32_to_f16(a / 15.0f);    /* binary32 division */
+            float sf = (float)f16_value(s16);
+            scales[n * G + g] = s16;
+            for (int k = 0; k < 64; ++k) {
+                int c = 0;
+                if (sf != 0.0f) {
+                    float r = rintf(wg[k] / sf);            /* binary32 division, half-even */
+                    if (r > 15.0f) r = 15.0f;
+                    if (r < -15.0f) r = -15.0f;
+                    c = (int)r;
+                }
+                codes[n * K + g * 64 + k] = (uint8_t)(c + 16);
+            }
+        }
+    }
+}
+
+/* y[m][n] = sum_k x[m][k] * c[n][k] * s[n][k/64], fp64, sequential in k. */
+EXPORT void oracle_w5_gemm(const uint16_t* x_bf16, int64_t M, int64_t K, const uint8_t* codes,
+                           const uint16_t* scales, int64_t N, double* y /* [M][N] */) {
+    const int64_t G = K / 64;
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += bf16_value(x_bf16[m * K + k]) * (double)((int)codes[n * K + k] - 16) *
+                       f16_value(scales[n * G + k / 64]);
+            y[m * N + n] = acc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* A third weight format: W6 ([BaseRT/方法] lists Q2 ... Q8; no layout).       */
 /* Reading: the W4 recipe with 6-bit codes -- codes in [-31, 31]; scale =     */
 /* fp16(absmax / 31) rounded to nearest-even; codes use the rounded scale,    */

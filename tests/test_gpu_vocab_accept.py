@@ -64,6 +64,33 @@ def test_stats_ties_and_signed_zero():
         check_stats(z, T, p)
 
 
+def test_stats_crowded_cutoff_bin():
+    """Level 3 publishes a chunk's non-empty bins of the cutoff's 22-bit key
+    prefix as a record of at most 59 entries, and its dense counts when it
+    has more.  Here the cutoff falls among up to 1024 consecutive floats just
+    above 1.0 (one prefix, every one its own bin); row 0 has chunks with 600
+    and 384 of them (dense) and one with 40 (record), row 1 50 per chunk in
+    9 chunks (records only), row 2 one chunk with 60 (dense) and one with
+    exactly 59 (record).  The other logits are -30, far below the cutoff."""
+    V = 40000                                       # chunked path: 10 chunks of 4096
+    rng = np.random.default_rng(31)
+    near = (np.float32(1.0) + np.arange(1024, dtype=np.float32) * np.float32(2.0 ** -23)).astype(np.float32)
+    z = np.full((3, V), -30.0, dtype=np.float32)
+    pos0 = np.concatenate([rng.choice(4096, 600, replace=False), 4096 + rng.choice(4096, 40, replace=False),
+                           5 * 4096 + rng.choice(4096, 384, replace=False)])
+    z[0, pos0] = rng.permutation(near)
+    pos1 = np.concatenate([c * 4096 + rng.choice(4096, 50, replace=False) for c in range(9)])
+    z[1, pos1] = rng.permutation(near)[:450]
+    pos2 = np.concatenate([2 * 4096 + rng.choice(4096, 60, replace=False),
+                           7 * 4096 + rng.choice(4096, 59, replace=False)])
+    z[2, pos2] = rng.permutation(near)[:119]
+    log("stats crowded cutoff bin")
+    for T, p in ((0.6, 0.95), (1.0, 0.5)):
+        for r in range(3):                          # the construction puts tau among the crowded values
+            assert near[0] <= oracle.warp(z[r], T, p).tau <= near[-1]
+        assert check_stats(z, T, p) == 0
+
+
 def test_stats_flag_non_finite():
     z = synth.synthetic_logits(5, 2, 300, 1.0)
     z[1, 7] = np.inf
