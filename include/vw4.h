@@ -476,6 +476,32 @@ VW4_API int w8_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_
                                     void* stream);
 
 /* ------------------------------------------------------------------------
+ * A fourth weight format: W5 (the same BaseRT section lists Q2 ... Q8; no
+ * layout).  Per row n and 64-element group g: scale = fp16_rne(absmax / 15),
+ * c_k = clamp(rint(w_k / scale), -15, 15) with the rounded scale, half-even;
+ * an all-zero group gets scale 0 and codes 0.  Canonical storage: u8
+ * codes[N][K] holding u = c + 16, fp16 scales[N][K/64].  Kernel storage: the
+ * low 4 bits of u in the W4 packed layout (vw4_w4_packed_bytes(N, K) bytes),
+ * the high bit in a 1-bit plane of vw4_w5_hi_plane_bytes(N, K) bytes (per
+ * 64-row tile and K-group 512 bytes; lane l = 16 kq + i owns 8 bytes, dword d
+ * holding rows 16 nb + i of row blocks nb = 2 d and 2 d + 1, the bit of
+ * k = 32 s + 8 kq + j at 4 (2 (nb & 1) + s) + j / 2 + 16 (j % 2)), and the W4
+ * packed scales.  The calls below behave as their W6 counterparts.
+ * ------------------------------------------------------------------------ */
+VW4_API int vw4_w5_quantize_host(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales);
+VW4_API size_t vw4_w5_hi_plane_bytes(int64_t N, int64_t K);
+VW4_API int vw4_w5_pack(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, uint8_t* hi,
+                        uint8_t* lo, uint16_t* packed_scales, void* stream);
+VW4_API size_t vw4_w5_workspace_bytes(int32_t M, int32_t N, int32_t K);
+VW4_API int w5_skinny_gemm(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, const uint8_t* w_lo,
+                           const uint16_t* scales_packed, void* y, int64_t ldy, int32_t y_dtype, int32_t M, int32_t N,
+                           int32_t K, void* ws, size_t ws_bytes, void* stream);
+VW4_API int vw4_w5_partials_layout(int32_t M, int32_t N, int32_t K, int32_t* S, int64_t* ldp);
+VW4_API int w5_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, const uint8_t* w_lo,
+                                    const uint16_t* scales_packed, float* part, int32_t M, int32_t N, int32_t K,
+                                    void* stream);
+
+/* ------------------------------------------------------------------------
  * A third weight format: W6 (the same BaseRT section lists Q2 ... Q8; no
  * layout).  Per row n and 64-element group g: scale = fp16_rne(absmax / 31),
  * c_k = clamp(rint(w_k / scale), -31, 31) with the rounded scale, half-even;

@@ -183,6 +183,23 @@ def test_w8_partials_layout_and_validation():
     assert _call("w8_skinny_gemm_partials", fake, 64, fake, fake, fake, None, 1, 64, 64, None) == B.VW4_EINVAL
 
 
+def test_w5_host_quantizer_matches_oracle_and_sizes():
+    rng = np.random.default_rng(11)
+    w = rng.normal(0.0, 0.02, (45, 384)).astype(np.float32)
+    w[3, 64:128] = 0.0
+    w[7, 100] = 4.0
+    c1, s1 = B.w5_quantize_host(w)
+    c2, s2 = oracle.w5_quantize(w)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    assert c1.min() >= 1 and c1.max() <= 31
+    assert B.lib().vw4_w5_hi_plane_bytes(100, 320) == 128 * 320 // 8
+    assert B.lib().vw4_w5_hi_plane_bytes(10, 100) == 0
+    assert B.w5_workspace_bytes(9, 64, 64) == 0
+    fake = ctypes.c_void_p(0x100000)
+    assert _call("w5_skinny_gemm", fake, 64, fake, fake, fake, fake, 64, 0, 9, 64, 64, None, 0, None) == B.VW4_EINVAL
+    assert _call("w5_skinny_gemm_partials", fake, 64, fake, fake, fake, None, 1, 64, 64, None) == B.VW4_EINVAL
+
+
 def test_w6_host_quantizer_matches_oracle_and_sizes():
     rng = np.random.default_rng(13)
     w = rng.normal(0.0, 0.02, (45, 384)).astype(np.float32)

@@ -32,7 +32,7 @@
 //    the matrix cores form from the same A operand.  Then acc += scale[n] * D.
 //  * Formats are plane decoders (below): W4 is one 4-bit plane; W8 splits the
 //    8-bit code into a high and a low 4-bit plane; W6 into a 2-bit high plane
-//    and a 4-bit low plane.  Everything else -- lane mapping, pipeline, split
+//    and a 4-bit low plane; W5 into a 1-bit high plane and a 4-bit low plane.  Everything else -- lane mapping, pipeline, split
 //    plan, epilogues, reduction -- is one kernel template.
 //  * Split K: S_wg wavefronts of a workgroup take consecutive K slices of the
 //    same tile and are reduced through LDS; when the tiles are too few to fill
@@ -50,6 +50,7 @@ namespace sg {
 
 constexpr int MAX_M = 8;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr int PF = 4;                          // groups in flight per lane
@@ -64,6 +65,17 @@ __device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t mask_s, uint32_t
 }
 
 // 8 code nibbles (4-bit plane word) -> the 8 bf16 values 128 + u of one MFMA operand.
+// 1-bit fields, quarter q of a dword: element j of the 8 at bit 4 q + j / 2
+// (low half) or 16 + 4 q + j / 2 (high half), as bf16 pairs 128 + b.
+__device__ __forceinline__ bf16x8 one8(uint32_t w, int q, uint32_t magic_v) {
+    const uint32_t v = w >> (4 * q);
+    u32x4 r;
+    r.x = and_or(v, 0x00010001u, magic_v);
+    r.y = and_or(v >> 1, 0x00010001u, magic_v);
+    r.z = and_or(v >> 2, 0x00010001u, magic_v);
+    r.w = and_or(v >> 3, 0x00010001u, magic_v);
+    return __builtin_bit_cast(bf16x8, r);
+}
 __device__ __forceinline__ bf16x8 nib8(uint32_t w, uint32_t kmask, uint32_t magic_v) {
     u32x4 r;
     r.x = and_or(w, kmask, magic_v);
@@ -161,7 +173,7 @@ struct FmtW4 {
 // (128 + hi) and D_lo = sum x (128 + lo), 16 D_hi + D_lo = sum x (2176 + bias +
 // c), so sum x c = 16 (D_hi - (136 + bias / 16) sum x) + D_lo.  The high
 // plane's chain starts from x . (-(136 + bias / 16)) (NEG_PAIR): W8 (bias
-// 128) -144, W6 (bias 32) -138.
+// 128) -144, W6 (bias 32) -138, W5 (bias 16) -137.
 template <class Derived>
 struct TwoPlane {
     __device__ static void finish(const bf16x8 (&hb)[4][2], const bf16x8 (&lb)[4][2], bf16x8 a0, bf16x8 a1,
@@ -242,6 +254,43 @@ struct FmtW6 : TwoPlane<FmtW6> {
     }
     __host__ __device__ static Planes expert(Planes P, int64_t e, int64_t w_estride) {
         P.p0 += e * (w_estride / 2);
+        P.p1 += e * w_estride;
+        return P;
+    }
+};
+
+// W5: c in [-15, 15], u = c + 16 = 16 hi + lo with hi in {0, 1}; lo in the W4
+// layout, hi in a 1-bit plane with the same lane mapping (8 bytes per lane and
+// group: dword nb / 2 holds row blocks nb = 2 d and 2 d + 1, quarter
+// q = 2 (nb & 1) + s of it the k half s, element j at bit 4 q + j / 2 +
+// 16 (j % 2)).
+struct FmtW5 : TwoPlane<FmtW5> {
+    static constexpr int NW = 3;
+    static constexpr uint32_t NEG_PAIR = 0xC309C309u;   // two bf16 -137.0
+    __device__ static void base(const Planes& P, int64_t t, int G, int lane, const u32x4*& b0, const u32x4*& b1) {
+        b0 = (const u32x4*)((const u32x2*)P.p0 + t * G * 64 + lane);   // the 1-bit plane in 8-byte units
+        b1 = P.p1 + t * G * 128 + lane;
+    }
+    __device__ static void load(u32x4 (&w)[NW], const u32x4* b0, const u32x4* b1, int64_t g) {
+        const u32x2 h = __builtin_nontemporal_load((const u32x2*)b0 + g * 64);
+        w[0] = u32x4{h.x, h.y, 0u, 0u};
+        w[1] = __builtin_nontemporal_load(b1 + g * 128);
+        w[2] = __builtin_nontemporal_load(b1 + g * 128 + 64);
+    }
+    __device__ static void group(const u32x4 (&w)[NW], bf16x8 a0, bf16x8 a1, uint2 sc, uint32_t kmask,
+                                 uint32_t magic_v, f32x4 (&acc)[4]) {
+        bf16x8 hb[4][2], lb[4][2];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                hb[nb][s] = one8(w[0][nb >> 1], 2 * (nb & 1) + s, magic_v);
+                lb[nb][s] = nib8(w[1 + (nb >> 1)][2 * (nb & 1) + s], kmask, magic_v);
+            }
+        finish(hb, lb, a0, a1, sc, acc);
+    }
+    __host__ __device__ static Planes expert(Planes P, int64_t e, int64_t w_estride) {
+        P.p0 += e * (w_estride / 4);
         P.p1 += e * w_estride;
         return P;
     }

@@ -216,6 +216,49 @@ __global__ __launch_bounds__(256) void pack6_kernel(const uint8_t* __restrict__ 
     pscales[packed_scale(n, g, G)] = (n < N) ? scales[n * G + g] : (uint16_t)0;
 }
 
+// W5: one u8 code u = c + 16 per element.  The low 4 bits go to a plane in
+// the W4 packed layout; the high bit to a 1-bit plane with the same lane
+// mapping: per tile and K-group 512 bytes, lane l = 16 kq + i owning 8 bytes,
+// dword d holding rows 16 nb + i of the two row blocks nb = 2 d, 2 d + 1, the
+// bit of k = 32 s + 8 kq + j at 4 (2 (nb & 1) + s) + j / 2 + 16 (j % 2).  The
+// thread of an even row block writes the dword of both of its blocks.
+// Padding rows get u = 16 (code 0), scale 0.
+__global__ __launch_bounds__(256) void pack5_kernel(const uint8_t* __restrict__ codes,
+                                                    const uint16_t* __restrict__ scales, int64_t N, int64_t K,
+                                                    int64_t Npad, uint32_t* __restrict__ hi, uint32_t* __restrict__ lo,
+                                                    uint16_t* __restrict__ pscales) {
+    const int64_t G = K / 64;
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= Npad * G) return;
+    const int64_t n = id / G, g = id % G;
+    const uint8_t* src = codes + n * K + g * 64;
+    for (int o = 0; o < 8; ++o) {
+        uint32_t wl = 0;
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t u = (n < N) ? src[o * 8 + j] : 16u;
+            wl |= (u & 15u) << packed_nibble_shift(j);
+        }
+        lo[packed_dword(n, g * 64 + o * 8, G)] = wl;
+    }
+    const int64_t t = n >> 6;
+    const int i = (int)(n & 15), nb = (int)((n >> 4) & 3);
+    if ((nb & 1) == 0) {
+        for (int kq = 0; kq < 4; ++kq) {
+            uint32_t wh = 0;
+            for (int b = 0; b < 2; ++b) {
+                const int64_t row = n + 16 * b;   // row blocks nb, nb + 1 of the same tile
+                for (int s = 0; s < 2; ++s)
+                    for (int j = 0; j < 8; ++j) {
+                        const uint32_t u = (row < N) ? codes[row * K + g * 64 + 32 * s + 8 * kq + j] : 16u;
+                        wh |= ((u >> 4) & 1u) << (4 * (2 * b + s) + (j >> 1) + 16 * (j & 1));
+                    }
+            }
+            hi[((t * G + g) * 64 + kq * 16 + i) * 2 + (nb >> 1)] = wh;
+        }
+    }
+    pscales[packed_scale(n, g, G)] = (n < N) ? scales[n * G + g] : (uint16_t)0;
+}
+
 __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict__ packed,
                                                      const uint16_t* __restrict__ pscales, int64_t N, int64_t K,
                                                      uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
@@ -372,6 +415,45 @@ int vw4_w6_quantize_host(const float* w, int64_t N, int64_t K, uint8_t* codes, u
         }
     }
     return VW4_OK;
+}
+
+int vw4_w5_quantize_host(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales) {
+    int rc = check_shape(N, K);
+    if (rc) return rc;
+    VW4_REQUIRE(w && codes && scales, VW4_EINVAL, "null pointer");
+    const int64_t G = K / 64;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < G; ++g) {
+            const float* wg = w + n * K + g * 64;
+            float a = 0.0f;
+            for (int k = 0; k < 64; ++k) a = fmaxf(a, fabsf(wg[k]));
+            const uint16_t s16 = host_f32_to_f16(a / 15.0f);
+            const float sf = host_f16_to_f32(s16);
+            scales[n * G + g] = s16;
+            for (int k = 0; k < 64; ++k) {
+                const int c = sf != 0.0f ? (int)fminf(fmaxf(rintf(wg[k] / sf), -15.0f), 15.0f) : 0;
+                codes[n * K + g * 64 + k] = (uint8_t)(c + 16);
+            }
+        }
+    }
+    return VW4_OK;
+}
+
+size_t vw4_w5_hi_plane_bytes(int64_t N, int64_t K) {
+    if (check_shape(N, K)) return 0;
+    return (size_t)(pad64(N) * (K / 8));
+}
+
+int vw4_w5_pack(const uint8_t* codes_dev, const uint16_t* scales_dev, int64_t N, int64_t K, uint8_t* hi_dev,
+                uint8_t* lo_dev, uint16_t* packed_scales_dev, void* stream) {
+    int rc = check_shape(N, K);
+    if (rc) return rc;
+    VW4_REQUIRE(codes_dev && scales_dev && hi_dev && lo_dev && packed_scales_dev, VW4_EINVAL, "null pointer");
+    VW4_REQUIRE(aligned(hi_dev, 16) && aligned(lo_dev, 16), VW4_EINVAL, "packed planes must be 16-byte aligned");
+    const int64_t Np = pad64(N), total = Np * (K / 64);
+    hipLaunchKernelGGL(pack5_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                       codes_dev, scales_dev, N, K, Np, (uint32_t*)hi_dev, (uint32_t*)lo_dev, packed_scales_dev);
+    return check_launch("vw4_w5_pack");
 }
 
 size_t vw4_w6_hi_plane_bytes(int64_t N, int64_t K) {
