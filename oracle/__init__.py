@@ -109,6 +109,10 @@ def lib():
         L.oracle_w8_gemm.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P]
         L.oracle_w5_quantize.argtypes = [_P, _I64, _I64, _P, _P]
         L.oracle_w5_gemm.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P]
+        L.oracle_w3_quantize.argtypes = [_P, _I64, _I64, _P, _P]
+        L.oracle_w3_gemm.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P]
+        L.oracle_w2_quantize.argtypes = [_P, _I64, _I64, _P, _P]
+        L.oracle_w2_gemm.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P]
         L.oracle_w6_quantize.argtypes = [_P, _I64, _I64, _P, _P]
         L.oracle_w6_gemm.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P]
         L.oracle_embed_rows.argtypes = [_P, _I64, _I64, _P, _I64, _P]
@@ -453,6 +457,52 @@ def w5_gemm(x_bf16: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> np.nda
     assert codes.shape == (N, K) and scales.shape == (N, K // 64)
     y = np.zeros((M, N), dtype=np.float64)
     lib().oracle_w5_gemm(_ptr(x_bf16), M, K, _ptr(np.ascontiguousarray(codes)), _ptr(np.ascontiguousarray(scales)),
+                         N, _ptr(y))
+    return y
+
+
+def w3_quantize(w: np.ndarray):
+    """w: float32 [N][K] (K % 64 == 0) -> (codes u8 [N][K] holding c + 4, scales u16 [N][K/64])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    assert K % 64 == 0
+    codes = np.zeros((N, K), dtype=np.uint8)
+    scales = np.zeros((N, K // 64), dtype=np.uint16)
+    lib().oracle_w3_quantize(_ptr(w), N, K, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def w3_gemm(x_bf16: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """x_bf16: uint16 [M][K]; codes u8 [N][K] (c + 4); returns float64 [M][N]."""
+    x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    M, K = x_bf16.shape
+    N = codes.shape[0]
+    assert codes.shape == (N, K) and scales.shape == (N, K // 64)
+    y = np.zeros((M, N), dtype=np.float64)
+    lib().oracle_w3_gemm(_ptr(x_bf16), M, K, _ptr(np.ascontiguousarray(codes)), _ptr(np.ascontiguousarray(scales)),
+                         N, _ptr(y))
+    return y
+
+
+def w2_quantize(w: np.ndarray):
+    """w: float32 [N][K] (K % 64 == 0) -> (codes u8 [N][K] holding c + 1, scales u16 [N][K/64])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    assert K % 64 == 0
+    codes = np.zeros((N, K), dtype=np.uint8)
+    scales = np.zeros((N, K // 64), dtype=np.uint16)
+    lib().oracle_w2_quantize(_ptr(w), N, K, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def w2_gemm(x_bf16: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """x_bf16: uint16 [M][K]; codes u8 [N][K] (c + 1); returns float64 [M][N]."""
+    x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    M, K = x_bf16.shape
+    N = codes.shape[0]
+    assert codes.shape == (N, K) and scales.shape == (N, K // 64)
+    y = np.zeros((M, N), dtype=np.float64)
+    lib().oracle_w2_gemm(_ptr(x_bf16), M, K, _ptr(np.ascontiguousarray(codes)), _ptr(np.ascontiguousarray(scales)),
                          N, _ptr(y))
     return y
 

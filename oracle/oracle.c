@@ -745,6 +745,96 @@ EXPORT void oracle_w5_gemm(const uint16_t* x_bf16, int64_t M, int64_t K, const u
 }
 
 /* ------------------------------------------------------------------------ */
+/* Two narrower weight formats: W3 and W2 (the same BaseRT section lists Q2   */
+/* ... Q8 among the GEMV's formats; no layout).  Reading: the W4 recipe with  */
+/* b-bit codes in [-(2^(b-1) - 1), 2^(b-1) - 1] -- W3: [-3, 3], scale =       */
+/* fp16(absmax / 3); W2: [-1, 1], scale = fp16(absmax / 1) -- codes against   */
+/* the rounded scale, half-even, clamped; an all-zero group gets scale 0 and  */
+/* codes 0.  Canonical storage: u8 codes[N][K] holding u = c + 2^(b-1)        */
+/* (W3: c + 4, W2: c + 1); f16 scales[N][K/64].                               */
+/* ------------------------------------------------------------------------ */
+EXPORT void oracle_w3_quantize(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales) {
+    const int64_t G = K / 64;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < G; ++g) {
+            const float* wg = w + n * K + g * 64;
+            float a = 0.0f;
+            for (int k = 0; k < 64; ++k) {
+                float v = fabsf(wg[k]);
+                if (v > a) a = v;
+            }
+            uint16_t s16 = oracle_f32_to_f16(a / 3.0f);     /* binary32 division */
+            float sf = (float)f16_value(s16);
+            scales[n * G + g] = s16;
+            for (int k = 0; k < 64; ++k) {
+                int c = 0;
+                if (sf != 0.0f) {
+                    float r = rintf(wg[k] / sf);            /* binary32 division, half-even */
+                    if (r > 3.0f) r = 3.0f;
+                    if (r < -3.0f) r = -3.0f;
+                    c = (int)r;
+                }
+                codes[n * K + g * 64 + k] = (uint8_t)(c + 4);
+            }
+        }
+    }
+}
+
+EXPORT void oracle_w2_quantize(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales) {
+    const int64_t G = K / 64;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < G; ++g) {
+            const float* wg = w + n * K + g * 64;
+            float a = 0.0f;
+            for (int k = 0; k < 64; ++k) {
+                float v = fabsf(wg[k]);
+                if (v > a) a = v;
+            }
+            uint16_t s16 = oracle_f32_to_f16(a);            /* absmax / 1 */
+            float sf = (float)f16_value(s16);
+            scales[n * G + g] = s16;
+            for (int k = 0; k < 64; ++k) {
+                int c = 0;
+                if (sf != 0.0f) {
+                    float r = rintf(wg[k] / sf);            /* binary32 division, half-even */
+                    if (r > 1.0f) r = 1.0f;
+                    if (r < -1.0f) r = -1.0f;
+                    c = (int)r;
+                }
+                codes[n * K + g * 64 + k] = (uint8_t)(c + 1);
+            }
+        }
+    }
+}
+
+/* y[m][n] = sum_k x[m][k] * (u[n][k] - bias) * s[n][k/64], fp64, sequential in k
+ * (bias 4 for W3 codes, 1 for W2 codes). */
+static void w_small_gemm(const uint16_t* x_bf16, int64_t M, int64_t K, const uint8_t* codes, int bias,
+                         const uint16_t* scales, int64_t N, double* y) {
+    const int64_t G = K / 64;
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += bf16_value(x_bf16[m * K + k]) * (double)((int)codes[n * K + k] - bias) *
+                       f16_value(scales[n * G + k / 64]);
+            y[m * N + n] = acc;
+        }
+    }
+}
+
+EXPORT void oracle_w3_gemm(const uint16_t* x_bf16, int64_t M, int64_t K, const uint8_t* codes,
+                           const uint16_t* scales, int64_t N, double* y /* [M][N] */) {
+    w_small_gemm(x_bf16, M, K, codes, 4, scales, N, y);
+}
+
+EXPORT void oracle_w2_gemm(const uint16_t* x_bf16, int64_t M, int64_t K, const uint8_t* codes,
+                           const uint16_t* scales, int64_t N, double* y /* [M][N] */) {
+    w_small_gemm(x_bf16, M, K, codes, 1, scales, N, y);
+}
+
+/* ------------------------------------------------------------------------ */
 /* A third weight format: W6 ([BaseRT/方法] lists Q2 ... Q8; no layout).       */
 /* Reading: the W4 recipe with 6-bit codes -- codes in [-31, 31]; scale =     */
 /* fp16(absmax / 31) rounded to nearest-even; codes use the rounded scale,    */
