@@ -831,11 +831,12 @@ def verify27b_cpu_baseline_layer(reps=8):
 
 
 def layer_linears_w8_cpu_baseline(reps=4, fmt="w8"):
-    """The CPU oracle's W8 (or W6, W5) GEMM on the four linears of one layer at M=4 (fp64), reps row sets."""
+    """The CPU oracle's W8 (or W6, W5, W3, W2) GEMM on the four linears of one layer at M=4 (fp64), reps row sets."""
     import oracle
     from verify_step_w4_amd import synth
     quant, gemm = {"w8": (oracle.w8_quantize, oracle.w8_gemm), "w6": (oracle.w6_quantize, oracle.w6_gemm),
-                   "w5": (oracle.w5_quantize, oracle.w5_gemm)}[fmt]
+                   "w5": (oracle.w5_quantize, oracle.w5_gemm), "w3": (oracle.w3_quantize, oracle.w3_gemm),
+                   "w2": (oracle.w2_quantize, oracle.w2_gemm)}[fmt]
     g = synth.rng(synth.SEED_BASE + 9)
     tot = 0.0
     for N, K in [(7168, 5120), (5120, 5120), (34816, 5120), (5120, 17408)]:
@@ -1209,26 +1210,42 @@ def layer_linears_w5_workload(args):
     return layer_linears_w8_workload(args, fmt="w5")
 
 
+def layer_linears_w3_workload(args):
+    return layer_linears_w8_workload(args, fmt="w3")
+
+
+def layer_linears_w2_workload(args):
+    return layer_linears_w8_workload(args, fmt="w2")
+
+
 def layer_linears_w8_workload(args, fmt="w8"):
     """The same four linears of one 27B-shaped layer in the W8 format (int8
     codes, fp16 scale per 64 K: 1.03125 bytes per weight, 351 MB per layer),
-    or the W6 (0.78125 bytes per weight) or W5 (0.65625) format; plain GEMM
+    or the W6 (0.78125 bytes per weight), W5 (0.65625), W3 (0.40625) or W2
+    (0.28125) format; plain GEMM
     outputs (gate|up as one [34816][5120] product); 4 layers' weights rotated.
     A step is one pass over a layer's four linears at M = 4."""
     import torch
 
     from verify_step_w4_amd import binding as B
-    from verify_step_w4_amd.model import W5Linear, W6Linear, W8Linear
+    from verify_step_w4_amd.model import W2Linear, W3Linear, W5Linear, W6Linear, W8Linear
 
     d, F, nqkv = 5120, 17408, 7168
     nlay = 4
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20261209)
     shapes = {"qkv": (nqkv, d), "o": (d, d), "gate_up": (2 * F, d), "down": (d, F)}
-    Lin = {"w8": W8Linear, "w6": W6Linear, "w5": W5Linear}[fmt]
-    code_bytes = {"w8": 1.0, "w6": 0.75, "w5": 0.625}[fmt]
-    gemm = {"w8": B.w8_skinny_gemm, "w6": B.w6_skinny_gemm, "w5": B.w5_skinny_gemm}[fmt]
-    wsb = {"w8": B.w8_workspace_bytes, "w6": B.w6_workspace_bytes, "w5": B.w5_workspace_bytes}[fmt]
+    Lin = {"w8": W8Linear, "w6": W6Linear, "w5": W5Linear, "w3": W3Linear, "w2": W2Linear}[fmt]
+    code_bytes = {"w8": 1.0, "w6": 0.75, "w5": 0.625, "w3": 0.375, "w2": 0.25}[fmt]
+    two_plane = {"w8": B.w8_skinny_gemm, "w6": B.w6_skinny_gemm, "w5": B.w5_skinny_gemm, "w3": B.w3_skinny_gemm}
+
+    def gemm(x, L, y, M, N, K, ws):
+        if fmt == "w2":
+            B.w2_skinny_gemm(x, L.packed, L.pscales, y, M, N, K, ws=ws)
+        else:
+            two_plane[fmt](x, L.hi, L.lo, L.pscales, y, M, N, K, ws=ws)
+    wsb = {"w8": B.w8_workspace_bytes, "w6": B.w6_workspace_bytes, "w5": B.w5_workspace_bytes,
+           "w3": B.w3_workspace_bytes, "w2": B.w2_workspace_bytes}[fmt]
     log(f"generating {nlay} layers of {fmt.upper()} linears")
     layers = [{nm: Lin.random(N, K, gen) for nm, (N, K) in shapes.items()} for _ in range(nlay)]
     M = 4
@@ -1241,7 +1258,7 @@ def layer_linears_w8_workload(args, fmt="w8"):
         for L in layers:
             for nm in names:
                 N, K = shapes[nm]
-                gemm(xs[K], L[nm].hi, L[nm].lo, L[nm].pscales, ys[nm], M, N, K, ws=ws[nm])
+                gemm(xs[K], L[nm], ys[nm], M, N, K, ws[nm])
                 n += 1
         return n
 
@@ -1267,7 +1284,9 @@ def layer_linears_w8_workload(args, fmt="w8"):
                 "down": [d, F], "M": M, "rotated_layers": nlay,
                 "weights": {"w8": "int8 group-64 symmetric, fp16 scales (two nibble planes)",
                             "w6": "6-bit group-64 symmetric, fp16 scales (2-bit + 4-bit planes)",
-                            "w5": "5-bit group-64 symmetric, fp16 scales (1-bit + 4-bit planes)"}[fmt]},
+                            "w5": "5-bit group-64 symmetric, fp16 scales (1-bit + 4-bit planes)",
+                            "w3": "3-bit group-64 symmetric, fp16 scales (1-bit + 2-bit planes)",
+                            "w2": "2-bit group-64 symmetric (codes -1..1), fp16 scales (one 2-bit plane)"}[fmt]},
         roofline={"bound": "hbm", "achieved": round(lb / (layer_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
                   "unit": "GB/s", "frac": round(lb / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
                   "kernel": f"{fmt}_gemm_kernel (+ {fmt}_reduce_kernel; the four linears of a layer at M=4, "
@@ -1372,7 +1391,9 @@ WORKLOADS = {"lm_head_verify": (lm_head_workload, lm_head_cpu_baseline),
              "spec_loop_27b": (spec_loop_workload, lambda: verify27b_cpu_baseline()),
              "layer_linears_w8": (layer_linears_w8_workload, lambda: layer_linears_w8_cpu_baseline()),
              "layer_linears_w6": (layer_linears_w6_workload, lambda: layer_linears_w8_cpu_baseline(fmt="w6")),
-             "layer_linears_w5": (layer_linears_w5_workload, lambda: layer_linears_w8_cpu_baseline(fmt="w5"))}
+             "layer_linears_w5": (layer_linears_w5_workload, lambda: layer_linears_w8_cpu_baseline(fmt="w5")),
+             "layer_linears_w3": (layer_linears_w3_workload, lambda: layer_linears_w8_cpu_baseline(fmt="w3")),
+             "layer_linears_w2": (layer_linears_w2_workload, lambda: layer_linears_w8_cpu_baseline(fmt="w2"))}
 
 
 def main():
@@ -1423,7 +1444,8 @@ def main():
     for k in ("stages_us", "w4_gemm_by_linear", "accepted_length_hist", "flagged_steps", "m1_ar_step_ms",
               "verify_over_ar", "step_hbm_gbs", "experts_per_step", "grouped_gemm_gbs", "m_sweep", "unit_note",
               "context_sweep", "stats_accept_sweep", "sustained", "attention_by_context", "spec_loop",
-              "w8_gemm_by_linear", "w6_gemm_by_linear", "w5_gemm_by_linear"):
+              "w8_gemm_by_linear", "w6_gemm_by_linear", "w5_gemm_by_linear", "w3_gemm_by_linear",
+              "w2_gemm_by_linear"):
         if k in res:
             out[k] = res[k]
     if not args.no_cpu_baseline:

@@ -476,6 +476,61 @@ VW4_API int w8_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_
                                     void* stream);
 
 /* ------------------------------------------------------------------------
+ * The narrowest weight formats: W3 and W2 (the same BaseRT section lists Q2
+ * ... Q8; no layout).  Per row n and 64-element group g: scale =
+ * fp16_rne(absmax / qmax), c_k = clamp(rint(w_k / scale), -qmax, qmax) with
+ * the rounded scale, half-even; an all-zero group gets scale 0 and codes 0.
+ * W3: qmax 3, canonical u8 codes[N][K] holding u = c + 4; W2: qmax 1,
+ * u = c + 1; fp16 scales[N][K/64].
+ *
+ * Kernel storage, W3: the high bit of u in the 1-bit plane of the W5 layout
+ * (vw4_w3_hi_plane_bytes(N, K) = pad64(N) * K / 8 bytes), the low 2 bits in
+ * a 2-bit plane (vw4_w3_lo_plane_bytes(N, K) = pad64(N) * K / 4 bytes: per
+ * 64-row tile and K-group 1 KiB, lane l = 16 kq + i owning 16 bytes, dword
+ * nb holding row 16 nb + i, the field of k = 32 s + 8 kq + j at bits
+ * 8 s + 2 (j / 2) + 16 (j % 2)), and the W4 packed scales.  W2: c = u - 1
+ * in sign-magnitude (field bit 0 = (c != 0), bit 1 = (c < 0)) in one 2-bit
+ * plane of that layout (vw4_w2_packed_bytes(N, K) bytes) and the W4 packed
+ * scales.  Padding rows hold code 0 and scale 0.  Planes are 16-byte
+ * aligned.
+ *
+ * The quantisers run on the host (VW4_EINVAL on a bad shape or a null
+ * pointer); the packs read device codes and scales and write device planes
+ * on `stream`.  The GEMM calls behave as their W6 / W4 counterparts: x bf16
+ * [M][ldx] (ldx >= K, ldx % 8 == 0, 16-byte aligned), y fp32 or bf16
+ * [M][ldy], M in 1..8, K % 64 == 0 and K <= 65536; a workspace of at least
+ * vw4_wN_workspace_bytes(M, N, K) bytes (256-byte aligned) when that is not
+ * 0, else VW4_EWORKSPACE; the partials calls write S slices of [M][ldp]
+ * fp32 sums (vw4_wN_partials_layout) that add up, in slice order, to y.
+ * ------------------------------------------------------------------------ */
+VW4_API int vw4_w3_quantize_host(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales);
+VW4_API size_t vw4_w3_hi_plane_bytes(int64_t N, int64_t K);
+VW4_API size_t vw4_w3_lo_plane_bytes(int64_t N, int64_t K);
+VW4_API int vw4_w3_pack(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, uint8_t* hi,
+                        uint8_t* lo, uint16_t* packed_scales, void* stream);
+VW4_API size_t vw4_w3_workspace_bytes(int32_t M, int32_t N, int32_t K);
+VW4_API int w3_skinny_gemm(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, const uint8_t* w_lo,
+                           const uint16_t* scales_packed, void* y, int64_t ldy, int32_t y_dtype, int32_t M, int32_t N,
+                           int32_t K, void* ws, size_t ws_bytes, void* stream);
+VW4_API int vw4_w3_partials_layout(int32_t M, int32_t N, int32_t K, int32_t* S, int64_t* ldp);
+VW4_API int w3_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, const uint8_t* w_lo,
+                                    const uint16_t* scales_packed, float* part, int32_t M, int32_t N, int32_t K,
+                                    void* stream);
+
+VW4_API int vw4_w2_quantize_host(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales);
+VW4_API size_t vw4_w2_packed_bytes(int64_t N, int64_t K);
+VW4_API int vw4_w2_pack(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, uint8_t* packed,
+                        uint16_t* packed_scales, void* stream);
+VW4_API size_t vw4_w2_workspace_bytes(int32_t M, int32_t N, int32_t K);
+VW4_API int w2_skinny_gemm(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, const uint16_t* scales_packed,
+                           void* y, int64_t ldy, int32_t y_dtype, int32_t M, int32_t N, int32_t K, void* ws,
+                           size_t ws_bytes, void* stream);
+VW4_API int vw4_w2_partials_layout(int32_t M, int32_t N, int32_t K, int32_t* S, int64_t* ldp);
+VW4_API int w2_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w_packed,
+                                    const uint16_t* scales_packed, float* part, int32_t M, int32_t N, int32_t K,
+                                    void* stream);
+
+/* ------------------------------------------------------------------------
  * A fourth weight format: W5 (the same BaseRT section lists Q2 ... Q8; no
  * layout).  Per row n and 64-element group g: scale = fp16_rne(absmax / 15),
  * c_k = clamp(rint(w_k / scale), -15, 15) with the rounded scale, half-even;

@@ -183,6 +183,35 @@ def test_w8_partials_layout_and_validation():
     assert _call("w8_skinny_gemm_partials", fake, 64, fake, fake, fake, None, 1, 64, 64, None) == B.VW4_EINVAL
 
 
+@pytest.mark.parametrize("b", [3, 2])
+def test_w3_w2_host_quantizers_match_oracle_and_sizes(b):
+    rng = np.random.default_rng(20 + b)
+    w = rng.normal(0.0, 0.02, (45, 384)).astype(np.float32)
+    w[3, 64:128] = 0.0
+    w[7, 100] = 4.0
+    c1, s1 = getattr(B, f"w{b}_quantize_host")(w)
+    c2, s2 = getattr(oracle, f"w{b}_quantize")(w)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    assert c1.min() >= (1 if b == 3 else 0) and c1.max() <= (7 if b == 3 else 2)
+    if b == 3:
+        assert B.lib().vw4_w3_hi_plane_bytes(100, 320) == 128 * 320 // 8
+        assert B.lib().vw4_w3_lo_plane_bytes(100, 320) == 128 * 320 // 4
+        assert B.lib().vw4_w3_lo_plane_bytes(10, 100) == 0
+        assert B.w3_workspace_bytes(9, 64, 64) == 0
+    else:
+        assert B.lib().vw4_w2_packed_bytes(100, 320) == 128 * 320 // 4
+        assert B.lib().vw4_w2_packed_bytes(10, 100) == 0
+        assert B.w2_workspace_bytes(9, 64, 64) == 0
+    fake = ctypes.c_void_p(0x100000)
+    if b == 3:
+        assert _call("w3_skinny_gemm", fake, 64, fake, fake, fake, fake, 64, 0, 9, 64, 64, None, 0, None) == B.VW4_EINVAL
+        assert _call("w3_skinny_gemm_partials", fake, 64, fake, fake, fake, None, 1, 64, 64, None) == B.VW4_EINVAL
+    else:
+        assert _call("w2_skinny_gemm", fake, 64, fake, fake, fake, 64, 0, 9, 64, 64, None, 0, None) == B.VW4_EINVAL
+        assert _call("w2_skinny_gemm", fake, 60, fake, fake, fake, 64, 0, 1, 64, 64, None, 0, None) == B.VW4_EINVAL
+        assert _call("w2_skinny_gemm_partials", fake, 64, fake, fake, None, 1, 64, 64, None) == B.VW4_EINVAL
+
+
 def test_w5_host_quantizer_matches_oracle_and_sizes():
     rng = np.random.default_rng(11)
     w = rng.normal(0.0, 0.02, (45, 384)).astype(np.float32)

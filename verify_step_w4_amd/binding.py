@@ -72,6 +72,23 @@ SIGNATURES = {
     "vw4_w8_partials_layout": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
                                               ctypes.POINTER(ctypes.c_int64)]),
     "w8_skinny_gemm_partials": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
+    "vw4_w3_quantize_host": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
+    "vw4_w3_hi_plane_bytes": (_SZ, [_I64, _I64]),
+    "vw4_w3_lo_plane_bytes": (_SZ, [_I64, _I64]),
+    "vw4_w3_pack": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P, _P]),
+    "vw4_w3_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "w3_skinny_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+    "vw4_w3_partials_layout": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
+                                              ctypes.POINTER(ctypes.c_int64)]),
+    "w3_skinny_gemm_partials": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
+    "vw4_w2_quantize_host": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
+    "vw4_w2_packed_bytes": (_SZ, [_I64, _I64]),
+    "vw4_w2_pack": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "vw4_w2_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "w2_skinny_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+    "vw4_w2_partials_layout": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
+                                              ctypes.POINTER(ctypes.c_int64)]),
+    "w2_skinny_gemm_partials": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I32, _I32, _I32, _P]),
     "vw4_w5_quantize_host": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
     "vw4_w5_hi_plane_bytes": (_SZ, [_I64, _I64]),
     "vw4_w5_pack": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P, _P]),
@@ -402,6 +419,102 @@ def w8_skinny_gemm_partials(x, w_hi, w_lo, scales_packed, part, M: int, N: int, 
     _check("w8_skinny_gemm_partials", lib().w8_skinny_gemm_partials(_ptr(x), ldx, _ptr(w_hi), _ptr(w_lo),
                                                                     _ptr(scales_packed), _ptr(part), M, N, K,
                                                                     _stream(stream)))
+
+
+def w3_quantize_host(w: np.ndarray):
+    """fp32 [N][K] host array -> (codes u8 [N][K] holding c + 4, scales u16 [N][K/64])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    codes = np.zeros((N, K), dtype=np.uint8)
+    scales = np.zeros((N, K // 64), dtype=np.uint16)
+    _check("vw4_w3_quantize_host", lib().vw4_w3_quantize_host(w.ctypes.data_as(ctypes.c_void_p), N, K,
+                                                              codes.ctypes.data_as(ctypes.c_void_p),
+                                                              scales.ctypes.data_as(ctypes.c_void_p)))
+    return codes, scales
+
+
+def w3_pack(codes, scales, N: int, K: int, hi, lo, pscales, stream=None):
+    _check("vw4_w3_pack", lib().vw4_w3_pack(_ptr(codes), _ptr(scales), N, K, _ptr(hi), _ptr(lo), _ptr(pscales),
+                                            _stream(stream)))
+
+
+def w3_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().vw4_w3_workspace_bytes(M, N, K))
+
+
+def w3_partials_layout(M: int, N: int, K: int):
+    S, ldp = ctypes.c_int32(0), ctypes.c_int64(0)
+    _check("vw4_w3_partials_layout", lib().vw4_w3_partials_layout(M, N, K, ctypes.byref(S), ctypes.byref(ldp)))
+    return int(S.value), int(ldp.value)
+
+
+def w3_skinny_gemm_partials(x, w_hi, w_lo, scales_packed, part, M: int, N: int, K: int, stream=None,
+                            ldx: int | None = None):
+    ldx = x.stride(0) if ldx is None else ldx
+    _check("w3_skinny_gemm_partials", lib().w3_skinny_gemm_partials(_ptr(x), ldx, _ptr(w_hi), _ptr(w_lo),
+                                                                    _ptr(scales_packed), _ptr(part), M, N, K,
+                                                                    _stream(stream)))
+
+
+def w3_skinny_gemm(x, w_hi, w_lo, scales_packed, y, M: int, N: int, K: int, ws=None, stream=None,
+                   ldx: int | None = None, ldy: int | None = None):
+    """y[M][N] (fp32 or bf16 tensor) = x[M][K] (bf16 bits) @ W3^T."""
+    import torch
+    ydt = VW4_F32 if y.dtype == torch.float32 else VW4_BF16
+    ldx = x.stride(0) if ldx is None else ldx
+    ldy = y.stride(0) if ldy is None else ldy
+    nbytes = ws.numel() if ws is not None else 0
+    _check("w3_skinny_gemm", lib().w3_skinny_gemm(_ptr(x), ldx, _ptr(w_hi), _ptr(w_lo), _ptr(scales_packed), _ptr(y),
+                                                  ldy, ydt, M, N, K, _ptr(ws), nbytes, _stream(stream)))
+    return y
+
+
+def w2_quantize_host(w: np.ndarray):
+    """fp32 [N][K] host array -> (codes u8 [N][K] holding c + 1, scales u16 [N][K/64])."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    codes = np.zeros((N, K), dtype=np.uint8)
+    scales = np.zeros((N, K // 64), dtype=np.uint16)
+    _check("vw4_w2_quantize_host", lib().vw4_w2_quantize_host(w.ctypes.data_as(ctypes.c_void_p), N, K,
+                                                              codes.ctypes.data_as(ctypes.c_void_p),
+                                                              scales.ctypes.data_as(ctypes.c_void_p)))
+    return codes, scales
+
+
+def w2_pack(codes, scales, N: int, K: int, packed, pscales, stream=None):
+    _check("vw4_w2_pack", lib().vw4_w2_pack(_ptr(codes), _ptr(scales), N, K, _ptr(packed), _ptr(pscales),
+                                            _stream(stream)))
+
+
+def w2_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().vw4_w2_workspace_bytes(M, N, K))
+
+
+def w2_partials_layout(M: int, N: int, K: int):
+    S, ldp = ctypes.c_int32(0), ctypes.c_int64(0)
+    _check("vw4_w2_partials_layout", lib().vw4_w2_partials_layout(M, N, K, ctypes.byref(S), ctypes.byref(ldp)))
+    return int(S.value), int(ldp.value)
+
+
+def w2_skinny_gemm_partials(x, w_packed, scales_packed, part, M: int, N: int, K: int, stream=None,
+                            ldx: int | None = None):
+    ldx = x.stride(0) if ldx is None else ldx
+    _check("w2_skinny_gemm_partials", lib().w2_skinny_gemm_partials(_ptr(x), ldx, _ptr(w_packed),
+                                                                    _ptr(scales_packed), _ptr(part), M, N, K,
+                                                                    _stream(stream)))
+
+
+def w2_skinny_gemm(x, w_packed, scales_packed, y, M: int, N: int, K: int, ws=None, stream=None,
+                   ldx: int | None = None, ldy: int | None = None):
+    """y[M][N] (fp32 or bf16 tensor) = x[M][K] (bf16 bits) @ W2^T."""
+    import torch
+    ydt = VW4_F32 if y.dtype == torch.float32 else VW4_BF16
+    ldx = x.stride(0) if ldx is None else ldx
+    ldy = y.stride(0) if ldy is None else ldy
+    nbytes = ws.numel() if ws is not None else 0
+    _check("w2_skinny_gemm", lib().w2_skinny_gemm(_ptr(x), ldx, _ptr(w_packed), _ptr(scales_packed), _ptr(y),
+                                                  ldy, ydt, M, N, K, _ptr(ws), nbytes, _stream(stream)))
+    return y
 
 
 def w5_quantize_host(w: np.ndarray):

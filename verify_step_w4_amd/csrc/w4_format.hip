@@ -259,6 +259,79 @@ __global__ __launch_bounds__(256) void pack5_kernel(const uint8_t* __restrict__ 
     pscales[packed_scale(n, g, G)] = (n < N) ? scales[n * G + g] : (uint16_t)0;
 }
 
+// The 2-bit plane (the layout of W6's high plane, W3's low plane and W2's
+// only plane) for row n and K-group g: field (u >> shift) & 3 of each code,
+// or, with sign_mag, the sign-magnitude form of c = u - 1 in {-1, 0, 1} (bit 0
+// = (c != 0), bit 1 = (c < 0)); padding rows take u = pad_u.  One thread per
+// (n, g) writes its row's four dwords (one per kq).
+__device__ __forceinline__ void write_plane2(const uint8_t* __restrict__ codes, int64_t N, int64_t K, int64_t n,
+                                             int64_t g, int shift, uint32_t pad_u, bool sign_mag,
+                                             uint32_t* __restrict__ plane) {
+    const int64_t G = K / 64, t = n >> 6;
+    const int i = (int)(n & 15), nb = (int)((n >> 4) & 3);
+    const uint8_t* src = codes + n * K + g * 64;
+    for (int kq = 0; kq < 4; ++kq) {
+        uint32_t wd = 0;
+        for (int s = 0; s < 2; ++s)
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t u = (n < N) ? src[32 * s + 8 * kq + j] : pad_u;
+                const uint32_t f = sign_mag ? (uint32_t)(u != 1u) | ((uint32_t)(u == 0u) << 1) : (u >> shift) & 3u;
+                wd |= f << (8 * s + 2 * (j >> 1) + 16 * (j & 1));
+            }
+        plane[((t * G + g) * 64 + kq * 16 + i) * 4 + nb] = wd;
+    }
+}
+
+// The 1-bit plane (the layout of W5's and W3's high planes) for row n and
+// K-group g: bit (u >> shift) & 1 of each code.  The thread of an even row
+// block writes the dwords of its block and the next (rows n and n + 16).
+__device__ __forceinline__ void write_plane1(const uint8_t* __restrict__ codes, int64_t N, int64_t K, int64_t n,
+                                             int64_t g, int shift, uint32_t pad_u, uint32_t* __restrict__ plane) {
+    const int64_t G = K / 64, t = n >> 6;
+    const int i = (int)(n & 15), nb = (int)((n >> 4) & 3);
+    if (nb & 1) return;
+    for (int kq = 0; kq < 4; ++kq) {
+        uint32_t wd = 0;
+        for (int b = 0; b < 2; ++b) {
+            const int64_t row = n + 16 * b;
+            for (int s = 0; s < 2; ++s)
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t u = (row < N) ? codes[row * K + g * 64 + 32 * s + 8 * kq + j] : pad_u;
+                    wd |= ((u >> shift) & 1u) << (4 * (2 * b + s) + (j >> 1) + 16 * (j & 1));
+                }
+        }
+        plane[((t * G + g) * 64 + kq * 16 + i) * 2 + (nb >> 1)] = wd;
+    }
+}
+
+// W3: u = c + 4 = 4 hi + lo; lo (2 bits) to a 2-bit plane, hi (1 bit) to a
+// 1-bit plane.  W2: c = u - 1 in sign-magnitude to one 2-bit plane.  Padding
+// rows get code 0.
+__global__ __launch_bounds__(256) void pack3_kernel(const uint8_t* __restrict__ codes,
+                                                    const uint16_t* __restrict__ scales, int64_t N, int64_t K,
+                                                    int64_t Npad, uint32_t* __restrict__ hi, uint32_t* __restrict__ lo,
+                                                    uint16_t* __restrict__ pscales) {
+    const int64_t G = K / 64;
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= Npad * G) return;
+    const int64_t n = id / G, g = id % G;
+    write_plane2(codes, N, K, n, g, 0, 4u, false, lo);
+    write_plane1(codes, N, K, n, g, 2, 4u, hi);
+    pscales[packed_scale(n, g, G)] = (n < N) ? scales[n * G + g] : (uint16_t)0;
+}
+
+__global__ __launch_bounds__(256) void pack2_kernel(const uint8_t* __restrict__ codes,
+                                                    const uint16_t* __restrict__ scales, int64_t N, int64_t K,
+                                                    int64_t Npad, uint32_t* __restrict__ plane,
+                                                    uint16_t* __restrict__ pscales) {
+    const int64_t G = K / 64;
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= Npad * G) return;
+    const int64_t n = id / G, g = id % G;
+    write_plane2(codes, N, K, n, g, 0, 1u, true, plane);
+    pscales[packed_scale(n, g, G)] = (n < N) ? scales[n * G + g] : (uint16_t)0;
+}
+
 __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict__ packed,
                                                      const uint16_t* __restrict__ pscales, int64_t N, int64_t K,
                                                      uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
@@ -454,6 +527,79 @@ int vw4_w5_pack(const uint8_t* codes_dev, const uint16_t* scales_dev, int64_t N,
     hipLaunchKernelGGL(pack5_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
                        codes_dev, scales_dev, N, K, Np, (uint32_t*)hi_dev, (uint32_t*)lo_dev, packed_scales_dev);
     return check_launch("vw4_w5_pack");
+}
+
+// The b-bit symmetric recipe on the host: scale = fp16(absmax / qmax), codes
+// against the rounded scale (binary32 division, half-even), clamped to
+// [-qmax, qmax], stored as c + bias.
+static int quantize_sym_host(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales, float qmax,
+                             int bias) {
+    int rc = check_shape(N, K);
+    if (rc) return rc;
+    VW4_REQUIRE(w && codes && scales, VW4_EINVAL, "null pointer");
+    const int64_t G = K / 64;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < G; ++g) {
+            const float* wg = w + n * K + g * 64;
+            float a = 0.0f;
+            for (int k = 0; k < 64; ++k) a = fmaxf(a, fabsf(wg[k]));
+            const uint16_t s16 = host_f32_to_f16(a / qmax);
+            const float sf = host_f16_to_f32(s16);
+            scales[n * G + g] = s16;
+            for (int k = 0; k < 64; ++k) {
+                const int c = sf != 0.0f ? (int)fminf(fmaxf(rintf(wg[k] / sf), -qmax), qmax) : 0;
+                codes[n * K + g * 64 + k] = (uint8_t)(c + bias);
+            }
+        }
+    }
+    return VW4_OK;
+}
+
+int vw4_w3_quantize_host(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales) {
+    return quantize_sym_host(w, N, K, codes, scales, 3.0f, 4);
+}
+
+int vw4_w2_quantize_host(const float* w, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales) {
+    return quantize_sym_host(w, N, K, codes, scales, 1.0f, 1);
+}
+
+size_t vw4_w3_hi_plane_bytes(int64_t N, int64_t K) {
+    if (check_shape(N, K)) return 0;
+    return (size_t)(pad64(N) * (K / 8));
+}
+
+size_t vw4_w3_lo_plane_bytes(int64_t N, int64_t K) {
+    if (check_shape(N, K)) return 0;
+    return (size_t)(pad64(N) * (K / 4));
+}
+
+size_t vw4_w2_packed_bytes(int64_t N, int64_t K) {
+    if (check_shape(N, K)) return 0;
+    return (size_t)(pad64(N) * (K / 4));
+}
+
+int vw4_w3_pack(const uint8_t* codes_dev, const uint16_t* scales_dev, int64_t N, int64_t K, uint8_t* hi_dev,
+                uint8_t* lo_dev, uint16_t* packed_scales_dev, void* stream) {
+    int rc = check_shape(N, K);
+    if (rc) return rc;
+    VW4_REQUIRE(codes_dev && scales_dev && hi_dev && lo_dev && packed_scales_dev, VW4_EINVAL, "null pointer");
+    VW4_REQUIRE(aligned(hi_dev, 16) && aligned(lo_dev, 16), VW4_EINVAL, "packed planes must be 16-byte aligned");
+    const int64_t Np = pad64(N), total = Np * (K / 64);
+    hipLaunchKernelGGL(pack3_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                       codes_dev, scales_dev, N, K, Np, (uint32_t*)hi_dev, (uint32_t*)lo_dev, packed_scales_dev);
+    return check_launch("vw4_w3_pack");
+}
+
+int vw4_w2_pack(const uint8_t* codes_dev, const uint16_t* scales_dev, int64_t N, int64_t K, uint8_t* packed_dev,
+                uint16_t* packed_scales_dev, void* stream) {
+    int rc = check_shape(N, K);
+    if (rc) return rc;
+    VW4_REQUIRE(codes_dev && scales_dev && packed_dev && packed_scales_dev, VW4_EINVAL, "null pointer");
+    VW4_REQUIRE(aligned(packed_dev, 16), VW4_EINVAL, "packed plane must be 16-byte aligned");
+    const int64_t Np = pad64(N), total = Np * (K / 64);
+    hipLaunchKernelGGL(pack2_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                       codes_dev, scales_dev, N, K, Np, (uint32_t*)packed_dev, packed_scales_dev);
+    return check_launch("vw4_w2_pack");
 }
 
 size_t vw4_w6_hi_plane_bytes(int64_t N, int64_t K) {

@@ -88,6 +88,84 @@ class W8Linear:
         return self.N * self.K + self.N * (self.K // 64) * 2
 
 
+class W3Linear:
+    """A [N][K] matrix in the W3 format (3-bit codes, fp16 scale per 64 K): the
+    1-bit high plane, the 2-bit low plane and the packed scales."""
+
+    def __init__(self, hi, lo, pscales, N: int, K: int):
+        self.hi, self.lo, self.pscales, self.N, self.K = hi, lo, pscales, N, K
+
+    @classmethod
+    def from_codes(cls, codes, scales, stream=None):
+        """codes: uint8 device [N][K] (c + 4); scales: int16 device [N][K/64] (fp16 bits)."""
+        import torch
+        N, K = codes.shape
+        _, sb = B.packed_sizes(N, K)
+        cb = int(B.lib().vw4_w3_lo_plane_bytes(N, K))
+        hb = int(B.lib().vw4_w3_hi_plane_bytes(N, K))
+        hi = torch.empty(hb, dtype=torch.uint8, device=codes.device)
+        lo = torch.empty(cb, dtype=torch.uint8, device=codes.device)
+        ps = torch.empty(sb // 2, dtype=torch.int16, device=codes.device)
+        B.w3_pack(codes, scales, N, K, hi, lo, ps, stream)
+        return cls(hi, lo, ps, N, K)
+
+    @classmethod
+    def from_fp32(cls, w, device="cuda"):
+        import torch
+        wn = w.detach().cpu().numpy() if hasattr(w, "detach") else w
+        codes, scales = B.w3_quantize_host(wn)
+        return cls.from_codes(torch.from_numpy(codes).to(device), torch.from_numpy(scales.view("int16")).to(device))
+
+    @classmethod
+    def random(cls, N: int, K: int, gen, device="cuda"):
+        """Uniform codes in [-3, 3] and fp16 scales in [4e-4, 1.2e-3] (timing inputs)."""
+        import torch
+        codes = torch.randint(1, 8, (N, K), generator=gen, device=device, dtype=torch.int32).to(torch.uint8)
+        scales = (4e-4 + 8e-4 * torch.rand((N, K // 64), generator=gen, device=device)).to(torch.float16)
+        return cls.from_codes(codes, scales.view(torch.int16))
+
+    def nbytes(self) -> int:
+        return self.N * self.K * 3 // 8 + self.N * (self.K // 64) * 2
+
+
+class W2Linear:
+    """A [N][K] matrix in the W2 format (2-bit codes, fp16 scale per 64 K): one
+    2-bit plane and the packed scales."""
+
+    def __init__(self, packed, pscales, N: int, K: int):
+        self.packed, self.pscales, self.N, self.K = packed, pscales, N, K
+
+    @classmethod
+    def from_codes(cls, codes, scales, stream=None):
+        """codes: uint8 device [N][K] (c + 1); scales: int16 device [N][K/64] (fp16 bits)."""
+        import torch
+        N, K = codes.shape
+        _, sb = B.packed_sizes(N, K)
+        pb = int(B.lib().vw4_w2_packed_bytes(N, K))
+        packed = torch.empty(pb, dtype=torch.uint8, device=codes.device)
+        ps = torch.empty(sb // 2, dtype=torch.int16, device=codes.device)
+        B.w2_pack(codes, scales, N, K, packed, ps, stream)
+        return cls(packed, ps, N, K)
+
+    @classmethod
+    def from_fp32(cls, w, device="cuda"):
+        import torch
+        wn = w.detach().cpu().numpy() if hasattr(w, "detach") else w
+        codes, scales = B.w2_quantize_host(wn)
+        return cls.from_codes(torch.from_numpy(codes).to(device), torch.from_numpy(scales.view("int16")).to(device))
+
+    @classmethod
+    def random(cls, N: int, K: int, gen, device="cuda"):
+        """Uniform codes in [-1, 1] and fp16 scales in [4e-4, 1.2e-3] (timing inputs)."""
+        import torch
+        codes = torch.randint(0, 3, (N, K), generator=gen, device=device, dtype=torch.int32).to(torch.uint8)
+        scales = (4e-4 + 8e-4 * torch.rand((N, K // 64), generator=gen, device=device)).to(torch.float16)
+        return cls.from_codes(codes, scales.view(torch.int16))
+
+    def nbytes(self) -> int:
+        return self.N * self.K // 4 + self.N * (self.K // 64) * 2
+
+
 class W5Linear:
     """A [N][K] matrix in the W5 format (5-bit codes, fp16 scale per 64 K): the
     1-bit high plane, the 4-bit low plane (W4 layout) and the packed scales."""
