@@ -109,6 +109,7 @@ def lib():
         L.oracle_w8_gemm.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P]
         L.oracle_w5_quantize.argtypes = [_P, _I64, _I64, _P, _P]
         L.oracle_w5_gemm.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P]
+        L.oracle_f16_gemm.argtypes = [_P, _I64, _I64, _P, _I64, _P]
         L.oracle_w3_quantize.argtypes = [_P, _I64, _I64, _P, _P]
         L.oracle_w3_gemm.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P]
         L.oracle_w2_quantize.argtypes = [_P, _I64, _I64, _P, _P]
@@ -458,6 +459,18 @@ def w5_gemm(x_bf16: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> np.nda
     y = np.zeros((M, N), dtype=np.float64)
     lib().oracle_w5_gemm(_ptr(x_bf16), M, K, _ptr(np.ascontiguousarray(codes)), _ptr(np.ascontiguousarray(scales)),
                          N, _ptr(y))
+    return y
+
+
+def f16_gemm(x_bf16: np.ndarray, w_f16: np.ndarray) -> np.ndarray:
+    """x_bf16: uint16 [M][K]; w_f16: uint16 [N][K] (fp16 bit patterns); returns float64 [M][N]."""
+    x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    w_f16 = np.ascontiguousarray(w_f16, dtype=np.uint16)
+    M, K = x_bf16.shape
+    N = w_f16.shape[0]
+    assert w_f16.shape == (N, K)
+    y = np.zeros((M, N), dtype=np.float64)
+    lib().oracle_f16_gemm(_ptr(x_bf16), M, K, _ptr(w_f16), N, _ptr(y))
     return y
 
 
