@@ -110,6 +110,7 @@ def lib():
         L.oracle_w5_quantize.argtypes = [_P, _I64, _I64, _P, _P]
         L.oracle_w5_gemm.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P]
         L.oracle_f16_gemm.argtypes = [_P, _I64, _I64, _P, _I64, _P]
+        L.oracle_b16_gemm.argtypes = [_P, _I64, _I64, _P, _I64, _P]
         L.oracle_w3_quantize.argtypes = [_P, _I64, _I64, _P, _P]
         L.oracle_w3_gemm.argtypes = [_P, _I64, _I64, _P, _P, _I64, _P]
         L.oracle_w2_quantize.argtypes = [_P, _I64, _I64, _P, _P]
@@ -471,6 +472,18 @@ def f16_gemm(x_bf16: np.ndarray, w_f16: np.ndarray) -> np.ndarray:
     assert w_f16.shape == (N, K)
     y = np.zeros((M, N), dtype=np.float64)
     lib().oracle_f16_gemm(_ptr(x_bf16), M, K, _ptr(w_f16), N, _ptr(y))
+    return y
+
+
+def b16_gemm(x_bf16: np.ndarray, w_bf16: np.ndarray) -> np.ndarray:
+    """x_bf16: uint16 [M][K]; w_bf16: uint16 [N][K] (bf16 bit patterns); returns float64 [M][N]."""
+    x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    w_bf16 = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    M, K = x_bf16.shape
+    N = w_bf16.shape[0]
+    assert w_bf16.shape == (N, K)
+    y = np.zeros((M, N), dtype=np.float64)
+    lib().oracle_b16_gemm(_ptr(x_bf16), M, K, _ptr(w_bf16), N, _ptr(y))
     return y
 
 

@@ -746,7 +746,8 @@ EXPORT void oracle_w5_gemm(const uint16_t* x_bf16, int64_t M, int64_t K, const u
 
 /* ------------------------------------------------------------------------ */
 /* The widest format of the same BaseRT list (Q2 ... FP16): unquantised fp16  */
-/* weights, w[N][K] as IEEE binary16 bit patterns, no scales.                 */
+/* weights, w[N][K] as IEEE binary16 bit patterns, no scales; and the same    */
+/* with bf16 weights (the 16-bit float type of bf16 checkpoints).             */
 /* y[m][n] = sum_k x[m][k] * w[n][k], fp64, sequential in k.                  */
 /* ------------------------------------------------------------------------ */
 EXPORT void oracle_f16_gemm(const uint16_t* x_bf16, int64_t M, int64_t K, const uint16_t* w_f16, int64_t N,
@@ -756,6 +757,18 @@ EXPORT void oracle_f16_gemm(const uint16_t* x_bf16, int64_t M, int64_t K, const 
         for (int64_t m = 0; m < M; ++m) {
             double acc = 0.0;
             for (int64_t k = 0; k < K; ++k) acc += bf16_value(x_bf16[m * K + k]) * f16_value(w_f16[n * K + k]);
+            y[m * N + n] = acc;
+        }
+    }
+}
+
+EXPORT void oracle_b16_gemm(const uint16_t* x_bf16, int64_t M, int64_t K, const uint16_t* w_bf16, int64_t N,
+                            double* y /* [M][N] */) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += bf16_value(x_bf16[m * K + k]) * bf16_value(w_bf16[n * K + k]);
             y[m * N + n] = acc;
         }
     }
