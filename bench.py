@@ -834,6 +834,8 @@ def layer_linears_w8_cpu_baseline(reps=4, fmt="w8"):
     """The CPU oracle's W8 (or W6, W5, W3, W2) GEMM on the four linears of one layer at M=4 (fp64), reps row sets."""
     import oracle
     from verify_step_w4_amd import synth
+    if fmt in ("f16", "bf16"):
+        return layer_linears_w16_cpu_baseline(fmt, reps)
     quant, gemm = {"w8": (oracle.w8_quantize, oracle.w8_gemm), "w6": (oracle.w6_quantize, oracle.w6_gemm),
                    "w5": (oracle.w5_quantize, oracle.w5_gemm), "w3": (oracle.w3_quantize, oracle.w3_gemm),
                    "w2": (oracle.w2_quantize, oracle.w2_gemm)}[fmt]
@@ -850,6 +852,27 @@ def layer_linears_w8_cpu_baseline(reps=4, fmt="w8"):
     return {"value": round(reps / tot, 4), "unit": "layer passes/s", "cores": cores, "kind": "oracle",
             "sample": f"one 27B-class layer's four {fmt.upper()} GEMMs at M=4 on {reps} row sets; "
                       "quantisation untimed"}
+
+
+def layer_linears_w16_cpu_baseline(fmt, reps=4):
+    """The CPU oracle's fp16 (or bf16) weight GEMM on the four linears of one layer at M=4 (fp64)."""
+    import numpy as np
+
+    import oracle
+    from verify_step_w4_amd import synth
+    g = synth.rng(synth.SEED_BASE + 9)
+    tot = 0.0
+    for N, K in [(7168, 5120), (5120, 5120), (34816, 5120), (5120, 17408)]:
+        w = synth.normal_f32(g, (N, K), 0.02)
+        bits = w.astype(np.float16).view(np.uint16) if fmt == "f16" else synth.f32_to_bf16_bits(w)
+        for r in range(reps):
+            x = synth.f32_to_bf16_bits(synth.normal_f32(g, (4, K), 1.0))
+            t0 = time.perf_counter()
+            (oracle.f16_gemm if fmt == "f16" else oracle.b16_gemm)(x, bits)
+            tot += time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(reps / tot, 4), "unit": "layer passes/s", "cores": cores, "kind": "oracle",
+            "sample": f"one 27B-class layer's four {fmt.upper()}-weight GEMMs at M=4 on {reps} row sets"}
 
 
 def verify27b_cpu_baseline(context=8192, M=4):
@@ -1218,36 +1241,51 @@ def layer_linears_w2_workload(args):
     return layer_linears_w8_workload(args, fmt="w2")
 
 
+def layer_linears_f16_workload(args):
+    return layer_linears_w8_workload(args, fmt="f16")
+
+
+def layer_linears_bf16_workload(args):
+    return layer_linears_w8_workload(args, fmt="bf16")
+
+
 def layer_linears_w8_workload(args, fmt="w8"):
     """The same four linears of one 27B-shaped layer in the W8 format (int8
     codes, fp16 scale per 64 K: 1.03125 bytes per weight, 351 MB per layer),
     or the W6 (0.78125 bytes per weight), W5 (0.65625), W3 (0.40625) or W2
-    (0.28125) format; plain GEMM
+    (0.28125) format, or unquantised fp16 / bf16 (2 bytes, no scales; 2
+    layers rotated, 1.5 GB); plain GEMM
     outputs (gate|up as one [34816][5120] product); 4 layers' weights rotated.
     A step is one pass over a layer's four linears at M = 4."""
     import torch
 
     from verify_step_w4_amd import binding as B
-    from verify_step_w4_amd.model import W2Linear, W3Linear, W5Linear, W6Linear, W8Linear
+    from verify_step_w4_amd.model import W2Linear, W3Linear, W5Linear, W6Linear, W8Linear, W16Linear
 
     d, F, nqkv = 5120, 17408, 7168
-    nlay = 4
+    w16 = fmt in ("f16", "bf16")
+    nlay = 2 if w16 else 4
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20261209)
     shapes = {"qkv": (nqkv, d), "o": (d, d), "gate_up": (2 * F, d), "down": (d, F)}
-    Lin = {"w8": W8Linear, "w6": W6Linear, "w5": W5Linear, "w3": W3Linear, "w2": W2Linear}[fmt]
-    code_bytes = {"w8": 1.0, "w6": 0.75, "w5": 0.625, "w3": 0.375, "w2": 0.25}[fmt]
+    Lin = {"w8": W8Linear, "w6": W6Linear, "w5": W5Linear, "w3": W3Linear, "w2": W2Linear}.get(fmt)
+    code_bytes = {"w8": 1.0, "w6": 0.75, "w5": 0.625, "w3": 0.375, "w2": 0.25, "f16": 2.0, "bf16": 2.0}[fmt]
     two_plane = {"w8": B.w8_skinny_gemm, "w6": B.w6_skinny_gemm, "w5": B.w5_skinny_gemm, "w3": B.w3_skinny_gemm}
 
     def gemm(x, L, y, M, N, K, ws):
-        if fmt == "w2":
+        if w16:
+            B.w16_skinny_gemm(x, L.packed, y, M, N, K, kind=fmt, ws=ws)
+        elif fmt == "w2":
             B.w2_skinny_gemm(x, L.packed, L.pscales, y, M, N, K, ws=ws)
         else:
             two_plane[fmt](x, L.hi, L.lo, L.pscales, y, M, N, K, ws=ws)
     wsb = {"w8": B.w8_workspace_bytes, "w6": B.w6_workspace_bytes, "w5": B.w5_workspace_bytes,
-           "w3": B.w3_workspace_bytes, "w2": B.w2_workspace_bytes}[fmt]
+           "w3": B.w3_workspace_bytes, "w2": B.w2_workspace_bytes,
+           "f16": lambda M, N, K: B.w16_workspace_bytes(M, N, K, "f16"),
+           "bf16": lambda M, N, K: B.w16_workspace_bytes(M, N, K, "bf16")}[fmt]
     log(f"generating {nlay} layers of {fmt.upper()} linears")
-    layers = [{nm: Lin.random(N, K, gen) for nm, (N, K) in shapes.items()} for _ in range(nlay)]
+    mk = (lambda N, K: W16Linear.random(N, K, gen, fmt)) if w16 else (lambda N, K: Lin.random(N, K, gen))
+    layers = [{nm: mk(N, K) for nm, (N, K) in shapes.items()} for _ in range(nlay)]
     M = 4
     xs = {K: torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16) for K in (d, F)}
     ys = {nm: torch.empty((M, N), dtype=torch.float32, device="cuda") for nm, (N, K) in shapes.items()}
@@ -1264,7 +1302,7 @@ def layer_linears_w8_workload(args, fmt="w8"):
 
     def alg(nm):
         N, K = shapes[nm]
-        return int(N * K * code_bytes) + N * (K // 64) * 2 + M * K * 2 + M * N * 4
+        return int(N * K * code_bytes) + (0 if w16 else N * (K // 64) * 2) + M * K * 2 + M * N * 4
 
     reps = max(1, args.steps // nlay)
     ms_launch, n_launch = time_graphs([issue], reps)
@@ -1286,7 +1324,9 @@ def layer_linears_w8_workload(args, fmt="w8"):
                             "w6": "6-bit group-64 symmetric, fp16 scales (2-bit + 4-bit planes)",
                             "w5": "5-bit group-64 symmetric, fp16 scales (1-bit + 4-bit planes)",
                             "w3": "3-bit group-64 symmetric, fp16 scales (1-bit + 2-bit planes)",
-                            "w2": "2-bit group-64 symmetric (codes -1..1), fp16 scales (one 2-bit plane)"}[fmt]},
+                            "w2": "2-bit group-64 symmetric (codes -1..1), fp16 scales (one 2-bit plane)",
+                            "f16": "fp16, unquantised (exact two-part bf16 split on the matrix cores)",
+                            "bf16": "bf16, unquantised"}[fmt]},
         roofline={"bound": "hbm", "achieved": round(lb / (layer_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
                   "unit": "GB/s", "frac": round(lb / (layer_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
                   "kernel": f"{fmt}_gemm_kernel (+ {fmt}_reduce_kernel; the four linears of a layer at M=4, "
@@ -1393,7 +1433,9 @@ WORKLOADS = {"lm_head_verify": (lm_head_workload, lm_head_cpu_baseline),
              "layer_linears_w6": (layer_linears_w6_workload, lambda: layer_linears_w8_cpu_baseline(fmt="w6")),
              "layer_linears_w5": (layer_linears_w5_workload, lambda: layer_linears_w8_cpu_baseline(fmt="w5")),
              "layer_linears_w3": (layer_linears_w3_workload, lambda: layer_linears_w8_cpu_baseline(fmt="w3")),
-             "layer_linears_w2": (layer_linears_w2_workload, lambda: layer_linears_w8_cpu_baseline(fmt="w2"))}
+             "layer_linears_w2": (layer_linears_w2_workload, lambda: layer_linears_w8_cpu_baseline(fmt="w2")),
+             "layer_linears_f16": (layer_linears_f16_workload, lambda: layer_linears_w8_cpu_baseline(fmt="f16")),
+             "layer_linears_bf16": (layer_linears_bf16_workload, lambda: layer_linears_w8_cpu_baseline(fmt="bf16"))}
 
 
 def main():
@@ -1445,7 +1487,7 @@ def main():
               "verify_over_ar", "step_hbm_gbs", "experts_per_step", "grouped_gemm_gbs", "m_sweep", "unit_note",
               "context_sweep", "stats_accept_sweep", "sustained", "attention_by_context", "spec_loop",
               "w8_gemm_by_linear", "w6_gemm_by_linear", "w5_gemm_by_linear", "w3_gemm_by_linear",
-              "w2_gemm_by_linear"):
+              "w2_gemm_by_linear", "f16_gemm_by_linear", "bf16_gemm_by_linear"):
         if k in res:
             out[k] = res[k]
     if not args.no_cpu_baseline:

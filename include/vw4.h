@@ -476,6 +476,44 @@ VW4_API int w8_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_
                                     void* stream);
 
 /* ------------------------------------------------------------------------
+ * Unquantised 16-bit float weights: the widest end of the same BaseRT list
+ * (Q2 ... FP16), as fp16 and as bf16.  w[N][K] holds IEEE binary16 (fp16)
+ * or bfloat16 bit patterns; there are no scales.
+ *
+ * vw4_w16_pack: w (device, [N][K] row-major) -> the operand-tiled layout
+ * (vw4_w16_packed_bytes(N, K) = pad64(N) * K * 2 bytes, 16-byte aligned):
+ * per 64-row tile t and K-group g 8 KiB, the 16-byte word
+ * ((t * K/64 + g) * 8 + 2 nb + s) * 64 + 16 kq + i holding row
+ * 64 t + 16 nb + i at k = 64 g + 32 s + 8 kq + 0..7; padding rows are zero.
+ * The same pack serves both types.
+ *
+ * f16_skinny_gemm / bf16_skinny_gemm: y = x @ W^T with the conventions of
+ * w4_skinny_gemm (x bf16 [M][ldx], ldx >= K, ldx % 8 == 0, 16-byte aligned;
+ * y fp32 or bf16 [M][ldy]; M in 1..8, K % 64 == 0 and K <= 65536; a
+ * workspace of at least vw4_{f16,bf16}_workspace_bytes(M, N, K) bytes,
+ * 256-byte aligned, when that is not 0, else VW4_EWORKSPACE).  fp16 weights
+ * are split exactly into two bf16 parts, so every product is exact in fp32;
+ * sums are fp32.  The partials calls write S slices of [M][ldp] fp32 sums
+ * (vw4_{f16,bf16}_partials_layout) that add up, in slice order, to y.
+ * ------------------------------------------------------------------------ */
+VW4_API size_t vw4_w16_packed_bytes(int64_t N, int64_t K);
+VW4_API int vw4_w16_pack(const uint16_t* w, int64_t N, int64_t K, uint8_t* packed, void* stream);
+VW4_API size_t vw4_f16_workspace_bytes(int32_t M, int32_t N, int32_t K);
+VW4_API size_t vw4_bf16_workspace_bytes(int32_t M, int32_t N, int32_t K);
+VW4_API int f16_skinny_gemm(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, void* y, int64_t ldy,
+                            int32_t y_dtype, int32_t M, int32_t N, int32_t K, void* ws, size_t ws_bytes,
+                            void* stream);
+VW4_API int bf16_skinny_gemm(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, void* y, int64_t ldy,
+                             int32_t y_dtype, int32_t M, int32_t N, int32_t K, void* ws, size_t ws_bytes,
+                             void* stream);
+VW4_API int vw4_f16_partials_layout(int32_t M, int32_t N, int32_t K, int32_t* S, int64_t* ldp);
+VW4_API int vw4_bf16_partials_layout(int32_t M, int32_t N, int32_t K, int32_t* S, int64_t* ldp);
+VW4_API int f16_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, float* part,
+                                     int32_t M, int32_t N, int32_t K, void* stream);
+VW4_API int bf16_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, float* part,
+                                      int32_t M, int32_t N, int32_t K, void* stream);
+
+/* ------------------------------------------------------------------------
  * The narrowest weight formats: W3 and W2 (the same BaseRT section lists Q2
  * ... Q8; no layout).  Per row n and 64-element group g: scale =
  * fp16_rne(absmax / qmax), c_k = clamp(rint(w_k / scale), -qmax, qmax) with

@@ -183,6 +183,21 @@ def test_w8_partials_layout_and_validation():
     assert _call("w8_skinny_gemm_partials", fake, 64, fake, fake, fake, None, 1, 64, 64, None) == B.VW4_EINVAL
 
 
+def test_w16_sizes_and_validation():
+    assert B.lib().vw4_w16_packed_bytes(100, 320) == 128 * 320 * 2
+    assert B.lib().vw4_w16_packed_bytes(10, 100) == 0
+    for kind in ("f16", "bf16"):
+        assert B.w16_workspace_bytes(9, 64, 64, kind) == 0
+        assert B.w16_workspace_bytes(4, 5120, 5120, kind) == B.gemm_workspace_bytes(4, 5120, 5120)
+        assert B.w16_partials_layout(4, 5120, 5120, kind) == B.w16_partials_layout(1, 5120, 5120, kind)
+        fake = ctypes.c_void_p(0x100000)
+        assert _call(f"{kind}_skinny_gemm", fake, 64, fake, fake, 64, 0, 9, 64, 64, None, 0, None) == B.VW4_EINVAL
+        assert _call(f"{kind}_skinny_gemm", fake, 64, None, fake, 64, 0, 1, 64, 64, None, 0, None) == B.VW4_EINVAL
+        assert _call(f"{kind}_skinny_gemm", fake, 64, fake, fake, 64, 0, 1, 64, 100, None, 0, None) == B.VW4_EINVAL
+        assert _call(f"{kind}_skinny_gemm_partials", fake, 64, fake, None, 1, 64, 64, None) == B.VW4_EINVAL
+    assert _call("vw4_w16_pack", None, 64, 64, ctypes.c_void_p(0x100000), None) == B.VW4_EINVAL
+
+
 @pytest.mark.parametrize("b", [3, 2])
 def test_w3_w2_host_quantizers_match_oracle_and_sizes(b):
     rng = np.random.default_rng(20 + b)

@@ -72,6 +72,18 @@ SIGNATURES = {
     "vw4_w8_partials_layout": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
                                               ctypes.POINTER(ctypes.c_int64)]),
     "w8_skinny_gemm_partials": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
+    "vw4_w16_packed_bytes": (_SZ, [_I64, _I64]),
+    "vw4_w16_pack": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
+    "vw4_f16_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "vw4_bf16_workspace_bytes": (_SZ, [_I32, _I32, _I32]),
+    "f16_skinny_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+    "bf16_skinny_gemm": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+    "vw4_f16_partials_layout": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
+                                               ctypes.POINTER(ctypes.c_int64)]),
+    "vw4_bf16_partials_layout": (ctypes.c_int, [_I32, _I32, _I32, ctypes.POINTER(ctypes.c_int32),
+                                                ctypes.POINTER(ctypes.c_int64)]),
+    "f16_skinny_gemm_partials": (ctypes.c_int, [_P, _I64, _P, _P, _I32, _I32, _I32, _P]),
+    "bf16_skinny_gemm_partials": (ctypes.c_int, [_P, _I64, _P, _P, _I32, _I32, _I32, _P]),
     "vw4_w3_quantize_host": (ctypes.c_int, [_P, _I64, _I64, _P, _P]),
     "vw4_w3_hi_plane_bytes": (_SZ, [_I64, _I64]),
     "vw4_w3_lo_plane_bytes": (_SZ, [_I64, _I64]),
@@ -419,6 +431,46 @@ def w8_skinny_gemm_partials(x, w_hi, w_lo, scales_packed, part, M: int, N: int, 
     _check("w8_skinny_gemm_partials", lib().w8_skinny_gemm_partials(_ptr(x), ldx, _ptr(w_hi), _ptr(w_lo),
                                                                     _ptr(scales_packed), _ptr(part), M, N, K,
                                                                     _stream(stream)))
+
+
+def w16_pack(w, N: int, K: int, packed, stream=None):
+    """16-bit weights (fp16 or bf16 bit patterns, device [N][K]) -> the operand-tiled layout."""
+    _check("vw4_w16_pack", lib().vw4_w16_pack(_ptr(w), N, K, _ptr(packed), _stream(stream)))
+
+
+def w16_workspace_bytes(M: int, N: int, K: int, kind: str = "f16") -> int:
+    return int(getattr(lib(), f"vw4_{kind}_workspace_bytes")(M, N, K))
+
+
+def w16_partials_layout(M: int, N: int, K: int, kind: str = "f16"):
+    S, ldp = ctypes.c_int32(0), ctypes.c_int64(0)
+    name = f"vw4_{kind}_partials_layout"
+    _check(name, getattr(lib(), name)(M, N, K, ctypes.byref(S), ctypes.byref(ldp)))
+    return int(S.value), int(ldp.value)
+
+
+def w16_skinny_gemm(x, w_packed, y, M: int, N: int, K: int, kind: str = "f16", ws=None, stream=None,
+                    ldx: int | None = None, ldy: int | None = None):
+    """y[M][N] (fp32 or bf16 tensor) = x[M][K] (bf16 bits) @ W^T, W fp16 (kind "f16") or bf16 ("bf16")."""
+    import torch
+    assert kind in ("f16", "bf16")
+    ydt = VW4_F32 if y.dtype == torch.float32 else VW4_BF16
+    ldx = x.stride(0) if ldx is None else ldx
+    ldy = y.stride(0) if ldy is None else ldy
+    nbytes = ws.numel() if ws is not None else 0
+    name = f"{kind}_skinny_gemm"
+    _check(name, getattr(lib(), name)(_ptr(x), ldx, _ptr(w_packed), _ptr(y), ldy, ydt, M, N, K, _ptr(ws), nbytes,
+                                      _stream(stream)))
+    return y
+
+
+def w16_skinny_gemm_partials(x, w_packed, part, M: int, N: int, K: int, kind: str = "f16", stream=None,
+                             ldx: int | None = None):
+    assert kind in ("f16", "bf16")
+    ldx = x.stride(0) if ldx is None else ldx
+    name = f"{kind}_skinny_gemm_partials"
+    _check(name, getattr(lib(), name)(_ptr(x), ldx, _ptr(w_packed), _ptr(part), M, N, K, _stream(stream)))
+    return part
 
 
 def w3_quantize_host(w: np.ndarray):

@@ -34,8 +34,9 @@
 //    2-bit plane; W8 splits the 8-bit code into a high and a low 4-bit plane;
 //    W6 into a 2-bit high plane and a 4-bit low plane; W5 into a 1-bit high
 //    plane and a 4-bit low plane; W3 into a 1-bit high plane and a 2-bit low
-//    plane.  Everything else -- lane mapping, pipeline, split plan,
-//    epilogues, reduction -- is one kernel template.
+//    plane; 16-bit float weights (bf16, fp16) are read as whole operands.
+//    Everything else -- lane mapping, pipeline, split plan, epilogues,
+//    reduction -- is one kernel template.
 //  * Split K: S_wg wavefronts of a workgroup take consecutive K slices of the
 //    same tile and are reduced through LDS; when the tiles are too few to fill
 //    the chip, S_grid workgroups per tile write fp32 partials and the consumer
@@ -55,7 +56,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
-constexpr int PF = 4;                          // groups in flight per lane
+constexpr int PF = 4;                          // groups in flight per lane (default)
 constexpr int NORM_MAX_K = 64 * NORM_CHUNK;    // NORM mode: at most 64 chunk sums per row
 
 // (v & mask) | magic in one instruction: gfx950's three-input bitwise op with
@@ -120,6 +121,28 @@ __device__ __forceinline__ void scales4(uint2 sc, float (&f)[4]) {
 struct Planes {
     const u32x4* p0;
     const u32x4* p1;
+};
+
+// Per-format options, read through these traits: PF_GROUPS (groups in flight
+// per lane, default PF) and NO_SCALES (a format without group scales: the
+// kernel loads none and the decoder ignores its scale argument).
+template <class...>
+using void_t = void;
+template <class F, class = void>
+struct FmtPF {
+    static constexpr int v = PF;
+};
+template <class F>
+struct FmtPF<F, void_t<decltype(F::PF_GROUPS)>> {
+    static constexpr int v = F::PF_GROUPS;
+};
+template <class F, class = void>
+struct FmtScaled {
+    static constexpr bool v = true;
+};
+template <class F>
+struct FmtScaled<F, void_t<decltype(F::NO_SCALES)>> {
+    static constexpr bool v = false;
 };
 
 // ---------------------------------------------------------------------------
@@ -379,6 +402,75 @@ struct FmtW3 : TwoPlane<FmtW3> {
     }
 };
 
+// 16-bit float weights, no scales.  Layout (vw4_w16_pack): per 64-row tile
+// and K-group 8 KiB, eight 1 KiB words; word 2 nb + s of lane l = 16 kq + i
+// holds the eight 16-bit weights of row 16 nb + i at k = 32 s + 8 kq + j,
+// j = 0..7 -- exactly the B operand of one row block and k half.  Two groups
+// in flight per lane (16 words, 64 registers).
+//
+// BF16: the words are the B operands as they stand; the products accumulate
+// straight into acc (one matrix-core chain per row block).
+struct FmtB16 {
+    static constexpr int NW = 8;
+    static constexpr int PF_GROUPS = 2;
+    static constexpr bool NO_SCALES = true;
+    __device__ static void base(const Planes& P, int64_t t, int G, int lane, const u32x4*& b0, const u32x4*& b1) {
+        b0 = P.p0 + t * G * 512 + lane;
+        b1 = b0;
+    }
+    __device__ static void load(u32x4 (&w)[NW], const u32x4* b0, const u32x4*, int64_t g) {
+#pragma unroll
+        for (int q = 0; q < NW; ++q) w[q] = __builtin_nontemporal_load(b0 + g * 512 + q * 64);
+    }
+    __device__ static void group(const u32x4 (&w)[NW], bf16x8 a0, bf16x8 a1, uint2, uint32_t, uint32_t,
+                                 f32x4 (&acc)[4]) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+            acc[nb] = mfma16(a1, __builtin_bit_cast(bf16x8, w[2 * nb + 1]),
+                             mfma16(a0, __builtin_bit_cast(bf16x8, w[2 * nb]), acc[nb]));
+    }
+    __host__ __device__ static Planes expert(Planes P, int64_t e, int64_t w_estride) {
+        P.p0 += e * w_estride * 4;
+        return P;
+    }
+};
+
+// FP16: each weight w (11-bit significand) is split exactly into two bf16
+// values, hi = w truncated to 8 significant bits and lo = w - hi (at most 3
+// significant bits, so exact in bf16): hi is the top half of w's binary32
+// form, lo the top half of the binary32 difference.  Both products with the
+// bf16 activations are exact in fp32; the chain adds x . hi, then x . lo.
+// (The word's dwords are copied to scalars first: a bit cast applied to a
+// subscripted element of a vector value was compiled as a read of element 0.)
+__device__ __forceinline__ void split_f16x8(u32x4 w, bf16x8& hi, bf16x8& lo) {
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const float f0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd[d] & 0xFFFFu));
+        const float f1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd[d] >> 16));
+        const uint32_t u0 = __builtin_bit_cast(uint32_t, f0), u1 = __builtin_bit_cast(uint32_t, f1);
+        const float r0 = f0 - __builtin_bit_cast(float, u0 & 0xFFFF0000u);
+        const float r1 = f1 - __builtin_bit_cast(float, u1 & 0xFFFF0000u);
+        h[d] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);   // the high halves of f0 (low), f1 (high)
+        l[d] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, r1), __builtin_bit_cast(uint32_t, r0), 0x07060302u);
+    }
+    hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+}
+struct FmtF16 : FmtB16 {
+    __device__ static void group(const u32x4 (&w)[NW], bf16x8 a0, bf16x8 a1, uint2, uint32_t, uint32_t,
+                                 f32x4 (&acc)[4]) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            bf16x8 h0, l0, h1, l1;
+            split_f16x8(w[2 * nb], h0, l0);
+            split_f16x8(w[2 * nb + 1], h1, l1);
+            acc[nb] = mfma16(a1, l1, mfma16(a0, l0, mfma16(a1, h1, mfma16(a0, h0, acc[nb]))));
+        }
+    }
+};
+
 // Eight activations of one row: h = bf16((r * inv) * gamma) per element, the
 // standalone normalisation's arithmetic in its order.
 __device__ __forceinline__ u32x4 norm8(u32x4 r, u32x4 g, float inv) {
@@ -432,6 +524,7 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(const uint16_t* __rest
                                                           int S_grid, float* __restrict__ part, int64_t Npad,
                                                           uint32_t kmask, uint32_t kmagic, GemmGroup grp,
                                                           NormIn nrm) {
+    constexpr int PFL = FmtPF<Fmt>::v;
     __shared__ float red[4][16][64];     // [wavefront][4 nb + r][lane]
     if (grp.n_slots) {
         const int slot = blockIdx.z;
@@ -483,13 +576,13 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(const uint16_t* __rest
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // PF groups in flight per lane, each in its own registers: the main loop
-    // consumes buffer j and refills it with the group PF further on (clamped to
+    // PFL groups in flight per lane, each in its own registers: the main loop
+    // consumes buffer j and refills it with the group PFL further on (clamped to
     // the slice's last group, so every load address is valid and the loop body
-    // has no branches); the last < PF groups are consumed after the loop.
+    // has no branches); the last < PFL groups are consumed after the loop.
     const int glast = g1 > g0 ? g1 - 1 : g0;
-    u32x4 bw[PF][Fmt::NW], bx0[PF], bx1[PF], bg0[PF], bg1[PF];
-    uint2 bs[PF];
+    u32x4 bw[PFL][Fmt::NW], bx0[PFL], bx1[PFL], bg0[PFL], bg1[PFL];
+    uint2 bs[PFL];
     auto issue = [&](int j, int gi) {
         Fmt::load(bw[j], wb0, wb1, gi);
         bx0[j] = xbase[(int64_t)gi * 8];
@@ -498,16 +591,17 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(const uint16_t* __rest
             bg0[j] = gbase[(int64_t)gi * 8];
             bg1[j] = gbase[(int64_t)gi * 8 + 4];
         }
-        bs[j] = sbase[(int64_t)gi * 16];
+        if (FmtScaled<Fmt>::v) bs[j] = sbase[(int64_t)gi * 16];
+        else bs[j] = uint2{0u, 0u};
     };
     // g0 < G always (S <= G), so these addresses are valid even for an empty
     // slice.  The prologue issues group by group, in the order the loop
-    // refills: the wait counts at the loop head then leave PF - 1 groups in
+    // refills: the wait counts at the loop head then leave PFL - 1 groups in
     // flight.  (Prologue loads split around a branch -- weight words in one
     // block, activations and scales in the next -- made the compiler wait for
     // most of the prefetch at every loop head: 14 % slower on the 27B layer.)
 #pragma unroll
-    for (int j = 0; j < PF; ++j) issue(j, min(g0 + j, glast));
+    for (int j = 0; j < PFL; ++j) issue(j, min(g0 + j, glast));
     __builtin_amdgcn_sched_barrier(0);
 
     // NORM, part 2: the chunk sums (at most 64: K <= 64 * NORM_CHUNK) added in
@@ -539,19 +633,19 @@ __global__ __launch_bounds__(256) void skinny_gemm_kernel(const uint16_t* __rest
     // (an empty slice, g0 == g1, runs neither loop; no branch guards them, so
     // that the prologue's loads stay together ahead of the loop)
     int g = g0;
-    for (; g + PF <= g1; g += PF) {
+    for (; g + PFL <= g1; g += PFL) {
 #pragma unroll
-        for (int j = 0; j < PF; ++j) {
+        for (int j = 0; j < PFL; ++j) {
             consume(j);
             // keep the refill right after its buffer's last use: the
             // scheduler would otherwise sink all refills to the loop end
             __builtin_amdgcn_sched_barrier(0);
-            issue(j, min(g + j + PF, glast));
+            issue(j, min(g + j + PFL, glast));
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
-    for (int j = 0; j < PF - 1; ++j)
+    for (int j = 0; j < PFL - 1; ++j)
         if (g + j < g1) consume(j);
 
     // Reduce the S_wg slices of this workgroup in slice order.

@@ -332,6 +332,30 @@ __global__ __launch_bounds__(256) void pack2_kernel(const uint8_t* __restrict__ 
     pscales[packed_scale(n, g, G)] = (n < N) ? scales[n * G + g] : (uint16_t)0;
 }
 
+// 16-bit float weights (bf16 or fp16 bit patterns, [N][K] row-major) to the
+// operand-tiled layout: per 64-row tile and K-group 8 KiB, word 2 nb + s of
+// lane l = 16 kq + i (16-byte index ((t G + g) * 8 + 2 nb + s) * 64 + l)
+// holding row 16 nb + i at k = 32 s + 8 kq + 0..7.  One thread per (n, g)
+// writes its row's eight 16-byte words; padding rows are zero.
+__global__ __launch_bounds__(256) void pack16_kernel(const uint16_t* __restrict__ w, int64_t N, int64_t K,
+                                                     int64_t Npad, uint4* __restrict__ out) {
+    const int64_t G = K / 64;
+    const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (id >= Npad * G) return;
+    const int64_t n = id / G, g = id % G, t = n >> 6;
+    const int i = (int)(n & 15), nb = (int)((n >> 4) & 3);
+    for (int s = 0; s < 2; ++s)
+        for (int kq = 0; kq < 4; ++kq) {
+            uint32_t d[4];
+            for (int p = 0; p < 4; ++p) {
+                const int64_t k = g * 64 + 32 * s + 8 * kq + 2 * p;
+                const uint32_t lo = (n < N) ? w[n * K + k] : 0u, hi = (n < N) ? w[n * K + k + 1] : 0u;
+                d[p] = lo | (hi << 16);
+            }
+            out[((t * G + g) * 8 + 2 * nb + s) * 64 + 16 * kq + i] = make_uint4(d[0], d[1], d[2], d[3]);
+        }
+}
+
 __global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* __restrict__ packed,
                                                      const uint16_t* __restrict__ pscales, int64_t N, int64_t K,
                                                      uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
@@ -600,6 +624,22 @@ int vw4_w2_pack(const uint8_t* codes_dev, const uint16_t* scales_dev, int64_t N,
     hipLaunchKernelGGL(pack2_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
                        codes_dev, scales_dev, N, K, Np, (uint32_t*)packed_dev, packed_scales_dev);
     return check_launch("vw4_w2_pack");
+}
+
+size_t vw4_w16_packed_bytes(int64_t N, int64_t K) {
+    if (check_shape(N, K)) return 0;
+    return (size_t)(pad64(N) * K * 2);
+}
+
+int vw4_w16_pack(const uint16_t* w_dev, int64_t N, int64_t K, uint8_t* packed_dev, void* stream) {
+    int rc = check_shape(N, K);
+    if (rc) return rc;
+    VW4_REQUIRE(w_dev && packed_dev, VW4_EINVAL, "null pointer");
+    VW4_REQUIRE(aligned(packed_dev, 16), VW4_EINVAL, "packed weights must be 16-byte aligned");
+    const int64_t Np = pad64(N), total = Np * (K / 64);
+    hipLaunchKernelGGL(pack16_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, (hipStream_t)stream, w_dev,
+                       N, K, Np, (uint4*)packed_dev);
+    return check_launch("vw4_w16_pack");
 }
 
 size_t vw4_w6_hi_plane_bytes(int64_t N, int64_t K) {

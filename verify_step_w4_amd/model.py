@@ -88,6 +88,34 @@ class W8Linear:
         return self.N * self.K + self.N * (self.K // 64) * 2
 
 
+class W16Linear:
+    """A [N][K] matrix of unquantised 16-bit float weights (kind "f16": fp16,
+    "bf16": bf16) in the operand-tiled layout; no scales."""
+
+    def __init__(self, packed, N: int, K: int, kind: str):
+        self.packed, self.N, self.K, self.kind = packed, N, K, kind
+
+    @classmethod
+    def from_bits(cls, w, kind: str, stream=None):
+        """w: int16/uint16-bit device tensor [N][K] of fp16 or bf16 bit patterns."""
+        import torch
+        N, K = w.shape
+        packed = torch.empty(int(B.lib().vw4_w16_packed_bytes(N, K)), dtype=torch.uint8, device=w.device)
+        B.w16_pack(w, N, K, packed, stream)
+        return cls(packed, N, K, kind)
+
+    @classmethod
+    def random(cls, N: int, K: int, gen, kind: str, device="cuda"):
+        """N(0, 0.02) weights rounded to the kind's type (timing inputs)."""
+        import torch
+        dt = torch.float16 if kind == "f16" else torch.bfloat16
+        w = (0.02 * torch.randn((N, K), generator=gen, device=device)).to(dt).view(torch.int16)
+        return cls.from_bits(w, kind)
+
+    def nbytes(self) -> int:
+        return self.N * self.K * 2
+
+
 class W3Linear:
     """A [N][K] matrix in the W3 format (3-bit codes, fp16 scale per 64 K): the
     1-bit high plane, the 2-bit low plane and the packed scales."""
