@@ -42,6 +42,15 @@ if ROOT not in sys.path:
 
 METRIC = "verify steps/s and achieved HBM GB/s (W4 skinny GEMM, M=4) vs peak"
 HBM_PEAK_GBS = 8000.0
+# bytes per weight (codes + one fp16 scale per 64, or the 16-bit weight) and a
+# description of each weight format the decoder takes
+WEIGHT_FORMATS = ("w4", "w8", "w6", "w5", "w3", "w2", "f16", "bf16")
+WEIGHT_BYTES = {"w4": 0.53125, "w8": 1.03125, "w6": 0.78125, "w5": 0.65625, "w3": 0.40625, "w2": 0.28125,
+                "f16": 2.0, "bf16": 2.0}
+WEIGHT_DESC = {"w4": "int4 group-64 symmetric, fp16 scales", "w8": "int8 group-64 symmetric, fp16 scales",
+               "w6": "6-bit group-64 symmetric, fp16 scales", "w5": "5-bit group-64 symmetric, fp16 scales",
+               "w3": "3-bit group-64 symmetric, fp16 scales", "w2": "2-bit group-64 symmetric, fp16 scales",
+               "f16": "fp16, unquantised", "bf16": "bf16, unquantised"}
 CALIB_COPY_BYTES = 256 << 20
 
 
@@ -478,7 +487,7 @@ def verify27b_workload(args):
     log(f"generating the 64-layer {fmt.upper()} decoder (d=5120, GQA 40/8x128, FFN 17408) + LM head, KV cache for "
         f"{Lcap} positions, timed context L={L}")
     dec = Decoder(cfg, M, Lcap + M + 8, gen=gen, fmt=fmt)
-    bpw = BYTES_PER_WEIGHT if fmt == "w4" else 1.03125
+    bpw = WEIGHT_BYTES[fmt]
     torch.cuda.synchronize()
     log(f"weights ready in {time.perf_counter() - t0:.1f} s ({dec.weight_bytes() / 1e9:.2f} GB {fmt.upper()})")
     V, d = cfg["V"], cfg["d"]
@@ -646,7 +655,7 @@ def verify27b_workload(args):
         attention_by_context=attention,
         config={"workload": "verify27b", "layers": 64, "d_model": d, "heads_q_kv_dim": [40, 8, 128],
                 "ffn": cfg["F"], "V": V, "context": L, "M": M, "draft_depth": D, "temperature": T, "top_p": top_p,
-                "weights": ("int4" if fmt == "w4" else "int8") + " group-64 symmetric, fp16 scales",
+                "weights": WEIGHT_DESC[fmt],
                 "kv_cache": "bf16"},
         roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                   "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -706,9 +715,9 @@ def spec_loop_workload(args):
         f"context {L}")
     dec = Decoder(cfg, 4, L + 72, gen=gen, fmt=fmt)
     E = torch.randn((V, d), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
-    # a W8 target drafts with a draft-only W4 LM head (the pages' design); its
-    # shared-head cost is timed too
-    draft_lm = W4Linear.random(V, d, 0.02, gen) if fmt == "w8" else None
+    # a target in another format drafts with a draft-only W4 LM head (the
+    # pages' design); its shared-head cost is timed too
+    draft_lm = W4Linear.random(V, d, 0.02, gen) if fmt != "w4" else None
     head = MTPHead(dec, E, gen=gen, lm_head=draft_lm)
     torch.cuda.synchronize()
     K, W = max(10, args.steps // 4), max(3, args.warmup // 4)
@@ -1445,7 +1454,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="verify27b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--weights", default="w4", choices=("w4", "w8"),
+    ap.add_argument("--weights", default="w4", choices=WEIGHT_FORMATS,
                     help="verify27b: weight format of the decoder's linears and LM head")
     ap.add_argument("--context", type=int, default=8192, help="KV context length L of the verify27b workload")
     ap.add_argument("--no-context-sweep", action="store_true",

@@ -59,17 +59,16 @@ class DecoderCapture:
         self.layers = []
         self.final = {}
 
-    def _parts(self, name, fmt):
+    def _parts(self, name):
         dec, M = self.dec, self.M
         N, K = dec.shapes[name]
-        S, ldp = (B.w8_partials_layout if fmt == "w8" else B.gemm_partials_layout)(M, N, K)
+        S, ldp = dec.layers[0][name].partials_layout(M)
         return host(dec.parts[name][:S * M * ldp]).reshape(S, M, ldp)[:, :, :N].copy()
 
     def __call__(self, when, name):
         import torch
         torch.cuda.synchronize()
         dec, M = self.dec, self.M
-        fmt = "w8" if type(dec.layers[0]["qkv"]).__name__ == "W8Linear" else "w4"
         if when == "pre" and name == "qkv":
             li = len(self.layers)
             self.layers.append(dict(h1=host(dec.h[:M]).copy(), resid1=host(dec.resid[:M]).copy()))
@@ -78,7 +77,7 @@ class DecoderCapture:
                 self.layers[li - 1]["h_next"] = self.layers[li]["h1"]
         cur = self.layers[-1] if self.layers else None
         if when == "post" and name == "qkv":
-            cur["qkv"] = self._parts("qkv", fmt)
+            cur["qkv"] = self._parts("qkv")
         elif when == "pre" and name == "o":
             li = len(self.layers) - 1
             cur["q"] = host(dec.q[:M]).copy()
@@ -86,14 +85,14 @@ class DecoderCapture:
             cur["Kc"] = host(dec.Kc[li]).copy()
             cur["Vc"] = rows_from_vb(host(dec.Vc[li]))
         elif when == "post" and name == "o":
-            cur["o"] = self._parts("o", fmt)
+            cur["o"] = self._parts("o")
         elif when == "pre" and name == "gate_up":
             cur["resid2"] = host(dec.resid2[:M]).copy()
             cur["h2"] = host(dec.h[:M]).copy()
         elif when == "post" and name == "gate_up":
             cur["a"] = host(dec.a[:M]).copy()
         elif when == "post" and name == "down":
-            cur["down"] = self._parts("down", fmt)
+            cur["down"] = self._parts("down")
         elif when == "pre" and name == "lm_head":
             self.final = dict(resid=host(dec.resid[:M]).copy(), h=host(dec.h[:M]).copy())
             cur["resid_next"], cur["h_next"] = self.final["resid"], self.final["h"]

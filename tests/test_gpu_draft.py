@@ -192,8 +192,8 @@ def _loop_setup(seed, D, L0, fmt="w4"):
     gen.manual_seed(seed)
     target = Decoder(cfg, D + 1, L0 + 64, gen=gen, fmt=fmt)
     E = torch.randn((cfg["V"], cfg["d"]), generator=gen, device="cuda").to(torch.bfloat16).view(torch.int16)
-    # a W8 target gets a draft-only W4 LM head
-    lm = W4Linear.random(cfg["V"], cfg["d"], 0.02, gen) if fmt == "w8" else None
+    # a target in another format gets a draft-only W4 LM head
+    lm = W4Linear.random(cfg["V"], cfg["d"], 0.02, gen) if fmt != "w4" else None
     head = MTPHead(target, E, gen=gen, lm_head=lm)
     kv = ([k.clone() for k in target.Kc], [v.clone() for v in target.Vc],
           [k.clone() for k in head.block.Kc], [v.clone() for v in head.block.Vc])
@@ -219,7 +219,7 @@ def _ar_sequence(target, head, kv, L0, t0, n, T, top_p):
     return seq
 
 
-@pytest.mark.parametrize("D,fmt", [(1, "w4"), (3, "w4"), (5, "w4"), (3, "w8")])
+@pytest.mark.parametrize("D,fmt", [(1, "w4"), (3, "w4"), (5, "w4"), (3, "w8"), (2, "w5"), (2, "w2"), (2, "bf16")])
 def test_spec_loop_greedy_equals_autoregressive(D, fmt):
     import torch
     L0, t0, n = 700, 123, 14
@@ -266,7 +266,11 @@ def test_spec_loop_sampling_deterministic():
     assert runs[0] == runs[1]
 
 
-@pytest.mark.parametrize("fmt", ["w4", "w8"])
+PER_WEIGHT = {"w4": 0.53125, "w8": 1.03125, "w6": 0.78125, "w5": 0.65625, "w3": 0.40625, "w2": 0.28125,
+              "f16": 2.0, "bf16": 2.0}
+
+
+@pytest.mark.parametrize("fmt", ["w4", "w8", "w6", "w5", "w3", "w2", "f16", "bf16"])
 def test_gemm_pass_counts_and_bytes(fmt):
     """The GEMM-only pass the bench times issues one launch per linear plus the
     LM head, and its algorithmic bytes are the weights' bytes plus activations."""
@@ -281,11 +285,16 @@ def test_gemm_pass_counts_and_bytes(fmt):
     assert n == 4 * cfg["layers"] + 1
     wb = dec.weight_bytes()
     alg = dec.gemm_alg_bytes(4)
-    assert wb < alg < wb * 1.01
-    per_w = 0.53125 if fmt == "w4" else 1.03125
-    d, F, nqkv = cfg["d"], cfg["F"], (cfg["nq"] + 2 * cfg["nkv"]) * cfg["hd"]
+    per_w = PER_WEIGHT[fmt]
+    M, d, F, nqkv = 4, cfg["d"], cfg["F"], (cfg["nq"] + 2 * cfg["nkv"]) * cfg["hd"]
     nw = cfg["layers"] * (nqkv * d + d * d + 2 * F * d + d * F) + cfg["V"] * d
     assert wb == int(round(nw * per_w))
+    # activations in (bf16) and outputs out (fp32 partial sums; W4's gate|up
+    # writes the bf16 SwiGLU of its epilogue instead)
+    gate_up_out = M * F * 2 if fmt == "w4" else M * 2 * F * 4
+    act = cfg["layers"] * (M * d * 2 + M * nqkv * 4 + M * d * 2 + M * d * 4 + M * d * 2 + gate_up_out
+                           + M * F * 2 + M * d * 4) + M * d * 2 + M * cfg["V"] * 4
+    assert alg == wb + act
 
 
 def test_depth_autotune():

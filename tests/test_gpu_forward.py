@@ -20,7 +20,7 @@ import pytest
 import oracle
 from verify_step_w4_amd import binding as B
 from verify_step_w4_amd import synth
-from verify_step_w4_amd.model import DENSE_27B, Decoder, VerifyStep, W4Linear, W8Linear
+from verify_step_w4_amd.model import DENSE_27B, LINEAR_FORMATS, Decoder, VerifyStep, W4Linear, W16Linear
 
 from helpers import GEMM_RTOL, dev, gemm_rel_err, host, log, rows_from_vb, vb_from_rows
 from layer_parity import DecoderCapture, bf16_close, check_decoder_ops, end_to_end
@@ -45,6 +45,30 @@ def _host_model(cfg, seed):
                 lm_head=synth.normal_f32(g, (V, d), 0.02))
 
 
+def _f16_bits(w):
+    return (w.astype(np.float16).view(np.uint16),)
+
+
+def _bf16_bits(w):
+    return (oracle.bf16_round(w.astype(np.float64)),)
+
+
+# the oracle's (quantiser, GEMM) of each format other than W4; a quantiser
+# returns the arguments the GEMM takes after x
+ORACLE_FORMATS = {"w8": (oracle.w8_quantize, oracle.w8_gemm), "w6": (oracle.w6_quantize, oracle.w6_gemm),
+                  "w5": (oracle.w5_quantize, oracle.w5_gemm), "w3": (oracle.w3_quantize, oracle.w3_gemm),
+                  "w2": (oracle.w2_quantize, oracle.w2_gemm), "f16": (_f16_bits, oracle.f16_gemm),
+                  "bf16": (_bf16_bits, oracle.b16_gemm)}
+
+
+def _linear(v, fmt):
+    """A device matrix in format fmt from host fp32 weights (natural row order)."""
+    if fmt in ("f16", "bf16"):
+        bits = ORACLE_FORMATS[fmt][0](v)[0]
+        return W16Linear.from_bits(dev(bits.view(np.int16)), fmt)
+    return LINEAR_FORMATS[fmt].from_fp32(v)
+
+
 def _device_weights(hm, fmt="w4"):
     layers = []
     for l in hm["layers"]:
@@ -52,14 +76,14 @@ def _device_weights(hm, fmt="w4"):
         for k, v in l.items():
             if k in ("g1", "g2"):
                 d[k] = dev(v)
-            elif fmt == "w8":      # W8: natural gate|up order (the SwiGLU runs on the partials)
-                d[k] = W8Linear.from_fp32(v)
+            elif fmt != "w4":      # natural gate|up order (the SwiGLU runs on the partials)
+                d[k] = _linear(v, fmt)
             elif k == "gate_up":   # the fused SwiGLU GEMM takes gate/up-interleaved rows
                 d[k] = W4Linear.from_fp32(dev(B.interleave_gate_up(v)))
             else:
                 d[k] = W4Linear.from_fp32(dev(v))
         layers.append(d)
-    lm = W8Linear.from_fp32(hm["lm_head"]) if fmt == "w8" else W4Linear.from_fp32(dev(hm["lm_head"]))
+    lm = _linear(hm["lm_head"], fmt) if fmt != "w4" else W4Linear.from_fp32(dev(hm["lm_head"]))
     return dict(layers=layers, final_gamma=dev(hm["final_gamma"]), lm_head=lm)
 
 
@@ -143,10 +167,12 @@ def _dense_cfg(layers, V):
     return c
 
 
-@pytest.mark.parametrize("fmt", ["w8"])
+@pytest.mark.parametrize("fmt", ["w8", "w6", "w5", "w3", "w2", "f16", "bf16"])
 def test_forward_matches_oracle_small_decoder_other_format(fmt):
-    """The same small decoder with W8 linears and LM head (gate|up partials
-    through the standalone SwiGLU) against the oracle's W8 composition."""
+    """The same small decoder with every linear and the LM head in another
+    weight format (gate|up partials through the standalone SwiGLU) against
+    the oracle's composition in that format: each op on the GPU's own inputs
+    at its bar, then the verify rows equal to the one-row steps bit for bit."""
     import torch
     cfg = TINY
     M, L, Lmax = 4, 37, 64
@@ -163,9 +189,9 @@ def test_forward_matches_oracle_small_decoder_other_format(fmt):
     cap = DecoderCapture(dec, M)
     logits = host(dec.forward(dev(x), L, M, gemm_hook=cap)).copy()
     torch.cuda.synchronize()
-    worst, ident = check_decoder_ops(cap, hm, cfg, x, L, quant=oracle.w8_quantize, gemm=oracle.w8_gemm)
-    ref = _oracle_forward(cfg, hm, [k.copy() for k in Kh], [v.copy() for v in Vh], x, L,
-                          quant=oracle.w8_quantize, gemm=oracle.w8_gemm)
+    quant, gemm = ORACLE_FORMATS[fmt]
+    worst, ident = check_decoder_ops(cap, hm, cfg, x, L, quant=quant, gemm=gemm)
+    ref = _oracle_forward(cfg, hm, [k.copy() for k in Kh], [v.copy() for v in Vh], x, L, quant=quant, gemm=gemm)
     mx, med = end_to_end(logits, ref)
     print(f"[forward {fmt}] per op: worst fp32 rel {worst:.2e}, bf16 identical >= {ident:.4f}; "
           f"end to end (statistic): max rel {mx:.3e}, median {med:.3e}", flush=True)

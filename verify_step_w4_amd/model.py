@@ -45,13 +45,47 @@ class W4Linear:
             del w
         return cls(packed, pscales, N, K)
 
+    # the interface every weight format's matrix offers the decoder
+    def partials(self, x, part, M: int, stream=None):
+        B.w4_skinny_gemm_partials(x, self.packed, self.pscales, part, M, self.N, self.K, stream)
+
+    def partials_layout(self, M: int):
+        return B.gemm_partials_layout(M, self.N, self.K)
+
+    def gemm(self, x, y, M: int, ws=None, stream=None):
+        B.w4_skinny_gemm(x, self.packed, self.pscales, y, M, self.N, self.K, ws=ws, stream=stream)
+
+    def workspace_bytes(self, M: int) -> int:
+        return B.gemm_workspace_bytes(M, self.N, self.K)
+
     def nbytes(self) -> int:
         return int(self.N * self.K * BYTES_PER_WEIGHT)
 
 
-class W8Linear:
+class _TwoPlaneOps:
+    """The decoder interface of the two-plane formats (hi, lo planes and packed
+    scales), through the binding's calls named after _FMT."""
+    _FMT = ""
+
+    def partials(self, x, part, M: int, stream=None):
+        getattr(B, f"{self._FMT}_skinny_gemm_partials")(x, self.hi, self.lo, self.pscales, part, M, self.N, self.K,
+                                                         stream)
+
+    def partials_layout(self, M: int):
+        return getattr(B, f"{self._FMT}_partials_layout")(M, self.N, self.K)
+
+    def gemm(self, x, y, M: int, ws=None, stream=None):
+        getattr(B, f"{self._FMT}_skinny_gemm")(x, self.hi, self.lo, self.pscales, y, M, self.N, self.K, ws=ws,
+                                               stream=stream)
+
+    def workspace_bytes(self, M: int) -> int:
+        return getattr(B, f"{self._FMT}_workspace_bytes")(M, self.N, self.K)
+
+
+class W8Linear(_TwoPlaneOps):
     """A [N][K] matrix in the W8 format (int8 codes, fp16 scale per 64 K), kept
     as its two packed nibble planes and the packed scales."""
+    _FMT = "w8"
 
     def __init__(self, hi, lo, pscales, N: int, K: int):
         self.hi, self.lo, self.pscales, self.N, self.K = hi, lo, pscales, N, K
@@ -112,13 +146,34 @@ class W16Linear:
         w = (0.02 * torch.randn((N, K), generator=gen, device=device)).to(dt).view(torch.int16)
         return cls.from_bits(w, kind)
 
+    @classmethod
+    def from_fp32(cls, w, kind: str, device="cuda"):
+        """fp32 weights rounded to the kind's type (round to nearest even) and packed."""
+        import torch
+        wt = w.detach() if hasattr(w, "detach") else torch.from_numpy(w)
+        dt = torch.float16 if kind == "f16" else torch.bfloat16
+        return cls.from_bits(wt.to(device).to(dt).view(torch.int16), kind)
+
+    def partials(self, x, part, M: int, stream=None):
+        B.w16_skinny_gemm_partials(x, self.packed, part, M, self.N, self.K, kind=self.kind, stream=stream)
+
+    def partials_layout(self, M: int):
+        return B.w16_partials_layout(M, self.N, self.K, self.kind)
+
+    def gemm(self, x, y, M: int, ws=None, stream=None):
+        B.w16_skinny_gemm(x, self.packed, y, M, self.N, self.K, kind=self.kind, ws=ws, stream=stream)
+
+    def workspace_bytes(self, M: int) -> int:
+        return B.w16_workspace_bytes(M, self.N, self.K, self.kind)
+
     def nbytes(self) -> int:
         return self.N * self.K * 2
 
 
-class W3Linear:
+class W3Linear(_TwoPlaneOps):
     """A [N][K] matrix in the W3 format (3-bit codes, fp16 scale per 64 K): the
     1-bit high plane, the 2-bit low plane and the packed scales."""
+    _FMT = "w3"
 
     def __init__(self, hi, lo, pscales, N: int, K: int):
         self.hi, self.lo, self.pscales, self.N, self.K = hi, lo, pscales, N, K
@@ -190,13 +245,26 @@ class W2Linear:
         scales = (4e-4 + 8e-4 * torch.rand((N, K // 64), generator=gen, device=device)).to(torch.float16)
         return cls.from_codes(codes, scales.view(torch.int16))
 
+    def partials(self, x, part, M: int, stream=None):
+        B.w2_skinny_gemm_partials(x, self.packed, self.pscales, part, M, self.N, self.K, stream)
+
+    def partials_layout(self, M: int):
+        return B.w2_partials_layout(M, self.N, self.K)
+
+    def gemm(self, x, y, M: int, ws=None, stream=None):
+        B.w2_skinny_gemm(x, self.packed, self.pscales, y, M, self.N, self.K, ws=ws, stream=stream)
+
+    def workspace_bytes(self, M: int) -> int:
+        return B.w2_workspace_bytes(M, self.N, self.K)
+
     def nbytes(self) -> int:
         return self.N * self.K // 4 + self.N * (self.K // 64) * 2
 
 
-class W5Linear:
+class W5Linear(_TwoPlaneOps):
     """A [N][K] matrix in the W5 format (5-bit codes, fp16 scale per 64 K): the
     1-bit high plane, the 4-bit low plane (W4 layout) and the packed scales."""
+    _FMT = "w5"
 
     def __init__(self, hi, lo, pscales, N: int, K: int):
         self.hi, self.lo, self.pscales, self.N, self.K = hi, lo, pscales, N, K
@@ -233,9 +301,10 @@ class W5Linear:
         return self.N * self.K * 5 // 8 + self.N * (self.K // 64) * 2
 
 
-class W6Linear:
+class W6Linear(_TwoPlaneOps):
     """A [N][K] matrix in the W6 format (6-bit codes, fp16 scale per 64 K): the
     2-bit high plane, the 4-bit low plane (W4 layout) and the packed scales."""
+    _FMT = "w6"
 
     def __init__(self, hi, lo, pscales, N: int, K: int):
         self.hi, self.lo, self.pscales, self.N, self.K = hi, lo, pscales, N, K
@@ -270,6 +339,11 @@ class W6Linear:
 
     def nbytes(self) -> int:
         return self.N * self.K * 3 // 4 + self.N * (self.K // 64) * 2
+
+
+# the quantised formats whose matrices come from (N, K, gen, device) random draws
+LINEAR_FORMATS = {"w8": W8Linear, "w6": W6Linear, "w5": W5Linear, "w3": W3Linear, "w2": W2Linear}
+WEIGHT_FORMATS = ("w4", "w8", "w6", "w5", "w3", "w2", "f16", "bf16")
 
 
 class LMHeadVerify:
@@ -313,8 +387,10 @@ DENSE_27B = dict(d=5120, nq=40, nkv=8, hd=128, F=17408, layers=64, V=151936, eps
 
 class Decoder:
     """Pre-norm dense decoder with GQA attention and a SwiGLU FFN, every linear
-    a W4 skinny GEMM (the gate|up matrix in the gate/up-interleaved row order
-    of B.interleave_gate_up, with the SwiGLU in that GEMM's epilogue).  One call of ``forward`` scores M rows at positions
+    a skinny GEMM in one weight format (fmt, one of WEIGHT_FORMATS).  In W4 the
+    gate|up matrix is in the gate/up-interleaved row order of
+    B.interleave_gate_up, with the SwiGLU in that GEMM's epilogue; the other
+    formats keep the natural order and run the SwiGLU on the partial sums.  One call of ``forward`` scores M rows at positions
     L .. L+M-1 (the verify pass); M = 1 is an autoregressive step.  Weights,
     KV caches and activation buffers are allocated once (device-resident)."""
 
@@ -357,21 +433,22 @@ class Decoder:
         self.attn = torch.empty((M_max, nq * hd), dtype=i16, device=device)
         self.a = torch.empty((M_max, F), dtype=i16, device=device)
         self.parts = {}
-        for name, (N, K) in self.shapes.items():
-            S, ldp = B.gemm_partials_layout(M_max, N, K)
-            S8, ldp8 = B.w8_partials_layout(M_max, N, K)
-            self.parts[name] = torch.empty(max(S * ldp, S8 * ldp8) * M_max, dtype=torch.float32, device=device)
+        for name in self.shapes:
+            S, ldp = self.layers[0][name].partials_layout(M_max)
+            self.parts[name] = torch.empty(S * ldp * M_max, dtype=torch.float32, device=device)
         self.attn_ws = B.workspace(B.attn_workspace_bytes(M_max, nq, nkv, hd, Lmax), device)
         self.norm_ws = B.workspace(B.norm_workspace_bytes(M_max, d), device)
         self.logits = torch.empty((M_max, V), dtype=torch.float32, device=device)
-        self.lm_ws = B.workspace(max(B.gemm_workspace_bytes(M_max, V, d), B.w8_workspace_bytes(M_max, V, d)), device)
+        self.lm_ws = B.workspace(self.lm_head.workspace_bytes(M_max), device)
 
     @staticmethod
     def random_weights(cfg: dict, gen, device="cuda", fmt: str = "w4"):
         """W4: ~N(0, 0.02) fp32 weights drawn on the device and quantised; W8:
-        uniform int8 codes with fp16 scales in [1e-4, 3e-4] (the same spread).
-        RMSNorm gains ~N(1, 0.02) in bf16.  In W8 the gate|up matrix keeps its
-        natural row order (the SwiGLU runs on its partials)."""
+        uniform int8 codes with fp16 scales in [1e-4, 3e-4] (the same spread);
+        W6, W5, W3, W2: uniform codes with fp16 scales in [4e-4, 1.2e-3]; f16,
+        bf16: N(0, 0.02) rounded to the type.  RMSNorm gains ~N(1, 0.02) in
+        bf16.  Outside W4 the gate|up matrix keeps its natural row order (the
+        SwiGLU runs on its partials)."""
         import torch
         d, nq, nkv, hd, F, nl, V = (cfg[k] for k in ("d", "nq", "nkv", "hd", "F", "layers", "V"))
         nqkv = (nq + 2 * nkv) * hd
@@ -380,9 +457,11 @@ class Decoder:
             return (1.0 + 0.02 * torch.randn(d, generator=gen, device=device)).to(torch.bfloat16).view(torch.int16)
 
         def lin(N, K):
-            if fmt == "w8":
-                return W8Linear.random(N, K, gen, device)
-            return W4Linear.random(N, K, 0.02, gen, device)
+            if fmt == "w4":
+                return W4Linear.random(N, K, 0.02, gen, device)
+            if fmt in ("f16", "bf16"):
+                return W16Linear.random(N, K, gen, fmt, device)
+            return LINEAR_FORMATS[fmt].random(N, K, gen, device)
 
         layers = []
         for _ in range(nl):
@@ -439,11 +518,11 @@ class Decoder:
             # FFN block: gate|up with the SwiGLU in the GEMM epilogue
             N, K = self.shapes["gate_up"]
             hook("pre", "gate_up")
-            if isinstance(W["gate_up"], W8Linear):
+            if isinstance(W["gate_up"], W4Linear):
+                B.w4_skinny_gemm_swiglu(h, W["gate_up"].packed, W["gate_up"].pscales, self.a, F, M, F, K, stream)
+            else:
                 S, ldp = self._partials(W, "gate_up", h, M, stream)
                 B.swiglu(self.parts["gate_up"], S, ldp, M, F, self.a, stream)
-            else:
-                B.w4_skinny_gemm_swiglu(h, W["gate_up"].packed, W["gate_up"].pscales, self.a, F, M, F, K, stream)
             hook("post", "gate_up")
             hook("pre", "down")
             S, ldp = self._partials(W, "down", self.a[:M], M, stream)
@@ -459,21 +538,11 @@ class Decoder:
     def _partials(self, W, name, x, M, stream):
         """Split-K partial sums of linear `name` into self.parts[name]; returns (S, ldp)."""
         lin = W[name]
-        N, K = self.shapes[name]
-        if isinstance(lin, W8Linear):
-            B.w8_skinny_gemm_partials(x, lin.hi, lin.lo, lin.pscales, self.parts[name], M, N, K, stream)
-            return B.w8_partials_layout(M, N, K)
-        B.w4_skinny_gemm_partials(x, lin.packed, lin.pscales, self.parts[name], M, N, K, stream)
-        return B.gemm_partials_layout(M, N, K)
+        lin.partials(x, self.parts[name], M, stream)
+        return lin.partials_layout(M)
 
     def _lm_head(self, h, M, stream):
-        c, lm = self.cfg, self.lm_head
-        if isinstance(lm, W8Linear):
-            B.w8_skinny_gemm(h, lm.hi, lm.lo, lm.pscales, self.logits[:M], M, c["V"], c["d"], ws=self.lm_ws,
-                             stream=stream)
-        else:
-            B.w4_skinny_gemm(h, lm.packed, lm.pscales, self.logits[:M], M, c["V"], c["d"], ws=self.lm_ws,
-                             stream=stream)
+        self.lm_head.gemm(h, self.logits[:M], M, ws=self.lm_ws, stream=stream)
 
     def gemm_pass(self, M: int, stream=None, names=("qkv", "o", "gate_up", "down", "lm_head")):
         """Only the W4 GEMM launches of one forward (same shapes, weights and
@@ -487,7 +556,7 @@ class Decoder:
                 if name not in names:
                     continue
                 N, K = self.shapes[name]
-                if name == "gate_up" and not isinstance(W[name], W8Linear):
+                if name == "gate_up" and isinstance(W[name], W4Linear):
                     B.w4_skinny_gemm_swiglu(self.h[:M], W[name].packed, W[name].pscales, self.a, F, M, F, K, stream)
                 else:
                     x = {"qkv": self.h, "o": self.attn, "gate_up": self.h, "down": self.a}[name]
@@ -499,14 +568,15 @@ class Decoder:
         return n
 
     def gemm_alg_bytes(self, M: int) -> int:
-        """Algorithmic bytes of one forward's W4 GEMMs: each weight (code +
-        scale) once, activations in, fp32 outputs out."""
+        """Algorithmic bytes of one forward's GEMMs: each weight (code + scale,
+        or 16-bit weight) once, activations in, fp32 outputs out (W4's gate|up:
+        the bf16 SwiGLU of its epilogue)."""
         c = self.cfg
         tot = 0.0
         for name, (N, K) in self.shapes.items():
-            w8 = isinstance(self.layers[0][name], W8Linear)
-            # SwiGLU epilogue output (bf16), or fp32 partial sums
-            out = M * (N // 2) * 2 if (name == "gate_up" and not w8) else M * N * 4
+            fused = isinstance(self.layers[0][name], W4Linear)
+            # SwiGLU epilogue output (bf16, W4), or fp32 partial sums
+            out = M * (N // 2) * 2 if (name == "gate_up" and fused) else M * N * 4
             tot += sum(l[name].nbytes() for l in self.layers) + c["layers"] * (M * K * 2 + out)
         tot += self.lm_head.nbytes() + M * c["d"] * 2 + M * c["V"] * 4
         return int(tot)
