@@ -14,7 +14,7 @@
 // shares; sums are fp32 in an order that depends only on (N, K): row m of an
 // M-row call equals the one-row call bit for bit.  The template's scale
 // pointer is not read for these formats; the weights' pointer stands in.
-#include "skinny_gemm.h"
+#include "skinny_formats.h"
 
 using namespace vw4;
 

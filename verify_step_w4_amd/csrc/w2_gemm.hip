@@ -14,7 +14,7 @@
 // (scale / 2) times that.  Products are exact in fp32; sums are fp32 in an
 // order that depends only on (N, K): row m of an M-row call equals the
 // one-row call bit for bit.
-#include "skinny_gemm.h"
+#include "skinny_formats.h"
 
 using namespace vw4;
 

@@ -11,7 +11,7 @@
 // sum x) + D_lo), and the split plan every format shares.  Products are exact
 // in fp32 (bf16 x 8-bit integer); sums are fp32 in an order that depends only
 // on (N, K): row m of an M-row call equals the one-row call bit for bit.
-#include "skinny_gemm.h"
+#include "skinny_formats.h"
 
 using namespace vw4;
 
