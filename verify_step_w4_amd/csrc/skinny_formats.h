@@ -81,12 +81,11 @@ struct FmtW2 {
     }
 };
 
-// The two-plane formats, code u = c + bias = R hi + lo (R = 16 with a 4-bit
-// low plane, 4 with a 2-bit one): with D_hi = sum x (128 + hi) and D_lo =
-// sum x (128 + lo), R D_hi + D_lo = sum x (128 (R + 1) + bias + c), so
-// sum x c = R (D_hi - (128 + (128 + bias) / R) sum x) + D_lo.  The high
-// plane's chain starts from x . (-(128 + (128 + bias) / R)) (NEG_PAIR): W8
-// (bias 128, R 16) -144, W6 (32, 16) -138, W5 (16, 16) -137, W3 (4, 4) -161.
+// The two-chain form, for W8 (u = c + 128 up to 255: 128 + u is not exact in
+// bf16): code u = 16 hi + lo over two 4-bit planes; with D_hi = sum x (128 +
+// hi) and D_lo = sum x (128 + lo), 16 D_hi + D_lo = sum x (2304 + c), so
+// sum x c = 16 (D_hi - 144 sum x) + D_lo: the high plane's chain starts from
+// x . (-144) (NEG_PAIR).
 template <class Derived>
 struct TwoPlane {
     __device__ static void finish(const bf16x8 (&hb)[4][2], const bf16x8 (&lb)[4][2], bf16x8 a0, bf16x8 a1,
@@ -139,13 +138,50 @@ struct FmtW8 : TwoPlane<FmtW8> {
     }
 };
 
+// Single-chain formats: a code u = c + bias < 128 split over a low plane of
+// BL bits and a high plane.  Per bf16 pair both fields are moved into place
+// (the low field to bits 0 .. BL-1 of each half, the high field just above),
+// merged with a bit-field insert, and and-or'ed with the magic into the bf16
+// pair 128 + u; one matrix-core chain per row block starts from
+// x . (-(128 + bias)), and acc += scale * D as in W4.  Derived supplies
+// merge8(w, nb, s, magic): the 8 operands of row block nb, k half s.
+__device__ __forceinline__ uint32_t shr_signed(uint32_t v, int sh) {   // sh < 0: shift left
+    return sh >= 0 ? v >> sh : v << -sh;
+}
+template <uint32_t LO_MASK, uint32_t U_MASK>
+__device__ __forceinline__ uint32_t merge_pair(uint32_t lo_sh, uint32_t hi_sh, uint32_t magic_v) {
+    const uint32_t t = (lo_sh & LO_MASK) | (hi_sh & ~LO_MASK);
+    return and_or(t, U_MASK, magic_v);
+}
+template <class Derived>
+struct SingleChain {
+    template <int NWD>
+    __device__ static void group(const u32x4 (&w)[NWD], bf16x8 a0, bf16x8 a1, uint2 sc, uint32_t, uint32_t magic_v,
+                                 f32x4 (&acc)[4]) {
+        const bf16x8 neg = pair8(Derived::NEG_PAIR);
+        f32x4 off = {0.f, 0.f, 0.f, 0.f};
+        off = mfma16(a0, neg, off);
+        off = mfma16(a1, neg, off);
+        f32x4 d[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+            d[nb] = mfma16(a1, Derived::merge8(w, nb, 1, magic_v), mfma16(a0, Derived::merge8(w, nb, 0, magic_v), off));
+        float f[4];
+        scales4(sc, f);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[nb][r] = fmaf(f[nb], d[nb][r], acc[nb][r]);
+    }
+};
+
 // W6: c in [-31, 31], u = c + 32 = 16 hi + lo; lo in the W4 layout, hi in a
 // 2-bit plane with the same lane mapping (one 16-byte word per lane and group,
-// dword nb = row block nb, both k halves).
-struct FmtW6 : TwoPlane<FmtW6> {
-    static constexpr float R = 16.0f;
+// dword nb = row block nb, element j of k half s at bits 8 s + 2 (j / 2) +
+// 16 (j % 2)).  Offset 160 = 128 + 32.
+struct FmtW6 : SingleChain<FmtW6> {
     static constexpr int NW = 3;
-    static constexpr uint32_t NEG_PAIR = 0xC30AC30Au;   // two bf16 -138.0
+    static constexpr uint32_t NEG_PAIR = 0xC320C320u;   // two bf16 -160.0
     __device__ static void base(const Planes& P, int64_t t, int G, int lane, const u32x4*& b0, const u32x4*& b1) {
         b0 = P.p0 + t * G * 64 + lane;
         b1 = P.p1 + t * G * 128 + lane;
@@ -155,17 +191,13 @@ struct FmtW6 : TwoPlane<FmtW6> {
         w[1] = __builtin_nontemporal_load(b1 + g * 128);
         w[2] = __builtin_nontemporal_load(b1 + g * 128 + 64);
     }
-    __device__ static void group(const u32x4 (&w)[NW], bf16x8 a0, bf16x8 a1, uint2 sc, uint32_t kmask,
-                                 uint32_t magic_v, f32x4 (&acc)[4]) {
-        bf16x8 hb[4][2], lb[4][2];
+    __device__ static bf16x8 merge8(const u32x4 (&w)[NW], int nb, int s, uint32_t magic_v) {
+        const uint32_t lo = w[1 + (nb >> 1)][2 * (nb & 1) + s], hi = w[0][nb];
+        uint32_t r[4];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                hb[nb][s] = two8(w[0][nb], s, magic_v);
-                lb[nb][s] = nib8(w[1 + (nb >> 1)][2 * (nb & 1) + s], kmask, magic_v);
-            }
-        finish(hb, lb, a0, a1, sc, acc);
+        for (int p = 0; p < 4; ++p)   // pair p: low nibbles at 4 p, high fields at 8 s + 2 p -> bits 4-5
+            r[p] = merge_pair<0x000F000Fu, 0x003F003Fu>(lo >> (4 * p), shr_signed(hi, 8 * s + 2 * p - 4), magic_v);
+        return __builtin_bit_cast(bf16x8, u32x4{r[0], r[1], r[2], r[3]});
     }
     __host__ __device__ static Planes expert(Planes P, int64_t e, int64_t w_estride) {
         P.p0 += e * (w_estride / 2);
@@ -178,11 +210,10 @@ struct FmtW6 : TwoPlane<FmtW6> {
 // layout, hi in a 1-bit plane with the same lane mapping (8 bytes per lane and
 // group: dword nb / 2 holds row blocks nb = 2 d and 2 d + 1, quarter
 // q = 2 (nb & 1) + s of it the k half s, element j at bit 4 q + j / 2 +
-// 16 (j % 2)).
-struct FmtW5 : TwoPlane<FmtW5> {
-    static constexpr float R = 16.0f;
+// 16 (j % 2)).  Offset 144 = 128 + 16.
+struct FmtW5 : SingleChain<FmtW5> {
     static constexpr int NW = 3;
-    static constexpr uint32_t NEG_PAIR = 0xC309C309u;   // two bf16 -137.0
+    static constexpr uint32_t NEG_PAIR = 0xC310C310u;   // two bf16 -144.0
     __device__ static void base(const Planes& P, int64_t t, int G, int lane, const u32x4*& b0, const u32x4*& b1) {
         b0 = (const u32x4*)((const u32x2*)P.p0 + t * G * 64 + lane);   // the 1-bit plane in 8-byte units
         b1 = P.p1 + t * G * 128 + lane;
@@ -193,17 +224,14 @@ struct FmtW5 : TwoPlane<FmtW5> {
         w[1] = __builtin_nontemporal_load(b1 + g * 128);
         w[2] = __builtin_nontemporal_load(b1 + g * 128 + 64);
     }
-    __device__ static void group(const u32x4 (&w)[NW], bf16x8 a0, bf16x8 a1, uint2 sc, uint32_t kmask,
-                                 uint32_t magic_v, f32x4 (&acc)[4]) {
-        bf16x8 hb[4][2], lb[4][2];
+    __device__ static bf16x8 merge8(const u32x4 (&w)[NW], int nb, int s, uint32_t magic_v) {
+        const uint32_t lo = w[1 + (nb >> 1)][2 * (nb & 1) + s], hi = w[0][nb >> 1];
+        const int q = 2 * (nb & 1) + s;
+        uint32_t r[4];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                hb[nb][s] = one8(w[0][nb >> 1], 2 * (nb & 1) + s, magic_v);
-                lb[nb][s] = nib8(w[1 + (nb >> 1)][2 * (nb & 1) + s], kmask, magic_v);
-            }
-        finish(hb, lb, a0, a1, sc, acc);
+        for (int p = 0; p < 4; ++p)   // pair p: low nibbles at 4 p, high bits at 4 q + p -> bit 4
+            r[p] = merge_pair<0x000F000Fu, 0x001F001Fu>(lo >> (4 * p), shr_signed(hi, 4 * q + p - 4), magic_v);
+        return __builtin_bit_cast(bf16x8, u32x4{r[0], r[1], r[2], r[3]});
     }
     __host__ __device__ static Planes expert(Planes P, int64_t e, int64_t w_estride) {
         P.p0 += e * (w_estride / 4);
@@ -213,11 +241,11 @@ struct FmtW5 : TwoPlane<FmtW5> {
 };
 
 // W3: c in [-3, 3], u = c + 4 = 4 hi + lo with hi in {0, 1}; hi in the 1-bit
-// plane of the W5 layout, lo in the 2-bit plane of the W2 layout.
-struct FmtW3 : TwoPlane<FmtW3> {
-    static constexpr float R = 4.0f;
+// plane of the W5 layout, lo in the 2-bit plane of the W2 layout.  Offset
+// 132 = 128 + 4.
+struct FmtW3 : SingleChain<FmtW3> {
     static constexpr int NW = 2;
-    static constexpr uint32_t NEG_PAIR = 0xC321C321u;   // two bf16 -161.0
+    static constexpr uint32_t NEG_PAIR = 0xC304C304u;   // two bf16 -132.0
     __device__ static void base(const Planes& P, int64_t t, int G, int lane, const u32x4*& b0, const u32x4*& b1) {
         b0 = (const u32x4*)((const u32x2*)P.p0 + t * G * 64 + lane);   // the 1-bit plane in 8-byte units
         b1 = P.p1 + t * G * 64 + lane;
@@ -227,17 +255,14 @@ struct FmtW3 : TwoPlane<FmtW3> {
         w[0] = u32x4{h.x, h.y, 0u, 0u};
         w[1] = __builtin_nontemporal_load(b1 + g * 64);
     }
-    __device__ static void group(const u32x4 (&w)[NW], bf16x8 a0, bf16x8 a1, uint2 sc, uint32_t,
-                                 uint32_t magic_v, f32x4 (&acc)[4]) {
-        bf16x8 hb[4][2], lb[4][2];
+    __device__ static bf16x8 merge8(const u32x4 (&w)[NW], int nb, int s, uint32_t magic_v) {
+        const uint32_t lo = w[1][nb], hi = w[0][nb >> 1];
+        const int q = 2 * (nb & 1) + s;
+        uint32_t r[4];
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                hb[nb][s] = one8(w[0][nb >> 1], 2 * (nb & 1) + s, magic_v);
-                lb[nb][s] = two8(w[1][nb], s, magic_v);
-            }
-        finish(hb, lb, a0, a1, sc, acc);
+        for (int p = 0; p < 4; ++p)   // pair p: low fields at 8 s + 2 p -> bits 0-1, high bits at 4 q + p -> bit 2
+            r[p] = merge_pair<0x00030003u, 0x00070007u>(lo >> (8 * s + 2 * p), shr_signed(hi, 4 * q + p - 2), magic_v);
+        return __builtin_bit_cast(bf16x8, u32x4{r[0], r[1], r[2], r[3]});
     }
     __host__ __device__ static Planes expert(Planes P, int64_t e, int64_t w_estride) {
         P.p0 += e * (w_estride / 4);
