@@ -183,6 +183,22 @@ def test_w8_partials_layout_and_validation():
     assert _call("w8_skinny_gemm_partials", fake, 64, fake, fake, fake, None, 1, 64, 64, None) == B.VW4_EINVAL
 
 
+def test_k_beyond_the_largest_is_rejected():
+    """K = 65536 is the largest accepted; the next multiple of 64 is refused
+    by every format's workspace query and partial-slice layout."""
+    for name in ("vw4_w8_workspace_bytes", "vw4_w6_workspace_bytes", "vw4_w5_workspace_bytes",
+                 "vw4_w3_workspace_bytes", "vw4_w2_workspace_bytes", "vw4_f16_workspace_bytes",
+                 "vw4_bf16_workspace_bytes"):
+        assert getattr(B.lib(), name)(4, 64, 65600) == 0, name
+    for fn in (B.w8_partials_layout, B.w6_partials_layout, B.w5_partials_layout, B.w3_partials_layout,
+               B.w2_partials_layout):
+        with pytest.raises(B.VW4Error):
+            fn(4, 64, 65600)
+        assert fn(4, 64, 65536)[0] >= 1
+    with pytest.raises(B.VW4Error):
+        B.gemm_partials_layout(4, 64, 65600)
+
+
 def test_w16_sizes_and_validation():
     assert B.lib().vw4_w16_packed_bytes(100, 320) == 128 * 320 * 2
     assert B.lib().vw4_w16_packed_bytes(10, 100) == 0
