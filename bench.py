@@ -628,7 +628,7 @@ def verify27b_workload(args):
     linears = {}
     for nm in by_name:
         N, Kd = shapes[nm]
-        b = N * Kd * bpw + M * Kd * 2 + (M * (N // 2) * 2 if (nm == "gate_up" and fmt == "w4") else M * N * 4)
+        b = N * Kd * bpw + M * Kd * 2 + (M * (N // 2) * 2 if nm == "gate_up" else M * N * 4)
         us = time_graphs([lambda nm=nm: dec.gemm_pass(M, names=(nm,))], 20 if nm != "lm_head" else 200)[0] * 1e3
         linears[nm] = {"N": N, "K": Kd, "avg_us": round(us, 2), "GBs": round(b / (us * 1e-6) / 1e9, 1),
                        "frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}

@@ -476,6 +476,37 @@ VW4_API int w8_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_
                                     void* stream);
 
 /* ------------------------------------------------------------------------
+ * Gate|up projection with the SwiGLU in the epilogue, in the formats other
+ * than W4 (w4_skinny_gemm_swiglu above): a[m][f] = bf16(silu(g) * u), row
+ * stride lda >= F, from one matrix of 2 F rows in the gate/up-interleaved
+ * order of w4_skinny_gemm_rmsnorm_swiglu (rows 64 t .. 64 t + 31 the gate rows
+ * of features 32 t .. 32 t + 31, rows 64 t + 32 .. 64 t + 63 their up rows;
+ * F % 32 == 0), packed by the format's own pack.  x bf16 [M][ldx] (ldx >= K,
+ * ldx % 8 == 0, 16-byte aligned), M in 1..8, K % 64 == 0 and K <= 65536.
+ * Each GEMM's sums are fp32 in an order that depends only on (F, K).
+ * VW4_EINVAL on a bad shape, a null or misaligned pointer.
+ * ------------------------------------------------------------------------ */
+VW4_API int w8_skinny_gemm_swiglu(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, const uint8_t* w_lo,
+                                  const uint16_t* scales_packed, uint16_t* a, int64_t lda, int32_t M, int32_t F,
+                                  int32_t K, void* stream);
+VW4_API int w6_skinny_gemm_swiglu(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, const uint8_t* w_lo,
+                                  const uint16_t* scales_packed, uint16_t* a, int64_t lda, int32_t M, int32_t F,
+                                  int32_t K, void* stream);
+VW4_API int w5_skinny_gemm_swiglu(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, const uint8_t* w_lo,
+                                  const uint16_t* scales_packed, uint16_t* a, int64_t lda, int32_t M, int32_t F,
+                                  int32_t K, void* stream);
+VW4_API int w3_skinny_gemm_swiglu(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, const uint8_t* w_lo,
+                                  const uint16_t* scales_packed, uint16_t* a, int64_t lda, int32_t M, int32_t F,
+                                  int32_t K, void* stream);
+VW4_API int w2_skinny_gemm_swiglu(const uint16_t* x, int64_t ldx, const uint8_t* w_packed,
+                                  const uint16_t* scales_packed, uint16_t* a, int64_t lda, int32_t M, int32_t F,
+                                  int32_t K, void* stream);
+VW4_API int f16_skinny_gemm_swiglu(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, uint16_t* a,
+                                   int64_t lda, int32_t M, int32_t F, int32_t K, void* stream);
+VW4_API int bf16_skinny_gemm_swiglu(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, uint16_t* a,
+                                    int64_t lda, int32_t M, int32_t F, int32_t K, void* stream);
+
+/* ------------------------------------------------------------------------
  * Unquantised 16-bit float weights: the widest end of the same BaseRT list
  * (Q2 ... FP16), as fp16 and as bf16.  w[N][K] holds IEEE binary16 (fp16)
  * or bfloat16 bit patterns; there are no scales.

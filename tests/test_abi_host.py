@@ -199,6 +199,18 @@ def test_k_beyond_the_largest_is_rejected():
         B.gemm_partials_layout(4, 64, 65600)
 
 
+def test_swiglu_entry_points_validate():
+    fake = ctypes.c_void_p(0x100000)
+    for fmt in ("w8", "w6", "w5", "w3"):
+        f = f"{fmt}_skinny_gemm_swiglu"
+        assert _call(f, fake, 64, fake, fake, fake, fake, 32, 4, 48, 64, None) == B.VW4_EINVAL     # F % 32
+        assert _call(f, fake, 64, fake, fake, fake, fake, 16, 4, 32, 64, None) == B.VW4_EINVAL     # lda < F
+        assert _call(f, fake, 64, fake, fake, fake, None, 32, 4, 32, 64, None) == B.VW4_EINVAL     # null a
+    assert _call("w2_skinny_gemm_swiglu", fake, 64, fake, fake, fake, 32, 9, 32, 64, None) == B.VW4_EINVAL
+    for kind in ("f16", "bf16"):
+        assert _call(f"{kind}_skinny_gemm_swiglu", fake, 60, fake, fake, 32, 1, 32, 64, None) == B.VW4_EINVAL
+
+
 def test_w16_sizes_and_validation():
     assert B.lib().vw4_w16_packed_bytes(100, 320) == 128 * 320 * 2
     assert B.lib().vw4_w16_packed_bytes(10, 100) == 0

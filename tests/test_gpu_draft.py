@@ -289,9 +289,9 @@ def test_gemm_pass_counts_and_bytes(fmt):
     M, d, F, nqkv = 4, cfg["d"], cfg["F"], (cfg["nq"] + 2 * cfg["nkv"]) * cfg["hd"]
     nw = cfg["layers"] * (nqkv * d + d * d + 2 * F * d + d * F) + cfg["V"] * d
     assert wb == int(round(nw * per_w))
-    # activations in (bf16) and outputs out (fp32 partial sums; W4's gate|up
-    # writes the bf16 SwiGLU of its epilogue instead)
-    gate_up_out = M * F * 2 if fmt == "w4" else M * 2 * F * 4
+    # activations in (bf16) and outputs out (fp32 partial sums; gate|up writes
+    # the bf16 SwiGLU of its epilogue instead)
+    gate_up_out = M * F * 2
     act = cfg["layers"] * (M * d * 2 + M * nqkv * 4 + M * d * 2 + M * d * 4 + M * d * 2 + gate_up_out
                            + M * F * 2 + M * d * 4) + M * d * 2 + M * cfg["V"] * 4
     assert alg == wb + act

@@ -62,7 +62,7 @@ ORACLE_FORMATS = {"w8": (oracle.w8_quantize, oracle.w8_gemm), "w6": (oracle.w6_q
 
 
 def _linear(v, fmt):
-    """A device matrix in format fmt from host fp32 weights (natural row order)."""
+    """A device matrix in format fmt from host fp32 weights (rows as given)."""
     if fmt in ("f16", "bf16"):
         bits = ORACLE_FORMATS[fmt][0](v)[0]
         return W16Linear.from_bits(dev(bits.view(np.int16)), fmt)
@@ -76,10 +76,11 @@ def _device_weights(hm, fmt="w4"):
         for k, v in l.items():
             if k in ("g1", "g2"):
                 d[k] = dev(v)
-            elif fmt != "w4":      # natural gate|up order (the SwiGLU runs on the partials)
-                d[k] = _linear(v, fmt)
             elif k == "gate_up":   # the fused SwiGLU GEMM takes gate/up-interleaved rows
-                d[k] = W4Linear.from_fp32(dev(B.interleave_gate_up(v)))
+                vi = B.interleave_gate_up(v)
+                d[k] = W4Linear.from_fp32(dev(vi)) if fmt == "w4" else _linear(vi, fmt)
+            elif fmt != "w4":
+                d[k] = _linear(v, fmt)
             else:
                 d[k] = W4Linear.from_fp32(dev(v))
         layers.append(d)
@@ -170,8 +171,8 @@ def _dense_cfg(layers, V):
 @pytest.mark.parametrize("fmt", ["w8", "w6", "w5", "w3", "w2", "f16", "bf16"])
 def test_forward_matches_oracle_small_decoder_other_format(fmt):
     """The same small decoder with every linear and the LM head in another
-    weight format (gate|up partials through the standalone SwiGLU) against
-    the oracle's composition in that format: each op on the GPU's own inputs
+    weight format (gate|up with the SwiGLU in its epilogue) against the
+    oracle's composition in that format: each op on the GPU's own inputs
     at its bar, then the verify rows equal to the one-row steps bit for bit."""
     import torch
     cfg = TINY

@@ -132,6 +132,13 @@ SIGNATURES = {
     "w4_skinny_gemm_rmsnorm_partials": (ctypes.c_int, [_P, _P, _P, _F32, _P, _P, _P, _I32, _I32, _I32, _P]),
     "w4_skinny_gemm_rmsnorm_swiglu": (ctypes.c_int, [_P, _P, _P, _F32, _P, _P, _P, _I64, _I32, _I32, _I32, _P]),
     "w4_skinny_gemm_swiglu": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I64, _I32, _I32, _I32, _P]),
+    "w8_skinny_gemm_swiglu": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P]),
+    "w6_skinny_gemm_swiglu": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P]),
+    "w5_skinny_gemm_swiglu": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P]),
+    "w3_skinny_gemm_swiglu": (ctypes.c_int, [_P, _I64, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _P]),
+    "w2_skinny_gemm_swiglu": (ctypes.c_int, [_P, _I64, _P, _P, _P, _I64, _I32, _I32, _I32, _P]),
+    "f16_skinny_gemm_swiglu": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _I32, _I32, _I32, _P]),
+    "bf16_skinny_gemm_swiglu": (ctypes.c_int, [_P, _I64, _P, _P, _I64, _I32, _I32, _I32, _P]),
     "w4_grouped_gemm_swiglu": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _P, _I32, _P, _I64, _I32,
                                               _I32, _I32, _P]),
     "vw4_moe_route": (ctypes.c_int, [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
@@ -808,6 +815,34 @@ def interleave_gate_up(w):
         return _np.ascontiguousarray(w[order])
     import torch
     return w[torch.as_tensor(order, device=w.device)].contiguous()
+
+
+def two_plane_gemm_swiglu(fmt: str, x, w_hi, w_lo, scales_packed, a, lda: int, M: int, F: int, K: int,
+                          stream=None, ldx: int | None = None):
+    """Gate|up with the SwiGLU epilogue in a two-plane format (fmt w8, w6, w5, w3; gate/up-interleaved rows)."""
+    assert fmt in ("w8", "w6", "w5", "w3")
+    ldx = x.stride(0) if ldx is None else ldx
+    name = f"{fmt}_skinny_gemm_swiglu"
+    _check(name, getattr(lib(), name)(_ptr(x), ldx, _ptr(w_hi), _ptr(w_lo), _ptr(scales_packed), _ptr(a), lda, M, F,
+                                      K, _stream(stream)))
+    return a
+
+
+def w2_skinny_gemm_swiglu(x, w_packed, scales_packed, a, lda: int, M: int, F: int, K: int, stream=None,
+                          ldx: int | None = None):
+    ldx = x.stride(0) if ldx is None else ldx
+    _check("w2_skinny_gemm_swiglu", lib().w2_skinny_gemm_swiglu(_ptr(x), ldx, _ptr(w_packed), _ptr(scales_packed),
+                                                                _ptr(a), lda, M, F, K, _stream(stream)))
+    return a
+
+
+def w16_skinny_gemm_swiglu(x, w_packed, a, lda: int, M: int, F: int, K: int, kind: str = "f16", stream=None,
+                           ldx: int | None = None):
+    assert kind in ("f16", "bf16")
+    ldx = x.stride(0) if ldx is None else ldx
+    name = f"{kind}_skinny_gemm_swiglu"
+    _check(name, getattr(lib(), name)(_ptr(x), ldx, _ptr(w_packed), _ptr(a), lda, M, F, K, _stream(stream)))
+    return a
 
 
 def w4_skinny_gemm_swiglu(x, w_packed, scales_packed, a, lda: int, M: int, F: int, K: int, stream=None,

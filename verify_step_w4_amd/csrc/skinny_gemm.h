@@ -433,6 +433,9 @@ struct GemmPlan {
 // matrices per launch (grouped launches spread the wavefront target over all
 // of them).  Defined in w4_gemm.hip.
 GemmPlan plan_gemm(int M, int N, int K, int slots = 1);
+// The plan of a gate|up GEMM with the SwiGLU epilogue (N = 2 F rows): one K slice
+// per tile (S_grid == 1), S_wg wavefronts per workgroup.
+GemmPlan plan_swiglu(int N, int K, int slots = 1);
 
 // The plain call of any format: validated, one launch (plus the reduction
 // launch of split plans).  w0 / w1: the format's planes (w1 unused for W4).
@@ -489,6 +492,27 @@ int skinny_gemm_partials_run(const char* name, const uint16_t* x, int64_t ldx, c
     hipLaunchKernelGGL((skinny_gemm_kernel<Fmt, false, false>), dim3(p.ntiles, p.S_grid, max_slots),
                        dim3(64 * p.S_wg), 0, st, x, ldx, P, s, (void*)part, p.Npad, VW4_F32, M, N, p.G, p.S_wg,
                        p.S_grid, part, p.Npad, 0x000F000Fu, 0x43004300u, grp, NormIn{});
+    return check_launch(name);
+}
+
+// Gate|up projection of any format with the SwiGLU in its epilogue: the
+// matrix holds 2 F rows in the gate/up-interleaved order of the SWIGLU mode;
+// a[m][f] = bf16(silu(g) * u), row stride lda >= F.
+template <class Fmt>
+int skinny_gemm_swiglu_run(const char* name, const uint16_t* x, int64_t ldx, const uint8_t* w0, const uint8_t* w1,
+                           const uint16_t* s, uint16_t* a, int64_t lda, int M, int F, int K, hipStream_t st) {
+    VW4_REQUIRE(M >= 1 && M <= MAX_M && F >= 32 && F % 32 == 0 && K >= 64 && K % 64 == 0 && K <= 65536, VW4_EINVAL,
+                "%s: bad shape M=%d F=%d K=%d (F must be a multiple of 32)", name, M, F, K);
+    VW4_REQUIRE(x && w0 && w1 && s && a && lda >= F, VW4_EINVAL, "%s: bad output or null pointer", name);
+    VW4_REQUIRE(ldx >= K && ldx % 8 == 0 && aligned(x, 16), VW4_EINVAL,
+                "%s: x needs ldx >= K, ldx %% 8 == 0 and 16-byte alignment", name);
+    VW4_REQUIRE(aligned(w0, 16) && aligned(w1, 16) && aligned(s, 8) && aligned(a, 2), VW4_EINVAL,
+                "%s: misaligned pointer", name);
+    const GemmPlan p = plan_swiglu(2 * F, K, 1);
+    const Planes P{(const u32x4*)w0, (const u32x4*)w1};
+    hipLaunchKernelGGL((skinny_gemm_kernel<Fmt, false, true>), dim3(p.ntiles, 1, 1), dim3(64 * p.S_wg), 0, st, x,
+                       ldx, P, s, (void*)a, lda, VW4_BF16, M, 2 * F, p.G, p.S_wg, p.S_grid, (float*)nullptr, p.Npad,
+                       0x000F000Fu, 0x43004300u, GemmGroup{}, NormIn{});
     return check_launch(name);
 }
 

@@ -83,4 +83,16 @@ int bf16_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w_p
     return w16_partials<sg::FmtB16>("bf16_skinny_gemm_partials", x, ldx, w_packed, part, M, N, K, stream);
 }
 
+int f16_skinny_gemm_swiglu(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, uint16_t* a, int64_t lda,
+                           int32_t M, int32_t F, int32_t K, void* stream) {
+    return sg::skinny_gemm_swiglu_run<sg::FmtF16>("f16_skinny_gemm_swiglu", x, ldx, w_packed, w_packed,
+                                                  (const uint16_t*)w_packed, a, lda, M, F, K, (hipStream_t)stream);
+}
+
+int bf16_skinny_gemm_swiglu(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, uint16_t* a, int64_t lda,
+                            int32_t M, int32_t F, int32_t K, void* stream) {
+    return sg::skinny_gemm_swiglu_run<sg::FmtB16>("bf16_skinny_gemm_swiglu", x, ldx, w_packed, w_packed,
+                                                  (const uint16_t*)w_packed, a, lda, M, F, K, (hipStream_t)stream);
+}
+
 }  // extern "C"

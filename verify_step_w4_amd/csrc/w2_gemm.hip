@@ -47,4 +47,10 @@ int w2_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w_pac
                                                    scales_packed, part, M, N, K, (hipStream_t)stream);
 }
 
+int w2_skinny_gemm_swiglu(const uint16_t* x, int64_t ldx, const uint8_t* w_packed, const uint16_t* scales_packed,
+                          uint16_t* a, int64_t lda, int32_t M, int32_t F, int32_t K, void* stream) {
+    return sg::skinny_gemm_swiglu_run<sg::FmtW2>("w2_skinny_gemm_swiglu", x, ldx, w_packed, w_packed, scales_packed, a,
+                                                 lda, M, F, K, (hipStream_t)stream);
+}
+
 }  // extern "C"

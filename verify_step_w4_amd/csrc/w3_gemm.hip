@@ -50,4 +50,11 @@ int w3_skinny_gemm_partials(const uint16_t* x, int64_t ldx, const uint8_t* w_hi,
                                                    M, N, K, (hipStream_t)stream);
 }
 
+int w3_skinny_gemm_swiglu(const uint16_t* x, int64_t ldx, const uint8_t* w_hi, const uint8_t* w_lo,
+                          const uint16_t* scales_packed, uint16_t* a, int64_t lda, int32_t M, int32_t F, int32_t K,
+                          void* stream) {
+    return sg::skinny_gemm_swiglu_run<sg::FmtW3>("w3_skinny_gemm_swiglu", x, ldx, w_hi, w_lo, scales_packed, a,
+                                                   lda, M, F, K, (hipStream_t)stream);
+}
+
 }  // extern "C"

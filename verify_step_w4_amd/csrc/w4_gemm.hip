@@ -79,6 +79,29 @@ GemmPlan plan_gemm(int M, int N, int K, int slots) {
 }
 
 
+// SwiGLU epilogue: one slice of K per tile, S_wg wavefronts per workgroup.
+// One wavefront per tile as soon as the tiles alone give one per CU: measured
+// on MI355X at M = 4, gate|up 34816 x 5120 (544 tiles) takes 21.5 us with one
+// wavefront per tile against 24.7 with four (the LDS reduction and the
+// uneven 2-3 four-wavefront workgroups per CU cost more than the longer
+// per-wavefront K stream), and the grouped 30 x 1536 x 2048 (720 tiles) 12.1
+// against 15.0 with three.  Fewer tiles: up to 4 wavefronts split K.
+GemmPlan plan_swiglu(int N, int K, int slots) {
+    GemmPlan p;
+    p.G = K / 64;
+    p.ntiles = (N + 63) / 64;
+    p.Npad = (int64_t)p.ntiles * 64;
+    const int units = p.ntiles * slots;
+    const int ncu = device_cus();
+    int swg = (ncu + units - 1) / units;
+    if (swg > 4) swg = 4;
+    if (swg > p.G) swg = p.G;
+    p.S_wg = swg < 1 ? 1 : swg;
+    p.S_grid = 1;
+    p.ws_bytes = 0;
+    return p;
+}
+
 }  // namespace sg
 
 template <bool NORM, bool SWIGLU>
@@ -123,36 +146,13 @@ int gemm_rmsnorm_partials(const uint16_t* resid, const uint16_t* gamma, const fl
     return check_launch("w4_skinny_gemm_rmsnorm_partials");
 }
 
-// SwiGLU epilogue: one slice of K per tile, S_wg wavefronts per workgroup.
-// One wavefront per tile as soon as the tiles alone give one per CU: measured
-// on MI355X at M = 4, gate|up 34816 x 5120 (544 tiles) takes 21.5 us with one
-// wavefront per tile against 24.7 with four (the LDS reduction and the
-// uneven 2-3 four-wavefront workgroups per CU cost more than the longer
-// per-wavefront K stream), and the grouped 30 x 1536 x 2048 (720 tiles) 12.1
-// against 15.0 with three.  Fewer tiles: up to 4 wavefronts split K.
-static GemmPlan plan_swiglu(int N, int K, int slots) {
-    GemmPlan p;
-    p.G = K / 64;
-    p.ntiles = (N + 63) / 64;
-    p.Npad = (int64_t)p.ntiles * 64;
-    const int units = p.ntiles * slots;
-    const int ncu = device_cus();
-    int swg = (ncu + units - 1) / units;
-    if (swg > 4) swg = 4;
-    if (swg > p.G) swg = p.G;
-    p.S_wg = swg < 1 ? 1 : swg;
-    p.S_grid = 1;
-    p.ws_bytes = 0;
-    return p;
-}
-
 int gemm_swiglu(const uint16_t* x, int64_t ldx, const NormIn* nrm, const uint8_t* w, const uint16_t* s, uint16_t* a,
                 int64_t lda, int M, int F, int K, hipStream_t st, const GemmGroup& grp, int slots) {
     VW4_REQUIRE(M >= 1 && M <= GEMM_MAX_M && F >= 32 && F % 32 == 0 && K >= 64 && K % 64 == 0 && K <= 65536,
                 VW4_EINVAL, "w4 GEMM + SwiGLU: bad shape M=%d F=%d K=%d (F must be a multiple of 32)", M, F, K);
     VW4_REQUIRE(w && s && a && lda >= F, VW4_EINVAL, "w4 GEMM + SwiGLU: bad output or null pointer");
     VW4_REQUIRE(aligned(w, 16) && aligned(s, 8) && aligned(a, 2), VW4_EINVAL, "w4 GEMM + SwiGLU: misaligned pointer");
-    const GemmPlan p = plan_swiglu(2 * F, K, slots);
+    const GemmPlan p = sg::plan_swiglu(2 * F, K, slots);
     int rc;
     if (nrm) {
         VW4_REQUIRE(nrm->resid && nrm->gamma && nrm->ssq && aligned(nrm->resid, 16) && aligned(nrm->gamma, 16),

@@ -58,6 +58,10 @@ class W4Linear:
     def workspace_bytes(self, M: int) -> int:
         return B.gemm_workspace_bytes(M, self.N, self.K)
 
+    def swiglu(self, x, a, M: int, stream=None):
+        """a[:M][:N/2] = bf16(silu(gate) * up): this matrix holds gate/up-interleaved rows (B.interleave_gate_up)."""
+        B.w4_skinny_gemm_swiglu(x, self.packed, self.pscales, a, a.stride(0), M, self.N // 2, self.K, stream)
+
     def nbytes(self) -> int:
         return int(self.N * self.K * BYTES_PER_WEIGHT)
 
@@ -80,6 +84,10 @@ class _TwoPlaneOps:
 
     def workspace_bytes(self, M: int) -> int:
         return getattr(B, f"{self._FMT}_workspace_bytes")(M, self.N, self.K)
+
+    def swiglu(self, x, a, M: int, stream=None):
+        B.two_plane_gemm_swiglu(self._FMT, x, self.hi, self.lo, self.pscales, a, a.stride(0), M, self.N // 2, self.K,
+                                stream)
 
 
 class W8Linear(_TwoPlaneOps):
@@ -165,6 +173,9 @@ class W16Linear:
 
     def workspace_bytes(self, M: int) -> int:
         return B.w16_workspace_bytes(M, self.N, self.K, self.kind)
+
+    def swiglu(self, x, a, M: int, stream=None):
+        B.w16_skinny_gemm_swiglu(x, self.packed, a, a.stride(0), M, self.N // 2, self.K, kind=self.kind, stream=stream)
 
     def nbytes(self) -> int:
         return self.N * self.K * 2
@@ -256,6 +267,9 @@ class W2Linear:
 
     def workspace_bytes(self, M: int) -> int:
         return B.w2_workspace_bytes(M, self.N, self.K)
+
+    def swiglu(self, x, a, M: int, stream=None):
+        B.w2_skinny_gemm_swiglu(x, self.packed, self.pscales, a, a.stride(0), M, self.N // 2, self.K, stream)
 
     def nbytes(self) -> int:
         return self.N * self.K // 4 + self.N * (self.K // 64) * 2
@@ -387,10 +401,9 @@ DENSE_27B = dict(d=5120, nq=40, nkv=8, hd=128, F=17408, layers=64, V=151936, eps
 
 class Decoder:
     """Pre-norm dense decoder with GQA attention and a SwiGLU FFN, every linear
-    a skinny GEMM in one weight format (fmt, one of WEIGHT_FORMATS).  In W4 the
-    gate|up matrix is in the gate/up-interleaved row order of
-    B.interleave_gate_up, with the SwiGLU in that GEMM's epilogue; the other
-    formats keep the natural order and run the SwiGLU on the partial sums.  One call of ``forward`` scores M rows at positions
+    a skinny GEMM in one weight format (fmt, one of WEIGHT_FORMATS).  In every
+    format the gate|up matrix is in the gate/up-interleaved row order of
+    B.interleave_gate_up, with the SwiGLU in that GEMM's epilogue.  One call of ``forward`` scores M rows at positions
     L .. L+M-1 (the verify pass); M = 1 is an autoregressive step.  Weights,
     KV caches and activation buffers are allocated once (device-resident)."""
 
@@ -447,8 +460,9 @@ class Decoder:
         uniform int8 codes with fp16 scales in [1e-4, 3e-4] (the same spread);
         W6, W5, W3, W2: uniform codes with fp16 scales in [4e-4, 1.2e-3]; f16,
         bf16: N(0, 0.02) rounded to the type.  RMSNorm gains ~N(1, 0.02) in
-        bf16.  Outside W4 the gate|up matrix keeps its natural row order (the
-        SwiGLU runs on its partials)."""
+        bf16.  The gate|up matrices are random draws, so their row order is
+        immaterial; weights from a checkpoint would be interleaved with
+        B.interleave_gate_up before packing."""
         import torch
         d, nq, nkv, hd, F, nl, V = (cfg[k] for k in ("d", "nq", "nkv", "hd", "F", "layers", "V"))
         nqkv = (nq + 2 * nkv) * hd
@@ -518,11 +532,7 @@ class Decoder:
             # FFN block: gate|up with the SwiGLU in the GEMM epilogue
             N, K = self.shapes["gate_up"]
             hook("pre", "gate_up")
-            if isinstance(W["gate_up"], W4Linear):
-                B.w4_skinny_gemm_swiglu(h, W["gate_up"].packed, W["gate_up"].pscales, self.a, F, M, F, K, stream)
-            else:
-                S, ldp = self._partials(W, "gate_up", h, M, stream)
-                B.swiglu(self.parts["gate_up"], S, ldp, M, F, self.a, stream)
+            W["gate_up"].swiglu(h, self.a, M, stream)
             hook("post", "gate_up")
             hook("pre", "down")
             S, ldp = self._partials(W, "down", self.a[:M], M, stream)
@@ -556,8 +566,8 @@ class Decoder:
                 if name not in names:
                     continue
                 N, K = self.shapes[name]
-                if name == "gate_up" and isinstance(W[name], W4Linear):
-                    B.w4_skinny_gemm_swiglu(self.h[:M], W[name].packed, W[name].pscales, self.a, F, M, F, K, stream)
+                if name == "gate_up":
+                    W[name].swiglu(self.h[:M], self.a, M, stream)
                 else:
                     x = {"qkv": self.h, "o": self.attn, "gate_up": self.h, "down": self.a}[name]
                     self._partials(W, name, x[:M], M, stream)
@@ -569,14 +579,13 @@ class Decoder:
 
     def gemm_alg_bytes(self, M: int) -> int:
         """Algorithmic bytes of one forward's GEMMs: each weight (code + scale,
-        or 16-bit weight) once, activations in, fp32 outputs out (W4's gate|up:
-        the bf16 SwiGLU of its epilogue)."""
+        or 16-bit weight) once, activations in, fp32 outputs out (gate|up: the
+        bf16 SwiGLU of its epilogue)."""
         c = self.cfg
         tot = 0.0
         for name, (N, K) in self.shapes.items():
-            fused = isinstance(self.layers[0][name], W4Linear)
-            # SwiGLU epilogue output (bf16, W4), or fp32 partial sums
-            out = M * (N // 2) * 2 if (name == "gate_up" and fused) else M * N * 4
+            # SwiGLU epilogue output (bf16) of gate|up, fp32 partial sums otherwise
+            out = M * (N // 2) * 2 if name == "gate_up" else M * N * 4
             tot += sum(l[name].nbytes() for l in self.layers) + c["layers"] * (M * K * 2 + out)
         tot += self.lm_head.nbytes() + M * c["d"] * 2 + M * c["V"] * 4
         return int(tot)
