@@ -326,8 +326,10 @@ def test_graph_replay_matches_eager_steps():
     assert int(step_dev.item()) == 3
 
 
-def test_graph_replays_match_oracle_small_decoder():
-    """The verify step of the small decoder captured as a HIP graph (the form
+@pytest.mark.parametrize("fmt", ["w4", "w8", "w2", "bf16"])
+def test_graph_replays_match_oracle_small_decoder(fmt):
+    """The verify step of the small decoder (weights in format fmt) captured
+    as a HIP graph (the form
     the benchmark times) and replayed three times, with eager work and a new
     Philox step each time.  Every replay: its logits equal those of an eager
     forward whose every op passed the teacher-forced oracle checks; its LM
@@ -340,9 +342,10 @@ def test_graph_replays_match_oracle_small_decoder():
     cfg = TINY
     M, L, Lmax = 4, 37, 64
     d, nq, hd, V, eps = cfg["d"], cfg["nq"], cfg["hd"], cfg["V"], cfg["eps"]
-    log("graph replays vs oracle, small decoder")
+    log(f"graph replays vs oracle, small decoder, {fmt}")
     hm = _host_model(cfg, 4244)
-    dec = Decoder(cfg, M, Lmax, weights=_device_weights(hm), kv_fill=False)
+    dec = Decoder(cfg, M, Lmax, weights=_device_weights(hm, fmt), kv_fill=False)
+    quant, gemm = (oracle.w4_quantize, oracle.w4_gemm) if fmt == "w4" else ORACLE_FORMATS[fmt]
     g = synth.rng(83)
     for li in range(cfg["layers"]):
         dec.Kc[li].copy_(dev(synth.f32_to_bf16_bits(synth.normal_f32(g, (cfg["nkv"], Lmax, hd), 1.0))))
@@ -358,13 +361,13 @@ def test_graph_replays_match_oracle_small_decoder():
     cap = DecoderCapture(dec, M)
     vs.run(xd, L, qd, dd, T, top_p, seed, 0, gemm_hook=cap)
     torch.cuda.synchronize()
-    check_decoder_ops(cap, hm, cfg, x, L)
+    check_decoder_ops(cap, hm, cfg, x, L, quant=quant, gemm=gemm)
     eager = host(dec.logits[:M]).copy()
     step_dev = torch.zeros(1, dtype=torch.int64, device="cuda")
     gr = vs.capture(xd, L, qd, dd, T, top_p, seed, step_dev)
     step_dev.zero_()
     torch.cuda.synchronize()
-    lm_q = oracle.w4_quantize(hm["lm_head"])
+    lm_q = quant(hm["lm_head"])
     ties = B.FLAG_TOPP_TIE | B.FLAG_ACCEPT_TIE | B.FLAG_CDF_TIE
     last = cfg["layers"] - 1
     flagged = 0
@@ -375,7 +378,7 @@ def test_graph_replays_match_oracle_small_decoder():
         z = host(dec.logits[:M]).copy()
         assert np.array_equal(z, eager), k
         hfin = host(dec.h[:M]).copy()
-        assert gemm_rel_err(z, oracle.w4_gemm(hfin, *lm_q)) <= GEMM_RTOL, k
+        assert gemm_rel_err(z, gemm(hfin, *lm_q)) <= GEMM_RTOL, k
         bf16_close(hfin, oracle.rmsnorm(host(dec.last_resid[:M]), hm["final_gamma"], eps), what=f"final norm {k}")
         att_ref = oracle.decode_attn(oracle.bf16_value(host(dec.q[:M])), host(dec.Kc[last]),
                                      rows_from_vb(host(dec.Vc[last])), L).reshape(M, nq * hd)
