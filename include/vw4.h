@@ -49,7 +49,7 @@ extern "C" {
 
 #define VW4_OK 0
 #define VW4_EINVAL (-1)       /* bad shape, alignment or parameter */
-#define VW4_EUNSUPPORTED (-2) /* valid request this build does not handle */
+#define VW4_EUNSUPPORTED (-2) /* valid request the library does not handle */
 #define VW4_EHIP (-3)         /* HIP runtime or launch failure */
 #define VW4_EWORKSPACE (-4)   /* workspace missing or too small */
 
