@@ -197,7 +197,9 @@ VW4_API int verify_logits(const uint16_t* hidden, int64_t ldh, const uint8_t* lm
  * out_flags[b] = VW4_FLAG_* bits (a row flagged non-finite gives tokens -1 and
  * n_acc -1).  D = 0 is plain sampling of p_0 (one autoregressive step).
  * Requires 1 <= B <= 2^24, 0 <= D <= 7, 1 <= V <= 2^24, draft ids in [0, V).
- * Workspace: vw4_accept_workspace_bytes(B, V).
+ * Workspace: vw4_accept_workspace_bytes(B, V) (for V > 16384 and B <= 8 it
+ * also holds the row's fp64 residual masses, 8 V bytes per problem, which the
+ * sampling pass reads back instead of recomputing them).
  * ------------------------------------------------------------------------ */
 VW4_API size_t vw4_accept_workspace_bytes(int32_t B, int32_t V);
 

@@ -187,6 +187,60 @@ def test_accept_matches_oracle(V, D, T, top_p):
         assert len(set(nacc.tolist())) >= 2   # more than one acceptance length occurred
 
 
+@pytest.mark.parametrize("V,D,T,top_p,case", [
+    (151936, 3, 0.6, 0.95, "mixed"), (151936, 0, 0.6, 0.95, "mixed"), (20000, 2, 1.0, 1.0, "mixed"),
+    (151936, 2, 1.0, 0.95, "r_zero"),
+])
+def test_accept_kept_masses_equal_recomputed(V, D, T, top_p, case):
+    """Above 16384 entries, batches of at most 8 problems keep the chunk pass's
+    residual masses for the sampling pass, larger batches recompute them: the
+    same 24 problems as three batches of 8 and as one batch of 24 give the same
+    tokens, counts and flags, and the kept form matches the oracle outside
+    flagged near-ties.  "r_zero": q >= p on the rejected row, so R = 0 and the
+    sampler falls back to p (the kept masses are not used there)."""
+    Bn, M = 24, D + 1
+    log(f"accept kept vs recomputed masses V={V} D={D} T={T} top_p={top_p} {case}")
+    z = synth.synthetic_logits(V + 31 * D, Bn * M, V, 1.5).reshape(Bn, M, V)
+    g = synth.rng(V * 11 + D)
+    if case == "r_zero":
+        # row 0: q slightly above p everywhere and the draft outside the top-p set
+        # (p = 0 there, q > 0): certain rejection at k = 0 with R = 0
+        q = np.zeros((Bn, D, V), np.float32)
+        drafts = np.zeros((Bn, D), np.int32)
+        for b in range(Bn):
+            for i in range(D):
+                _, pi = oracle.warp(z[b, i], T, top_p, want_p=True)
+                q[b, i] = (pi * (1 + 1e-6)).astype(np.float32)
+                out = np.flatnonzero(pi == 0.0)
+                drafts[b, i] = int(out[b % len(out)])
+                q[b, i, drafts[b, i]] = 1e-3
+    else:
+        ql = synth.normal_f32(g, (Bn, max(D, 1), V), 3.0)
+        ql[: Bn // 2, :, :] = z[: Bn // 2, :max(D, 1), :] / np.float32(T)
+        q = synth.softmax_f32(ql)[:, :D, :] if D else np.zeros((Bn, 0, V), np.float32)
+        drafts = (np.stack([synth.sample_drafts(g, q[b], 1)[0] for b in range(Bn)]) if D
+                  else np.zeros((Bn, 0), np.int32))
+    seed, step0 = synth.PHILOX_SEED_BASE + 5, 77
+    assert B.accept_workspace_bytes(8, V) > B.accept_workspace_bytes(9, V)    # the two layouts
+    tok, nacc, fl = run_accept(z, q, drafts, T, top_p, seed, step0)
+    parts = [run_accept(z[i:i + 8], q[i:i + 8], drafts[i:i + 8], T, top_p, seed, step0 + i) for i in range(0, Bn, 8)]
+    assert np.array_equal(np.concatenate([p[0] for p in parts]), tok)
+    assert np.array_equal(np.concatenate([p[1] for p in parts]), nacc)
+    assert np.array_equal(np.concatenate([p[2] for p in parts]), fl)
+    ties = B.FLAG_TOPP_TIE | B.FLAG_ACCEPT_TIE | B.FLAG_CDF_TIE
+    flagged = 0
+    for b in range(Bn):
+        ot, on, of = oracle.spec_accept(z[b], q[b] if D else np.zeros((0, V), np.float32),
+                                        drafts[b] if D else np.zeros(0, np.int32), T, top_p, seed, step0 + b)[:3]
+        if (of | int(fl[b])) & ties:
+            flagged += 1
+            continue
+        assert int(fl[b]) == of and int(nacc[b]) == on and np.array_equal(tok[b], ot), b
+    assert flagged <= 2
+    if case == "r_zero":
+        assert np.all(nacc == 0) and np.all(fl & B.FLAG_R_ZERO)
+
+
 def test_accept_special_cases():
     V, D = 2000, 3
     M = D + 1

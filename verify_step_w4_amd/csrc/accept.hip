@@ -38,6 +38,7 @@ constexpr int ASH = AT1 / 64 + 4;  // block-reduction scratch
 constexpr int ACHUNK = 4096;     // vocabulary entries per workgroup
 constexpr int AMAXP = 64;
 constexpr int AMAXD = 7;
+constexpr int AU = 16;  // elements per thread loaded together (one latency per tile)
 
 struct AcceptPart {
     double r;       // chunk sum of the residual r
@@ -46,9 +47,17 @@ struct AcceptPart {
     int32_t last_p; // last index with p_k > 0
 };
 
+// Problems per call whose residual masses the chunk kernel keeps for the
+// finishing workgroup (P * chunk doubles each, 1.2 MB at V = 151936): with
+// them the finish loads the located chunk's masses instead of recomputing
+// them (16 fp64 exponentials per thread on one CU).  Larger batches recompute;
+// both read the same values in the same order.
+constexpr int AKEEP_B = 8;
+
 struct AcceptLayout {
     int P, chunk, threads;
-    size_t off_part, off_state, total;
+    bool keep_r;
+    size_t off_part, off_state, off_r, total;
 };
 
 static AcceptLayout accept_layout(int B, int V) {
@@ -70,12 +79,16 @@ static AcceptLayout accept_layout(int B, int V) {
             L.P = ceil_div(V, L.chunk);
         }
     }
+    L.keep_r = L.P > 1 && L.chunk <= AT * AU && B <= AKEEP_B;
     size_t o = 0;
     L.off_part = o;
     o += (size_t)B * L.P * sizeof(AcceptPart);
     o = (o + 255) / 256 * 256;
     L.off_state = o;
     o += (size_t)B * 64;
+    o = (o + 255) / 256 * 256;
+    L.off_r = o;
+    if (L.keep_r) o += (size_t)B * L.P * L.chunk * sizeof(double);
     L.total = (o + 255) / 256 * 256;
     return L;
 }
@@ -112,7 +125,6 @@ __device__ __forceinline__ double p_val(float v, const vw4_rowstat& s, double T,
     return exp(((double)v - (double)s.max_logit) / T - s.log_z);
 }
 
-constexpr int AU = 16;  // elements per thread loaded together (one latency per tile)
 
 template <int NT>
 __device__ __forceinline__ double blk_sum(double v, double* sh) {
@@ -226,10 +238,11 @@ __device__ __forceinline__ ProblemState problem_state(const float* __restrict__ 
 }
 
 // Chunk w of the residual row of problem b: fixed-order sums of r and p_k.
+// rout (if set) receives each entry's mass r (chunk-relative index).
 template <int NT>
 __device__ __forceinline__ AcceptPart chunk_sums(const float* __restrict__ zk, const vw4_rowstat& sk,
                                                  const float* __restrict__ qk, double T, int c0, int c1, double* sh,
-                                                 int* shi) {
+                                                 int* shi, double* __restrict__ rout) {
     double sr = 0.0, sp = 0.0;
     int lr = -1, lp = -1;
     for (int base = c0; base < c1; base += NT * AU) {
@@ -251,6 +264,7 @@ __device__ __forceinline__ AcceptPart chunk_sums(const float* __restrict__ zk, c
             if (j < c1) {
                 const double pj = p_val(zv[u], sk, T, j);
                 const double rj = qk ? fmax(0.0, pj - (double)qv[u]) : pj;
+                if (rout) rout[j - c0] = rj;
                 sr += rj;
                 sp += pj;
                 if (rj > 0.0) lr = j;
@@ -268,11 +282,13 @@ __device__ __forceinline__ AcceptPart chunk_sums(const float* __restrict__ zk, c
 
 // Locate u * R among the chunk sums, rescan the chunk that holds it and
 // write the outputs of problem b.  pb: the P chunk parts (in LDS or global).
+// rkept (if set): the chunk kernel's masses r of this problem, [P][chunk].
 template <int NT>
 __device__ void finish_problem(const float* __restrict__ zk, const vw4_rowstat& sk, const float* __restrict__ qk,
                                const int32_t* __restrict__ db, const AcceptPart* pb, int P, int chunk, int D, int V,
                                double T, const ProblemState& ps, const double* s_u, int32_t* __restrict__ tb,
-                               int32_t* __restrict__ nacc_b, uint32_t* __restrict__ flags_b, double* sh, int* shi) {
+                               int32_t* __restrict__ nacc_b, uint32_t* __restrict__ flags_b, double* sh, int* shi,
+                               const double* __restrict__ rkept) {
     __shared__ int s_y;
     const int k = ps.k;
     uint32_t flags = ps.flags;
@@ -309,21 +325,31 @@ __device__ void finish_problem(const float* __restrict__ zk, const vw4_rowstat& 
         double cp = 0.0, cc = 0.0;
         if (per <= AU) {
             // the whole run in registers: one load, the masses computed once
-            float zv[AU], qv[AU];
-#pragma unroll
-            for (int u = 0; u < AU; ++u) {
-                zv[u] = (j0 + u < j1) ? zk[j0 + u] : 0.0f;
-                qv[u] = (resid && j0 + u < j1) ? qk[j0 + u] : 0.0f;
-            }
+            // (or, kept by the chunk kernel, loaded: the same values)
             double rv[AU];
             double mine = 0.0;
+            const double* rw = (rkept && !use_p) ? rkept + (int64_t)wc * chunk - a0 : nullptr;
+            if (rw) {
 #pragma unroll
-            for (int u = 0; u < AU; ++u) {
-                rv[u] = 0.0;
-                if (j0 + u < j1) {
-                    const double pj = p_val(zv[u], sk, T, j0 + u);
-                    rv[u] = resid ? fmax(0.0, pj - (double)qv[u]) : pj;
-                    mine += rv[u];
+                for (int u = 0; u < AU; ++u) rv[u] = (j0 + u < j1) ? rw[j0 + u] : 0.0;
+#pragma unroll
+                for (int u = 0; u < AU; ++u)
+                    if (j0 + u < j1) mine += rv[u];
+            } else {
+                float zv[AU], qv[AU];
+#pragma unroll
+                for (int u = 0; u < AU; ++u) {
+                    zv[u] = (j0 + u < j1) ? zk[j0 + u] : 0.0f;
+                    qv[u] = (resid && j0 + u < j1) ? qk[j0 + u] : 0.0f;
+                }
+#pragma unroll
+                for (int u = 0; u < AU; ++u) {
+                    rv[u] = 0.0;
+                    if (j0 + u < j1) {
+                        const double pj = p_val(zv[u], sk, T, j0 + u);
+                        rv[u] = resid ? fmax(0.0, pj - (double)qv[u]) : pj;
+                        mine += rv[u];
+                    }
                 }
             }
             double run = before + blk_prefix_excl<NT>(mine, sh);
@@ -424,6 +450,7 @@ struct AcceptArgs {
     uint32_t* out_flags;
     AcceptPart* parts;
     ProblemSlot* states;   // per problem, written by workgroup 0 of the chunk kernel
+    double* rkept;         // [B][P][chunk] masses r kept for the finish, or null
     const uint64_t* step_dev;  // if set, the first problem's step is read here (graph replays)
     uint64_t row0, cstream;    // Philox counter words 1 (row offset) and 2 (stream): 0 for verify
 };
@@ -465,7 +492,8 @@ __global__ __launch_bounds__(NT) void accept_chunk_kernel(AcceptArgs a) {
     const vw4_rowstat sk = s_st[k];
     const float* qk = (k < a.D) ? qb + (int64_t)k * a.V : nullptr;
     const int c0 = w * a.chunk, c1 = min(a.V, c0 + a.chunk);
-    const AcceptPart part = chunk_sums<NT>(zk, sk, qk, T, c0, c1, sh, shi);
+    double* rout = (a.P > 1 && a.rkept) ? a.rkept + (b * a.P + w) * (int64_t)a.chunk : nullptr;
+    const AcceptPart part = chunk_sums<NT>(zk, sk, qk, T, c0, c1, sh, shi, rout);
     if (a.P > 1) {
         if (threadIdx.x == 0) {
             a.parts[b * a.P + w] = part;
@@ -484,7 +512,7 @@ __global__ __launch_bounds__(NT) void accept_chunk_kernel(AcceptArgs a) {
     if (threadIdx.x == 0) s_part = part;
     __syncthreads();
     finish_problem<NT>(zk, sk, qk, db, &s_part, 1, a.chunk, a.D, a.V, T, ps, s_u, a.out_tokens + b * (a.D + 1),
-                       a.out_nacc + b, a.out_flags + b, sh, shi);
+                       a.out_nacc + b, a.out_flags + b, sh, shi, nullptr);
 }
 
 // grid (B): combine the P chunk sums of problem b and sample its token.
@@ -516,7 +544,8 @@ __global__ __launch_bounds__(NT) void accept_finish_kernel(AcceptArgs a) {
     const vw4_rowstat sk = s_slot.sk;
     const float* qk = (k < a.D) ? qb + (int64_t)k * a.V : nullptr;
     finish_problem<NT>(zk, sk, qk, db, sp, a.P, a.chunk, a.D, a.V, T, ps, s_u, a.out_tokens + b * (a.D + 1),
-                       a.out_nacc + b, a.out_flags + b, sh, shi);
+                       a.out_nacc + b, a.out_flags + b, sh, shi,
+                       a.rkept ? a.rkept + b * a.P * (int64_t)a.chunk : nullptr);
 }
 
 // T == 0: every target row is one-hot at its argmax a_i, so the outcome of the
@@ -589,6 +618,7 @@ static int spec_accept_impl(const float* logits, int64_t logits_bstride, const v
     a.out_tokens = out_tokens; a.out_nacc = out_n_acc; a.out_flags = out_flags;
     a.parts = (AcceptPart*)((char*)ws + L.off_part);
     a.states = (ProblemSlot*)((char*)ws + L.off_state);
+    a.rkept = L.keep_r ? (double*)((char*)ws + L.off_r) : nullptr;
     a.step_dev = step_dev;
     a.row0 = row0; a.cstream = cstream;
     hipStream_t st = (hipStream_t)stream;
