@@ -20,20 +20,24 @@
 // dependent launch about 1.7 us), and every cross-workgroup combination is a
 // fixed-order sum, so all statistics are reproducible bit for bit:
 //   1. per chunk: local max m_w, e_j relative to m_w (stored, fp64), E_w, and a
-//      mass histogram of the top 11 key bits (LDS)
-//   2. combine: rescale by exp((m_w - m)/T), sum the histograms in chunk order
-//   3. per chunk: descend the level-1 histogram to the bin holding the cutoff;
-//      histogram of the next 11 key bits inside it
-//   4. combine level 2
-//   5. per chunk: descend both levels; fixed-order mass and count above the
-//      22-bit key prefix of the cutoff; counts of the last 10 key bits inside it,
-//      published as a short list of the non-empty bins (the dense counts only
-//      when the list overflows its 256-byte record)
-//   6. per row: with the 10-bit counts every bin is one float value, so its mass
+//      mass histogram of the top 11 key bits (LDS), stored with its 64 coarse
+//      sums (32 bins each)
+//   2. per chunk: combine the chunks' coarse sums (rescaled by exp((m_w - m)/T),
+//      chunk order), descend them to the coarse bin holding the cutoff, then
+//      combine and descend only that coarse bin's 32 histogram bins: the
+//      level-1 cutoff bin (workgroup 0 publishes it); histogram of the next 11
+//      key bits inside it, with its coarse sums
+//   3. per chunk: the same two-step descent of level 2 from the published
+//      level-1 result; fixed-order mass and count above the 22-bit key prefix
+//      of the cutoff; counts of the last 10 key bits inside it, published as a
+//      short list of the non-empty bins (the dense counts only when the list
+//      overflows its 256-byte record)
+//   4. per row: with the 10-bit counts every bin is one float value, so its mass
 //      is count * exp((z - m)/T) exactly; finish the descent, tau, Z, n_kept.
-// The LDS histogram atomics only steer steps 3 and 5; the final decision in
-// step 6 uses fixed-order sums and flags (VW4_FLAG_TOPP_TIE) any row whose
-// boundary mass lies within 1e-9 * E of top_p * E.
+// The LDS histogram atomics and the coarse sums only steer steps 2 and 3; the
+// final decision in step 4 uses fixed-order sums and flags (VW4_FLAG_TOPP_TIE)
+// any row whose boundary mass lies within 1e-9 * E of top_p * E, which is also
+// where a steering sum could pick a neighbouring bin.
 #include <math.h>
 
 #include "common.h"
@@ -46,7 +50,8 @@ constexpr int VMAXP = 64;      // workgroups per row at most
 constexpr int L1BITS = 11, L2BITS = 11, L3BITS = 10;
 constexpr int HB = 2048;       // histogram bins of levels 1 and 2
 constexpr int HB3 = 1024;      // bins of level 3
-constexpr int CB = 256;        // bins combined per workgroup in the combine kernel
+constexpr int NC = 64;         // coarse bins per level (HB / NC = 32 histogram bins each)
+constexpr int FPC = HB / NC;   // histogram bins per coarse bin
 
 struct ChunkPart {   // per-workgroup results of phase 1
     float m;
@@ -70,9 +75,17 @@ struct ChunkSums {   // per-workgroup results of phase 5
 constexpr int REC = 64, REC_HEAD = 5, REC_CAP = REC - REC_HEAD;
 static_assert(sizeof(ChunkSums) == 16, "ChunkSums fills record words 0-3");
 
+// The level-1 cutoff bin and the mass above it, as the level-2 pass found
+// them (every workgroup of a row finds the same; workgroup 0 publishes).
+struct Steer {
+    int32_t b;
+    int32_t pad;
+    double above;
+};
+
 struct VocabLayout {
     int P, chunk, V, rows;
-    size_t off_part, off_e, off_h1p, off_h1, off_h2p, off_h2, off_rec, off_c3, total;
+    size_t off_part, off_e, off_h1p, off_h1c, off_h2p, off_h2c, off_steer, off_rec, off_c3, total;
 };
 
 static size_t al256(size_t o) { return (o + 255) / 256 * 256; }
@@ -93,9 +106,10 @@ static VocabLayout vocab_layout(int rows, int V) {
     L.off_part = o; o = al256(o + (size_t)rows * P * sizeof(ChunkPart));
     L.off_e = o;    o = al256(o + (size_t)rows * V * sizeof(double));
     L.off_h1p = o;  o = al256(o + (size_t)rows * P * HB * sizeof(double));
-    L.off_h1 = o;   o = al256(o + (size_t)rows * HB * sizeof(double));
+    L.off_h1c = o;  o = al256(o + (size_t)rows * P * NC * sizeof(double));
     L.off_h2p = o;  o = al256(o + (size_t)rows * P * HB * sizeof(double));
-    L.off_h2 = o;   o = al256(o + (size_t)rows * HB * sizeof(double));
+    L.off_h2c = o;  o = al256(o + (size_t)rows * P * NC * sizeof(double));
+    L.off_steer = o; o = al256(o + (size_t)rows * sizeof(Steer));
     L.off_rec = o;  o = al256(o + (size_t)rows * P * REC * sizeof(uint32_t));
     L.off_c3 = o;   o = al256(o + (size_t)rows * P * HB3 * sizeof(uint32_t));
     L.total = o;
@@ -105,10 +119,11 @@ static VocabLayout vocab_layout(int rows, int V) {
 struct RowView {     // pointers of one row inside the workspace
     ChunkPart* part;
     double* e;
-    double* h1p;
-    double* h1;
+    double* h1p;     // [P][HB] chunk histograms of level 1
+    double* h1c;     // [P][NC] their coarse sums
     double* h2p;
-    double* h2;
+    double* h2c;
+    Steer* steer;
     uint32_t* rec;
     uint32_t* c3;
 };
@@ -118,9 +133,10 @@ __device__ __forceinline__ RowView row_view(char* ws, const VocabLayout& L, int 
     v.part = (ChunkPart*)(ws + L.off_part) + (int64_t)r * L.P;
     v.e = (double*)(ws + L.off_e) + (int64_t)r * L.V;
     v.h1p = (double*)(ws + L.off_h1p) + (int64_t)r * L.P * HB;
-    v.h1 = (double*)(ws + L.off_h1) + (int64_t)r * HB;
+    v.h1c = (double*)(ws + L.off_h1c) + (int64_t)r * L.P * NC;
     v.h2p = (double*)(ws + L.off_h2p) + (int64_t)r * L.P * HB;
-    v.h2 = (double*)(ws + L.off_h2) + (int64_t)r * HB;
+    v.h2c = (double*)(ws + L.off_h2c) + (int64_t)r * L.P * NC;
+    v.steer = (Steer*)(ws + L.off_steer) + r;
     v.rec = (uint32_t*)(ws + L.off_rec) + (int64_t)r * L.P * REC;
     v.c3 = (uint32_t*)(ws + L.off_c3) + (int64_t)r * L.P * HB3;
     return v;
@@ -258,15 +274,9 @@ __device__ __forceinline__ double wave_combine_E(const ChunkPart* sp, int P, flo
 
 // Descend nb combined bins (ascending key, HB/VT = 8 per thread, this
 // thread's slice in h): the largest bin b with
-// above + sum_{b' >= b} H[b'] >= target.  Returns -1 if none.
-// This thread's slice of a combined histogram (requested early, so that it
-// travels together with the kernel's other loads).
-__device__ __forceinline__ void load_slice(const double* __restrict__ H, int nb, double (&h)[HB / VT]) {
-    const int b0 = threadIdx.x * (HB / VT);
-#pragma unroll
-    for (int i = 0; i < HB / VT; ++i) h[i] = (b0 + i < nb) ? H[b0 + i] : 0.0;
-}
-
+// above + sum_{b' >= b} H[b'] >= target, and the mass above it.  If rounding
+// leaves the target beyond every bin, the lowest non-empty bin (-1 if all are
+// empty); the finishing pass flags such a row.
 __device__ int descend(const double (&h)[HB / VT], int nb, double above, double target, double* new_above,
                        double* sh, int* shi) {
     const int per = HB / VT;
@@ -309,6 +319,88 @@ __device__ int descend(const double (&h)[HB / VT], int nb, double above, double 
     }
     *new_above = na;
     return b;
+}
+
+// Coarse sums of a chunk histogram in LDS: coarse bin c is the sum of bins
+// c*FPC .. c*FPC + FPC - 1, four threads of 8 bins each (the reading order
+// rotated by c against LDS bank conflicts), then combined pairwise; written to
+// dst[c].  A fixed order: the sums are the same at every call.
+__device__ __forceinline__ void write_coarse(const double* hist, double* __restrict__ dst) {
+    const int c = threadIdx.x >> 2, q = threadIdx.x & 3;
+    double a = 0.0;
+#pragma unroll
+    for (int i = 0; i < FPC / 4; ++i) a += hist[c * FPC + q * (FPC / 4) + ((i + c) & (FPC / 4 - 1))];
+    a += __shfl_xor(a, 1, 64);
+    a += __shfl_xor(a, 2, 64);
+    if (q == 0) dst[c] = a;
+}
+static_assert(VT == 4 * NC && FPC % 4 == 0, "write_coarse: four threads per coarse bin");
+
+// The P chunks' coarse sums [P][NC] into LDS, loads issued together.
+constexpr int SC_U = VMAXP * NC / VT;
+__device__ __forceinline__ void stage_coarse(const double* __restrict__ hc, int P, double* s_c) {
+    double v[SC_U];
+    const int n = P * NC;
+#pragma unroll
+    for (int u = 0; u < SC_U; ++u) v[u] = hc[min((int)threadIdx.x + u * VT, n - 1)];
+#pragma unroll
+    for (int u = 0; u < SC_U; ++u)
+        if ((int)threadIdx.x + u * VT < n) s_c[threadIdx.x + u * VT] = v[u];
+    __syncthreads();
+}
+
+// One level's cutoff bin from the chunk histograms hp [P][HB] and their coarse
+// sums (staged in s_c [P][NC]): combine the coarse sums over the chunks in
+// chunk order (times f[k] if f is set), descend to the coarse bin c holding
+// the target, then load, combine and descend only the FPC histogram bins of c.
+// Returns the bin (or -1 as descend does) and the mass above it.  Where
+// rounding makes the coarse and the fine sums disagree about the crossing
+// (a target within rounding of a coarse boundary), descend's fallback keeps a
+// bin and the finishing pass, whose sums are exact in a fixed order, flags
+// the row.  s_c is reused for the fine bins.
+__device__ int steer(const double* __restrict__ hp, double* s_c, const double* f, int P, double above,
+                     double target, double* new_above, double* s_bins, double* sh, int* shi) {
+    const int tid = threadIdx.x;
+    if (tid < NC) {
+        double a = 0.0;
+        for (int k = 0; k < P; ++k) a += f ? f[k] * s_c[k * NC + tid] : s_c[k * NC + tid];
+        s_bins[tid] = a;
+    }
+    __syncthreads();
+    double h[HB / VT];
+#pragma unroll
+    for (int i = 0; i < HB / VT; ++i) h[i] = (tid < NC / (HB / VT)) ? s_bins[tid * (HB / VT) + i] : 0.0;
+    double above_c;
+    const int c = descend(h, NC, above, target, &above_c, sh, shi);
+    if (c < 0) {
+        *new_above = above_c;
+        return -1;
+    }
+    // the fine bins of c from every chunk, loads issued together
+    constexpr int SF_U = VMAXP * FPC / VT;
+    double v[SF_U];
+    const int n = P * FPC;
+#pragma unroll
+    for (int u = 0; u < SF_U; ++u) {
+        const int i = min(tid + u * VT, n - 1);
+        v[u] = hp[(int64_t)(i / FPC) * HB + c * FPC + i % FPC];
+    }
+#pragma unroll
+    for (int u = 0; u < SF_U; ++u)
+        if (tid + u * VT < n) s_c[tid + u * VT] = v[u];
+    __syncthreads();
+    if (tid < FPC) {
+        double a = 0.0;
+        for (int k = 0; k < P; ++k) a += f ? f[k] * s_c[k * FPC + tid] : s_c[k * FPC + tid];
+        s_bins[tid] = a;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < HB / VT; ++i) h[i] = (tid < FPC / (HB / VT)) ? s_bins[tid * (HB / VT) + i] : 0.0;
+    double above_f;
+    const int bf = descend(h, FPC, above_c, target, &above_f, sh, shi);
+    *new_above = above_f;
+    return bf < 0 ? -1 : c * FPC + bf;
 }
 
 // ---------------------------------------------------------------------------
@@ -398,44 +490,16 @@ __global__ __launch_bounds__(VT) void vs_chunk_kernel(const float* __restrict__ 
             }
         }
         E_w = block_sum_f64(es, shd);
-        if (hist_on)
+        if (hist_on) {
             for (int b = tid; b < HB; b += VT) rv.h1p[(int64_t)w * HB + b] = hist[b];
+            write_coarse(hist, rv.h1c + (int64_t)w * NC);
+        }
     }
     if (tid == 0) {
         ChunkPart p;
         p.m = m_w; p.argmax = a_w; p.bad = bad_w; p.mn = mn_w; p.E = E_w;
         rv.part[w] = p;
     }
-}
-
-// Phases 2 and 4: combine the chunk histograms of one level, in chunk order.
-// Level 1 rescales chunk w by exp((m_w - m)/T); level 2 histograms are
-// already relative to the row max.  grid = (HB / CB, rows), CB threads.
-template <int LEVEL>
-__global__ __launch_bounds__(CB) void vs_combine_kernel(float temperature, char* __restrict__ ws, VocabLayout L) {
-    __shared__ double f[VMAXP];
-    __shared__ ChunkPart sp[VMAXP];
-    const int r = blockIdx.y, b = blockIdx.x * CB + threadIdx.x;
-    const RowView rv = row_view(ws, L, r);
-    stage_parts(rv.part, L.P, sp);
-    const RowMax mx = combine_max(sp, L.P);
-    if (mx.bad || !(temperature > 0.0f)) return;
-    const double T = (double)temperature;
-    if (LEVEL == 1) {
-        for (int k = threadIdx.x; k < L.P; k += CB) f[k] = exp(((double)sp[k].m - (double)mx.m) / T);
-        __syncthreads();
-    }
-    const double* src = (LEVEL == 1) ? rv.h1p : rv.h2p;
-    double* dst = (LEVEL == 1) ? rv.h1 : rv.h2;
-    // all P partials of this bin in flight at once (P <= VMAXP), then summed in order
-    double v[VMAXP];
-#pragma unroll
-    for (int i = 0; i < VMAXP; ++i) v[i] = (i < L.P) ? src[(int64_t)i * HB + b] : 0.0;
-    double acc = 0.0;
-#pragma unroll
-    for (int i = 0; i < VMAXP; ++i)
-        if (i < L.P) acc += (LEVEL == 1) ? f[i] * v[i] : v[i];
-    dst[b] = acc;
 }
 
 // Phase 3: level-2 histogram of the chunk's logits inside the level-1 cutoff bin.
@@ -446,17 +510,19 @@ __global__ __launch_bounds__(VT) void vs_level2_kernel(const float* __restrict__
     __shared__ int shi[4];
     __shared__ ChunkPart sp[VMAXP];
     __shared__ double f[VMAXP];
+    __shared__ double s_c[VMAXP * NC];
+    __shared__ double s_bins[NC];
     const int w = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
     const RowView rv = row_view(ws, L, r);
     const float* z = logits + (int64_t)r * L.V;
     const int c0 = w * L.chunk, c1 = min(L.V, c0 + L.chunk);
     // every independent load first (one memory round trip): the chunk's first
-    // tile of logits and e, this thread's level-1 slice, the chunk parts
+    // tile of logits and e, the level-1 coarse sums, the chunk parts
     float v0[VU];
-    double e0[VU], h1[HB / VT];
+    double e0[VU];
     load_tile(z, c0, c1, v0);
     load_tile((const double*)rv.e, c0, c1, e0);
-    load_slice(rv.h1, HB, h1);
+    stage_coarse(rv.h1c, L.P, s_c);
     stage_parts(rv.part, L.P, sp);
     const RowMax mx = combine_max(sp, L.P);
     if (mx.bad || !(temperature > 0.0f)) return;
@@ -464,7 +530,12 @@ __global__ __launch_bounds__(VT) void vs_level2_kernel(const float* __restrict__
     const double E = combine_E(sp, L.P, mx.m, T, f);
     const double target = (double)top_p * E;
     double above1;
-    int b1 = descend(h1, HB, 0.0, target, &above1, shd, shi);
+    const int b1 = steer(rv.h1p, s_c, f, L.P, 0.0, target, &above1, s_bins, shd, shi);
+    if (w == 0 && tid == 0) {
+        Steer st;
+        st.b = b1; st.pad = 0; st.above = above1;
+        *rv.steer = st;
+    }
     const double fw = f[w];
     for (int b = tid; b < HB; b += VT) hist[b] = 0.0;
     __syncthreads();
@@ -490,6 +561,7 @@ __global__ __launch_bounds__(VT) void vs_level2_kernel(const float* __restrict__
     }
     __syncthreads();
     for (int b = tid; b < HB; b += VT) rv.h2p[(int64_t)w * HB + b] = hist[b];
+    write_coarse(hist, rv.h2c + (int64_t)w * NC);
 }
 
 // Phase 5: fixed-order mass/count above the 22-bit cutoff prefix and the
@@ -503,26 +575,30 @@ __global__ __launch_bounds__(VT) void vs_level3_kernel(const float* __restrict__
     __shared__ ChunkPart sp[VMAXP];
     __shared__ double f[VMAXP];
     __shared__ uint32_t s_nz;
+    __shared__ double s_c[VMAXP * NC];
+    __shared__ double s_bins[NC];
     const int w = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
     const RowView rv = row_view(ws, L, r);
     const float* z = logits + (int64_t)r * L.V;
     const int c0 = w * L.chunk, c1 = min(L.V, c0 + L.chunk);
-    // every independent load first (one memory round trip)
+    // every independent load first (one memory round trip): the tiles, the
+    // level-1 cutoff the level-2 pass published, the level-2 coarse sums
     float v0[VU];
-    double e0[VU], h1[HB / VT], h2[HB / VT];
+    double e0[VU];
     load_tile(z, c0, c1, v0);
     load_tile((const double*)rv.e, c0, c1, e0);
-    load_slice(rv.h1, HB, h1);
-    load_slice(rv.h2, HB, h2);
+    const Steer st1 = *rv.steer;
+    stage_coarse(rv.h2c, L.P, s_c);
     stage_parts(rv.part, L.P, sp);
     const RowMax mx = combine_max(sp, L.P);
     if (mx.bad || !(temperature > 0.0f)) return;
     const double T = (double)temperature;
     const double E = combine_E(sp, L.P, mx.m, T, f);
     const double target = (double)top_p * E;
-    double above1, above2 = 0.0;
-    int b1 = descend(h1, HB, 0.0, target, &above1, shd, shi);
-    int b2 = (b1 >= 0) ? descend(h2, HB, above1, target, &above2, shd, shi) : -1;
+    const int b1 = st1.b;
+    const double above1 = st1.above;
+    double above2 = 0.0;
+    const int b2 = (b1 >= 0) ? steer(rv.h2p, s_c, nullptr, L.P, above1, target, &above2, s_bins, shd, shi) : -1;
     const double fw = f[w];
     for (int b = tid; b < HB3; b += VT) cnt[b] = 0u;
     if (tid == 0) s_nz = 0u;
@@ -1045,12 +1121,10 @@ int verify_logits(const uint16_t* hidden, int64_t ldh, const uint8_t* lm_packed,
         return check_launch("verify_logits");
     }
     char* w = (char*)ws;
-    const dim3 grid(L.P, rows), cgrid(HB / CB, rows);
+    const dim3 grid(L.P, rows);
     hipLaunchKernelGGL(vs_chunk_kernel, grid, dim3(VT), 0, st, logits, temperature, top_p, w, L);
     if (temperature > 0.0f && top_p < 1.0f) {
-        hipLaunchKernelGGL(vs_combine_kernel<1>, cgrid, dim3(CB), 0, st, temperature, w, L);
         hipLaunchKernelGGL(vs_level2_kernel, grid, dim3(VT), 0, st, logits, temperature, top_p, w, L);
-        hipLaunchKernelGGL(vs_combine_kernel<2>, cgrid, dim3(CB), 0, st, temperature, w, L);
         hipLaunchKernelGGL(vs_level3_kernel, grid, dim3(VT), 0, st, logits, temperature, top_p, w, L);
     }
     hipLaunchKernelGGL(vs_finish_kernel, dim3(rows), dim3(HB3), 0, st, temperature, top_p, w, L, stats);
