@@ -334,15 +334,21 @@ __device__ __forceinline__ void write_coarse(const double* hist, double* __restr
     a += __shfl_xor(a, 2, 64);
     if (q == 0) dst[c] = a;
 }
-static_assert(VT == 4 * NC && FPC % 4 == 0, "write_coarse: four threads per coarse bin");
+static_assert(VT == 4 * NC && VT == 8 * FPC && FPC % 4 == 0 && VMAXP % 8 == 0,
+              "four threads per coarse bin, eight per histogram bin of a coarse bin");
 
-// The P chunks' coarse sums [P][NC] into LDS, loads issued together.
+// The P chunks' coarse sums [P][NC]: the loads issued together (load_coarse,
+// early, so that they travel with the kernel's other loads), then stored in
+// LDS (commit_coarse).
 constexpr int SC_U = VMAXP * NC / VT;
-__device__ __forceinline__ void stage_coarse(const double* __restrict__ hc, int P, double* s_c) {
-    double v[SC_U];
+__device__ __forceinline__ void load_coarse(const double* __restrict__ hc, int P, double (&v)[SC_U]) {
     const int n = P * NC;
 #pragma unroll
     for (int u = 0; u < SC_U; ++u) v[u] = hc[min((int)threadIdx.x + u * VT, n - 1)];
+}
+
+__device__ __forceinline__ void commit_coarse(const double (&v)[SC_U], int P, double* s_c) {
+    const int n = P * NC;
 #pragma unroll
     for (int u = 0; u < SC_U; ++u)
         if ((int)threadIdx.x + u * VT < n) s_c[threadIdx.x + u * VT] = v[u];
@@ -350,7 +356,7 @@ __device__ __forceinline__ void stage_coarse(const double* __restrict__ hc, int 
 }
 
 // One level's cutoff bin from the chunk histograms hp [P][HB] and their coarse
-// sums (staged in s_c [P][NC]): combine the coarse sums over the chunks in
+// sums (in LDS, s_c [P][NC]): combine the coarse sums over the chunks in
 // chunk order (times f[k] if f is set), descend to the coarse bin c holding
 // the target, then load, combine and descend only the FPC histogram bins of c.
 // Returns the bin (or -1 as descend does) and the mass above it.  Where
@@ -361,10 +367,27 @@ __device__ __forceinline__ void stage_coarse(const double* __restrict__ hc, int 
 __device__ int steer(const double* __restrict__ hp, double* s_c, const double* f, int P, double above,
                      double target, double* new_above, double* s_bins, double* sh, int* shi) {
     const int tid = threadIdx.x;
-    if (tid < NC) {
+    // coarse bin tid / 4 over chunk slots 16 (tid % 4) .. +16, then the four
+    // partial sums pairwise (the reads of a run issued together)
+    {
+        const int cb = tid >> 2, q = tid & 3;
         double a = 0.0;
-        for (int k = 0; k < P; ++k) a += f ? f[k] * s_c[k * NC + tid] : s_c[k * NC + tid];
-        s_bins[tid] = a;
+        if (f) {
+#pragma unroll
+            for (int u = 0; u < VMAXP / 4; ++u) {
+                const int k = q * (VMAXP / 4) + u;
+                if (k < P) a += f[k] * s_c[k * NC + cb];
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < VMAXP / 4; ++u) {
+                const int k = q * (VMAXP / 4) + u;
+                if (k < P) a += s_c[k * NC + cb];
+            }
+        }
+        a += __shfl_xor(a, 1, 64);
+        a += __shfl_xor(a, 2, 64);
+        if (q == 0) s_bins[cb] = a;
     }
     __syncthreads();
     double h[HB / VT];
@@ -389,10 +412,28 @@ __device__ int steer(const double* __restrict__ hp, double* s_c, const double* f
     for (int u = 0; u < SF_U; ++u)
         if (tid + u * VT < n) s_c[tid + u * VT] = v[u];
     __syncthreads();
-    if (tid < FPC) {
+    // bin tid / 8 of c over chunk slots 8 (tid % 8) .. +8, then the eight
+    // partial sums pairwise
+    {
+        const int fb = tid >> 3, q = tid & 7;
         double a = 0.0;
-        for (int k = 0; k < P; ++k) a += f ? f[k] * s_c[k * FPC + tid] : s_c[k * FPC + tid];
-        s_bins[tid] = a;
+        if (f) {
+#pragma unroll
+            for (int u = 0; u < VMAXP / 8; ++u) {
+                const int k = q * (VMAXP / 8) + u;
+                if (k < P) a += f[k] * s_c[k * FPC + fb];
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < VMAXP / 8; ++u) {
+                const int k = q * (VMAXP / 8) + u;
+                if (k < P) a += s_c[k * FPC + fb];
+            }
+        }
+        a += __shfl_xor(a, 1, 64);
+        a += __shfl_xor(a, 2, 64);
+        a += __shfl_xor(a, 4, 64);
+        if (q == 0) s_bins[fb] = a;
     }
     __syncthreads();
 #pragma unroll
@@ -519,11 +560,12 @@ __global__ __launch_bounds__(VT) void vs_level2_kernel(const float* __restrict__
     // every independent load first (one memory round trip): the chunk's first
     // tile of logits and e, the level-1 coarse sums, the chunk parts
     float v0[VU];
-    double e0[VU];
+    double e0[VU], cv[SC_U];
     load_tile(z, c0, c1, v0);
     load_tile((const double*)rv.e, c0, c1, e0);
-    stage_coarse(rv.h1c, L.P, s_c);
+    load_coarse(rv.h1c, L.P, cv);
     stage_parts(rv.part, L.P, sp);
+    commit_coarse(cv, L.P, s_c);
     const RowMax mx = combine_max(sp, L.P);
     if (mx.bad || !(temperature > 0.0f)) return;
     const double T = (double)temperature;
@@ -584,12 +626,13 @@ __global__ __launch_bounds__(VT) void vs_level3_kernel(const float* __restrict__
     // every independent load first (one memory round trip): the tiles, the
     // level-1 cutoff the level-2 pass published, the level-2 coarse sums
     float v0[VU];
-    double e0[VU];
+    double e0[VU], cv[SC_U];
     load_tile(z, c0, c1, v0);
     load_tile((const double*)rv.e, c0, c1, e0);
     const Steer st1 = *rv.steer;
-    stage_coarse(rv.h2c, L.P, s_c);
+    load_coarse(rv.h2c, L.P, cv);
     stage_parts(rv.part, L.P, sp);
+    commit_coarse(cv, L.P, s_c);
     const RowMax mx = combine_max(sp, L.P);
     if (mx.bad || !(temperature > 0.0f)) return;
     const double T = (double)temperature;
