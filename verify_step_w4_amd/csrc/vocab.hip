@@ -209,30 +209,6 @@ __device__ __forceinline__ void stage_parts(const ChunkPart* __restrict__ part, 
     __syncthreads();
 }
 
-__device__ __forceinline__ RowMax combine_max(const ChunkPart* sp, int P) {
-    RowMax r;
-    r.m = -INFINITY;
-    r.mn = INFINITY;
-    r.argmax = 0;
-    r.bad = 0;
-    for (int k = 0; k < P; ++k) {
-        r.bad |= sp[k].bad;
-        r.mn = fminf(r.mn, sp[k].mn);
-        if (sp[k].m > r.m) { r.m = sp[k].m; r.argmax = sp[k].argmax; }  // chunks ascend: first max = lowest index
-    }
-    return r;
-}
-
-// Rescale factors f_w = exp((m_w - m)/T) into LDS, then
-// E = sum_w f_w E_w in chunk order.
-__device__ __forceinline__ double combine_E(const ChunkPart* sp, int P, float m, double T, double* f) {
-    for (int k = threadIdx.x; k < P; k += blockDim.x) f[k] = exp(((double)sp[k].m - (double)m) / T);
-    __syncthreads();
-    double E = 0.0;
-    for (int k = 0; k < P; ++k) E += f[k] * sp[k].E;
-    return E;
-}
-
 // Row header by one wavefront, lane k holding chunk part k (P <= 64), for
 // the 1024-thread finishing kernel, where the whole-block loops over the parts
 // cost one LDS round trip per part in each of 16 wavefronts.  The max, its
@@ -270,6 +246,32 @@ __device__ __forceinline__ double wave_combine_E(const ChunkPart* sp, int P, flo
     double E = 0.0;
     for (int k = 0; k < P; ++k) E = fma(readlane_f64(f, k), readlane_f64(e, k), E);
     return E;
+}
+
+// The row max and E for the level passes, where they only steer: wavefront 0
+// reduces the chunk parts (lane k holds part k, P <= 64; the max is a pure
+// selection, the same as a scan in chunk order), and the result is broadcast
+// through LDS.  The factors f[k] = exp((m_k - m)/T) are formed in fp64 as in
+// every pass; E is their fixed-tree sum, which may differ from the
+// chunk-order chain of the finishing pass in the last bits.
+__device__ __forceinline__ RowMax steer_max(const ChunkPart* sp, int P, RowMax* s_mx) {
+    if (threadIdx.x < 64) {
+        const RowMax h = wave_combine_max(sp, P);
+        if (threadIdx.x == 0) *s_mx = h;
+    }
+    __syncthreads();
+    return *s_mx;
+}
+
+__device__ __forceinline__ double steer_E(const ChunkPart* sp, int P, float m, double T, double* f, double* s_E) {
+    for (int k = threadIdx.x; k < P; k += blockDim.x) f[k] = exp(((double)sp[k].m - (double)m) / T);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const double e = wave_sum((int)threadIdx.x < P ? f[threadIdx.x] * sp[threadIdx.x].E : 0.0);
+        if (threadIdx.x == 0) *s_E = e;
+    }
+    __syncthreads();
+    return *s_E;
 }
 
 // Descend nb combined bins (ascending key, HB/VT = 8 per thread, this
@@ -566,10 +568,12 @@ __global__ __launch_bounds__(VT) void vs_level2_kernel(const float* __restrict__
     load_coarse(rv.h1c, L.P, cv);
     stage_parts(rv.part, L.P, sp);
     commit_coarse(cv, L.P, s_c);
-    const RowMax mx = combine_max(sp, L.P);
+    __shared__ RowMax s_mx;
+    __shared__ double s_E;
+    const RowMax mx = steer_max(sp, L.P, &s_mx);
     if (mx.bad || !(temperature > 0.0f)) return;
     const double T = (double)temperature;
-    const double E = combine_E(sp, L.P, mx.m, T, f);
+    const double E = steer_E(sp, L.P, mx.m, T, f, &s_E);
     const double target = (double)top_p * E;
     double above1;
     const int b1 = steer(rv.h1p, s_c, f, L.P, 0.0, target, &above1, s_bins, shd, shi);
@@ -633,10 +637,12 @@ __global__ __launch_bounds__(VT) void vs_level3_kernel(const float* __restrict__
     load_coarse(rv.h2c, L.P, cv);
     stage_parts(rv.part, L.P, sp);
     commit_coarse(cv, L.P, s_c);
-    const RowMax mx = combine_max(sp, L.P);
+    __shared__ RowMax s_mx;
+    __shared__ double s_E;
+    const RowMax mx = steer_max(sp, L.P, &s_mx);
     if (mx.bad || !(temperature > 0.0f)) return;
     const double T = (double)temperature;
-    const double E = combine_E(sp, L.P, mx.m, T, f);
+    const double E = steer_E(sp, L.P, mx.m, T, f, &s_E);
     const double target = (double)top_p * E;
     const int b1 = st1.b;
     const double above1 = st1.above;
