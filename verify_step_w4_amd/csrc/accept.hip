@@ -34,7 +34,7 @@ namespace vw4 {
 
 constexpr int AT = 256;          // threads per workgroup for large vocabularies
 constexpr int AT1 = 512;         // one workgroup per problem up to AT1 * 32 entries
-constexpr int ASH = AT1 / 64 + 4;  // block-reduction scratch
+constexpr int ASH = 2 * (AT1 / 64) + 4;  // block-reduction scratch (two values per wavefront)
 constexpr int ACHUNK = 4096;     // vocabulary entries per workgroup
 constexpr int AMAXP = 64;
 constexpr int AMAXD = 7;
@@ -125,32 +125,6 @@ __device__ __forceinline__ double p_val(float v, const vw4_rowstat& s, double T,
     return exp(((double)v - (double)s.max_logit) / T - s.log_z);
 }
 
-
-template <int NT>
-__device__ __forceinline__ double blk_sum(double v, double* sh) {
-    v = wave_sum(v);
-    if (NT == 64) return v;
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) sh[w] = v;
-    __syncthreads();
-    double s = sh[0];
-    for (int k = 1; k < NT / 64; ++k) s += sh[k];
-    __syncthreads();
-    return s;
-}
-
-template <int NT>
-__device__ __forceinline__ int blk_max_i(int v, int* sh) {
-    for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
-    if (NT == 64) return v;
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) sh[w] = v;
-    __syncthreads();
-    int s = sh[0];
-    for (int k = 1; k < NT / 64; ++k) s = max(s, sh[k]);
-    __syncthreads();
-    return s;
-}
 
 // Exclusive prefix sum over threads in thread order (fixed combination order).
 template <int NT>
@@ -272,11 +246,41 @@ __device__ __forceinline__ AcceptPart chunk_sums(const float* __restrict__ zk, c
             }
         }
     }
+    // the four block reductions in one pass: wavefront reductions (fixed
+    // xor trees), one barrier, then the wavefronts' values combined in
+    // wavefront order (the maxima are order-free)
+    double r = wave_sum(sr), p = wave_sum(sp);
+    for (int off = 32; off > 0; off >>= 1) {
+        lr = max(lr, __shfl_xor(lr, off, 64));
+        lp = max(lp, __shfl_xor(lp, off, 64));
+    }
+    if (NT > 64) {
+        constexpr int NW = NT / 64;
+        const int w = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) == 0) {
+            sh[w] = r;
+            sh[NW + w] = p;
+            shi[w] = lr;
+            shi[NW + w] = lp;
+        }
+        __syncthreads();
+        r = sh[0];
+        p = sh[NW];
+        lr = shi[0];
+        lp = shi[NW];
+        for (int k = 1; k < NW; ++k) {
+            r += sh[k];
+            p += sh[NW + k];
+            lr = max(lr, shi[k]);
+            lp = max(lp, shi[NW + k]);
+        }
+        __syncthreads();
+    }
     AcceptPart a;
-    a.r = blk_sum<NT>(sr, sh);
-    a.p = blk_sum<NT>(sp, sh);
-    a.last_r = blk_max_i<NT>(lr, shi);
-    a.last_p = blk_max_i<NT>(lp, shi);
+    a.r = r;
+    a.p = p;
+    a.last_r = lr;
+    a.last_p = lp;
     return a;
 }
 
