@@ -212,11 +212,13 @@ __device__ __forceinline__ ProblemState problem_state(const float* __restrict__ 
 }
 
 // Chunk w of the residual row of problem b: fixed-order sums of r and p_k.
-// rout (if set) receives each entry's mass r (chunk-relative index).
+// rout (if set) receives each entry's mass r (chunk-relative index); qout
+// (if set) the row's p(j) as binary32 (the draft distribution draft_sample
+// returns, written here instead of by a launch of its own).
 template <int NT>
 __device__ __forceinline__ AcceptPart chunk_sums(const float* __restrict__ zk, const vw4_rowstat& sk,
                                                  const float* __restrict__ qk, double T, int c0, int c1, double* sh,
-                                                 int* shi, double* __restrict__ rout) {
+                                                 int* shi, double* __restrict__ rout, float* __restrict__ qout) {
     double sr = 0.0, sp = 0.0;
     int lr = -1, lp = -1;
     for (int base = c0; base < c1; base += NT * AU) {
@@ -239,6 +241,7 @@ __device__ __forceinline__ AcceptPart chunk_sums(const float* __restrict__ zk, c
                 const double pj = p_val(zv[u], sk, T, j);
                 const double rj = qk ? fmax(0.0, pj - (double)qv[u]) : pj;
                 if (rout) rout[j - c0] = rj;
+                if (qout) qout[j] = (float)pj;
                 sr += rj;
                 sp += pj;
                 if (rj > 0.0) lr = j;
@@ -455,6 +458,7 @@ struct AcceptArgs {
     AcceptPart* parts;
     ProblemSlot* states;   // per problem, written by workgroup 0 of the chunk kernel
     double* rkept;         // [B][P][chunk] masses r kept for the finish, or null
+    float* q_out;          // draft_sample (B = 1, D = 0): p of the row as binary32, or null
     const uint64_t* step_dev;  // if set, the first problem's step is read here (graph replays)
     uint64_t row0, cstream;    // Philox counter words 1 (row offset) and 2 (stream): 0 for verify
 };
@@ -488,6 +492,10 @@ __global__ __launch_bounds__(NT) void accept_chunk_kernel(AcceptArgs a) {
     const ProblemState ps =
         problem_state<NT>(zb, sb, qb, db, a.D, a.V, T, a.seed, first_step(a) + (uint64_t)b, a.row0, a.cstream, s_u, s_st);
     if (ps.bad) {
+        if (a.q_out) {  // the same values p_val gives for this row's statistics
+            const int c0 = w * a.chunk, c1 = min(a.V, c0 + a.chunk);
+            for (int j = c0 + (int)threadIdx.x; j < c1; j += NT) a.q_out[j] = (float)p_val(zb[j], s_st[0], T, j);
+        }
         if (w == 0) write_bad(a, b);
         return;
     }
@@ -497,7 +505,7 @@ __global__ __launch_bounds__(NT) void accept_chunk_kernel(AcceptArgs a) {
     const float* qk = (k < a.D) ? qb + (int64_t)k * a.V : nullptr;
     const int c0 = w * a.chunk, c1 = min(a.V, c0 + a.chunk);
     double* rout = (a.P > 1 && a.rkept) ? a.rkept + (b * a.P + w) * (int64_t)a.chunk : nullptr;
-    const AcceptPart part = chunk_sums<NT>(zk, sk, qk, T, c0, c1, sh, shi, rout);
+    const AcceptPart part = chunk_sums<NT>(zk, sk, qk, T, c0, c1, sh, shi, rout, a.q_out);
     if (a.P > 1) {
         if (threadIdx.x == 0) {
             a.parts[b * a.P + w] = part;
@@ -601,7 +609,8 @@ static int spec_accept_impl(const float* logits, int64_t logits_bstride, const v
                             int64_t stats_bstride, const float* q, int64_t q_bstride, const int32_t* draft, int32_t B,
                             int32_t D, int32_t V, float temperature, uint64_t seed, uint64_t step0,
                             const uint64_t* step_dev, int32_t* out_tokens, int32_t* out_n_acc, uint32_t* out_flags,
-                            void* ws, size_t ws_bytes, void* stream, uint64_t row0 = 0, uint64_t cstream = 0) {
+                            void* ws, size_t ws_bytes, void* stream, uint64_t row0 = 0, uint64_t cstream = 0,
+                            float* q_out = nullptr) {
     VW4_REQUIRE(B >= 1 && B <= (1 << 24), VW4_EINVAL, "spec_accept: B=%d out of range", B);
     VW4_REQUIRE(D >= 0 && D <= AMAXD, VW4_EINVAL, "spec_accept: D=%d must be in [0, 7]", D);
     VW4_REQUIRE(V >= 1 && V <= (1 << 24), VW4_EINVAL, "spec_accept: V=%d out of range", V);
@@ -625,6 +634,7 @@ static int spec_accept_impl(const float* logits, int64_t logits_bstride, const v
     a.rkept = L.keep_r ? (double*)((char*)ws + L.off_r) : nullptr;
     a.step_dev = step_dev;
     a.row0 = row0; a.cstream = cstream;
+    a.q_out = q_out;
     hipStream_t st = (hipStream_t)stream;
     if (temperature == 0.0f) {
         hipLaunchKernelGGL(accept_greedy_kernel, dim3((unsigned)B), dim3(64), 0, st, a);
@@ -700,7 +710,9 @@ int draft_sample(const float* logits, const vw4_rowstat* stats, int32_t V, float
     VW4_REQUIRE(ws && ws_bytes >= tail + 256 && aligned(ws, 256), VW4_EWORKSPACE,
                 "draft_sample: needs a 256-byte aligned workspace of %zu bytes", tail + 256);
     hipStream_t st = (hipStream_t)stream;
-    if (q_out) {
+    // T > 0: the sampling pass writes q as it forms p; T == 0 samples without
+    // a pass over the vocabulary, so q (one-hot) gets a launch of its own
+    if (q_out && temperature == 0.0f) {
         hipLaunchKernelGGL(draft_q_kernel, dim3((unsigned)ceil_div(V, 256)), dim3(256), 0, st, logits, stats, V,
                            (double)temperature, q_out);
         const int rc = check_launch("draft_sample");
@@ -708,7 +720,8 @@ int draft_sample(const float* logits, const vw4_rowstat* stats, int32_t V, float
     }
     int32_t* n_acc = (int32_t*)((char*)ws + tail);
     return spec_accept_impl(logits, 0, stats, 0, nullptr, 0, nullptr, 1, 0, V, temperature, seed, step, step_dev,
-                            token_out, n_acc, flags_out, ws, tail, stream, (uint64_t)depth, 1);
+                            token_out, n_acc, flags_out, ws, tail, stream, (uint64_t)depth, 1,
+                            temperature > 0.0f ? q_out : nullptr);
 }
 
 int vw4_step_advance(uint64_t* step_dev, uint64_t inc, void* stream) {
