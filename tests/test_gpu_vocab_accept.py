@@ -241,6 +241,37 @@ def test_accept_kept_masses_equal_recomputed(V, D, T, top_p, case):
         assert np.all(nacc == 0) and np.all(fl & B.FLAG_R_ZERO)
 
 
+@pytest.mark.parametrize("V", [1_000_000, 1 << 20])
+def test_stats_and_accept_at_the_chunk_cap(V):
+    """Vocabularies past 64 chunks of 4096: the chunks grow (15872 or 16384
+    entries, 63 or 64 of them), so the statistics passes run several tiles per
+    chunk and steer with the largest coarse and fine stagings, and the
+    acceptance rescans multi-tile chunks (its masses recomputed).  Statistics
+    and acceptance against the oracle, outside flagged near-ties."""
+    log(f"stats + accept at V={V}")
+    z = synth.synthetic_logits(V % 997 + 3, 4, V, 2.0)
+    for T, top_p in ((0.6, 0.95), (1.0, 0.5), (0.6, 1.0)):
+        assert check_stats(z, T, top_p) <= 1
+    Bn, D, T, top_p = 3, 1, 0.6, 0.95
+    zb = synth.synthetic_logits(V % 991 + 7, Bn * (D + 1), V, 2.0).reshape(Bn, D + 1, V)
+    g = synth.rng(V % 983)
+    ql = synth.normal_f32(g, (Bn, D, V), 3.0)
+    ql[0] = zb[0, :D] / np.float32(T)           # one problem whose draft law is the target's
+    q = synth.softmax_f32(ql)
+    drafts = np.stack([synth.sample_drafts(g, q[b], 1)[0] for b in range(Bn)])
+    seed, step0 = synth.PHILOX_SEED_BASE + 9, 31
+    tok, nacc, fl = run_accept(zb, q, drafts, T, top_p, seed, step0)
+    ties = B.FLAG_TOPP_TIE | B.FLAG_ACCEPT_TIE | B.FLAG_CDF_TIE
+    checked = 0
+    for b in range(Bn):
+        ot, on, of = oracle.spec_accept(zb[b], q[b], drafts[b], T, top_p, seed, step0 + b)[:3]
+        if (of | int(fl[b])) & ties:
+            continue
+        assert int(fl[b]) == of and int(nacc[b]) == on and np.array_equal(tok[b], ot), b
+        checked += 1
+    assert checked >= Bn - 1
+
+
 def test_accept_special_cases():
     V, D = 2000, 3
     M = D + 1
