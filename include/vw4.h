@@ -297,6 +297,20 @@ VW4_API int w4_skinny_gemm_rmsnorm_swiglu(const uint16_t* resid, const uint16_t*
                                           float eps, const uint8_t* w_packed, const uint16_t* scales_packed,
                                           uint16_t* a, int64_t lda, int32_t M, int32_t F, int32_t K, void* stream);
 
+/* vw4_moe_combine followed by vw4_add_rmsnorm_out (with the combined rows as
+ * its single partial slice) in one launch: resid_out = bf16(resid_in + y) and
+ * h = bf16(rmsnorm(resid_out) * gamma), y the weighted sum of the routed
+ * experts' down-projection partials of vw4_moe_combine (gist.science BaseRT
+ * summary, "メソドロジー": fused decode operator sequences; "結果": MoE models
+ * of the Qwen3-30B-A3B class).  Bitwise the two calls' results.  Arguments as
+ * the two calls (part [slot][S][M][ldp] fp32, slot stride p_sstride, 16-byte
+ * aligned, ldp and p_sstride multiples of 4).  Built for topk <= 8 with
+ * D <= 2048 and S <= 4, or D <= 4096 and S <= 2; VW4_EUNSUPPORTED otherwise. */
+VW4_API int vw4_moe_add_rmsnorm(const uint16_t* resid_in, const float* part, int32_t S, int64_t ldp,
+                                int64_t p_sstride, const int32_t* row_slot, const float* weights, int32_t topk,
+                                const uint16_t* gamma, float eps, int32_t M, int32_t D, uint16_t* resid_out,
+                                uint16_t* h, void* stream);
+
 /* From the fused q|k|v projection (partials of [M][(nq + 2 nkv) * hd]): rotary
  * embedding (rotate-half, base theta, position L + m) of q and k; q -> q_out
  * [M][nq][hd]; k appended to the key cache Kc [nkv][Lmax][hd] and v to the

@@ -255,7 +255,15 @@ def test_moe_step_logits_against_oracle():
 
 def _check_moe_step(cap, mv, x, lg, topk, gu, dn, gamma, lm_w, logits):
     """The expert layer (check_moe_layer), then the residual add, the final
-    RMSNorm and the LM head, each from the GPU's own input."""
+    RMSNorm and the LM head, each from the GPU's own input.  With the combine
+    fused into the final norm (MoEVerify.fuse_combine), the forward keeps only
+    the experts' partials; y is formed from them by vw4_moe_combine, whose
+    values the fused launch uses bit for bit."""
+    if mv.fuse_combine:
+        import torch
+        B.moe_combine(mv.part_dn, mv.dn_S, mv.dn_ldp, mv.dn_sstride, mv.row_slot, mv.weights, mv.M, mv.topk, mv.d,
+                      mv.y, mv.d)
+        torch.cuda.synchronize()
     y = host(mv.y).astype(np.float64)
     check_moe_layer(cap, x, lg, topk, gu, dn, y)
     resid = host(mv.resid).copy()
@@ -318,6 +326,58 @@ def test_moe_full_size_grouped_equals_per_expert_dense():
     err = gemm_rel_err(y, ref)
     print(f"[moe full] rel err {err:.3e}", flush=True)
     assert err <= GEMM_RTOL
+
+
+def test_moe_fused_add_rmsnorm_equals_combine_then_norm():
+    """The expert combine inside the final add + RMSNorm launch
+    (vw4_moe_add_rmsnorm) against vw4_moe_combine then vw4_add_rmsnorm_out:
+    the residual and normalised rows bitwise equal, on the full-size MoE step
+    (top-8 of 128, d = 2048) and through MoEVerify.forward with and without
+    the fusion (logits bitwise equal too)."""
+    import torch
+    log("moe fused combine + add + rmsnorm == the two calls")
+    bank, mv = _full_moe(31)
+    c = MOE_30B
+    M, d = 4, c["d"]
+    x = dev(synth.activations_bf16(32, M, d))
+    lg = dev(synth.synthetic_logits(33, M, c["n_exp"], 1.0))
+    outs = []
+    for fused in (False, True):
+        mv.fuse_combine = fused
+        logits = host(mv.forward(x, lg, bank)).copy()
+        torch.cuda.synchronize()
+        outs.append((logits, host(mv.resid).copy(), host(mv.h).copy()))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+    # the call itself on the same partials, against the two calls
+    mv.moe(x, lg, bank)
+    torch.cuda.synchronize()
+    r1 = torch.empty_like(mv.resid)
+    h1 = torch.empty_like(mv.h)
+    B.add_rmsnorm_out(x[:M], mv.y, 1, d, mv.final_gamma, c["eps"], M, d, r1, h1)
+    r2 = torch.full_like(mv.resid, -1)
+    h2 = torch.full_like(mv.h, -1)
+    B.moe_add_rmsnorm(x[:M], mv.part_dn, mv.dn_S, mv.dn_ldp, mv.dn_sstride, mv.row_slot, mv.weights, c["topk"],
+                      mv.final_gamma, c["eps"], M, d, r2, h2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(r1), host(r2)) and np.array_equal(host(h1), host(h2))
+
+
+def test_moe_fused_add_rmsnorm_rejects_unsupported():
+    import torch
+    M, d = 4, 2048
+    part = torch.zeros(4 * 9 * M * d, dtype=torch.float32, device="cuda")
+    rs = torch.zeros((M, 16), dtype=torch.int32, device="cuda")
+    wt = torch.zeros((M, 16), dtype=torch.float32, device="cuda")
+    g = torch.zeros(d, dtype=torch.int16, device="cuda")
+    x = torch.zeros((M, d), dtype=torch.int16, device="cuda")
+    r, h = torch.zeros_like(x), torch.zeros_like(x)
+    with pytest.raises(B.VW4Error, match="built"):
+        B.moe_add_rmsnorm(x, part, 2, d, 2 * M * d, rs, wt, 9, g, 1e-6, M, d, r, h)
+    with pytest.raises(B.VW4Error, match="built"):
+        B.moe_add_rmsnorm(x, part, 5, d, 5 * M * d, rs, wt, 8, g, 1e-6, M, d, r, h)
+    with pytest.raises(B.VW4Error, match="overlap"):
+        B.moe_add_rmsnorm(x, part, 2, d, 2 * M * d, rs, wt, 8, g, 1e-6, M, d, x, h)
 
 
 def test_moe_step_graph_replay_matches_eager():

@@ -127,6 +127,7 @@ SIGNATURES = {
     "vw4_swiglu": (ctypes.c_int, [_P, _I32, _I64, _I32, _I32, _P, _P]),
     "vw4_attn_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I64]),
     "vw4_decode_attn": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "vw4_moe_add_rmsnorm": (ctypes.c_int, [_P, _P, _I32, _I64, _I64, _P, _P, _I32, _P, _F32, _I32, _I32, _P, _P, _P]),
     "vw4_add_sumsq": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _I32, _P, _SZ, _P]),
     "vw4_add_rmsnorm_out": (ctypes.c_int, [_P, _P, _I32, _I64, _P, _F32, _I32, _I32, _P, _P, _P]),
     "w4_skinny_gemm_rmsnorm_partials": (ctypes.c_int, [_P, _P, _P, _F32, _P, _P, _P, _I32, _I32, _I32, _P]),
@@ -718,6 +719,14 @@ def swiglu(part, S: int, ldp: int, M: int, F: int, a, stream=None):
 
 def attn_workspace_bytes(M: int, nq: int, nkv: int, hd: int, ctx: int) -> int:
     return int(lib().vw4_attn_workspace_bytes(M, nq, nkv, hd, ctx))
+
+
+def moe_add_rmsnorm(resid_in, part, S: int, ldp: int, p_sstride: int, row_slot, weights, topk: int, gamma,
+                    eps: float, M: int, D: int, resid_out, h, stream=None):
+    _check("vw4_moe_add_rmsnorm",
+           lib().vw4_moe_add_rmsnorm(_ptr(resid_in), _ptr(part), S, ldp, p_sstride, _ptr(row_slot), _ptr(weights),
+                                     topk, _ptr(gamma), float(eps), M, D, _ptr(resid_out), _ptr(h), _stream(stream)))
+    return resid_out, h
 
 
 def decode_attn(q, Kc, Vc, Lmax: int, L: int, M: int, nq: int, nkv: int, hd: int, out, ws, stream=None):

@@ -140,6 +140,98 @@ __global__ __launch_bounds__(FN_MAXW * 64) void add_rmsnorm_fused_kernel(
     *(uint2*)(h + (int64_t)m * D + col) = ho;
 }
 
+// The MoE block's combine fused into the one-launch add + RMSNorm: the row
+// added to resid_in is y[m][c] = sum_t weights[m][t] * (sum over the S slices
+// of slot row_slot[m][t]'s partials), formed exactly as moe_combine_kernel
+// forms it (the slices summed over 8 clamped slots in slice order, 0 added
+// past S, as sum_parts does; the experts in selection order), then added as
+// the single-slice partial of add_rmsnorm_fused_kernel (0 + y).  So
+// resid_out and h are bitwise those of vw4_moe_combine followed by
+// vw4_add_rmsnorm_out.  Layout and ownership as add_rmsnorm_fused_kernel;
+// topk <= 8, S * 8 * CPW <= 32 four-float loads per lane.
+template <int S, int CPW>
+__global__ __launch_bounds__(FN_MAXW * 64) void moe_add_rmsnorm_kernel(
+    const uint16_t* __restrict__ rin, const float* __restrict__ part, int64_t ldp, int64_t p_sstride,
+    const int32_t* __restrict__ row_slot, const float* __restrict__ weights, int topk,
+    const uint16_t* __restrict__ gamma, float eps, int M, int D, uint16_t* __restrict__ rout,
+    uint16_t* __restrict__ h) {
+    constexpr int TK = 8;
+    __shared__ float s_ssq[FN_MAXCH];
+    const int ch = blockIdx.x, m = blockIdx.y, nch = gridDim.x;
+    const int nw = blockDim.x >> 6;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int own_j = ch / nw, own_w = ch % nw;
+    int64_t sbase[TK];
+    float wt[TK];
+#pragma unroll
+    for (int t = 0; t < TK; ++t) {
+        const int tt = t < topk ? t : topk - 1;
+        sbase[t] = (int64_t)row_slot[m * topk + tt] * p_sstride;
+        wt[t] = weights[m * topk + tt];
+    }
+    uint2 rr[CPW];
+    f32x4 pp[CPW][TK][S];
+    const int gcol = ch * NCOL + 4 * lane < D ? ch * NCOL + 4 * lane : D - 4;
+    const uint2 gg = *(const uint2*)(gamma + gcol);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+        int c = w + nw * j;
+        c = c < nch ? c : nch - 1;
+        int col = c * NCOL + 4 * lane;
+        col = col < D ? col : D - 4;                      // D % 4 == 0
+        rr[j] = *(const uint2*)(rin + (int64_t)m * D + col);
+#pragma unroll
+        for (int t = 0; t < TK; ++t)
+#pragma unroll
+            for (int k = 0; k < S; ++k)
+                pp[j][t][k] = *(const f32x4*)(part + sbase[t] + ((int64_t)k * M + m) * ldp + col);
+    }
+    float own[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+        const int c = w + nw * j;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int t = 0; t < TK; ++t) {
+                float sv = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) sv += (i < S) ? pp[j][t][i < S ? i : S - 1][e] : 0.0f;
+                if (t < topk) acc += wt[t] * sv;
+            }
+            float sp = 0.0f;
+            sp += acc;
+            float x = bf16_to_f32((uint16_t)((e < 2 ? rr[j].x : rr[j].y) >> (16 * (e & 1))));
+            x = bf16_to_f32(f32_to_bf16(x + sp));
+            v[e] = (c < nch && c * NCOL + 4 * lane + e < D) ? x : 0.0f;
+        }
+        const float q = chunk_sumsq(v);
+        if (c < nch && lane == 0) s_ssq[c] = q;
+        if (j == own_j && w == own_w) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) own[e] = v[e];
+        }
+    }
+    __syncthreads();
+    if (w != own_w) return;
+    float tot = 0.0f;
+    for (int c = 0; c < nch; ++c) tot += s_ssq[c];      // chunk order
+    const float inv = 1.0f / sqrtf(tot / (float)D + eps);
+    const int col = ch * NCOL + 4 * lane;
+    if (col >= D) return;
+    const float g[4] = {bf16_to_f32((uint16_t)(gg.x & 0xffffu)), bf16_to_f32((uint16_t)(gg.x >> 16)),
+                        bf16_to_f32((uint16_t)(gg.y & 0xffffu)), bf16_to_f32((uint16_t)(gg.y >> 16))};
+    uint2 ro, ho;
+    ro.x = f32x2_to_bf16x2(own[0], own[1]);
+    ro.y = f32x2_to_bf16x2(own[2], own[3]);
+    ho.x = f32x2_to_bf16x2(own[0] * inv * g[0], own[1] * inv * g[1]);
+    ho.y = f32x2_to_bf16x2(own[2] * inv * g[2], own[3] * inv * g[3]);
+    *(uint2*)(rout + (int64_t)m * D + col) = ro;
+    *(uint2*)(h + (int64_t)m * D + col) = ho;
+}
+
 __global__ __launch_bounds__(NCOL) void rmsnorm_apply_kernel(const uint16_t* __restrict__ resid,
                                                              const uint16_t* __restrict__ gamma, float eps, int D,
                                                              const float* __restrict__ ssq, int nch,
@@ -817,6 +909,43 @@ int vw4_add_rmsnorm_out(const uint16_t* resid_in, const float* part, int32_t S, 
 #undef VW4_FN_CASE
     }
     return check_launch("vw4_add_rmsnorm_out");
+}
+
+int vw4_moe_add_rmsnorm(const uint16_t* resid_in, const float* part, int32_t S, int64_t ldp, int64_t p_sstride,
+                        const int32_t* row_slot, const float* weights, int32_t topk, const uint16_t* gamma, float eps,
+                        int32_t M, int32_t D, uint16_t* resid_out, uint16_t* h, void* stream) {
+    VW4_REQUIRE(resid_in && part && row_slot && weights && gamma && resid_out && h, VW4_EINVAL,
+                "vw4_moe_add_rmsnorm: null pointer");
+    VW4_REQUIRE(M >= 1 && M <= 64 && D >= 4 && D % 4 == 0 && D <= FN_MAXCH * NCOL, VW4_EINVAL,
+                "vw4_moe_add_rmsnorm: need 1 <= M <= 64, D %% 4 == 0, 4 <= D <= %d", FN_MAXCH * NCOL);
+    VW4_REQUIRE(S >= 1 && ldp >= D && ldp % 4 == 0 && p_sstride >= (int64_t)S * M * ldp && p_sstride % 4 == 0 &&
+                    aligned(part, 16),
+                VW4_EINVAL, "vw4_moe_add_rmsnorm: bad partial layout (ldp, slot stride %% 4 == 0, 16-byte aligned)");
+    VW4_REQUIRE(aligned(resid_in, 8) && aligned(resid_out, 8) && aligned(h, 8) && aligned(gamma, 8), VW4_EINVAL,
+                "vw4_moe_add_rmsnorm: resid_in, resid_out, h and gamma need 8-byte alignment");
+    VW4_REQUIRE(eps >= 0.0f, VW4_EINVAL, "vw4_moe_add_rmsnorm: eps must be >= 0");
+    const size_t nb = (size_t)M * D * 2;
+    VW4_REQUIRE(!overlaps(resid_in, nb, resid_out, nb) && !overlaps(resid_in, nb, h, nb) &&
+                    !overlaps(resid_out, nb, h, nb),
+                VW4_EINVAL, "vw4_moe_add_rmsnorm: resid_in, resid_out and h must not overlap");
+    const int nch = (D + NCOL - 1) / NCOL;
+    const int cpw = nch <= 8 ? 1 : (nch <= 16 ? 2 : 3);
+    VW4_REQUIRE(topk >= 1 && topk <= 8 && S * 8 * cpw <= 32, VW4_EUNSUPPORTED,
+                "vw4_moe_add_rmsnorm: topk=%d, S=%d at D=%d (built: topk <= 8, S * 8 * chunks per wavefront <= 32)",
+                topk, S, D);
+    const int nw = (nch + cpw - 1) / cpw;
+    const dim3 grid(nch, M), blk(nw * 64);
+    hipStream_t st = (hipStream_t)stream;
+    switch (S * 4 + cpw) {
+#define VW4_MN_CASE(s, c)                                                                                            \
+    case s * 4 + c:                                                                                                \
+        hipLaunchKernelGGL((moe_add_rmsnorm_kernel<s, c>), grid, blk, 0, st, resid_in, part, ldp, p_sstride, row_slot, \
+                           weights, topk, gamma, eps, M, D, resid_out, h);                                         \
+        break;
+        VW4_MN_CASE(1, 1) VW4_MN_CASE(2, 1) VW4_MN_CASE(3, 1) VW4_MN_CASE(4, 1) VW4_MN_CASE(1, 2) VW4_MN_CASE(2, 2)
+#undef VW4_MN_CASE
+    }
+    return check_launch("vw4_moe_add_rmsnorm");
 }
 
 int vw4_rope_kv_append(const float* part, int32_t S, int64_t ldp, int32_t M, int32_t nq, int32_t nkv, int32_t hd,

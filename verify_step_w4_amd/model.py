@@ -1001,6 +1001,9 @@ class MoEVerify:
         self.y = torch.empty((M, d), dtype=torch.float32, device=device)
         self.resid = torch.empty((M, d), dtype=torch.int16, device=device)
         self.h = torch.empty((M, d), dtype=torch.int16, device=device)
+        # the expert combine inside the final add + RMSNorm launch; False runs
+        # vw4_moe_combine and vw4_add_rmsnorm_out
+        self.fuse_combine = True
         self.norm_ws = B.workspace(B.norm_workspace_bytes(M, d), device)
         self.logits = torch.empty((M, V), dtype=torch.float32, device=device)
         self.lm_ws = B.workspace(B.gemm_workspace_bytes(M, V, d), device)
@@ -1011,8 +1014,9 @@ class MoEVerify:
         self.n_acc = self.outputs[M:M + 1]
         self.flags = self.outputs[M + 1:M + 2]
 
-    def moe(self, x, router_logits, bank: ExpertBank, stream=None, gemm_hook=None):
-        """y[M][d] (fp32) = routed SwiGLU experts of the bf16 rows x."""
+    def moe(self, x, router_logits, bank: ExpertBank, stream=None, gemm_hook=None, combine: bool = True):
+        """y[M][d] (fp32) = routed SwiGLU experts of the bf16 rows x (combine=False
+        stops at the down-projection partials, for a consumer that combines them)."""
         hook = gemm_hook or (lambda when, name: None)
         M, d, F, ms = self.M, self.d, self.F, self.max_slots
         B.moe_route(router_logits, M, self.E, self.topk, self.experts, self.weights, self.slot_expert, self.n_slots,
@@ -1027,8 +1031,9 @@ class MoEVerify:
                           bank.dn_estride[1], self.slot_expert, self.n_slots, ms, self.part_dn, self.dn_sstride,
                           M, d, F, stream)
         hook("post", "down")
-        B.moe_combine(self.part_dn, self.dn_S, self.dn_ldp, self.dn_sstride, self.row_slot, self.weights, M,
-                      self.topk, d, self.y, d, stream)
+        if combine:
+            B.moe_combine(self.part_dn, self.dn_S, self.dn_ldp, self.dn_sstride, self.row_slot, self.weights, M,
+                          self.topk, d, self.y, d, stream)
         return self.y
 
     def gemm_pass(self, bank: ExpertBank, stream=None):
@@ -1049,8 +1054,18 @@ class MoEVerify:
         """Logits [M][V] of the M rows: LM head of bf16(rmsnorm(x + moe(x)) * gamma)."""
         hook = gemm_hook or (lambda when, name: None)
         M, d = self.M, self.d
-        self.moe(x, router_logits, bank, stream, gemm_hook)
-        B.add_rmsnorm_out(x[:M], self.y, 1, d, self.final_gamma, self.cfg["eps"], M, d, self.resid, self.h, stream)
+        nch = (d + 255) // 256
+        cpw = 1 if nch <= 8 else (2 if nch <= 16 else 3)
+        if self.fuse_combine and self.topk <= 8 and self.dn_S * 8 * cpw <= 32 and d % 4 == 0:
+            # the expert combine inside the add + RMSNorm launch (bitwise the two calls)
+            self.moe(x, router_logits, bank, stream, gemm_hook, combine=False)
+            B.moe_add_rmsnorm(x[:M], self.part_dn, self.dn_S, self.dn_ldp, self.dn_sstride, self.row_slot,
+                              self.weights, self.topk, self.final_gamma, self.cfg["eps"], M, d, self.resid, self.h,
+                              stream)
+        else:
+            self.moe(x, router_logits, bank, stream, gemm_hook)
+            B.add_rmsnorm_out(x[:M], self.y, 1, d, self.final_gamma, self.cfg["eps"], M, d, self.resid, self.h,
+                              stream)
         hook("pre", "lm_head")
         B.w4_skinny_gemm(self.h, self.lm_head.packed, self.lm_head.pscales, self.logits, M, self.V, d, ws=self.lm_ws,
                          stream=stream)
