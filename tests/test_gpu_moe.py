@@ -363,6 +363,38 @@ def test_moe_fused_add_rmsnorm_equals_combine_then_norm():
     assert np.array_equal(host(r1), host(r2)) and np.array_equal(host(h1), host(h2))
 
 
+@pytest.mark.parametrize("S,D", [(1, 2048), (2, 2048), (3, 2048), (4, 2048), (1, 4096), (2, 4096), (3, 1028),
+                                 (2, 2500), (4, 4), (1, 3840)])
+@pytest.mark.parametrize("M,topk", [(1, 1), (4, 8), (7, 5)])
+def test_moe_fused_add_rmsnorm_every_instance(S, D, M, topk):
+    """Every built (slices, chunks per wavefront) form of vw4_moe_add_rmsnorm,
+    ragged widths (D not a multiple of 256) and padded partial layouts, against
+    vw4_moe_combine then vw4_add_rmsnorm_out: bitwise equal."""
+    import torch
+    log(f"moe fused norm S={S} D={D} M={M} topk={topk}")
+    n_slots, ldp = 11, D + 12
+    sstride = S * M * ldp + 20
+    g = synth.rng(1000 * S + D + 17 * M + topk)
+    part = dev(synth.normal_f32(g, (n_slots * sstride,), 0.5))
+    rs = np.stack([g.permutation(n_slots)[:topk] for _ in range(M)]).astype(np.int32)
+    wt = g.random((M, topk)).astype(np.float32)
+    wt /= wt.sum(axis=1, keepdims=True)
+    row_slot, weights = dev(rs), dev(wt)
+    x = dev(synth.activations_bf16(D + M, M, D))
+    gamma = dev(synth.f32_to_bf16_bits(1 + synth.normal_f32(g, (D,), 0.1)))
+    y = torch.full((M, D), float("nan"), dtype=torch.float32, device="cuda")
+    B.moe_combine(part, S, ldp, sstride, row_slot, weights, M, topk, D, y, D)
+    r1 = torch.full((M, D), -1, dtype=torch.int16, device="cuda")
+    h1 = torch.full_like(r1, -1)
+    B.add_rmsnorm_out(x, y, 1, D, gamma, 1e-6, M, D, r1, h1)
+    r2 = torch.full_like(r1, -1)
+    h2 = torch.full_like(r1, -1)
+    B.moe_add_rmsnorm(x, part, S, ldp, sstride, row_slot, weights, topk, gamma, 1e-6, M, D, r2, h2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(r1), host(r2))
+    assert np.array_equal(host(h1), host(h2))
+
+
 def test_moe_fused_add_rmsnorm_rejects_unsupported():
     import torch
     M, d = 4, 2048
